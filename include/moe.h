@@ -1,0 +1,200 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) deterministic mixture-of-experts layer library.
+ *
+ * The layer is one GPU's share of a DeepSeek-V3-type MoE layer, the layer type the pages
+ * name (pulsen.vercel.app, "Cursor åpner megakernelen som ga 41 prosent flere tokens i
+ * sekundet", ¶6), run forward in BF16 or MXFP8 and backward in BF16 (same page, ¶3;
+ * aiexpert.news, "Megakernels are dead and back", ¶4), fully deterministic (pulsen ¶3-¶4;
+ * ki-pruefstand.de, "Cursor veröffentlicht MoE-Megakernel Mixture-of-Kittens als Open
+ * Source", ¶2): repeated calls with the same inputs give bit-identical outputs.  No kernel
+ * uses floating-point atomics; every sum runs in one fixed order.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers owned by the caller unless marked "host".  The library
+ *    never allocates, frees or synchronises; scratch memory comes in through `ws`.
+ *  - bf16 tensors are raw 16-bit patterns (uint16_t storage), row-major, rows contiguous.
+ *  - `stream` is a hipStream_t (NULL: the null stream).  Calls only enqueue work on it and
+ *    never read device data back to the host (no CPU-GPU synchronisation; aiexpert.news ¶3,
+ *    ki-pruefstand.de "Kommunikation im Kernel" ¶2).  A kernel fault surfaces at the
+ *    caller's next synchronisation.
+ *  - Arguments are validated on the host before any HIP call; an invalid call returns a
+ *    negative code and enqueues nothing.  Device-resident indices (src, pos, offsets) are
+ *    clamped by the kernels, so that corrupt indices cannot access memory out of bounds.
+ *  - Calls on distinct streams with distinct workspaces may run concurrently; the library
+ *    holds no mutable global state.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* return codes */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)        /* invalid argument (null pointer, size, configuration) */
+#define MOE_EWORKSPACE (-2)    /* workspace missing or smaller than *_workspace_size() */
+#define MOE_EHIP (-3)          /* a HIP launch failed */
+#define MOE_EUNSUPPORTED (-4)  /* current device is not gfx950 */
+
+/* router score functions */
+#define MOE_SCORE_SOFTMAX 0
+#define MOE_SCORE_SIGMOID 1
+
+/* data types */
+#define MOE_BF16 0
+#define MOE_MXFP8 1   /* E4M3 codes with one E8M0 scale per 32 values along K */
+#define MOE_F32 2
+
+/* MX shared-scale rules */
+#define MOE_MX_FLOOR 0  /* 2^(floor(log2 amax) - 8); elements above 448 saturate */
+#define MOE_MX_CEIL 1   /* smallest power of two keeping amax within 448 */
+
+int moe_abi_version(void);
+const char *moe_strerror(int code);
+
+/* ------------------------------------------------------------------ routing
+ * Router configuration (host struct, read during the call).
+ *   score:        MOE_SCORE_SOFTMAX (selection key = logit) or MOE_SCORE_SIGMOID (key =
+ *                 sigmoid(logit) + sel_bias[e]; the sigmoid is a fixed fp32 recipe, see the
+ *                 routing kernel, so keys are reproducible bit for bit);
+ *   n_groups:     >1: experts form n_groups contiguous groups; a group's score is the sum of
+ *                 its top k/topk_groups keys; only the topk_groups best groups stay;
+ *   renorm:       softmax: weights renormalised over the k selected experts (else the full
+ *                 softmax); sigmoid: w = route_scale * s / sum(selected s) (else route_scale*s);
+ *   sel_bias:     DEVICE [E] fp32 added to sigmoid keys for selection only, or NULL.
+ * Ties rank the lower expert (group) id first; slot j holds the j-th best expert. */
+typedef struct moe_route_cfg {
+    int score;
+    int n_groups;
+    int topk_groups;
+    int renorm;
+    float route_scale;
+    const float *sel_bias;
+} moe_route_cfg;
+
+size_t moe_route_workspace_size(int T, int k, int E);
+
+/* moe_route: top-k routing plus the expert-contiguous permutation.
+ *   logits   [T,E] fp32.  Read; or, when w_router != NULL, first WRITTEN with the router
+ *            projection logits[t,e] = sum_h x[t,h]*w_router[e,h], accumulated in fp32 in
+ *            ascending h (exact products, so the result is fixed bit for bit).
+ *   x        [T,H] bf16 and w_router [E,H] bf16: both NULL, or both given.
+ *   idx_in   [T,k] int32 or NULL.  Given: the expert of every routed pair is taken from it
+ *            (one GPU's share of a larger layer); selection is skipped and logits, idx, w,
+ *            s_sel are not touched (may be NULL).
+ *   idx      [T,k] int32  selected experts, slot order = rank order.
+ *   w        [T,k] fp32   routing weights.
+ *   s_sel    [T,k] fp32   selected scores (sigmoid value, or the logit for softmax).
+ *   counts   [E]   int32  routed rows per expert.
+ *   offsets  [E+1] int32  exclusive prefix sum of counts (offsets[E] = T*k).
+ *   pos      [T,k] int32  row of pair (t,j) in expert-contiguous order; rows of one expert are
+ *            in ascending (t,j) order.
+ *   src      [T*k] int32  inverse of pos: src[pos[t,j]] = t*k + j.
+ * Limits: 1 <= k <= min(E, 64), E <= 1024, T >= 0, H % 8 == 0 when projecting.
+ * Outputs are bit-exact functions of the inputs. */
+int moe_route(const float *logits, const void *x, const void *w_router, int T, int H, int E,
+              int k, const moe_route_cfg *cfg, const int32_t *idx_in, int32_t *idx, float *w,
+              float *s_sel, int32_t *counts, int32_t *offsets, int32_t *pos, int32_t *src,
+              void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ dispatch
+ * moe_dispatch: gather token rows into expert-contiguous order ("pull": the destination row
+ * fetches its source, pulsen.vercel.app ¶5): xp[r,:] = x[src[r]/k,:], r in [0,R).
+ *   xp        [R,H] bf16 or NULL: bf16 copy (bit-exact).
+ *   xp_codes  [R,H] E4M3 and xp_scales [R,H/32] E8M0, or both NULL: the rows MX-quantised
+ *             (MOE_MX_FLOOR) in the same pass.  At least one output must be given.
+ * src values outside [0, T*k) produce zero rows.  H % 8 == 0 (H % 32 == 0 for MX). */
+int moe_dispatch(const void *x, int T, int H, int k, const int32_t *src, int R, void *xp,
+                 uint8_t *xp_codes, uint8_t *xp_scales, void *stream);
+
+/* ------------------------------------------------------------------ expert FFN
+ * moe_expert_ffn: per expert e, for its rows r in [offsets[e], offsets[e+1]):
+ *   [g | u] = xp_r . w1[e]^T  (w1[e] is [2I,H]: gate rows 0..I-1 over up rows I..2I-1),
+ *   h = silu(g) * u,  y_r = h . w2[e]^T  (w2[e] is [H,I]);  fp32 accumulation.
+ * The offsets are read on the device (no host readback); each expert's tile list is derived
+ * from them inside the kernels.  offsets == NULL: every one of the E experts takes all R rows
+ * (shared experts) and the outputs are stacked per expert: y [E,R,H], gu [E,R,2I], h [E,R,I].
+ *   dtype = MOE_BF16:  xp [R,H] bf16, w1/w2 bf16, *_scales NULL.  gu_save [R,2I] bf16 and
+ *            h_save [R,I] bf16 are optional saves for the backward (NULL: not written).
+ *   dtype = MOE_MXFP8: xp/w1/w2 are E4M3 codes with E8M0 scales per 32 values along their
+ *            last (K) dimension: xp_scales [R,H/32], w1_scales [E,2I,H/32], w2_scales
+ *            [E,H,I/32].  h is MX-quantised along I from fp32 before the down projection.
+ *            gu_save and h_save must be NULL.
+ *   y [R,H] bf16 (routed rows, expert order).
+ * Limits: H % 64 == 0, I % 64 == 0, offsets non-decreasing with offsets[E] <= R.
+ * Workspace: moe_ffn_workspace_size(). */
+size_t moe_ffn_workspace_size(int dtype, int E, int R, int H, int I, int shared);
+int moe_expert_ffn(int dtype, const void *xp, const uint8_t *xp_scales, const int32_t *offsets,
+                   int E, int R, int H, int I, const void *w1, const uint8_t *w1_scales,
+                   const void *w2, const uint8_t *w2_scales, void *gu_save, void *h_save,
+                   void *y, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ combine
+ * moe_combine: out[t,:] = sum_{j<k} w[t,j] * y[pos[t,j],:] + sum_{s<S} ys[s,t,:], summed in
+ * fp32 in exactly that order (slots, then shared experts), rounded once to bf16 ("push" of
+ * each routed result to its token, pulsen.vercel.app ¶5; weighted combine, no atomics).
+ *   y [R,H] bf16, pos [T,k], w [T,k] fp32, ys [S,T,H] bf16 or NULL (S = 0), out [T,H] bf16.
+ * pos values outside [0,R) contribute nothing.  H % 8 == 0. */
+int moe_combine(const void *y, const int32_t *pos, const float *w, int T, int k, int H, int R,
+                const void *ys, int S, void *out, void *stream);
+
+/* ------------------------------------------------------------------ backward
+ * BF16 backward of the whole layer (pulsen.vercel.app ¶3) given the upstream gradient dout
+ * and the forward's saved tensors.  Gradients flow to x (through the routed and the shared
+ * experts), to every expert weight, to the routing weights and through them to the logits;
+ * no gradient flows through the selection itself.  Weight gradients are full reductions
+ * over each expert's rows in a fixed order (no split-K, no atomics). */
+typedef struct moe_bwd_args {
+    int T, H, E, k, I, R;       /* routed part (R = rows = offsets[E]) */
+    int S, Is;                  /* shared experts (S = 0: none) */
+    int E_router;               /* width of the logits (experts the router scores) */
+    int score, renorm;
+    float route_scale;
+    /* saved forward state */
+    const void *x;              /* [T,H] bf16 (input of the shared experts) */
+    const void *xp;             /* [R,H] bf16 dispatched rows */
+    const void *gu;             /* [R,2I] bf16 saved gate/up pre-activations */
+    const void *h;              /* [R,I] bf16 saved SwiGLU outputs */
+    const void *y;              /* [R,H] bf16 expert outputs */
+    const int32_t *offsets;     /* [E+1] */
+    const int32_t *pos;         /* [T,k] */
+    const int32_t *idx;         /* [T,k] router expert ids, in [0, E_router) */
+    const float *w;             /* [T,k] routing weights */
+    const float *s_sel;         /* [T,k] selected scores */
+    const float *logits;        /* [T,E_router]; read only for softmax without renorm */
+    const void *w1, *w2;        /* [E,2I,H], [E,H,I] bf16 */
+    const void *gus, *hs;       /* [S,T,2Is], [S,T,Is] bf16 (shared experts' saves) */
+    const void *ws1, *ws2;      /* [S,2Is,H], [S,H,Is] bf16 */
+    const void *dout;           /* [T,H] bf16 upstream gradient */
+    /* outputs */
+    void *dx;                   /* [T,H] bf16 */
+    void *dw1, *dw2;            /* [E,2I,H], [E,H,I] bf16 */
+    void *dws1, *dws2;          /* [S,2Is,H], [S,H,Is] bf16 (NULL when S = 0) */
+    float *dw_route;            /* [T,k] fp32: dL/dw[t,j] = <dout[t], y[pos[t,j]]> */
+    float *dlogits;             /* [T,E_router] fp32 */
+} moe_bwd_args;
+
+size_t moe_backward_workspace_size(const moe_bwd_args *a);
+int moe_backward(const moe_bwd_args *a, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ MX quantisation
+ * mx_quantize: OCP microscaling, one E8M0 scale per 32 consecutive values along K and E4M3
+ * ("FN": bias 7, no infinity, max 448) codes, rounded to nearest even and saturating.
+ * MOE_MX_FLOOR: scale 2^(floor(log2 amax) - 8); MOE_MX_CEIL: smallest power of two with
+ * amax/scale <= 448.  An all-zero block gets scale code 0.  Bit-exact.
+ *   in [rows,K] (in_dtype MOE_BF16 or MOE_F32), codes [rows,K] u8, scales [rows,K/32] u8.
+ * K % 32 == 0. */
+int mx_quantize(const void *in, int in_dtype, int rows, int K, uint8_t *codes, uint8_t *scales,
+                int scale_mode, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

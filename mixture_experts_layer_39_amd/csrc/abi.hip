@@ -1,0 +1,176 @@
+// Host side of the C ABI: validation, workspace layout and the call sequences of
+// moe_expert_ffn and moe_backward.  Every call only enqueues kernels on the caller's stream.
+#include <string.h>
+
+#include "common.h"
+
+using moe::bf16_t;
+
+int moe_ffn_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, int I,
+                 const bf16_t* w1, const bf16_t* w2, bf16_t* gu, bf16_t* h, bf16_t* y,
+                 hipStream_t st);
+int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, int I,
+                     const bf16_t* w1, const bf16_t* w2, const bf16_t* gu, const bf16_t* h,
+                     const bf16_t* dy, bf16_t* dgu, bf16_t* dxp, bf16_t* dw1, bf16_t* dw2,
+                     hipStream_t st);
+int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int E, int R, int H,
+               int I, const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q,
+               const uint8_t* w2s, float* hf, uint8_t* hq, uint8_t* hs, bf16_t* y, hipStream_t st);
+int moe_launch_combine_bwd(const bf16_t* dout, const bf16_t* y, const int32_t* pos, const float* w,
+                           int T, int k, int H, int R, bf16_t* dy, float* dw, hipStream_t st);
+int moe_launch_unpermute(const bf16_t* dxp, const int32_t* pos, int T, int k, int H, int R,
+                         const bf16_t* dxs, int S, bf16_t* dx, hipStream_t st);
+int moe_launch_router_bwd(const int32_t* idx, const float* w, const float* s_sel, const float* dw,
+                          const float* logits, int T, int E, int k, int score, int renorm, float c,
+                          float* dL, hipStream_t st);
+
+int moe_check_device() {
+    static int cached[64];  // 0 unknown, 1 ok, 2 unsupported
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+    if (dev < 0 || dev >= 64) return MOE_EUNSUPPORTED;
+    if (cached[dev] == 0) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) return MOE_EHIP;
+        cached[dev] = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    return cached[dev] == 1 ? MOE_OK : MOE_EUNSUPPORTED;
+}
+
+extern "C" int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+extern "C" const char* moe_strerror(int code) {
+    switch (code) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument";
+        case MOE_EWORKSPACE: return "workspace missing or too small";
+        case MOE_EHIP: return "HIP launch failed";
+        case MOE_EUNSUPPORTED: return "device is not gfx950";
+        default: return "unknown error";
+    }
+}
+
+// ---------------------------------------------------------------------- expert FFN
+extern "C" size_t moe_ffn_workspace_size(int dtype, int E, int R, int H, int I, int shared) {
+    if (E < 1 || R < 0 || H < 1 || I < 1) return 0;
+    size_t rows = shared ? (size_t)E * R : (size_t)R;
+    if (dtype == MOE_MXFP8)
+        return moe_align256(rows * I * 4) + moe_align256(rows * I) + moe_align256(rows * (I / 32)) + 256;
+    return moe_align256(rows * I * 2) + 256;
+}
+
+extern "C" int moe_expert_ffn(int dtype, const void* xp, const uint8_t* xp_scales,
+                              const int32_t* offsets, int E, int R, int H, int I, const void* w1,
+                              const uint8_t* w1_scales, const void* w2, const uint8_t* w2_scales,
+                              void* gu_save, void* h_save, void* y, void* ws, size_t ws_bytes,
+                              void* stream) {
+    MOE_REQUIRE(dtype == MOE_BF16 || dtype == MOE_MXFP8);
+    MOE_REQUIRE(E >= 1 && R >= 0 && H >= 64 && H % 64 == 0 && I >= 64 && I % 64 == 0);
+    MOE_REQUIRE(E <= 1024);
+    MOE_REQUIRE((int64_t)R * H < (1ll << 31) && (int64_t)R * 2 * I < (1ll << 31));
+    MOE_REQUIRE(xp && w1 && w2 && y);
+    if (dtype == MOE_MXFP8) {
+        MOE_REQUIRE(xp_scales && w1_scales && w2_scales && !gu_save && !h_save);
+    } else {
+        MOE_REQUIRE(!xp_scales && !w1_scales && !w2_scales);
+    }
+    size_t need = moe_ffn_workspace_size(dtype, E, R, H, I, offsets == nullptr);
+    const bool need_ws = dtype == MOE_MXFP8 || h_save == nullptr;
+    if (need_ws && (!ws || ws_bytes < need)) return MOE_EWORKSPACE;
+    if (R == 0) return MOE_OK;
+    int rc = moe_check_device();
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    size_t rows = offsets ? (size_t)R : (size_t)E * R;
+    if (dtype == MOE_BF16) {
+        bf16_t* h = h_save ? (bf16_t*)h_save : (bf16_t*)ws;
+        return moe_ffn_bf16((const bf16_t*)xp, offsets, E, R, H, I, (const bf16_t*)w1,
+                            (const bf16_t*)w2, (bf16_t*)gu_save, h, (bf16_t*)y, st);
+    }
+    char* p = (char*)ws;
+    float* hf = (float*)p;
+    p += moe_align256(rows * I * 4);
+    uint8_t* hq = (uint8_t*)p;
+    p += moe_align256(rows * I);
+    uint8_t* hs = (uint8_t*)p;
+    return moe_ffn_mx((const uint8_t*)xp, xp_scales, offsets, E, R, H, I, (const uint8_t*)w1,
+                      w1_scales, (const uint8_t*)w2, w2_scales, hf, hq, hs, (bf16_t*)y, st);
+}
+
+// ---------------------------------------------------------------------- backward
+namespace {
+struct BwdLayout {
+    size_t dy, dgu, dxp, dgus, dxs, total;
+};
+BwdLayout bwd_layout(const moe_bwd_args* a) {
+    BwdLayout L;
+    size_t o = 0;
+    L.dy = o;   o += moe_align256((size_t)a->R * a->H * 2);
+    L.dgu = o;  o += moe_align256((size_t)a->R * 2 * a->I * 2);
+    L.dxp = o;  o += moe_align256((size_t)a->R * a->H * 2);
+    L.dgus = o; o += moe_align256((size_t)a->S * a->T * 2 * a->Is * 2);
+    L.dxs = o;  o += moe_align256((size_t)a->S * a->T * a->H * 2);
+    L.total = o + 256;
+    return L;
+}
+}  // namespace
+
+extern "C" size_t moe_backward_workspace_size(const moe_bwd_args* a) {
+    if (!a || a->R < 0 || a->T < 0 || a->H < 1 || a->I < 1 || a->S < 0) return 0;
+    return bwd_layout(a).total;
+}
+
+extern "C" int moe_backward(const moe_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+    MOE_REQUIRE(a);
+    MOE_REQUIRE(a->T >= 0 && a->R >= 0 && a->E >= 1 && a->E <= 1024 && a->k >= 1 && a->k <= 64);
+    MOE_REQUIRE(a->H >= 64 && a->H % 64 == 0 && a->I >= 64 && a->I % 64 == 0);
+    MOE_REQUIRE(a->S >= 0 && (a->S == 0 || (a->Is >= 64 && a->Is % 64 == 0)));
+    MOE_REQUIRE(a->E_router >= 1 && a->E_router <= 1024);
+    MOE_REQUIRE(a->score == MOE_SCORE_SOFTMAX || a->score == MOE_SCORE_SIGMOID);
+    MOE_REQUIRE((int64_t)a->R * a->H < (1ll << 31) && (int64_t)a->T * a->H < (1ll << 31));
+    if (a->T > 0) {
+        MOE_REQUIRE(a->xp && a->gu && a->h && a->y && a->offsets && a->pos && a->idx && a->w &&
+                    a->s_sel && a->w1 && a->w2 && a->dout && a->dx && a->dw1 && a->dw2 &&
+                    a->dw_route && a->dlogits);
+        if (a->score == MOE_SCORE_SOFTMAX && !a->renorm) MOE_REQUIRE(a->logits);
+        if (a->S > 0)
+            MOE_REQUIRE(a->x && a->gus && a->hs && a->ws1 && a->ws2 && a->dws1 && a->dws2);
+    }
+    BwdLayout L = bwd_layout(a);
+    if (!ws || ws_bytes < L.total) return MOE_EWORKSPACE;
+    if (a->T == 0) return MOE_OK;
+    int rc = moe_check_device();
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    char* base = (char*)ws;
+    bf16_t* dy = (bf16_t*)(base + L.dy);
+    bf16_t* dgu = (bf16_t*)(base + L.dgu);
+    bf16_t* dxp = (bf16_t*)(base + L.dxp);
+    bf16_t* dgus = (bf16_t*)(base + L.dgus);
+    bf16_t* dxs = (bf16_t*)(base + L.dxs);
+    // combine backward: dy rows and the routing-weight gradient
+    rc = moe_launch_combine_bwd((const bf16_t*)a->dout, (const bf16_t*)a->y, a->pos, a->w, a->T,
+                                a->k, a->H, a->R, dy, a->dw_route, st);
+    if (rc) return rc;
+    // routed experts
+    if (a->R > 0) {
+        rc = moe_ffn_bwd_bf16((const bf16_t*)a->xp, a->offsets, a->E, a->R, a->H, a->I,
+                              (const bf16_t*)a->w1, (const bf16_t*)a->w2, (const bf16_t*)a->gu,
+                              (const bf16_t*)a->h, dy, dgu, dxp, (bf16_t*)a->dw1,
+                              (bf16_t*)a->dw2, st);
+        if (rc) return rc;
+    }
+    // shared experts: gradient dout with weight one, input x, every expert takes all T rows
+    if (a->S > 0) {
+        rc = moe_ffn_bwd_bf16((const bf16_t*)a->x, nullptr, a->S, a->T, a->H, a->Is,
+                              (const bf16_t*)a->ws1, (const bf16_t*)a->ws2, (const bf16_t*)a->gus,
+                              (const bf16_t*)a->hs, (const bf16_t*)a->dout, dgus, dxs,
+                              (bf16_t*)a->dws1, (bf16_t*)a->dws2, st);
+        if (rc) return rc;
+    }
+    rc = moe_launch_unpermute(dxp, a->pos, a->T, a->k, a->H, a->R, a->S ? dxs : nullptr, a->S,
+                              (bf16_t*)a->dx, st);
+    if (rc) return rc;
+    return moe_launch_router_bwd(a->idx, a->w, a->s_sel, a->dw_route, a->logits, a->T, a->E_router,
+                                 a->k, a->score, a->renorm, a->route_scale, a->dlogits, st);
+}

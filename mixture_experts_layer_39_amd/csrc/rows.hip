@@ -1,0 +1,443 @@
+// Row-wise, HBM-bound kernels: dispatch (gather, optionally MX-quantising), combine, the
+// combine backward, the un-permute reduce of dX, the router backward and MX quantisation.
+//
+// Each token row is moved with 16-byte vector accesses by consecutive lanes, so every wave
+// access is a contiguous, fully coalesced 1 KB segment; a row gather needs no LDS staging
+// because source and destination rows are both contiguous.  Every reduction runs in a fixed
+// order (slots, then shared experts; fixed butterfly trees), so results are bit-identical
+// from run to run (pulsen.vercel.app, "Cursor åpner megakernelen…", ¶3-¶4).
+#include "common.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ E4M3 / E8M0
+// Round a finite fp32 value to E4M3 ("FN": bias 7, max 448, no infinity), nearest even,
+// saturating at +-448.  Pure integer work on the fp32 bit pattern.
+__device__ __forceinline__ uint32_t e4m3_rne(float a) {
+    uint32_t u = __float_as_uint(a);
+    uint32_t s = (u >> 24) & 0x80u;
+    u &= 0x7FFFFFFFu;
+    if (u >= 0x43E00000u) return s | 0x7Eu;            // |a| >= 448
+    int ex = (int)(u >> 23) - 127;
+    uint32_t code;
+    if (ex < -6) {
+        // subnormal range: multiples of 2^-9 (scaling by 2^9 is exact)
+        code = (uint32_t)rintf(__uint_as_float(u) * 512.0f);
+    } else {
+        uint32_t c = ((uint32_t)(ex + 7) << 23) | (u & 0x7FFFFFu);
+        c = c + 0x7FFFFu + ((c >> 20) & 1u);
+        code = c >> 20;
+        if (code > 0x7Eu) code = 0x7Eu;
+    }
+    return s | code;
+}
+
+// E8M0 code of a block maximum: floor(log2 amax) - 8 + 127 (MOE_MX_FLOOR) or the smallest
+// exponent keeping amax/2^e <= 448 (MOE_MX_CEIL); clamped to [0,254]; zero block -> 0.
+__device__ __forceinline__ int mx_scale_code(float amax, int mode) {
+    if (!(amax > 0.0f)) return 0;
+    int e = ilogbf(amax) - 8;
+    if (mode == MOE_MX_CEIL && ldexpf(amax, -e) > 448.0f) e += 1;
+    int code = e + 127;
+    return code < 0 ? 0 : (code > 254 ? 254 : code);
+}
+
+// Quantise 32 fp32 values (one block) held in v[]; returns the scale code, codes packed
+// little-endian into q[8].
+__device__ __forceinline__ int mx_block(const float* v, int mode, uint32_t* q) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    int sc = mx_scale_code(amax, mode);
+    int sh = 127 - sc;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) w |= e4m3_rne(ldexpf(v[4 * i + b], sh)) << (8 * b);
+        q[i] = w;
+    }
+    return sc;
+}
+
+// ------------------------------------------------------------------ dispatch
+// One block per destination row: xp[r,:] = x[src[r]/k,:].
+__global__ __launch_bounds__(128) void dispatch_kernel(const bf16_t* __restrict__ x, int64_t n_pairs,
+                                                       int H, int k, const int32_t* __restrict__ src,
+                                                       bf16_t* __restrict__ xp) {
+    const int r = blockIdx.x;
+    const int s = src[r];
+    const bool ok = s >= 0 && s < n_pairs;
+    const bf16_t* in = x + (size_t)(ok ? s / k : 0) * H;
+    bf16_t* out = xp + (size_t)r * H;
+    const int nc = H / 8;
+    for (int c = threadIdx.x; c < nc; c += 128) {
+        u32x4 v = ok ? ld16(in + c * 8) : u32x4{0, 0, 0, 0};
+        st16_nt(out + c * 8, v);
+    }
+}
+
+// Dispatch with MX quantisation: one thread per 32-value block of the destination row.
+__global__ __launch_bounds__(256) void dispatch_mx_kernel(const bf16_t* __restrict__ x, int64_t n_pairs,
+                                                          int H, int k, const int32_t* __restrict__ src,
+                                                          bf16_t* __restrict__ xp,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+    const int r = blockIdx.y;
+    const int nb = H / 32;
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nb) return;
+    const int s = src[r];
+    const bool ok = s >= 0 && s < n_pairs;
+    const bf16_t* in = x + (size_t)(ok ? s / k : 0) * H + b * 32;
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        u32x4 q = ok ? ld16(in + c * 8) : u32x4{0, 0, 0, 0};
+        if (xp) st16(xp + (size_t)r * H + b * 32 + c * 8, q);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[c * 8 + 2 * j] = lo_bf(q[j]);
+            v[c * 8 + 2 * j + 1] = hi_bf(q[j]);
+        }
+    }
+    uint32_t q[8];
+    int sc = mx_block(v, MOE_MX_FLOOR, q);
+    uint8_t* co = codes + (size_t)r * H + b * 32;
+    st16(co, u32x4{q[0], q[1], q[2], q[3]});
+    st16(co + 16, u32x4{q[4], q[5], q[6], q[7]});
+    scales[(size_t)r * nb + b] = (uint8_t)sc;
+}
+
+// ------------------------------------------------------------------ mx_quantize
+template <bool F32>
+__global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict__ in, int64_t nblocks,
+                                                          int mode, uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+    int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nblocks) return;
+    float v[32];
+    if (F32) {
+        const float* p = (const float*)in + b * 32;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            u32x4 q = ld16(p + c * 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[c * 4 + j] = __uint_as_float(q[j]);
+        }
+    } else {
+        const bf16_t* p = (const bf16_t*)in + b * 32;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            u32x4 q = ld16(p + c * 8);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[c * 8 + 2 * j] = lo_bf(q[j]);
+                v[c * 8 + 2 * j + 1] = hi_bf(q[j]);
+            }
+        }
+    }
+    uint32_t q[8];
+    int sc = mx_block(v, mode, q);
+    st16(codes + b * 32, u32x4{q[0], q[1], q[2], q[3]});
+    st16(codes + b * 32 + 16, u32x4{q[4], q[5], q[6], q[7]});
+    scales[b] = (uint8_t)sc;
+}
+
+// ------------------------------------------------------------------ combine
+// One block per token.  Per element, fp32: acc = 0; acc += w[t,j]*y[pos[t,j]] for j = 0..k-1;
+// acc += ys[s,t] for s = 0..S-1; one rounding to bf16.
+constexpr int MAXK = 64;
+
+__global__ __launch_bounds__(128) void combine_kernel(const bf16_t* __restrict__ y,
+                                                      const int32_t* __restrict__ pos,
+                                                      const float* __restrict__ w, int T, int k,
+                                                      int H, int R, const bf16_t* __restrict__ ys,
+                                                      int S, bf16_t* __restrict__ out) {
+    const int t = blockIdx.x;
+    __shared__ int sp[MAXK];
+    __shared__ float sw[MAXK];
+    if (threadIdx.x < k) {
+        int p = pos[(size_t)t * k + threadIdx.x];
+        sp[threadIdx.x] = (p >= 0 && p < R) ? p : -1;
+        sw[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
+    }
+    __syncthreads();
+    const int nc = H / 8;
+    for (int c = threadIdx.x; c < nc; c += 128) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            int p = sp[j];
+            if (p < 0) continue;
+            float wj = sw[j];
+            u32x4 v = ld16(y + (size_t)p * H + c * 8);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = __fadd_rn(acc[2 * q], __fmul_rn(wj, lo_bf(v[q])));
+                acc[2 * q + 1] = __fadd_rn(acc[2 * q + 1], __fmul_rn(wj, hi_bf(v[q])));
+            }
+        }
+        for (int s = 0; s < S; ++s) {
+            u32x4 v = ld16(ys + ((size_t)s * T + t) * H + c * 8);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = __fadd_rn(acc[2 * q], lo_bf(v[q]));
+                acc[2 * q + 1] = __fadd_rn(acc[2 * q + 1], hi_bf(v[q]));
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[2 * q], acc[2 * q + 1]);
+        st16_nt(out + (size_t)t * H + c * 8, o);
+    }
+}
+
+// ------------------------------------------------------------------ combine backward
+// One block per token: dy[pos[t,j],:] = bf16(w[t,j] * dout[t,:]) and
+// dw[t,j] = <dout[t,:], y[pos[t,j],:]> in fp32 with a fixed reduction tree.
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restrict__ dout,
+                                                          const bf16_t* __restrict__ y,
+                                                          const int32_t* __restrict__ pos,
+                                                          const float* __restrict__ w, int k,
+                                                          int H, int R, bf16_t* __restrict__ dy,
+                                                          float* __restrict__ dw) {
+    const int t = blockIdx.x;
+    __shared__ float red[4][MAXK];
+    const int nc = H / 8;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    for (int j = 0; j < k; ++j) {
+        int p = pos[(size_t)t * k + j];
+        bool ok = p >= 0 && p < R;
+        float wj = w[(size_t)t * k + j];
+        float part = 0.0f;
+        if (ok) {
+            for (int c = threadIdx.x; c < nc; c += 256) {
+                u32x4 g = ld16(dout + (size_t)t * H + c * 8);
+                u32x4 v = ld16(y + (size_t)p * H + c * 8);
+                u32x4 o;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float g0 = lo_bf(g[q]), g1 = hi_bf(g[q]);
+                    part = __fadd_rn(part, __fmul_rn(g0, lo_bf(v[q])));
+                    part = __fadd_rn(part, __fmul_rn(g1, hi_bf(v[q])));
+                    o[q] = pack_bf2(__fmul_rn(wj, g0), __fmul_rn(wj, g1));
+                }
+                st16(dy + (size_t)p * H + c * 8, o);
+            }
+        }
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) part = __fadd_rn(part, __shfl_xor(part, d, 64));
+        if (lane == 0) red[wid][j] = part;
+    }
+    __syncthreads();
+    if (threadIdx.x < k) {
+        int j = threadIdx.x;
+        float s = __fadd_rn(__fadd_rn(red[0][j], red[1][j]), __fadd_rn(red[2][j], red[3][j]));
+        dw[(size_t)t * k + j] = s;
+    }
+}
+
+// ------------------------------------------------------------------ un-permute reduce
+// dx[t,:] = sum_j dxp[pos[t,j],:] + sum_s dxs[s,t,:], fp32 in that order, one rounding.
+__global__ __launch_bounds__(128) void unpermute_kernel(const bf16_t* __restrict__ dxp,
+                                                        const int32_t* __restrict__ pos, int T,
+                                                        int k, int H, int R,
+                                                        const bf16_t* __restrict__ dxs, int S,
+                                                        bf16_t* __restrict__ dx) {
+    const int t = blockIdx.x;
+    __shared__ int sp[MAXK];
+    if (threadIdx.x < k) {
+        int p = pos[(size_t)t * k + threadIdx.x];
+        sp[threadIdx.x] = (p >= 0 && p < R) ? p : -1;
+    }
+    __syncthreads();
+    const int nc = H / 8;
+    for (int c = threadIdx.x; c < nc; c += 128) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            int p = sp[j];
+            if (p < 0) continue;
+            u32x4 v = ld16(dxp + (size_t)p * H + c * 8);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = __fadd_rn(acc[2 * q], lo_bf(v[q]));
+                acc[2 * q + 1] = __fadd_rn(acc[2 * q + 1], hi_bf(v[q]));
+            }
+        }
+        for (int s = 0; s < S; ++s) {
+            u32x4 v = ld16(dxs + ((size_t)s * T + t) * H + c * 8);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = __fadd_rn(acc[2 * q], lo_bf(v[q]));
+                acc[2 * q + 1] = __fadd_rn(acc[2 * q + 1], hi_bf(v[q]));
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[2 * q], acc[2 * q + 1]);
+        st16(dx + (size_t)t * H + c * 8, o);
+    }
+}
+
+// ------------------------------------------------------------------ router backward
+// One wave per token; lane l owns logits e = l + 64*i.  Derivative of the weight formulas
+// (selection passes no gradient):
+//   softmax renorm:    dL[i_j] = w_j (dw_j - sum w dw)
+//   softmax full:      dL[e]   = p_e (dw at e - sum w dw)
+//   sigmoid renorm:    dL[i_j] = s_j(1-s_j) (c/S)(dw_j - sum (w/c) dw),  S = sum s
+//   sigmoid plain:     dL[i_j] = c dw_j s_j (1-s_j)
+__global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restrict__ idx,
+                                                         const float* __restrict__ w,
+                                                         const float* __restrict__ s_sel,
+                                                         const float* __restrict__ dw,
+                                                         const float* __restrict__ logits, int T,
+                                                         int E, int k, int score, int renorm,
+                                                         float c, float* __restrict__ dL) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const bool act = lane < k;
+    const size_t o = (size_t)t * k + lane;
+    int id = act ? idx[o] : -1;
+    float wj = act ? w[o] : 0.0f, gj = act ? dw[o] : 0.0f, sj = act ? s_sel[o] : 0.0f;
+    float wg = wj * gj;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) wg = __fadd_rn(wg, __shfl_xor(wg, d, 64));
+    float ssum = sj;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) ssum = __fadd_rn(ssum, __shfl_xor(ssum, d, 64));
+    float contrib = 0.0f;  // this slot's gradient at its expert
+    if (score == MOE_SCORE_SOFTMAX) {
+        contrib = renorm ? wj * (gj - wg) : wj * gj;
+    } else {
+        float ds = renorm ? (c / ssum) * (gj - wg / c) : c * gj;
+        contrib = ds * sj * (1.0f - sj);
+    }
+    float m = 0.0f, se = 1.0f;
+    const bool full = score == MOE_SCORE_SOFTMAX && !renorm;
+    if (full) {
+        const float* L = logits + (size_t)t * E;
+        m = -INFINITY;
+        for (int e = lane; e < E; e += 64) m = fmaxf(m, L[e]);
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+        se = 0.0f;
+        for (int e = lane; e < E; e += 64) se += expf(L[e] - m);
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) se = __fadd_rn(se, __shfl_xor(se, d, 64));
+    }
+    for (int e0 = 0; e0 < E; e0 += 64) {
+        int e = e0 + lane;
+        float v = 0.0f;
+        if (full && e < E) v = -(expf(logits[(size_t)t * E + e] - m) / se) * wg;
+        for (int j = 0; j < k; ++j) {
+            int idj = __shfl(id, j, 64);
+            float cj = __shfl(contrib, j, 64);
+            if (idj == e) v += cj;
+        }
+        if (e < E) dL[(size_t)t * E + e] = v;
+    }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+// ------------------------------------------------------------------ C ABI
+extern "C" int moe_dispatch(const void* x, int T, int H, int k, const int32_t* src, int R,
+                            void* xp, uint8_t* xp_codes, uint8_t* xp_scales, void* stream) {
+    MOE_REQUIRE(T >= 0 && H >= 8 && H % 8 == 0 && k >= 1 && R >= 0);
+    MOE_REQUIRE((xp_codes == nullptr) == (xp_scales == nullptr));
+    MOE_REQUIRE(xp || xp_codes);
+    if (xp_codes) MOE_REQUIRE(H % 32 == 0);
+    MOE_REQUIRE(R == 0 || (x && src));
+    if (R == 0) return MOE_OK;
+    int rc = moe_check_device();
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    int64_t n_pairs = (int64_t)T * k;
+    if (xp_codes) {
+        int nb = H / 32;
+        dim3 grid((nb + 255) / 256, R);
+        dispatch_mx_kernel<<<grid, 256, 0, st>>>((const bf16_t*)x, n_pairs, H, k, src,
+                                                  (bf16_t*)xp, xp_codes, xp_scales);
+    } else {
+        dispatch_kernel<<<R, 128, 0, st>>>((const bf16_t*)x, n_pairs, H, k, src, (bf16_t*)xp);
+    }
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+extern "C" int moe_combine(const void* y, const int32_t* pos, const float* w, int T, int k, int H,
+                           int R, const void* ys, int S, void* out, void* stream) {
+    MOE_REQUIRE(T >= 0 && k >= 1 && k <= MAXK && H >= 8 && H % 8 == 0 && R >= 0 && S >= 0);
+    MOE_REQUIRE((S == 0) == (ys == nullptr));
+    MOE_REQUIRE(T == 0 || (y && pos && w && out));
+    if (T == 0) return MOE_OK;
+    int rc = moe_check_device();
+    if (rc) return rc;
+    combine_kernel<<<T, 128, 0, (hipStream_t)stream>>>((const bf16_t*)y, pos, w, T, k, H, R,
+                                                       (const bf16_t*)ys, S, (bf16_t*)out);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+extern "C" int mx_quantize(const void* in, int in_dtype, int rows, int K, uint8_t* codes,
+                           uint8_t* scales, int scale_mode, void* stream) {
+    MOE_REQUIRE(rows >= 0 && K >= 32 && K % 32 == 0);
+    MOE_REQUIRE(in_dtype == MOE_BF16 || in_dtype == MOE_F32);
+    MOE_REQUIRE(scale_mode == MOE_MX_FLOOR || scale_mode == MOE_MX_CEIL);
+    MOE_REQUIRE(rows == 0 || (in && codes && scales));
+    if (rows == 0) return MOE_OK;
+    int rc = moe_check_device();
+    if (rc) return rc;
+    int64_t nb = (int64_t)rows * (K / 32);
+    dim3 grid((unsigned)((nb + 255) / 256));
+    if (in_dtype == MOE_F32)
+        mx_quantize_kernel<true><<<grid, 256, 0, (hipStream_t)stream>>>(in, nb, scale_mode, codes, scales);
+    else
+        mx_quantize_kernel<false><<<grid, 256, 0, (hipStream_t)stream>>>(in, nb, scale_mode, codes, scales);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+// Internal launchers used by the backward orchestration.
+int moe_launch_combine_bwd(const bf16_t* dout, const bf16_t* y, const int32_t* pos, const float* w,
+                           int T, int k, int H, int R, bf16_t* dy, float* dw, hipStream_t st) {
+    if (T == 0) return MOE_OK;
+    combine_bwd_kernel<<<T, 256, 0, st>>>(dout, y, pos, w, k, H, R, dy, dw);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+int moe_launch_unpermute(const bf16_t* dxp, const int32_t* pos, int T, int k, int H, int R,
+                         const bf16_t* dxs, int S, bf16_t* dx, hipStream_t st) {
+    if (T == 0) return MOE_OK;
+    unpermute_kernel<<<T, 128, 0, st>>>(dxp, pos, T, k, H, R, dxs, S, dx);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+int moe_launch_router_bwd(const int32_t* idx, const float* w, const float* s_sel, const float* dw,
+                          const float* logits, int T, int E, int k, int score, int renorm, float c,
+                          float* dL, hipStream_t st) {
+    if (T == 0) return MOE_OK;
+    router_bwd_kernel<<<(T + 3) / 4, 256, 0, st>>>(idx, w, s_sel, dw, logits, T, E, k, score,
+                                                   renorm, c, dL);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+int moe_launch_mx_quantize_f32(const float* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
+                               hipStream_t st) {
+    int64_t nb = rows * (K / 32);
+    if (nb == 0) return MOE_OK;
+    mx_quantize_kernel<true><<<(unsigned)((nb + 255) / 256), 256, 0, st>>>(in, nb, MOE_MX_FLOOR,
+                                                                         codes, scales);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}

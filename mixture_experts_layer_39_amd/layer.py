@@ -1,0 +1,196 @@
+"""A whole MoE layer step as a sequence of the library's C-ABI calls.
+
+``MoELayer`` owns the device buffers of one layer configuration (allocated once, with torch)
+and runs forward (route -> dispatch -> expert FFN -> combine) and backward through
+libmoe.so.  It holds no arithmetic: every value is produced by the HIP kernels.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+from . import (BF16, MXFP8, F32, SCORE_SIGMOID, backward_workspace_size, bwd_args,
+               ffn_workspace_size, moe_backward, moe_combine, moe_dispatch, moe_expert_ffn,
+               moe_route, mx_quantize, route_workspace_size)
+
+
+@dataclasses.dataclass
+class LayerCfg:
+    T: int
+    H: int
+    E: int
+    k: int
+    I: int
+    S: int = 0
+    Is: int = 0
+    score: int = 0
+    renorm: bool = True
+    route_scale: float = 1.0
+    n_groups: int = 1
+    topk_groups: int = 1
+    E_router: int = 0          # width of the router (0: E)
+    local_share: bool = False  # expert of each routed pair comes from idx_local
+    router_proj: bool = False
+    mx: bool = False
+
+    @property
+    def ER(self):
+        return self.E_router or self.E
+
+    @staticmethod
+    def from_workload(wl) -> "LayerCfg":
+        return LayerCfg(T=wl.T, H=wl.H, E=wl.E, k=wl.k,
+                        I=wl.I, S=wl.S, Is=wl.Is, score=wl.score, renorm=wl.renorm,
+                        route_scale=wl.route_scale, n_groups=wl.n_groups,
+                        topk_groups=wl.topk_groups, E_router=wl.E_router,
+                        local_share=wl.local_share, router_proj=wl.router_proj, mx=wl.mx)
+
+
+def _e(shape, dtype, dev):
+    return torch.empty(shape, dtype=dtype, device=dev)
+
+
+class MoELayer:
+    def __init__(self, cfg: LayerCfg, inp: dict, device="cuda", backward: bool = True):
+        c = self.cfg = cfg
+        d = self.dev = torch.device(device)
+        self.inp = inp
+        T, H, E, I = c.T, c.H, c.E, c.I
+        kr = inp["idx_local"].shape[1] if c.local_share else c.k  # routed slots per token
+        if kr != c.k:
+            raise ValueError("local share must have k routed rows per token")
+        self.k_router = c.k
+        self.kr = kr
+        R = self.R = T * kr
+        ER = c.ER
+        i32, f32, bf = torch.int32, torch.float32, torch.bfloat16
+        # routing
+        self.logits = inp["logits"] if "logits" in inp else _e((T, ER), f32, d)
+        self.idx = _e((T, self.k_router), i32, d)
+        self.w = _e((T, self.k_router), f32, d)
+        self.s_sel = _e((T, self.k_router), f32, d)
+        self.counts = _e((E,), i32, d)
+        self.offsets = _e((E + 1,), i32, d)
+        self.pos = _e((T, kr), i32, d)
+        self.src = _e((R,), i32, d)
+        self.route_ws = _e((max(route_workspace_size(T, kr, E),
+                                route_workspace_size(T, self.k_router, ER), 256),),
+                           torch.uint8, d)
+        if c.local_share:   # router outputs over E_router experts, kept apart
+            self.g_counts = _e((ER,), i32, d)
+            self.g_offsets = _e((ER + 1,), i32, d)
+            self.g_pos = _e((T, self.k_router), i32, d)
+            self.g_src = _e((T * self.k_router,), i32, d)
+        # expert FFN
+        if c.mx:
+            self.xq = _e((R, H), torch.uint8, d)
+            self.xs = _e((R, H // 32), torch.uint8, d)
+            self.w1q = _e(tuple(inp["w1"].shape), torch.uint8, d)
+            self.w1s = _e(tuple(inp["w1"].shape[:-1]) + (H // 32,), torch.uint8, d)
+            self.w2q = _e(tuple(inp["w2"].shape), torch.uint8, d)
+            self.w2s = _e(tuple(inp["w2"].shape[:-1]) + (I // 32,), torch.uint8, d)
+            self.quantize_weights()
+            self.xp = None
+            self.gu = self.h = None
+        else:
+            self.xp = _e((R, H), bf, d)
+            self.gu = _e((R, 2 * I), bf, d) if backward else None
+            self.h = _e((R, I), bf, d)
+        self.y = _e((R, H), bf, d)
+        self.ffn_ws = _e((max(ffn_workspace_size(MXFP8 if c.mx else BF16, E, R, H, I), 256),),
+                         torch.uint8, d)
+        if c.S:
+            self.ys = _e((c.S, T, H), bf, d)
+            self.gus = _e((c.S, T, 2 * c.Is), bf, d) if backward else None
+            self.hs = _e((c.S, T, c.Is), bf, d)
+            self.sh_ws = _e((max(ffn_workspace_size(BF16, c.S, T, H, c.Is, True), 256),),
+                            torch.uint8, d)
+        else:
+            self.ys = None
+        self.out = _e((T, H), bf, d)
+        self.has_bwd = backward
+        if backward:
+            self.dx = _e((T, H), bf, d)
+            self.dw1 = torch.empty_like(inp["w1"])
+            self.dw2 = torch.empty_like(inp["w2"])
+            self.dws1 = torch.empty_like(inp["ws1"]) if c.S else None
+            self.dws2 = torch.empty_like(inp["ws2"]) if c.S else None
+            self.dw_route = _e((T, kr), f32, d)
+            self.dlogits = _e((T, ER), f32, d)
+            self.bargs = self._bwd_args()
+            self.bwd_ws = _e((max(backward_workspace_size(self.bargs), 256),), torch.uint8, d)
+
+    # ------------------------------------------------------------------ setup
+    def quantize_weights(self):
+        c, inp = self.cfg, self.inp
+        E, H, I = c.E, c.H, c.I
+        mx_quantize(inp["w1"], BF16, E * 2 * I, H, self.w1q, self.w1s)
+        mx_quantize(inp["w2"], BF16, E * H, I, self.w2q, self.w2s)
+
+    def _bwd_args(self):
+        c, inp = self.cfg, self.inp
+        return bwd_args(T=c.T, H=c.H, E=c.E, k=self.kr, I=c.I, R=self.R, S=c.S, Is=c.Is,
+                        E_router=c.ER, score=c.score, renorm=c.renorm,
+                        route_scale=c.route_scale, x=inp["x"], xp=self.xp, gu=self.gu,
+                        h=self.h, y=self.y, offsets=self.offsets, pos=self.pos, idx=self.idx,
+                        w=self.w, s_sel=self.s_sel, logits=self.logits, w1=inp["w1"],
+                        w2=inp["w2"], gus=self.gus if c.S else None,
+                        hs=self.hs if c.S else None, ws1=inp.get("ws1"), ws2=inp.get("ws2"),
+                        dout=inp.get("dout"), dx=self.dx, dw1=self.dw1, dw2=self.dw2,
+                        dws1=self.dws1, dws2=self.dws2, dw_route=self.dw_route,
+                        dlogits=self.dlogits)
+
+    # ------------------------------------------------------------------ steps
+    def route(self):
+        c, inp = self.cfg, self.inp
+        common = dict(score=c.score, n_groups=c.n_groups, topk_groups=c.topk_groups,
+                      renorm=c.renorm, route_scale=c.route_scale, ws=self.route_ws)
+        if c.local_share:
+            moe_route(self.logits, c.T, c.ER, self.k_router, idx=self.idx, w=self.w,
+                      s_sel=self.s_sel, counts=self.g_counts, offsets=self.g_offsets,
+                      pos=self.g_pos, src=self.g_src, **common)
+            moe_route(None, c.T, c.E, self.kr, idx_in=inp["idx_local"], counts=self.counts,
+                      offsets=self.offsets, pos=self.pos, src=self.src, **common)
+        else:
+            moe_route(self.logits, c.T, c.E, c.k, x=inp["x"] if c.router_proj else None,
+                      w_router=inp.get("w_router"), H=c.H, idx=self.idx, w=self.w,
+                      s_sel=self.s_sel, counts=self.counts, offsets=self.offsets, pos=self.pos,
+                      src=self.src, **common)
+
+    def dispatch(self):
+        c = self.cfg
+        if c.mx:
+            moe_dispatch(self.inp["x"], c.T, c.H, self.kr, self.src, self.R, None, self.xq,
+                         self.xs)
+        else:
+            moe_dispatch(self.inp["x"], c.T, c.H, self.kr, self.src, self.R, self.xp)
+
+    def experts(self):
+        c, inp = self.cfg, self.inp
+        if c.mx:
+            moe_expert_ffn(MXFP8, self.xq, self.offsets, c.E, self.R, c.H, c.I, self.w1q,
+                           self.w2q, self.y, xp_scales=self.xs, w1_scales=self.w1s,
+                           w2_scales=self.w2s, ws=self.ffn_ws)
+        else:
+            moe_expert_ffn(BF16, self.xp, self.offsets, c.E, self.R, c.H, c.I, inp["w1"],
+                           inp["w2"], self.y, gu_save=self.gu, h_save=self.h, ws=self.ffn_ws)
+        if c.S:
+            moe_expert_ffn(BF16, inp["x"], None, c.S, c.T, c.H, c.Is, inp["ws1"], inp["ws2"],
+                           self.ys, gu_save=self.gus, h_save=self.hs, ws=self.sh_ws)
+
+    def combine(self):
+        c = self.cfg
+        moe_combine(self.y, self.pos, self.w, c.T, self.kr, c.H, self.R, self.out, self.ys,
+                    c.S)
+
+    def forward(self):
+        self.route()
+        self.dispatch()
+        self.experts()
+        self.combine()
+        return self.out
+
+    def backward(self):
+        moe_backward(self.bargs, self.bwd_ws)
+        return self.dx

@@ -1,0 +1,132 @@
+"""The C ABI on the host: every declared symbol is exported and argument validation returns
+its error codes before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_39_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\([^;{]*\)\s*;", src, re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_backward",
+            "mx_quantize"} <= set(names)
+    lib = moe.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror():
+    assert moe.abi_version() == 1
+    assert moe.strerror(0) == "ok"
+    assert "workspace" in moe.strerror(-2)
+    assert moe.strerror(12345) == "unknown error"
+
+
+L = None
+
+
+def lib():
+    return moe.lib()
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def route(**kw):
+    a = dict(logits=FAKE, x=None, wr=None, T=16, H=64, E=8, k=2, cfg=moe.RouteCfg(0, 1, 1, 1, 1.0, None),
+             idx_in=None, idx=FAKE, w=FAKE, s=FAKE, counts=FAKE, offsets=FAKE, pos=FAKE, src=FAKE,
+             ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return lib().moe_route(a["logits"], a["x"], a["wr"], a["T"], a["H"], a["E"], a["k"],
+                           ctypes.byref(a["cfg"]), a["idx_in"], a["idx"], a["w"], a["s"],
+                           a["counts"], a["offsets"], a["pos"], a["src"], a["ws"], a["wsb"], None)
+
+
+def test_route_validation():
+    assert route(k=9) == moe.MOE_EINVAL                  # k > E
+    assert route(k=0) == moe.MOE_EINVAL
+    assert route(E=2000) == moe.MOE_EINVAL               # E > 1024
+    assert route(counts=None) == moe.MOE_EINVAL
+    assert route(x=FAKE) == moe.MOE_EINVAL               # x without w_router
+    assert route(cfg=moe.RouteCfg(7, 1, 1, 1, 1.0, None)) == moe.MOE_EINVAL
+    assert route(cfg=moe.RouteCfg(1, 3, 1, 1, 1.0, None)) == moe.MOE_EINVAL   # E % groups
+    assert route(cfg=moe.RouteCfg(1, 4, 5, 1, 1.0, None)) == moe.MOE_EINVAL   # topk_groups > groups
+    assert route(k=8, cfg=moe.RouteCfg(1, 4, 2, 1, 1.0, None)) == moe.MOE_EINVAL  # k > kept experts
+    assert route(x=FAKE, wr=FAKE, H=60) == moe.MOE_EINVAL  # H % 8
+    assert route(ws=None) == moe.MOE_EWORKSPACE
+    assert route(wsb=16) == moe.MOE_EWORKSPACE
+    assert moe.route_workspace_size(2048, 8, 256) >= 64 * 256 * 4
+
+
+def test_dispatch_combine_mx_validation():
+    L_ = lib()
+    assert L_.moe_dispatch(FAKE, 16, 60, 2, FAKE, 32, FAKE, None, None, None) == moe.MOE_EINVAL
+    assert L_.moe_dispatch(FAKE, 16, 64, 2, FAKE, 32, None, None, None, None) == moe.MOE_EINVAL
+    assert L_.moe_dispatch(FAKE, 16, 64, 2, FAKE, 32, None, FAKE, None, None) == moe.MOE_EINVAL
+    assert L_.moe_dispatch(FAKE, 16, 72, 2, FAKE, 32, None, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert L_.moe_dispatch(FAKE, 16, 64, 2, FAKE, 0, FAKE, None, None, None) == moe.MOE_OK  # empty
+    assert L_.moe_combine(FAKE, FAKE, FAKE, 16, 2, 64, 32, None, 1, FAKE, None) == moe.MOE_EINVAL
+    assert L_.moe_combine(FAKE, FAKE, FAKE, 16, 65, 64, 32, None, 0, FAKE, None) == moe.MOE_EINVAL
+    assert L_.moe_combine(FAKE, FAKE, FAKE, 0, 2, 64, 0, None, 0, FAKE, None) == moe.MOE_OK
+    assert L_.mx_quantize(FAKE, moe.BF16, 4, 48, FAKE, FAKE, 0, None) == moe.MOE_EINVAL
+    assert L_.mx_quantize(FAKE, 9, 4, 64, FAKE, FAKE, 0, None) == moe.MOE_EINVAL
+    assert L_.mx_quantize(FAKE, moe.BF16, 4, 64, FAKE, FAKE, 5, None) == moe.MOE_EINVAL
+
+
+def ffn(**kw):
+    a = dict(dtype=moe.BF16, xp=FAKE, xs=None, off=FAKE, E=4, R=64, H=128, I=128, w1=FAKE,
+             w1s=None, w2=FAKE, w2s=None, gu=None, h=FAKE, y=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib().moe_expert_ffn(a["dtype"], a["xp"], a["xs"], a["off"], a["E"], a["R"], a["H"],
+                                a["I"], a["w1"], a["w1s"], a["w2"], a["w2s"], a["gu"], a["h"],
+                                a["y"], a["ws"], a["wsb"], None)
+
+
+def test_ffn_validation():
+    assert ffn(H=96) == moe.MOE_EINVAL
+    assert ffn(I=100) == moe.MOE_EINVAL
+    assert ffn(E=0) == moe.MOE_EINVAL
+    assert ffn(y=None) == moe.MOE_EINVAL
+    assert ffn(dtype=7) == moe.MOE_EINVAL
+    assert ffn(xs=FAKE) == moe.MOE_EINVAL                                   # scales in BF16
+    assert ffn(dtype=moe.MXFP8) == moe.MOE_EINVAL                           # no scales
+    assert ffn(dtype=moe.MXFP8, xs=FAKE, w1s=FAKE, w2s=FAKE, gu=FAKE) == moe.MOE_EINVAL
+    assert ffn(h=None, ws=None) == moe.MOE_EWORKSPACE
+    assert ffn(h=None, wsb=100) == moe.MOE_EWORKSPACE
+    assert ffn(R=0) == moe.MOE_OK
+    assert moe.ffn_workspace_size(moe.BF16, 4, 64, 128, 128) >= 64 * 128 * 2
+    assert moe.ffn_workspace_size(moe.MXFP8, 4, 64, 128, 128) >= 64 * 128 * 5
+
+
+def test_backward_validation():
+    a = moe.bwd_args(T=16, H=128, E=4, k=2, I=128, R=32, S=0, Is=0, E_router=4, score=0,
+                     renorm=1)
+    assert lib().moe_backward(None, FAKE, 1 << 30, None) == moe.MOE_EINVAL
+    assert lib().moe_backward(ctypes.byref(a), FAKE, 1 << 30, None) == moe.MOE_EINVAL  # nulls
+    need = moe.backward_workspace_size(a)
+    assert need >= 32 * 128 * 2 * 3
+    b = moe.bwd_args(T=0, H=128, E=4, k=2, I=128, R=0, S=0, Is=0, E_router=4, score=0, renorm=1)
+    assert lib().moe_backward(ctypes.byref(b), FAKE, 0, None) == moe.MOE_EWORKSPACE
+    assert lib().moe_backward(ctypes.byref(b), FAKE, 1 << 20, None) == moe.MOE_OK
+    c = moe.bwd_args(T=16, H=100, E=4, k=2, I=128, R=32, E_router=4)
+    assert lib().moe_backward(ctypes.byref(c), FAKE, 1 << 30, None) == moe.MOE_EINVAL
+
+
+def test_binding_raises_on_error_code():
+    with pytest.raises(moe.MoeError):
+        moe._check("moe_route", moe.MOE_EINVAL)
