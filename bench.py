@@ -1,0 +1,275 @@
+"""Throughput of the deterministic MoE layer on one MI355X, with its roofline and a CPU baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole layer over one batch: routing (router top-k and the
+expert-contiguous permutation), dispatch, the grouped-GEMM expert FFN, the weighted combine and,
+for workloads with a backward, the BF16 backward of all of it.  Inputs are seeded synthetic
+tensors already resident in HBM; every step runs through the HIP kernels of libmoe.so.
+
+The default workload is the DeepSeek-V3-shaped one-GPU share at expert-parallel degree 64
+(2048 source tokens per GPU, 4 local experts receiving 16384 routed rows, hidden 7168,
+SwiGLU intermediate 2048), the per-GPU shape the pages measure their layer at.
+
+Printed: ONE JSON line.  `value` is forward+backward tokens/s (source tokens per second of
+wall time, K steps bracketed by device synchronisation).  `fwd_tokens_per_s` times forward-only
+steps the same way.  `roofline` is for the kernel that takes the largest share of a step:
+its algorithmic flops (or bytes) per launch over its average launch duration, measured with
+HIP events the library records around each of its launches on the launch stream.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s fwd & fwd+bwd (1 GPU); grouped-GEMM MFMA % of peak"
+
+# MI355X published peaks (dense)
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_MXFP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+
+GEMM_ROLES = {  # role -> (flops per routed row in units of H*I, MX)
+    "gemm1_swiglu": (4, False), "gemm2_down": (2, False),
+    "dgrad_down_dswiglu": (2, False), "dgrad_gate_up": (4, False),
+    "wgrad_down": (2, False), "wgrad_gate_up": (4, False),
+    "mx_gemm1_swiglu": (4, True), "mx_gemm2_down": (2, True),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_ep64")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=16,
+                    help="source tokens of the CPU-oracle sample")
+    ap.add_argument("--breakdown", action="store_true",
+                    help="also print per-role times to stderr")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- algorithmic work
+def role_work(wl, role: str, shared: bool) -> tuple[str, float]:
+    """Algorithmic work of one launch of `role`: ("flop", n) or ("byte", n)."""
+    H, I, R, T, k = wl.H, wl.I, wl.R, wl.T, (wl.R // wl.T if wl.T else wl.k)
+    if shared:
+        I, R = wl.Is, wl.T
+    if role in GEMM_ROLES:
+        return "flop", float(GEMM_ROLES[role][0]) * H * I * R
+    bf = 2
+    if role == "dispatch":          # unique source rows read once + every routed row written
+        return "byte", float(T * H * bf + R * H * bf + R * 4)
+    if role == "dispatch_mx":
+        return "byte", float(T * H * bf + R * H + R * H // 32 + R * 4)
+    if role == "combine":
+        return "byte", float(R * H * bf + wl.S * T * H * bf + T * H * bf + T * k * 8)
+    if role == "combine_bwd":
+        return "byte", float(T * H * bf + 2 * R * H * bf + T * k * 12)
+    if role == "unpermute":
+        return "byte", float(R * H * bf + wl.S * T * H * bf + T * H * bf + T * k * 4)
+    if role == "topk":
+        return "byte", float(T * wl.ER * 4 + T * wl.k * 12)
+    if role == "router_bwd":
+        return "byte", float(T * wl.ER * 4 + T * wl.k * 16)
+    if role == "mx_quantize_h":
+        return "byte", float(R * I * 4 + R * I + R * I // 32)
+    return "byte", 0.0
+
+
+def roofline_of(wl, role: str, per_launch_ms: float, traffic) -> dict:
+    kind, work = role_work(wl, role, shared=False)
+    if kind == "flop":
+        peak = PEAK_MXFP8_TFLOPS if GEMM_ROLES[role][1] else PEAK_BF16_TFLOPS
+        ach = work / (per_launch_ms * 1e-3) / 1e12
+        return {"kernel": role, "bound": "mfma", "achieved": round(ach, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
+                "work_per_launch": work, "avg_launch_ms": round(per_launch_ms, 4)}
+    ach = work / (per_launch_ms * 1e-3) / 1e9
+    return {"kernel": role, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "work_per_launch": work, "avg_launch_ms": round(per_launch_ms, 4)}
+
+
+def kernel_source_digest() -> str:
+    """Digest of the HIP sources; stored HBM-traffic counts are valid only for this digest."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_layer_39_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, role: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
+    summary is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    ent = d.get("workloads", {}).get(workload, {}).get(role)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl, inp, n_tokens: int) -> dict:
+    """The CPU oracle (fp64 plain loops) on the first n_tokens source tokens of the workload,
+    forward (+ backward when the workload has one); tokens/s of that sample."""
+    import oracle as orc
+    import workloads as wk
+    n = min(n_tokens, wl.T)
+    p = dict(x=wk.bf16_bits(inp["x"][:n]), k=wl.k, score=wl.score, renorm=wl.renorm,
+             route_scale=wl.route_scale, n_groups=wl.n_groups, topk_groups=wl.topk_groups,
+             mx=wl.mx, w1=wk.bf16_bits(inp["w1"]), w2=wk.bf16_bits(inp["w2"]))
+    if "w_router" in inp:
+        p["w_router"] = wk.bf16_bits(inp["w_router"])
+    else:
+        p["logits"] = inp["logits"][:n].cpu().numpy()
+    if "idx_local" in inp:
+        p["idx_local"] = inp["idx_local"][:n].cpu().numpy()
+    if wl.S:
+        p["ws1"], p["ws2"] = wk.bf16_bits(inp["ws1"]), wk.bf16_bits(inp["ws2"])
+    dout = wk.bf16_bits(inp["dout"][:n]) if wl.backward else None
+    orc.lib()
+    t0 = time.perf_counter()
+    r = orc.layer_forward(p)
+    if wl.backward:
+        orc.layer_backward(p, r, dout)
+    dt = time.perf_counter() - t0
+    rows = int(p["idx_local"].size) if "idx_local" in p else n * wl.k
+    what = "forward+backward" if wl.backward else "forward"
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": orc.threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"first {n} of {wl.T} source tokens ({rows} routed rows) with the full "
+                      f"expert weights, oracle {what} in fp64"}
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    a = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the layer on one GPU; runs on more than one "
+              "GPU are not part of this build (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as wk
+    import mixture_experts_layer_39_amd as moe
+    from mixture_experts_layer_39_amd.layer import LayerCfg, MoELayer
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    moe.lib()  # fails loudly when the HIP library is missing
+    wl = wk.WORKLOADS[a.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inp = wk.make_inputs(wl, device=dev)
+    layer = MoELayer(LayerCfg.from_workload(wl), inp, dev, backward=wl.backward)
+
+    def step():
+        layer.forward()
+        if wl.backward:
+            layer.backward()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed: K whole steps, with per-launch events recorded by the library
+    moe.trace_begin(max(64, 64 * a.steps))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    recs = moe.trace_end()
+    elapsed = t1 - t0
+    ms_step = elapsed * 1e3 / a.steps
+
+    # forward-only steps, untraced
+    for _ in range(2):
+        layer.forward()
+    torch.cuda.synchronize()
+    f0 = time.perf_counter()
+    for _ in range(a.steps):
+        layer.forward()
+    torch.cuda.synchronize()
+    fwd_ms = (time.perf_counter() - f0) * 1e3 / a.steps
+
+    # per-role statistics over the timed region
+    roles: dict[str, list[float]] = {}
+    for name, ms in recs:
+        roles.setdefault(name, []).append(ms)
+    per_step = {r: sum(v) / a.steps for r, v in roles.items()}
+    dominant = max(per_step, key=per_step.get)
+    avg = sum(roles[dominant]) / len(roles[dominant])
+    roof = roofline_of(wl, dominant, avg, measured_traffic(a.workload, dominant))
+
+    flops_fwd = wl.fwd_flops()
+    flops_step = flops_fwd * (3.0 if wl.backward else 1.0)
+    breakdown = {}
+    for r in sorted(per_step, key=per_step.get, reverse=True):
+        n = len(roles[r]) / a.steps
+        ent = {"launches_per_step": n, "ms_per_step": round(per_step[r], 4),
+               "share": round(per_step[r] / ms_step, 4)}
+        if r in GEMM_ROLES and n == 1:
+            kind, work = role_work(wl, r, False)
+            ent["tflops"] = round(work / (per_step[r] * 1e-3) / 1e12, 1)
+        elif r not in GEMM_ROLES and n == 1:
+            kind, work = role_work(wl, r, False)
+            if work:
+                ent["gbs"] = round(work / (per_step[r] * 1e-3) / 1e9, 1)
+        breakdown[r] = ent
+    if a.breakdown:
+        for r, e in breakdown.items():
+            print(f"  {r:22s} {e}", file=sys.stderr)
+
+    cfg = {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "I": wl.I,
+           "routed_rows": wl.R, "S": wl.S, "Is": wl.Is, "E_router": wl.ER,
+           "score": "sigmoid" if wl.score == wk.SIGMOID else "softmax",
+           "n_groups": wl.n_groups, "topk_groups": wl.topk_groups,
+           "precision": "mxfp8" if wl.mx else "bf16", "backward": wl.backward,
+           "parallelism": "none (one GPU's share)"}
+    out = {
+        "metric": METRIC,
+        "value": round(wl.T * a.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp8" if wl.mx else "bf16",
+        "data": "synthetic (seeded; random-init weights of the layer's shape)",
+        "config": cfg,
+        "fwd_tokens_per_s": round(wl.T / (fwd_ms * 1e-3), 1),
+        "fwd_ms_per_step": round(fwd_ms, 4),
+        "step_tflops": round(flops_step / (ms_step * 1e-3) / 1e12, 1),
+        "fwd_tflops": round(flops_fwd / (fwd_ms * 1e-3) / 1e12, 1),
+        "roofline": roof,
+        "breakdown": breakdown,
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, a.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

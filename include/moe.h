@@ -21,7 +21,7 @@
  *    negative code and enqueues nothing.  Device-resident indices (src, pos, offsets) are
  *    clamped by the kernels, so that corrupt indices cannot access memory out of bounds.
  *  - Calls on distinct streams with distinct workspaces may run concurrently; the library
- *    holds no mutable global state.
+ *    holds no mutable global state apart from the optional, per-thread launch trace below.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -192,6 +192,22 @@ int moe_backward(const moe_bwd_args *a, void *ws, size_t ws_bytes, void *stream)
  * K % 32 == 0. */
 int mx_quantize(const void *in, int in_dtype, int rows, int K, uint8_t *codes, uint8_t *scales,
                 int scale_mode, void *stream);
+
+/* ------------------------------------------------------------------ launch tracing
+ * Optional timing of the library's own kernels, for profiling (the layer needs none of it).
+ * moe_trace_begin(cap) arms tracing on the calling host thread: every kernel the library
+ * then launches from this thread is bracketed by two hipEvent records on its stream, for the
+ * first cap launches (later launches run untraced).  The events are created on the first
+ * call (hipEventCreate; no device memory is allocated) and reused afterwards.  Returns
+ * MOE_EINVAL unless 1 <= cap <= 2^20, MOE_EHIP if an event cannot be created.
+ * moe_trace_end() disarms tracing and returns the number of launches recorded since
+ * moe_trace_begin.  moe_trace_get(i, &name, &ms), for 0 <= i < that number, waits for
+ * launch i to finish and returns its role name (a static string such as "gemm1_swiglu" or
+ * "dispatch") and its duration in milliseconds; MOE_EINVAL for i out of range, MOE_EHIP on
+ * an event error.  Records stay readable until the next moe_trace_begin on the thread. */
+int moe_trace_begin(int cap);
+int moe_trace_end(void);
+int moe_trace_get(int i, const char **name, float *ms);
 
 #ifdef __cplusplus
 }

@@ -74,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.moe_backward_workspace_size.argtypes = [ctypes.POINTER(BwdArgs)]
         L.moe_backward.argtypes = [ctypes.POINTER(BwdArgs), _vp, _sz, _vp]
         L.mx_quantize.argtypes = [_vp, _i, _i, _i, _vp, _vp, _i, _vp]
+        L.moe_trace_begin.argtypes = [_i]
+        L.moe_trace_end.argtypes = []
+        L.moe_trace_get.argtypes = [_i, ctypes.POINTER(ctypes.c_char_p),
+                                    ctypes.POINTER(ctypes.c_float)]
         _lib = L
     return _lib
 
@@ -183,3 +187,22 @@ def mx_quantize(inp, in_dtype, rows, K, codes, scales, scale_mode=MX_FLOOR, stre
     rc = lib().mx_quantize(_p(inp), in_dtype, rows, K, _p(codes), _p(scales), scale_mode,
                            _stream(stream))
     _check("mx_quantize", rc)
+
+
+# ----------------------------------------------------------------------------- tracing
+def trace_begin(cap: int = 4096):
+    """Arm per-launch event tracing of the library's kernels on this thread."""
+    _check("moe_trace_begin", lib().moe_trace_begin(cap))
+
+
+def trace_end() -> list[tuple[str, float]]:
+    """Disarm tracing; returns (role name, milliseconds) of every recorded launch, in order
+    (waits for the launches to finish)."""
+    L = lib()
+    n = L.moe_trace_end()
+    out = []
+    name, ms = ctypes.c_char_p(), ctypes.c_float()
+    for i in range(n):
+        _check("moe_trace_get", L.moe_trace_get(i, ctypes.byref(name), ctypes.byref(ms)))
+        out.append((name.value.decode(), float(ms.value)))
+    return out

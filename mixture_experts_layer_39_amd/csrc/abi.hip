@@ -2,6 +2,8 @@
 // moe_expert_ffn and moe_backward.  Every call only enqueues kernels on the caller's stream.
 #include <string.h>
 
+#include <vector>
+
 #include "common.h"
 
 using moe::bf16_t;
@@ -38,6 +40,71 @@ int moe_check_device() {
 }
 
 extern "C" int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+// ---------------------------------------------------------------------- launch tracing
+// Per host thread: a pool of event pairs (created once, reused), the number of launches
+// recorded since moe_trace_begin, and whether tracing is armed.  Off by default, so the
+// calls cost one thread-local flag test when nobody traces.
+namespace {
+struct TraceRec {
+    const char* name;
+    hipEvent_t a, b;
+};
+struct TraceState {
+    std::vector<TraceRec> recs;
+    int cap = 0, n = 0;
+    bool on = false, pending = false;
+};
+thread_local TraceState g_trace;
+}  // namespace
+
+void moe_trace_pre(hipStream_t st) {
+    TraceState& t = g_trace;
+    t.pending = false;
+    if (!t.on || t.n >= t.cap) return;
+    if (hipEventRecord(t.recs[t.n].a, st) == hipSuccess) t.pending = true;
+}
+
+void moe_trace_post(const char* name, hipStream_t st) {
+    TraceState& t = g_trace;
+    if (!t.pending) return;
+    t.pending = false;
+    if (hipEventRecord(t.recs[t.n].b, st) != hipSuccess) return;
+    t.recs[t.n].name = name;
+    ++t.n;
+}
+
+extern "C" int moe_trace_begin(int cap) {
+    if (cap < 1 || cap > (1 << 20)) return MOE_EINVAL;
+    TraceState& t = g_trace;
+    while ((int)t.recs.size() < cap) {
+        TraceRec r{"", nullptr, nullptr};
+        if (hipEventCreate(&r.a) != hipSuccess) return MOE_EHIP;
+        if (hipEventCreate(&r.b) != hipSuccess) {
+            hipEventDestroy(r.a);
+            return MOE_EHIP;
+        }
+        t.recs.push_back(r);
+    }
+    t.cap = cap;
+    t.n = 0;
+    t.on = true;
+    return MOE_OK;
+}
+
+extern "C" int moe_trace_end(void) {
+    g_trace.on = false;
+    return g_trace.n;
+}
+
+extern "C" int moe_trace_get(int i, const char** name, float* ms) {
+    TraceState& t = g_trace;
+    if (i < 0 || i >= t.n || !name || !ms) return MOE_EINVAL;
+    if (hipEventSynchronize(t.recs[i].b) != hipSuccess) return MOE_EHIP;
+    if (hipEventElapsedTime(ms, t.recs[i].a, t.recs[i].b) != hipSuccess) return MOE_EHIP;
+    *name = t.recs[i].name;
+    return MOE_OK;
+}
 
 extern "C" const char* moe_strerror(int code) {
     switch (code) {

@@ -71,4 +71,15 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // Returns MOE_OK when the current device is gfx950 (cached per device).
 int moe_check_device();
 
+// Optional launch tracing (moe_trace_begin in moe.h): with tracing armed on the calling
+// thread, each launch is bracketed by two event records on its stream.
+void moe_trace_pre(hipStream_t st);
+void moe_trace_post(const char* name, hipStream_t st);
+#define MOE_TRACED(name, st, ...)       \
+    do {                                \
+        moe_trace_pre(st);              \
+        __VA_ARGS__;                    \
+        moe_trace_post(name, st);       \
+    } while (0)
+
 static inline size_t moe_align256(size_t n) { return (n + 255) & ~(size_t)255; }

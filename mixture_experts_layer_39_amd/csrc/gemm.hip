@@ -83,8 +83,7 @@ __device__ __forceinline__ void transpose8x8(const u32x4* in, u32x4* out) {
 }
 
 template <bool A_K, bool B_K, int EPI, bool GK>
-__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_kernel(GemmArgs g) {
+__device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     __shared__ __attribute__((aligned(16))) char smem[4 * 256 * 128];
     __shared__ int s_tp[1024];
     __shared__ int s_total;
@@ -366,21 +365,35 @@ void gemm_kernel(GemmArgs g) {
     }
 }
 
+// One kernel symbol per product of the layer, so that profiles name each role.
+#define MOE_GEMM_KERNEL(NAME, AK, BK, EPI, GK)                                         \
+    __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) void \
+    NAME(GemmArgs g) {                                                                 \
+        gemm_body<AK, BK, EPI, GK>(g);                                                 \
+    }
+MOE_GEMM_KERNEL(gemm1_swiglu, true, true, EPI_SWIGLU, false)     // [g|u] = Xp W1^T, h
+MOE_GEMM_KERNEL(gemm2_down, true, true, EPI_STORE, false)        // y = h W2^T
+MOE_GEMM_KERNEL(dgrad_down_dswiglu, true, false, EPI_DSWIGLU, false)  // dh = dy W2 -> dg|du
+MOE_GEMM_KERNEL(dgrad_gate_up, true, false, EPI_STORE, false)    // dXp = dGU W1
+MOE_GEMM_KERNEL(wgrad_down, false, false, EPI_STORE, true)       // dW2 = dy^T h
+MOE_GEMM_KERNEL(wgrad_gate_up, false, false, EPI_STORE, true)    // dW1 = dGU^T Xp
+#undef MOE_GEMM_KERNEL
+
 // Upper bound on the tile count of a ragged-M product (host side, no device data).
 static int ragged_tiles_bound(int R, int E, int NT) {
     int64_t mt = ((int64_t)R + (int64_t)E * (BM - 1)) / BM;
     return (int)(mt * NT);
 }
 
-template <bool A_K, bool B_K, int EPI, bool GK>
-static int launch(const GemmArgs& g, hipStream_t st) {
+template <int EPI, bool GK>
+static int launch(void (*kern)(GemmArgs), const char* name, const GemmArgs& g, hipStream_t st) {
     int NT = (EPI == EPI_SWIGLU) ? cdiv(g.I, 128) : cdiv(g.N, BN);
     int grid;
     if (GK) grid = g.total;
     else if (g.offsets) grid = ragged_tiles_bound(g.R, g.E, NT);
     else grid = g.total;
     if (grid <= 0) return MOE_OK;
-    gemm_kernel<A_K, B_K, EPI, GK><<<grid, NTH, 0, st>>>(g);
+    MOE_TRACED(name, st, kern<<<grid, NTH, 0, st>>>(g));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -407,7 +420,7 @@ int moe_ffn_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, 
     g.C2 = gu; g.c2_es = shared ? (int64_t)R * 2 * I : 0; g.ldc2 = 2 * I;
     g.offsets = offsets; g.E = E; g.R = R; g.N = 2 * I; g.K = H; g.I = I;
     g.total = shared ? E * cdiv(R, BM) * cdiv(I, 128) : 0;
-    int rc = launch<true, true, EPI_SWIGLU, false>(g, st);
+    int rc = launch<EPI_SWIGLU, false>(gemm1_swiglu, "gemm1_swiglu", g, st);
     if (rc) return rc;
     GemmArgs g2 = blank();
     g2.A = h; g2.a_es = shared ? (int64_t)R * I : 0; g2.lda = I;
@@ -415,7 +428,7 @@ int moe_ffn_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, 
     g2.C = y; g2.c_es = shared ? (int64_t)R * H : 0; g2.ldc = H;
     g2.offsets = offsets; g2.E = E; g2.R = R; g2.N = H; g2.K = I; g2.I = I;
     g2.total = shared ? E * cdiv(R, BM) * cdiv(H, BN) : 0;
-    return launch<true, true, EPI_STORE, false>(g2, st);
+    return launch<EPI_STORE, false>(gemm2_down, "gemm2_down", g2, st);
 }
 
 // Backward of the FFN for one group of experts.
@@ -436,7 +449,7 @@ int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int
         g.C2 = const_cast<bf16_t*>(gu); g.c2_es = shared ? (int64_t)R * 2 * I : 0; g.ldc2 = 2 * I;
         g.offsets = offsets; g.E = E; g.R = R; g.N = I; g.K = H; g.I = I;
         g.total = shared ? E * cdiv(R, BM) * cdiv(I, BN) : 0;
-        rc = launch<true, false, EPI_DSWIGLU, false>(g, st);
+        rc = launch<EPI_DSWIGLU, false>(dgrad_down_dswiglu, "dgrad_down_dswiglu", g, st);
         if (rc) return rc;
     }
     {   // dXp = dGU_e W1_e (W1_e is [2I,H]: N-contiguous in H)
@@ -446,7 +459,7 @@ int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int
         g.C = dxp; g.c_es = shared ? (int64_t)R * H : 0; g.ldc = H;
         g.offsets = offsets; g.E = E; g.R = R; g.N = H; g.K = 2 * I; g.I = I;
         g.total = shared ? E * cdiv(R, BM) * cdiv(H, BN) : 0;
-        rc = launch<true, false, EPI_STORE, false>(g, st);
+        rc = launch<EPI_STORE, false>(dgrad_gate_up, "dgrad_gate_up", g, st);
         if (rc) return rc;
     }
     {   // dW2_e = dy_e^T h_e: M = H, N = I, K = the expert's rows
@@ -456,7 +469,7 @@ int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int
         g.C = dw2; g.c_es = (int64_t)H * I; g.ldc = I;
         g.offsets = offsets; g.E = E; g.R = R; g.M = H; g.N = I; g.I = I;
         g.total = E * cdiv(H, BM) * cdiv(I, BN);
-        rc = launch<false, false, EPI_STORE, true>(g, st);
+        rc = launch<EPI_STORE, true>(wgrad_down, "wgrad_down", g, st);
         if (rc) return rc;
     }
     {   // dW1_e = dGU_e^T Xp_e: M = 2I, N = H
@@ -466,7 +479,7 @@ int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int
         g.C = dw1; g.c_es = (int64_t)2 * I * H; g.ldc = H;
         g.offsets = offsets; g.E = E; g.R = R; g.M = 2 * I; g.N = H; g.I = I;
         g.total = E * cdiv(2 * I, BM) * cdiv(H, BN);
-        rc = launch<false, false, EPI_STORE, true>(g, st);
+        rc = launch<EPI_STORE, true>(wgrad_gate_up, "wgrad_gate_up", g, st);
         if (rc) return rc;
     }
     return MOE_OK;

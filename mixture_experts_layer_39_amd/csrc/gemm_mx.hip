@@ -54,8 +54,7 @@ __device__ __forceinline__ uint32_t xlds(int row, int chunk) {
 __host__ __device__ __forceinline__ int xcdiv(int a, int b) { return (a + b - 1) / b; }
 
 template <int EPI>
-__global__ __launch_bounds__(XNTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mx_gemm_kernel(MxArgs g) {
+__device__ __forceinline__ void mx_gemm_body(const MxArgs& g) {
     __shared__ __attribute__((aligned(16))) char smem[4 * 256 * 128];
     __shared__ uint32_t s_sc[2][2][256];
     __shared__ int s_tp[1024];
@@ -277,6 +276,11 @@ void mx_gemm_kernel(MxArgs g) {
     }
 }
 
+__global__ __launch_bounds__(XNTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mx_gemm1_swiglu(MxArgs g) { mx_gemm_body<XEPI_SWIGLU_F32>(g); }
+__global__ __launch_bounds__(XNTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mx_gemm2_down(MxArgs g) { mx_gemm_body<XEPI_STORE_BF16>(g); }
+
 template <int EPI>
 static int mx_launch(const MxArgs& g, hipStream_t st) {
     int NT = (EPI == XEPI_SWIGLU_F32) ? xcdiv(g.I, 128) : xcdiv(g.N, XBN);
@@ -288,7 +292,10 @@ static int mx_launch(const MxArgs& g, hipStream_t st) {
         grid = g.total;
     }
     if (grid <= 0) return MOE_OK;
-    mx_gemm_kernel<EPI><<<grid, XNTH, 0, st>>>(g);
+    if (EPI == XEPI_SWIGLU_F32)
+        MOE_TRACED("mx_gemm1_swiglu", st, mx_gemm1_swiglu<<<grid, XNTH, 0, st>>>(g));
+    else
+        MOE_TRACED("mx_gemm2_down", st, mx_gemm2_down<<<grid, XNTH, 0, st>>>(g));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

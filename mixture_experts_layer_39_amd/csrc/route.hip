@@ -349,34 +349,38 @@ extern "C" int moe_route(const float* logits, const void* x, const void* w_route
     if (T > 0 && !idx_in) {
         if (w_router) {
             int tot = T * E;
-            router_proj_kernel<<<(tot + 255) / 256, 256, 0, st>>>(
-                (const bf16_t*)x, (const bf16_t*)w_router, T, H, E, (float*)logits);
+            MOE_TRACED("router_proj", st,
+                       router_proj_kernel<<<(tot + 255) / 256, 256, 0, st>>>(
+                           (const bf16_t*)x, (const bf16_t*)w_router, T, H, E, (float*)logits));
             MOE_LAUNCH_CHECK();
         }
         TopkParams p{logits, cfg->sel_bias, T, E, k, cfg->score, n_groups, topk_groups,
                      per_group, cfg->renorm, cfg->route_scale, idx, w, s_sel};
         int nv = (E + 63) / 64;
         dim3 grid((T + 3) / 4), block(256);
-        if (nv <= 1) topk_kernel<1><<<grid, block, 0, st>>>(p);
-        else if (nv <= 2) topk_kernel<2><<<grid, block, 0, st>>>(p);
-        else if (nv <= 4) topk_kernel<4><<<grid, block, 0, st>>>(p);
-        else if (nv <= 8) topk_kernel<8><<<grid, block, 0, st>>>(p);
-        else topk_kernel<16><<<grid, block, 0, st>>>(p);
+        MOE_TRACED("topk", st,
+                   if (nv <= 1) topk_kernel<1><<<grid, block, 0, st>>>(p);
+                   else if (nv <= 2) topk_kernel<2><<<grid, block, 0, st>>>(p);
+                   else if (nv <= 4) topk_kernel<4><<<grid, block, 0, st>>>(p);
+                   else if (nv <= 8) topk_kernel<8><<<grid, block, 0, st>>>(p);
+                   else topk_kernel<16><<<grid, block, 0, st>>>(p));
         MOE_LAUNCH_CHECK();
     }
     const int32_t* ids = idx_in ? idx_in : idx;
     int nch = (int)((n + CHUNK - 1) / CHUNK);
     int32_t* blk = (int32_t*)ws;
     if (nch > 0) {
-        count_kernel<<<nch, 256, E * sizeof(int), st>>>(ids, n, E, blk);
+        MOE_TRACED("perm_count", st,
+                   count_kernel<<<nch, 256, E * sizeof(int), st>>>(ids, n, E, blk));
         MOE_LAUNCH_CHECK();
     }
-    scan_kernel<<<1, 1024, 0, st>>>(blk, nch, E, counts, offsets);
+    MOE_TRACED("perm_scan", st, scan_kernel<<<1, 1024, 0, st>>>(blk, nch, E, counts, offsets));
     MOE_LAUNCH_CHECK();
     if (nch > 0) {
         int nbits = 0;
         while ((1 << nbits) < E) ++nbits;
-        rank_kernel<<<nch, 64, E * sizeof(int), st>>>(ids, n, E, nbits, blk, pos, src);
+        MOE_TRACED("perm_rank", st,
+                   rank_kernel<<<nch, 64, E * sizeof(int), st>>>(ids, n, E, nbits, blk, pos, src));
         MOE_LAUNCH_CHECK();
     }
     return MOE_OK;

@@ -363,10 +363,13 @@ extern "C" int moe_dispatch(const void* x, int T, int H, int k, const int32_t* s
     if (xp_codes) {
         int nb = H / 32;
         dim3 grid((nb + 255) / 256, R);
-        dispatch_mx_kernel<<<grid, 256, 0, st>>>((const bf16_t*)x, n_pairs, H, k, src,
-                                                  (bf16_t*)xp, xp_codes, xp_scales);
+        MOE_TRACED("dispatch_mx", st,
+                   dispatch_mx_kernel<<<grid, 256, 0, st>>>((const bf16_t*)x, n_pairs, H, k, src,
+                                                             (bf16_t*)xp, xp_codes, xp_scales));
     } else {
-        dispatch_kernel<<<R, 128, 0, st>>>((const bf16_t*)x, n_pairs, H, k, src, (bf16_t*)xp);
+        MOE_TRACED("dispatch", st,
+                   dispatch_kernel<<<R, 128, 0, st>>>((const bf16_t*)x, n_pairs, H, k, src,
+                                                      (bf16_t*)xp));
     }
     MOE_LAUNCH_CHECK();
     return MOE_OK;
@@ -380,8 +383,10 @@ extern "C" int moe_combine(const void* y, const int32_t* pos, const float* w, in
     if (T == 0) return MOE_OK;
     int rc = moe_check_device();
     if (rc) return rc;
-    combine_kernel<<<T, 128, 0, (hipStream_t)stream>>>((const bf16_t*)y, pos, w, T, k, H, R,
-                                                       (const bf16_t*)ys, S, (bf16_t*)out);
+    hipStream_t st = (hipStream_t)stream;
+    MOE_TRACED("combine", st,
+               combine_kernel<<<T, 128, 0, st>>>((const bf16_t*)y, pos, w, T, k, H, R,
+                                                 (const bf16_t*)ys, S, (bf16_t*)out));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -397,10 +402,12 @@ extern "C" int mx_quantize(const void* in, int in_dtype, int rows, int K, uint8_
     if (rc) return rc;
     int64_t nb = (int64_t)rows * (K / 32);
     dim3 grid((unsigned)((nb + 255) / 256));
-    if (in_dtype == MOE_F32)
-        mx_quantize_kernel<true><<<grid, 256, 0, (hipStream_t)stream>>>(in, nb, scale_mode, codes, scales);
-    else
-        mx_quantize_kernel<false><<<grid, 256, 0, (hipStream_t)stream>>>(in, nb, scale_mode, codes, scales);
+    hipStream_t st = (hipStream_t)stream;
+    MOE_TRACED("mx_quantize", st,
+               if (in_dtype == MOE_F32)
+                   mx_quantize_kernel<true><<<grid, 256, 0, st>>>(in, nb, scale_mode, codes, scales);
+               else
+                   mx_quantize_kernel<false><<<grid, 256, 0, st>>>(in, nb, scale_mode, codes, scales));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -409,7 +416,8 @@ extern "C" int mx_quantize(const void* in, int in_dtype, int rows, int K, uint8_
 int moe_launch_combine_bwd(const bf16_t* dout, const bf16_t* y, const int32_t* pos, const float* w,
                            int T, int k, int H, int R, bf16_t* dy, float* dw, hipStream_t st) {
     if (T == 0) return MOE_OK;
-    combine_bwd_kernel<<<T, 256, 0, st>>>(dout, y, pos, w, k, H, R, dy, dw);
+    MOE_TRACED("combine_bwd", st,
+               combine_bwd_kernel<<<T, 256, 0, st>>>(dout, y, pos, w, k, H, R, dy, dw));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -417,7 +425,8 @@ int moe_launch_combine_bwd(const bf16_t* dout, const bf16_t* y, const int32_t* p
 int moe_launch_unpermute(const bf16_t* dxp, const int32_t* pos, int T, int k, int H, int R,
                          const bf16_t* dxs, int S, bf16_t* dx, hipStream_t st) {
     if (T == 0) return MOE_OK;
-    unpermute_kernel<<<T, 128, 0, st>>>(dxp, pos, T, k, H, R, dxs, S, dx);
+    MOE_TRACED("unpermute", st,
+               unpermute_kernel<<<T, 128, 0, st>>>(dxp, pos, T, k, H, R, dxs, S, dx));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -426,8 +435,9 @@ int moe_launch_router_bwd(const int32_t* idx, const float* w, const float* s_sel
                           const float* logits, int T, int E, int k, int score, int renorm, float c,
                           float* dL, hipStream_t st) {
     if (T == 0) return MOE_OK;
-    router_bwd_kernel<<<(T + 3) / 4, 256, 0, st>>>(idx, w, s_sel, dw, logits, T, E, k, score,
-                                                   renorm, c, dL);
+    MOE_TRACED("router_bwd", st,
+               router_bwd_kernel<<<(T + 3) / 4, 256, 0, st>>>(idx, w, s_sel, dw, logits, T, E, k,
+                                                              score, renorm, c, dL));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -436,8 +446,9 @@ int moe_launch_mx_quantize_f32(const float* in, int64_t rows, int K, uint8_t* co
                                hipStream_t st) {
     int64_t nb = rows * (K / 32);
     if (nb == 0) return MOE_OK;
-    mx_quantize_kernel<true><<<(unsigned)((nb + 255) / 256), 256, 0, st>>>(in, nb, MOE_MX_FLOOR,
-                                                                         codes, scales);
+    MOE_TRACED("mx_quantize_h", st,
+               mx_quantize_kernel<true><<<(unsigned)((nb + 255) / 256), 256, 0, st>>>(
+                   in, nb, MOE_MX_FLOOR, codes, scales));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

@@ -57,6 +57,11 @@ def _c(a, dtype):
 
 
 # ----------------------------------------------------------------------------- steps
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_threads())
+
+
 def bf16_to_f64(b: np.ndarray) -> np.ndarray:
     b = _c(b, np.uint16)
     out = np.empty(b.shape, np.float64)

@@ -43,6 +43,14 @@ static float bff(uint16_t b) { return (float)bf(b); }
 
 int orc_version(void) { return 1; }
 
+/* Threads the OpenMP loops of this library use (1 when built without OpenMP). */
+#ifdef _OPENMP
+#include <omp.h>
+int orc_threads(void) { return omp_get_max_threads(); }
+#else
+int orc_threads(void) { return 1; }
+#endif
+
 /* bf16 bit patterns -> fp64 (exact). */
 void orc_bf16_to_f64(const uint16_t *in, int64_t n, double *out)
 {
