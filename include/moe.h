@@ -6,7 +6,7 @@
  * sekundet", ¶6), run forward in BF16 or MXFP8 and backward in BF16 (same page, ¶3;
  * aiexpert.news, "Megakernels are dead and back", ¶4), fully deterministic (pulsen ¶3-¶4;
  * ki-pruefstand.de, "Cursor veröffentlicht MoE-Megakernel Mixture-of-Kittens als Open
- * Source", ¶2): repeated calls with the same inputs give bit-identical outputs.  No kernel
+ * Source", ¶3): repeated calls with the same inputs give bit-identical outputs.  No kernel
  * uses floating-point atomics; every sum runs in one fixed order.
  *
  * Conventions for every call:
