@@ -17,6 +17,10 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int WAVE = 64;
 
+// A value every lane of the wave holds alike, made visibly uniform to the compiler (kept in
+// a scalar register), so that address math and buffer descriptors built from it stay scalar.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // fp32 -> bf16, round to nearest even (inputs are finite).

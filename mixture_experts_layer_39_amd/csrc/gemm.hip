@@ -31,9 +31,15 @@ namespace moe {
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+// Buffer descriptor of a block-uniform range: base and size pass through readfirstlane so that
+// the descriptor lives in scalar registers (a descriptor the compiler sees as divergent costs
+// a waterfall loop around every load).
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
-                                             0x00020000);
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)uni((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)uni((int)(uint32_t)(a >> 32));
+    void* q = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, uni((int)bytes), 0x00020000);
 }
 __device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
@@ -65,30 +71,132 @@ struct GemmArgs {
     int total;    // tile count when it is static (ragged-K or shared mode)
 };
 
+// ---------------------------------------------------------------- LDS tiles
+// One pipeline stage holds one K step (BK = 64) of both operands, 32 KB each.  Two layouts:
+//  K-major   (operand contiguous along K in memory): tile row r (an M or N index) is 128 bytes,
+//            eight 16-byte chunks of 8 k values; chunk c is stored at chunk c ^ swz(r), so the
+//            8 rows read by one 128-byte phase of a fragment read hit 8 distinct bank groups.
+//  MN-major  (operand contiguous along M or N): k-row kr is 512 bytes, 32 chunks of 8 m (n)
+//            values; chunk c is stored at chunk (c + 2*(kr % 4)) % 32, so the 4 k-rows read
+//            by one 16-lane group of a transpose read hit 4 distinct 32-byte bank groups.
+// Both are filled by direct global-to-LDS loads (buffer_load ... lds): lane L of a wave
+// writes 16 bytes at LDS base + 16 L, so each lane fetches the global chunk that belongs at
+// its LDS position and the swizzle lives entirely in the global offsets.
+constexpr int OPB = 256 * 128;  // bytes of one operand in one stage
+
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ uint32_t lds_off(int buf, int row, int chunk) {
-    return (uint32_t)((buf * 256 + row) * 128 + ((chunk ^ swz(row)) << 4));
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void lds_load16(rsrc_t r, char* lds_dst, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds_dst, 16, voff, soff, 0, 0);
 }
+
+// Transposed 8-byte LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
+// receives element i % 4 of the 8-byte chunks addressed by lanes i/4 + 4j, j = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(p));
+}
+
 __host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// 8x8 transpose of bf16: in[kk] holds 8 m-values at k = kk; out[mm] holds 8 k-values at m = mm.
-__device__ __forceinline__ void transpose8x8(const u32x4* in, u32x4* out) {
+// Per-lane description of one operand's global->LDS loads (8 per wave per K step) and of
+// its MFMA fragment reads (4 sub-tiles of 32 rows per wave).
+struct Operand {
+    rsrc_t r;
+    uint32_t voff[8];   // byte offset of this lane's 16-byte chunk, per load instruction
+    uint32_t kstep;     // byte advance of the global offset per K step
+    int ldsrow[8];      // LDS byte offset (within the operand's stage area) per load instruction
+    uint32_t rd[4];     // fragment-read base offset per sub-tile (K-major: row base | chunk bit)
+    int rs[4];          // K-major: swizzle bits 1-2 of the sub-tile's row
+};
+
+// K-major operand.  rowmap(nn) gives the global row (relative to the descriptor base) of
+// tile row nn.  Each wave loads tile rows 64 w .. 64 w + 63 (eight 8-row instructions).
+template <typename RowMap>
+__device__ __forceinline__ void setup_kmajor(Operand& o, const void* base, uint32_t bytes, int ld,
+                                             int wid, int lane, int wsub, RowMap rowmap) {
+    o.r = make_rsrc(base, bytes);
 #pragma unroll
-    for (int mm = 0; mm < 8; ++mm) {
-        const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
+    for (int i = 0; i < 8; ++i) {
+        const int r = 64 * wid + 8 * i + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
+        o.voff[i] = (uint32_t)rowmap(r) * (uint32_t)ld * 2u + (uint32_t)c * 16u;
+        o.ldsrow[i] = (64 * wid + 8 * i) * 128;
+    }
+    o.kstep = BK * 2;
+    // fragment reads: lane reads row rb + lane%32, logical chunk 2 kk + lane/32
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            out[mm][j] = __builtin_amdgcn_perm(in[2 * j + 1][mm >> 1], in[2 * j][mm >> 1], sel);
+    for (int t = 0; t < 4; ++t) {
+        const int r = wsub + 32 * t + (lane & 31);
+        const int s = swz(r);
+        o.rd[t] = (uint32_t)(r * 128) | ((uint32_t)(((lane >> 5) ^ s) & 1) << 4);
+        o.rs[t] = s & 6;
+    }
+}
+
+// MN-major operand: element (mn, k) at base + k*ld + mn (bytes x2).  Each wave loads k-rows
+// 16 w .. 16 w + 15 of the step (eight 2-row instructions).
+__device__ __forceinline__ void setup_mnmajor(Operand& o, const void* base, uint32_t bytes, int ld,
+                                              int wid, int lane, int wsub) {
+    o.r = make_rsrc(base, bytes);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int kr = 16 * wid + 2 * i + (lane >> 5);
+        const int c = ((lane & 31) - 2 * (kr & 3)) & 31;
+        o.voff[i] = (uint32_t)kr * (uint32_t)ld * 2u + (uint32_t)c * 16u;
+        o.ldsrow[i] = (16 * wid + 2 * i) * 512;
+    }
+    o.kstep = (uint32_t)BK * (uint32_t)ld * 2u;
+    // transpose reads: lane group g = lane/16, q = lane%4, j = (lane%16)/4 reads k-row
+    // 16 kk + 8 (g/2) + 4 h + j at columns mnb + 16 (g%2) + 4 q .. +3
+    const int gq = lane >> 4, q = lane & 3, j = (lane >> 2) & 3;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int mn = wsub + 32 * t + 16 * (gq & 1) + 4 * q;
+        const int kr = 8 * (gq >> 1) + j;
+        const int pc = ((mn >> 3) + 2 * j) & 31;
+        o.rd[t] = (uint32_t)(kr * 512 + pc * 16 + 8 * (q & 1));
+        o.rs[t] = 0;
+    }
+}
+
+template <bool KMAJ>
+__device__ __forceinline__ void issue_loads(const Operand& o, char* stage_op, int ks) {
+    const uint32_t so = (uint32_t)ks * o.kstep;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lds_load16(o.r, stage_op + o.ldsrow[i], o.voff[i], so);
+}
+
+// The 32x32x16 MFMA fragment of sub-tile t at k sub-step kk: 8 bf16 (k = 8 (lane/32) .. +7 of
+// the sub-step) of row (or column) lane % 32.
+template <bool KMAJ>
+__device__ __forceinline__ bf16x8 read_frag(const Operand& o, const char* stage_op, int t, int kk) {
+    if (KMAJ) {
+        const uint32_t off = o.rd[t] + ((uint32_t)((2 * kk) ^ o.rs[t]) << 4);
+        return *reinterpret_cast<const bf16x8*>(stage_op + off);
+    } else {
+        const char* p = stage_op + o.rd[t] + 16 * kk * 512;
+        i16x4 lo = lds_read_tr(p);
+        i16x4 hi = lds_read_tr(p + 4 * 512);
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, v);
     }
 }
 
 template <bool A_K, bool B_K, int EPI, bool GK>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
-    __shared__ __attribute__((aligned(16))) char smem[4 * 256 * 128];
+    // two pipeline stages, as distinct arrays so that the compiler can tell a stage being
+    // filled by direct loads from the stage being read
+    __shared__ __attribute__((aligned(1024))) char st0[2 * OPB];
+    __shared__ __attribute__((aligned(1024))) char st1[2 * OPB];
     __shared__ int s_tp[1024];
     __shared__ int s_total;
 
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wid = uni(tid >> 6);
     const int wm = wid >> 1, wn = wid & 1;
     const int NT = (EPI == EPI_SWIGLU) ? cdiv(g.I, 128) : cdiv(g.N, BN);
 
@@ -112,7 +220,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             if (lane == 0) s_total = run;
         }
         __syncthreads();
-        total = s_total;
+        total = uni(s_total);
     } else {
         total = g.total;
     }
@@ -131,12 +239,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             int mid = (lo + hi) >> 1;
             if (s_tp[mid] > logical) hi = mid; else lo = mid + 1;
         }
-        e = lo;
-        t_local = logical - (e ? s_tp[e - 1] : 0);
+        e = uni(lo);
+        t_local = uni(logical - (e ? s_tp[e - 1] : 0));
         int a = min(max(g.offsets[e], 0), g.R);
         int b = min(max(g.offsets[e + 1], a), g.R);
-        row0 = a;
-        Mrows = b - a;
+        row0 = uni(a);
+        Mrows = uni(b - a);
     } else {
         int per = GK ? cdiv(g.M, BM) * NT : cdiv(g.R, BM) * NT;
         e = logical / per;
@@ -145,8 +253,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             if (g.offsets) {
                 int a = min(max(g.offsets[e], 0), g.R);
                 int b = min(max(g.offsets[e + 1], a), g.R);
-                row0 = a;
-                Mrows = b - a;  // here: the K extent (rows of the expert)
+                row0 = uni(a);
+                Mrows = uni(b - a);  // here: the K extent (rows of the expert)
             } else {
                 row0 = 0;
                 Mrows = g.R;
@@ -169,56 +277,42 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     const int m0 = tm * BM;
     const int Kdim = GK ? Mrows : g.K;
     const int Mvalid = GK ? g.M : Mrows;
-
-    // ---------------------------------------------------------------- operand setup
-    // A: K-contiguous (row m at A_e + (row0 + m)*lda)  or  M-contiguous (wgrad: element
-    // (m,k) at A_e + (row0 + k)*lda + m).
-    rsrc_t ra, rb;
-    uint32_t va[8], vb[8];
-    uint32_t a_kstep, b_kstep;
-    if (A_K) {
-        const bf16_t* base = g.A + e * g.a_es + (int64_t)(row0 + m0) * g.lda;
-        ra = make_rsrc(base, (uint32_t)max(Mrows - m0, 0) * (uint32_t)g.lda * 2u);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            va[i] = (uint32_t)((tid >> 3) + 32 * i) * (uint32_t)g.lda * 2u + (uint32_t)(tid & 7) * 16u;
-        a_kstep = BK * 2;
-    } else {
-        const bf16_t* base = g.A + e * g.a_es + (int64_t)row0 * g.lda + m0;
-        ra = make_rsrc(base, (uint32_t)Kdim * (uint32_t)g.lda * 2u - (uint32_t)m0 * 2u);
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-            va[kk] = (uint32_t)((tid >> 5) * 8 + kk) * (uint32_t)g.lda * 2u + (uint32_t)(tid & 31) * 16u;
-        a_kstep = (uint32_t)BK * (uint32_t)g.lda * 2u;
-    }
     const int n0 = tn * BN;
     const int ch0 = tn * 128;  // SwiGLU channel base
+
+    // ---------------------------------------------------------------- operands
+    // A: K-major rows m at A_e + (row0 + m)*lda; or MN-major (wgrad): (m, k) at
+    //    A_e + (row0 + k)*lda + m.
+    // B: K-major rows n at B_e + n*ldb (SwiGLU: gate and up rows interleaved so a tile holds
+    //    128 channels of each); or MN-major: (n, k) at B_e + (kbase + k)*ldb + n, kbase = row0
+    //    for wgrad (the expert's tokens), else 0 (a weight with K rows).
+    Operand oa, ob;
+    if (A_K) {
+        const bf16_t* base = g.A + e * g.a_es + (int64_t)(row0 + m0) * g.lda;
+        setup_kmajor(oa, base, (uint32_t)max(Mrows - m0, 0) * (uint32_t)g.lda * 2u, g.lda, wid,
+                     lane, wm * 128, [](int r) { return r; });
+    } else {
+        const bf16_t* base = g.A + e * g.a_es + (int64_t)row0 * g.lda + m0;
+        setup_mnmajor(oa, base, (uint32_t)Kdim * (uint32_t)g.lda * 2u - (uint32_t)m0 * 2u, g.lda,
+                      wid, lane, wm * 128);
+    }
     if (B_K) {
         const bf16_t* base = g.B + e * g.b_es;
-        rb = make_rsrc(base, (uint32_t)g.b_rows * (uint32_t)g.ldb * 2u);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            int nn = (tid >> 3) + 32 * i;
-            int row;
-            if (EPI == EPI_SWIGLU) {
-                int q = nn & 127;
-                row = (q >> 6) * g.I + ch0 + (nn >> 7) * 64 + (q & 63);
-            } else {
-                row = n0 + nn;
-            }
-            vb[i] = (uint32_t)row * (uint32_t)g.ldb * 2u + (uint32_t)(tid & 7) * 16u;
-        }
-        b_kstep = BK * 2;
+        const int I = g.I;
+        if (EPI == EPI_SWIGLU)
+            setup_kmajor(ob, base, (uint32_t)g.b_rows * (uint32_t)g.ldb * 2u, g.ldb, wid, lane,
+                         wn * 128, [=](int nn) {
+                             int q = nn & 127;
+                             return (q >> 6) * I + ch0 + (nn >> 7) * 64 + (q & 63);
+                         });
+        else
+            setup_kmajor(ob, base, (uint32_t)g.b_rows * (uint32_t)g.ldb * 2u, g.ldb, wid, lane,
+                         wn * 128, [=](int nn) { return n0 + nn; });
     } else {
-        // N-contiguous: element (n,k) at B_e + (row0_k + k)*ldb + n; in ragged-M mode B is a
-        // weight with K rows (row0_k = 0); in ragged-K mode the rows are the expert's tokens.
         const int64_t kbase = GK ? row0 : 0;
         const bf16_t* base = g.B + e * g.b_es + kbase * g.ldb + n0;
-        rb = make_rsrc(base, (uint32_t)Kdim * (uint32_t)g.ldb * 2u - (uint32_t)n0 * 2u);
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-            vb[kk] = (uint32_t)((tid >> 5) * 8 + kk) * (uint32_t)g.ldb * 2u + (uint32_t)(tid & 31) * 16u;
-        b_kstep = (uint32_t)BK * (uint32_t)g.ldb * 2u;
+        setup_mnmajor(ob, base, (uint32_t)Kdim * (uint32_t)g.ldb * 2u - (uint32_t)n0 * 2u, g.ldb,
+                      wid, lane, wn * 128);
     }
 
     f32x16 acc[4][4];
@@ -229,139 +323,154 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    u32x4 ra_reg[8], rb_reg[8];
-    auto gload = [&](int ks) {
-        const uint32_t ao = (uint32_t)ks * a_kstep, bo = (uint32_t)ks * b_kstep;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ra_reg[i] = bload(ra, va[i] + ao);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) rb_reg[i] = bload(rb, vb[i] + bo);
-    };
-    auto lstore = [&](int buf) {
-        char* sA = smem + (2 * buf) * 256 * 128;
-        char* sB = smem + (2 * buf + 1) * 256 * 128;
-        if (A_K) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                st16(sA + lds_off(0, (tid >> 3) + 32 * i, tid & 7), ra_reg[i]);
-        } else {
-            u32x4 t[8];
-            transpose8x8(ra_reg, t);
-#pragma unroll
-            for (int mm = 0; mm < 8; ++mm) st16(sA + lds_off(0, (tid & 31) * 8 + mm, tid >> 5), t[mm]);
-        }
-        if (B_K) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                st16(sB + lds_off(0, (tid >> 3) + 32 * i, tid & 7), rb_reg[i]);
-        } else {
-            u32x4 t[8];
-            transpose8x8(rb_reg, t);
-#pragma unroll
-            for (int mm = 0; mm < 8; ++mm) st16(sB + lds_off(0, (tid & 31) * 8 + mm, tid >> 5), t[mm]);
-        }
-    };
-
+    // ---------------------------------------------------------------- main loop
+    // Per K step: 4 sub-steps of 16 k.  Fragments of sub-step kk+1 are read while the MFMAs of
+    // kk run; at the end of a step the barrier (all waves done reading this stage, all loads
+    // of the next stage landed) sits before the last sub-step's MFMAs, so the first fragments
+    // of the next step are read while they run.  The loads of step ks+2 go into the stage
+    // just freed, one step ahead of their use.
+    // The MFMA takes the B fragment as its first operand, so each lane's accumulators hold
+    // one output row (m) and 4-column runs (n): the epilogue stores 8-byte vectors.
     const int nk = cdiv(Kdim, BK);
-    if (nk > 0) {
-        gload(0);
-        lstore(0);
-    }
-    __syncthreads();
-    for (int ks = 0; ks < nk; ++ks) {
-        const int buf = ks & 1;
-        if (ks + 1 < nk) gload(ks + 1);
-        const char* sA = smem + (2 * buf) * 256 * 128;
-        const char* sB = smem + (2 * buf + 1) * 256 * 128;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            bf16x8 af[4], bfr[4];
-            const int chunk = kk * 2 + (lane >> 5);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(sA + lds_off(0, wm * 128 + i * 32 + (lane & 31), chunk));
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(sB + lds_off(0, wn * 128 + j * 32 + (lane & 31), chunk));
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
-        if (ks + 1 < nk) lstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    // ---------------------------------------------------------------- epilogue
-    // Accumulator layout of v_mfma_f32_32x32x16: lane l holds column l%32 and rows
-    // 8*(v/4) + 4*(l/32) + v%4 of its 32x32 tile, v = 0..15.
-    const int lc = lane & 31, lr = (lane >> 5) * 4;
-    if (EPI == EPI_STORE) {
-        bf16_t* C = g.C + e * g.c_es + (GK ? 0 : (int64_t)row0 * g.ldc);
+    bf16x8 fa[2][4], fb[2][4];
+    auto mfmas = [&](int f) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = n0 + wn * 128 + j * 32 + lc;
-                const bool cok = col < g.N;
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j],
+                                                                    0, 0, 0);
+    };
+    auto reads = [&](const char* st, int kk, int f) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + lr + (v & 3);
-                    const float val = acc[i][j][v];
-                    if (cok && row < Mvalid) C[(int64_t)row * g.ldc + col] = f2bf(val);
+        for (int t = 0; t < 4; ++t) fa[f][t] = read_frag<A_K>(oa, st, t, kk);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) fb[f][t] = read_frag<B_K>(ob, st + OPB, t, kk);
+    };
+    // one K step from stage `cur` (`nxt` holds step ks+1 once the barrier passes)
+    auto kstep = [&](char* cur, char* nxt, int ks) {
+        reads(cur, 1, 1);
+        mfmas(0);
+        reads(cur, 2, 0);
+        mfmas(1);
+        reads(cur, 3, 1);
+        mfmas(0);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of step ks+1 and its reads are done
+        __syncthreads();
+        if (ks + 2 < nk) {
+            issue_loads<A_K>(oa, cur, ks + 2);
+            issue_loads<B_K>(ob, cur + OPB, ks + 2);
+        }
+        if (ks + 1 < nk) reads(nxt, 0, 0);
+        // keep the loads and reads above issued before the MFMAs below
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(1);
+    };
+    if (nk > 0) {
+        issue_loads<A_K>(oa, st0, 0);
+        issue_loads<B_K>(ob, st0 + OPB, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (nk > 1) {
+            issue_loads<A_K>(oa, st1, 1);
+            issue_loads<B_K>(ob, st1 + OPB, 1);
+        }
+        reads(st0, 0, 0);
+        int ks = 0;
+        for (; ks + 1 < nk; ks += 2) {
+            kstep(st0, st1, ks);
+            kstep(st1, st0, ks + 1);
+        }
+        if (ks < nk) kstep(st0, st1, ks);
+    }
+
+    // ---------------------------------------------------------------- epilogue
+    // Accumulator layout (B fragment first): lane l holds row l % 32 of its 32x32 block and
+    // columns 8 (v/4) + 4 (l/32) + v%4, v = 0..15: four runs of 4 consecutive columns.
+    const int lrow = lane & 31, lcol = (lane >> 5) * 4;
+    if (EPI == EPI_STORE) {
+        bf16_t* C = g.C + e * g.c_es + (GK ? 0 : (int64_t)row0 * g.ldc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + wm * 128 + i * 32 + lrow;
+            if (row >= Mvalid) continue;
+            bf16_t* Crow = C + (int64_t)row * g.ldc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = n0 + wn * 128 + j * 32 + 8 * q + lcol;
+                    if (col < g.N) {
+                        uint2 v = make_uint2(pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                             pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+                        *reinterpret_cast<uint2*>(Crow + col) = v;
+                    }
                 }
-            }
+        }
     } else if (EPI == EPI_SWIGLU) {
         bf16_t* C = g.C + e * g.c_es + (int64_t)row0 * g.ldc;
         bf16_t* C2 = g.C2 ? g.C2 + e * g.c2_es + (int64_t)row0 * g.ldc2 : nullptr;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + wm * 128 + i * 32 + lrow;
+            if (row >= Mvalid) continue;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int ch = ch0 + wn * 64 + j * 32 + lc;
-                const bool cok = ch < g.I;
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + lr + (v & 3);
-                    const float gv = acc[i][j][v], uv = acc[i][j + 2][v];
-                    const float hv = gv / (1.0f + __expf(-gv)) * uv;
-                    if (cok && row < Mvalid) {
-                        C[(int64_t)row * g.ldc + ch] = f2bf(hv);
-                        if (C2) {
-                            C2[(int64_t)row * g.ldc2 + ch] = f2bf(gv);
-                            C2[(int64_t)row * g.ldc2 + g.I + ch] = f2bf(uv);
-                        }
+                for (int q = 0; q < 4; ++q) {
+                    const int ch = ch0 + wn * 64 + j * 32 + 8 * q + lcol;
+                    if (ch >= g.I) continue;
+                    float hv[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float gv = acc[i][j][4 * q + c], uv = acc[i][j + 2][4 * q + c];
+                        hv[c] = gv / (1.0f + __expf(-gv)) * uv;
+                    }
+                    *reinterpret_cast<uint2*>(C + (int64_t)row * g.ldc + ch) =
+                        make_uint2(pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3]));
+                    if (C2) {
+                        bf16_t* gr = C2 + (int64_t)row * g.ldc2;
+                        *reinterpret_cast<uint2*>(gr + ch) =
+                            make_uint2(pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                       pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+                        *reinterpret_cast<uint2*>(gr + g.I + ch) =
+                            make_uint2(pack_bf2(acc[i][j + 2][4 * q], acc[i][j + 2][4 * q + 1]),
+                                       pack_bf2(acc[i][j + 2][4 * q + 2], acc[i][j + 2][4 * q + 3]));
                     }
                 }
-            }
+        }
     } else {  // EPI_DSWIGLU: acc = dh; read saved g|u, write dg|du
         bf16_t* C = g.C + e * g.c_es + (int64_t)row0 * g.ldc;
         const bf16_t* GU = g.C2 + e * g.c2_es + (int64_t)row0 * g.ldc2;
-#pragma clang loop unroll(full)
-        for (int i = 0; i < 4; ++i)
-#pragma clang loop unroll(full)
-            for (int j = 0; j < 4; ++j) {
-                const int ch = n0 + wn * 128 + j * 32 + lc;
-                const bool cok = ch < g.N;
-#pragma clang loop unroll(full)
-                for (int v = 0; v < 16; ++v) {
-                    const int row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + lr + (v & 3);
-                    const float dh = acc[i][j][v];
-                    const bool ok = cok && row < Mvalid;
-                    // clamped (always in-bounds) reads keep the loop branch-free
-                    const int64_t gro = (int64_t)(ok ? row : 0) * g.ldc2 + (cok ? ch : 0);
-                    const float gv = bf2f(GU[gro]);
-                    const float uv = bf2f(GU[gro + g.I]);
-                    const float sg = 1.0f / (1.0f + __expf(-gv));
-                    const float dg = dh * uv * sg * (1.0f + gv * (1.0f - sg));
-                    const float du = dh * gv * sg;
-                    if (ok) {
-                        C[(int64_t)row * g.ldc + ch] = f2bf(dg);
-                        C[(int64_t)row * g.ldc + g.I + ch] = f2bf(du);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + wm * 128 + i * 32 + lrow;
+            if (row >= Mvalid) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int ch = n0 + wn * 128 + j * 32 + 8 * q + lcol;
+                    if (ch >= g.N) continue;
+                    const uint2 gg = *reinterpret_cast<const uint2*>(GU + (int64_t)row * g.ldc2 + ch);
+                    const uint2 uu = *reinterpret_cast<const uint2*>(GU + (int64_t)row * g.ldc2 + g.I + ch);
+                    const float gv[4] = {lo_bf(gg.x), hi_bf(gg.x), lo_bf(gg.y), hi_bf(gg.y)};
+                    const float uv[4] = {lo_bf(uu.x), hi_bf(uu.x), lo_bf(uu.y), hi_bf(uu.y)};
+                    float dg[4], du[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float dh = acc[i][j][4 * q + c];
+                        const float sg = 1.0f / (1.0f + __expf(-gv[c]));
+                        dg[c] = dh * uv[c] * sg * (1.0f + gv[c] * (1.0f - sg));
+                        du[c] = dh * gv[c] * sg;
                     }
+                    bf16_t* cr = C + (int64_t)row * g.ldc;
+                    *reinterpret_cast<uint2*>(cr + ch) =
+                        make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
+                    *reinterpret_cast<uint2*>(cr + g.I + ch) =
+                        make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
                 }
-            }
+        }
     }
 }
 

@@ -17,9 +17,13 @@ namespace moe {
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+// Buffer descriptor of a block-uniform range, kept in scalar registers (see make_rsrc).
 __device__ __forceinline__ rsrc_t mx_rsrc(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
-                                             0x00020000);
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)uni((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)uni((int)(uint32_t)(a >> 32));
+    void* q = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, uni((int)bytes), 0x00020000);
 }
 __device__ __forceinline__ u32x4 mx_bload16(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
@@ -83,7 +87,7 @@ __device__ __forceinline__ void mx_gemm_body(const MxArgs& g) {
             if (lane == 0) s_total = run;
         }
         __syncthreads();
-        total = s_total;
+        total = uni(s_total);
     } else {
         total = g.total;
     }
@@ -101,12 +105,12 @@ __device__ __forceinline__ void mx_gemm_body(const MxArgs& g) {
             int mid = (lo + hi) >> 1;
             if (s_tp[mid] > logical) hi = mid; else lo = mid + 1;
         }
-        e = lo;
-        t_local = logical - (e ? s_tp[e - 1] : 0);
+        e = uni(lo);
+        t_local = uni(logical - (e ? s_tp[e - 1] : 0));
         int a = min(max(g.offsets[e], 0), g.R);
         int b = min(max(g.offsets[e + 1], a), g.R);
-        row0 = a;
-        Mrows = b - a;
+        row0 = uni(a);
+        Mrows = uni(b - a);
     } else {
         int per = xcdiv(g.R, XBM) * NT;
         e = logical / per;
