@@ -45,8 +45,10 @@ __device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
-constexpr int BM = 256, BN = 256, BK = 64, NTH = 256;
-constexpr int GM = 4;  // M tiles per L2 group
+constexpr int BM = 256, BN = 256, BK = 32, NTH = 256;
+constexpr int KK = BK / 16;   // 32x32x16 MFMA sub-steps per K step
+constexpr int NST = 4;        // pipeline stages (K steps resident or in flight)
+constexpr int GM = 4;         // M tiles per L2 group
 
 enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
 
@@ -72,25 +74,37 @@ struct GemmArgs {
 };
 
 // ---------------------------------------------------------------- LDS tiles
-// One pipeline stage holds one K step (BK = 64) of both operands, 32 KB each.  Two layouts:
-//  K-major   (operand contiguous along K in memory): tile row r (an M or N index) is 128 bytes,
-//            eight 16-byte chunks of 8 k values; chunk c is stored at chunk c ^ swz(r), so the
-//            8 rows read by one 128-byte phase of a fragment read hit 8 distinct bank groups.
+// One pipeline stage holds one K step (BK = 32) of both operands, 16 KB each.  Two layouts:
+//  K-major   (operand contiguous along K in memory): tile row r (an M or N index) is 64 bytes,
+//            four 16-byte chunks of 8 k values; chunk c is stored at chunk c ^ kswz(r).  The
+//            rows read by one 128-byte (8-lane) or 256-byte (16-lane) phase of a fragment read
+//            then hit distinct bank groups.
 //  MN-major  (operand contiguous along M or N): k-row kr is 512 bytes, 32 chunks of 8 m (n)
 //            values; chunk c is stored at chunk (c + 2*(kr % 4)) % 32, so the 4 k-rows read
 //            by one 16-lane group of a transpose read hit 4 distinct 32-byte bank groups.
 // Both are filled by direct global-to-LDS loads (buffer_load ... lds): lane L of a wave
 // writes 16 bytes at LDS base + 16 L, so each lane fetches the global chunk that belongs at
 // its LDS position and the swizzle lives entirely in the global offsets.
-constexpr int OPB = 256 * 128;  // bytes of one operand in one stage
+constexpr int KROW = BK * 2;          // bytes of one K-major tile row
+constexpr int OPB = 256 * BK * 2;     // bytes of one operand in one stage
+constexpr int LPW = OPB / 1024 / 4;   // direct-load instructions per operand per wave per step
+constexpr int LPS = 2 * LPW;          // ... for both operands
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int kswz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
+// Direct load of 16 bytes per lane into LDS at M0 + 16 * lane.  Issued through inline asm:
+// the compiler's own wait-count tracking of such loads cannot tell the pipeline stages apart
+// and would drain every stage in flight before each LDS read; the main loop waits for exactly
+// the stage it needs instead (wait_vm_lgkm0).  The loads are ordered like any volatile asm.
 __device__ __forceinline__ void lds_load16(rsrc_t r, char* lds_dst, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds_dst, 16, voff, soff, 0, 0);
+    const uint32_t m0 = (uint32_t)uni((int)(uint32_t)(uintptr_t)(lds_ptr)lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(r), "s"(soff)
+                 : "memory", "m0");
 }
 
 // Transposed 8-byte LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
@@ -100,54 +114,61 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
         (__attribute__((address_space(3))) i16x4*)(p));
 }
 
+// s_waitcnt: at most n vector-memory operations outstanding, no LDS operation outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
+
 __host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// Per-lane description of one operand's global->LDS loads (8 per wave per K step) and of
+// Per-lane description of one operand's global->LDS loads (LPW per wave per K step) and of
 // its MFMA fragment reads (4 sub-tiles of 32 rows per wave).
 struct Operand {
     rsrc_t r;
-    uint32_t voff[8];   // byte offset of this lane's 16-byte chunk, per load instruction
-    uint32_t kstep;     // byte advance of the global offset per K step
-    int ldsrow[8];      // LDS byte offset (within the operand's stage area) per load instruction
-    uint32_t rd[4];     // fragment-read base offset per sub-tile (K-major: row base | chunk bit)
-    int rs[4];          // K-major: swizzle bits 1-2 of the sub-tile's row
+    uint32_t voff[LPW];  // byte offset of this lane's 16-byte chunk, per load instruction
+    uint32_t kstep;      // byte advance of the global offset per K step
+    int ldsrow[LPW];     // LDS byte offset (within the operand's stage area) per instruction
+    uint32_t rd[4];      // fragment-read base offset per sub-tile
+    int rs[4];           // K-major: swizzle bit 1 of the sub-tile's row
 };
 
 // K-major operand.  rowmap(nn) gives the global row (relative to the descriptor base) of
-// tile row nn.  Each wave loads tile rows 64 w .. 64 w + 63 (eight 8-row instructions).
+// tile row nn.  Each wave loads 64 tile rows, 16 rows per instruction.
 template <typename RowMap>
 __device__ __forceinline__ void setup_kmajor(Operand& o, const void* base, uint32_t bytes, int ld,
                                              int wid, int lane, int wsub, RowMap rowmap) {
     o.r = make_rsrc(base, bytes);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = 64 * wid + 8 * i + (lane >> 3);
-        const int c = (lane & 7) ^ swz(r);
+    for (int i = 0; i < LPW; ++i) {
+        const int r = 64 * wid + 16 * i + (lane >> 2);
+        const int c = (lane & 3) ^ kswz(r);
         o.voff[i] = (uint32_t)rowmap(r) * (uint32_t)ld * 2u + (uint32_t)c * 16u;
-        o.ldsrow[i] = (64 * wid + 8 * i) * 128;
+        o.ldsrow[i] = (64 * wid + 16 * i) * KROW;
     }
     o.kstep = BK * 2;
     // fragment reads: lane reads row rb + lane%32, logical chunk 2 kk + lane/32
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int r = wsub + 32 * t + (lane & 31);
-        const int s = swz(r);
-        o.rd[t] = (uint32_t)(r * 128) | ((uint32_t)(((lane >> 5) ^ s) & 1) << 4);
-        o.rs[t] = s & 6;
+        const int s = kswz(r);
+        o.rd[t] = (uint32_t)(r * KROW) | ((uint32_t)(((lane >> 5) ^ s) & 1) << 4);
+        o.rs[t] = s & 2;
     }
 }
 
-// MN-major operand: element (mn, k) at base + k*ld + mn (bytes x2).  Each wave loads k-rows
-// 16 w .. 16 w + 15 of the step (eight 2-row instructions).
+// MN-major operand: element (mn, k) at base + k*ld + mn (bytes x2).  Each wave loads
+// BK/4 k-rows of the step, 2 per instruction.
 __device__ __forceinline__ void setup_mnmajor(Operand& o, const void* base, uint32_t bytes, int ld,
                                               int wid, int lane, int wsub) {
     o.r = make_rsrc(base, bytes);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int kr = 16 * wid + 2 * i + (lane >> 5);
+    for (int i = 0; i < LPW; ++i) {
+        const int kr = (BK / 4) * wid + 2 * i + (lane >> 5);
         const int c = ((lane & 31) - 2 * (kr & 3)) & 31;
         o.voff[i] = (uint32_t)kr * (uint32_t)ld * 2u + (uint32_t)c * 16u;
-        o.ldsrow[i] = (16 * wid + 2 * i) * 512;
+        o.ldsrow[i] = ((BK / 4) * wid + 2 * i) * 512;
     }
     o.kstep = (uint32_t)BK * (uint32_t)ld * 2u;
     // transpose reads: lane group g = lane/16, q = lane%4, j = (lane%16)/4 reads k-row
@@ -163,11 +184,10 @@ __device__ __forceinline__ void setup_mnmajor(Operand& o, const void* base, uint
     }
 }
 
-template <bool KMAJ>
 __device__ __forceinline__ void issue_loads(const Operand& o, char* stage_op, int ks) {
     const uint32_t so = (uint32_t)ks * o.kstep;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) lds_load16(o.r, stage_op + o.ldsrow[i], o.voff[i], so);
+    for (int i = 0; i < LPW; ++i) lds_load16(o.r, stage_op + o.ldsrow[i], o.voff[i], so);
 }
 
 // The 32x32x16 MFMA fragment of sub-tile t at k sub-step kk: 8 bf16 (k = 8 (lane/32) .. +7 of
@@ -189,10 +209,12 @@ __device__ __forceinline__ bf16x8 read_frag(const Operand& o, const char* stage_
 
 template <bool A_K, bool B_K, int EPI, bool GK>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
-    // two pipeline stages, as distinct arrays so that the compiler can tell a stage being
-    // filled by direct loads from the stage being read
+    // the pipeline stages, as distinct arrays so that the compiler can tell a stage being
+    // filled by direct loads from the stages being read
     __shared__ __attribute__((aligned(1024))) char st0[2 * OPB];
     __shared__ __attribute__((aligned(1024))) char st1[2 * OPB];
+    __shared__ __attribute__((aligned(1024))) char st2[2 * OPB];
+    __shared__ __attribute__((aligned(1024))) char st3[2 * OPB];
     __shared__ int s_tp[1024];
     __shared__ int s_total;
 
@@ -226,12 +248,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     }
     const int bid = blockIdx.x;
     if (bid >= total) return;
-    // XCD-aware renumbering: XCD x = bid % 8 takes a contiguous range of tile ids.
-    int logical;
-    {
-        int q = total >> 3, r = total & 7, x = bid & 7;
-        logical = x * q + min(x, r) + (bid >> 3);
-    }
+    // Tiles run in id order: the blocks in flight at once (spread over all XCDs) work on
+    // neighbouring tiles, which share operand panels in the shared last-level cache.
+    const int logical = bid;
     int e, t_local, Mrows, row0;
     if (ragged_m) {
         int lo = 0, hi = g.E - 1;
@@ -324,11 +343,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     // ---------------------------------------------------------------- main loop
-    // Per K step: 4 sub-steps of 16 k.  Fragments of sub-step kk+1 are read while the MFMAs of
-    // kk run; at the end of a step the barrier (all waves done reading this stage, all loads
-    // of the next stage landed) sits before the last sub-step's MFMAs, so the first fragments
-    // of the next step are read while they run.  The loads of step ks+2 go into the stage
-    // just freed, one step ahead of their use.
+    // NST stages in a ring: at the end of K step ks the stage it used is refilled with step
+    // ks + NST, so every load has NST - 1 steps to land.  Each step has KK sub-steps of 16 k;
+    // the fragments of sub-step kk+1 are read while the MFMAs of kk run, and the step barrier
+    // (every wave done reading this stage; step ks+1 landed) sits before the last sub-step's
+    // MFMAs, so the first fragments of the next step are read while they run.
     // The MFMA takes the B fragment as its first operand, so each lane's accumulators hold
     // one output row (m) and 4-column runs (n): the epilogue stores 8-byte vectors.
     const int nk = cdiv(Kdim, BK);
@@ -347,41 +366,52 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) fb[f][t] = read_frag<B_K>(ob, st + OPB, t, kk);
     };
-    // one K step from stage `cur` (`nxt` holds step ks+1 once the barrier passes)
+    auto load_step = [&](char* st, int ks) {
+        issue_loads(oa, st, ks);
+        issue_loads(ob, st + OPB, ks);
+    };
+    // wait until step ks+1 has landed: the loads issued after it (steps ks+2 ..
+    // min(ks+NST-1, nk-1)) may stay in flight
+    auto wait_next = [&](int ks) {
+        const int after = min(ks + NST - 1, nk - 1) - (ks + 1);
+        if (after >= 2) wait_vm_lgkm0<2 * LPS>();
+        else if (after == 1) wait_vm_lgkm0<LPS>();
+        else wait_vm_lgkm0<0>();
+    };
     auto kstep = [&](char* cur, char* nxt, int ks) {
-        reads(cur, 1, 1);
-        mfmas(0);
-        reads(cur, 2, 0);
-        mfmas(1);
-        reads(cur, 3, 1);
-        mfmas(0);
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of step ks+1 and its reads are done
-        __syncthreads();
-        if (ks + 2 < nk) {
-            issue_loads<A_K>(oa, cur, ks + 2);
-            issue_loads<B_K>(ob, cur + OPB, ks + 2);
+#pragma unroll
+        for (int kk = 1; kk < KK; ++kk) {
+            reads(cur, kk, kk & 1);
+            mfmas((kk - 1) & 1);
         }
+        wait_next(ks);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + NST < nk) load_step(cur, ks + NST);
         if (ks + 1 < nk) reads(nxt, 0, 0);
         // keep the loads and reads above issued before the MFMAs below
         __builtin_amdgcn_sched_barrier(0);
-        mfmas(1);
+        mfmas((KK - 1) & 1);
     };
+    static_assert(NST == 4, "the ring below is unrolled for 4 stages");
     if (nk > 0) {
-        issue_loads<A_K>(oa, st0, 0);
-        issue_loads<B_K>(ob, st0 + OPB, 0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (nk > 1) {
-            issue_loads<A_K>(oa, st1, 1);
-            issue_loads<B_K>(ob, st1 + OPB, 1);
-        }
+        load_step(st0, 0);
+        if (nk > 1) load_step(st1, 1);
+        if (nk > 2) load_step(st2, 2);
+        if (nk > 3) load_step(st3, 3);
+        if (nk > 3) wait_vm_lgkm0<3 * LPS>();  // step 0 landed; steps 1-3 may be in flight
+        else if (nk == 3) wait_vm_lgkm0<2 * LPS>();
+        else if (nk == 2) wait_vm_lgkm0<LPS>();
+        else wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
         reads(st0, 0, 0);
-        int ks = 0;
-        for (; ks + 1 < nk; ks += 2) {
+        for (int ks = 0; ks < nk; ks += NST) {
             kstep(st0, st1, ks);
-            kstep(st1, st0, ks + 1);
+            if (ks + 1 < nk) kstep(st1, st2, ks + 1);
+            if (ks + 2 < nk) kstep(st2, st3, ks + 2);
+            if (ks + 3 < nk) kstep(st3, st0, ks + 3);
         }
-        if (ks < nk) kstep(st0, st1, ks);
     }
 
     // ---------------------------------------------------------------- epilogue
@@ -475,10 +505,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 }
 
 // One kernel symbol per product of the layer, so that profiles name each role.
-#define MOE_GEMM_KERNEL(NAME, AK, BK, EPI, GK)                                         \
+#define MOE_GEMM_KERNEL(NAME, AKM, BKM, EPI, GK)                                       \
     __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) void \
     NAME(GemmArgs g) {                                                                 \
-        gemm_body<AK, BK, EPI, GK>(g);                                                 \
+        gemm_body<AKM, BKM, EPI, GK>(g);                                               \
     }
 MOE_GEMM_KERNEL(gemm1_swiglu, true, true, EPI_SWIGLU, false)     // [g|u] = Xp W1^T, h
 MOE_GEMM_KERNEL(gemm2_down, true, true, EPI_STORE, false)        // y = h W2^T
