@@ -80,8 +80,9 @@ struct GemmArgs {
 //            rows read by one 128-byte (8-lane) or 256-byte (16-lane) phase of a fragment read
 //            then hit distinct bank groups.
 //  MN-major  (operand contiguous along M or N): k-row kr is 512 bytes, 32 chunks of 8 m (n)
-//            values; chunk c is stored at chunk (c + 2*(kr % 4)) % 32, so the 4 k-rows read
-//            by one 16-lane group of a transpose read hit 4 distinct 32-byte bank groups.
+//            values; chunk c is stored at chunk c ^ mswz(kr % 4), mswz = {0, 6, 10, 12}, so
+//            the k-rows and columns read by one 16-lane (128-byte) or 32-lane (256-byte) phase
+//            of a transpose read hit distinct banks.
 // Both are filled by direct global-to-LDS loads (buffer_load ... lds): lane L of a wave
 // writes 16 bytes at LDS base + 16 L, so each lane fetches the global chunk that belongs at
 // its LDS position and the swizzle lives entirely in the global offsets.
@@ -91,6 +92,7 @@ constexpr int LPW = OPB / 1024 / 4;   // direct-load instructions per operand pe
 constexpr int LPS = 2 * LPW;          // ... for both operands
 
 __device__ __forceinline__ int kswz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+__device__ __forceinline__ int mswz(int kr) { return (0xCA60 >> (4 * (kr & 3))) & 15; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -99,12 +101,16 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // the compiler's own wait-count tracking of such loads cannot tell the pipeline stages apart
 // and would drain every stage in flight before each LDS read; the main loop waits for exactly
 // the stage it needs instead (wait_vm_lgkm0).  The loads are ordered like any volatile asm.
-__device__ __forceinline__ void lds_load16(rsrc_t r, char* lds_dst, uint32_t voff, uint32_t soff) {
-    const uint32_t m0 = (uint32_t)uni((int)(uint32_t)(uintptr_t)(lds_ptr)lds_dst);
+__device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t lds_dst, uint32_t voff, uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :
-                 : "s"(m0), "v"(voff), "s"(r), "s"(soff)
+                 : "s"(lds_dst), "v"(voff), "s"(r), "s"(soff)
                  : "memory", "m0");
+}
+
+// 32-bit LDS address of a __shared__ object (wave-uniform).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)uni((int)(uint32_t)(uintptr_t)(lds_ptr)p);
 }
 
 // Transposed 8-byte LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
@@ -166,7 +172,7 @@ __device__ __forceinline__ void setup_mnmajor(Operand& o, const void* base, uint
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
         const int kr = (BK / 4) * wid + 2 * i + (lane >> 5);
-        const int c = ((lane & 31) - 2 * (kr & 3)) & 31;
+        const int c = (lane & 31) ^ mswz(kr);
         o.voff[i] = (uint32_t)kr * (uint32_t)ld * 2u + (uint32_t)c * 16u;
         o.ldsrow[i] = ((BK / 4) * wid + 2 * i) * 512;
     }
@@ -178,16 +184,19 @@ __device__ __forceinline__ void setup_mnmajor(Operand& o, const void* base, uint
     for (int t = 0; t < 4; ++t) {
         const int mn = wsub + 32 * t + 16 * (gq & 1) + 4 * q;
         const int kr = 8 * (gq >> 1) + j;
-        const int pc = ((mn >> 3) + 2 * j) & 31;
+        const int pc = (mn >> 3) ^ mswz(j);
         o.rd[t] = (uint32_t)(kr * 512 + pc * 16 + 8 * (q & 1));
         o.rs[t] = 0;
     }
 }
 
-__device__ __forceinline__ void issue_loads(const Operand& o, char* stage_op, int ks) {
-    const uint32_t so = (uint32_t)ks * o.kstep;
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) lds_load16(o.r, stage_op + o.ldsrow[i], o.voff[i], so);
+// Load instruction i of K step ks into the operand's area of a stage.  Steps past the end
+// of K use an empty descriptor: the load still issues (so every step issues the same number
+// of loads and the wait counts are constants) but fetches nothing and writes zeros.
+__device__ __forceinline__ void issue_load(const Operand& o, uint32_t stage_op, int ks, int i,
+                                           bool live) {
+    const rsrc_t r = live ? o.r : make_rsrc(nullptr, 0);
+    lds_load16(r, stage_op + (uint32_t)o.ldsrow[i], o.voff[i], live ? (uint32_t)ks * o.kstep : 0u);
 }
 
 // The 32x32x16 MFMA fragment of sub-tile t at k sub-step kk: 8 bf16 (k = 8 (lane/32) .. +7 of
@@ -248,8 +257,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     }
     const int bid = blockIdx.x;
     if (bid >= total) return;
-    // Tiles run in id order: the blocks in flight at once (spread over all XCDs) work on
-    // neighbouring tiles, which share operand panels in the shared last-level cache.
+    // Tiles run in launch order: the blocks in flight at once, spread over all XCDs, work on
+    // neighbouring tiles whose operand panels meet in the shared last-level cache (measured
+    // faster than giving each XCD its own compact block of tiles).
     const int logical = bid;
     int e, t_local, Mrows, row0;
     if (ragged_m) {
@@ -344,74 +354,72 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 
     // ---------------------------------------------------------------- main loop
     // NST stages in a ring: at the end of K step ks the stage it used is refilled with step
-    // ks + NST, so every load has NST - 1 steps to land.  Each step has KK sub-steps of 16 k;
-    // the fragments of sub-step kk+1 are read while the MFMAs of kk run, and the step barrier
-    // (every wave done reading this stage; step ks+1 landed) sits before the last sub-step's
-    // MFMAs, so the first fragments of the next step are read while they run.
+    // ks + NST, so every load has NST - 1 steps to land.  A step is two sub-steps of 16 k
+    // (16 MFMAs each).  The LDS reads of the next sub-step's fragments and the global->LDS
+    // loads are interleaved one per MFMA, so they issue while the MFMA pipe is busy; the step
+    // barrier (all waves done reading this stage; step ks+1 landed) sits between the two
+    // sub-steps.  Fragment reads follow the order the MFMAs consume them.
     // The MFMA takes the B fragment as its first operand, so each lane's accumulators hold
     // one output row (m) and 4-column runs (n): the epilogue stores 8-byte vectors.
+    static_assert(KK == 2 && LPW == 4 && NST == 4, "the step below is written for these");
     const int nk = cdiv(Kdim, BK);
     bf16x8 fa[2][4], fb[2][4];
-    auto mfmas = [&](int f) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j],
-                                                                    0, 0, 0);
+    // read number r (0..7) of a sub-step, in MFMA consumption order: a0 b0 b1 b2 b3 a1 a2 a3
+    auto read_one = [&](const char* st, int kk, int f, int r) {
+        if (r == 0) fa[f][0] = read_frag<A_K>(oa, st, 0, kk);
+        else if (r <= 4) fb[f][r - 1] = read_frag<B_K>(ob, st + OPB, r - 1, kk);
+        else fa[f][r - 4] = read_frag<A_K>(oa, st, r - 4, kk);
     };
-    auto reads = [&](const char* st, int kk, int f) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) fa[f][t] = read_frag<A_K>(oa, st, t, kk);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) fb[f][t] = read_frag<B_K>(ob, st + OPB, t, kk);
+    auto mfma_one = [&](int f, int n) {
+        const int i = n >> 2, j = n & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0);
     };
-    auto load_step = [&](char* st, int ks) {
-        issue_loads(oa, st, ks);
-        issue_loads(ob, st + OPB, ks);
-    };
-    // wait until step ks+1 has landed: the loads issued after it (steps ks+2 ..
-    // min(ks+NST-1, nk-1)) may stay in flight
-    auto wait_next = [&](int ks) {
-        const int after = min(ks + NST - 1, nk - 1) - (ks + 1);
-        if (after >= 2) wait_vm_lgkm0<2 * LPS>();
-        else if (after == 1) wait_vm_lgkm0<LPS>();
-        else wait_vm_lgkm0<0>();
-    };
-    auto kstep = [&](char* cur, char* nxt, int ks) {
+    auto kstep = [&](char* cur, char* nxt, uint32_t cur32, int ks) {
+        // sub-step 0 (fragments f = 0) with the reads of sub-step 1
 #pragma unroll
-        for (int kk = 1; kk < KK; ++kk) {
-            reads(cur, kk, kk & 1);
-            mfmas((kk - 1) & 1);
+        for (int n = 0; n < 16; ++n) {
+            mfma_one(0, n);
+            if (n < 8) read_one(cur, 1, 1, n);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        wait_next(ks);
+        wait_vm_lgkm0<2 * LPS>();  // step ks+1 landed (steps ks+2, ks+3 may be in flight)
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        if (ks + NST < nk) load_step(cur, ks + NST);
-        if (ks + 1 < nk) reads(nxt, 0, 0);
-        // keep the loads and reads above issued before the MFMAs below
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas((KK - 1) & 1);
+        // sub-step 1 (f = 1) with the loads of step ks+NST into this stage and the reads of
+        // the next step's sub-step 0
+        const bool live = ks + NST < nk, more = ks + 1 < nk;
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+            mfma_one(1, n);
+            if (n < 4) issue_load(oa, cur32, ks + NST, n, live);
+            else if (n < 8) issue_load(ob, cur32 + OPB, ks + NST, n - 4, live);
+            else if (more) read_one(nxt, 0, 0, n - 8);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
-    static_assert(NST == 4, "the ring below is unrolled for 4 stages");
     if (nk > 0) {
-        load_step(st0, 0);
-        if (nk > 1) load_step(st1, 1);
-        if (nk > 2) load_step(st2, 2);
-        if (nk > 3) load_step(st3, 3);
-        if (nk > 3) wait_vm_lgkm0<3 * LPS>();  // step 0 landed; steps 1-3 may be in flight
-        else if (nk == 3) wait_vm_lgkm0<2 * LPS>();
-        else if (nk == 2) wait_vm_lgkm0<LPS>();
-        else wait_vm_lgkm0<0>();
+        const uint32_t a0 = lds_addr(st0), a1 = lds_addr(st1), a2 = lds_addr(st2),
+                       a3 = lds_addr(st3);
+        const uint32_t stg[NST] = {a0, a1, a2, a3};
+#pragma unroll
+        for (int p = 0; p < NST; ++p)
+#pragma unroll
+            for (int i = 0; i < LPW; ++i) {
+                issue_load(oa, stg[p], p, i, p < nk);
+                issue_load(ob, stg[p] + OPB, p, i, p < nk);
+            }
+        wait_vm_lgkm0<3 * LPS>();  // step 0 landed
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        reads(st0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) read_one(st0, 0, 0, r);
         for (int ks = 0; ks < nk; ks += NST) {
-            kstep(st0, st1, ks);
-            if (ks + 1 < nk) kstep(st1, st2, ks + 1);
-            if (ks + 2 < nk) kstep(st2, st3, ks + 2);
-            if (ks + 3 < nk) kstep(st3, st0, ks + 3);
+            kstep(st0, st1, a0, ks);
+            if (ks + 1 < nk) kstep(st1, st2, a1, ks + 1);
+            if (ks + 2 < nk) kstep(st2, st3, a2, ks + 2);
+            if (ks + 3 < nk) kstep(st3, st0, a3, ks + 3);
         }
+        wait_vm_lgkm0<0>();  // no load may still be writing LDS when the block ends
     }
 
     // ---------------------------------------------------------------- epilogue
