@@ -1,6 +1,6 @@
 // Grouped GEMMs of the expert FFN on gfx950 MFMA, forward and backward.
 //
-// One kernel template covers every product of the layer:
+// One tile routine covers every product of the layer:
 //   forward   GEMM1  [g|u] = Xp_e W1_e^T  with the SwiGLU epilogue (h, optional saved g/u)
 //             GEMM2  y = h_e W2_e^T
 //   backward  dgrad  dh = dy_e W2_e  with the SwiGLU-backward epilogue (dg, du)
@@ -13,18 +13,19 @@
 // Design (CDNA4, wave64):
 //  - 256x256 output tile per 256-thread block, 4 waves in 2x2, each wave a 128x128 sub-tile
 //    of 4x4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane, one wave per SIMD).
-//  - K steps of 64; operands staged global -> registers -> LDS, LDS double-buffered so one
-//    barrier per K step suffices; loads of step k+1 are in flight during the MFMAs of step k.
-//  - LDS rows are K-contiguous (16-byte chunks XOR-swizzled by row) so every MFMA operand is
-//    one conflict-free ds_read_b128.  Operands that are M- or N-contiguous in memory (the
-//    weights in dgrad, both operands in wgrad) are transposed 8x8 in registers on the way.
-//  - Global loads are raw buffer loads whose range check returns zeros past the end of an
-//    expert's rows, which pads ragged M tails and ragged K (wgrad) tails for free.
+//  - K steps of 32 through a ring of 4 LDS stages (128 KB), filled by direct global-to-LDS
+//    buffer loads three steps ahead of their use; one barrier per step.
+//  - Operands contiguous along K are read from LDS with ds_read_b128; operands contiguous
+//    along M or N (the weights in dgrad, both operands in wgrad) are stored as loaded and
+//    read with the transposing ds_read_b64_tr_b16.  Both LDS layouts are swizzled so that
+//    every read is free of bank conflicts.
+//  - Loads and LDS reads are interleaved one per MFMA.
+//  - Buffer loads return zeros past the end of an expert's rows, which pads ragged M tails
+//    and ragged K (wgrad) tails for free.
 //  - Expert tile lists are derived on the device from the offsets (no host readback): each
-//    block scans the per-expert tile counts in a wave and finds its tile.  Block b runs on
-//    XCD b % 8; tiles are renumbered so each XCD works on a contiguous range of the tile
-//    order, which is grouped 4 M-tiles at a time so concurrent tiles share A and B panels in
-//    that XCD's L2.
+//    block scans the per-expert tile counts in a wave and finds its tile.
+//  - The backward's independent dgrad/wgrad pairs share one launch each (bwd_down,
+//    bwd_gate_up), so that one fills the other's last partial round of tiles.
 #include "common.h"
 
 namespace moe {
@@ -40,9 +41,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
     const uint32_t hi = (uint32_t)uni((int)(uint32_t)(a >> 32));
     void* q = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
     return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, uni((int)bytes), 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
 constexpr int BM = 256, BN = 256, BK = 32, NTH = 256;
@@ -216,51 +214,60 @@ __device__ __forceinline__ bf16x8 read_frag(const Operand& o, const char* stage_
     }
 }
 
+// Shared memory of one GEMM block: the pipeline stages and the per-expert tile prefix.
+struct alignas(1024) GemmSmem {
+    char st[NST][2 * OPB];
+    int tp[1024];  // inclusive prefix sum of per-expert tile counts (ragged-M products)
+    int total;
+};
+
+template <int EPI>
+__device__ __forceinline__ int n_tiles(const GemmArgs& g) {
+    return (EPI == EPI_SWIGLU) ? cdiv(g.I, 128) : cdiv(g.N, BN);
+}
+
+// Tile count of a product.  Ragged-M products (expert rows from device offsets) count their
+// tiles on the device: the first wave scans the per-expert tile counts into sm.tp.
+template <int EPI, bool GK>
+__device__ __forceinline__ int tile_total(const GemmArgs& g, GemmSmem& sm) {
+    if (GK || g.offsets == nullptr) return g.total;
+    const int lane = threadIdx.x & 63;
+    const int NT = n_tiles<EPI>(g);
+    if (threadIdx.x < 64) {
+        int run = 0;
+        for (int base = 0; base < g.E; base += 64) {
+            int e = base + lane, tiles = 0;
+            if (e < g.E) {
+                int lo = min(max(g.offsets[e], 0), g.R);
+                int hi = min(max(g.offsets[e + 1], lo), g.R);
+                tiles = cdiv(hi - lo, BM) * NT;
+            }
+            int inc = wave_incl_scan(tiles) + run;
+            if (e < g.E) sm.tp[e] = inc;
+            run = __shfl(inc, 63, 64);
+        }
+        if (lane == 0) sm.total = run;
+    }
+    __syncthreads();
+    return uni(sm.total);
+}
+
+// One 256 x 256 output tile, number `logical` of the product (tiles run in launch order: the
+// blocks in flight at once, spread over all XCDs, work on neighbouring tiles whose operand
+// panels meet in the shared last-level cache, which measured faster than giving each XCD
+// its own compact block of tiles).
 template <bool A_K, bool B_K, int EPI, bool GK>
-__device__ __forceinline__ void gemm_body(const GemmArgs& g) {
-    // the pipeline stages, as distinct arrays so that the compiler can tell a stage being
-    // filled by direct loads from the stages being read
-    __shared__ __attribute__((aligned(1024))) char st0[2 * OPB];
-    __shared__ __attribute__((aligned(1024))) char st1[2 * OPB];
-    __shared__ __attribute__((aligned(1024))) char st2[2 * OPB];
-    __shared__ __attribute__((aligned(1024))) char st3[2 * OPB];
-    __shared__ int s_tp[1024];
-    __shared__ int s_total;
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const int logical) {
+    char* st0 = sm.st[0];
+    char* st1 = sm.st[1];
+    char* st2 = sm.st[2];
+    char* st3 = sm.st[3];
+    int* s_tp = sm.tp;
 
     const int tid = threadIdx.x, lane = tid & 63, wid = uni(tid >> 6);
     const int wm = wid >> 1, wn = wid & 1;
-    const int NT = (EPI == EPI_SWIGLU) ? cdiv(g.I, 128) : cdiv(g.N, BN);
-
-    // ---------------------------------------------------------------- locate the tile
-    int total;
+    const int NT = n_tiles<EPI>(g);
     const bool ragged_m = !GK && g.offsets != nullptr;
-    if (ragged_m) {
-        if (wid == 0) {
-            int run = 0;
-            for (int base = 0; base < g.E; base += 64) {
-                int e = base + lane, tiles = 0;
-                if (e < g.E) {
-                    int lo = min(max(g.offsets[e], 0), g.R);
-                    int hi = min(max(g.offsets[e + 1], lo), g.R);
-                    tiles = cdiv(hi - lo, BM) * NT;
-                }
-                int inc = wave_incl_scan(tiles) + run;
-                if (e < g.E) s_tp[e] = inc;
-                run = __shfl(inc, 63, 64);
-            }
-            if (lane == 0) s_total = run;
-        }
-        __syncthreads();
-        total = uni(s_total);
-    } else {
-        total = g.total;
-    }
-    const int bid = blockIdx.x;
-    if (bid >= total) return;
-    // Tiles run in launch order: the blocks in flight at once, spread over all XCDs, work on
-    // neighbouring tiles whose operand panels meet in the shared last-level cache (measured
-    // faster than giving each XCD its own compact block of tiles).
-    const int logical = bid;
     int e, t_local, Mrows, row0;
     if (ragged_m) {
         int lo = 0, hi = g.E - 1;
@@ -516,15 +523,36 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 #define MOE_GEMM_KERNEL(NAME, AKM, BKM, EPI, GK)                                       \
     __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) void \
     NAME(GemmArgs g) {                                                                 \
-        gemm_body<AKM, BKM, EPI, GK>(g);                                               \
+        __shared__ GemmSmem sm;                                                        \
+        const int total = tile_total<EPI, GK>(g, sm);                                  \
+        if ((int)blockIdx.x < total) gemm_tile<AKM, BKM, EPI, GK>(g, sm, blockIdx.x);  \
     }
 MOE_GEMM_KERNEL(gemm1_swiglu, true, true, EPI_SWIGLU, false)     // [g|u] = Xp W1^T, h
 MOE_GEMM_KERNEL(gemm2_down, true, true, EPI_STORE, false)        // y = h W2^T
-MOE_GEMM_KERNEL(dgrad_down_dswiglu, true, false, EPI_DSWIGLU, false)  // dh = dy W2 -> dg|du
-MOE_GEMM_KERNEL(dgrad_gate_up, true, false, EPI_STORE, false)    // dXp = dGU W1
-MOE_GEMM_KERNEL(wgrad_down, false, false, EPI_STORE, true)       // dW2 = dy^T h
-MOE_GEMM_KERNEL(wgrad_gate_up, false, false, EPI_STORE, true)    // dW1 = dGU^T Xp
 #undef MOE_GEMM_KERNEL
+
+// The backward's two pairs of independent products run as one launch each, the dgrad tiles
+// first and the wgrad tiles after them, so that the second product fills the last,
+// partly empty round of the first (256 CUs, one tile each at a time).
+//   bwd_down:     dh = dy W2 -> dg|du (SwiGLU backward)   and   dW2 = dy^T h
+//   bwd_gate_up:  dXp = dGU W1                           and   dW1 = dGU^T Xp
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_down(GemmArgs gd, GemmArgs gw) {
+    __shared__ GemmSmem sm;
+    const int td = tile_total<EPI_DSWIGLU, false>(gd, sm);
+    const int b = blockIdx.x;
+    if (b < td) gemm_tile<true, false, EPI_DSWIGLU, false>(gd, sm, b);
+    else if (b - td < gw.total) gemm_tile<false, false, EPI_STORE, true>(gw, sm, b - td);
+}
+
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_gate_up(GemmArgs gd, GemmArgs gw) {
+    __shared__ GemmSmem sm;
+    const int td = tile_total<EPI_STORE, false>(gd, sm);
+    const int b = blockIdx.x;
+    if (b < td) gemm_tile<true, false, EPI_STORE, false>(gd, sm, b);
+    else if (b - td < gw.total) gemm_tile<false, false, EPI_STORE, true>(gw, sm, b - td);
+}
 
 // Upper bound on the tile count of a ragged-M product (host side, no device data).
 static int ragged_tiles_bound(int R, int E, int NT) {
@@ -532,15 +560,27 @@ static int ragged_tiles_bound(int R, int E, int NT) {
     return (int)(mt * NT);
 }
 
-template <int EPI, bool GK>
-static int launch(void (*kern)(GemmArgs), const char* name, const GemmArgs& g, hipStream_t st) {
-    int NT = (EPI == EPI_SWIGLU) ? cdiv(g.I, 128) : cdiv(g.N, BN);
-    int grid;
-    if (GK) grid = g.total;
-    else if (g.offsets) grid = ragged_tiles_bound(g.R, g.E, NT);
-    else grid = g.total;
+// Blocks to launch for a product: its tile count, or for ragged-M products an upper bound
+// (surplus blocks exit at once).
+static int grid_of(const GemmArgs& g, int NT, bool GK) {
+    if (GK || !g.offsets) return g.total;
+    return ragged_tiles_bound(g.R, g.E, NT);
+}
+
+static int launch(void (*kern)(GemmArgs), const char* name, const GemmArgs& g, int NT,
+                  hipStream_t st) {
+    const int grid = grid_of(g, NT, false);
     if (grid <= 0) return MOE_OK;
     MOE_TRACED(name, st, kern<<<grid, NTH, 0, st>>>(g));
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+static int launch_pair(void (*kern)(GemmArgs, GemmArgs), const char* name, const GemmArgs& gd,
+                       const GemmArgs& gw, hipStream_t st) {
+    const int grid = grid_of(gd, cdiv(gd.N, BN), false) + gw.total;
+    if (grid <= 0) return MOE_OK;
+    MOE_TRACED(name, st, kern<<<grid, NTH, 0, st>>>(gd, gw));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -567,7 +607,7 @@ int moe_ffn_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, 
     g.C2 = gu; g.c2_es = shared ? (int64_t)R * 2 * I : 0; g.ldc2 = 2 * I;
     g.offsets = offsets; g.E = E; g.R = R; g.N = 2 * I; g.K = H; g.I = I;
     g.total = shared ? E * cdiv(R, BM) * cdiv(I, 128) : 0;
-    int rc = launch<EPI_SWIGLU, false>(gemm1_swiglu, "gemm1_swiglu", g, st);
+    int rc = launch(gemm1_swiglu, "gemm1_swiglu", g, cdiv(I, 128), st);
     if (rc) return rc;
     GemmArgs g2 = blank();
     g2.A = h; g2.a_es = shared ? (int64_t)R * I : 0; g2.lda = I;
@@ -575,7 +615,7 @@ int moe_ffn_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, 
     g2.C = y; g2.c_es = shared ? (int64_t)R * H : 0; g2.ldc = H;
     g2.offsets = offsets; g2.E = E; g2.R = R; g2.N = H; g2.K = I; g2.I = I;
     g2.total = shared ? E * cdiv(R, BM) * cdiv(H, BN) : 0;
-    return launch<EPI_STORE, false>(gemm2_down, "gemm2_down", g2, st);
+    return launch(gemm2_down, "gemm2_down", g2, cdiv(H, BN), st);
 }
 
 // Backward of the FFN for one group of experts.
@@ -588,46 +628,38 @@ int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int
                      hipStream_t st) {
     const bool shared = offsets == nullptr;
     int rc;
-    {   // dh = dy_e W2_e (W2_e is [H,I]: N-contiguous in I), SwiGLU backward -> dgu
-        GemmArgs g = blank();
-        g.A = dy; g.a_es = 0; g.lda = H;
-        g.B = w2; g.b_es = (int64_t)H * I; g.ldb = I; g.b_rows = H;
-        g.C = dgu; g.c_es = shared ? (int64_t)R * 2 * I : 0; g.ldc = 2 * I;
-        g.C2 = const_cast<bf16_t*>(gu); g.c2_es = shared ? (int64_t)R * 2 * I : 0; g.ldc2 = 2 * I;
-        g.offsets = offsets; g.E = E; g.R = R; g.N = I; g.K = H; g.I = I;
-        g.total = shared ? E * cdiv(R, BM) * cdiv(I, BN) : 0;
-        rc = launch<EPI_DSWIGLU, false>(dgrad_down_dswiglu, "dgrad_down_dswiglu", g, st);
-        if (rc) return rc;
-    }
-    {   // dXp = dGU_e W1_e (W1_e is [2I,H]: N-contiguous in H)
-        GemmArgs g = blank();
-        g.A = dgu; g.a_es = shared ? (int64_t)R * 2 * I : 0; g.lda = 2 * I;
-        g.B = w1; g.b_es = (int64_t)2 * I * H; g.ldb = H; g.b_rows = 2 * I;
-        g.C = dxp; g.c_es = shared ? (int64_t)R * H : 0; g.ldc = H;
-        g.offsets = offsets; g.E = E; g.R = R; g.N = H; g.K = 2 * I; g.I = I;
-        g.total = shared ? E * cdiv(R, BM) * cdiv(H, BN) : 0;
-        rc = launch<EPI_STORE, false>(dgrad_gate_up, "dgrad_gate_up", g, st);
-        if (rc) return rc;
-    }
-    {   // dW2_e = dy_e^T h_e: M = H, N = I, K = the expert's rows
-        GemmArgs g = blank();
-        g.A = dy; g.a_es = 0; g.lda = H;
-        g.B = h; g.b_es = shared ? (int64_t)R * I : 0; g.ldb = I;
-        g.C = dw2; g.c_es = (int64_t)H * I; g.ldc = I;
-        g.offsets = offsets; g.E = E; g.R = R; g.M = H; g.N = I; g.I = I;
-        g.total = E * cdiv(H, BM) * cdiv(I, BN);
-        rc = launch<EPI_STORE, true>(wgrad_down, "wgrad_down", g, st);
-        if (rc) return rc;
-    }
-    {   // dW1_e = dGU_e^T Xp_e: M = 2I, N = H
-        GemmArgs g = blank();
-        g.A = dgu; g.a_es = shared ? (int64_t)R * 2 * I : 0; g.lda = 2 * I;
-        g.B = xp; g.b_es = 0; g.ldb = H;
-        g.C = dw1; g.c_es = (int64_t)2 * I * H; g.ldc = H;
-        g.offsets = offsets; g.E = E; g.R = R; g.M = 2 * I; g.N = H; g.I = I;
-        g.total = E * cdiv(2 * I, BM) * cdiv(H, BN);
-        rc = launch<EPI_STORE, true>(wgrad_gate_up, "wgrad_gate_up", g, st);
-        if (rc) return rc;
-    }
+    // dh = dy_e W2_e (W2_e is [H,I]: N-contiguous in I), SwiGLU backward -> dgu
+    GemmArgs gd = blank();
+    gd.A = dy; gd.a_es = 0; gd.lda = H;
+    gd.B = w2; gd.b_es = (int64_t)H * I; gd.ldb = I; gd.b_rows = H;
+    gd.C = dgu; gd.c_es = shared ? (int64_t)R * 2 * I : 0; gd.ldc = 2 * I;
+    gd.C2 = const_cast<bf16_t*>(gu); gd.c2_es = shared ? (int64_t)R * 2 * I : 0; gd.ldc2 = 2 * I;
+    gd.offsets = offsets; gd.E = E; gd.R = R; gd.N = I; gd.K = H; gd.I = I;
+    gd.total = shared ? E * cdiv(R, BM) * cdiv(I, BN) : 0;
+    // dW2_e = dy_e^T h_e: M = H, N = I, K = the expert's rows
+    GemmArgs gw = blank();
+    gw.A = dy; gw.a_es = 0; gw.lda = H;
+    gw.B = h; gw.b_es = shared ? (int64_t)R * I : 0; gw.ldb = I;
+    gw.C = dw2; gw.c_es = (int64_t)H * I; gw.ldc = I;
+    gw.offsets = offsets; gw.E = E; gw.R = R; gw.M = H; gw.N = I; gw.I = I;
+    gw.total = E * cdiv(H, BM) * cdiv(I, BN);
+    rc = launch_pair(bwd_down, "bwd_down", gd, gw, st);
+    if (rc) return rc;
+    // dXp = dGU_e W1_e (W1_e is [2I,H]: N-contiguous in H)
+    GemmArgs gd2 = blank();
+    gd2.A = dgu; gd2.a_es = shared ? (int64_t)R * 2 * I : 0; gd2.lda = 2 * I;
+    gd2.B = w1; gd2.b_es = (int64_t)2 * I * H; gd2.ldb = H; gd2.b_rows = 2 * I;
+    gd2.C = dxp; gd2.c_es = shared ? (int64_t)R * H : 0; gd2.ldc = H;
+    gd2.offsets = offsets; gd2.E = E; gd2.R = R; gd2.N = H; gd2.K = 2 * I; gd2.I = I;
+    gd2.total = shared ? E * cdiv(R, BM) * cdiv(H, BN) : 0;
+    // dW1_e = dGU_e^T Xp_e: M = 2I, N = H
+    GemmArgs gw2 = blank();
+    gw2.A = dgu; gw2.a_es = shared ? (int64_t)R * 2 * I : 0; gw2.lda = 2 * I;
+    gw2.B = xp; gw2.b_es = 0; gw2.ldb = H;
+    gw2.C = dw1; gw2.c_es = (int64_t)2 * I * H; gw2.ldc = H;
+    gw2.offsets = offsets; gw2.E = E; gw2.R = R; gw2.M = 2 * I; gw2.N = H; gw2.I = I;
+    gw2.total = E * cdiv(2 * I, BM) * cdiv(H, BN);
+    rc = launch_pair(bwd_gate_up, "bwd_gate_up", gd2, gw2, st);
+    if (rc) return rc;
     return MOE_OK;
 }
