@@ -57,6 +57,9 @@ def parse():
                     help="source tokens of the CPU-oracle sample")
     ap.add_argument("--breakdown", action="store_true",
                     help="also print per-role times to stderr")
+    ap.add_argument("--ring-depth", type=int, default=16,
+                    help="minibatches per pass of the macrobatch ring (workloads that stream "
+                         "tokens in minibatches)")
     return ap.parse_args()
 
 
@@ -181,7 +184,8 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     inp = wk.make_inputs(wl, device=dev)
-    layer = MoELayer(LayerCfg.from_workload(wl), inp, dev, backward=wl.backward)
+    ring = dict(minibatch=wl.minibatch, ring_depth=a.ring_depth) if wl.minibatch else {}
+    layer = MoELayer(LayerCfg.from_workload(wl), inp, dev, backward=wl.backward, **ring)
 
     def step():
         layer.forward()
@@ -193,7 +197,7 @@ def main():
     torch.cuda.synchronize()
 
     # timed: K whole steps, with per-launch events recorded by the library
-    moe.trace_begin(max(64, 64 * a.steps))
+    moe.trace_begin(max(512, 512 * a.steps))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(a.steps):
@@ -248,6 +252,8 @@ def main():
            "n_groups": wl.n_groups, "topk_groups": wl.topk_groups,
            "precision": "mxfp8" if wl.mx else "bf16", "backward": wl.backward,
            "parallelism": "none (one GPU's share)"}
+    if layer.ring:
+        cfg.update(minibatch=layer.mb, ring_depth=layer.D, ring_passes=layer.passes)
     out = {
         "metric": METRIC,
         "value": round(wl.T * a.steps / elapsed, 1),

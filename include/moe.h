@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* return codes */
 #define MOE_OK 0
@@ -178,6 +178,13 @@ typedef struct moe_bwd_args {
     void *dws1, *dws2;          /* [S,2Is,H], [S,H,Is] bf16 (NULL when S = 0) */
     float *dw_route;            /* [T,k] fp32: dL/dw[t,j] = <dout[t], y[pos[t,j]]> */
     float *dlogits;             /* [T,E_router] fp32 */
+    /* Macrobatch walked in passes (aiexpert.news ¶4: a fixed ring buffer walked at minibatch
+     * granularity).  passes <= 1: one pass, offsets [E+1], pos rows in [0,R).  passes > 1: the
+     * tokens form consecutive passes of pass_tokens tokens (the last may hold fewer); pass p's
+     * routed rows occupy rows [p*pass_rows, (p+1)*pass_rows) of xp, gu, h and y, offsets is
+     * [passes][E+1] and pos holds rows local to the token's pass.  Weight gradients reduce
+     * over the rows of every pass, in pass order.  R must equal passes * pass_rows. */
+    int passes, pass_tokens, pass_rows;
 } moe_bwd_args;
 
 size_t moe_backward_workspace_size(const moe_bwd_args *a);

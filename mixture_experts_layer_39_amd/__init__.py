@@ -43,7 +43,11 @@ class BwdArgs(ctypes.Structure):
                [(n, _vp) for n in ("x", "xp", "gu", "h", "y", "offsets", "pos", "idx", "w",
                                    "s_sel", "logits", "w1", "w2", "gus", "hs", "ws1", "ws2",
                                    "dout", "dx", "dw1", "dw2", "dws1", "dws2", "dw_route",
-                                   "dlogits")]
+                                   "dlogits")] + \
+               [(n, _i) for n in ("passes", "pass_tokens", "pass_rows")]
+
+_INT_FIELDS = ("T", "H", "E", "k", "I", "R", "S", "Is", "E_router", "score", "renorm", "passes",
+               "pass_tokens", "pass_rows")
 
 
 _lib = None
@@ -165,8 +169,7 @@ def bwd_args(**kw) -> BwdArgs:
             continue
         if name == "route_scale":
             a.route_scale = float(v)
-        elif isinstance(v, (bool, int)) and name in ("T", "H", "E", "k", "I", "R", "S", "Is",
-                                                      "E_router", "score", "renorm"):
+        elif isinstance(v, (bool, int)) and name in _INT_FIELDS:
             setattr(a, name, int(v))
         else:
             setattr(a, name, v if isinstance(v, int) else v.data_ptr())

@@ -13,7 +13,7 @@ int moe_ffn_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, 
                  hipStream_t st);
 int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, int I,
                      const bf16_t* w1, const bf16_t* w2, const bf16_t* gu, const bf16_t* h,
-                     const bf16_t* dy, bf16_t* dgu, bf16_t* dxp, bf16_t* dw1, bf16_t* dw2,
+                     const bf16_t* dy, bf16_t* dgu, bf16_t* dxp, const MoeWgradSpan* wg,
                      hipStream_t st);
 int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int E, int R, int H,
                int I, const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q,
@@ -21,7 +21,7 @@ int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int
 int moe_launch_combine_bwd(const bf16_t* dout, const bf16_t* y, const int32_t* pos, const float* w,
                            int T, int k, int H, int R, bf16_t* dy, float* dw, hipStream_t st);
 int moe_launch_unpermute(const bf16_t* dxp, const int32_t* pos, int T, int k, int H, int R,
-                         const bf16_t* dxs, int S, bf16_t* dx, hipStream_t st);
+                         const bf16_t* dxs, int S, int ldT, bf16_t* dx, hipStream_t st);
 int moe_launch_router_bwd(const int32_t* idx, const float* w, const float* s_sel, const float* dw,
                           const float* logits, int T, int E, int k, int score, int renorm, float c,
                           float* dL, hipStream_t st);
@@ -195,6 +195,15 @@ extern "C" int moe_backward(const moe_bwd_args* a, void* ws, size_t ws_bytes, vo
     MOE_REQUIRE(a->E_router >= 1 && a->E_router <= 1024);
     MOE_REQUIRE(a->score == MOE_SCORE_SOFTMAX || a->score == MOE_SCORE_SIGMOID);
     MOE_REQUIRE((int64_t)a->R * a->H < (1ll << 31) && (int64_t)a->T * a->H < (1ll << 31));
+    const int passes = a->passes < 1 ? 1 : a->passes;
+    if (passes > 1) {
+        // every pass but the last holds exactly pass_tokens tokens; R spans all pass regions
+        MOE_REQUIRE(a->pass_tokens >= 1 && a->pass_rows >= 0 && passes <= 4096);
+        MOE_REQUIRE((int64_t)passes * a->pass_rows == a->R);
+        MOE_REQUIRE((int64_t)(passes - 1) * a->pass_tokens < a->T &&
+                    a->T <= (int64_t)passes * a->pass_tokens);
+        MOE_REQUIRE((int64_t)a->pass_tokens * a->k <= a->pass_rows);
+    }
     if (a->T > 0) {
         MOE_REQUIRE(a->xp && a->gu && a->h && a->y && a->offsets && a->pos && a->idx && a->w &&
                     a->s_sel && a->w1 && a->w2 && a->dout && a->dx && a->dw1 && a->dw2 &&
@@ -215,29 +224,45 @@ extern "C" int moe_backward(const moe_bwd_args* a, void* ws, size_t ws_bytes, vo
     bf16_t* dxp = (bf16_t*)(base + L.dxp);
     bf16_t* dgus = (bf16_t*)(base + L.dgus);
     bf16_t* dxs = (bf16_t*)(base + L.dxs);
-    // combine backward: dy rows and the routing-weight gradient
-    rc = moe_launch_combine_bwd((const bf16_t*)a->dout, (const bf16_t*)a->y, a->pos, a->w, a->T,
-                                a->k, a->H, a->R, dy, a->dw_route, st);
-    if (rc) return rc;
-    // routed experts
-    if (a->R > 0) {
-        rc = moe_ffn_bwd_bf16((const bf16_t*)a->xp, a->offsets, a->E, a->R, a->H, a->I,
-                              (const bf16_t*)a->w1, (const bf16_t*)a->w2, (const bf16_t*)a->gu,
-                              (const bf16_t*)a->h, dy, dgu, dxp, (bf16_t*)a->dw1,
-                              (bf16_t*)a->dw2, st);
-        if (rc) return rc;
-    }
+    const int H = a->H, I = a->I, k = a->k, E = a->E;
     // shared experts: gradient dout with weight one, input x, every expert takes all T rows
     if (a->S > 0) {
-        rc = moe_ffn_bwd_bf16((const bf16_t*)a->x, nullptr, a->S, a->T, a->H, a->Is,
+        MoeWgradSpan sw{(const bf16_t*)a->x, (const bf16_t*)a->hs, (const bf16_t*)a->dout, dgus,
+                        nullptr, 1, 0, a->T, (bf16_t*)a->dws1, (bf16_t*)a->dws2};
+        rc = moe_ffn_bwd_bf16((const bf16_t*)a->x, nullptr, a->S, a->T, H, a->Is,
                               (const bf16_t*)a->ws1, (const bf16_t*)a->ws2, (const bf16_t*)a->gus,
-                              (const bf16_t*)a->hs, (const bf16_t*)a->dout, dgus, dxs,
-                              (bf16_t*)a->dws1, (bf16_t*)a->dws2, st);
+                              (const bf16_t*)a->hs, (const bf16_t*)a->dout, dgus, dxs, &sw, st);
         if (rc) return rc;
     }
-    rc = moe_launch_unpermute(dxp, a->pos, a->T, a->k, a->H, a->R, a->S ? dxs : nullptr, a->S,
-                              (bf16_t*)a->dx, st);
-    if (rc) return rc;
+    // routed experts, one pass at a time (a macrobatch walked in passes keeps each pass's
+    // rows in its own region); the weight gradients over every pass run with the last pass
+    const int prow = passes > 1 ? a->pass_rows : a->R;
+    const int ptok = passes > 1 ? a->pass_tokens : a->T;
+    MoeWgradSpan wg{(const bf16_t*)a->xp, (const bf16_t*)a->h, dy, dgu, a->offsets, passes,
+                    passes > 1 ? a->pass_rows : 0, a->R, (bf16_t*)a->dw1, (bf16_t*)a->dw2};
+    for (int p = 0; p < passes; ++p) {
+        const int t0 = p * ptok, Tp = min(ptok, a->T - t0);
+        const size_t r0 = (size_t)p * prow;
+        const bf16_t* dout_p = (const bf16_t*)a->dout + (size_t)t0 * H;
+        const int32_t* pos_p = a->pos + (size_t)t0 * k;
+        // combine backward: dy rows of the pass and the routing-weight gradient of its tokens
+        rc = moe_launch_combine_bwd(dout_p, (const bf16_t*)a->y + r0 * H, pos_p,
+                                    a->w + (size_t)t0 * k, Tp, k, H, prow, dy + r0 * H,
+                                    a->dw_route + (size_t)t0 * k, st);
+        if (rc) return rc;
+        if (prow > 0) {
+            rc = moe_ffn_bwd_bf16((const bf16_t*)a->xp + r0 * H, a->offsets + (size_t)p * (E + 1),
+                                  E, prow, H, I, (const bf16_t*)a->w1, (const bf16_t*)a->w2,
+                                  (const bf16_t*)a->gu + r0 * 2 * I, (const bf16_t*)a->h + r0 * I,
+                                  dy + r0 * H, dgu + r0 * 2 * I, dxp + r0 * H,
+                                  p == passes - 1 ? &wg : nullptr, st);
+            if (rc) return rc;
+        }
+        rc = moe_launch_unpermute(dxp + r0 * H, pos_p, Tp, k, H, prow,
+                                  a->S ? dxs + (size_t)t0 * H : nullptr, a->S, a->T,
+                                  (bf16_t*)a->dx + (size_t)t0 * H, st);
+        if (rc) return rc;
+    }
     return moe_launch_router_bwd(a->idx, a->w, a->s_sel, a->dw_route, a->logits, a->T, a->E_router,
                                  a->k, a->score, a->renorm, a->route_scale, a->dlogits, st);
 }

@@ -72,6 +72,21 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
         if (hipGetLastError() != hipSuccess) return MOE_EHIP;   \
     } while (0)
 
+// Rows the weight-gradient products of the backward reduce over: the routed rows of every
+// pass of a macrobatch (pass p's rows start at row p * pass_rows; offsets [P][E+1] are
+// pass-local), or of one pass (P = 1, offsets [E+1]), or all R rows (offsets null: shared
+// experts).
+struct MoeWgradSpan {
+    const moe::bf16_t* xp;
+    const moe::bf16_t* h;
+    const moe::bf16_t* dy;
+    const moe::bf16_t* dgu;
+    const int32_t* offsets;
+    int P, pass_rows, R;
+    moe::bf16_t* dw1;
+    moe::bf16_t* dw2;
+};
+
 // Returns MOE_OK when the current device is gfx950 (cached per device).
 int moe_check_device();
 

@@ -69,6 +69,11 @@ struct GemmArgs {
     int I;        // SwiGLU channels
     int b_rows;   // rows of B per expert (K-contiguous B) or K (N-contiguous B)
     int total;    // tile count when it is static (ragged-K or shared mode)
+    // wgrad over a macrobatch walked in P passes: offsets is [P][E+1] (pass-local rows) and
+    // pass p's rows start at row p * pass_rows of A and B; the K loop of a tile walks the
+    // expert's rows of every pass in pass order.  P = 1: one pass, offsets [E+1].
+    int P;
+    int pass_rows;
 };
 
 // ---------------------------------------------------------------- LDS tiles
@@ -191,10 +196,14 @@ __device__ __forceinline__ void setup_mnmajor(Operand& o, const void* base, uint
 // Load instruction i of K step ks into the operand's area of a stage.  Steps past the end
 // of K use an empty descriptor: the load still issues (so every step issues the same number
 // of loads and the wait counts are constants) but fetches nothing and writes zeros.
-__device__ __forceinline__ void issue_load(const Operand& o, uint32_t stage_op, int ks, int i,
-                                           bool live) {
-    const rsrc_t r = live ? o.r : make_rsrc(nullptr, 0);
-    lds_load16(r, stage_op + (uint32_t)o.ldsrow[i], o.voff[i], live ? (uint32_t)ks * o.kstep : 0u);
+__device__ __forceinline__ void issue_load(const Operand& o, uint32_t stage_op, int i, rsrc_t r,
+                                           uint32_t soff) {
+    lds_load16(r, stage_op + (uint32_t)o.ldsrow[i], o.voff[i], soff);
+}
+
+// Bytes of an MN-major operand range: `rows` k-rows of `ld` elements from column offset m0.
+__device__ __forceinline__ uint32_t mn_bytes(int rows, int ld, int m0) {
+    return (uint32_t)max((int64_t)rows * ld * 2 - (int64_t)m0 * 2, (int64_t)0);
 }
 
 // The 32x32x16 MFMA fragment of sub-tile t at k sub-step kk: 8 bf16 (k = 8 (lane/32) .. +7 of
@@ -287,10 +296,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         t_local = logical - e * per;
         if (GK) {
             if (g.offsets) {
-                int a = min(max(g.offsets[e], 0), g.R);
-                int b = min(max(g.offsets[e + 1], a), g.R);
+                // K extent: the expert's rows (of the first pass when P > 1)
+                const int lim = g.P > 1 ? g.pass_rows : g.R;
+                int a = min(max(g.offsets[e], 0), lim);
+                int b = min(max(g.offsets[e + 1], a), lim);
                 row0 = uni(a);
-                Mrows = uni(b - a);  // here: the K extent (rows of the expert)
+                Mrows = uni(b - a);
             } else {
                 row0 = 0;
                 Mrows = g.R;
@@ -329,8 +340,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
                      lane, wm * 128, [](int r) { return r; });
     } else {
         const bf16_t* base = g.A + e * g.a_es + (int64_t)row0 * g.lda + m0;
-        setup_mnmajor(oa, base, (uint32_t)Kdim * (uint32_t)g.lda * 2u - (uint32_t)m0 * 2u, g.lda,
-                      wid, lane, wm * 128);
+        setup_mnmajor(oa, base, mn_bytes(Kdim, g.lda, m0), g.lda, wid, lane, wm * 128);
     }
     if (B_K) {
         const bf16_t* base = g.B + e * g.b_es;
@@ -347,8 +357,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     } else {
         const int64_t kbase = GK ? row0 : 0;
         const bf16_t* base = g.B + e * g.b_es + kbase * g.ldb + n0;
-        setup_mnmajor(ob, base, (uint32_t)Kdim * (uint32_t)g.ldb * 2u - (uint32_t)n0 * 2u, g.ldb,
-                      wid, lane, wn * 128);
+        setup_mnmajor(ob, base, mn_bytes(Kdim, g.ldb, n0), g.ldb, wid, lane, wn * 128);
     }
 
     f32x16 acc[4][4];
@@ -369,7 +378,57 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     // The MFMA takes the B fragment as its first operand, so each lane's accumulators hold
     // one output row (m) and 4-column runs (n): the epilogue stores 8-byte vectors.
     static_assert(KK == 2 && LPW == 4 && NST == 4, "the step below is written for these");
-    const int nk = cdiv(Kdim, BK);
+    // K segments: one, except for wgrad over P > 1 passes (the expert's rows of each pass)
+    const int P = (GK && g.offsets) ? max(g.P, 1) : 1;
+    auto seg = [&](int p, int& first, int& len) {
+        const int32_t* off = g.offsets + (int64_t)p * (g.E + 1);
+        const int a = min(max(off[e], 0), g.pass_rows);
+        const int b = min(max(off[e + 1], a), g.pass_rows);
+        first = uni(p * g.pass_rows + a);
+        len = uni(b - a);
+    };
+    int nk = cdiv(Kdim, BK);
+    if (P > 1) {
+        for (int p = 1; p < P; ++p) {
+            int f, l;
+            seg(p, f, l);
+            nk += cdiv(l, BK);
+        }
+    }
+    // The load cursor: the segment holding the K step being loaded (steps are loaded in
+    // increasing order).  Each segment has its own buffer descriptors, so the K tail of
+    // every segment reads zeros.
+    int cur_p = 0, cur_start = 0, cur_steps = cdiv(Kdim, BK);
+    const rsrc_t rnull = make_rsrc(nullptr, 0);
+    auto load_src = [&](int ks, rsrc_t& ra_, rsrc_t& rb_, uint32_t& sa, uint32_t& sb) {
+        if (ks >= nk) {  // past the end: empty descriptors (the load writes zeros)
+            ra_ = rnull;
+            rb_ = rnull;
+            sa = sb = 0;
+            return;
+        }
+        if (P > 1 && ks >= cur_start + cur_steps) {
+            int p = cur_p, start = cur_start + cur_steps, f = 0, l = 0;
+            for (;;) {
+                ++p;
+                seg(p, f, l);
+                const int st = cdiv(l, BK);
+                if (ks < start + st) {
+                    cur_steps = st;
+                    break;
+                }
+                start += st;
+            }
+            cur_p = p;
+            cur_start = start;
+            oa.r = make_rsrc(g.A + e * g.a_es + (int64_t)f * g.lda + m0, mn_bytes(l, g.lda, m0));
+            ob.r = make_rsrc(g.B + e * g.b_es + (int64_t)f * g.ldb + n0, mn_bytes(l, g.ldb, n0));
+        }
+        ra_ = oa.r;
+        rb_ = ob.r;
+        sa = (uint32_t)(ks - cur_start) * oa.kstep;
+        sb = (uint32_t)(ks - cur_start) * ob.kstep;
+    };
     bf16x8 fa[2][4], fb[2][4];
     // read number r (0..7) of a sub-step, in MFMA consumption order: a0 b0 b1 b2 b3 a1 a2 a3
     auto read_one = [&](const char* st, int kk, int f, int r) {
@@ -394,12 +453,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         __builtin_amdgcn_sched_barrier(0);
         // sub-step 1 (f = 1) with the loads of step ks+NST into this stage and the reads of
         // the next step's sub-step 0
-        const bool live = ks + NST < nk, more = ks + 1 < nk;
+        const bool more = ks + 1 < nk;
+        rsrc_t ra_, rb_;
+        uint32_t sa, sb;
+        load_src(ks + NST, ra_, rb_, sa, sb);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
             mfma_one(1, n);
-            if (n < 4) issue_load(oa, cur32, ks + NST, n, live);
-            else if (n < 8) issue_load(ob, cur32 + OPB, ks + NST, n - 4, live);
+            if (n < 4) issue_load(oa, cur32, n, ra_, sa);
+            else if (n < 8) issue_load(ob, cur32 + OPB, n - 4, rb_, sb);
             else if (more) read_one(nxt, 0, 0, n - 8);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -409,12 +472,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
                        a3 = lds_addr(st3);
         const uint32_t stg[NST] = {a0, a1, a2, a3};
 #pragma unroll
-        for (int p = 0; p < NST; ++p)
+        for (int p = 0; p < NST; ++p) {
+            rsrc_t ra_, rb_;
+            uint32_t sa, sb;
+            load_src(p, ra_, rb_, sa, sb);
 #pragma unroll
             for (int i = 0; i < LPW; ++i) {
-                issue_load(oa, stg[p], p, i, p < nk);
-                issue_load(ob, stg[p] + OPB, p, i, p < nk);
+                issue_load(oa, stg[p], i, ra_, sa);
+                issue_load(ob, stg[p] + OPB, i, rb_, sb);
             }
+        }
         wait_vm_lgkm0<3 * LPS>();  // step 0 landed
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
@@ -618,14 +685,19 @@ int moe_ffn_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, 
     return launch(gemm2_down, "gemm2_down", g2, cdiv(H, BN), st);
 }
 
-// Backward of the FFN for one group of experts.
-//   dy [rows,H] (shared mode: one [R,H] gradient used by every expert, dy_shared = true)
-//   gu, h: saved forward values; xp: forward input rows (shared mode: one [R,H] input).
-//   Outputs dgu (workspace) [rows,2I], dxp [rows,H], dw1 [E,2I,H], dw2 [E,H,I].
+// Backward of the FFN for one group of experts, over the rows of one pass (pointers already
+// at the pass's rows; offsets [E+1] pass-local, or null in shared mode: every expert takes
+// all R rows and dy / xp are one [R,H] array used by every expert).
+//   dgrad: dgu [rows,2I] (dh = dy W2 with the SwiGLU backward, from the saved g|u) and
+//          dxp [rows,H] = dGU W1.
+//   wgrad: when wg is given, dW2 = dy^T h and dW1 = dGU^T Xp over every pass it spans, in the
+//          same launches as the dgrad products (the caller passes it with the last pass, once
+//          dy and dGU of all passes exist).
 int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, int I,
                      const bf16_t* w1, const bf16_t* w2, const bf16_t* gu, const bf16_t* h,
-                     const bf16_t* dy, bf16_t* dgu, bf16_t* dxp, bf16_t* dw1, bf16_t* dw2,
+                     const bf16_t* dy, bf16_t* dgu, bf16_t* dxp, const MoeWgradSpan* wg,
                      hipStream_t st) {
+    (void)xp;
     const bool shared = offsets == nullptr;
     int rc;
     // dh = dy_e W2_e (W2_e is [H,I]: N-contiguous in I), SwiGLU backward -> dgu
@@ -636,13 +708,16 @@ int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int
     gd.C2 = const_cast<bf16_t*>(gu); gd.c2_es = shared ? (int64_t)R * 2 * I : 0; gd.ldc2 = 2 * I;
     gd.offsets = offsets; gd.E = E; gd.R = R; gd.N = I; gd.K = H; gd.I = I;
     gd.total = shared ? E * cdiv(R, BM) * cdiv(I, BN) : 0;
-    // dW2_e = dy_e^T h_e: M = H, N = I, K = the expert's rows
+    // dW2_e = dy_e^T h_e: M = H, N = I, K = the expert's rows (of every pass)
     GemmArgs gw = blank();
-    gw.A = dy; gw.a_es = 0; gw.lda = H;
-    gw.B = h; gw.b_es = shared ? (int64_t)R * I : 0; gw.ldb = I;
-    gw.C = dw2; gw.c_es = (int64_t)H * I; gw.ldc = I;
-    gw.offsets = offsets; gw.E = E; gw.R = R; gw.M = H; gw.N = I; gw.I = I;
-    gw.total = E * cdiv(H, BM) * cdiv(I, BN);
+    if (wg) {
+        gw.A = wg->dy; gw.a_es = 0; gw.lda = H;
+        gw.B = wg->h; gw.b_es = shared ? (int64_t)wg->R * I : 0; gw.ldb = I;
+        gw.C = wg->dw2; gw.c_es = (int64_t)H * I; gw.ldc = I;
+        gw.offsets = wg->offsets; gw.E = E; gw.R = wg->R; gw.M = H; gw.N = I; gw.I = I;
+        gw.P = wg->P; gw.pass_rows = wg->pass_rows;
+        gw.total = E * cdiv(H, BM) * cdiv(I, BN);
+    }
     rc = launch_pair(bwd_down, "bwd_down", gd, gw, st);
     if (rc) return rc;
     // dXp = dGU_e W1_e (W1_e is [2I,H]: N-contiguous in H)
@@ -654,11 +729,14 @@ int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int
     gd2.total = shared ? E * cdiv(R, BM) * cdiv(H, BN) : 0;
     // dW1_e = dGU_e^T Xp_e: M = 2I, N = H
     GemmArgs gw2 = blank();
-    gw2.A = dgu; gw2.a_es = shared ? (int64_t)R * 2 * I : 0; gw2.lda = 2 * I;
-    gw2.B = xp; gw2.b_es = 0; gw2.ldb = H;
-    gw2.C = dw1; gw2.c_es = (int64_t)2 * I * H; gw2.ldc = H;
-    gw2.offsets = offsets; gw2.E = E; gw2.R = R; gw2.M = 2 * I; gw2.N = H; gw2.I = I;
-    gw2.total = E * cdiv(2 * I, BM) * cdiv(H, BN);
+    if (wg) {
+        gw2.A = wg->dgu; gw2.a_es = shared ? (int64_t)wg->R * 2 * I : 0; gw2.lda = 2 * I;
+        gw2.B = wg->xp; gw2.b_es = 0; gw2.ldb = H;
+        gw2.C = wg->dw1; gw2.c_es = (int64_t)2 * I * H; gw2.ldc = H;
+        gw2.offsets = wg->offsets; gw2.E = E; gw2.R = wg->R; gw2.M = 2 * I; gw2.N = H; gw2.I = I;
+        gw2.P = wg->P; gw2.pass_rows = wg->pass_rows;
+        gw2.total = E * cdiv(2 * I, BM) * cdiv(H, BN);
+    }
     rc = launch_pair(bwd_gate_up, "bwd_gate_up", gd2, gw2, st);
     if (rc) return rc;
     return MOE_OK;

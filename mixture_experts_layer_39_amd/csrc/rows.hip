@@ -245,7 +245,7 @@ __global__ __launch_bounds__(128) void unpermute_kernel(const bf16_t* __restrict
                                                         const int32_t* __restrict__ pos, int T,
                                                         int k, int H, int R,
                                                         const bf16_t* __restrict__ dxs, int S,
-                                                        bf16_t* __restrict__ dx) {
+                                                        int ldT, bf16_t* __restrict__ dx) {
     const int t = blockIdx.x;
     __shared__ int sp[MAXK];
     if (threadIdx.x < k) {
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(128) void unpermute_kernel(const bf16_t* __restrict
             }
         }
         for (int s = 0; s < S; ++s) {
-            u32x4 v = ld16(dxs + ((size_t)s * T + t) * H + c * 8);
+            u32x4 v = ld16(dxs + ((size_t)s * ldT + t) * H + c * 8);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 acc[2 * q] = __fadd_rn(acc[2 * q], lo_bf(v[q]));
@@ -422,11 +422,12 @@ int moe_launch_combine_bwd(const bf16_t* dout, const bf16_t* y, const int32_t* p
     return MOE_OK;
 }
 
+// dxs: S arrays of ldT token rows (the caller may point into the middle of them).
 int moe_launch_unpermute(const bf16_t* dxp, const int32_t* pos, int T, int k, int H, int R,
-                         const bf16_t* dxs, int S, bf16_t* dx, hipStream_t st) {
+                         const bf16_t* dxs, int S, int ldT, bf16_t* dx, hipStream_t st) {
     if (T == 0) return MOE_OK;
     MOE_TRACED("unpermute", st,
-               unpermute_kernel<<<T, 128, 0, st>>>(dxp, pos, T, k, H, R, dxs, S, dx));
+               unpermute_kernel<<<T, 128, 0, st>>>(dxp, pos, T, k, H, R, dxs, S, ldT, dx));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

@@ -3,6 +3,16 @@
 ``MoELayer`` owns the device buffers of one layer configuration (allocated once, with torch)
 and runs forward (route -> dispatch -> expert FFN -> combine) and backward through
 libmoe.so.  It holds no arithmetic: every value is produced by the HIP kernels.
+
+Macrobatch ring (``ring_depth = D``; the ring buffer walked at minibatch granularity that the
+pages describe, aiexpert.news "Megakernels are dead and back", ¶4): the tokens stream in
+minibatches; each minibatch is routed on its own, and every D minibatches form a pass whose
+routed rows are permuted into D ring slots, run through one grouped-GEMM pass and combined
+back one minibatch at a time.  No token is dropped: every routed row of every minibatch is
+dispatched, computed and combined exactly once.  Forward-only layers reuse one ring region
+of D slots for every pass; training layers keep each pass's region for the backward, which
+walks the passes again (one moe_backward call) and reduces the weight gradients over the
+rows of every pass.
 """
 from __future__ import annotations
 
@@ -52,7 +62,8 @@ def _e(shape, dtype, dev):
 
 
 class MoELayer:
-    def __init__(self, cfg: LayerCfg, inp: dict, device="cuda", backward: bool = True):
+    def __init__(self, cfg: LayerCfg, inp: dict, device="cuda", backward: bool = True,
+                 minibatch: int = 0, ring_depth: int = 0):
         c = self.cfg = cfg
         d = self.dev = torch.device(device)
         self.inp = inp
@@ -62,7 +73,21 @@ class MoELayer:
             raise ValueError("local share must have k routed rows per token")
         self.k_router = c.k
         self.kr = kr
-        R = self.R = T * kr
+        # macrobatch ring: minibatches of `minibatch` tokens, D of them per pass
+        self.ring = minibatch > 0 and ring_depth > 0
+        if self.ring:
+            if c.local_share or c.mx or c.router_proj or c.S > 1:
+                raise ValueError("ring mode supports routed layers with at most one shared expert")
+            self.mb = minibatch
+            self.n_mb = -(-T // minibatch)
+            self.D = min(ring_depth, self.n_mb)
+            self.passes = -(-self.n_mb // self.D)
+            self.pass_tokens = self.D * minibatch
+            self.pass_rows = self.pass_tokens * kr
+            regions = self.passes if backward else 1
+            R = self.R = regions * self.pass_rows
+        else:
+            R = self.R = T * kr
         ER = c.ER
         i32, f32, bf = torch.int32, torch.float32, torch.bfloat16
         # routing
@@ -70,10 +95,22 @@ class MoELayer:
         self.idx = _e((T, self.k_router), i32, d)
         self.w = _e((T, self.k_router), f32, d)
         self.s_sel = _e((T, self.k_router), f32, d)
-        self.counts = _e((E,), i32, d)
-        self.offsets = _e((E + 1,), i32, d)
+        if self.ring:
+            P = self.passes
+            self.counts = _e((P, E), i32, d)
+            self.offsets = _e((P, E + 1), i32, d)
+            self.src = _e((P, self.pass_rows), i32, d)
+            # per-minibatch routing also yields a minibatch permutation (unused scratch)
+            mbk = self.mb * kr
+            self.mb_counts = _e((E,), i32, d)
+            self.mb_offsets = _e((E + 1,), i32, d)
+            self.mb_pos = _e((self.mb, kr), i32, d)
+            self.mb_src = _e((mbk,), i32, d)
+        else:
+            self.counts = _e((E,), i32, d)
+            self.offsets = _e((E + 1,), i32, d)
+            self.src = _e((R,), i32, d)
         self.pos = _e((T, kr), i32, d)
-        self.src = _e((R,), i32, d)
         self.route_ws = _e((max(route_workspace_size(T, kr, E),
                                 route_workspace_size(T, self.k_router, ER), 256),),
                            torch.uint8, d)
@@ -130,7 +167,9 @@ class MoELayer:
 
     def _bwd_args(self):
         c, inp = self.cfg, self.inp
-        return bwd_args(T=c.T, H=c.H, E=c.E, k=self.kr, I=c.I, R=self.R, S=c.S, Is=c.Is,
+        ring = dict(passes=self.passes, pass_tokens=self.pass_tokens,
+                    pass_rows=self.pass_rows) if self.ring else {}
+        return bwd_args(**ring, T=c.T, H=c.H, E=c.E, k=self.kr, I=c.I, R=self.R, S=c.S, Is=c.Is,
                         E_router=c.ER, score=c.score, renorm=c.renorm,
                         route_scale=c.route_scale, x=inp["x"], xp=self.xp, gu=self.gu,
                         h=self.h, y=self.y, offsets=self.offsets, pos=self.pos, idx=self.idx,
@@ -185,10 +224,55 @@ class MoELayer:
                     c.S)
 
     def forward(self):
+        if self.ring:
+            return self.forward_ring()
         self.route()
         self.dispatch()
         self.experts()
         self.combine()
+        return self.out
+
+    # ------------------------------------------------------------------ macrobatch ring
+    def _route_minibatch(self, a, b):
+        c = self.cfg
+        moe_route(self.logits[a:b], b - a, c.E, c.k, idx=self.idx[a:b], w=self.w[a:b],
+                  s_sel=self.s_sel[a:b], counts=self.mb_counts, offsets=self.mb_offsets,
+                  pos=self.mb_pos, src=self.mb_src, score=c.score, n_groups=c.n_groups,
+                  topk_groups=c.topk_groups, renorm=c.renorm, route_scale=c.route_scale,
+                  ws=self.route_ws)
+
+    def forward_ring(self):
+        c, inp = self.cfg, self.inp
+        T, H, E, I, k, mb = c.T, c.H, c.E, c.I, self.kr, self.mb
+        x = inp["x"]
+        for p in range(self.passes):
+            t0 = p * self.pass_tokens
+            t1 = min(T, t0 + self.pass_tokens)
+            Tp, Rp = t1 - t0, (t1 - t0) * k
+            # route every minibatch of the pass on its own
+            for a in range(t0, t1, mb):
+                self._route_minibatch(a, min(t1, a + mb))
+            # the pass's rows into the ring slots: permutation, dispatch, one GEMM pass
+            moe_route(None, Tp, E, k, idx_in=self.idx[t0:t1], counts=self.counts[p],
+                      offsets=self.offsets[p], pos=self.pos[t0:t1], src=self.src[p],
+                      ws=self.route_ws)
+            r0 = (p if self.has_bwd else 0) * self.pass_rows
+            xp, y = self.xp[r0:r0 + Rp], self.y[r0:r0 + Rp]
+            moe_dispatch(x[t0:t1], Tp, H, k, self.src[p], Rp, xp)
+            moe_expert_ffn(BF16, xp, self.offsets[p], E, Rp, H, I, inp["w1"], inp["w2"], y,
+                           gu_save=None if self.gu is None else self.gu[r0:r0 + Rp],
+                           h_save=self.h[r0:r0 + Rp], ws=self.ffn_ws)
+            ys = None
+            if c.S:
+                ys = self.ys[0, t0:t1]
+                moe_expert_ffn(BF16, x[t0:t1], None, 1, Tp, H, c.Is, inp["ws1"], inp["ws2"], ys,
+                               gu_save=None if self.gus is None else self.gus[0, t0:t1],
+                               h_save=self.hs[0, t0:t1], ws=self.sh_ws)
+            # combine one minibatch at a time
+            for a in range(t0, t1, mb):
+                b = min(t1, a + mb)
+                moe_combine(y, self.pos[a:b], self.w[a:b], b - a, k, H, Rp, self.out[a:b],
+                            None if ys is None else self.ys[0, a:b], c.S)
         return self.out
 
     def backward(self):
