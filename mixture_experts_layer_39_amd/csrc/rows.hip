@@ -61,7 +61,11 @@ __device__ __forceinline__ int mx_block(const float* v, int mode, uint32_t* q) {
 }
 
 // ------------------------------------------------------------------ dispatch
-// One block per destination row: xp[r,:] = x[src[r]/k,:].
+// One block per destination row: xp[r,:] = x[src[r]/k,:].  Each thread issues all of its
+// 16-byte loads (up to UN) before any store, so a CU keeps enough bytes in flight to cover
+// the memory latency.
+constexpr int ROW_UN = 8;
+
 __global__ __launch_bounds__(128) void dispatch_kernel(const bf16_t* __restrict__ x, int64_t n_pairs,
                                                        int H, int k, const int32_t* __restrict__ src,
                                                        bf16_t* __restrict__ xp) {
@@ -71,9 +75,18 @@ __global__ __launch_bounds__(128) void dispatch_kernel(const bf16_t* __restrict_
     const bf16_t* in = x + (size_t)(ok ? s / k : 0) * H;
     bf16_t* out = xp + (size_t)r * H;
     const int nc = H / 8;
-    for (int c = threadIdx.x; c < nc; c += 128) {
-        u32x4 v = ok ? ld16(in + c * 8) : u32x4{0, 0, 0, 0};
-        st16_nt(out + c * 8, v);
+    for (int c0 = threadIdx.x; c0 < nc; c0 += 128 * ROW_UN) {
+        u32x4 v[ROW_UN];
+#pragma unroll
+        for (int u = 0; u < ROW_UN; ++u) {
+            const int c = c0 + u * 128;
+            v[u] = (ok && c < nc) ? ld16(in + c * 8) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < ROW_UN; ++u) {
+            const int c = c0 + u * 128;
+            if (c < nc) st16_nt(out + c * 8, v[u]);
+        }
     }
 }
 
@@ -168,15 +181,25 @@ __global__ __launch_bounds__(128) void combine_kernel(const bf16_t* __restrict__
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            int p = sp[j];
-            if (p < 0) continue;
-            float wj = sw[j];
-            u32x4 v = ld16(y + (size_t)p * H + c * 8);
+        // the rows of up to 8 slots are loaded before any is summed (slot order unchanged)
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            u32x4 v[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] = __fadd_rn(acc[2 * q], __fmul_rn(wj, lo_bf(v[q])));
-                acc[2 * q + 1] = __fadd_rn(acc[2 * q + 1], __fmul_rn(wj, hi_bf(v[q])));
+            for (int u = 0; u < 8; ++u) {
+                const int j = j0 + u;
+                const int p = j < k ? sp[j] : -1;
+                v[u] = p >= 0 ? ld16(y + (size_t)p * H + c * 8) : u32x4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = j0 + u;
+                if (j >= k || sp[j] < 0) continue;
+                const float wj = sw[j];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] = __fadd_rn(acc[2 * q], __fmul_rn(wj, lo_bf(v[u][q])));
+                    acc[2 * q + 1] = __fadd_rn(acc[2 * q + 1], __fmul_rn(wj, hi_bf(v[u][q])));
+                }
             }
         }
         for (int s = 0; s < S; ++s) {
@@ -196,7 +219,11 @@ __global__ __launch_bounds__(128) void combine_kernel(const bf16_t* __restrict__
 
 // ------------------------------------------------------------------ combine backward
 // One block per token: dy[pos[t,j],:] = bf16(w[t,j] * dout[t,:]) and
-// dw[t,j] = <dout[t,:], y[pos[t,j],:]> in fp32 with a fixed reduction tree.
+// dw[t,j] = <dout[t,:], y[pos[t,j],:]> in fp32 with a fixed reduction tree.  For each slot,
+// each thread issues the loads of up to CB_UN chunks of dout[t] and of y[pos[t,j]] before
+// reducing them (chunks in ascending order).
+constexpr int CB_UN = 4;
+
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restrict__ dout,
                                                           const bf16_t* __restrict__ y,
                                                           const int32_t* __restrict__ pos,
@@ -207,24 +234,36 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restri
     __shared__ float red[4][MAXK];
     const int nc = H / 8;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const bf16_t* g_row = dout + (size_t)t * H;
     for (int j = 0; j < k; ++j) {
-        int p = pos[(size_t)t * k + j];
-        bool ok = p >= 0 && p < R;
-        float wj = w[(size_t)t * k + j];
+        const int p = pos[(size_t)t * k + j];
+        const bool ok = p >= 0 && p < R;
+        const float wj = w[(size_t)t * k + j];
         float part = 0.0f;
         if (ok) {
-            for (int c = threadIdx.x; c < nc; c += 256) {
-                u32x4 g = ld16(dout + (size_t)t * H + c * 8);
-                u32x4 v = ld16(y + (size_t)p * H + c * 8);
-                u32x4 o;
+            const bf16_t* y_row = y + (size_t)p * H;
+            for (int c0 = threadIdx.x; c0 < nc; c0 += 256 * CB_UN) {
+                u32x4 g[CB_UN], v[CB_UN];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float g0 = lo_bf(g[q]), g1 = hi_bf(g[q]);
-                    part = __fadd_rn(part, __fmul_rn(g0, lo_bf(v[q])));
-                    part = __fadd_rn(part, __fmul_rn(g1, hi_bf(v[q])));
-                    o[q] = pack_bf2(__fmul_rn(wj, g0), __fmul_rn(wj, g1));
+                for (int u = 0; u < CB_UN; ++u) {
+                    const int c = c0 + u * 256;
+                    g[u] = c < nc ? ld16(g_row + c * 8) : u32x4{0, 0, 0, 0};
+                    v[u] = c < nc ? ld16(y_row + c * 8) : u32x4{0, 0, 0, 0};
                 }
-                st16(dy + (size_t)p * H + c * 8, o);
+#pragma unroll
+                for (int u = 0; u < CB_UN; ++u) {
+                    const int c = c0 + u * 256;
+                    if (c >= nc) continue;
+                    u32x4 o;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float g0 = lo_bf(g[u][q]), g1 = hi_bf(g[u][q]);
+                        part = __fadd_rn(part, __fmul_rn(g0, lo_bf(v[u][q])));
+                        part = __fadd_rn(part, __fmul_rn(g1, hi_bf(v[u][q])));
+                        o[q] = pack_bf2(__fmul_rn(wj, g0), __fmul_rn(wj, g1));
+                    }
+                    st16(dy + (size_t)p * H + c * 8, o);
+                }
             }
         }
 #pragma unroll
@@ -258,14 +297,23 @@ __global__ __launch_bounds__(128) void unpermute_kernel(const bf16_t* __restrict
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            int p = sp[j];
-            if (p < 0) continue;
-            u32x4 v = ld16(dxp + (size_t)p * H + c * 8);
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            u32x4 v[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] = __fadd_rn(acc[2 * q], lo_bf(v[q]));
-                acc[2 * q + 1] = __fadd_rn(acc[2 * q + 1], hi_bf(v[q]));
+            for (int u = 0; u < 8; ++u) {
+                const int j = j0 + u;
+                const int p = j < k ? sp[j] : -1;
+                v[u] = p >= 0 ? ld16(dxp + (size_t)p * H + c * 8) : u32x4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = j0 + u;
+                if (j >= k || sp[j] < 0) continue;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] = __fadd_rn(acc[2 * q], lo_bf(v[u][q]));
+                    acc[2 * q + 1] = __fadd_rn(acc[2 * q + 1], hi_bf(v[u][q]));
+                }
             }
         }
         for (int s = 0; s < S; ++s) {
@@ -279,7 +327,7 @@ __global__ __launch_bounds__(128) void unpermute_kernel(const bf16_t* __restrict
         u32x4 o;
 #pragma unroll
         for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[2 * q], acc[2 * q + 1]);
-        st16(dx + (size_t)t * H + c * 8, o);
+        st16_nt(dx + (size_t)t * H + c * 8, o);
     }
 }
 
