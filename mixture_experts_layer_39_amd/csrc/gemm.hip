@@ -26,22 +26,9 @@
 //    block scans the per-expert tile counts in a wave and finds its tile.
 //  - The backward's independent dgrad/wgrad pairs share one launch each (bwd_down,
 //    bwd_gate_up), so that one fills the other's last partial round of tiles.
-#include "common.h"
+#include "pipe.h"
 
 namespace moe {
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Buffer descriptor of a block-uniform range: base and size pass through readfirstlane so that
-// the descriptor lives in scalar registers (a descriptor the compiler sees as divergent costs
-// a waterfall loop around every load).
-__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = (uint32_t)uni((int)(uint32_t)a);
-    const uint32_t hi = (uint32_t)uni((int)(uint32_t)(a >> 32));
-    void* q = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, uni((int)bytes), 0x00020000);
-}
 
 constexpr int BM = 256, BN = 256, BK = 32, NTH = 256;
 constexpr int KK = BK / 16;   // 32x32x16 MFMA sub-steps per K step
@@ -94,27 +81,9 @@ constexpr int OPB = 256 * BK * 2;     // bytes of one operand in one stage
 constexpr int LPW = OPB / 1024 / 4;   // direct-load instructions per operand per wave per step
 constexpr int LPS = 2 * LPW;          // ... for both operands
 
-__device__ __forceinline__ int kswz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 __device__ __forceinline__ int mswz(int kr) { return (0xCA60 >> (4 * (kr & 3))) & 15; }
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-// Direct load of 16 bytes per lane into LDS at M0 + 16 * lane.  Issued through inline asm:
-// the compiler's own wait-count tracking of such loads cannot tell the pipeline stages apart
-// and would drain every stage in flight before each LDS read; the main loop waits for exactly
-// the stage it needs instead (wait_vm_lgkm0).  The loads are ordered like any volatile asm.
-__device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t lds_dst, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "s"(lds_dst), "v"(voff), "s"(r), "s"(soff)
-                 : "memory", "m0");
-}
-
-// 32-bit LDS address of a __shared__ object (wave-uniform).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)uni((int)(uint32_t)(uintptr_t)(lds_ptr)p);
-}
 
 // Transposed 8-byte LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
 // receives element i % 4 of the 8-byte chunks addressed by lanes i/4 + 4j, j = 0..3.
@@ -122,15 +91,6 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) i16x4*)(p));
 }
-
-// s_waitcnt: at most n vector-memory operations outstanding, no LDS operation outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
-}
-
-__host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // Per-lane description of one operand's global->LDS loads (LPW per wave per K step) and of
 // its MFMA fragment reads (4 sub-tiles of 32 rows per wave).
@@ -380,7 +340,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     static_assert(KK == 2 && LPW == 4 && NST == 4, "the step below is written for these");
     // K segments: one, except for wgrad over P > 1 passes (the expert's rows of each pass)
     const int P = (GK && g.offsets) ? max(g.P, 1) : 1;
-    auto seg = [&](int p, int& first, int& len) {
+    auto seg = [&](int p, int& first, int& len) __attribute__((always_inline)) {
         const int32_t* off = g.offsets + (int64_t)p * (g.E + 1);
         const int a = min(max(off[e], 0), g.pass_rows);
         const int b = min(max(off[e + 1], a), g.pass_rows);
@@ -400,7 +360,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     // every segment reads zeros.
     int cur_p = 0, cur_start = 0, cur_steps = cdiv(Kdim, BK);
     const rsrc_t rnull = make_rsrc(nullptr, 0);
-    auto load_src = [&](int ks, rsrc_t& ra_, rsrc_t& rb_, uint32_t& sa, uint32_t& sb) {
+    auto load_src = [&](int ks, rsrc_t& ra_, rsrc_t& rb_, uint32_t& sa, uint32_t& sb) __attribute__((always_inline)) {
         if (ks >= nk) {  // past the end: empty descriptors (the load writes zeros)
             ra_ = rnull;
             rb_ = rnull;
@@ -431,16 +391,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     };
     bf16x8 fa[2][4], fb[2][4];
     // read number r (0..7) of a sub-step, in MFMA consumption order: a0 b0 b1 b2 b3 a1 a2 a3
-    auto read_one = [&](const char* st, int kk, int f, int r) {
+    auto read_one = [&](const char* st, int kk, int f, int r) __attribute__((always_inline)) {
         if (r == 0) fa[f][0] = read_frag<A_K>(oa, st, 0, kk);
         else if (r <= 4) fb[f][r - 1] = read_frag<B_K>(ob, st + OPB, r - 1, kk);
         else fa[f][r - 4] = read_frag<A_K>(oa, st, r - 4, kk);
     };
-    auto mfma_one = [&](int f, int n) {
+    auto mfma_one = [&](int f, int n) __attribute__((always_inline)) {
         const int i = n >> 2, j = n & 3;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0);
     };
-    auto kstep = [&](char* cur, char* nxt, uint32_t cur32, int ks) {
+    auto kstep = [&](char* cur, char* nxt, uint32_t cur32, int ks) __attribute__((always_inline)) {
         // sub-step 0 (fragments f = 0) with the reads of sub-step 1
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
