@@ -183,11 +183,9 @@ __device__ __forceinline__ bf16x8 read_frag(const Operand& o, const char* stage_
     }
 }
 
-// Shared memory of one GEMM block: the pipeline stages and the per-expert tile prefix.
+// Shared memory of one GEMM block: the pipeline stages.
 struct alignas(1024) GemmSmem {
     char st[NST][2 * OPB];
-    int tp[1024];  // inclusive prefix sum of per-expert tile counts (ragged-M products)
-    int total;
 };
 
 template <int EPI>
@@ -195,30 +193,41 @@ __device__ __forceinline__ int n_tiles(const GemmArgs& g) {
     return (EPI == EPI_SWIGLU) ? cdiv(g.I, 128) : cdiv(g.N, BN);
 }
 
-// Tile count of a product.  Ragged-M products (expert rows from device offsets) count their
-// tiles on the device: the first wave scans the per-expert tile counts into sm.tp.
-template <int EPI, bool GK>
-__device__ __forceinline__ int tile_total(const GemmArgs& g, GemmSmem& sm) {
-    if (GK || g.offsets == nullptr) return g.total;
+// Ragged-M products (expert rows from device offsets) find their tiles on the device: every
+// wave scans the per-expert tile counts itself, 64 experts at a time (no LDS, no barrier).
+// ragged_scan returns the tile count; with `logical` >= 0 it also finds the expert owning
+// tile `logical` and that expert's first tile.
+__device__ __forceinline__ int ragged_scan(const GemmArgs& g, int NT, int logical, int* e_out,
+                                           int* first_out) {
     const int lane = threadIdx.x & 63;
-    const int NT = n_tiles<EPI>(g);
-    if (threadIdx.x < 64) {
-        int run = 0;
-        for (int base = 0; base < g.E; base += 64) {
-            int e = base + lane, tiles = 0;
-            if (e < g.E) {
-                int lo = min(max(g.offsets[e], 0), g.R);
-                int hi = min(max(g.offsets[e + 1], lo), g.R);
-                tiles = cdiv(hi - lo, BM) * NT;
-            }
-            int inc = wave_incl_scan(tiles) + run;
-            if (e < g.E) sm.tp[e] = inc;
-            run = __shfl(inc, 63, 64);
+    int run = 0;
+    for (int base = 0; base < g.E; base += 64) {
+        const int e = base + lane;
+        int tiles = 0;
+        if (e < g.E) {
+            const int lo = min(max(g.offsets[e], 0), g.R);
+            const int hi = min(max(g.offsets[e + 1], lo), g.R);
+            tiles = cdiv(hi - lo, BM) * NT;
         }
-        if (lane == 0) sm.total = run;
+        const int inc = wave_incl_scan(tiles) + run;
+        if (logical >= 0) {
+            const uint64_t m = __ballot(e < g.E && inc > logical);
+            if (m) {
+                const int l = __ffsll((unsigned long long)m) - 1;
+                *e_out = base + l;
+                *first_out = __shfl(inc - tiles, l, 64);
+                return -1;
+            }
+        }
+        run = __shfl(inc, 63, 64);
     }
-    __syncthreads();
-    return uni(sm.total);
+    return run;
+}
+
+template <int EPI, bool GK>
+__device__ __forceinline__ int tile_total(const GemmArgs& g) {
+    if (GK || g.offsets == nullptr) return g.total;
+    return uni(ragged_scan(g, n_tiles<EPI>(g), -1, nullptr, nullptr));
 }
 
 // One 256 x 256 output tile, number `logical` of the product (tiles run in launch order: the
@@ -227,25 +236,16 @@ __device__ __forceinline__ int tile_total(const GemmArgs& g, GemmSmem& sm) {
 // its own compact block of tiles).
 template <bool A_K, bool B_K, int EPI, bool GK>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const int logical) {
-    char* st0 = sm.st[0];
-    char* st1 = sm.st[1];
-    char* st2 = sm.st[2];
-    char* st3 = sm.st[3];
-    int* s_tp = sm.tp;
-
     const int tid = threadIdx.x, lane = tid & 63, wid = uni(tid >> 6);
     const int wm = wid >> 1, wn = wid & 1;
     const int NT = n_tiles<EPI>(g);
     const bool ragged_m = !GK && g.offsets != nullptr;
     int e, t_local, Mrows, row0;
     if (ragged_m) {
-        int lo = 0, hi = g.E - 1;
-        while (lo < hi) {
-            int mid = (lo + hi) >> 1;
-            if (s_tp[mid] > logical) hi = mid; else lo = mid + 1;
-        }
-        e = uni(lo);
-        t_local = uni(logical - (e ? s_tp[e - 1] : 0));
+        int ee = 0, first = 0;
+        ragged_scan(g, NT, logical, &ee, &first);
+        e = uni(ee);
+        t_local = uni(logical - first);
         int a = min(max(g.offsets[e], 0), g.R);
         int b = min(max(g.offsets[e + 1], a), g.R);
         row0 = uni(a);
@@ -337,7 +337,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     // sub-steps.  Fragment reads follow the order the MFMAs consume them.
     // The MFMA takes the B fragment as its first operand, so each lane's accumulators hold
     // one output row (m) and 4-column runs (n): the epilogue stores 8-byte vectors.
-    static_assert(KK == 2 && LPW == 4 && NST == 4, "the step below is written for these");
+    static_assert(KK == 2 && LPW == 4 && NST >= 3, "the step below is written for these");
     // K segments: one, except for wgrad over P > 1 passes (the expert's rows of each pass)
     const int P = (GK && g.offsets) ? max(g.P, 1) : 1;
     auto seg = [&](int p, int& first, int& len) __attribute__((always_inline)) {
@@ -408,7 +408,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
             if (n < 8) read_one(cur, 1, 1, n);
             __builtin_amdgcn_sched_barrier(0);
         }
-        wait_vm_lgkm0<2 * LPS>();  // step ks+1 landed (steps ks+2, ks+3 may be in flight)
+        wait_vm_lgkm0<(NST - 2) * LPS>();  // step ks+1 landed (later steps may be in flight)
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         // sub-step 1 (f = 1) with the loads of step ks+NST into this stage and the reads of
@@ -428,9 +428,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         }
     };
     if (nk > 0) {
-        const uint32_t a0 = lds_addr(st0), a1 = lds_addr(st1), a2 = lds_addr(st2),
-                       a3 = lds_addr(st3);
-        const uint32_t stg[NST] = {a0, a1, a2, a3};
+        const uint32_t st_base = lds_addr(sm.st[0]);  // stage p at st_base + p * 2 * OPB
 #pragma unroll
         for (int p = 0; p < NST; ++p) {
             rsrc_t ra_, rb_;
@@ -438,20 +436,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
             load_src(p, ra_, rb_, sa, sb);
 #pragma unroll
             for (int i = 0; i < LPW; ++i) {
-                issue_load(oa, stg[p], i, ra_, sa);
-                issue_load(ob, stg[p] + OPB, i, rb_, sb);
+                issue_load(oa, st_base + p * 2 * OPB, i, ra_, sa);
+                issue_load(ob, st_base + p * 2 * OPB + OPB, i, rb_, sb);
             }
         }
-        wait_vm_lgkm0<3 * LPS>();  // step 0 landed
+        wait_vm_lgkm0<(NST - 1) * LPS>();  // step 0 landed
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) read_one(st0, 0, 0, r);
+        for (int r = 0; r < 8; ++r) read_one(sm.st[0], 0, 0, r);
         for (int ks = 0; ks < nk; ks += NST) {
-            kstep(st0, st1, a0, ks);
-            if (ks + 1 < nk) kstep(st1, st2, a1, ks + 1);
-            if (ks + 2 < nk) kstep(st2, st3, a2, ks + 2);
-            if (ks + 3 < nk) kstep(st3, st0, a3, ks + 3);
+#pragma unroll
+            for (int u = 0; u < NST; ++u)
+                if (ks + u < nk)
+                    kstep(sm.st[u], sm.st[(u + 1) % NST], st_base + u * 2 * OPB, ks + u);
         }
         wait_vm_lgkm0<0>();  // no load may still be writing LDS when the block ends
     }
@@ -551,7 +549,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) void \
     NAME(GemmArgs g) {                                                                 \
         __shared__ GemmSmem sm;                                                        \
-        const int total = tile_total<EPI, GK>(g, sm);                                  \
+        const int total = tile_total<EPI, GK>(g);                                      \
         if ((int)blockIdx.x < total) gemm_tile<AKM, BKM, EPI, GK>(g, sm, blockIdx.x);  \
     }
 MOE_GEMM_KERNEL(gemm1_swiglu, true, true, EPI_SWIGLU, false)     // [g|u] = Xp W1^T, h
@@ -566,7 +564,7 @@ MOE_GEMM_KERNEL(gemm2_down, true, true, EPI_STORE, false)        // y = h W2^T
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_down(GemmArgs gd, GemmArgs gw) {
     __shared__ GemmSmem sm;
-    const int td = tile_total<EPI_DSWIGLU, false>(gd, sm);
+    const int td = tile_total<EPI_DSWIGLU, false>(gd);
     const int b = blockIdx.x;
     if (b < td) gemm_tile<true, false, EPI_DSWIGLU, false>(gd, sm, b);
     else if (b - td < gw.total) gemm_tile<false, false, EPI_STORE, true>(gw, sm, b - td);
@@ -575,7 +573,7 @@ void bwd_down(GemmArgs gd, GemmArgs gw) {
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_gate_up(GemmArgs gd, GemmArgs gw) {
     __shared__ GemmSmem sm;
-    const int td = tile_total<EPI_STORE, false>(gd, sm);
+    const int td = tile_total<EPI_STORE, false>(gd);
     const int b = blockIdx.x;
     if (b < td) gemm_tile<true, false, EPI_STORE, false>(gd, sm, b);
     else if (b - td < gw.total) gemm_tile<false, false, EPI_STORE, true>(gw, sm, b - td);
