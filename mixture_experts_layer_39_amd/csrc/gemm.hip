@@ -13,8 +13,10 @@
 // Design (CDNA4, wave64):
 //  - 256x256 output tile per 256-thread block, 4 waves in 2x2, each wave a 128x128 sub-tile
 //    of 4x4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane, one wave per SIMD).
-//  - K steps of 32 through a ring of 4 LDS stages (128 KB), filled by direct global-to-LDS
-//    buffer loads three steps ahead of their use; one barrier per step.
+//  - K steps of 64 through two LDS stages of 64 KB, filled by direct global-to-LDS buffer
+//    loads one step ahead of their use; one barrier per step.  A K-major tile row is then
+//    128 contiguous bytes per step (a whole L2 line), which halves the L2 requests of the
+//    32-wide step: the loads, not the MFMAs, are what the L2 can serve at this tile size.
 //  - Operands contiguous along K are read from LDS with ds_read_b128; operands contiguous
 //    along M or N (the weights in dgrad, both operands in wgrad) are stored as loaded and
 //    read with the transposing ds_read_b64_tr_b16.  Both LDS layouts are swizzled so that
@@ -30,9 +32,7 @@
 
 namespace moe {
 
-constexpr int BM = 256, BN = 256, BK = 32, NTH = 256;
-constexpr int KK = BK / 16;   // 32x32x16 MFMA sub-steps per K step
-constexpr int NST = 4;        // pipeline stages (K steps resident or in flight)
+constexpr int BM = 256, BN = 256, NTH = 256;
 constexpr int GM = 4;         // M tiles per L2 group
 
 enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
@@ -64,11 +64,15 @@ struct GemmArgs {
 };
 
 // ---------------------------------------------------------------- LDS tiles
-// One pipeline stage holds one K step (BK = 32) of both operands, 16 KB each.  Two layouts:
-//  K-major   (operand contiguous along K in memory): tile row r (an M or N index) is 64 bytes,
-//            four 16-byte chunks of 8 k values; chunk c is stored at chunk c ^ kswz(r).  The
-//            rows read by one 128-byte (8-lane) or 256-byte (16-lane) phase of a fragment read
-//            then hit distinct bank groups.
+// The K step is BK = 32 or 64 (a template parameter of the tile); the stages fill 128 KB of
+// LDS, 4 of BK = 32 or 2 of BK = 64.  A 64-wide step makes each K-major tile row 128
+// contiguous bytes (a whole L2 line per request, half the requests of 64-byte rows); a 32-wide
+// step keeps three steps in flight instead of one, which pays where the rows are long
+// already (MN-major operands).  One stage holds one K step of both operands.  Two layouts:
+//  K-major   (operand contiguous along K in memory): tile row r (an M or N index) is BK * 2
+//            bytes of 16-byte chunks of 8 k values; chunk c is stored at chunk c ^ swz(r),
+//            swz = kswz4 (BK = 32) or kswz8 (BK = 64).  The rows read by one 128-byte (8-lane)
+//            or 256-byte (16-lane) phase of a fragment read then hit distinct bank groups.
 //  MN-major  (operand contiguous along M or N): k-row kr is 512 bytes, 32 chunks of 8 m (n)
 //            values; chunk c is stored at chunk c ^ mswz(kr % 4), mswz = {0, 6, 10, 12}, so
 //            the k-rows and columns read by one 16-lane (128-byte) or 32-lane (256-byte) phase
@@ -76,12 +80,35 @@ struct GemmArgs {
 // Both are filled by direct global-to-LDS loads (buffer_load ... lds): lane L of a wave
 // writes 16 bytes at LDS base + 16 L, so each lane fetches the global chunk that belongs at
 // its LDS position and the swizzle lives entirely in the global offsets.
-constexpr int KROW = BK * 2;          // bytes of one K-major tile row
-constexpr int OPB = 256 * BK * 2;     // bytes of one operand in one stage
-constexpr int LPW = OPB / 1024 / 4;   // direct-load instructions per operand per wave per step
-constexpr int LPS = 2 * LPW;          // ... for both operands
+constexpr int LDS_STAGES_BYTES = 128 * 1024;
+#ifndef MOE_GEMM_SLOTS5
+#define MOE_GEMM_SLOTS5 1
+#endif
+// LDS of one block: the stage ring (128 KB), or for BK = 64 five operand slots (160 KB).
+constexpr int LDS_BYTES = MOE_GEMM_SLOTS5 ? 160 * 1024 : LDS_STAGES_BYTES;
+
+template <int BK_>
+struct Pipe {
+    static constexpr int BK = BK_;
+    static constexpr int KK = BK / 16;              // 32x32x16 MFMA sub-steps per K step
+    static constexpr int KROW = BK * 2;             // bytes of one K-major tile row
+    static constexpr int OPB = 256 * BK * 2;        // bytes of one operand in one stage
+    static constexpr int NST = LDS_STAGES_BYTES / (2 * OPB);  // pipeline stages
+    static constexpr int LPW = OPB / 1024 / 4;      // direct loads per operand per wave per step
+    static constexpr int LPS = 2 * LPW;             // ... for both operands
+    static constexpr int RPI = 1024 / KROW;         // K-major tile rows per load instruction
+    static_assert(BK == 32 || BK == 64, "K step");
+};
 
 __device__ __forceinline__ int mswz(int kr) { return (0xCA60 >> (4 * (kr & 3))) & 15; }
+// K-major row swizzles, chosen so that the rows read by one 128-byte (8-lane) or 256-byte
+// (16-lane) phase of a 16-byte-per-lane fragment read hit distinct bank groups: kswz4 for
+// rows of four chunks, kswz8 for rows of eight (distinct over any 8 consecutive rows, and
+// over the even (odd) rows of any 16 consecutive rows).
+__device__ __forceinline__ int kswz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+__device__ __forceinline__ int kswz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+template <int BK>
+__device__ __forceinline__ int kswz_of(int r) { return BK == 64 ? kswz8(r) : kswz4(r); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -93,52 +120,63 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
 }
 
 // Per-lane description of one operand's global->LDS loads (LPW per wave per K step) and of
-// its MFMA fragment reads (4 sub-tiles of 32 rows per wave).
+// its MFMA fragment reads (4 sub-tiles of 32 rows per wave).  Wave w fills the quarter of
+// the operand's stage area at w OPB/4, 1 KB per instruction.  The global offset of load i
+// is voff[i % 2] + ((i / 2) % 2) ist1 + (i / 4) ist2: the swizzled chunk depends only on the
+// parity of i, and the rows of one wave's loads advance by two scalar strides.
 struct Operand {
     rsrc_t r;
-    uint32_t voff[LPW];  // byte offset of this lane's 16-byte chunk, per load instruction
-    uint32_t kstep;      // byte advance of the global offset per K step
-    int ldsrow[LPW];     // LDS byte offset (within the operand's stage area) per instruction
-    uint32_t rd[4];      // fragment-read base offset per sub-tile
-    int rs[4];           // K-major: swizzle bit 1 of the sub-tile's row
+    uint32_t voff[2];  // byte offset of this lane's 16-byte chunk, even / odd instructions
+    uint32_t ist1, ist2;  // byte advances of instructions 2, 3 and 4-7 (see above)
+    uint32_t kstep;    // byte advance of the global offset per K step
+    // fragment-read offsets: K-major, per sub-step kk (sub-tile t adds 32 t KROW, an
+    // immediate); MN-major, per sub-tile t (sub-step kk adds 8192 kk)
+    uint32_t rd[4];
 };
 
 // K-major operand.  rowmap(nn) gives the global row (relative to the descriptor base) of
-// tile row nn.  Each wave loads 64 tile rows, 16 rows per instruction.
-template <typename RowMap>
+// tile row nn.  Each wave loads 64 tile rows, RPI rows of BK * 2 bytes per instruction:
+// tile rows 64 w + RPI i + L / (64 / RPI) for instruction i, whose global rows must be those
+// of instruction i % 2 plus ((i / 2) % 2) rs1 + (i / 4) rs2.
+template <int BK, typename RowMap>
 __device__ __forceinline__ void setup_kmajor(Operand& o, const void* base, uint32_t bytes, int ld,
-                                             int wid, int lane, int wsub, RowMap rowmap) {
+                                             int wid, int lane, int wsub, RowMap rowmap,
+                                             int rs1, int rs2) {
+    typedef Pipe<BK> PP;
+    constexpr int CPR = PP::KROW / 16;  // 16-byte chunks per row
     o.r = make_rsrc(base, bytes);
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-        const int r = 64 * wid + 16 * i + (lane >> 2);
-        const int c = (lane & 3) ^ kswz(r);
-        o.voff[i] = (uint32_t)rowmap(r) * (uint32_t)ld * 2u + (uint32_t)c * 16u;
-        o.ldsrow[i] = (64 * wid + 16 * i) * KROW;
+    for (int par = 0; par < 2; ++par) {
+        const int r = 64 * wid + PP::RPI * par + lane / CPR;
+        const int c = (lane % CPR) ^ kswz_of<BK>(r);
+        o.voff[par] = (uint32_t)rowmap(r) * (uint32_t)ld * 2u + (uint32_t)c * 16u;
     }
+    o.ist1 = (uint32_t)rs1 * (uint32_t)ld * 2u;
+    o.ist2 = (uint32_t)rs2 * (uint32_t)ld * 2u;
     o.kstep = BK * 2;
-    // fragment reads: lane reads row rb + lane%32, logical chunk 2 kk + lane/32
+    // fragment reads: lane reads row wsub + 32 t + lane%32, logical chunk 2 kk + lane/32,
+    // stored at chunk (2 kk + lane/32) ^ swz(row); swz does not depend on t
+    const int r = wsub + (lane & 31);
+    const int x = (lane >> 5) ^ kswz_of<BK>(r);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int r = wsub + 32 * t + (lane & 31);
-        const int s = kswz(r);
-        o.rd[t] = (uint32_t)(r * KROW) | ((uint32_t)(((lane >> 5) ^ s) & 1) << 4);
-        o.rs[t] = s & 2;
-    }
+    for (int kk = 0; kk < PP::KK; ++kk)
+        o.rd[kk] = (uint32_t)(r * PP::KROW) + ((uint32_t)((2 * kk) ^ x) << 4);
 }
 
 // MN-major operand: element (mn, k) at base + k*ld + mn (bytes x2).  Each wave loads
 // BK/4 k-rows of the step, 2 per instruction.
+template <int BK>
 __device__ __forceinline__ void setup_mnmajor(Operand& o, const void* base, uint32_t bytes, int ld,
                                               int wid, int lane, int wsub) {
     o.r = make_rsrc(base, bytes);
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-        const int kr = (BK / 4) * wid + 2 * i + (lane >> 5);
+    for (int par = 0; par < 2; ++par) {
+        const int kr = (BK / 4) * wid + 2 * par + (lane >> 5);
         const int c = (lane & 31) ^ mswz(kr);
-        o.voff[i] = (uint32_t)kr * (uint32_t)ld * 2u + (uint32_t)c * 16u;
-        o.ldsrow[i] = ((BK / 4) * wid + 2 * i) * 512;
+        o.voff[par] = (uint32_t)kr * (uint32_t)ld * 2u + (uint32_t)c * 16u;
     }
+    o.ist1 = 4u * (uint32_t)ld * 2u;
+    o.ist2 = 8u * (uint32_t)ld * 2u;
     o.kstep = (uint32_t)BK * (uint32_t)ld * 2u;
     // transpose reads: lane group g = lane/16, q = lane%4, j = (lane%16)/4 reads k-row
     // 16 kk + 8 (g/2) + 4 h + j at columns mnb + 16 (g%2) + 4 q .. +3
@@ -149,16 +187,17 @@ __device__ __forceinline__ void setup_mnmajor(Operand& o, const void* base, uint
         const int kr = 8 * (gq >> 1) + j;
         const int pc = (mn >> 3) ^ mswz(j);
         o.rd[t] = (uint32_t)(kr * 512 + pc * 16 + 8 * (q & 1));
-        o.rs[t] = 0;
     }
 }
 
 // Load instruction i of K step ks into the operand's area of a stage.  Steps past the end
 // of K use an empty descriptor: the load still issues (so every step issues the same number
 // of loads and the wait counts are constants) but fetches nothing and writes zeros.
-__device__ __forceinline__ void issue_load(const Operand& o, uint32_t stage_op, int i, rsrc_t r,
-                                           uint32_t soff) {
-    lds_load16(r, stage_op + (uint32_t)o.ldsrow[i], o.voff[i], soff);
+template <int BK>
+__device__ __forceinline__ void issue_load(const Operand& o, uint32_t stage_op, int wid, int i,
+                                           rsrc_t r, uint32_t soff) {
+    lds_load16(r, stage_op + (uint32_t)(wid * (Pipe<BK>::OPB / 4) + i * 1024), o.voff[i & 1],
+               soff + (uint32_t)((i >> 1) & 1) * o.ist1 + (uint32_t)(i >> 2) * o.ist2);
 }
 
 // Bytes of an MN-major operand range: `rows` k-rows of `ld` elements from column offset m0.
@@ -168,11 +207,10 @@ __device__ __forceinline__ uint32_t mn_bytes(int rows, int ld, int m0) {
 
 // The 32x32x16 MFMA fragment of sub-tile t at k sub-step kk: 8 bf16 (k = 8 (lane/32) .. +7 of
 // the sub-step) of row (or column) lane % 32.
-template <bool KMAJ>
+template <int BK, bool KMAJ>
 __device__ __forceinline__ bf16x8 read_frag(const Operand& o, const char* stage_op, int t, int kk) {
     if (KMAJ) {
-        const uint32_t off = o.rd[t] + ((uint32_t)((2 * kk) ^ o.rs[t]) << 4);
-        return *reinterpret_cast<const bf16x8*>(stage_op + off);
+        return *reinterpret_cast<const bf16x8*>(stage_op + o.rd[kk] + t * 32 * Pipe<BK>::KROW);
     } else {
         const char* p = stage_op + o.rd[t] + 16 * kk * 512;
         i16x4 lo = lds_read_tr(p);
@@ -185,7 +223,7 @@ __device__ __forceinline__ bf16x8 read_frag(const Operand& o, const char* stage_
 
 // Shared memory of one GEMM block: the pipeline stages.
 struct alignas(1024) GemmSmem {
-    char st[NST][2 * OPB];
+    char st[LDS_BYTES];
 };
 
 template <int EPI>
@@ -234,8 +272,11 @@ __device__ __forceinline__ int tile_total(const GemmArgs& g) {
 // blocks in flight at once, spread over all XCDs, work on neighbouring tiles whose operand
 // panels meet in the shared last-level cache, which measured faster than giving each XCD
 // its own compact block of tiles).
-template <bool A_K, bool B_K, int EPI, bool GK>
+template <int BK, bool A_K, bool B_K, int EPI, bool GK>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const int logical) {
+    typedef Pipe<BK> PP;
+    constexpr int KK = PP::KK, NST = PP::NST, OPB = PP::OPB, LPW = PP::LPW, LPS = PP::LPS;
+    constexpr bool SLOTS5 = (BK == 64) && MOE_GEMM_SLOTS5;
     const int tid = threadIdx.x, lane = tid & 63, wid = uni(tid >> 6);
     const int wm = wid >> 1, wn = wid & 1;
     const int NT = n_tiles<EPI>(g);
@@ -290,34 +331,36 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     // ---------------------------------------------------------------- operands
     // A: K-major rows m at A_e + (row0 + m)*lda; or MN-major (wgrad): (m, k) at
     //    A_e + (row0 + k)*lda + m.
-    // B: K-major rows n at B_e + n*ldb (SwiGLU: gate and up rows interleaved so a tile holds
-    //    128 channels of each); or MN-major: (n, k) at B_e + (kbase + k)*ldb + n, kbase = row0
-    //    for wgrad (the expert's tokens), else 0 (a weight with K rows).
+    // B: K-major rows n at B_e + n*ldb; or MN-major: (n, k) at B_e + (kbase + k)*ldb + n,
+    //    kbase = row0 for wgrad (the expert's tokens), else 0 (a weight with K rows).
+    //    SwiGLU: a tile holds gate and up rows of 128 channels.  Each 32-column MFMA block
+    //    takes 16 channels, gate in its columns 0-15 and up in 16-31, so that every lane
+    //    holds the gate and up values of the same channels in one accumulator block.
     Operand oa, ob;
     if (A_K) {
         const bf16_t* base = g.A + e * g.a_es + (int64_t)(row0 + m0) * g.lda;
-        setup_kmajor(oa, base, (uint32_t)max(Mrows - m0, 0) * (uint32_t)g.lda * 2u, g.lda, wid,
-                     lane, wm * 128, [](int r) { return r; });
+        setup_kmajor<BK>(oa, base, (uint32_t)max(Mrows - m0, 0) * (uint32_t)g.lda * 2u, g.lda, wid,
+                     lane, wm * 128, [](int r) { return r; }, 2 * PP::RPI, 4 * PP::RPI);
     } else {
         const bf16_t* base = g.A + e * g.a_es + (int64_t)row0 * g.lda + m0;
-        setup_mnmajor(oa, base, mn_bytes(Kdim, g.lda, m0), g.lda, wid, lane, wm * 128);
+        setup_mnmajor<BK>(oa, base, mn_bytes(Kdim, g.lda, m0), g.lda, wid, lane, wm * 128);
     }
     if (B_K) {
         const bf16_t* base = g.B + e * g.b_es;
         const int I = g.I;
         if (EPI == EPI_SWIGLU)
-            setup_kmajor(ob, base, (uint32_t)g.b_rows * (uint32_t)g.ldb * 2u, g.ldb, wid, lane,
+            setup_kmajor<BK>(ob, base, (uint32_t)g.b_rows * (uint32_t)g.ldb * 2u, g.ldb, wid, lane,
                          wn * 128, [=](int nn) {
-                             int q = nn & 127;
-                             return (q >> 6) * I + ch0 + (nn >> 7) * 64 + (q & 63);
-                         });
+                             return ((nn >> 4) & 1) * I + ch0 + (nn >> 7) * 64 +
+                                    ((nn & 127) >> 5) * 16 + (nn & 15);
+                         }, PP::RPI == 8 ? I : 16, PP::RPI == 8 ? 16 : 32);
         else
-            setup_kmajor(ob, base, (uint32_t)g.b_rows * (uint32_t)g.ldb * 2u, g.ldb, wid, lane,
-                         wn * 128, [=](int nn) { return n0 + nn; });
+            setup_kmajor<BK>(ob, base, (uint32_t)g.b_rows * (uint32_t)g.ldb * 2u, g.ldb, wid, lane,
+                         wn * 128, [=](int nn) { return n0 + nn; }, 2 * PP::RPI, 4 * PP::RPI);
     } else {
         const int64_t kbase = GK ? row0 : 0;
         const bf16_t* base = g.B + e * g.b_es + kbase * g.ldb + n0;
-        setup_mnmajor(ob, base, mn_bytes(Kdim, g.ldb, n0), g.ldb, wid, lane, wn * 128);
+        setup_mnmajor<BK>(ob, base, mn_bytes(Kdim, g.ldb, n0), g.ldb, wid, lane, wn * 128);
     }
 
     f32x16 acc[4][4];
@@ -327,17 +370,29 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    // The accumulators live in the AGPRs across the K loop (they fill them exactly).  With
+    // the SwiGLU epilogue the register allocator otherwise splits them over both register
+    // files and spills inside the loop; pinning them there at the start prevents that (the
+    // other products allocate better without it).
+    auto pin_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+    };
+    if (EPI == EPI_SWIGLU) pin_acc();
 
     // ---------------------------------------------------------------- main loop
     // NST stages in a ring: at the end of K step ks the stage it used is refilled with step
-    // ks + NST, so every load has NST - 1 steps to land.  A step is two sub-steps of 16 k
-    // (16 MFMAs each).  The LDS reads of the next sub-step's fragments and the global->LDS
-    // loads are interleaved one per MFMA, so they issue while the MFMA pipe is busy; the step
-    // barrier (all waves done reading this stage; step ks+1 landed) sits between the two
-    // sub-steps.  Fragment reads follow the order the MFMAs consume them.
+    // ks + NST.  A step is KK sub-steps of 16 k (16 MFMAs each).  The LDS reads of the next
+    // sub-step's fragments and the global->LDS loads are interleaved with the MFMAs, so they
+    // issue while the MFMA pipe is busy.  The step barrier (all waves done reading this
+    // stage; step ks+1 landed) sits before the last sub-step, whose fragments were read
+    // during the one before; the last sub-step then refills the stage and reads the next
+    // step's first fragments.  Fragment reads follow the order the MFMAs consume them.
     // The MFMA takes the B fragment as its first operand, so each lane's accumulators hold
     // one output row (m) and 4-column runs (n): the epilogue stores 8-byte vectors.
-    static_assert(KK == 2 && LPW == 4 && NST >= 3, "the step below is written for these");
+    static_assert(KK >= 2 && LPS <= 16 && NST >= 2, "the step below is written for these");
     // K segments: one, except for wgrad over P > 1 passes (the expert's rows of each pass)
     const int P = (GK && g.offsets) ? max(g.P, 1) : 1;
     auto seg = [&](int p, int& first, int& len) __attribute__((always_inline)) {
@@ -391,44 +446,118 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     };
     bf16x8 fa[2][4], fb[2][4];
     // read number r (0..7) of a sub-step, in MFMA consumption order: a0 b0 b1 b2 b3 a1 a2 a3
+    auto read_ab = [&](const char* sa_, const char* sb_, int kk, int f, int r) __attribute__((always_inline)) {
+        if (r == 0) fa[f][0] = read_frag<BK, A_K>(oa, sa_, 0, kk);
+        else if (r <= 4) fb[f][r - 1] = read_frag<BK, B_K>(ob, sb_, r - 1, kk);
+        else fa[f][r - 4] = read_frag<BK, A_K>(oa, sa_, r - 4, kk);
+    };
     auto read_one = [&](const char* st, int kk, int f, int r) __attribute__((always_inline)) {
-        if (r == 0) fa[f][0] = read_frag<A_K>(oa, st, 0, kk);
-        else if (r <= 4) fb[f][r - 1] = read_frag<B_K>(ob, st + OPB, r - 1, kk);
-        else fa[f][r - 4] = read_frag<A_K>(oa, st, r - 4, kk);
+        read_ab(st, st + OPB, kk, f, r);
     };
     auto mfma_one = [&](int f, int n) __attribute__((always_inline)) {
         const int i = n >> 2, j = n & 3;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0);
     };
     auto kstep = [&](char* cur, char* nxt, uint32_t cur32, int ks) __attribute__((always_inline)) {
-        // sub-step 0 (fragments f = 0) with the reads of sub-step 1
+        // sub-steps 0 .. KK-2 (fragments kk % 2), each with the reads of the next one
 #pragma unroll
-        for (int n = 0; n < 16; ++n) {
-            mfma_one(0, n);
-            if (n < 8) read_one(cur, 1, 1, n);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int kk = 0; kk < KK - 1; ++kk) {
+#pragma unroll
+            for (int n = 0; n < 16; ++n) {
+                mfma_one(kk & 1, n);
+                if (n < 8) read_one(cur, kk + 1, (kk + 1) & 1, n);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         wait_vm_lgkm0<(NST - 2) * LPS>();  // step ks+1 landed (later steps may be in flight)
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        // sub-step 1 (f = 1) with the loads of step ks+NST into this stage and the reads of
-        // the next step's sub-step 0
+        // last sub-step with the loads of step ks+NST into this stage and the reads of the
+        // next step's sub-step 0
         const bool more = ks + 1 < nk;
         rsrc_t ra_, rb_;
         uint32_t sa, sb;
         load_src(ks + NST, ra_, rb_, sa, sb);
         __builtin_amdgcn_sched_barrier(0);
+        constexpr int fl = (KK - 1) & 1;
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
-            mfma_one(1, n);
-            if (n < 4) issue_load(oa, cur32, n, ra_, sa);
-            else if (n < 8) issue_load(ob, cur32 + OPB, n - 4, rb_, sb);
-            else if (more) read_one(nxt, 0, 0, n - 8);
+            mfma_one(fl, n);
+            if (n < LPW) issue_load<BK>(oa, cur32, wid, n, ra_, sa);
+            else if (n < LPS) issue_load<BK>(ob, cur32 + OPB, wid, n - LPW, rb_, sb);
+            if (n >= 8 && more) read_one(nxt, 0, 0, n - 8);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    if (nk > 0) {
-        const uint32_t st_base = lds_addr(sm.st[0]);  // stage p at st_base + p * 2 * OPB
+    // Five operand slots (BK = 64): operand slots of OPB bytes in a ring of five, A of step s
+    // in slot 2s mod 5 and B in slot 2s+1 mod 5.  Of each step's loads, A(s+2) goes into the
+    // slot B(s-1) left at the previous step's barrier and is issued during the first two
+    // sub-steps, B(s+2) into the slot A(s) leaves at this step's barrier and is issued in the
+    // last sub-step: half of the loads get two steps to land instead of one, and the loads
+    // are spread over the step instead of bunched after the barrier.
+    auto kstep5 = [&](int u, int ks) __attribute__((always_inline)) {
+        char* const cA = sm.st + ((2 * u) % 5) * OPB;
+        char* const cB = sm.st + ((2 * u + 1) % 5) * OPB;
+        char* const nA = sm.st + ((2 * u + 2) % 5) * OPB;
+        char* const nB = sm.st + ((2 * u + 3) % 5) * OPB;
+        const uint32_t base32 = lds_addr(sm.st);
+        const uint32_t lA = base32 + ((2 * u + 4) % 5) * OPB;  // A(ks+2): slot of B(ks-1)
+        const uint32_t lB = base32 + ((2 * u) % 5) * OPB;      // B(ks+2): slot of A(ks)
+        rsrc_t ra_, rb_;
+        uint32_t sa, sb;
+        load_src(ks + 2, ra_, rb_, sa, sb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < KK - 1; ++kk) {
+#pragma unroll
+            for (int n = 0; n < 16; ++n) {
+                mfma_one(kk & 1, n);
+                if (n < 8) read_ab(cA, cB, kk + 1, (kk + 1) & 1, n);
+                else if (kk < 2 && (n & 1) == 0) issue_load<BK>(oa, lA, wid, 4 * kk + (n - 8) / 2, ra_, sa);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        wait_vm_lgkm0<LPW>();  // A(ks+1), B(ks+1) landed; A(ks+2) may be in flight
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        const bool more = ks + 1 < nk;
+        constexpr int fl = (KK - 1) & 1;
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+            mfma_one(fl, n);
+            if (n < LPW) issue_load<BK>(ob, lB, wid, n, rb_, sb);
+            if (n >= 8 && more) read_ab(nA, nB, 0, 0, n - 8);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if (nk > 0 && SLOTS5) {
+        static_assert(!SLOTS5 || (KK == 4 && LPW == 8 && 5 * OPB <= (int)sizeof(GemmSmem)),
+                      "five-slot ring layout");
+        const uint32_t base32 = lds_addr(sm.st);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            rsrc_t ra_, rb_;
+            uint32_t sa, sb;
+            load_src(p, ra_, rb_, sa, sb);
+#pragma unroll
+            for (int i = 0; i < LPW; ++i) {
+                issue_load<BK>(oa, base32 + (2 * p) * OPB, wid, i, ra_, sa);
+                issue_load<BK>(ob, base32 + (2 * p + 1) * OPB, wid, i, rb_, sb);
+            }
+        }
+        wait_vm_lgkm0<LPS>();  // step 0 landed
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) read_ab(sm.st, sm.st + OPB, 0, 0, r);
+        for (int ks = 0; ks < nk; ks += 5) {
+#pragma unroll
+            for (int u = 0; u < 5; ++u)
+                if (ks + u < nk) kstep5(u, ks + u);
+        }
+        wait_vm_lgkm0<0>();  // no load may still be writing LDS when the block ends
+    } else if (nk > 0) {
+        const uint32_t st_base = lds_addr(sm.st);  // stage p at st_base + p * 2 * OPB
 #pragma unroll
         for (int p = 0; p < NST; ++p) {
             rsrc_t ra_, rb_;
@@ -436,20 +565,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
             load_src(p, ra_, rb_, sa, sb);
 #pragma unroll
             for (int i = 0; i < LPW; ++i) {
-                issue_load(oa, st_base + p * 2 * OPB, i, ra_, sa);
-                issue_load(ob, st_base + p * 2 * OPB + OPB, i, rb_, sb);
+                issue_load<BK>(oa, st_base + p * 2 * OPB, wid, i, ra_, sa);
+                issue_load<BK>(ob, st_base + p * 2 * OPB + OPB, wid, i, rb_, sb);
             }
         }
         wait_vm_lgkm0<(NST - 1) * LPS>();  // step 0 landed
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) read_one(sm.st[0], 0, 0, r);
+        for (int r = 0; r < 8; ++r) read_one(sm.st, 0, 0, r);
         for (int ks = 0; ks < nk; ks += NST) {
 #pragma unroll
             for (int u = 0; u < NST; ++u)
                 if (ks + u < nk)
-                    kstep(sm.st[u], sm.st[(u + 1) % NST], st_base + u * 2 * OPB, ks + u);
+                    kstep(sm.st + u * 2 * OPB, sm.st + ((u + 1) % NST) * 2 * OPB, st_base + u * 2 * OPB, ks + u);
         }
         wait_vm_lgkm0<0>();  // no load may still be writing LDS when the block ends
     }
@@ -478,6 +607,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
                 }
         }
     } else if (EPI == EPI_SWIGLU) {
+        // block (i, j) of a lane: channels ch0 + 64 wn + 16 j + 8 hf + lcol .. +3 (hf = 0, 1),
+        // gate at accumulators 4 hf .. +3, up at 8 + 4 hf .. +3
         bf16_t* C = g.C + e * g.c_es + (int64_t)row0 * g.ldc;
         bf16_t* C2 = g.C2 ? g.C2 + e * g.c2_es + (int64_t)row0 * g.ldc2 : nullptr;
 #pragma unroll
@@ -485,15 +616,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
             const int row = m0 + wm * 128 + i * 32 + lrow;
             if (row >= Mvalid) continue;
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int ch = ch0 + wn * 64 + j * 32 + 8 * q + lcol;
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int ch = ch0 + wn * 64 + j * 16 + 8 * hf + lcol;
                     if (ch >= g.I) continue;
+                    const f32x16& a = acc[i][j];
                     float hv[4];
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
-                        const float gv = acc[i][j][4 * q + c], uv = acc[i][j + 2][4 * q + c];
+                        const float gv = a[4 * hf + c], uv = a[8 + 4 * hf + c];
                         hv[c] = gv / (1.0f + __expf(-gv)) * uv;
                     }
                     *reinterpret_cast<uint2*>(C + (int64_t)row * g.ldc + ch) =
@@ -501,11 +633,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
                     if (C2) {
                         bf16_t* gr = C2 + (int64_t)row * g.ldc2;
                         *reinterpret_cast<uint2*>(gr + ch) =
-                            make_uint2(pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                                       pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+                            make_uint2(pack_bf2(a[4 * hf], a[4 * hf + 1]),
+                                       pack_bf2(a[4 * hf + 2], a[4 * hf + 3]));
                         *reinterpret_cast<uint2*>(gr + g.I + ch) =
-                            make_uint2(pack_bf2(acc[i][j + 2][4 * q], acc[i][j + 2][4 * q + 1]),
-                                       pack_bf2(acc[i][j + 2][4 * q + 2], acc[i][j + 2][4 * q + 3]));
+                            make_uint2(pack_bf2(a[8 + 4 * hf], a[8 + 4 * hf + 1]),
+                                       pack_bf2(a[8 + 4 * hf + 2], a[8 + 4 * hf + 3]));
                     }
                 }
         }
@@ -545,12 +677,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
 }
 
 // One kernel symbol per product of the layer, so that profiles name each role.
+// K step per product: 64 where both operands are K-major (128-byte rows), 32 for the wgrad
+// products (MN-major operands: deeper prefetch); the dgrad products mix one of each.
+#ifndef MOE_BK_DGRAD
+#define MOE_BK_DGRAD 64
+#endif
+constexpr int BK_FWD = 64, BK_DGRAD = MOE_BK_DGRAD, BK_WGRAD = 32;
+
 #define MOE_GEMM_KERNEL(NAME, AKM, BKM, EPI, GK)                                       \
     __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) void \
     NAME(GemmArgs g) {                                                                 \
         __shared__ GemmSmem sm;                                                        \
         const int total = tile_total<EPI, GK>(g);                                      \
-        if ((int)blockIdx.x < total) gemm_tile<AKM, BKM, EPI, GK>(g, sm, blockIdx.x);  \
+        if ((int)blockIdx.x < total) gemm_tile<BK_FWD, AKM, BKM, EPI, GK>(g, sm, blockIdx.x);  \
     }
 MOE_GEMM_KERNEL(gemm1_swiglu, true, true, EPI_SWIGLU, false)     // [g|u] = Xp W1^T, h
 MOE_GEMM_KERNEL(gemm2_down, true, true, EPI_STORE, false)        // y = h W2^T
@@ -566,8 +705,8 @@ void bwd_down(GemmArgs gd, GemmArgs gw) {
     __shared__ GemmSmem sm;
     const int td = tile_total<EPI_DSWIGLU, false>(gd);
     const int b = blockIdx.x;
-    if (b < td) gemm_tile<true, false, EPI_DSWIGLU, false>(gd, sm, b);
-    else if (b - td < gw.total) gemm_tile<false, false, EPI_STORE, true>(gw, sm, b - td);
+    if (b < td) gemm_tile<BK_DGRAD, true, false, EPI_DSWIGLU, false>(gd, sm, b);
+    else if (b - td < gw.total) gemm_tile<BK_WGRAD, false, false, EPI_STORE, true>(gw, sm, b - td);
 }
 
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -575,8 +714,8 @@ void bwd_gate_up(GemmArgs gd, GemmArgs gw) {
     __shared__ GemmSmem sm;
     const int td = tile_total<EPI_STORE, false>(gd);
     const int b = blockIdx.x;
-    if (b < td) gemm_tile<true, false, EPI_STORE, false>(gd, sm, b);
-    else if (b - td < gw.total) gemm_tile<false, false, EPI_STORE, true>(gw, sm, b - td);
+    if (b < td) gemm_tile<BK_DGRAD, true, false, EPI_STORE, false>(gd, sm, b);
+    else if (b - td < gw.total) gemm_tile<BK_WGRAD, false, false, EPI_STORE, true>(gw, sm, b - td);
 }
 
 // Upper bound on the tile count of a ragged-M product (host side, no device data).
