@@ -13,10 +13,12 @@
 // Design (CDNA4, wave64):
 //  - 256x256 output tile per 256-thread block, 4 waves in 2x2, each wave a 128x128 sub-tile
 //    of 4x4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane, one wave per SIMD).
-//  - K steps of 64 through two LDS stages of 64 KB, filled by direct global-to-LDS buffer
-//    loads one step ahead of their use; one barrier per step.  A K-major tile row is then
-//    128 contiguous bytes per step (a whole L2 line), which halves the L2 requests of the
-//    32-wide step: the loads, not the MFMAs, are what the L2 can serve at this tile size.
+//  - K steps of 64: a K-major tile row is then 128 contiguous bytes per step (a whole L2
+//    line per request).  At this tile size the chip's L2 can just about feed the MFMAs
+//    (both need about a tile's K loop worth of 229K cycles), so the loads must stream
+//    evenly: the operands of a step sit in a ring of five 32 KB LDS slots, filled by direct
+//    global-to-LDS buffer loads one to two steps ahead, four loads per 16-MFMA sub-step;
+//    one barrier per step.
 //  - Operands contiguous along K are read from LDS with ds_read_b128; operands contiguous
 //    along M or N (the weights in dgrad, both operands in wgrad) are stored as loaded and
 //    read with the transposing ds_read_b64_tr_b16.  Both LDS layouts are swizzled so that
@@ -490,19 +492,25 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         }
     };
     // Five operand slots (BK = 64): operand slots of OPB bytes in a ring of five, A of step s
-    // in slot 2s mod 5 and B in slot 2s+1 mod 5.  Of each step's loads, A(s+2) goes into the
-    // slot B(s-1) left at the previous step's barrier and is issued during the first two
-    // sub-steps, B(s+2) into the slot A(s) leaves at this step's barrier and is issued in the
-    // last sub-step: half of the loads get two steps to land instead of one, and the loads
-    // are spread over the step instead of bunched after the barrier.
+    // in slot 2s mod 5 and B in slot 2s+1 mod 5.  Slots free up at the step barriers (which
+    // follow the last LDS reads of a step): A(s+2) goes into the slot B(s-1) left, B(s+2)
+    // into the slot A(s) leaves.  Four loads are issued per sub-step: in step s, the second
+    // half of B(s+1) (sub-step 0), A(s+2) (sub-steps 1, 2) and after the barrier the first
+    // half of B(s+2) (sub-step 3).  A gets two steps to land, B more than one, and the load
+    // path sees an even stream instead of bursts after each barrier.
+    rsrc_t pend_rb = make_rsrc(nullptr, 0);  // descriptor and offset of B(s+1)'s second half
+    uint32_t pend_sb = 0;
     auto kstep5 = [&](int u, int ks) __attribute__((always_inline)) {
         char* const cA = sm.st + ((2 * u) % 5) * OPB;
         char* const cB = sm.st + ((2 * u + 1) % 5) * OPB;
         char* const nA = sm.st + ((2 * u + 2) % 5) * OPB;
         char* const nB = sm.st + ((2 * u + 3) % 5) * OPB;
         const uint32_t base32 = lds_addr(sm.st);
-        const uint32_t lA = base32 + ((2 * u + 4) % 5) * OPB;  // A(ks+2): slot of B(ks-1)
-        const uint32_t lB = base32 + ((2 * u) % 5) * OPB;      // B(ks+2): slot of A(ks)
+        const uint32_t lB1 = base32 + ((2 * u + 3) % 5) * OPB;  // B(ks+1): slot of A(ks-1)
+        const uint32_t lA = base32 + ((2 * u + 4) % 5) * OPB;   // A(ks+2): slot of B(ks-1)
+        const uint32_t lB = base32 + ((2 * u) % 5) * OPB;       // B(ks+2): slot of A(ks)
+        const rsrc_t rb1 = pend_rb;
+        const uint32_t sb1 = pend_sb;
         rsrc_t ra_, rb_;
         uint32_t sa, sb;
         load_src(ks + 2, ra_, rb_, sa, sb);
@@ -513,7 +521,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
             for (int n = 0; n < 16; ++n) {
                 mfma_one(kk & 1, n);
                 if (n < 8) read_ab(cA, cB, kk + 1, (kk + 1) & 1, n);
-                else if (kk < 2 && (n & 1) == 0) issue_load<BK>(oa, lA, wid, 4 * kk + (n - 8) / 2, ra_, sa);
+                else if ((n & 1) == 0) {
+                    const int q = (n - 8) / 2;  // 0..3
+                    if (kk == 0) issue_load<BK>(ob, lB1, wid, 4 + q, rb1, sb1);
+                    else issue_load<BK>(oa, lA, wid, 4 * (kk - 1) + q, ra_, sa);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -525,15 +537,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
             mfma_one(fl, n);
-            if (n < LPW) issue_load<BK>(ob, lB, wid, n, rb_, sb);
+            if (n < 8 && (n & 1) == 0) issue_load<BK>(ob, lB, wid, n / 2, rb_, sb);
             if (n >= 8 && more) read_ab(nA, nB, 0, 0, n - 8);
             __builtin_amdgcn_sched_barrier(0);
         }
+        pend_rb = rb_;
+        pend_sb = sb;
     };
     if (nk > 0 && SLOTS5) {
         static_assert(!SLOTS5 || (KK == 4 && LPW == 8 && 5 * OPB <= (int)sizeof(GemmSmem)),
                       "five-slot ring layout");
         const uint32_t base32 = lds_addr(sm.st);
+        // A(0), B(0), A(1) and the first half of B(1); step 0 issues B(1)'s second half
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             rsrc_t ra_, rb_;
@@ -542,10 +557,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
 #pragma unroll
             for (int i = 0; i < LPW; ++i) {
                 issue_load<BK>(oa, base32 + (2 * p) * OPB, wid, i, ra_, sa);
-                issue_load<BK>(ob, base32 + (2 * p + 1) * OPB, wid, i, rb_, sb);
+                if (p == 0 || i < LPW / 2)
+                    issue_load<BK>(ob, base32 + (2 * p + 1) * OPB, wid, i, rb_, sb);
             }
+            pend_rb = rb_;
+            pend_sb = sb;
         }
-        wait_vm_lgkm0<LPS>();  // step 0 landed
+        wait_vm_lgkm0<LPW + LPW / 2>();  // step 0 landed
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -677,12 +695,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
 }
 
 // One kernel symbol per product of the layer, so that profiles name each role.
-// K step per product: 64 where both operands are K-major (128-byte rows), 32 for the wgrad
-// products (MN-major operands: deeper prefetch); the dgrad products mix one of each.
-#ifndef MOE_BK_DGRAD
-#define MOE_BK_DGRAD 64
-#endif
-constexpr int BK_FWD = 64, BK_DGRAD = MOE_BK_DGRAD, BK_WGRAD = 32;
+// K step per product.  Every product measures fastest with 64-wide steps in the five-slot
+// ring (the 32-wide ring of four stages stays available to the tile routine).
+constexpr int BK_FWD = 64, BK_DGRAD = 64, BK_WGRAD = 64;
 
 #define MOE_GEMM_KERNEL(NAME, AKM, BKM, EPI, GK)                                       \
     __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) void \
