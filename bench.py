@@ -60,6 +60,12 @@ def parse():
     ap.add_argument("--ring-depth", type=int, default=16,
                     help="minibatches per pass of the macrobatch ring (workloads that stream "
                          "tokens in minibatches)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="calibration run: only a plain device copy (read N MiB, write N MiB) "
+                         "a few times, for scaling hardware byte counters; prints its size")
+    ap.add_argument("--traffic-from", default="",
+                    help="no GPU: condense rocprofv3 counter runs under this folder (subfolders "
+                         "fetch/, write/, copy_fetch/, copy_write/) into profiles/hbm_traffic.json")
     return ap.parse_args()
 
 
@@ -91,18 +97,30 @@ def role_work(wl, role: str, shared: bool) -> tuple[str, float]:
     return "byte", 0.0
 
 
-def roofline_of(wl, role: str, per_launch_ms: float, traffic) -> dict:
+def step_work(wl, role: str) -> tuple[str, float]:
+    """Algorithmic work of `role` over one step: the routed experts' share plus, for the BF16
+    GEMMs, the shared experts' (each of them runs on every source token)."""
     kind, work = role_work(wl, role, shared=False)
+    if role in GEMM_ROLES and not GEMM_ROLES[role][1] and wl.S and not wl.local_share:
+        work += wl.S * role_work(wl, role, shared=True)[1]
+    return kind, work
+
+
+def roofline_of(wl, role: str, ms_per_step: float, launches: float, traffic) -> dict:
+    """Roofline of `role`: its algorithmic work per step over its measured time per step (the
+    sum of its launch durations), and the same per launch."""
+    kind, work = step_work(wl, role)
+    per_launch_ms = ms_per_step / launches
+    common = {"work_per_launch": work / launches, "avg_launch_ms": round(per_launch_ms, 4),
+              "launches_per_step": launches}
     if kind == "flop":
         peak = PEAK_MXFP8_TFLOPS if GEMM_ROLES[role][1] else PEAK_BF16_TFLOPS
-        ach = work / (per_launch_ms * 1e-3) / 1e12
+        ach = work / (ms_per_step * 1e-3) / 1e12
         return {"kernel": role, "bound": "mfma", "achieved": round(ach, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
-                "work_per_launch": work, "avg_launch_ms": round(per_launch_ms, 4)}
-    ach = work / (per_launch_ms * 1e-3) / 1e9
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic, **common}
+    ach = work / (ms_per_step * 1e-3) / 1e9
     return {"kernel": role, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "work_per_launch": work, "avg_launch_ms": round(per_launch_ms, 4)}
+            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, **common}
 
 
 def kernel_source_digest() -> str:
@@ -128,6 +146,92 @@ def measured_traffic(workload: str, role: str):
         return None
     ent = d.get("workloads", {}).get(workload, {}).get(role)
     return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- HBM traffic
+COPY_KERNEL_HINT = "MulFunctor"   # torch's elementwise multiply: the calibration copy
+
+
+def role_of_symbol(sym: str) -> str:
+    """Launch role of a kernel symbol as rocprofv3 names it (demangled)."""
+    base = sym.split("(")[0].split("<")[0].strip()
+    base = base.split(" ")[-1].split("::")[-1]
+    if base.endswith("_kernel"):
+        base = base[: -len("_kernel")]
+    return {"count": "perm_count", "scan": "perm_scan", "rank": "perm_rank"}.get(base, base)
+
+
+def _counter_means(folder: str, counter: str) -> dict[str, tuple[int, float]]:
+    """kernel symbol -> (dispatches, mean counter value) over every counter CSV in folder."""
+    import csv
+    import glob
+    acc: dict[str, list[float]] = {}
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (len(v), sum(v) / len(v)) for k, v in acc.items()}
+
+
+def write_traffic(folder: str, workload: str, copy_mib: int) -> None:
+    """profiles/hbm_traffic.json from four rocprofv3 --pmc runs: FETCH_SIZE and WRITE_SIZE (KiB
+    per dispatch) of the layer's kernels, each scaled by the ratio of the known size of a plain
+    copy to what the same counter reads for it."""
+    known_kib = copy_mib * 1024.0
+    scale = {}
+    for ctr, sub in (("FETCH_SIZE", "copy_fetch"), ("WRITE_SIZE", "copy_write")):
+        m = {k: v for k, v in _counter_means(os.path.join(folder, sub), ctr).items()
+             if COPY_KERNEL_HINT in k}
+        if not m:
+            raise SystemExit(f"no copy kernel ({COPY_KERNEL_HINT}) in {sub}")
+        _, kib = max(m.values(), key=lambda t: t[1])
+        scale[ctr] = known_kib / kib
+    fetch = _counter_means(os.path.join(folder, "fetch"), "FETCH_SIZE")
+    write = _counter_means(os.path.join(folder, "write"), "WRITE_SIZE")
+    roles = {}
+    for sym in sorted(set(fetch) | set(write)):
+        if COPY_KERNEL_HINT in sym or "moe::" not in sym:
+            continue
+        role = role_of_symbol(sym)
+        n, fk = fetch.get(sym, (0, 0.0))
+        _, wk_ = write.get(sym, (0, 0.0))
+        fb, wb = fk * 1024 * scale["FETCH_SIZE"], wk_ * 1024 * scale["WRITE_SIZE"]
+        roles[role] = {"symbol": sym, "dispatches": n, "fetch_kib_raw": round(fk, 1),
+                       "write_kib_raw": round(wk_, 1), "fetch_bytes": round(fb),
+                       "write_bytes": round(wb), "hbm_bytes_per_launch": round(fb + wb)}
+    out = {"kernel_source_digest": kernel_source_digest(),
+           "counters": "rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE (separate runs), "
+                       "mean KiB per dispatch",
+           "copy_calibration": {"kernel": COPY_KERNEL_HINT, "mib": copy_mib,
+                                "fetch_scale": round(scale["FETCH_SIZE"], 4),
+                                "write_scale": round(scale["WRITE_SIZE"], 4)},
+           "workloads": {workload: roles}}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(f"| role | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes/launch (scaled) |")
+    print(f"|---|---|---|---|---|")
+    for r, e in roles.items():
+        print(f"| {r} | {e['dispatches']} | {e['fetch_kib_raw']} | {e['write_kib_raw']} | "
+              f"{e['hbm_bytes_per_launch']:.4g} |")
+    print(f"copy scales: fetch {scale['FETCH_SIZE']:.4f} write {scale['WRITE_SIZE']:.4f}; "
+          f"wrote {path}")
+
+
+def copy_calibration(mib: int) -> None:
+    """A plain device copy of known size (read mib MiB, write mib MiB), five times."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_mib": mib, "read_bytes": n * 4, "write_bytes": n * 4}), flush=True)
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -166,6 +270,9 @@ def cpu_baseline(wl, inp, n_tokens: int) -> dict:
 # ----------------------------------------------------------------------------- main
 def main():
     a = parse()
+    if a.traffic_from:
+        write_traffic(a.traffic_from, a.workload, a.copy_mib or 1024)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print("bench.py measures one GPU's share of the layer on one GPU; runs on more than one "
@@ -179,6 +286,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if a.copy_mib:
+        copy_calibration(a.copy_mib)
+        return
     moe.lib()  # fails loudly when the HIP library is missing
     wl = wk.WORKLOADS[a.workload]
     dev = "cuda:0"
@@ -224,8 +334,8 @@ def main():
         roles.setdefault(name, []).append(ms)
     per_step = {r: sum(v) / a.steps for r, v in roles.items()}
     dominant = max(per_step, key=per_step.get)
-    avg = sum(roles[dominant]) / len(roles[dominant])
-    roof = roofline_of(wl, dominant, avg, measured_traffic(a.workload, dominant))
+    roof = roofline_of(wl, dominant, per_step[dominant], len(roles[dominant]) / a.steps,
+                       measured_traffic(a.workload, dominant))
 
     flops_fwd = wl.fwd_flops()
     flops_step = flops_fwd * (3.0 if wl.backward else 1.0)
@@ -234,13 +344,11 @@ def main():
         n = len(roles[r]) / a.steps
         ent = {"launches_per_step": n, "ms_per_step": round(per_step[r], 4),
                "share": round(per_step[r] / ms_step, 4)}
-        if r in GEMM_ROLES and n == 1:
-            kind, work = role_work(wl, r, False)
+        kind, work = step_work(wl, r)
+        if kind == "flop":
             ent["tflops"] = round(work / (per_step[r] * 1e-3) / 1e12, 1)
-        elif r not in GEMM_ROLES and n == 1:
-            kind, work = role_work(wl, r, False)
-            if work:
-                ent["gbs"] = round(work / (per_step[r] * 1e-3) / 1e9, 1)
+        elif work and n == 1:
+            ent["gbs"] = round(work / (per_step[r] * 1e-3) / 1e9, 1)
         breakdown[r] = ent
     if a.breakdown:
         for r, e in breakdown.items():
