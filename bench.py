@@ -88,6 +88,8 @@ def role_work(wl, role: str, shared: bool) -> tuple[str, float]:
         return "byte", float(T * H * bf + 2 * R * H * bf + T * k * 12)
     if role == "unpermute":
         return "byte", float(R * H * bf + wl.S * T * H * bf + T * H * bf + T * k * 4)
+    if role == "router_proj":       # x and the router weight read, fp32 logits written
+        return "byte", float(T * H * bf + wl.ER * H * bf + T * wl.ER * 4)
     if role == "topk":
         return "byte", float(T * wl.ER * 4 + T * wl.k * 12)
     if role == "router_bwd":
