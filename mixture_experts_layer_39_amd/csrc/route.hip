@@ -237,21 +237,39 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
 }
 
 // One block: counts[e] = sum over chunks; offsets = exclusive scan over e; blk[c][e]
-// becomes the first row of expert e owned by chunk c.
+// becomes the first row of expert e owned by chunk c.  The chunk histograms are staged
+// through LDS with coalesced loads when they fit (SCAN_LDS ints), so that the per-expert
+// running sums walk LDS instead of a chain of dependent global loads and stores.
+constexpr int SCAN_LDS = 32768;  // 128 KB
+
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blk, int nchunks, int E,
                                                     int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets) {
     __shared__ int wsum[16];
+    __shared__ int exo[1024];    // offsets[e], for the write-back
+    __shared__ int hs[SCAN_LDS];  // [nchunks][E] when staged
     const int e = threadIdx.x;
+    const int64_t tot = (int64_t)nchunks * E;
+    const bool staged = tot <= SCAN_LDS;
     int run = 0;
-    if (e < E) {
+    if (staged) {
+        for (int i = threadIdx.x; i < (int)tot; i += 1024) hs[i] = blk[i];
+        __syncthreads();
+        if (e < E) {
+            for (int c = 0; c < nchunks; ++c) {
+                const int v = hs[c * E + e];
+                hs[c * E + e] = run;
+                run += v;
+            }
+        }
+    } else if (e < E) {
         for (int c = 0; c < nchunks; ++c) {
-            int v = blk[(size_t)c * E + e];
+            const int v = blk[(size_t)c * E + e];
             blk[(size_t)c * E + e] = run;
             run += v;
         }
-        counts[e] = run;
     }
+    if (e < E) counts[e] = run;
     // exclusive scan of run over e (block of 1024 = 16 waves)
     int incl = wave_incl_scan(e < E ? run : 0);
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -259,13 +277,18 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blk, i
     __syncthreads();
     int base = 0;
     for (int w = 0; w < wid; ++w) base += wsum[w];
-    int excl = base + incl - (e < E ? run : 0);
-    if (e < E) {
-        offsets[e] = excl;
-        for (int c = 0; c < nchunks; ++c) blk[(size_t)c * E + e] += excl;
-    }
+    const int excl = base + incl - (e < E ? run : 0);
+    if (e < E) offsets[e] = excl;
     if (e == E - 1) offsets[E] = excl + run;
     if (E == 0 && e == 0) offsets[0] = 0;
+    if (staged) {
+        // every thread writes back entries of every expert: publish the offsets in LDS
+        if (e < E) exo[e] = excl;
+        __syncthreads();
+        for (int i = threadIdx.x; i < (int)tot; i += 1024) blk[i] = hs[i] + exo[i % E];
+    } else if (e < E) {
+        for (int c = 0; c < nchunks; ++c) blk[(size_t)c * E + e] += excl;
+    }
 }
 
 // One wave per chunk: ranks the chunk's pairs in order.  Pairs with equal expert among
