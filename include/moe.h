@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* return codes */
 #define MOE_OK 0
@@ -104,14 +104,21 @@ int moe_route(const float *logits, const void *x, const void *w_router, int T, i
               void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------ dispatch
- * moe_dispatch: gather token rows into expert-contiguous order ("pull": the destination row
- * fetches its source, pulsen.vercel.app ¶5): xp[r,:] = x[src[r]/k,:], r in [0,R).
+ * moe_dispatch: gather token rows into expert-contiguous order ("pull": the expert-side rows
+ * fetch their source, pulsen.vercel.app ¶5): xp[r,:] = x[src[r]/k,:], r in [0,R).
+ *   src       [R] (the permutation of moe_route), or NULL when pos is given.
+ *   pos       [T,k] (the inverse permutation of moe_route), or NULL.  When given, each token's
+ *             k destination rows are filled together from one read of its source row (the
+ *             source is read once instead of k times): xp[pos[t,j],:] = x[t,:] for every
+ *             pos[t,j] in [0,R); rows that no pos entry names are left unwritten.  When NULL,
+ *             every row r in [0,R) is written from src, and src values outside [0, T*k)
+ *             produce zero rows.
  *   xp        [R,H] bf16 or NULL: bf16 copy (bit-exact).
  *   xp_codes  [R,H] E4M3 and xp_scales [R,H/32] E8M0, or both NULL: the rows MX-quantised
  *             (MOE_MX_FLOOR) in the same pass.  At least one output must be given.
- * src values outside [0, T*k) produce zero rows.  H % 8 == 0 (H % 32 == 0 for MX). */
-int moe_dispatch(const void *x, int T, int H, int k, const int32_t *src, int R, void *xp,
-                 uint8_t *xp_codes, uint8_t *xp_scales, void *stream);
+ * H % 8 == 0 (H % 32 == 0 for MX); k <= 64 when pos is given. */
+int moe_dispatch(const void *x, int T, int H, int k, const int32_t *src, const int32_t *pos,
+                 int R, void *xp, uint8_t *xp_codes, uint8_t *xp_scales, void *stream);
 
 /* ------------------------------------------------------------------ expert FFN
  * moe_expert_ffn: per expert e, for its rows r in [offsets[e], offsets[e+1]):

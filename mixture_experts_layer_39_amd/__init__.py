@@ -68,7 +68,7 @@ def lib() -> ctypes.CDLL:
         L.moe_route_workspace_size.argtypes = [_i, _i, _i]
         L.moe_route.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, ctypes.POINTER(RouteCfg), _vp,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
-        L.moe_dispatch.argtypes = [_vp, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _vp]
+        L.moe_dispatch.argtypes = [_vp, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp]
         L.moe_ffn_workspace_size.restype = _sz
         L.moe_ffn_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i]
         L.moe_expert_ffn.argtypes = [_i, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
@@ -135,9 +135,10 @@ def moe_route(logits, T, E, k, *, x=None, w_router=None, H=0, score=SCORE_SOFTMA
     _check("moe_route", rc)
 
 
-def moe_dispatch(x, T, H, k, src, R, xp=None, xp_codes=None, xp_scales=None, stream=None):
-    rc = lib().moe_dispatch(_p(x), T, H, k, _p(src), R, _p(xp), _p(xp_codes), _p(xp_scales),
-                            _stream(stream))
+def moe_dispatch(x, T, H, k, src, R, xp=None, xp_codes=None, xp_scales=None, stream=None,
+                 pos=None):
+    rc = lib().moe_dispatch(_p(x), T, H, k, _p(src), _p(pos), R, _p(xp), _p(xp_codes),
+                            _p(xp_scales), _stream(stream))
     _check("moe_dispatch", rc)
 
 

@@ -497,7 +497,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     // into the slot A(s) leaves.  Four loads are issued per sub-step: in step s, the second
     // half of B(s+1) (sub-step 0), A(s+2) (sub-steps 1, 2) and after the barrier the first
     // half of B(s+2) (sub-step 3).  A gets two steps to land, B more than one, and the load
-    // path sees an even stream instead of bursts after each barrier.
+    // path sees an even stream instead of bursts after each barrier.  Within a sub-step the
+    // 8 fragment reads take the even MFMA slots and the 4 loads every fourth odd one.
     rsrc_t pend_rb = make_rsrc(nullptr, 0);  // descriptor and offset of B(s+1)'s second half
     uint32_t pend_sb = 0;
     auto kstep5 = [&](int u, int ks) __attribute__((always_inline)) {
@@ -520,9 +521,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
 #pragma unroll
             for (int n = 0; n < 16; ++n) {
                 mfma_one(kk & 1, n);
-                if (n < 8) read_ab(cA, cB, kk + 1, (kk + 1) & 1, n);
-                else if ((n & 1) == 0) {
-                    const int q = (n - 8) / 2;  // 0..3
+                if ((n & 1) == 0) read_ab(cA, cB, kk + 1, (kk + 1) & 1, n / 2);
+                else if ((n & 3) == 1) {
+                    const int q = n / 4;  // 0..3
                     if (kk == 0) issue_load<BK>(ob, lB1, wid, 4 + q, rb1, sb1);
                     else issue_load<BK>(oa, lA, wid, 4 * (kk - 1) + q, ra_, sa);
                 }
@@ -537,8 +538,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
             mfma_one(fl, n);
-            if (n < 8 && (n & 1) == 0) issue_load<BK>(ob, lB, wid, n / 2, rb_, sb);
-            if (n >= 8 && more) read_ab(nA, nB, 0, 0, n - 8);
+            if ((n & 3) == 1) issue_load<BK>(ob, lB, wid, n / 4, rb_, sb);
+            if ((n & 1) == 0 && more) read_ab(nA, nB, 0, 0, n / 2);
             __builtin_amdgcn_sched_barrier(0);
         }
         pend_rb = rb_;

@@ -65,6 +65,7 @@ __device__ __forceinline__ int mx_block(const float* v, int mode, uint32_t* q) {
 // 16-byte loads (up to UN) before any store, so a CU keeps enough bytes in flight to cover
 // the memory latency.
 constexpr int ROW_UN = 8;
+constexpr int MAXK = 64;  // largest k the row kernels stage in LDS
 
 __global__ __launch_bounds__(128) void dispatch_kernel(const bf16_t* __restrict__ x, int64_t n_pairs,
                                                        int H, int k, const int32_t* __restrict__ src,
@@ -85,7 +86,39 @@ __global__ __launch_bounds__(128) void dispatch_kernel(const bf16_t* __restrict_
 #pragma unroll
         for (int u = 0; u < ROW_UN; ++u) {
             const int c = c0 + u * 128;
-            if (c < nc) st16_nt(out + c * 8, v[u]);
+            if (c < nc) st16(out + c * 8, v[u]);
+        }
+    }
+}
+
+// Token-driven dispatch: one block per source token fills the token's k destination rows
+// (pos[t,j]) from one read of its source row.
+__global__ __launch_bounds__(128) void dispatch_tok_kernel(const bf16_t* __restrict__ x, int H,
+                                                           int k, const int32_t* __restrict__ pos,
+                                                           int R, bf16_t* __restrict__ xp) {
+    __shared__ int sp[MAXK];
+    const int t = blockIdx.x;
+    const bf16_t* in = x + (size_t)t * H;
+    if (threadIdx.x < k) sp[threadIdx.x] = pos[(size_t)t * k + threadIdx.x];
+    const int nc = H / 8;
+    // the loop bound is block-uniform, so the barrier (pos staged) in its first pass is too
+    for (int c0 = 0; c0 < nc; c0 += 128 * ROW_UN) {
+        u32x4 v[ROW_UN];
+#pragma unroll
+        for (int u = 0; u < ROW_UN; ++u) {
+            const int c = c0 + threadIdx.x + u * 128;
+            v[u] = c < nc ? ld16(in + c * 8) : u32x4{0, 0, 0, 0};
+        }
+        if (c0 == 0) __syncthreads();
+        for (int j = 0; j < k; ++j) {
+            const int r = sp[j];
+            if (r < 0 || r >= R) continue;
+            bf16_t* out = xp + (size_t)r * H;
+#pragma unroll
+            for (int u = 0; u < ROW_UN; ++u) {
+                const int c = c0 + threadIdx.x + u * 128;
+                if (c < nc) st16(out + c * 8, v[u]);
+            }
         }
     }
 }
@@ -120,6 +153,49 @@ __global__ __launch_bounds__(256) void dispatch_mx_kernel(const bf16_t* __restri
     st16(co, u32x4{q[0], q[1], q[2], q[3]});
     st16(co + 16, u32x4{q[4], q[5], q[6], q[7]});
     scales[(size_t)r * nb + b] = (uint8_t)sc;
+}
+
+// Token-driven MX dispatch: one thread per 32-value block of a source token, quantised once
+// and written to each of the token's k destination rows.
+__global__ __launch_bounds__(256) void dispatch_mx_tok_kernel(const bf16_t* __restrict__ x, int H,
+                                                              int k, const int32_t* __restrict__ pos,
+                                                              int R, bf16_t* __restrict__ xp,
+                                                              uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales) {
+    __shared__ int sp[MAXK];
+    const int t = blockIdx.y;
+    const int nb = H / 32;
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    const bool live = b < nb;
+    const bf16_t* in = x + (size_t)t * H + (live ? b : 0) * 32;
+    u32x4 raw[4];
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw[c] = ld16(in + c * 8);
+    if (threadIdx.x < k) sp[threadIdx.x] = pos[(size_t)t * k + threadIdx.x];
+    __syncthreads();
+    if (!live) return;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[c * 8 + 2 * j] = lo_bf(raw[c][j]);
+            v[c * 8 + 2 * j + 1] = hi_bf(raw[c][j]);
+        }
+    uint32_t q[8];
+    const int sc = mx_block(v, MOE_MX_FLOOR, q);
+    for (int j = 0; j < k; ++j) {
+        const int r = sp[j];
+        if (r < 0 || r >= R) continue;
+        if (xp) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) st16(xp + (size_t)r * H + b * 32 + c * 8, raw[c]);
+        }
+        uint8_t* co = codes + (size_t)r * H + b * 32;
+        st16(co, u32x4{q[0], q[1], q[2], q[3]});
+        st16(co + 16, u32x4{q[4], q[5], q[6], q[7]});
+        scales[(size_t)r * nb + b] = (uint8_t)sc;
+    }
 }
 
 // ------------------------------------------------------------------ mx_quantize
@@ -158,9 +234,9 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict
 }
 
 // ------------------------------------------------------------------ combine
+constexpr int RG = 2;  // 16-byte chunks per thread per pass in the gather-reduce kernels
 // One block per token.  Per element, fp32: acc = 0; acc += w[t,j]*y[pos[t,j]] for j = 0..k-1;
 // acc += ys[s,t] for s = 0..S-1; one rounding to bf16.
-constexpr int MAXK = 64;
 
 __global__ __launch_bounds__(128) void combine_kernel(const bf16_t* __restrict__ y,
                                                       const int32_t* __restrict__ pos,
@@ -177,43 +253,55 @@ __global__ __launch_bounds__(128) void combine_kernel(const bf16_t* __restrict__
     }
     __syncthreads();
     const int nc = H / 8;
-    for (int c = threadIdx.x; c < nc; c += 128) {
-        float acc[8];
+    // each thread takes RG chunks per pass and loads every slot's rows of them before
+    // summing any (the summation order per element is unchanged)
+    for (int c0 = threadIdx.x; c0 < nc; c0 += 128 * RG) {
+        float acc[RG][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-        // the rows of up to 8 slots are loaded before any is summed (slot order unchanged)
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
         for (int j0 = 0; j0 < k; j0 += 8) {
-            u32x4 v[8];
+            u32x4 v[RG][8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int j = j0 + u;
-                const int p = j < k ? sp[j] : -1;
-                v[u] = p >= 0 ? ld16(y + (size_t)p * H + c * 8) : u32x4{0, 0, 0, 0};
-            }
+            for (int g = 0; g < RG; ++g)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int j = j0 + u, c = c0 + g * 128;
+                    const int p = j < k ? sp[j] : -1;
+                    v[g][u] = (p >= 0 && c < nc) ? ld16(y + (size_t)p * H + c * 8) : u32x4{0, 0, 0, 0};
+                }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int j = j0 + u;
                 if (j >= k || sp[j] < 0) continue;
                 const float wj = sw[j];
 #pragma unroll
+                for (int g = 0; g < RG; ++g)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[g][2 * q] = __fadd_rn(acc[g][2 * q], __fmul_rn(wj, lo_bf(v[g][u][q])));
+                        acc[g][2 * q + 1] = __fadd_rn(acc[g][2 * q + 1], __fmul_rn(wj, hi_bf(v[g][u][q])));
+                    }
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const int c = c0 + g * 128;
+            if (c >= nc) continue;
+            for (int s = 0; s < S; ++s) {
+                u32x4 v = ld16(ys + ((size_t)s * T + t) * H + c * 8);
+#pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    acc[2 * q] = __fadd_rn(acc[2 * q], __fmul_rn(wj, lo_bf(v[u][q])));
-                    acc[2 * q + 1] = __fadd_rn(acc[2 * q + 1], __fmul_rn(wj, hi_bf(v[u][q])));
+                    acc[g][2 * q] = __fadd_rn(acc[g][2 * q], lo_bf(v[q]));
+                    acc[g][2 * q + 1] = __fadd_rn(acc[g][2 * q + 1], hi_bf(v[q]));
                 }
             }
-        }
-        for (int s = 0; s < S; ++s) {
-            u32x4 v = ld16(ys + ((size_t)s * T + t) * H + c * 8);
+            u32x4 o;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] = __fadd_rn(acc[2 * q], lo_bf(v[q]));
-                acc[2 * q + 1] = __fadd_rn(acc[2 * q + 1], hi_bf(v[q]));
-            }
+            for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[g][2 * q], acc[g][2 * q + 1]);
+            st16(out + (size_t)t * H + c * 8, o);
         }
-        u32x4 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[2 * q], acc[2 * q + 1]);
-        st16_nt(out + (size_t)t * H + c * 8, o);
     }
 }
 
@@ -293,41 +381,54 @@ __global__ __launch_bounds__(128) void unpermute_kernel(const bf16_t* __restrict
     }
     __syncthreads();
     const int nc = H / 8;
-    for (int c = threadIdx.x; c < nc; c += 128) {
-        float acc[8];
+    // each thread takes RG chunks per pass and loads every slot's rows of them before
+    // summing any (the summation order per element is unchanged)
+    for (int c0 = threadIdx.x; c0 < nc; c0 += 128 * RG) {
+        float acc[RG][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
         for (int j0 = 0; j0 < k; j0 += 8) {
-            u32x4 v[8];
+            u32x4 v[RG][8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int j = j0 + u;
-                const int p = j < k ? sp[j] : -1;
-                v[u] = p >= 0 ? ld16(dxp + (size_t)p * H + c * 8) : u32x4{0, 0, 0, 0};
-            }
+            for (int g = 0; g < RG; ++g)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int j = j0 + u, c = c0 + g * 128;
+                    const int p = j < k ? sp[j] : -1;
+                    v[g][u] = (p >= 0 && c < nc) ? ld16(dxp + (size_t)p * H + c * 8) : u32x4{0, 0, 0, 0};
+                }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int j = j0 + u;
                 if (j >= k || sp[j] < 0) continue;
 #pragma unroll
+                for (int g = 0; g < RG; ++g)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[g][2 * q] = __fadd_rn(acc[g][2 * q], lo_bf(v[g][u][q]));
+                        acc[g][2 * q + 1] = __fadd_rn(acc[g][2 * q + 1], hi_bf(v[g][u][q]));
+                    }
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const int c = c0 + g * 128;
+            if (c >= nc) continue;
+            for (int s = 0; s < S; ++s) {
+                u32x4 v = ld16(dxs + ((size_t)s * ldT + t) * H + c * 8);
+#pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    acc[2 * q] = __fadd_rn(acc[2 * q], lo_bf(v[u][q]));
-                    acc[2 * q + 1] = __fadd_rn(acc[2 * q + 1], hi_bf(v[u][q]));
+                    acc[g][2 * q] = __fadd_rn(acc[g][2 * q], lo_bf(v[q]));
+                    acc[g][2 * q + 1] = __fadd_rn(acc[g][2 * q + 1], hi_bf(v[q]));
                 }
             }
-        }
-        for (int s = 0; s < S; ++s) {
-            u32x4 v = ld16(dxs + ((size_t)s * ldT + t) * H + c * 8);
+            u32x4 o;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] = __fadd_rn(acc[2 * q], lo_bf(v[q]));
-                acc[2 * q + 1] = __fadd_rn(acc[2 * q + 1], hi_bf(v[q]));
-            }
+            for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[g][2 * q], acc[g][2 * q + 1]);
+            st16(dx + (size_t)t * H + c * 8, o);
         }
-        u32x4 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[2 * q], acc[2 * q + 1]);
-        st16_nt(dx + (size_t)t * H + c * 8, o);
     }
 }
 
@@ -396,19 +497,34 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restri
 using namespace moe;
 
 // ------------------------------------------------------------------ C ABI
-extern "C" int moe_dispatch(const void* x, int T, int H, int k, const int32_t* src, int R,
-                            void* xp, uint8_t* xp_codes, uint8_t* xp_scales, void* stream) {
+extern "C" int moe_dispatch(const void* x, int T, int H, int k, const int32_t* src,
+                            const int32_t* pos, int R, void* xp, uint8_t* xp_codes,
+                            uint8_t* xp_scales, void* stream) {
     MOE_REQUIRE(T >= 0 && H >= 8 && H % 8 == 0 && k >= 1 && R >= 0);
     MOE_REQUIRE((xp_codes == nullptr) == (xp_scales == nullptr));
     MOE_REQUIRE(xp || xp_codes);
     if (xp_codes) MOE_REQUIRE(H % 32 == 0);
-    MOE_REQUIRE(R == 0 || (x && src));
-    if (R == 0) return MOE_OK;
+    MOE_REQUIRE(R == 0 || (x && (src || pos)));
+    MOE_REQUIRE(!pos || k <= MAXK);
+    if (R == 0 || (pos && T == 0)) return MOE_OK;
     int rc = moe_check_device();
     if (rc) return rc;
     hipStream_t st = (hipStream_t)stream;
     int64_t n_pairs = (int64_t)T * k;
-    if (xp_codes) {
+    if (pos) {
+        if (xp_codes) {
+            int nb = H / 32;
+            dim3 grid((nb + 255) / 256, T);
+            MOE_TRACED("dispatch_mx", st,
+                       dispatch_mx_tok_kernel<<<grid, 256, 0, st>>>((const bf16_t*)x, H, k, pos, R,
+                                                                    (bf16_t*)xp, xp_codes,
+                                                                    xp_scales));
+        } else {
+            MOE_TRACED("dispatch", st,
+                       dispatch_tok_kernel<<<T, 128, 0, st>>>((const bf16_t*)x, H, k, pos, R,
+                                                              (bf16_t*)xp));
+        }
+    } else if (xp_codes) {
         int nb = H / 32;
         dim3 grid((nb + 255) / 256, R);
         MOE_TRACED("dispatch_mx", st,

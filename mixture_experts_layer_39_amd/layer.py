@@ -201,9 +201,10 @@ class MoELayer:
         c = self.cfg
         if c.mx:
             moe_dispatch(self.inp["x"], c.T, c.H, self.kr, self.src, self.R, None, self.xq,
-                         self.xs)
+                         self.xs, pos=self.pos)
         else:
-            moe_dispatch(self.inp["x"], c.T, c.H, self.kr, self.src, self.R, self.xp)
+            moe_dispatch(self.inp["x"], c.T, c.H, self.kr, self.src, self.R, self.xp,
+                         pos=self.pos)
 
     def experts(self):
         c, inp = self.cfg, self.inp
@@ -258,7 +259,7 @@ class MoELayer:
                       ws=self.route_ws)
             r0 = (p if self.has_bwd else 0) * self.pass_rows
             xp, y = self.xp[r0:r0 + Rp], self.y[r0:r0 + Rp]
-            moe_dispatch(x[t0:t1], Tp, H, k, self.src[p], Rp, xp)
+            moe_dispatch(x[t0:t1], Tp, H, k, self.src[p], Rp, xp, pos=self.pos[t0:t1])
             moe_expert_ffn(BF16, xp, self.offsets[p], E, Rp, H, I, inp["w1"], inp["w2"], y,
                            gu_save=None if self.gu is None else self.gu[r0:r0 + Rp],
                            h_save=self.h[r0:r0 + Rp], ws=self.ffn_ws)

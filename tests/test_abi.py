@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert moe.abi_version() == 2
+    assert moe.abi_version() == 3
     assert moe.strerror(0) == "ok"
     assert "workspace" in moe.strerror(-2)
     assert moe.strerror(12345) == "unknown error"
@@ -75,11 +75,13 @@ def test_route_validation():
 
 def test_dispatch_combine_mx_validation():
     L_ = lib()
-    assert L_.moe_dispatch(FAKE, 16, 60, 2, FAKE, 32, FAKE, None, None, None) == moe.MOE_EINVAL
-    assert L_.moe_dispatch(FAKE, 16, 64, 2, FAKE, 32, None, None, None, None) == moe.MOE_EINVAL
-    assert L_.moe_dispatch(FAKE, 16, 64, 2, FAKE, 32, None, FAKE, None, None) == moe.MOE_EINVAL
-    assert L_.moe_dispatch(FAKE, 16, 72, 2, FAKE, 32, None, FAKE, FAKE, None) == moe.MOE_EINVAL
-    assert L_.moe_dispatch(FAKE, 16, 64, 2, FAKE, 0, FAKE, None, None, None) == moe.MOE_OK  # empty
+    assert L_.moe_dispatch(FAKE, 16, 60, 2, FAKE, None, 32, FAKE, None, None, None) == moe.MOE_EINVAL
+    assert L_.moe_dispatch(FAKE, 16, 64, 2, FAKE, None, 32, None, None, None, None) == moe.MOE_EINVAL
+    assert L_.moe_dispatch(FAKE, 16, 64, 2, FAKE, None, 32, None, FAKE, None, None) == moe.MOE_EINVAL
+    assert L_.moe_dispatch(FAKE, 16, 72, 2, FAKE, None, 32, None, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert L_.moe_dispatch(FAKE, 16, 64, 2, None, None, 32, FAKE, None, None, None) == moe.MOE_EINVAL
+    assert L_.moe_dispatch(FAKE, 16, 64, 2, FAKE, None, 0, FAKE, None, None, None) == moe.MOE_OK  # empty
+    assert L_.moe_dispatch(FAKE, 0, 64, 2, None, FAKE, 32, FAKE, None, None, None) == moe.MOE_OK  # no tokens
     assert L_.moe_combine(FAKE, FAKE, FAKE, 16, 2, 64, 32, None, 1, FAKE, None) == moe.MOE_EINVAL
     assert L_.moe_combine(FAKE, FAKE, FAKE, 16, 65, 64, 32, None, 0, FAKE, None) == moe.MOE_EINVAL
     assert L_.moe_combine(FAKE, FAKE, FAKE, 0, 2, 64, 0, None, 0, FAKE, None) == moe.MOE_OK

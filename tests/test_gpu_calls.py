@@ -128,6 +128,17 @@ def test_dispatch_bit_exact_and_mx():
     ref = orc.dispatch(wk.bf16_bits(x), k, src)
     assert np.array_equal(wk.bf16_bits(xp), ref)
     assert np.array_equal(wk.bf16_bits(xp2), ref)
+    # token-driven form (pos): same rows, bit for bit, in both precisions
+    pos_ = np.empty(R, dtype=np.int32)
+    pos_[src] = np.arange(R, dtype=np.int32)
+    pos_d = torch.from_numpy(pos_.reshape(T, k)).to(DEV)
+    xp3 = torch.empty_like(xp)
+    moe.moe_dispatch(x, T, H, k, None, R, xp3, pos=pos_d)
+    xq3, xs3 = torch.empty_like(xq), torch.empty_like(xs)
+    moe.moe_dispatch(x, T, H, k, None, R, None, xq3, xs3, pos=pos_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(wk.bf16_bits(xp3), ref)
+    assert torch.equal(xq3, xq) and torch.equal(xs3, xs)
     cq, cs = orc.mx_quantize(orc.bf16_to_f64(ref))
     assert np.array_equal(host(xq), cq) and np.array_equal(host(xs), cs)
 
