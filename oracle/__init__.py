@@ -117,6 +117,15 @@ def permute(idx, E):
     return counts, offsets, pos, src
 
 
+def update_bias(counts, bias, gamma):
+    """Load-balancing bias update (auxiliary-loss-free balancing of DeepSeek-V3): returns the
+    new fp32 bias; see ``orc_update_bias``."""
+    c = _c(counts, np.int32)
+    b = np.array(bias, dtype=np.float32, copy=True)
+    lib().orc_update_bias(_p(c), int(c.size), ctypes.c_float(gamma), _p(b))
+    return b
+
+
 def dispatch(x_bf16, k, src):
     x = _c(x_bf16, np.uint16)
     src = _c(src, np.int32)

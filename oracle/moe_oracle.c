@@ -256,6 +256,24 @@ void orc_permute(const int32_t *idx, int T, int k, int E, int32_t *counts, int32
     free(fill);
 }
 
+/* ------------------------------------------------------------------ load-balancing bias
+ * Auxiliary-loss-free balancing of DeepSeek-V3 (the layer type of pulsen.vercel.app ¶6; the
+ * rule itself is from the DeepSeek-V3 Technical Report, arXiv:2412.19437, §2.1.2): after a
+ * step, each expert's selection bias moves by gamma against its load -- down when the expert
+ * received more than the mean load, up when it received less, unchanged at the mean.
+ * Reading: load = counts[e], mean = (sum of counts) / E, compared exactly as
+ * counts[e] * E against the sum; the new bias is the fp32 sum bias + (+-gamma), one rounding. */
+void orc_update_bias(const int32_t *counts, int E, float gamma, float *bias)
+{
+    int64_t total = 0;
+    for (int e = 0; e < E; e++) total += counts[e];
+    for (int e = 0; e < E; e++) {
+        int64_t scaled = (int64_t)counts[e] * E;
+        if (scaled > total) bias[e] = bias[e] - gamma;
+        else if (scaled < total) bias[e] = bias[e] + gamma;
+    }
+}
+
 /* ------------------------------------------------------------------ dispatch
  * xp[r,:] = x[src[r] / k, :]  (byte copy). */
 void orc_dispatch(const uint16_t *x, int T, int H, int k, const int32_t *src, int R,
