@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--ring-depth", type=int, default=16,
                     help="minibatches per pass of the macrobatch ring (workloads that stream "
                          "tokens in minibatches)")
+    ap.add_argument("--bias-gamma", type=float, default=0.0,
+                    help="> 0: the sigmoid router's load-balancing bias is updated from the "
+                         "step's loads with this speed (auxiliary-loss-free balancing)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="calibration run: only a plain device copy (read N MiB, write N MiB) "
                          "a few times, for scaling hardware byte counters; prints its size")
@@ -92,6 +95,8 @@ def role_work(wl, role: str, shared: bool) -> tuple[str, float]:
         return "byte", float(T * H * bf + wl.ER * H * bf + T * wl.ER * 4)
     if role == "topk":
         return "byte", float(T * wl.ER * 4 + T * wl.k * 12)
+    if role == "bias_update":       # loads read, bias read and written
+        return "byte", float(wl.ER * 12)
     if role == "router_bwd":
         return "byte", float(T * wl.ER * 4 + T * wl.k * 16)
     if role == "mx_quantize_h":
@@ -297,7 +302,9 @@ def main():
     torch.cuda.set_device(0)
     inp = wk.make_inputs(wl, device=dev)
     ring = dict(minibatch=wl.minibatch, ring_depth=a.ring_depth) if wl.minibatch else {}
-    layer = MoELayer(LayerCfg.from_workload(wl), inp, dev, backward=wl.backward, **ring)
+    lcfg = LayerCfg.from_workload(wl)
+    lcfg.bias_gamma = a.bias_gamma
+    layer = MoELayer(lcfg, inp, dev, backward=wl.backward, **ring)
 
     def step():
         layer.forward()
@@ -364,6 +371,8 @@ def main():
            "parallelism": "none (one GPU's share)"}
     if layer.ring:
         cfg.update(minibatch=layer.mb, ring_depth=layer.D, ring_passes=layer.passes)
+    if a.bias_gamma > 0:
+        cfg.update(bias_gamma=a.bias_gamma)
     out = {
         "metric": METRIC,
         "value": round(wl.T * a.steps / elapsed, 1),

@@ -103,6 +103,17 @@ int moe_route(const float *logits, const void *x, const void *w_router, int T, i
               float *s_sel, int32_t *counts, int32_t *offsets, int32_t *pos, int32_t *src,
               void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------ load balancing
+ * moe_update_bias: the auxiliary-loss-free load balancing of a DeepSeek-V3-type layer
+ * (layer type: pulsen.vercel.app ¶6; rule: DeepSeek-V3 Technical Report, arXiv:2412.19437,
+ * §2.1.2).  After a step, with load counts[e] (e.g. the counts of moe_route) and the mean
+ * load (sum of counts) / E:  bias[e] -= gamma where counts[e] is above the mean,
+ * bias[e] += gamma where it is below, unchanged where equal (compared exactly, as
+ * counts[e] * E against the sum); each update is one fp32 rounding.
+ *   counts  DEVICE [E] int32 (non-negative), bias DEVICE [E] fp32, updated in place (the
+ *           sel_bias of moe_route_cfg).  1 <= E <= 1024.  Bit-exact. */
+int moe_update_bias(const int32_t *counts, int E, float gamma, float *bias, void *stream);
+
 /* ------------------------------------------------------------------ dispatch
  * moe_dispatch: gather token rows into expert-contiguous order ("pull": the expert-side rows
  * fetch their source, pulsen.vercel.app ¶5): xp[r,:] = x[src[r]/k,:], r in [0,R).

@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
         L.moe_route.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, ctypes.POINTER(RouteCfg), _vp,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.moe_dispatch.argtypes = [_vp, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp]
+        L.moe_update_bias.argtypes = [_vp, _i, ctypes.c_float, _vp, _vp]
         L.moe_ffn_workspace_size.restype = _sz
         L.moe_ffn_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i]
         L.moe_expert_ffn.argtypes = [_i, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
@@ -133,6 +134,11 @@ def moe_route(logits, T, E, k, *, x=None, w_router=None, H=0, score=SCORE_SOFTMA
                          _p(pos), _p(src), _p(ws), ws.numel() * ws.element_size() if ws is not None else 0,
                          _stream(stream))
     _check("moe_route", rc)
+
+
+def moe_update_bias(counts, E, gamma, bias, stream=None):
+    rc = lib().moe_update_bias(_p(counts), E, float(gamma), _p(bias), _stream(stream))
+    _check("moe_update_bias", rc)
 
 
 def moe_dispatch(x, T, H, k, src, R, xp=None, xp_codes=None, xp_scales=None, stream=None,

@@ -329,9 +329,45 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
     }
 }
 
+// ------------------------------------------------------------------ load balancing
+// One block: total = sum of counts (integer, so any order gives the same value), then each
+// expert's bias moves by gamma against its load (counts[e] * E against total, exact).
+__global__ __launch_bounds__(1024) void bias_update_kernel(const int32_t* __restrict__ counts,
+                                                           int E, float gamma,
+                                                           float* __restrict__ bias) {
+    __shared__ long long part[16];
+    const int e = threadIdx.x;
+    const long long c = e < E ? (long long)counts[e] : 0;
+    long long v = c;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+    __syncthreads();
+    long long total = 0;
+    for (int w = 0; w < 16; ++w) total += part[w];
+    if (e < E) {
+        const long long scaled = c * E;
+        float b = bias[e];
+        if (scaled > total) b = __fsub_rn(b, gamma);
+        else if (scaled < total) b = __fadd_rn(b, gamma);
+        bias[e] = b;
+    }
+}
+
 }  // namespace moe
 
 using namespace moe;
+
+extern "C" int moe_update_bias(const int32_t* counts, int E, float gamma, float* bias,
+                               void* stream) {
+    MOE_REQUIRE(E >= 1 && E <= 1024 && counts && bias);
+    int rc = moe_check_device();
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    MOE_TRACED("bias_update", st, bias_update_kernel<<<1, 1024, 0, st>>>(counts, E, gamma, bias));
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
 
 extern "C" size_t moe_route_workspace_size(int T, int k, int E) {
     if (T < 0 || k < 1 || E < 1) return 0;

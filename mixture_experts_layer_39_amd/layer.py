@@ -22,7 +22,7 @@ import torch
 
 from . import (BF16, MXFP8, F32, SCORE_SIGMOID, backward_workspace_size, bwd_args,
                ffn_workspace_size, moe_backward, moe_combine, moe_dispatch, moe_expert_ffn,
-               moe_route, mx_quantize, route_workspace_size)
+               moe_route, moe_update_bias, mx_quantize, route_workspace_size)
 
 
 @dataclasses.dataclass
@@ -43,6 +43,7 @@ class LayerCfg:
     local_share: bool = False  # expert of each routed pair comes from idx_local
     router_proj: bool = False
     mx: bool = False
+    bias_gamma: float = 0.0    # > 0: sigmoid selection bias, updated from the loads each step
 
     @property
     def ER(self):
@@ -73,6 +74,11 @@ class MoELayer:
             raise ValueError("local share must have k routed rows per token")
         self.k_router = c.k
         self.kr = kr
+        if c.bias_gamma > 0 and (c.score != SCORE_SIGMOID or minibatch):
+            raise ValueError("the load-balancing bias applies to the sigmoid router of the "
+                             "unstreamed layer")
+        self.sel_bias = (torch.zeros(c.ER, dtype=torch.float32, device=d)
+                         if c.bias_gamma > 0 else None)
         # macrobatch ring: minibatches of `minibatch` tokens, D of them per pass
         self.ring = minibatch > 0 and ring_depth > 0
         if self.ring:
@@ -188,14 +194,19 @@ class MoELayer:
         if c.local_share:
             moe_route(self.logits, c.T, c.ER, self.k_router, idx=self.idx, w=self.w,
                       s_sel=self.s_sel, counts=self.g_counts, offsets=self.g_offsets,
-                      pos=self.g_pos, src=self.g_src, **common)
+                      pos=self.g_pos, src=self.g_src, sel_bias=self.sel_bias, **common)
             moe_route(None, c.T, c.E, self.kr, idx_in=inp["idx_local"], counts=self.counts,
                       offsets=self.offsets, pos=self.pos, src=self.src, **common)
+            loads = self.g_counts
         else:
             moe_route(self.logits, c.T, c.E, c.k, x=inp["x"] if c.router_proj else None,
                       w_router=inp.get("w_router"), H=c.H, idx=self.idx, w=self.w,
                       s_sel=self.s_sel, counts=self.counts, offsets=self.offsets, pos=self.pos,
-                      src=self.src, **common)
+                      src=self.src, sel_bias=self.sel_bias, **common)
+            loads = self.counts
+        if c.bias_gamma > 0:
+            # the loads of this step move the bias the next step selects with
+            moe_update_bias(loads, c.ER, c.bias_gamma, self.sel_bias)
 
     def dispatch(self):
         c = self.cfg

@@ -75,6 +75,10 @@ def test_route_validation():
 
 def test_dispatch_combine_mx_validation():
     L_ = lib()
+    assert L_.moe_update_bias(FAKE, 0, 0.1, FAKE, None) == moe.MOE_EINVAL
+    assert L_.moe_update_bias(FAKE, 1025, 0.1, FAKE, None) == moe.MOE_EINVAL
+    assert L_.moe_update_bias(None, 8, 0.1, FAKE, None) == moe.MOE_EINVAL
+    assert L_.moe_update_bias(FAKE, 8, 0.1, None, None) == moe.MOE_EINVAL
     assert L_.moe_dispatch(FAKE, 16, 60, 2, FAKE, None, 32, FAKE, None, None, None) == moe.MOE_EINVAL
     assert L_.moe_dispatch(FAKE, 16, 64, 2, FAKE, None, 32, None, None, None, None) == moe.MOE_EINVAL
     assert L_.moe_dispatch(FAKE, 16, 64, 2, FAKE, None, 32, None, FAKE, None, None) == moe.MOE_EINVAL
