@@ -17,7 +17,9 @@ int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int
                      hipStream_t st);
 int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int E, int R, int H,
                int I, const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q,
-               const uint8_t* w2s, float* hf, uint8_t* hq, uint8_t* hs, bf16_t* y, hipStream_t st);
+               const uint8_t* w2s, float* hf, uint8_t* hq, uint8_t* hs, uint8_t* panels,
+               bf16_t* y, hipStream_t st);
+size_t moe_mx_panel_bytes(int E, int R, int H, int I, bool shared);
 int moe_launch_combine_bwd(const bf16_t* dout, const bf16_t* y, const int32_t* pos, const float* w,
                            int T, int k, int H, int R, bf16_t* dy, float* dw, hipStream_t st);
 int moe_launch_unpermute(const bf16_t* dxp, const int32_t* pos, int T, int k, int H, int R,
@@ -122,7 +124,8 @@ extern "C" size_t moe_ffn_workspace_size(int dtype, int E, int R, int H, int I, 
     if (E < 1 || R < 0 || H < 1 || I < 1) return 0;
     size_t rows = shared ? (size_t)E * R : (size_t)R;
     if (dtype == MOE_MXFP8)
-        return moe_align256(rows * I * 4) + moe_align256(rows * I) + moe_align256(rows * (I / 32)) + 256;
+        return moe_align256(rows * I * 4) + moe_align256(rows * I) +
+               moe_align256(rows * (I / 32)) + moe_mx_panel_bytes(E, R, H, I, shared != 0) + 256;
     return moe_align256(rows * I * 2) + 256;
 }
 
@@ -160,8 +163,11 @@ extern "C" int moe_expert_ffn(int dtype, const void* xp, const uint8_t* xp_scale
     uint8_t* hq = (uint8_t*)p;
     p += moe_align256(rows * I);
     uint8_t* hs = (uint8_t*)p;
+    p += moe_align256(rows * (I / 32));
+    uint8_t* panels = (uint8_t*)p;
     return moe_ffn_mx((const uint8_t*)xp, xp_scales, offsets, E, R, H, I, (const uint8_t*)w1,
-                      w1_scales, (const uint8_t*)w2, w2_scales, hf, hq, hs, (bf16_t*)y, st);
+                      w1_scales, (const uint8_t*)w2, w2_scales, hf, hq, hs, panels, (bf16_t*)y,
+                      st);
 }
 
 // ---------------------------------------------------------------------- backward

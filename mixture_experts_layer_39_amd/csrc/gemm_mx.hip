@@ -5,97 +5,255 @@
 //   GEMM1: [g|u] = Xq_e W1q_e^T, epilogue h = silu(g)*u in fp32.
 //   GEMM2: y = hq_e W2q_e^T, bf16 output (h MX-quantised along I in between).
 //
-// The pipeline of the BF16 kernels, for byte codes: 256x256 tiles, 4 waves of 128x128, K steps
-// of 64 codes (one 64-byte swizzled LDS row per operand row) through a ring of 4 LDS stages
-// filled by direct global-to-LDS loads three steps ahead, loads and LDS reads interleaved one
-// per MFMA, buffer loads that zero-fill past an expert's rows, device-side expert tile lists,
-// tiles in launch order.  The E8M0 scales travel through LDS in groups of 8 K steps (16 bytes
-// per row), double-buffered; each lane hands the MFMA the scale of its row in the 32-code
-// block its lane group stands for.
+// The pipeline of the BF16 kernels for byte codes: 256x256 tiles, 4 waves of 128x128, K steps
+// of 128 codes (a 128-byte LDS row per operand row: the bytes, swizzle and load map of a
+// 64-wide BF16 step) in the ring of five 32 KB operand slots, filled by direct global-to-LDS
+// loads spread over the step; buffer loads that zero-fill past an expert's rows;
+// device-side expert tile lists; tiles in launch order.
+//
+// Scales.  The five slots take all 160 KB of LDS, so the E8M0 scales go straight to
+// registers.  Per K step and sub-tile a lane needs the scales of one row in two of the step's
+// four 32-code blocks; read from the [rows, K/32] layout those bytes are scattered over 32
+// rows per instruction.  A pre-pass therefore lays the scales of every 128-row operand panel
+// out per K step in the order the 64 lanes consume them (8 bytes per lane, one 512-byte run
+// per panel and step), and the K loop fetches them with one 8-byte load per lane and operand
+// per step, two steps ahead.
 #include "pipe.h"
 
 namespace moe {
 
-constexpr int XBM = 256, XBN = 256, XBK = 64, XNTH = 256;  // XBK: codes (bytes) per K step
-constexpr int XNST = 4;                  // pipeline stages
+constexpr int XBM = 256, XBN = 256, XNTH = 256;
+constexpr int XBK = 128;                 // codes (bytes) per K step
 constexpr int XGM = 4;                   // M tiles per L2 group
-constexpr int XOPB = 256 * XBK;          // bytes of one operand in one stage
-constexpr int XLPW = XOPB / 1024 / 4;    // direct loads per operand per wave per step
-constexpr int XLPS = 2 * XLPW;           // ... for both operands
-constexpr int SGRP = 8;                  // K steps per scale group (16 E8M0 bytes per row)
-constexpr int SOPB = 256 * 16;           // bytes of one operand's scale group
+typedef Pipe<64> XP;                     // 128-byte rows: the LDS layout of a 64-wide BF16 step
+constexpr int XOPB = XP::OPB;            // bytes of one operand step (one slot)
+constexpr int XLPW = XP::LPW;            // direct loads per operand per wave per step
+constexpr int SPAN = 512;                // bytes of one panel's scales for one K step
 
 enum { XEPI_SWIGLU_F32 = 0, XEPI_STORE_BF16 = 1 };
 
 struct MxArgs {
-    const uint8_t* A;   // codes [rows, K]
-    const uint8_t* As;  // scales [rows, K/32]
-    int64_t a_es;       // per-expert row stride (shared mode), in rows
-    const uint8_t* B;   // codes [E, b_rows, K]
-    const uint8_t* Bs;  // scales [E, b_rows, K/32]
+    const uint8_t* A;    // codes [rows, K]
+    const uint8_t* At;   // panel scales of A: [A panels][K/128][512]
+    int64_t a_es;        // per-expert row stride (shared mode), in rows
+    const uint8_t* B;    // codes [E, b_rows, K]
+    const uint8_t* Bt;   // panel scales of B: [E][NT][2][K/128][512]
     int b_rows;
-    void* C;            // SwiGLU: fp32 h [rows, I];  store: bf16 y [rows, N]
-    int64_t c_es;       // per-expert row stride of C (shared mode), in rows
+    void* C;             // SwiGLU: fp32 h [rows, I];  store: bf16 y [rows, N]
+    int64_t c_es;        // per-expert row stride of C (shared mode), in rows
     int ldc;
     const int32_t* offsets;
     int E, R, N, K, I;
-    int total;
+    int total;           // tile count when static (shared mode)
 };
 
 struct alignas(1024) MxSmem {
-    char st[XNST][2 * XOPB];  // code stages: A then B
-    char sc[2][2 * SOPB];     // scale groups: A then B, 16 bytes per tile row
-    int tp[1024];
-    int total;
+    char st[5 * XOPB];   // the five operand slots
 };
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-
 template <int EPI>
-__device__ __forceinline__ int mx_n_tiles(const MxArgs& g) {
-    return (EPI == XEPI_SWIGLU_F32) ? cdiv(g.I, 128) : cdiv(g.N, XBN);
+__host__ __device__ __forceinline__ int mx_n_tiles(int N, int I) {
+    return (EPI == XEPI_SWIGLU_F32) ? cdiv(I, 128) : cdiv(N, XBN);
 }
 
+// tile row nn -> B row.  SwiGLU: a tile holds gate and up rows of 128 channels; each
+// 32-column MFMA block takes 16 channels, gate in its columns 0-15 and up in 16-31.
 template <int EPI>
-__device__ __forceinline__ int mx_tile_total(const MxArgs& g, MxSmem& sm) {
-    if (g.offsets == nullptr) return g.total;
+__device__ __forceinline__ int mx_brow(int nn, int n0, int ch0, int I) {
+    if (EPI == XEPI_SWIGLU_F32)
+        return ((nn >> 4) & 1) * I + ch0 + (nn >> 7) * 64 + ((nn & 127) >> 5) * 16 + (nn & 15);
+    return n0 + nn;
+}
+
+// Ragged-M products: every wave scans the per-expert tile counts (NT tiles per 256-row M
+// tile) itself, 64 experts at a time.  Returns the tile count; with `logical` >= 0 it finds
+// the expert owning tile `logical` and that expert's first tile instead.
+__device__ __forceinline__ int mx_ragged_scan(const int32_t* offsets, int E, int R, int NT,
+                                              int logical, int* e_out, int* first_out) {
     const int lane = threadIdx.x & 63;
-    const int NT = mx_n_tiles<EPI>(g);
-    if (threadIdx.x < 64) {
-        int run = 0;
-        for (int base = 0; base < g.E; base += 64) {
-            int e = base + lane, tiles = 0;
-            if (e < g.E) {
-                int lo = min(max(g.offsets[e], 0), g.R);
-                int hi = min(max(g.offsets[e + 1], lo), g.R);
-                tiles = cdiv(hi - lo, XBM) * NT;
-            }
-            int inc = wave_incl_scan(tiles) + run;
-            if (e < g.E) sm.tp[e] = inc;
-            run = __shfl(inc, 63, 64);
+    int run = 0;
+    for (int base = 0; base < E; base += 64) {
+        const int e = base + lane;
+        int tiles = 0;
+        if (e < E) {
+            const int lo = min(max(offsets[e], 0), R);
+            const int hi = min(max(offsets[e + 1], lo), R);
+            tiles = cdiv(hi - lo, XBM) * NT;
         }
-        if (lane == 0) sm.total = run;
+        const int inc = wave_incl_scan(tiles) + run;
+        if (logical >= 0) {
+            const uint64_t m = __ballot(e < E && inc > logical);
+            if (m) {
+                const int l = __ffsll((unsigned long long)m) - 1;
+                *e_out = base + l;
+                *first_out = __shfl(inc - tiles, l, 64);
+                return -1;
+            }
+        }
+        run = __shfl(inc, 63, 64);
     }
-    __syncthreads();
-    return uni(sm.total);
+    return run;
 }
 
+// ---------------------------------------------------------------- panel scales
+// For the panel rows prow(32 t + l) (t = 0..3, l = 0..31) and K step s, byte 8 L + 2 t + kk of
+// the step's 512-byte run (lane L = 32 g + l) holds the scale of row prow(32 t + l) in the
+// 32-code block 4 s + 2 kk + g; rows outside the operand give 0.  In the scaled MFMA, lane
+// group g supplies the scale of block g of its 64-code sub-step.
+
+// One block per 256-row tile of an operand (both of its 128-row panels) and 64 scale
+// columns (16 K steps): the tile's scale rows pass through LDS, loaded with dword loads along
+// the rows, so that the gather of single bytes into lane order runs on LDS.
+constexpr int PS_COLS = 64;  // scale columns (bytes) staged per pass
+
+__device__ __forceinline__ void panel_tile(const uint8_t* __restrict__ sc, int KB, int nsteps,
+                                           const int* srow, uint8_t* __restrict__ out,
+                                           uint8_t (*stg)[PS_COLS + 4]) {
+    const int tid = threadIdx.x;
+    {
+        const int c0 = (int)blockIdx.y * PS_COLS;
+        __syncthreads();  // srow written
+        // 256 rows x 16 dwords: thread i loads dword i % 16 of row i / 16 (+16 rows per pass)
+        for (int i = tid; i < 256 * (PS_COLS / 4); i += 256) {
+            const int row = i / (PS_COLS / 4), col = c0 + 4 * (i % (PS_COLS / 4));
+            const int rr = srow[row];
+            uint32_t v = 0;
+            if (rr >= 0 && col < KB) v = *reinterpret_cast<const uint32_t*>(sc + (int64_t)rr * KB + col);
+            *reinterpret_cast<uint32_t*>(&stg[row][col - c0]) = v;
+        }
+        __syncthreads();
+        // entries (half w, step s, lane L): 2 x 16 x 64 per pass, 8 per thread
+        const int s0 = c0 / 4;
+        for (int i = tid; i < 2 * (PS_COLS / 4) * 64; i += 256) {
+            const int L = i & 63, ds = (i >> 6) % (PS_COLS / 4), w = i / (64 * (PS_COLS / 4));
+            const int s = s0 + ds;
+            if (s >= nsteps) continue;
+            const int l = L & 31, g = L >> 5;
+            uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int col = 4 * ds + 2 * kk + g;
+                    const uint32_t v = (c0 + col < KB) ? stg[w * 128 + 32 * t + l][col] : 0u;
+                    wd[t >> 1] |= v << (8 * (2 * (t & 1) + kk));
+                }
+            *reinterpret_cast<uint2*>(out + ((int64_t)w * nsteps + s) * SPAN + 8 * L) =
+                make_uint2(wd[0], wd[1]);
+        }
+    }
+}
+
+// A operand: tile `bx` (a 256-row M tile), panels 2 bx + half.
+__device__ __forceinline__ void panel_a(int bx, const uint8_t* __restrict__ sc,
+                                        const int32_t* __restrict__ offsets, int E, int R,
+                                        int64_t a_es, int KB, int nsteps, int total_static,
+                                        uint8_t* __restrict__ out, uint8_t (*stg)[PS_COLS + 4],
+                                        int* srow) {
+    int e, tm, row0, M;
+    if (offsets) {
+        const int total = uni(mx_ragged_scan(offsets, E, R, 1, -1, nullptr, nullptr));
+        if (bx >= total) return;
+        int ee = 0, first = 0;
+        mx_ragged_scan(offsets, E, R, 1, bx, &ee, &first);
+        e = uni(ee);
+        tm = uni(bx - first);
+        const int a = min(max(offsets[e], 0), R);
+        const int b = min(max(offsets[e + 1], a), R);
+        row0 = a;
+        M = b - a;
+    } else {
+        if (bx >= total_static) return;
+        const int MT = cdiv(R, XBM);
+        e = bx / MT;
+        tm = bx % MT;
+        row0 = 0;
+        M = R;
+    }
+    const int rr = tm * XBM + (int)threadIdx.x;
+    srow[threadIdx.x] = rr < M ? (int)((int64_t)e * a_es + row0 + rr) : -1;
+    panel_tile(sc, KB, nsteps, srow, out + (int64_t)(2 * bx) * nsteps * SPAN, stg);
+}
+
+// B operand: tile `bx` = e NT + tn, panels 2 bx + half.
+template <int EPI>
+__device__ __forceinline__ void panel_b(int bx, const uint8_t* __restrict__ sc, int b_rows, int N,
+                                        int I, int KB, int nsteps, uint8_t* __restrict__ out,
+                                        uint8_t (*stg)[PS_COLS + 4], int* srow) {
+    const int NT = mx_n_tiles<EPI>(N, I);
+    const int e = bx / NT, tn = bx % NT;
+    const int rr = mx_brow<EPI>((int)threadIdx.x, tn * XBN, tn * 128, I);
+    srow[threadIdx.x] = rr < b_rows ? (int)((int64_t)e * b_rows + rr) : -1;
+    panel_tile(sc, KB, nsteps, srow, out + (int64_t)(2 * bx) * nsteps * SPAN, stg);
+}
+
+struct PanelJobs {
+    // A panels of GEMM1 (xp scales), B panels of both GEMMs (weight scales)
+    const uint8_t* xs; const int32_t* offsets; int E, R, H, I, na, total_static;
+    const uint8_t* w1s; const uint8_t* w2s;
+    uint8_t* pa1; uint8_t* pb1; uint8_t* pb2;
+};
+
+// One launch for the panels known before GEMM1: x blocks [0, na) A panels of xp, then E NT1
+// B panels of W1, then E NT2 B panels of W2; y blocks: 64-column chunks of each operand's
+// scales (blocks past an operand's chunks exit).
+__global__ __launch_bounds__(256) void mx_panel_scales_pre(PanelJobs j) {
+    __shared__ uint8_t stg[256][PS_COLS + 4];
+    __shared__ int srow[256];
+    const int nb1 = j.E * mx_n_tiles<XEPI_SWIGLU_F32>(2 * j.I, j.I);
+    const int bx = blockIdx.x;
+    const int KBh = j.H / 32, KBi = j.I / 32;
+    if (bx < j.na) {
+        if ((int)blockIdx.y * PS_COLS >= KBh) return;
+        panel_a(bx, j.xs, j.offsets, j.E, j.R, 0, KBh, j.H / XBK, j.total_static, j.pa1, stg, srow);
+    } else if (bx < j.na + nb1) {
+        if ((int)blockIdx.y * PS_COLS >= KBh) return;
+        panel_b<XEPI_SWIGLU_F32>(bx - j.na, j.w1s, 2 * j.I, 2 * j.I, j.I, KBh, j.H / XBK, j.pb1,
+                                 stg, srow);
+    } else {
+        if ((int)blockIdx.y * PS_COLS >= KBi) return;
+        panel_b<XEPI_STORE_BF16>(bx - j.na - nb1, j.w2s, j.H, j.H, j.I, KBi, j.I / XBK, j.pb2,
+                                 stg, srow);
+    }
+}
+
+// The A panels of GEMM2 (h scales, known after the MX quantisation of h).
+__global__ __launch_bounds__(256) void mx_panel_scales_h(const uint8_t* __restrict__ sc,
+                                                         const int32_t* __restrict__ offsets,
+                                                         int E, int R, int64_t a_es, int KB,
+                                                         int nsteps, int total_static,
+                                                         uint8_t* __restrict__ out) {
+    __shared__ uint8_t stg[256][PS_COLS + 4];
+    __shared__ int srow[256];
+    panel_a(blockIdx.x, sc, offsets, E, R, a_es, KB, nsteps, total_static, out, stg, srow);
+}
+
+// 8 bytes per lane straight to registers, issued through inline asm like the LDS loads so that
+// the pipeline's explicit wait counts cover both.  The registers are read only after a wait
+// that covers the load, followed by `settle`, which redefines the value for the compiler.
+__device__ __forceinline__ void vgpr_load8(uint2& dst, rsrc_t r, uint32_t voff, uint32_t soff) {
+    asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen"
+                 : "=v"(dst)
+                 : "v"(voff), "s"(r), "s"(soff)
+                 : "memory");
+}
+__device__ __forceinline__ void settle(uint2& v) { asm volatile("" : "+v"(v)); }
+
+// ---------------------------------------------------------------- one output tile
 template <int EPI>
 __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int logical) {
     const int tid = threadIdx.x, lane = tid & 63, wid = uni(tid >> 6);
     const int wm = wid >> 1, wn = wid & 1;
-    const int NT = mx_n_tiles<EPI>(g);
-    const int K = g.K, KB = g.K / 32;
+    const int NT = mx_n_tiles<EPI>(g.N, g.I);
+    const int K = g.K, nk = K / XBK;
 
-    int e, t_local, Mrows, row0;
+    int e, t_local, Mrows, row0, mt_first;
     if (g.offsets) {
-        int lo = 0, hi = g.E - 1;
-        while (lo < hi) {
-            int mid = (lo + hi) >> 1;
-            if (sm.tp[mid] > logical) hi = mid; else lo = mid + 1;
-        }
-        e = uni(lo);
-        t_local = uni(logical - (e ? sm.tp[e - 1] : 0));
+        int ee = 0, first = 0;
+        mx_ragged_scan(g.offsets, g.E, g.R, NT, logical, &ee, &first);
+        e = uni(ee);
+        t_local = uni(logical - first);
+        mt_first = uni(first / NT);  // M tiles of the experts before e
         int a = min(max(g.offsets[e], 0), g.R);
         int b = min(max(g.offsets[e + 1], a), g.R);
         row0 = uni(a);
@@ -104,6 +262,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
         int per = cdiv(g.R, XBM) * NT;
         e = logical / per;
         t_local = logical - e * per;
+        mt_first = e * cdiv(g.R, XBM);
         row0 = 0;
         Mrows = g.R;
     }
@@ -119,43 +278,24 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
     }
     const int m0 = tm * XBM, n0 = tn * XBN, ch0 = tn * 128;
 
-    // tile row -> B row (SwiGLU: 128 gate rows and the matching 128 up rows per tile)
-    auto brow = [&](int nn) __attribute__((always_inline)) {
-        if (EPI == XEPI_SWIGLU_F32) {
-            int q = nn & 127;
-            return (q >> 6) * g.I + ch0 + (nn >> 7) * 64 + (q & 63);
-        }
-        return n0 + nn;
-    };
     // ---------------------------------------------------------------- operands
+    // codes: the K-major load map of a 64-wide BF16 step (128-byte rows; ld in 2-byte units)
     const int64_t arow = (int64_t)e * g.a_es + row0 + m0;
     const uint32_t arows = (uint32_t)max(Mrows - m0, 0);
-    const rsrc_t ra = make_rsrc(g.A + arow * K, arows * (uint32_t)K);
-    const rsrc_t ras = make_rsrc(g.As + arow * KB, arows * (uint32_t)KB);
-    const rsrc_t rb = make_rsrc(g.B + (int64_t)e * g.b_rows * K, (uint32_t)g.b_rows * (uint32_t)K);
-    const rsrc_t rbs = make_rsrc(g.Bs + (int64_t)e * g.b_rows * KB, (uint32_t)g.b_rows * (uint32_t)KB);
-    // code loads: wave w loads tile rows 64w .. 64w+63, 16 rows per instruction; lane L of an
-    // instruction writes LDS row base + L/4, chunk L%4, which holds logical chunk
-    // (L%4) ^ kswz(row)
-    uint32_t va[XLPW], vb[XLPW];
-    int ldsrow[XLPW];
-#pragma unroll
-    for (int i = 0; i < XLPW; ++i) {
-        const int r = 64 * wid + 16 * i + (lane >> 2);
-        const int c = (lane & 3) ^ kswz(r);
-        va[i] = (uint32_t)r * (uint32_t)K + (uint32_t)c * 16u;
-        vb[i] = (uint32_t)brow(r) * (uint32_t)K + (uint32_t)c * 16u;
-        ldsrow[i] = (64 * wid + 16 * i) * XBK;
-    }
-    // scale loads: wave w loads the 16-byte group entries of tile rows 64w .. 64w+63
-    const uint32_t vas = (uint32_t)(64 * wid + lane) * (uint32_t)KB;
-    const uint32_t vbs = (uint32_t)brow(64 * wid + lane) * (uint32_t)KB;
-    // fragment reads: lane reads row (sub-tile base) + lane%32, logical chunks g and g+2
-    // (g = lane/32).  Sub-tile bases are multiples of 32, so the row swizzle is the lane's.
-    const int gsel = lane >> 5;
-    const uint32_t rowa = (uint32_t)(wm * 128 + (lane & 31)), rowb = (uint32_t)(wn * 128 + (lane & 31));
-    const uint32_t clo = (uint32_t)((gsel ^ kswz(lane & 31)) << 4);
-    const uint32_t chi = (uint32_t)(((gsel + 2) ^ kswz(lane & 31)) << 4);
+    Operand oa, ob;
+    setup_kmajor<64>(oa, g.A + arow * K, arows * (uint32_t)K, K / 2, wid, lane, wm * 128,
+                     [](int r) { return r; }, 2 * XP::RPI, 4 * XP::RPI);
+    const int I = g.I;
+    setup_kmajor<64>(ob, g.B + (int64_t)e * g.b_rows * K, (uint32_t)g.b_rows * (uint32_t)K, K / 2,
+                     wid, lane, wn * 128, [=](int nn) { return mx_brow<EPI>(nn, n0, ch0, I); },
+                     EPI == XEPI_SWIGLU_F32 ? I : 2 * XP::RPI,
+                     EPI == XEPI_SWIGLU_F32 ? 16 : 4 * XP::RPI);
+    // panel scales of this wave's A rows and B rows
+    const uint32_t pbytes = (uint32_t)nk * SPAN;
+    const rsrc_t rsa = make_rsrc(g.At + (int64_t)(2 * (mt_first + tm) + wm) * pbytes, pbytes);
+    const rsrc_t rsb = make_rsrc(g.Bt + (int64_t)(2 * (e * NT + tn) + wn) * pbytes, pbytes);
+    const uint32_t lso = (uint32_t)lane * 8u;
+    const rsrc_t rnull = make_rsrc(nullptr, 0);
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -166,97 +306,153 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     // ---------------------------------------------------------------- main loop
-    // One K step = 64 codes = one scaled MFMA per sub-tile pair (16 per wave).  At the top of
-    // each step one barrier certifies that step ks+1 has landed and that every wave has read
-    // step ks; the step's MFMAs then interleave the loads of step ks+4 into the stage just
-    // freed and the reads of step ks+1's fragments and scales.
-    //
-    // Operand layout of the 32x32x64 scaled MFMA: lane group g = lane/32 holds codes
-    // [16g, 16g+16) of each of the instruction's two 32-code blocks (first block in bytes
-    // 0-15, second in 16-31), and the scale of lane l is that of row l%32 in block g.
-    const int nk = cdiv(K, XBK);
-    const int ngrp = cdiv(nk, SGRP);
-    const rsrc_t rnull = make_rsrc(nullptr, 0);
-    const uint32_t sa0 = lds_addr(sm.st[0]), sa1 = lds_addr(sm.st[1]), sa2 = lds_addr(sm.st[2]),
-                   sa3 = lds_addr(sm.st[3]);
-    const uint32_t stg[XNST] = {sa0, sa1, sa2, sa3};
-    const uint32_t sc0 = lds_addr(sm.sc[0]);
+    // Slots as in the BF16 kernel: A of step s in slot 2s mod 5, B in slot 2s+1 mod 5; A(s+2)
+    // goes into the slot B(s-1) left, B(s+2) into the slot A(s) leaves at this step's
+    // barrier.  A step is two sub-steps of 16 scaled MFMAs (64 codes each).  Loads of step s:
+    //   sub-step 0: second half of B(s+1), first half of A(s+2), then the scales of step s+2
+    //   barrier (A(s+1), B(s+1) and the scales of s+1 landed; every read of step s done)
+    //   sub-step 1: second half of A(s+2), first half of B(s+2)
+    // The scales of steps s, s+1, s+2 live in three register sets, so the loop is unrolled
+    // over lcm(5, 3) = 15 steps; at its back edge the set in flight is waited for, so that no
+    // register still being written crosses it.
     i32x8 fa[2][4], fb[2][4];
-    int xa[2][4], xb[2][4];
-
-    auto load_step = [&](uint32_t st, int ks, int i) __attribute__((always_inline)) {  // instruction i of step ks (0..7)
-        const bool live = ks < nk;
-        const uint32_t so = live ? (uint32_t)ks * XBK : 0u;
-        if (i < XLPW) lds_load16(live ? ra : rnull, st + ldsrow[i], va[i], so);
-        else lds_load16(live ? rb : rnull, st + XOPB + ldsrow[i - XLPW], vb[i - XLPW], so);
+    uint2 sca[3], scb[3];
+    // fragment r (0..7) of sub-step kk, in MFMA consumption order a0 b0 b1 b2 b3 a1 a2 a3:
+    // 32 codes per lane, chunks 4 kk + g and 4 kk + 2 + g of the row (g = lane / 32)
+    auto read_ab = [&](const char* sa_, const char* sb_, int kk, int f, int r) __attribute__((always_inline)) {
+        const bool isa = (r == 0 || r >= 5);
+        const int t = r == 0 ? 0 : (r <= 4 ? r - 1 : r - 4);
+        const Operand& o = isa ? oa : ob;
+        const char* base = (isa ? sa_ : sb_) + t * 32 * XP::KROW;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(base + o.rd[2 * kk]);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(base + o.rd[2 * kk + 1]);
+        const i32x8 v = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        if (isa) fa[f][t] = v;
+        else fb[f][t] = v;
     };
-    auto load_scales = [&](int grp) __attribute__((always_inline)) {
-        const uint32_t dst = sc0 + (uint32_t)(grp & 1) * (2u * SOPB);  // sm.sc[grp & 1]
-        lds_load16(ras, dst + 64 * 16 * wid, vas, (uint32_t)grp * 16u);
-        lds_load16(rbs, dst + SOPB + 64 * 16 * wid, vbs, (uint32_t)grp * 16u);
-    };
-    // read number r (0..11) of step ks into set f: fragments a0 b0 b1 b2 b3 a1 a2 a3 (the
-    // order the MFMAs consume them), then the scale bytes of sub-tile r-8 of A and of B
-    auto read_one = [&](const char* st, int ks, int f, int r) __attribute__((always_inline)) {
-        if (r < 8) {
-            const bool isa = (r == 0 || r >= 5);
-            const int t = r == 0 ? 0 : (r <= 4 ? r - 1 : r - 4);
-            const char* base = st + (isa ? 0 : XOPB) + ((isa ? rowa : rowb) + 32 * t) * XBK;
-            const u32x4 lo = *reinterpret_cast<const u32x4*>(base + clo);
-            const u32x4 hi = *reinterpret_cast<const u32x4*>(base + chi);
-            const i32x8 v = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            if (isa) fa[f][t] = v;
-            else fb[f][t] = v;
-        } else {
-            const char* sc = sm.sc[(ks / SGRP) & 1];
-            const int byte = 2 * (ks % SGRP) + gsel;
-            const int t = r - 8;
-            xa[f][t] = (int)(uint8_t)sc[(rowa + 32 * t) * 16 + byte];
-            xb[f][t] = (int)(uint8_t)sc[SOPB + (rowb + 32 * t) * 16 + byte];
-        }
-    };
-    auto mfma_one = [&](int f, int n) __attribute__((always_inline)) {
+    // MFMA n of sub-step kk with fragment set f and scale set c: the scale of sub-tile t is
+    // byte 2 (t % 2) + kk of dword t / 2 (the MFMA's opsel operand picks the byte)
+    auto mfma_one = [&](int f, int kk, int c, int n) __attribute__((always_inline)) {
         const int i = n >> 2, j = n & 3;
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            fb[f][j], fa[f][i], acc[i][j], 0, 0, 0, xb[f][j], 0, xa[f][i]);
+        const int sa_w = (i >> 1) ? (int)sca[c].y : (int)sca[c].x;
+        const int sb_w = (j >> 1) ? (int)scb[c].y : (int)scb[c].x;
+        const int pa = 2 * (i & 1) + kk, pb = 2 * (j & 1) + kk;
+#define MX_MFMA(PA, PB)                                                                       \
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[f][j], fa[f][i], acc[i][j], \
+                                                               0, 0, PB, sb_w, PA, sa_w)
+#define MX_ROW(PA)                         \
+    if (pb == 0) MX_MFMA(PA, 0);           \
+    else if (pb == 1) MX_MFMA(PA, 1);      \
+    else if (pb == 2) MX_MFMA(PA, 2);      \
+    else MX_MFMA(PA, 3);
+        if (pa == 0) { MX_ROW(0) }
+        else if (pa == 1) { MX_ROW(1) }
+        else if (pa == 2) { MX_ROW(2) }
+        else { MX_ROW(3) }
+#undef MX_ROW
+#undef MX_MFMA
     };
-    // f: the fragment set step ks reads from (ks & 1, passed as a literal)
-    auto kstep = [&](int ks, int f, uint32_t cur32, const char* nxt) __attribute__((always_inline)) {
-        wait_vm_lgkm0<2 * XLPS>();  // step ks+1 (and the scale group it needs) landed
-        __builtin_amdgcn_s_barrier();
+    auto codes_src = [&](int ks, rsrc_t& ra_, rsrc_t& rb_, uint32_t& so) __attribute__((always_inline)) {
+        const bool live = ks < nk;
+        ra_ = live ? oa.r : rnull;
+        rb_ = live ? ob.r : rnull;
+        so = live ? (uint32_t)ks * XBK : 0u;
+    };
+    auto load_scales = [&](int ks, int c) __attribute__((always_inline)) {
+        const bool live = ks < nk;
+        const uint32_t so = live ? (uint32_t)ks * SPAN : 0u;
+        vgpr_load8(sca[c], live ? rsa : rnull, lso, so);
+        vgpr_load8(scb[c], live ? rsb : rnull, lso, so);
+    };
+    rsrc_t pend_rb = rnull;  // B(s+1)'s second half is issued in step s
+    uint32_t pend_so = 0;
+    auto kstep = [&](int u, int ks) __attribute__((always_inline)) {
+        const int su = u % 5, c = u % 3;
+        char* const cA = sm.st + ((2 * su) % 5) * XOPB;
+        char* const cB = sm.st + ((2 * su + 1) % 5) * XOPB;
+        char* const nA = sm.st + ((2 * su + 2) % 5) * XOPB;
+        char* const nB = sm.st + ((2 * su + 3) % 5) * XOPB;
+        const uint32_t base32 = lds_addr(sm.st);
+        const uint32_t lB1 = base32 + ((2 * su + 3) % 5) * XOPB;  // B(ks+1)
+        const uint32_t lA = base32 + ((2 * su + 4) % 5) * XOPB;   // A(ks+2): slot of B(ks-1)
+        const uint32_t lB = base32 + ((2 * su) % 5) * XOPB;       // B(ks+2): slot of A(ks)
+        const rsrc_t rb1 = pend_rb;
+        const uint32_t so1 = pend_so;
+        rsrc_t ra_, rb_;
+        uint32_t so;
+        codes_src(ks + 2, ra_, rb_, so);
         __builtin_amdgcn_sched_barrier(0);
-        if (ks % SGRP == 0 && ks / SGRP + 1 < ngrp) load_scales(ks / SGRP + 1);
-        const bool more = ks + 1 < nk;
+        // sub-step 0: fragment reads of sub-step 1; 4 + 4 code loads, then the scales of ks+2
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
-            mfma_one(f, n);
-            if (n < 8) {
-                load_step(cur32, ks + XNST, n);
-            } else if (more) {
-                read_one(nxt, ks + 1, f ^ 1, n - 8);
-                if (n >= 12) read_one(nxt, ks + 1, f ^ 1, n - 4);
+            mfma_one(0, 0, c, n);
+            if ((n & 1) == 0) read_ab(cA, cB, 1, 1, n / 2);
+            else if (n < 8) issue_load<64>(ob, lB1, wid, 4 + n / 2, rb1, so1);
+            else issue_load<64>(oa, lA, wid, (n - 8) / 2, ra_, so);
+            if (n == 15) load_scales(ks + 2, (u + 2) % 3);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_vm_lgkm0<XLPW / 2 + 2>();  // all but A(ks+2)'s first half and its scales
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        settle(sca[(u + 1) % 3]);
+        settle(scb[(u + 1) % 3]);
+        const bool more = ks + 1 < nk;
+        // sub-step 1: fragment reads of the next step's sub-step 0; 4 + 4 code loads
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+            mfma_one(1, 1, c, n);
+            if ((n & 1) == 0) {
+                if (more) read_ab(nA, nB, 0, 0, n / 2);
+            } else if (n < 8) {
+                issue_load<64>(oa, lA, wid, 4 + n / 2, ra_, so);
+            } else {
+                issue_load<64>(ob, lB, wid, (n - 8) / 2, rb_, so);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        pend_rb = rb_;
+        pend_so = so;
     };
     if (nk > 0) {
-        load_scales(0);
-        if (ngrp > 1) load_scales(1);
+        const uint32_t base32 = lds_addr(sm.st);
+        // scales of steps 0 and 1; A(0), B(0), A(1) and the first half of B(1)
+        load_scales(0, 0);
+        load_scales(1, 1);
 #pragma unroll
-        for (int p = 0; p < XNST; ++p)
+        for (int p = 0; p < 2; ++p) {
+            rsrc_t ra_, rb_;
+            uint32_t so;
+            codes_src(p, ra_, rb_, so);
 #pragma unroll
-            for (int i = 0; i < XLPS; ++i) load_step(stg[p], p, i);
-        wait_vm_lgkm0<3 * XLPS>();  // scales and step 0 landed
+            for (int i = 0; i < XLPW; ++i) {
+                issue_load<64>(oa, base32 + (2 * p) * XOPB, wid, i, ra_, so);
+                if (p == 0 || i < XLPW / 2)
+                    issue_load<64>(ob, base32 + (2 * p + 1) * XOPB, wid, i, rb_, so);
+            }
+            pend_rb = rb_;
+            pend_so = so;
+        }
+        wait_vm_lgkm0<XLPW + XLPW / 2>();  // the scales of steps 0, 1 and step 0 landed
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
+        settle(sca[0]);
+        settle(scb[0]);
+        settle(sca[1]);
+        settle(scb[1]);
 #pragma unroll
-        for (int r = 0; r < 12; ++r) read_one(sm.st[0], 0, 0, r);
-        for (int ks = 0; ks < nk; ks += XNST) {
-            kstep(ks, 0, sa0, sm.st[1]);
-            if (ks + 1 < nk) kstep(ks + 1, 1, sa1, sm.st[2]);
-            if (ks + 2 < nk) kstep(ks + 2, 0, sa2, sm.st[3]);
-            if (ks + 3 < nk) kstep(ks + 3, 1, sa3, sm.st[0]);
+        for (int r = 0; r < 8; ++r) read_ab(sm.st, sm.st + XOPB, 0, 0, r);
+        for (int ks = 0; ks < nk; ks += 15) {
+#pragma unroll
+            for (int u = 0; u < 15; ++u)
+                if (ks + u < nk) kstep(u, ks + u);
+            if (ks + 15 < nk) {
+                // back edge: the scales of ks+16 (set 1) were issued before the last 8 loads
+                wait_vm_lgkm0<XLPW>();
+                settle(sca[1]);
+                settle(scb[1]);
+            }
         }
         wait_vm_lgkm0<0>();  // no load may still be writing LDS when the block ends
     }
@@ -266,21 +462,24 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
     // 8 (v/4) + 4 (l/32) + v%4, v = 0..15: four runs of 4 consecutive columns.
     const int lrow = lane & 31, lcol = (lane >> 5) * 4;
     if (EPI == XEPI_SWIGLU_F32) {
+        // block (i, j): channels ch0 + 64 wn + 16 j + 8 hf + lcol .. +3; gate at accumulators
+        // 4 hf .. +3, up at 8 + 4 hf .. +3
         float* C = (float*)g.C + ((int64_t)e * g.c_es + row0) * g.ldc;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = m0 + wm * 128 + i * 32 + lrow;
             if (row >= Mrows) continue;
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int ch = ch0 + wn * 64 + j * 32 + 8 * q + lcol;
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int ch = ch0 + wn * 64 + j * 16 + 8 * hf + lcol;
                     if (ch >= g.I) continue;
+                    const f32x16& a = acc[i][j];
                     f32x4 hv;
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
-                        const float gv = acc[i][j][4 * q + c], uv = acc[i][j + 2][4 * q + c];
+                        const float gv = a[4 * hf + c], uv = a[8 + 4 * hf + c];
                         hv[c] = gv / (1.0f + __expf(-gv)) * uv;
                     }
                     *reinterpret_cast<f32x4*>(C + (int64_t)row * g.ldc + ch) = hv;
@@ -306,27 +505,30 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
     }
 }
 
-#define MOE_MX_KERNEL(NAME, EPI)                                                       \
-    __global__ __launch_bounds__(XNTH) __attribute__((amdgpu_waves_per_eu(1, 1))) void \
-    NAME(MxArgs g) {                                                                   \
-        __shared__ MxSmem sm;                                                          \
-        const int total = mx_tile_total<EPI>(g, sm);                                   \
-        if ((int)blockIdx.x < total) mx_tile<EPI>(g, sm, blockIdx.x);                  \
+#define MOE_MX_KERNEL(NAME, EPI)                                                          \
+    __global__ __launch_bounds__(XNTH) __attribute__((amdgpu_waves_per_eu(1, 1))) void    \
+    NAME(MxArgs g) {                                                                      \
+        __shared__ MxSmem sm;                                                             \
+        const int total = g.offsets ? uni(mx_ragged_scan(g.offsets, g.E, g.R,              \
+                                                         mx_n_tiles<EPI>(g.N, g.I), -1,   \
+                                                         nullptr, nullptr))               \
+                                    : g.total;                                            \
+        if ((int)blockIdx.x < total) mx_tile<EPI>(g, sm, blockIdx.x);                     \
     }
 MOE_MX_KERNEL(mx_gemm1_swiglu, XEPI_SWIGLU_F32)
 MOE_MX_KERNEL(mx_gemm2_down, XEPI_STORE_BF16)
 #undef MOE_MX_KERNEL
 
+// Upper bound on the 256-row M tiles of an operand (host side, no device data).
+static int mx_mtiles_bound(int R, int E, bool shared) {
+    if (shared) return E * cdiv(R, XBM);
+    return (int)(((int64_t)R + (int64_t)E * (XBM - 1)) / XBM);
+}
+
 template <int EPI>
 static int mx_launch(const MxArgs& g, hipStream_t st) {
-    int NT = (EPI == XEPI_SWIGLU_F32) ? cdiv(g.I, 128) : cdiv(g.N, XBN);
-    int grid;
-    if (g.offsets) {
-        int64_t mt = ((int64_t)g.R + (int64_t)g.E * (XBM - 1)) / XBM;
-        grid = (int)(mt * NT);
-    } else {
-        grid = g.total;
-    }
+    const int NT = mx_n_tiles<EPI>(g.N, g.I);
+    const int grid = g.offsets ? mx_mtiles_bound(g.R, g.E, false) * NT : g.total;
     if (grid <= 0) return MOE_OK;
     if (EPI == XEPI_SWIGLU_F32)
         MOE_TRACED("mx_gemm1_swiglu", st, mx_gemm1_swiglu<<<grid, XNTH, 0, st>>>(g));
@@ -336,6 +538,36 @@ static int mx_launch(const MxArgs& g, hipStream_t st) {
     return MOE_OK;
 }
 
+static int mx_panels_pre(const PanelJobs& j, hipStream_t st) {
+    const int nb = j.na + j.E * mx_n_tiles<XEPI_SWIGLU_F32>(2 * j.I, j.I) +
+                   j.E * mx_n_tiles<XEPI_STORE_BF16>(j.H, j.I);
+    const dim3 grid(nb, cdiv(max(j.H, j.I) / 32, PS_COLS));
+    MOE_TRACED("mx_panel_scales", st, mx_panel_scales_pre<<<grid, 256, 0, st>>>(j));
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+static int mx_panels_h(const uint8_t* sc, const int32_t* offsets, int E, int R, int64_t a_es,
+                       int K, uint8_t* out, hipStream_t st) {
+    const bool shared = offsets == nullptr;
+    const int grid = mx_mtiles_bound(R, E, shared);
+    if (grid <= 0) return MOE_OK;
+    const dim3 g2(grid, cdiv(K / 32, PS_COLS));
+    MOE_TRACED("mx_panel_scales", st,
+               mx_panel_scales_h<<<g2, 256, 0, st>>>(sc, offsets, E, R, a_es, K / 32, K / XBK,
+                                                     shared ? grid : 0, out));
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+static size_t mx_panel_a_bytes(int E, int R, int K, bool shared) {
+    return moe_align256(2 * (size_t)mx_mtiles_bound(R, E, shared) * (size_t)(K / XBK) * SPAN);
+}
+template <int EPI>
+static size_t mx_panel_b_bytes(int E, int N, int I, int K) {
+    return moe_align256(2 * (size_t)E * (size_t)mx_n_tiles<EPI>(N, I) * (size_t)(K / XBK) * SPAN);
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -343,27 +575,44 @@ using namespace moe;
 int moe_launch_mx_quantize_f32(const float* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
                                hipStream_t st);
 
+// Workspace bytes of the panel scales of both MXFP8 GEMMs (A and B operands).
+size_t moe_mx_panel_bytes(int E, int R, int H, int I, bool shared) {
+    return mx_panel_a_bytes(E, R, H, shared) + mx_panel_a_bytes(E, R, I, shared) +
+           mx_panel_b_bytes<XEPI_SWIGLU_F32>(E, 2 * I, I, H) +
+           mx_panel_b_bytes<XEPI_STORE_BF16>(E, H, I, I);
+}
+
 int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int E, int R, int H,
                int I, const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q,
-               const uint8_t* w2s, float* hf, uint8_t* hq, uint8_t* hs, bf16_t* y, hipStream_t st) {
-    // scale groups are 16-byte chunks of each row's K/32 scales: K a multiple of 128 keeps
-    // every chunk start 4-byte aligned
-    if (H % 128 || I % 128) return MOE_EINVAL;
+               const uint8_t* w2s, float* hf, uint8_t* hq, uint8_t* hs, uint8_t* panels,
+               bf16_t* y, hipStream_t st) {
+    // K steps of 128 codes: H and I multiples of 128
+    if (H % XBK || I % XBK) return MOE_EINVAL;
     const bool shared = offsets == nullptr;
+    uint8_t* pa1 = panels;
+    uint8_t* pa2 = pa1 + mx_panel_a_bytes(E, R, H, shared);
+    uint8_t* pb1 = pa2 + mx_panel_a_bytes(E, R, I, shared);
+    uint8_t* pb2 = pb1 + mx_panel_b_bytes<XEPI_SWIGLU_F32>(E, 2 * I, I, H);
+    PanelJobs pj{xs, offsets, E, R, H, I, mx_mtiles_bound(R, E, shared),
+                 shared ? mx_mtiles_bound(R, E, true) : 0, w1s, w2s, pa1, pb1, pb2};
+    int rc = mx_panels_pre(pj, st);
+    if (rc) return rc;
     MxArgs g{};
-    g.A = xq; g.As = xs; g.a_es = 0;
-    g.B = w1q; g.Bs = w1s; g.b_rows = 2 * I;
+    g.A = xq; g.At = pa1; g.a_es = 0;
+    g.B = w1q; g.Bt = pb1; g.b_rows = 2 * I;
     g.C = hf; g.c_es = shared ? R : 0; g.ldc = I;
     g.offsets = offsets; g.E = E; g.R = R; g.N = 2 * I; g.K = H; g.I = I;
     g.total = shared ? E * cdiv(R, XBM) * cdiv(I, 128) : 0;
-    int rc = mx_launch<XEPI_SWIGLU_F32>(g, st);
+    rc = mx_launch<XEPI_SWIGLU_F32>(g, st);
     if (rc) return rc;
     int64_t rows = shared ? (int64_t)E * R : R;
     rc = moe_launch_mx_quantize_f32(hf, rows, I, hq, hs, st);
     if (rc) return rc;
+    rc = mx_panels_h(hs, offsets, E, R, shared ? R : 0, I, pa2, st);
+    if (rc) return rc;
     MxArgs g2{};
-    g2.A = hq; g2.As = hs; g2.a_es = shared ? R : 0;
-    g2.B = w2q; g2.Bs = w2s; g2.b_rows = H;
+    g2.A = hq; g2.At = pa2; g2.a_es = shared ? R : 0;
+    g2.B = w2q; g2.Bt = pb2; g2.b_rows = H;
     g2.C = y; g2.c_es = shared ? R : 0; g2.ldc = H;
     g2.offsets = offsets; g2.E = E; g2.R = R; g2.N = H; g2.K = I; g2.I = I;
     g2.total = shared ? E * cdiv(R, XBM) * cdiv(H, XBN) : 0;

@@ -1,5 +1,6 @@
 // Pieces shared by the grouped-GEMM kernels (BF16 and MXFP8): scalar buffer descriptors,
-// direct global-to-LDS loads, explicit wait counts and the K-major LDS row swizzle.
+// direct global-to-LDS loads, explicit wait counts, and the LDS tile layouts, load maps and
+// operand set-up of the pipelined tiles.
 #pragma once
 
 #include "common.h"
@@ -43,11 +44,129 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
 }
 
-// Swizzle of 64-byte K-major LDS rows (four 16-byte chunks): chunk c of row r is stored at
-// chunk c ^ kswz(r), which keeps the rows read by one 128-byte (8-lane) or 256-byte
-// (16-lane) phase of a 16-byte-per-lane read on distinct banks.
-__device__ __forceinline__ int kswz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-
 __host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- LDS tiles (both GEMM files)
+// The K step is BK = 32 or 64 (a template parameter of the tile); the stages fill 128 KB of
+// LDS, 4 of BK = 32 or 2 of BK = 64.  A 64-wide step makes each K-major tile row 128
+// contiguous bytes (a whole L2 line per request, half the requests of 64-byte rows); a 32-wide
+// step keeps three steps in flight instead of one, which pays where the rows are long
+// already (MN-major operands).  One stage holds one K step of both operands.  Two layouts:
+//  K-major   (operand contiguous along K in memory): tile row r (an M or N index) is BK * 2
+//            bytes of 16-byte chunks of 8 k values; chunk c is stored at chunk c ^ swz(r),
+//            swz = kswz4 (BK = 32) or kswz8 (BK = 64).  The rows read by one 128-byte (8-lane)
+//            or 256-byte (16-lane) phase of a fragment read then hit distinct bank groups.
+//  MN-major  (operand contiguous along M or N): k-row kr is 512 bytes, 32 chunks of 8 m (n)
+//            values; chunk c is stored at chunk c ^ mswz(kr % 4), mswz = {0, 6, 10, 12}, so
+//            the k-rows and columns read by one 16-lane (128-byte) or 32-lane (256-byte) phase
+//            of a transpose read hit distinct banks.
+// Both are filled by direct global-to-LDS loads (buffer_load ... lds): lane L of a wave
+// writes 16 bytes at LDS base + 16 L, so each lane fetches the global chunk that belongs at
+// its LDS position and the swizzle lives entirely in the global offsets.
+constexpr int LDS_STAGES_BYTES = 128 * 1024;
+
+template <int BK_>
+struct Pipe {
+    static constexpr int BK = BK_;
+    static constexpr int KK = BK / 16;              // 32x32x16 MFMA sub-steps per K step
+    static constexpr int KROW = BK * 2;             // bytes of one K-major tile row
+    static constexpr int OPB = 256 * BK * 2;        // bytes of one operand in one stage
+    static constexpr int NST = LDS_STAGES_BYTES / (2 * OPB);  // pipeline stages
+    static constexpr int LPW = OPB / 1024 / 4;      // direct loads per operand per wave per step
+    static constexpr int LPS = 2 * LPW;             // ... for both operands
+    static constexpr int RPI = 1024 / KROW;         // K-major tile rows per load instruction
+    static_assert(BK == 32 || BK == 64, "K step");
+};
+
+__device__ __forceinline__ int mswz(int kr) { return (0xCA60 >> (4 * (kr & 3))) & 15; }
+// K-major row swizzles, chosen so that the rows read by one 128-byte (8-lane) or 256-byte
+// (16-lane) phase of a 16-byte-per-lane fragment read hit distinct bank groups: kswz4 for
+// rows of four chunks, kswz8 for rows of eight (distinct over any 8 consecutive rows, and
+// over the even (odd) rows of any 16 consecutive rows).
+__device__ __forceinline__ int kswz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+__device__ __forceinline__ int kswz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+template <int BK>
+__device__ __forceinline__ int kswz_of(int r) { return BK == 64 ? kswz8(r) : kswz4(r); }
+
+// Per-lane description of one operand's global->LDS loads (LPW per wave per K step) and of
+// its MFMA fragment reads (4 sub-tiles of 32 rows per wave).  Wave w fills the quarter of
+// the operand's stage area at w OPB/4, 1 KB per instruction.  The global offset of load i
+// is voff[i % 2] + ((i / 2) % 2) ist1 + (i / 4) ist2: the swizzled chunk depends only on the
+// parity of i, and the rows of one wave's loads advance by two scalar strides.
+struct Operand {
+    rsrc_t r;
+    uint32_t voff[2];  // byte offset of this lane's 16-byte chunk, even / odd instructions
+    uint32_t ist1, ist2;  // byte advances of instructions 2, 3 and 4-7 (see above)
+    uint32_t kstep;    // byte advance of the global offset per K step
+    // fragment-read offsets: K-major, per sub-step kk (sub-tile t adds 32 t KROW, an
+    // immediate); MN-major, per sub-tile t (sub-step kk adds 8192 kk)
+    uint32_t rd[4];
+};
+
+// K-major operand.  rowmap(nn) gives the global row (relative to the descriptor base) of
+// tile row nn.  Each wave loads 64 tile rows, RPI rows of BK * 2 bytes per instruction:
+// tile rows 64 w + RPI i + L / (64 / RPI) for instruction i, whose global rows must be those
+// of instruction i % 2 plus ((i / 2) % 2) rs1 + (i / 4) rs2.
+template <int BK, typename RowMap>
+__device__ __forceinline__ void setup_kmajor(Operand& o, const void* base, uint32_t bytes, int ld,
+                                             int wid, int lane, int wsub, RowMap rowmap,
+                                             int rs1, int rs2) {
+    typedef Pipe<BK> PP;
+    constexpr int CPR = PP::KROW / 16;  // 16-byte chunks per row
+    o.r = make_rsrc(base, bytes);
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        const int r = 64 * wid + PP::RPI * par + lane / CPR;
+        const int c = (lane % CPR) ^ kswz_of<BK>(r);
+        o.voff[par] = (uint32_t)rowmap(r) * (uint32_t)ld * 2u + (uint32_t)c * 16u;
+    }
+    o.ist1 = (uint32_t)rs1 * (uint32_t)ld * 2u;
+    o.ist2 = (uint32_t)rs2 * (uint32_t)ld * 2u;
+    o.kstep = BK * 2;
+    // fragment reads: lane reads row wsub + 32 t + lane%32, logical chunk 2 kk + lane/32,
+    // stored at chunk (2 kk + lane/32) ^ swz(row); swz does not depend on t
+    const int r = wsub + (lane & 31);
+    const int x = (lane >> 5) ^ kswz_of<BK>(r);
+#pragma unroll
+    for (int kk = 0; kk < PP::KK; ++kk)
+        o.rd[kk] = (uint32_t)(r * PP::KROW) + ((uint32_t)((2 * kk) ^ x) << 4);
+}
+
+// MN-major operand: element (mn, k) at base + k*ld + mn (bytes x2).  Each wave loads
+// BK/4 k-rows of the step, 2 per instruction.
+template <int BK>
+__device__ __forceinline__ void setup_mnmajor(Operand& o, const void* base, uint32_t bytes, int ld,
+                                              int wid, int lane, int wsub) {
+    o.r = make_rsrc(base, bytes);
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        const int kr = (BK / 4) * wid + 2 * par + (lane >> 5);
+        const int c = (lane & 31) ^ mswz(kr);
+        o.voff[par] = (uint32_t)kr * (uint32_t)ld * 2u + (uint32_t)c * 16u;
+    }
+    o.ist1 = 4u * (uint32_t)ld * 2u;
+    o.ist2 = 8u * (uint32_t)ld * 2u;
+    o.kstep = (uint32_t)BK * (uint32_t)ld * 2u;
+    // transpose reads: lane group g = lane/16, q = lane%4, j = (lane%16)/4 reads k-row
+    // 16 kk + 8 (g/2) + 4 h + j at columns mnb + 16 (g%2) + 4 q .. +3
+    const int gq = lane >> 4, q = lane & 3, j = (lane >> 2) & 3;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int mn = wsub + 32 * t + 16 * (gq & 1) + 4 * q;
+        const int kr = 8 * (gq >> 1) + j;
+        const int pc = (mn >> 3) ^ mswz(j);
+        o.rd[t] = (uint32_t)(kr * 512 + pc * 16 + 8 * (q & 1));
+    }
+}
+
+// Load instruction i of K step ks into the operand's area of a stage.  Steps past the end
+// of K use an empty descriptor: the load still issues (so every step issues the same number
+// of loads and the wait counts are constants) but fetches nothing and writes zeros.
+template <int BK>
+__device__ __forceinline__ void issue_load(const Operand& o, uint32_t stage_op, int wid, int i,
+                                           rsrc_t r, uint32_t soff) {
+    lds_load16(r, stage_op + (uint32_t)(wid * (Pipe<BK>::OPB / 4) + i * 1024), o.voff[i & 1],
+               soff + (uint32_t)((i >> 1) & 1) * o.ist1 + (uint32_t)(i >> 2) * o.ist2);
+}
 
 }  // namespace moe
