@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--ring-depth", type=int, default=16,
                     help="minibatches per pass of the macrobatch ring (workloads that stream "
                          "tokens in minibatches)")
+    ap.add_argument("--fused", action="store_true",
+                    help="run each step's forward as one cooperative launch (moe_layer_forward)")
     ap.add_argument("--bias-gamma", type=float, default=0.0,
                     help="> 0: the sigmoid router's load-balancing bias is updated from the "
                          "step's loads with this speed (auxiliary-loss-free balancing)")
@@ -305,9 +307,14 @@ def main():
     lcfg = LayerCfg.from_workload(wl)
     lcfg.bias_gamma = a.bias_gamma
     layer = MoELayer(lcfg, inp, dev, backward=wl.backward, **ring)
+    can_fuse = not wl.mx and not layer.ring and not (wl.local_share and a.bias_gamma > 0)
+    if a.fused and not can_fuse:
+        print("--fused runs the unstreamed BF16 layer only", file=sys.stderr)
+        sys.exit(2)
+    fwd = layer.forward_fused if a.fused else layer.forward
 
     def step():
-        layer.forward()
+        fwd()
         if wl.backward:
             layer.backward()
 
@@ -327,15 +334,20 @@ def main():
     elapsed = t1 - t0
     ms_step = elapsed * 1e3 / a.steps
 
-    # forward-only steps, untraced
-    for _ in range(2):
-        layer.forward()
-    torch.cuda.synchronize()
-    f0 = time.perf_counter()
-    for _ in range(a.steps):
-        layer.forward()
-    torch.cuda.synchronize()
-    fwd_ms = (time.perf_counter() - f0) * 1e3 / a.steps
+    # forward-only steps, untraced: the per-step calls, and (where it applies) the forward
+    # as one cooperative launch
+    def time_fwd(f):
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize()
+        f0 = time.perf_counter()
+        for _ in range(a.steps):
+            f()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - f0) * 1e3 / a.steps
+
+    fwd_ms = time_fwd(layer.forward)
+    fused_ms = time_fwd(layer.forward_fused) if can_fuse else None
 
     # per-role statistics over the timed region
     roles: dict[str, list[float]] = {}
@@ -373,6 +385,8 @@ def main():
         cfg.update(minibatch=layer.mb, ring_depth=layer.D, ring_passes=layer.passes)
     if a.bias_gamma > 0:
         cfg.update(bias_gamma=a.bias_gamma)
+    if a.fused:
+        cfg.update(forward="one cooperative launch")
     out = {
         "metric": METRIC,
         "value": round(wl.T * a.steps / elapsed, 1),
@@ -387,6 +401,8 @@ def main():
         "fwd_ms_per_step": round(fwd_ms, 4),
         "step_tflops": round(flops_step / (ms_step * 1e-3) / 1e12, 1),
         "fwd_tflops": round(flops_fwd / (fwd_ms * 1e-3) / 1e12, 1),
+        "fused_fwd_ms_per_step": round(fused_ms, 4) if fused_ms else None,
+        "fused_fwd_tokens_per_s": round(wl.T / (fused_ms * 1e-3), 1) if fused_ms else None,
         "roofline": roof,
         "breakdown": breakdown,
         "cpu_baseline": None,

@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* return codes */
 #define MOE_OK 0
@@ -161,6 +161,55 @@ int moe_expert_ffn(int dtype, const void *xp, const uint8_t *xp_scales, const in
  * pos values outside [0,R) contribute nothing.  H % 8 == 0. */
 int moe_combine(const void *y, const int32_t *pos, const float *w, int T, int k, int H, int R,
                 const void *ys, int S, void *out, void *stream);
+
+/* ------------------------------------------------------------------ the forward in one launch
+ * moe_layer_forward: the whole BF16 forward of the layer -- router projection (optional),
+ * top-k routing, the expert-contiguous permutation, dispatch, the routed and shared experts'
+ * GEMM1 + SwiGLU and GEMM2, and the weighted combine -- as ONE cooperative, persistent kernel
+ * launch (the single MoE kernel of pulsen.vercel.app ¶3 and ki-pruefstand.de "Kommunikation
+ * im Kernel" ¶2, at one GPU): one block per compute unit walks each step's work and
+ * device-wide barriers separate the steps, so no host round trip or launch gap sits between
+ * them.  Every output is bit-identical to the one the per-step calls give (moe_route with the
+ * same cfg, moe_dispatch with pos, moe_expert_ffn in BF16 for the routed experts and for the
+ * shared experts with offsets NULL, moe_combine).
+ * Fields (DEVICE pointers unless noted; R = T*k routed rows):
+ *   T, H, E, k, I      tokens, hidden size, routed experts on this GPU, slots, intermediate;
+ *   S, Is              shared experts (S = 0: none) and their intermediate size;
+ *   E_router           experts the router scores;  cfg: router configuration (as moe_route);
+ *   x [T,H] bf16;  w_router [E_router,H] bf16 or NULL;
+ *   logits [T,E_router] fp32: read, or first WRITTEN with the projection when w_router given;
+ *   idx_in [T,k] int32 local expert ids in [0,E), or NULL (then E must equal E_router and the
+ *          router's own choice is permuted).  Given: one GPU's share of a larger layer -- the
+ *          router still selects over E_router experts and its weights w scale the combine,
+ *          while the rows are permuted by idx_in;
+ *   w1 [E,2I,H], w2 [E,H,I], ws1 [S,2Is,H], ws2 [S,H,Is] bf16;
+ *   idx, w, s_sel [T,k];  counts [E], offsets [E+1], pos [T,k], src [R] (as moe_route);
+ *   xp [R,H], h [R,I], y [R,H] bf16;  gu [R,2I] bf16 or NULL (the backward's save);
+ *   hs [S,T,Is], ys [S,T,H] bf16;  gus [S,T,2Is] bf16 or NULL;  out [T,H] bf16.
+ * Limits: 1 <= E <= 256, 1 <= E_router <= 256, 1 <= k <= min(E_router, 64), T >= 1,
+ * H % 64 == 0, I % 64 == 0 (Is too when S > 0), R*max(H,2I) < 2^31.  The launch needs every
+ * block resident at once (one per CU); MOE_EHIP if the device refuses the cooperative launch.
+ * Workspace: moe_layer_forward_workspace_size(). */
+typedef struct moe_fwd_args {
+    int T, H, E, k, I;
+    int S, Is;
+    int E_router;
+    moe_route_cfg cfg;
+    const void *x;
+    const void *w_router;
+    float *logits;
+    const int32_t *idx_in;
+    const void *w1, *w2, *ws1, *ws2;
+    int32_t *idx;
+    float *w, *s_sel;
+    int32_t *counts, *offsets, *pos, *src;
+    void *xp, *gu, *h, *y;
+    void *gus, *hs, *ys;
+    void *out;
+} moe_fwd_args;
+
+size_t moe_layer_forward_workspace_size(const moe_fwd_args *a);
+int moe_layer_forward(const moe_fwd_args *a, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------ backward
  * BF16 backward of the whole layer (pulsen.vercel.app ¶3) given the upstream gradient dout

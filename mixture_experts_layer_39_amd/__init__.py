@@ -46,6 +46,14 @@ class BwdArgs(ctypes.Structure):
                                    "dlogits")] + \
                [(n, _i) for n in ("passes", "pass_tokens", "pass_rows")]
 
+class FwdArgs(ctypes.Structure):
+    _fields_ = [(n, _i) for n in ("T", "H", "E", "k", "I", "S", "Is", "E_router")] + \
+               [("cfg", RouteCfg)] + \
+               [(n, _vp) for n in ("x", "w_router", "logits", "idx_in", "w1", "w2", "ws1", "ws2",
+                                   "idx", "w", "s_sel", "counts", "offsets", "pos", "src", "xp",
+                                   "gu", "h", "y", "gus", "hs", "ys", "out")]
+
+
 _INT_FIELDS = ("T", "H", "E", "k", "I", "R", "S", "Is", "E_router", "score", "renorm", "passes",
                "pass_tokens", "pass_rows")
 
@@ -78,6 +86,9 @@ def lib() -> ctypes.CDLL:
         L.moe_backward_workspace_size.restype = _sz
         L.moe_backward_workspace_size.argtypes = [ctypes.POINTER(BwdArgs)]
         L.moe_backward.argtypes = [ctypes.POINTER(BwdArgs), _vp, _sz, _vp]
+        L.moe_layer_forward_workspace_size.restype = _sz
+        L.moe_layer_forward_workspace_size.argtypes = [ctypes.POINTER(FwdArgs)]
+        L.moe_layer_forward.argtypes = [ctypes.POINTER(FwdArgs), _vp, _sz, _vp]
         L.mx_quantize.argtypes = [_vp, _i, _i, _i, _vp, _vp, _i, _vp]
         L.moe_trace_begin.argtypes = [_i]
         L.moe_trace_end.argtypes = []
@@ -191,6 +202,33 @@ def moe_backward(a: BwdArgs, ws, stream=None):
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     rc = lib().moe_backward(ctypes.byref(a), _p(ws), nbytes, _stream(stream))
     _check("moe_backward", rc)
+
+
+def fwd_args(*, score=SCORE_SOFTMAX, n_groups=1, topk_groups=1, renorm=True, route_scale=1.0,
+             sel_bias=None, **kw) -> FwdArgs:
+    """Arguments of moe_layer_forward: sizes as ints, tensors (or raw device addresses)."""
+    a = FwdArgs()
+    a.cfg = RouteCfg(score, n_groups, topk_groups, int(renorm), route_scale,
+                     None if sel_bias is None else sel_bias.data_ptr())
+    for name, _ in FwdArgs._fields_:
+        v = kw.get(name)
+        if name == "cfg" or v is None:
+            continue
+        if name in ("T", "H", "E", "k", "I", "S", "Is", "E_router"):
+            setattr(a, name, int(v))
+        else:
+            setattr(a, name, v if isinstance(v, int) else v.data_ptr())
+    return a
+
+
+def layer_forward_workspace_size(a: FwdArgs) -> int:
+    return lib().moe_layer_forward_workspace_size(ctypes.byref(a))
+
+
+def moe_layer_forward(a: FwdArgs, ws, stream=None):
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    rc = lib().moe_layer_forward(ctypes.byref(a), _p(ws), nbytes, _stream(stream))
+    _check("moe_layer_forward", rc)
 
 
 def mx_quantize(inp, in_dtype, rows, K, codes, scales, scale_mode=MX_FLOOR, stream=None):

@@ -30,7 +30,11 @@
 //    block scans the per-expert tile counts in a wave and finds its tile.
 //  - The backward's independent dgrad/wgrad pairs share one launch each (bwd_down,
 //    bwd_gate_up), so that one fills the other's last partial round of tiles.
+#include <hip/hip_cooperative_groups.h>
+
 #include "pipe.h"
+#include "route_dev.h"
+#include "rows_dev.h"
 
 namespace moe {
 
@@ -645,6 +649,90 @@ static int launch_pair(void (*kern)(GemmArgs, GemmArgs), const char* name, const
     return MOE_OK;
 }
 
+// ---------------------------------------------------------------- the layer in one launch
+// The forward of the layer -- top-k routing, the expert-contiguous permutation, dispatch,
+// GEMM1 + SwiGLU, GEMM2 and the combine -- as one persistent, cooperative kernel: one block
+// per CU walks each step's work items in turn and device-wide barriers separate the steps, so
+// the GPU runs the whole layer from one launch with no host in between (the single fused
+// MoE kernel of pulsen.vercel.app, "Cursor åpner megakernelen…", ¶3, and ki-pruefstand.de,
+// "Cursor veröffentlicht MoE-Megakernel…", "Kommunikation im Kernel" ¶2, on one GPU).  Every
+// step runs the same device code as its own kernel, so the outputs are bit-identical to the
+// step-by-step launches.  The 160 KB of LDS serve every step in turn.
+struct FusedFwd {
+    const bf16_t* wr;         // router weights [E_router,H], or null: the logits are given
+    float* proj;              // logits written by the projection (tp.logits), or null
+    TopkParams tp;            // top-k over the router logits (tp.T tokens)
+    const int32_t* perm_ids;  // expert ids to permute: tp.idx, or the given local ids
+    int64_t n;                // pairs T * k
+    int E, nbits, nch;
+    int32_t* blk;             // [nch][E] chunk histograms (workspace)
+    int32_t *counts, *offsets, *pos, *src;
+    const bf16_t* x;
+    int T, H, k, R, S;
+    bf16_t* xp;
+    GemmArgs g1, g2;          // routed experts: GEMM1 + SwiGLU, GEMM2
+    GemmArgs s1, s2;          // shared experts (total 0 when there are none)
+    const bf16_t* ys;
+    bf16_t* out;
+};
+
+constexpr int FUSED_NV = 4;  // router experts per lane: E_router <= 256
+
+// The tiles of one forward product step: the routed product's (ragged, counted on the device
+// from the offsets) then the shared experts' (fixed count), spread over the resident blocks.
+template <int EPI>
+__device__ __forceinline__ void fused_gemm_step(const GemmArgs& routed, const GemmArgs& shared,
+                                                GemmSmem& sm) {
+    const int t1 = tile_total<EPI, false>(routed), total = t1 + shared.total;
+    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+        const bool r = tile < t1;
+        gemm_tile<BK_FWD, true, true, EPI, false>(r ? routed : shared, sm, r ? tile : tile - t1);
+        __syncthreads();  // the next tile's loads overwrite the slots
+    }
+}
+
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void layer_forward_fused(FusedFwd a) {
+    __shared__ GemmSmem sm;
+    cooperative_groups::grid_group grid = cooperative_groups::this_grid();
+    const int nb = gridDim.x, wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int* lds_i = reinterpret_cast<int*>(sm.st);
+    // 0. router projection (when the logits are not given): one thread per logit
+    if (a.wr) {
+        const int nl = a.tp.T * a.tp.E;
+        for (int id = blockIdx.x * NTH + threadIdx.x; id < nl; id += nb * NTH)
+            router_logit(a.x, a.wr, a.H, a.tp.E, id, a.proj);
+        grid.sync();
+    }
+    // 1. top-k and weights: one wave per token
+    for (int t = blockIdx.x * 4 + wid; t < a.tp.T; t += nb * 4)
+        topk_token<FUSED_NV>(a.tp, t, lane);
+    grid.sync();
+    // 2. chunk histograms of the expert ids: one block per chunk
+    for (int c = blockIdx.x; c < a.nch; c += nb) count_chunk(a.perm_ids, a.n, a.E, a.blk, c, lds_i);
+    grid.sync();
+    // 3. counts, offsets and chunk bases: one block
+    if (blockIdx.x == 0)
+        scan_body(a.blk, a.nch, a.E, a.counts, a.offsets, lds_i, lds_i + SCAN_LDS);
+    grid.sync();
+    // 4. ranks: one wave per chunk, each with its own counters
+    for (int c = blockIdx.x * 4 + wid; c < a.nch; c += nb * 4)
+        rank_chunk(a.perm_ids, a.n, a.E, a.nbits, a.blk, a.pos, a.src, c, lds_i + wid * a.E);
+    grid.sync();
+    // 5. dispatch: one block per source token
+    for (int t = blockIdx.x; t < a.T; t += nb) dispatch_token<NTH>(a.x, a.H, a.k, a.pos, a.R, a.xp, t, lds_i);
+    grid.sync();
+    // 6. GEMM1 + SwiGLU, 7. GEMM2
+    fused_gemm_step<EPI_SWIGLU>(a.g1, a.s1, sm);
+    grid.sync();
+    fused_gemm_step<EPI_STORE>(a.g2, a.s2, sm);
+    grid.sync();
+    // 8. combine: one block per token
+    for (int t = blockIdx.x; t < a.T; t += nb)
+        combine_token<NTH>(a.g2.C, a.pos, a.tp.w, a.T, a.k, a.H, a.R, a.ys, a.S, a.out, t,
+                           lds_i, reinterpret_cast<float*>(lds_i + MAXK));
+}
+
 static GemmArgs blank() {
     GemmArgs g{};
     return g;
@@ -656,26 +744,111 @@ using namespace moe;
 
 // ---------------------------------------------------------------------- internal API
 // Forward FFN in BF16.  offsets == null: shared mode (every expert takes all R rows).
-int moe_ffn_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, int I,
-                 const bf16_t* w1, const bf16_t* w2, bf16_t* gu, bf16_t* h, bf16_t* y,
-                 hipStream_t st) {
+// Arguments of the forward GEMMs (GEMM1 + SwiGLU, GEMM2) of one FFN call.
+static void ffn_args(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, int I,
+                     const bf16_t* w1, const bf16_t* w2, bf16_t* gu, bf16_t* h, bf16_t* y,
+                     GemmArgs& g, GemmArgs& g2) {
     const bool shared = offsets == nullptr;
-    GemmArgs g = blank();
+    g = blank();
     g.A = xp; g.a_es = 0; g.lda = H;
     g.B = w1; g.b_es = (int64_t)2 * I * H; g.ldb = H; g.b_rows = 2 * I;
     g.C = h; g.c_es = shared ? (int64_t)R * I : 0; g.ldc = I;
     g.C2 = gu; g.c2_es = shared ? (int64_t)R * 2 * I : 0; g.ldc2 = 2 * I;
     g.offsets = offsets; g.E = E; g.R = R; g.N = 2 * I; g.K = H; g.I = I;
     g.total = shared ? E * cdiv(R, BM) * cdiv(I, 128) : 0;
-    int rc = launch(gemm1_swiglu, "gemm1_swiglu", g, cdiv(I, 128), st);
-    if (rc) return rc;
-    GemmArgs g2 = blank();
+    g2 = blank();
     g2.A = h; g2.a_es = shared ? (int64_t)R * I : 0; g2.lda = I;
     g2.B = w2; g2.b_es = (int64_t)H * I; g2.ldb = I; g2.b_rows = H;
     g2.C = y; g2.c_es = shared ? (int64_t)R * H : 0; g2.ldc = H;
     g2.offsets = offsets; g2.E = E; g2.R = R; g2.N = H; g2.K = I; g2.I = I;
     g2.total = shared ? E * cdiv(R, BM) * cdiv(H, BN) : 0;
+}
+
+int moe_ffn_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, int I,
+                 const bf16_t* w1, const bf16_t* w2, bf16_t* gu, bf16_t* h, bf16_t* y,
+                 hipStream_t st) {
+    GemmArgs g, g2;
+    ffn_args(xp, offsets, E, R, H, I, w1, w2, gu, h, y, g, g2);
+    int rc = launch(gemm1_swiglu, "gemm1_swiglu", g, cdiv(I, 128), st);
+    if (rc) return rc;
     return launch(gemm2_down, "gemm2_down", g2, cdiv(H, BN), st);
+}
+
+extern "C" size_t moe_layer_forward_workspace_size(const moe_fwd_args* a) {
+    if (!a) return 0;
+    return moe_route_workspace_size(a->T, a->k, a->E);
+}
+
+extern "C" int moe_layer_forward(const moe_fwd_args* p, void* ws, size_t ws_bytes, void* stream) {
+    MOE_REQUIRE(p);
+    const moe_fwd_args& f = *p;
+    const moe_route_cfg& cfg = f.cfg;
+    MOE_REQUIRE(f.T >= 1 && f.k >= 1 && f.k <= MAXK && f.E >= 1 && f.E <= 256);
+    MOE_REQUIRE(f.E_router >= 1 && f.E_router <= 64 * FUSED_NV && f.k <= f.E_router);
+    MOE_REQUIRE(f.idx_in || f.E == f.E_router);
+    MOE_REQUIRE(f.H >= 64 && f.H % 64 == 0 && f.I >= 64 && f.I % 64 == 0);
+    MOE_REQUIRE(f.S >= 0 && (f.S == 0 || (f.Is >= 64 && f.Is % 64 == 0)));
+    const int64_t R = (int64_t)f.T * f.k;
+    MOE_REQUIRE(R * f.H < (1ll << 31) && R * 2 * f.I < (1ll << 31));
+    MOE_REQUIRE((int64_t)f.S * f.T * f.H < (1ll << 31) && (int64_t)f.S * f.T * 2 * f.Is < (1ll << 31));
+    MOE_REQUIRE(f.x && f.logits && f.w1 && f.w2 && f.idx && f.w && f.s_sel && f.counts &&
+                f.offsets && f.pos && f.src && f.xp && f.h && f.y && f.out);
+    MOE_REQUIRE(f.S == 0 || (f.ws1 && f.ws2 && f.hs && f.ys));
+    MOE_REQUIRE(cfg.score == MOE_SCORE_SOFTMAX || cfg.score == MOE_SCORE_SIGMOID);
+    const int n_groups = cfg.n_groups < 1 ? 1 : cfg.n_groups;
+    const int topk_groups = (cfg.topk_groups < 1 || n_groups == 1) ? n_groups : cfg.topk_groups;
+    MOE_REQUIRE(n_groups <= 64 && f.E_router % n_groups == 0 && topk_groups <= n_groups);
+    const int per_group = f.k / topk_groups < 1 ? 1 : f.k / topk_groups;
+    MOE_REQUIRE(per_group <= f.E_router / n_groups && f.k <= topk_groups * (f.E_router / n_groups));
+    const size_t need = moe_layer_forward_workspace_size(p);
+    if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+    int rc = moe_check_device();
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        ncu < 1)
+        return MOE_EHIP;
+    // one block per CU: every block of a cooperative launch must be resident at once
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, layer_forward_fused, NTH, 0) !=
+            hipSuccess || per_cu < 1)
+        return MOE_EHIP;
+    FusedFwd a{};
+    a.wr = (const bf16_t*)f.w_router;
+    a.proj = f.w_router ? f.logits : nullptr;
+    a.tp = TopkParams{f.logits, cfg.sel_bias, f.T, f.E_router, f.k, cfg.score, n_groups,
+                      topk_groups, per_group, cfg.renorm, cfg.route_scale, f.idx, f.w, f.s_sel};
+    a.perm_ids = f.idx_in ? f.idx_in : f.idx;
+    a.n = R;
+    a.E = f.E;
+    int nbits = 0;
+    while ((1 << nbits) < f.E) ++nbits;
+    a.nbits = nbits;
+    a.nch = (int)((R + CHUNK - 1) / CHUNK);
+    a.blk = (int32_t*)ws;
+    a.counts = f.counts; a.offsets = f.offsets; a.pos = f.pos; a.src = f.src;
+    a.x = (const bf16_t*)f.x;
+    a.T = f.T; a.H = f.H; a.k = f.k; a.R = (int)R; a.S = f.S;
+    a.xp = (bf16_t*)f.xp;
+    ffn_args((const bf16_t*)f.xp, f.offsets, f.E, a.R, f.H, f.I, (const bf16_t*)f.w1,
+             (const bf16_t*)f.w2, (bf16_t*)f.gu, (bf16_t*)f.h, (bf16_t*)f.y, a.g1, a.g2);
+    if (f.S > 0)
+        ffn_args((const bf16_t*)f.x, nullptr, f.S, f.T, f.H, f.Is, (const bf16_t*)f.ws1,
+                 (const bf16_t*)f.ws2, (bf16_t*)f.gus, (bf16_t*)f.hs, (bf16_t*)f.ys, a.s1, a.s2);
+    a.ys = (const bf16_t*)f.ys;
+    a.out = (bf16_t*)f.out;
+    void* params[] = {&a};
+    hipError_t err = hipSuccess;
+    MOE_TRACED("layer_forward_fused", st,
+               err = hipLaunchCooperativeKernel((const void*)layer_forward_fused, dim3(ncu),
+                                                dim3(NTH), params, 0, st));
+    if (err != hipSuccess) {
+        (void)hipGetLastError();
+        return MOE_EHIP;
+    }
+    return MOE_OK;
 }
 
 // Backward of the FFN for one group of experts, over the rows of one pass (pointers already

@@ -6,7 +6,7 @@
 // because source and destination rows are both contiguous.  Every reduction runs in a fixed
 // order (slots, then shared experts; fixed butterfly trees), so results are bit-identical
 // from run to run (pulsen.vercel.app, "Cursor åpner megakernelen…", ¶3-¶4).
-#include "common.h"
+#include "rows_dev.h"
 
 namespace moe {
 
@@ -64,8 +64,6 @@ __device__ __forceinline__ int mx_block(const float* v, int mode, uint32_t* q) {
 // One block per destination row: xp[r,:] = x[src[r]/k,:].  Each thread issues all of its
 // 16-byte loads (up to UN) before any store, so a CU keeps enough bytes in flight to cover
 // the memory latency.
-constexpr int ROW_UN = 8;
-constexpr int MAXK = 64;  // largest k the row kernels stage in LDS
 
 __global__ __launch_bounds__(128) void dispatch_kernel(const bf16_t* __restrict__ x, int64_t n_pairs,
                                                        int H, int k, const int32_t* __restrict__ src,
@@ -91,36 +89,11 @@ __global__ __launch_bounds__(128) void dispatch_kernel(const bf16_t* __restrict_
     }
 }
 
-// Token-driven dispatch: one block per source token fills the token's k destination rows
-// (pos[t,j]) from one read of its source row.
 __global__ __launch_bounds__(128) void dispatch_tok_kernel(const bf16_t* __restrict__ x, int H,
                                                            int k, const int32_t* __restrict__ pos,
                                                            int R, bf16_t* __restrict__ xp) {
     __shared__ int sp[MAXK];
-    const int t = blockIdx.x;
-    const bf16_t* in = x + (size_t)t * H;
-    if (threadIdx.x < k) sp[threadIdx.x] = pos[(size_t)t * k + threadIdx.x];
-    const int nc = H / 8;
-    // the loop bound is block-uniform, so the barrier (pos staged) in its first pass is too
-    for (int c0 = 0; c0 < nc; c0 += 128 * ROW_UN) {
-        u32x4 v[ROW_UN];
-#pragma unroll
-        for (int u = 0; u < ROW_UN; ++u) {
-            const int c = c0 + threadIdx.x + u * 128;
-            v[u] = c < nc ? ld16(in + c * 8) : u32x4{0, 0, 0, 0};
-        }
-        if (c0 == 0) __syncthreads();
-        for (int j = 0; j < k; ++j) {
-            const int r = sp[j];
-            if (r < 0 || r >= R) continue;
-            bf16_t* out = xp + (size_t)r * H;
-#pragma unroll
-            for (int u = 0; u < ROW_UN; ++u) {
-                const int c = c0 + threadIdx.x + u * 128;
-                if (c < nc) st16(out + c * 8, v[u]);
-            }
-        }
-    }
+    dispatch_token<128>(x, H, k, pos, R, xp, blockIdx.x, sp);
 }
 
 // Dispatch with MX quantisation: one thread per 32-value block of the destination row.
@@ -234,7 +207,6 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict
 }
 
 // ------------------------------------------------------------------ combine
-constexpr int RG = 2;  // 16-byte chunks per thread per pass in the gather-reduce kernels
 // One block per token.  Per element, fp32: acc = 0; acc += w[t,j]*y[pos[t,j]] for j = 0..k-1;
 // acc += ys[s,t] for s = 0..S-1; one rounding to bf16.
 
@@ -243,66 +215,9 @@ __global__ __launch_bounds__(128) void combine_kernel(const bf16_t* __restrict__
                                                       const float* __restrict__ w, int T, int k,
                                                       int H, int R, const bf16_t* __restrict__ ys,
                                                       int S, bf16_t* __restrict__ out) {
-    const int t = blockIdx.x;
     __shared__ int sp[MAXK];
     __shared__ float sw[MAXK];
-    if (threadIdx.x < k) {
-        int p = pos[(size_t)t * k + threadIdx.x];
-        sp[threadIdx.x] = (p >= 0 && p < R) ? p : -1;
-        sw[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
-    }
-    __syncthreads();
-    const int nc = H / 8;
-    // each thread takes RG chunks per pass and loads every slot's rows of them before
-    // summing any (the summation order per element is unchanged)
-    for (int c0 = threadIdx.x; c0 < nc; c0 += 128 * RG) {
-        float acc[RG][8];
-#pragma unroll
-        for (int g = 0; g < RG; ++g)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
-        for (int j0 = 0; j0 < k; j0 += 8) {
-            u32x4 v[RG][8];
-#pragma unroll
-            for (int g = 0; g < RG; ++g)
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int j = j0 + u, c = c0 + g * 128;
-                    const int p = j < k ? sp[j] : -1;
-                    v[g][u] = (p >= 0 && c < nc) ? ld16(y + (size_t)p * H + c * 8) : u32x4{0, 0, 0, 0};
-                }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int j = j0 + u;
-                if (j >= k || sp[j] < 0) continue;
-                const float wj = sw[j];
-#pragma unroll
-                for (int g = 0; g < RG; ++g)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[g][2 * q] = __fadd_rn(acc[g][2 * q], __fmul_rn(wj, lo_bf(v[g][u][q])));
-                        acc[g][2 * q + 1] = __fadd_rn(acc[g][2 * q + 1], __fmul_rn(wj, hi_bf(v[g][u][q])));
-                    }
-            }
-        }
-#pragma unroll
-        for (int g = 0; g < RG; ++g) {
-            const int c = c0 + g * 128;
-            if (c >= nc) continue;
-            for (int s = 0; s < S; ++s) {
-                u32x4 v = ld16(ys + ((size_t)s * T + t) * H + c * 8);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[g][2 * q] = __fadd_rn(acc[g][2 * q], lo_bf(v[q]));
-                    acc[g][2 * q + 1] = __fadd_rn(acc[g][2 * q + 1], hi_bf(v[q]));
-                }
-            }
-            u32x4 o;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[g][2 * q], acc[g][2 * q + 1]);
-            st16(out + (size_t)t * H + c * 8, o);
-        }
-    }
+    combine_token<128>(y, pos, w, T, k, H, R, ys, S, out, blockIdx.x, sp, sw);
 }
 
 // ------------------------------------------------------------------ combine backward

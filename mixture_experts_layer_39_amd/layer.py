@@ -21,8 +21,9 @@ import dataclasses
 import torch
 
 from . import (BF16, MXFP8, F32, SCORE_SIGMOID, backward_workspace_size, bwd_args,
-               ffn_workspace_size, moe_backward, moe_combine, moe_dispatch, moe_expert_ffn,
-               moe_route, moe_update_bias, mx_quantize, route_workspace_size)
+               ffn_workspace_size, fwd_args, layer_forward_workspace_size, moe_backward,
+               moe_combine, moe_dispatch, moe_expert_ffn, moe_layer_forward, moe_route,
+               moe_update_bias, mx_quantize, route_workspace_size)
 
 
 @dataclasses.dataclass
@@ -242,6 +243,35 @@ class MoELayer:
         self.dispatch()
         self.experts()
         self.combine()
+        return self.out
+
+    # ------------------------------------------------------------------ one launch
+    def forward_fused(self):
+        """The same forward as forward(), as one cooperative kernel launch (moe_layer_forward).
+        BF16, unstreamed layers; outputs are bit-identical to forward()'s."""
+        c, inp = self.cfg, self.inp
+        if self.ring or c.mx:
+            raise ValueError("the single-launch forward runs the unstreamed BF16 layer")
+        if c.local_share and c.bias_gamma > 0:
+            raise ValueError("the single-launch forward does not count the router's global "
+                             "loads of a local share")
+        if not hasattr(self, "fused"):
+            self.fused = fwd_args(
+                T=c.T, H=c.H, E=c.E, k=self.kr, I=c.I, S=c.S, Is=c.Is, E_router=c.ER,
+                score=c.score, n_groups=c.n_groups, topk_groups=c.topk_groups,
+                renorm=c.renorm, route_scale=c.route_scale, sel_bias=self.sel_bias,
+                x=inp["x"], w_router=inp.get("w_router") if c.router_proj else None,
+                logits=self.logits, idx_in=inp["idx_local"] if c.local_share else None,
+                w1=inp["w1"], w2=inp["w2"], ws1=inp.get("ws1") if c.S else None,
+                ws2=inp.get("ws2") if c.S else None, idx=self.idx, w=self.w, s_sel=self.s_sel,
+                counts=self.counts, offsets=self.offsets, pos=self.pos, src=self.src,
+                xp=self.xp, gu=self.gu, h=self.h, y=self.y, gus=self.gus if c.S else None,
+                hs=self.hs if c.S else None, ys=self.ys, out=self.out)
+            self.fused_ws = _e((max(layer_forward_workspace_size(self.fused), 256),),
+                               torch.uint8, self.dev)
+        moe_layer_forward(self.fused, self.fused_ws)
+        if c.bias_gamma > 0:
+            moe_update_bias(self.counts, c.ER, c.bias_gamma, self.sel_bias)
         return self.out
 
     # ------------------------------------------------------------------ macrobatch ring

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert moe.abi_version() == 3
+    assert moe.abi_version() == 4
     assert moe.strerror(0) == "ok"
     assert "workspace" in moe.strerror(-2)
     assert moe.strerror(12345) == "unknown error"
@@ -136,3 +136,63 @@ def test_backward_validation():
 def test_binding_raises_on_error_code():
     with pytest.raises(moe.MoeError):
         moe._check("moe_route", moe.MOE_EINVAL)
+
+
+def fwd(**kw):
+    base = dict(T=16, H=128, E=4, k=2, I=128, S=0, Is=0, E_router=4, x=FAKE.value,
+                logits=FAKE.value, w1=FAKE.value, w2=FAKE.value, idx=FAKE.value, w=FAKE.value,
+                s_sel=FAKE.value, counts=FAKE.value, offsets=FAKE.value, pos=FAKE.value,
+                src=FAKE.value, xp=FAKE.value, h=FAKE.value, y=FAKE.value, out=FAKE.value)
+    base.update(kw)
+    wsb = base.pop("wsb", 1 << 20)
+    ws = base.pop("ws", FAKE)
+    a = moe.fwd_args(**base)
+    return lib().moe_layer_forward(ctypes.byref(a), ws, wsb, None)
+
+
+def test_layer_forward_validation():
+    assert lib().moe_layer_forward(None, FAKE, 1 << 20, None) == moe.MOE_EINVAL
+    assert fwd(E=300, E_router=300) == moe.MOE_EINVAL      # more experts than the kernel holds
+    assert fwd(E_router=8) == moe.MOE_EINVAL               # E != E_router without idx_in
+    assert fwd(k=0) == moe.MOE_EINVAL
+    assert fwd(k=5) == moe.MOE_EINVAL                      # k > E_router
+    assert fwd(T=0) == moe.MOE_EINVAL
+    assert fwd(H=96) == moe.MOE_EINVAL
+    assert fwd(I=100) == moe.MOE_EINVAL
+    assert fwd(S=1, Is=128) == moe.MOE_EINVAL              # shared experts without weights
+    assert fwd(out=None) == moe.MOE_EINVAL
+    assert fwd(n_groups=3) == moe.MOE_EINVAL               # E_router % groups
+    assert fwd(ws=None) == moe.MOE_EWORKSPACE
+    assert fwd(wsb=8) == moe.MOE_EWORKSPACE
+    a = moe.fwd_args(T=2048, E=4, k=8, E_router=256)
+    assert moe.layer_forward_workspace_size(a) >= moe.route_workspace_size(2048, 8, 4)
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The ctypes mirrors of the argument structs have the C layout of include/moe.h."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "lay.c"
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', "int main(void){"]
+    for cname, cls in (("moe_bwd_args", moe.BwdArgs), ("moe_fwd_args", moe.FwdArgs),
+                       ("moe_route_cfg", moe.RouteCfg)):
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0;}")
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "lay"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    got = {}
+    for line in out.splitlines():
+        c, f, v = line.split()
+        got[(c, f)] = int(v)
+    for cname, cls in (("moe_bwd_args", moe.BwdArgs), ("moe_fwd_args", moe.FwdArgs),
+                       ("moe_route_cfg", moe.RouteCfg)):
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert got[(cname, f)] == getattr(cls, f).offset, (cname, f)
