@@ -187,8 +187,16 @@ int moe_combine(const void *y, const int32_t *pos, const float *w, int T, int k,
  *   xp [R,H], h [R,I], y [R,H] bf16;  gu [R,2I] bf16 or NULL (the backward's save);
  *   hs [S,T,Is], ys [S,T,H] bf16;  gus [S,T,2Is] bf16 or NULL;  out [T,H] bf16.
  * Limits: 1 <= E <= 256, 1 <= E_router <= 256, 1 <= k <= min(E_router, 64), T >= 1,
- * H % 64 == 0, I % 64 == 0 (Is too when S > 0), R*max(H,2I) < 2^31.  The launch needs every
- * block resident at once (one per CU); MOE_EHIP if the device refuses the cooperative launch.
+ * 0 <= S <= 64, H % 64 == 0, I % 64 == 0 (Is too when S > 0), R*max(H,2I) < 2^31.
+ * Execution: a one-block clear of the workspace's synchronisation words, then the cooperative
+ * kernel with one block per CU (every block resident at once; MOE_EHIP if the device refuses
+ * the launch).  Inside, the routing steps and the dispatch are separated by device-wide
+ * barriers; the expert products and the combine form one queue of work items (GEMM1 tiles,
+ * GEMM2 tiles, combine groups of tokens) claimed in order, each waiting only for the tiles it
+ * reads (per-row-block completion counters).  Every wait is bounded (2 s): one that runs out
+ * sets the 32-bit word at byte offset moe_layer_forward_error_offset() of ws to nonzero and
+ * the outputs are then undefined; the word is 0 after a call that completed normally.
+ * Concurrent calls need distinct workspaces.
  * Workspace: moe_layer_forward_workspace_size(). */
 typedef struct moe_fwd_args {
     int T, H, E, k, I;
@@ -209,6 +217,7 @@ typedef struct moe_fwd_args {
 } moe_fwd_args;
 
 size_t moe_layer_forward_workspace_size(const moe_fwd_args *a);
+size_t moe_layer_forward_error_offset(const moe_fwd_args *a);
 int moe_layer_forward(const moe_fwd_args *a, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------ backward

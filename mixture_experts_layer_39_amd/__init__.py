@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward_workspace_size.restype = _sz
         L.moe_layer_forward_workspace_size.argtypes = [ctypes.POINTER(FwdArgs)]
         L.moe_layer_forward.argtypes = [ctypes.POINTER(FwdArgs), _vp, _sz, _vp]
+        L.moe_layer_forward_error_offset.restype = _sz
+        L.moe_layer_forward_error_offset.argtypes = [ctypes.POINTER(FwdArgs)]
         L.mx_quantize.argtypes = [_vp, _i, _i, _i, _vp, _vp, _i, _vp]
         L.moe_trace_begin.argtypes = [_i]
         L.moe_trace_end.argtypes = []
@@ -223,6 +225,12 @@ def fwd_args(*, score=SCORE_SOFTMAX, n_groups=1, topk_groups=1, renorm=True, rou
 
 def layer_forward_workspace_size(a: FwdArgs) -> int:
     return lib().moe_layer_forward_workspace_size(ctypes.byref(a))
+
+
+def layer_forward_error(a: FwdArgs, ws) -> int:
+    """The single launch's error word in `ws` (0: every wait completed).  Reads the device."""
+    off = lib().moe_layer_forward_error_offset(ctypes.byref(a))
+    return int(ws[off:off + 4].view(torch.int32).item())
 
 
 def moe_layer_forward(a: FwdArgs, ws, stream=None):

@@ -30,7 +30,7 @@
 //    block scans the per-expert tile counts in a wave and finds its tile.
 //  - The backward's independent dgrad/wgrad pairs share one launch each (bwd_down,
 //    bwd_gate_up), so that one fills the other's last partial round of tiles.
-#include <hip/hip_cooperative_groups.h>
+#include <algorithm>
 
 #include "pipe.h"
 #include "route_dev.h"
@@ -154,60 +154,76 @@ __device__ __forceinline__ int tile_total(const GemmArgs& g) {
     return uni(ragged_scan(g, n_tiles<EPI>(g), -1, nullptr, nullptr));
 }
 
-// One 256 x 256 output tile, number `logical` of the product (tiles run in launch order: the
-// blocks in flight at once, spread over all XCDs, work on neighbouring tiles whose operand
-// panels meet in the shared last-level cache, which measured faster than giving each XCD
-// its own compact block of tiles).
-template <int BK, bool A_K, bool B_K, int EPI, bool GK>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const int logical) {
-    typedef Pipe<BK> PP;
-    constexpr int KK = PP::KK, NST = PP::NST, OPB = PP::OPB, LPW = PP::LPW, LPS = PP::LPS;
-    constexpr bool SLOTS5 = (BK == 64) && MOE_GEMM_SLOTS5;
-    const int tid = threadIdx.x, lane = tid & 63, wid = uni(tid >> 6);
-    const int wm = wid >> 1, wn = wid & 1;
+// Where tile `logical` of a product sits: its expert, the expert's rows [row0, row0+Mrows)
+// (ragged-M products: from the device offsets), its M and N tile within the expert, and its
+// row block: the index of (expert, M tile) among the row blocks of all experts in order.
+struct TileAt {
+    int e, row0, Mrows, tm, tn, mblock;
+};
+
+template <int EPI, bool GK>
+__device__ __forceinline__ TileAt tile_at(const GemmArgs& g, const int logical) {
     const int NT = n_tiles<EPI>(g);
     const bool ragged_m = !GK && g.offsets != nullptr;
-    int e, t_local, Mrows, row0;
+    TileAt t;
+    int t_local, mbase;
     if (ragged_m) {
         int ee = 0, first = 0;
         ragged_scan(g, NT, logical, &ee, &first);
-        e = uni(ee);
+        t.e = uni(ee);
         t_local = uni(logical - first);
-        int a = min(max(g.offsets[e], 0), g.R);
-        int b = min(max(g.offsets[e + 1], a), g.R);
-        row0 = uni(a);
-        Mrows = uni(b - a);
+        mbase = uni(first / NT);
+        int a = min(max(g.offsets[t.e], 0), g.R);
+        int b = min(max(g.offsets[t.e + 1], a), g.R);
+        t.row0 = uni(a);
+        t.Mrows = uni(b - a);
     } else {
         int per = GK ? cdiv(g.M, BM) * NT : cdiv(g.R, BM) * NT;
-        e = logical / per;
-        t_local = logical - e * per;
+        t.e = logical / per;
+        t_local = logical - t.e * per;
+        mbase = GK ? 0 : t.e * cdiv(g.R, BM);
         if (GK) {
             if (g.offsets) {
                 // K extent: the expert's rows (of the first pass when P > 1)
                 const int lim = g.P > 1 ? g.pass_rows : g.R;
-                int a = min(max(g.offsets[e], 0), lim);
-                int b = min(max(g.offsets[e + 1], a), lim);
-                row0 = uni(a);
-                Mrows = uni(b - a);
+                int a = min(max(g.offsets[t.e], 0), lim);
+                int b = min(max(g.offsets[t.e + 1], a), lim);
+                t.row0 = uni(a);
+                t.Mrows = uni(b - a);
             } else {
-                row0 = 0;
-                Mrows = g.R;
+                t.row0 = 0;
+                t.Mrows = g.R;
             }
         } else {
-            row0 = 0;
-            Mrows = g.R;
+            t.row0 = 0;
+            t.Mrows = g.R;
         }
     }
-    const int MT = GK ? cdiv(g.M, BM) : cdiv(Mrows, BM);
-    int tm, tn;
+    const int MT = GK ? cdiv(g.M, BM) : cdiv(t.Mrows, BM);
     {
         int grp = t_local / (GM * NT);
         int first = grp * GM;
         int gsz = min(MT - first, GM);
         int rr = t_local - grp * GM * NT;
-        tm = first + rr % gsz;
-        tn = rr / gsz;
+        t.tm = first + rr % gsz;
+        t.tn = rr / gsz;
     }
+    t.mblock = mbase + t.tm;
+    return t;
+}
+
+// One 256 x 256 output tile, number `logical` of the product (tiles run in launch order: the
+// blocks in flight at once, spread over all XCDs, work on neighbouring tiles whose operand
+// panels meet in the shared last-level cache, which measured faster than giving each XCD
+// its own compact block of tiles).
+template <int BK, bool A_K, bool B_K, int EPI, bool GK>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const TileAt& at) {
+    typedef Pipe<BK> PP;
+    constexpr int KK = PP::KK, NST = PP::NST, OPB = PP::OPB, LPW = PP::LPW, LPS = PP::LPS;
+    constexpr bool SLOTS5 = (BK == 64) && MOE_GEMM_SLOTS5;
+    const int tid = threadIdx.x, lane = tid & 63, wid = uni(tid >> 6);
+    const int wm = wid >> 1, wn = wid & 1;
+    const int e = at.e, row0 = at.row0, Mrows = at.Mrows, tm = at.tm, tn = at.tn;
     const int m0 = tm * BM;
     const int Kdim = GK ? Mrows : g.K;
     const int Mvalid = GK ? g.M : Mrows;
@@ -589,7 +605,8 @@ constexpr int BK_FWD = 64, BK_DGRAD = 64, BK_WGRAD = 64;
     NAME(GemmArgs g) {                                                                 \
         __shared__ GemmSmem sm;                                                        \
         const int total = tile_total<EPI, GK>(g);                                      \
-        if ((int)blockIdx.x < total) gemm_tile<BK_FWD, AKM, BKM, EPI, GK>(g, sm, blockIdx.x);  \
+        if ((int)blockIdx.x < total)                                                    \
+            gemm_tile<BK_FWD, AKM, BKM, EPI, GK>(g, sm, tile_at<EPI, GK>(g, blockIdx.x));  \
     }
 MOE_GEMM_KERNEL(gemm1_swiglu, true, true, EPI_SWIGLU, false)     // [g|u] = Xp W1^T, h
 MOE_GEMM_KERNEL(gemm2_down, true, true, EPI_STORE, false)        // y = h W2^T
@@ -605,8 +622,10 @@ void bwd_down(GemmArgs gd, GemmArgs gw) {
     __shared__ GemmSmem sm;
     const int td = tile_total<EPI_DSWIGLU, false>(gd);
     const int b = blockIdx.x;
-    if (b < td) gemm_tile<BK_DGRAD, true, false, EPI_DSWIGLU, false>(gd, sm, b);
-    else if (b - td < gw.total) gemm_tile<BK_WGRAD, false, false, EPI_STORE, true>(gw, sm, b - td);
+    if (b < td)
+        gemm_tile<BK_DGRAD, true, false, EPI_DSWIGLU, false>(gd, sm, tile_at<EPI_DSWIGLU, false>(gd, b));
+    else if (b - td < gw.total)
+        gemm_tile<BK_WGRAD, false, false, EPI_STORE, true>(gw, sm, tile_at<EPI_STORE, true>(gw, b - td));
 }
 
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -614,8 +633,10 @@ void bwd_gate_up(GemmArgs gd, GemmArgs gw) {
     __shared__ GemmSmem sm;
     const int td = tile_total<EPI_STORE, false>(gd);
     const int b = blockIdx.x;
-    if (b < td) gemm_tile<BK_DGRAD, true, false, EPI_STORE, false>(gd, sm, b);
-    else if (b - td < gw.total) gemm_tile<BK_WGRAD, false, false, EPI_STORE, true>(gw, sm, b - td);
+    if (b < td)
+        gemm_tile<BK_DGRAD, true, false, EPI_STORE, false>(gd, sm, tile_at<EPI_STORE, false>(gd, b));
+    else if (b - td < gw.total)
+        gemm_tile<BK_WGRAD, false, false, EPI_STORE, true>(gw, sm, tile_at<EPI_STORE, true>(gw, b - td));
 }
 
 // Upper bound on the tile count of a ragged-M product (host side, no device data).
@@ -650,14 +671,25 @@ static int launch_pair(void (*kern)(GemmArgs, GemmArgs), const char* name, const
 }
 
 // ---------------------------------------------------------------- the layer in one launch
-// The forward of the layer -- top-k routing, the expert-contiguous permutation, dispatch,
-// GEMM1 + SwiGLU, GEMM2 and the combine -- as one persistent, cooperative kernel: one block
-// per CU walks each step's work items in turn and device-wide barriers separate the steps, so
-// the GPU runs the whole layer from one launch with no host in between (the single fused
-// MoE kernel of pulsen.vercel.app, "Cursor åpner megakernelen…", ¶3, and ki-pruefstand.de,
-// "Cursor veröffentlicht MoE-Megakernel…", "Kommunikation im Kernel" ¶2, on one GPU).  Every
-// step runs the same device code as its own kernel, so the outputs are bit-identical to the
-// step-by-step launches.  The 160 KB of LDS serve every step in turn.
+// The forward of the layer -- router projection, top-k routing, the expert-contiguous
+// permutation, dispatch, GEMM1 + SwiGLU, GEMM2 and the combine -- as one persistent,
+// cooperative kernel (the single fused MoE kernel of pulsen.vercel.app, "Cursor åpner
+// megakernelen…", ¶3, and ki-pruefstand.de, "Cursor veröffentlicht MoE-Megakernel…",
+// "Kommunikation im Kernel" ¶2, on one GPU): one block per CU.  The routing steps, the
+// dispatch and the combine are separated by device-wide barriers.  The two expert products
+// run as one queue of tiles that blocks claim in order -- GEMM1 tiles, then GEMM2 tiles --
+// where a GEMM2 tile waits only for the GEMM1 tiles of its own row block, through per-row-
+// block completion counters (a tile-level dependency in place of a barrier between the
+// products, the idea of the tile-level triggers aiexpert.news, "Megakernels are dead and
+// back", ¶2, describes for kernel launches), so the last, partial round of GEMM1 tiles fills
+// with GEMM2 tiles.  Every item runs the same device code as its own kernel, so the outputs
+// are bit-identical to the step-by-step launches.  Claiming in order makes the queue
+// deadlock-free: a tile only waits for tiles claimed before it, which run on blocks that are
+// resident (a cooperative launch) and never wait for later tiles.
+// Visibility across XCDs: each XCD has its own L2, so a finished GEMM1 tile writes its L2
+// back (device-scope release) before it counts itself done; a GEMM2 tile drops stale lines
+// (acquire) before reading.  GEMM2 tiles do not signal: a write-back per tile of the second
+// product measured more costly than the barrier before the combine.
 struct FusedFwd {
     const bf16_t* wr;         // router weights [E_router,H], or null: the logits are given
     float* proj;              // logits written by the projection (tp.logits), or null
@@ -674,60 +706,158 @@ struct FusedFwd {
     GemmArgs s1, s2;          // shared experts (total 0 when there are none)
     const bf16_t* ys;
     bf16_t* out;
+    unsigned* sy;             // synchronisation words (workspace, cleared before the launch)
+    int mbr;                  // row blocks reserved for the routed experts (upper bound)
+    int mbs;                  // row blocks per shared expert: cdiv(T, BM)
 };
 
 constexpr int FUSED_NV = 4;  // router experts per lane: E_router <= 256
+// synchronisation words (4-byte units): barrier count and generation, the queue's claim
+// counter and the error flag on their own 128-byte lines; then the per-row-block counters of
+// finished GEMM1 tiles
+constexpr int SY_COUNT = 0, SY_GEN = 32, SY_CLAIM = 64, SY_ERR = 96, SY_READY = 128;
+constexpr uint64_t SPIN_TICKS = 200000000ull;  // 2 s of the 100 MHz clock: wait limit
 
-// The tiles of one forward product step: the routed product's (ragged, counted on the device
-// from the offsets) then the shared experts' (fixed count), spread over the resident blocks.
-template <int EPI>
-__device__ __forceinline__ void fused_gemm_step(const GemmArgs& routed, const GemmArgs& shared,
-                                                GemmSmem& sm) {
-    const int t1 = tile_total<EPI, false>(routed), total = t1 + shared.total;
-    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-        const bool r = tile < t1;
-        gemm_tile<BK_FWD, true, true, EPI, false>(r ? routed : shared, sm, r ? tile : tile - t1);
-        __syncthreads();  // the next tile's loads overwrite the slots
+// Every thread's global stores are acknowledged (vmcnt(0)), so that after the block barrier
+// that follows, one thread's device-scope release covers the whole block's writes.
+__device__ __forceinline__ void stores_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ unsigned ld_relaxed(const unsigned* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Spins (one thread) until *p >= need.  Bounded: past SPIN_TICKS it raises the error flag and
+// returns, so that a broken invariant ends the kernel instead of hanging the GPU.
+__device__ __forceinline__ void spin_until(const unsigned* p, unsigned need, unsigned* sy) {
+    if (ld_relaxed(p) >= need) return;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (ld_relaxed(p) < need) {
+        if (ld_relaxed(sy + SY_ERR)) return;  // an earlier wait ran out: do not wait again
+        __builtin_amdgcn_s_sleep(1);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > SPIN_TICKS) {
+            __hip_atomic_fetch_or(sy + SY_ERR, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
     }
+}
+
+// Device-wide barrier: every block's writes before it are visible to every block after it.
+// The arriving block makes its writes visible at device scope (L2 write-back), counts itself
+// in, and the last one to arrive resets the count and advances the generation the others
+// wait on; each then drops stale cached lines (acquire).
+__device__ __forceinline__ void grid_barrier(unsigned* sy) {
+    stores_done();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned gen = ld_relaxed(sy + SY_GEN);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const unsigned old =
+            __hip_atomic_fetch_add(sy + SY_COUNT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == gridDim.x - 1) {
+            __hip_atomic_exchange(sy + SY_COUNT, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(sy + SY_GEN, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            while (ld_relaxed(sy + SY_GEN) == gen) {
+                if (ld_relaxed(sy + SY_ERR)) break;
+                __builtin_amdgcn_s_sleep(1);
+                if (__builtin_amdgcn_s_memrealtime() - t0 > SPIN_TICKS) {
+                    __hip_atomic_fetch_or(sy + SY_ERR, 2u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+}
+
+// Marks one more tile of row block `mb` done, after every thread's stores of the tile are
+// acknowledged and made visible device-wide (L2 write-back).
+__device__ __forceinline__ void tile_done(unsigned* ready, int mb) {
+    stores_done();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(ready + mb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+__global__ void fused_clear(unsigned* sy, int words) {
+    for (int i = threadIdx.x; i < words; i += blockDim.x) sy[i] = 0;
 }
 
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void layer_forward_fused(FusedFwd a) {
     __shared__ GemmSmem sm;
-    cooperative_groups::grid_group grid = cooperative_groups::this_grid();
     const int nb = gridDim.x, wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
     int* lds_i = reinterpret_cast<int*>(sm.st);
+    unsigned* const ready1 = a.sy + SY_READY;
+    const bool local = a.perm_ids != a.tp.idx;
     // 0. router projection (when the logits are not given): one thread per logit
     if (a.wr) {
         const int nl = a.tp.T * a.tp.E;
         for (int id = blockIdx.x * NTH + threadIdx.x; id < nl; id += nb * NTH)
             router_logit(a.x, a.wr, a.H, a.tp.E, id, a.proj);
-        grid.sync();
+        grid_barrier(a.sy);
     }
-    // 1. top-k and weights: one wave per token
+    // 1. top-k and weights: one wave per token; 2. chunk histograms of the expert ids: one
+    // block per chunk (in the same step when the ids are given, not selected)
     for (int t = blockIdx.x * 4 + wid; t < a.tp.T; t += nb * 4)
         topk_token<FUSED_NV>(a.tp, t, lane);
-    grid.sync();
-    // 2. chunk histograms of the expert ids: one block per chunk
+    if (!local) grid_barrier(a.sy);
     for (int c = blockIdx.x; c < a.nch; c += nb) count_chunk(a.perm_ids, a.n, a.E, a.blk, c, lds_i);
-    grid.sync();
+    grid_barrier(a.sy);
     // 3. counts, offsets and chunk bases: one block
     if (blockIdx.x == 0)
         scan_body(a.blk, a.nch, a.E, a.counts, a.offsets, lds_i, lds_i + SCAN_LDS);
-    grid.sync();
+    grid_barrier(a.sy);
     // 4. ranks: one wave per chunk, each with its own counters
     for (int c = blockIdx.x * 4 + wid; c < a.nch; c += nb * 4)
         rank_chunk(a.perm_ids, a.n, a.E, a.nbits, a.blk, a.pos, a.src, c, lds_i + wid * a.E);
-    grid.sync();
+    grid_barrier(a.sy);
     // 5. dispatch: one block per source token
     for (int t = blockIdx.x; t < a.T; t += nb) dispatch_token<NTH>(a.x, a.H, a.k, a.pos, a.R, a.xp, t, lds_i);
-    grid.sync();
-    // 6. GEMM1 + SwiGLU, 7. GEMM2
-    fused_gemm_step<EPI_SWIGLU>(a.g1, a.s1, sm);
-    grid.sync();
-    fused_gemm_step<EPI_STORE>(a.g2, a.s2, sm);
-    grid.sync();
-    // 8. combine: one block per token
+    grid_barrier(a.sy);
+    // 6. the queue: GEMM1 tiles (routed, shared), then GEMM2 tiles (routed, shared)
+    const int n1r = tile_total<EPI_SWIGLU, false>(a.g1), n1 = n1r + a.s1.total;
+    const int n2r = tile_total<EPI_STORE, false>(a.g2), total = n1 + n2r + a.s2.total;
+    const unsigned nt1 = (unsigned)n_tiles<EPI_SWIGLU>(a.g1);
+    const unsigned nt1s = a.S ? (unsigned)n_tiles<EPI_SWIGLU>(a.s1) : 0u;
+    int* const bcast = reinterpret_cast<int*>(sm.st + LDS_BYTES - 16);
+    int item = blockIdx.x;
+    while (item < total) {
+        int next = 0;
+        if (threadIdx.x == 0)
+            next = nb + (int)__hip_atomic_fetch_add(a.sy + SY_CLAIM, 1u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+        if (item < n1) {
+            const bool r = item < n1r;
+            const GemmArgs& g = r ? a.g1 : a.s1;
+            const TileAt at = tile_at<EPI_SWIGLU, false>(g, r ? item : item - n1r);
+            gemm_tile<BK_FWD, true, true, EPI_SWIGLU, false>(g, sm, at);
+            tile_done(ready1, r ? at.mblock : a.mbr + at.mblock);
+        } else {
+            const int i2 = item - n1;
+            const bool r = i2 < n2r;
+            const GemmArgs& g = r ? a.g2 : a.s2;
+            const TileAt at = tile_at<EPI_STORE, false>(g, r ? i2 : i2 - n2r);
+            if (threadIdx.x == 0) {
+                spin_until(ready1 + (r ? at.mblock : a.mbr + at.mblock), r ? nt1 : nt1s, a.sy);
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            }
+            __syncthreads();
+            gemm_tile<BK_FWD, true, true, EPI_STORE, false>(g, sm, at);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) *bcast = next;
+        __syncthreads();
+        item = *bcast;
+        __syncthreads();
+    }
+    grid_barrier(a.sy);
+    // 7. combine: one block per token
     for (int t = blockIdx.x; t < a.T; t += nb)
         combine_token<NTH>(a.g2.C, a.pos, a.tp.w, a.T, a.k, a.H, a.R, a.ys, a.S, a.out, t,
                            lds_i, reinterpret_cast<float*>(lds_i + MAXK));
@@ -774,9 +904,26 @@ int moe_ffn_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, 
     return launch(gemm2_down, "gemm2_down", g2, cdiv(H, BN), st);
 }
 
+// Synchronisation words of the single launch: the fixed words and the GEMM1 counter of every
+// row block (routed: an upper bound; shared: S * cdiv(T, BM)).
+static int64_t fused_sync_words(const moe_fwd_args& f, int64_t* mbr, int64_t* mbs) {
+    const int64_t R = (int64_t)f.T * f.k;
+    *mbr = (R + (int64_t)f.E * (BM - 1)) / BM;
+    *mbs = cdiv(f.T, BM);
+    return SY_READY + *mbr + (int64_t)f.S * *mbs;
+}
+
 extern "C" size_t moe_layer_forward_workspace_size(const moe_fwd_args* a) {
-    if (!a) return 0;
-    return moe_route_workspace_size(a->T, a->k, a->E);
+    if (!a || a->T < 1 || a->k < 1 || a->E < 1 || a->S < 0) return 0;
+    int64_t mbr, mbs;
+    const int64_t words = fused_sync_words(*a, &mbr, &mbs);
+    return moe_align256(moe_route_workspace_size(a->T, a->k, a->E)) +
+           moe_align256((size_t)words * 4);
+}
+
+extern "C" size_t moe_layer_forward_error_offset(const moe_fwd_args* a) {
+    if (!a || a->T < 1 || a->k < 1 || a->E < 1) return 0;
+    return moe_align256(moe_route_workspace_size(a->T, a->k, a->E)) + SY_ERR * 4;
 }
 
 extern "C" int moe_layer_forward(const moe_fwd_args* p, void* ws, size_t ws_bytes, void* stream) {
@@ -787,7 +934,7 @@ extern "C" int moe_layer_forward(const moe_fwd_args* p, void* ws, size_t ws_byte
     MOE_REQUIRE(f.E_router >= 1 && f.E_router <= 64 * FUSED_NV && f.k <= f.E_router);
     MOE_REQUIRE(f.idx_in || f.E == f.E_router);
     MOE_REQUIRE(f.H >= 64 && f.H % 64 == 0 && f.I >= 64 && f.I % 64 == 0);
-    MOE_REQUIRE(f.S >= 0 && (f.S == 0 || (f.Is >= 64 && f.Is % 64 == 0)));
+    MOE_REQUIRE(f.S >= 0 && f.S <= 64 && (f.S == 0 || (f.Is >= 64 && f.Is % 64 == 0)));
     const int64_t R = (int64_t)f.T * f.k;
     MOE_REQUIRE(R * f.H < (1ll << 31) && R * 2 * f.I < (1ll << 31));
     MOE_REQUIRE((int64_t)f.S * f.T * f.H < (1ll << 31) && (int64_t)f.S * f.T * 2 * f.Is < (1ll << 31));
@@ -839,8 +986,15 @@ extern "C" int moe_layer_forward(const moe_fwd_args* p, void* ws, size_t ws_byte
                  (const bf16_t*)f.ws2, (bf16_t*)f.gus, (bf16_t*)f.hs, (bf16_t*)f.ys, a.s1, a.s2);
     a.ys = (const bf16_t*)f.ys;
     a.out = (bf16_t*)f.out;
+    int64_t mbr, mbs;
+    const int64_t words = fused_sync_words(f, &mbr, &mbs);
+    a.sy = (unsigned*)((char*)ws + moe_align256(moe_route_workspace_size(f.T, f.k, f.E)));
+    a.mbr = (int)mbr;
+    a.mbs = (int)mbs;
     void* params[] = {&a};
     hipError_t err = hipSuccess;
+    MOE_TRACED("fused_clear", st, fused_clear<<<1, 1024, 0, st>>>(a.sy, (int)words));
+    MOE_LAUNCH_CHECK();
     MOE_TRACED("layer_forward_fused", st,
                err = hipLaunchCooperativeKernel((const void*)layer_forward_fused, dim3(ncu),
                                                 dim3(NTH), params, 0, st));

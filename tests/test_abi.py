@@ -165,7 +165,10 @@ def test_layer_forward_validation():
     assert fwd(ws=None) == moe.MOE_EWORKSPACE
     assert fwd(wsb=8) == moe.MOE_EWORKSPACE
     a = moe.fwd_args(T=2048, E=4, k=8, E_router=256)
-    assert moe.layer_forward_workspace_size(a) >= moe.route_workspace_size(2048, 8, 4)
+    need = moe.layer_forward_workspace_size(a)
+    assert need >= moe.route_workspace_size(2048, 8, 4)
+    off = lib().moe_layer_forward_error_offset(ctypes.byref(a))
+    assert off % 4 == 0 and off + 4 <= need
 
 
 def test_struct_layouts_match_the_header(tmp_path):

@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import mixture_experts_layer_39_amd as moe
 import oracle as orc
 import workloads as wk
 from gpu_harness import TOL_BF16, assert_close, bf, digest, host, oracle_params
@@ -58,6 +59,7 @@ def _pair(wl, backward=True):
 
 
 def _assert_identical(step, fused):
+    assert moe.layer_forward_error(fused.fused, fused.fused_ws) == 0
     a, b = _buffers(step), _buffers(fused)
     for name in a:
         if a[name] is None:
@@ -97,6 +99,7 @@ def test_fused_full_size_bit_identical(name):
     d0 = digest(fused.out, fused.y, fused.h)
     fused.forward_fused()
     torch.cuda.synchronize()
+    assert moe.layer_forward_error(fused.fused, fused.fused_ws) == 0
     assert digest(fused.out, fused.y, fused.h) == d0
 
 
