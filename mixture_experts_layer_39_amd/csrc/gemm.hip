@@ -711,7 +711,8 @@ struct FusedFwd {
     int mbs;                  // row blocks per shared expert: cdiv(T, BM)
 };
 
-constexpr int FUSED_NV = 4;  // router experts per lane: E_router <= 256
+constexpr int FUSED_NV = 4;      // router experts per lane: E_router <= 256
+constexpr int RG_WAVE = 4;       // 16-byte row chunks a lane sums per pass (combine)
 // synchronisation words (4-byte units): barrier count and generation, the queue's claim
 // counter and the error flag on their own 128-byte lines; then the per-row-block counters of
 // finished GEMM1 tiles
@@ -817,7 +818,8 @@ void layer_forward_fused(FusedFwd a) {
     for (int c = blockIdx.x * 4 + wid; c < a.nch; c += nb * 4)
         rank_chunk(a.perm_ids, a.n, a.E, a.nbits, a.blk, a.pos, a.src, c, lds_i + wid * a.E);
     grid_barrier(a.sy);
-    // 5. dispatch: one block per source token
+    // 5. dispatch: one block per source token (measured faster here than a wave per token
+    // for wide rows; the gather-reduce of the combine is the other way round)
     for (int t = blockIdx.x; t < a.T; t += nb) dispatch_token<NTH>(a.x, a.H, a.k, a.pos, a.R, a.xp, t, lds_i);
     grid_barrier(a.sy);
     // 6. the queue: GEMM1 tiles (routed, shared), then GEMM2 tiles (routed, shared)
@@ -857,10 +859,10 @@ void layer_forward_fused(FusedFwd a) {
         __syncthreads();
     }
     grid_barrier(a.sy);
-    // 7. combine: one block per token
-    for (int t = blockIdx.x; t < a.T; t += nb)
-        combine_token<NTH>(a.g2.C, a.pos, a.tp.w, a.T, a.k, a.H, a.R, a.ys, a.S, a.out, t,
-                           lds_i, reinterpret_cast<float*>(lds_i + MAXK));
+    // 7. combine: one wave per token
+    for (int t = blockIdx.x * 4 + wid; t < a.T; t += nb * 4)
+        combine_token_wave<RG_WAVE>(a.g2.C, a.pos, a.tp.w, a.T, a.k, a.H, a.R, a.ys, a.S, a.out,
+                                    t, lane);
 }
 
 static GemmArgs blank() {

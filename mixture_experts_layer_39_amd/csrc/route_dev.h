@@ -255,15 +255,26 @@ __device__ __forceinline__ void scan_body(int32_t* __restrict__ blk, int nchunks
     // per-expert running sums over the chunks (chunk c's entry becomes its chunk-local base)
     for (int e = threadIdx.x; e < E; e += nt) {
         int run = 0;
-        for (int c = 0; c < nchunks; ++c) {
-            if (staged) {
+        if (staged) {
+            for (int c = 0; c < nchunks; ++c) {
                 const int v = hs[c * E + e];
                 hs[c * E + e] = run;
                 run += v;
-            } else {
-                const int v = blk[(size_t)c * E + e];
-                blk[(size_t)c * E + e] = run;
-                run += v;
+            }
+        } else {
+            // 16 chunks' counts are loaded before any is rewritten (independent loads in
+            // flight instead of one load-store round trip per chunk)
+            for (int c0 = 0; c0 < nchunks; c0 += 16) {
+                int v[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    v[u] = c0 + u < nchunks ? blk[(size_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    if (c0 + u < nchunks) {
+                        blk[(size_t)(c0 + u) * E + e] = run;
+                        run += v[u];
+                    }
             }
         }
         counts[e] = run;
@@ -287,9 +298,8 @@ __device__ __forceinline__ void scan_body(int32_t* __restrict__ blk, int nchunks
     for (int e = threadIdx.x; e < E; e += nt) offsets[e] = exo[e];
     if (staged) {
         for (int i = threadIdx.x; i < (int)tot; i += nt) blk[i] = hs[i] + exo[i % E];
-    } else {
-        for (int e = threadIdx.x; e < E; e += nt)
-            for (int c = 0; c < nchunks; ++c) blk[(size_t)c * E + e] += exo[e];
+    } else {  // every entry independently: consecutive threads take consecutive entries
+        for (int64_t i = threadIdx.x; i < tot; i += nt) blk[i] += exo[i % E];
     }
     __syncthreads();  // hs / exo may be reused
 }

@@ -113,4 +113,76 @@ __device__ __forceinline__ void combine_token(const bf16_t* __restrict__ y,
     __syncthreads();  // sp, sw may be reused
 }
 
+// The combine of one token by one wave (no LDS, no block barrier), for a kernel that keeps one
+// block per CU: each wave of the block works on its own token, so that a CU has several
+// tokens' loads in flight.  Same results, bit for bit, as combine_token (same order per
+// element).  pos / w of slot j are held by lane j and broadcast with a lane read.
+template <int G>
+__device__ __forceinline__ void combine_token_wave(const bf16_t* __restrict__ y,
+                                                   const int32_t* __restrict__ pos,
+                                                   const float* __restrict__ w, int T, int k,
+                                                   int H, int R, const bf16_t* __restrict__ ys,
+                                                   int S, bf16_t* __restrict__ out, const int t,
+                                                   const int lane) {
+    int myp = -1;
+    float myw = 0.0f;
+    if (lane < k) {
+        const int p = pos[(size_t)t * k + lane];
+        myp = (p >= 0 && p < R) ? p : -1;
+        myw = w[(size_t)t * k + lane];
+    }
+    const int nc = H / 8;
+    for (int c0 = lane; c0 < nc; c0 += 64 * G) {
+        float acc[G][8];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            u32x4 v[G][8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int p = __shfl(myp, (j0 + u) & 63, 64);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int c = c0 + g * 64;
+                    v[g][u] = (j0 + u < k && p >= 0 && c < nc) ? ld16(y + (size_t)p * H + c * 8)
+                                                               : u32x4{0, 0, 0, 0};
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = j0 + u;
+                const int p = __shfl(myp, j & 63, 64);
+                const float wj = __shfl(myw, j & 63, 64);
+                if (j >= k || p < 0) continue;
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[g][2 * q] = __fadd_rn(acc[g][2 * q], __fmul_rn(wj, lo_bf(v[g][u][q])));
+                        acc[g][2 * q + 1] = __fadd_rn(acc[g][2 * q + 1], __fmul_rn(wj, hi_bf(v[g][u][q])));
+                    }
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int c = c0 + g * 64;
+            if (c >= nc) continue;
+            for (int s = 0; s < S; ++s) {
+                u32x4 v = ld16(ys + ((size_t)s * T + t) * H + c * 8);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[g][2 * q] = __fadd_rn(acc[g][2 * q], lo_bf(v[q]));
+                    acc[g][2 * q + 1] = __fadd_rn(acc[g][2 * q + 1], hi_bf(v[q]));
+                }
+            }
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[g][2 * q], acc[g][2 * q + 1]);
+            st16(out + (size_t)t * H + c * 8, o);
+        }
+    }
+}
+
 }  // namespace moe
