@@ -194,6 +194,50 @@ def ffn_bwd(xp, offsets, w1, w2, dy):
     return dxp, dw1, dw2
 
 
+def ffn_bwd_mx(xp, offsets, w1, w2, dy, gu, h):
+    """Backward of the routed FFN after an MXFP8 forward, with MXFP8 dgrad products.
+
+    The two dgrad products take MX-quantised operands along their contraction dimension
+    (E4M3 codes, one E8M0 scale per 32 values, the MOE_MX_FLOOR rule of mx_quantize):
+      dh   = Q_H(dy) . Q_H(W2_e)^T      (dy per row along H; W2_e [H,I] per column, along H)
+      dGU  = SwiGLU backward of dh at the saved g|u   (fp64)
+      dXp  = Q_2I(dGU) . Q_2I(W1_e)^T   (dGU per row along 2I; W1_e [2I,H] per column)
+    The weight gradients are plain fp64 sums over the expert's rows of the unquantised dy and
+    dGU against the forward's GEMM inputs (h and xp as the forward consumed them):
+      dW2_e = dy_e^T h_e,   dW1_e = dGU_e^T xp_e.
+    xp [R,H], dy [R,H], gu [R,2I], h [R,I] f64; w1 [E,2I,H], w2 [E,H,I] f64 (bf16 values).
+    Returns dxp [R,H], dgu [R,2I], dw1, dw2.
+    """
+    xp, dy, gu, h = (_c(xp, np.float64), _c(dy, np.float64), _c(gu, np.float64),
+                     _c(h, np.float64))
+    w1, w2 = _c(w1, np.float64), _c(w2, np.float64)
+    off = _c(offsets, np.int32)
+    E, I2, H = w1.shape
+    I = I2 // 2
+    R = xp.shape[0]
+    dyq = mx_dequantize(*mx_quantize(dy)) if R else dy
+    dxp = np.zeros((R, H))
+    dgu = np.zeros((R, 2 * I))
+    dw1 = np.zeros_like(w1)
+    dw2 = np.zeros_like(w2)
+    for e in range(E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        w2t = mx_dequantize(*mx_quantize(np.ascontiguousarray(w2[e].T)))   # [I,H], along H
+        w1t = mx_dequantize(*mx_quantize(np.ascontiguousarray(w1[e].T)))   # [H,2I], along 2I
+        dh = dyq[r0:r1] @ w2t.T
+        g, u = gu[r0:r1, :I], gu[r0:r1, I:]
+        sg = 1.0 / (1.0 + np.exp(-g))
+        dgu[r0:r1, :I] = dh * u * sg * (1.0 + g * (1.0 - sg))
+        dgu[r0:r1, I:] = dh * g * sg
+        dguq = mx_dequantize(*mx_quantize(dgu[r0:r1]))
+        dxp[r0:r1] = dguq @ w1t.T
+        dw2[e] = dy[r0:r1].T @ h[r0:r1]
+        dw1[e] = dgu[r0:r1].T @ xp[r0:r1]
+    return dxp, dgu, dw1, dw2
+
+
 def unpermute(dxp, pos, dxs=None):
     dxp, pos = _c(dxp, np.float64), _c(pos, np.int32)
     T, k = pos.shape
@@ -293,11 +337,15 @@ def layer_forward(p: dict) -> dict:
 
 
 def layer_backward(p: dict, r: dict, dout_bf16) -> dict:
-    """Whole BF16-storage backward in fp64 given the forward record `r`."""
+    """Whole backward in fp64 given the forward record `r`: BF16-storage products, or after
+    an MXFP8 forward (p["mx"]) MXFP8 dgrad products (ffn_bwd_mx)."""
     dout = bf16_to_f64(dout_bf16)
     w1, w2 = bf16_to_f64(p["w1"]), bf16_to_f64(p["w2"])
     dy, dw = combine_bwd(dout, r["y"], r["pos"], r["w"])
-    dxp, dw1, dw2 = ffn_bwd(r["xp"], r["offsets"], w1, w2, dy)
+    if p.get("mx", False):
+        dxp, _, dw1, dw2 = ffn_bwd_mx(r["xp"], r["offsets"], w1, w2, dy, r["gu"], r["h"])
+    else:
+        dxp, dw1, dw2 = ffn_bwd(r["xp"], r["offsets"], w1, w2, dy)
     g = {"dw_route": dw, "dw1": dw1, "dw2": dw2}
     dxs = None
     if p.get("ws1") is not None and p["ws1"].shape[0] > 0:

@@ -1,0 +1,83 @@
+"""Pins of the oracle's backward with MXFP8 dgrad products (ffn_bwd_mx), CPU only.
+
+What fixes it without re-running its own formula:
+- lossless operands: when dy is exactly MX-representable along H and W2 / W1 along their
+  contraction dimensions (pre-quantised), every quantisation before dGU is the identity, so
+  dGU and both weight gradients equal the BF16 oracle's (itself pinned by finite
+  differences), and dXp differs from it only by one E4M3 rounding of dGU;
+- power-of-two equivariance: MX quantisation along a dimension commutes with scaling a whole
+  line along that dimension by 2^s (the block scale moves, the codes do not).  Scaling a row
+  of dy, a column of W1 or a column of W2 must therefore scale the matching output lines by
+  exactly 2^s; a quantisation along the wrong dimension would mix differently scaled values
+  in one block and break the equality.
+"""
+import numpy as np
+
+RS = np.random.default_rng(7)
+
+
+def _case(E=3, H=64, I=64, counts=(40, 0, 37)):
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(off[-1])
+    xp = RS.normal(size=(R, H))
+    w1 = RS.normal(size=(E, 2 * I, H)) * 0.1
+    w2 = RS.normal(size=(E, H, I)) * 0.1
+    dy = RS.normal(size=(R, H))
+    gu = RS.normal(size=(R, 2 * I)) * 2
+    h = RS.normal(size=(R, I))
+    return off, xp, w1, w2, dy, gu, h
+
+
+def _pre_rows(orc, a):        # exactly MX-representable along the last dimension
+    return orc.mx_dequantize(*orc.mx_quantize(a))
+
+
+def _pre_cols(orc, w):        # [E, A, B]: exactly representable along A, per column
+    return np.stack([_pre_rows(orc, np.ascontiguousarray(m.T)).T for m in w])
+
+
+def test_lossless_operands_match_bf16_oracle(orc):
+    off, xp, w1, w2, dy, gu, h = _case()
+    dy = _pre_rows(orc, dy)
+    w2 = _pre_cols(orc, w2)
+    w1 = _pre_cols(orc, w1)
+    # the BF16 oracle differentiates the forward itself: give the MX backward the g|u and h
+    # of the same forward
+    y, gu_f, h_f = orc.ffn_fwd(xp, off, w1, w2, want_gu=True, want_h=True)
+    dxp_m, dgu_m, dw1_m, dw2_m = orc.ffn_bwd_mx(xp, off, w1, w2, dy, gu_f, h_f)
+    dxp_b, dw1_b, dw2_b = orc.ffn_bwd(xp, off, w1, w2, dy)
+    assert np.allclose(dw1_m, dw1_b, rtol=1e-10, atol=1e-10)
+    assert np.allclose(dw2_m, dw2_b, rtol=1e-10, atol=1e-10)
+    rel = np.linalg.norm(dxp_m - dxp_b) / np.linalg.norm(dxp_b)
+    assert 1e-6 < rel < 0.1          # one E4M3 rounding of dGU, and not exact
+    # an expert with no rows has zero weight gradients
+    assert not dw1_m[1].any() and not dw2_m[1].any()
+
+
+def test_dy_rows_equivariant(orc):
+    off, xp, w1, w2, dy, gu, h = _case()
+    s = RS.integers(-3, 4, size=dy.shape[0]).astype(np.float64)
+    a = orc.ffn_bwd_mx(xp, off, w1, w2, dy, gu, h)
+    b = orc.ffn_bwd_mx(xp, off, w1, w2, dy * 2.0 ** s[:, None], gu, h)
+    assert np.array_equal(b[0], a[0] * 2.0 ** s[:, None])      # dXp rows
+    assert np.array_equal(b[1], a[1] * 2.0 ** s[:, None])      # dGU rows
+
+
+def test_w1_columns_equivariant(orc):
+    off, xp, w1, w2, dy, gu, h = _case()
+    s = RS.integers(-3, 4, size=w1.shape[2]).astype(np.float64)
+    a = orc.ffn_bwd_mx(xp, off, w1, w2, dy, gu, h)
+    b = orc.ffn_bwd_mx(xp, off, w1 * 2.0 ** s[None, None, :], w2, dy, gu, h)
+    assert np.array_equal(b[0], a[0] * 2.0 ** s[None, :])      # dXp columns
+
+
+def test_w2_columns_equivariant(orc):
+    off, xp, w1, w2, dy, gu, h = _case()
+    s = RS.integers(-3, 4, size=w2.shape[2]).astype(np.float64)
+    a = orc.ffn_bwd_mx(xp, off, w1, w2, dy, gu, h)
+    b = orc.ffn_bwd_mx(xp, off, w1, w2 * 2.0 ** s[None, None, :], dy, gu, h)
+    I = w2.shape[2]
+    sc = np.concatenate([s, s])
+    assert np.array_equal(b[1], a[1] * 2.0 ** sc[None, :])     # dGU channels (gate and up)
+    assert np.array_equal(b[2], a[2] * 2.0 ** sc[None, :, None])  # dW1 rows
+    assert np.array_equal(b[3], a[3])                          # dW2 does not see W2
