@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 /* return codes */
 #define MOE_OK 0
@@ -143,9 +143,12 @@ int moe_dispatch(const void *x, int T, int H, int k, const int32_t *src, const i
  *   dtype = MOE_MXFP8: xp/w1/w2 are E4M3 codes with E8M0 scales per 32 values along their
  *            last (K) dimension: xp_scales [R,H/32], w1_scales [E,2I,H/32], w2_scales
  *            [E,H,I/32].  h is MX-quantised along I from fp32 before the down projection.
- *            gu_save and h_save must be NULL.
+ *            Optional saves for the backward: gu_save [R,2I] bf16 (the fp32 pre-activations,
+ *            rounded) and h_save [R,I] bf16 (h as the down projection consumes it: the
+ *            MX-quantised values, which bf16 holds exactly).  H % 128 == 0, I % 128 == 0.
  *   y [R,H] bf16 (routed rows, expert order).
- * Limits: H % 64 == 0, I % 64 == 0, offsets non-decreasing with offsets[E] <= R.
+ * Limits: H % 64 == 0, I % 64 == 0 (both % 128 for MOE_MXFP8), offsets non-decreasing with
+ * offsets[E] <= R.
  * Workspace: moe_ffn_workspace_size(). */
 size_t moe_ffn_workspace_size(int dtype, int E, int R, int H, int I, int shared);
 int moe_expert_ffn(int dtype, const void *xp, const uint8_t *xp_scales, const int32_t *offsets,
@@ -261,6 +264,20 @@ typedef struct moe_bwd_args {
      * [passes][E+1] and pos holds rows local to the token's pass.  Weight gradients reduce
      * over the rows of every pass, in pass order.  R must equal passes * pass_rows. */
     int passes, pass_tokens, pass_rows;
+    /* MXFP8 dgrad (mx != 0; after an MXFP8 forward, one pass, H % 128 == 0, I % 128 == 0):
+     * the two dgrad products of the routed experts take MX-quantised operands along their
+     * contraction dimension, dh = Q(dy) Q(W2_e^T)^T (with the SwiGLU backward) and
+     * dXp = Q(dGU) Q(W1_e^T)^T, on the scaled FP8 MFMA; dy and dGU are quantised on the fly
+     * (MOE_MX_FLOOR), the weights come quantised along the contraction dimension, as
+     * mx_quantize_t writes them.  The weight gradients stay BF16 products of the unquantised
+     * dy and dGU against xp and h, which must then hold what the MX forward's GEMMs consumed:
+     * the dequantised xp codes (mx_dequantize) and the h_save of moe_expert_ffn.  gu is the
+     * MX forward's gu_save. */
+    int mx;
+    const uint8_t *w2t_codes;   /* [E,I,H]  W2_e^T codes, scales [E,I,H/32] (along H) */
+    const uint8_t *w2t_scales;
+    const uint8_t *w1t_codes;   /* [E,H,2I] W1_e^T codes, scales [E,H,2I/32] (along 2I) */
+    const uint8_t *w1t_scales;
 } moe_bwd_args;
 
 size_t moe_backward_workspace_size(const moe_bwd_args *a);
@@ -275,6 +292,19 @@ int moe_backward(const moe_bwd_args *a, void *ws, size_t ws_bytes, void *stream)
  * K % 32 == 0. */
 int mx_quantize(const void *in, int in_dtype, int rows, int K, uint8_t *codes, uint8_t *scales,
                 int scale_mode, void *stream);
+
+/* mx_quantize_t: the same quantisation along the FIRST dimension of each [A,B] bf16 matrix of a
+ * batch, written transposed: codes [batch,B,A], scales [batch,B,A/32] (so that the codes of
+ * a column of the input are contiguous: the layout a product contracting over A reads).  For
+ * the MXFP8 backward: W2 [E,H,I] -> W2^T along H, W1 [E,2I,H] -> W1^T along 2I.
+ * A % 32 == 0, batch <= 65535.  Bit-exact. */
+int mx_quantize_t(const void *in, int batch, int A, int B, uint8_t *codes, uint8_t *scales,
+                  int scale_mode, void *stream);
+
+/* mx_dequantize: out [rows,K] bf16 = E4M3(code) * 2^(scale - 127), rounded to nearest even
+ * (exact for every value in bf16's normal range).  K % 32 == 0.  Bit-exact. */
+int mx_dequantize(const uint8_t *codes, const uint8_t *scales, int rows, int K, void *out,
+                  void *stream);
 
 /* ------------------------------------------------------------------ launch tracing
  * Optional timing of the library's own kernels, for profiling (the layer needs none of it).

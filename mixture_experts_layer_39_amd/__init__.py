@@ -44,7 +44,9 @@ class BwdArgs(ctypes.Structure):
                                    "s_sel", "logits", "w1", "w2", "gus", "hs", "ws1", "ws2",
                                    "dout", "dx", "dw1", "dw2", "dws1", "dws2", "dw_route",
                                    "dlogits")] + \
-               [(n, _i) for n in ("passes", "pass_tokens", "pass_rows")]
+               [(n, _i) for n in ("passes", "pass_tokens", "pass_rows", "mx")] + \
+               [(n, _vp) for n in ("w2t_codes", "w2t_scales", "w1t_codes", "w1t_scales")]
+
 
 class FwdArgs(ctypes.Structure):
     _fields_ = [(n, _i) for n in ("T", "H", "E", "k", "I", "S", "Is", "E_router")] + \
@@ -55,7 +57,7 @@ class FwdArgs(ctypes.Structure):
 
 
 _INT_FIELDS = ("T", "H", "E", "k", "I", "R", "S", "Is", "E_router", "score", "renorm", "passes",
-               "pass_tokens", "pass_rows")
+               "pass_tokens", "pass_rows", "mx")
 
 
 _lib = None
@@ -92,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward_error_offset.restype = _sz
         L.moe_layer_forward_error_offset.argtypes = [ctypes.POINTER(FwdArgs)]
         L.mx_quantize.argtypes = [_vp, _i, _i, _i, _vp, _vp, _i, _vp]
+        L.mx_quantize_t.argtypes = [_vp, _i, _i, _i, _vp, _vp, _i, _vp]
+        L.mx_dequantize.argtypes = [_vp, _vp, _i, _i, _vp, _vp]
         L.moe_trace_begin.argtypes = [_i]
         L.moe_trace_end.argtypes = []
         L.moe_trace_get.argtypes = [_i, ctypes.POINTER(ctypes.c_char_p),
@@ -204,6 +208,17 @@ def moe_backward(a: BwdArgs, ws, stream=None):
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     rc = lib().moe_backward(ctypes.byref(a), _p(ws), nbytes, _stream(stream))
     _check("moe_backward", rc)
+
+
+def mx_quantize_t(inp, batch, A, B, codes, scales, scale_mode=MX_FLOOR, stream=None):
+    rc = lib().mx_quantize_t(_p(inp), batch, A, B, _p(codes), _p(scales), scale_mode,
+                             _stream(stream))
+    _check("mx_quantize_t", rc)
+
+
+def mx_dequantize(codes, scales, rows, K, out, stream=None):
+    rc = lib().mx_dequantize(_p(codes), _p(scales), rows, K, _p(out), _stream(stream))
+    _check("mx_dequantize", rc)
 
 
 def fwd_args(*, score=SCORE_SOFTMAX, n_groups=1, topk_groups=1, renorm=True, route_scale=1.0,

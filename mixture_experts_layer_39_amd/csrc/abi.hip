@@ -18,7 +18,13 @@ int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int
 int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int E, int R, int H,
                int I, const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q,
                const uint8_t* w2s, float* hf, uint8_t* hq, uint8_t* hs, uint8_t* panels,
-               bf16_t* y, hipStream_t st);
+               bf16_t* gu_save, bf16_t* h_save, bf16_t* y, hipStream_t st);
+size_t moe_ffn_bwd_mx_bytes(int E, int R, int H, int I);
+int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uint8_t* w1tq,
+                   const uint8_t* w1ts, const uint8_t* w2tq, const uint8_t* w2ts,
+                   const bf16_t* gu, const bf16_t* dy, bf16_t* dgu, bf16_t* dxp, uint8_t* ws,
+                   hipStream_t st);
+int moe_ffn_wgrad_bf16(const MoeWgradSpan* wg, int E, int H, int I, hipStream_t st);
 size_t moe_mx_panel_bytes(int E, int R, int H, int I, bool shared);
 int moe_launch_combine_bwd(const bf16_t* dout, const bf16_t* y, const int32_t* pos, const float* w,
                            int T, int k, int H, int R, bf16_t* dy, float* dw, hipStream_t st);
@@ -140,7 +146,7 @@ extern "C" int moe_expert_ffn(int dtype, const void* xp, const uint8_t* xp_scale
     MOE_REQUIRE((int64_t)R * H < (1ll << 31) && (int64_t)R * 2 * I < (1ll << 31));
     MOE_REQUIRE(xp && w1 && w2 && y);
     if (dtype == MOE_MXFP8) {
-        MOE_REQUIRE(xp_scales && w1_scales && w2_scales && !gu_save && !h_save);
+        MOE_REQUIRE(xp_scales && w1_scales && w2_scales && H % 128 == 0 && I % 128 == 0);
     } else {
         MOE_REQUIRE(!xp_scales && !w1_scales && !w2_scales);
     }
@@ -166,14 +172,14 @@ extern "C" int moe_expert_ffn(int dtype, const void* xp, const uint8_t* xp_scale
     p += moe_align256(rows * (I / 32));
     uint8_t* panels = (uint8_t*)p;
     return moe_ffn_mx((const uint8_t*)xp, xp_scales, offsets, E, R, H, I, (const uint8_t*)w1,
-                      w1_scales, (const uint8_t*)w2, w2_scales, hf, hq, hs, panels, (bf16_t*)y,
-                      st);
+                      w1_scales, (const uint8_t*)w2, w2_scales, hf, hq, hs, panels,
+                      (bf16_t*)gu_save, (bf16_t*)h_save, (bf16_t*)y, st);
 }
 
 // ---------------------------------------------------------------------- backward
 namespace {
 struct BwdLayout {
-    size_t dy, dgu, dxp, dgus, dxs, total;
+    size_t dy, dgu, dxp, dgus, dxs, mx, total;
 };
 BwdLayout bwd_layout(const moe_bwd_args* a) {
     BwdLayout L;
@@ -183,6 +189,8 @@ BwdLayout bwd_layout(const moe_bwd_args* a) {
     L.dxp = o;  o += moe_align256((size_t)a->R * a->H * 2);
     L.dgus = o; o += moe_align256((size_t)a->S * a->T * 2 * a->Is * 2);
     L.dxs = o;  o += moe_align256((size_t)a->S * a->T * a->H * 2);
+    L.mx = o;
+    if (a->mx) o += moe_align256(moe_ffn_bwd_mx_bytes(a->E, a->R, a->H, a->I));
     L.total = o + 256;
     return L;
 }
@@ -209,6 +217,10 @@ extern "C" int moe_backward(const moe_bwd_args* a, void* ws, size_t ws_bytes, vo
         MOE_REQUIRE((int64_t)(passes - 1) * a->pass_tokens < a->T &&
                     a->T <= (int64_t)passes * a->pass_tokens);
         MOE_REQUIRE((int64_t)a->pass_tokens * a->k <= a->pass_rows);
+    }
+    if (a->mx) {  // MXFP8 dgrad products: one pass, K steps of 128 codes
+        MOE_REQUIRE(passes == 1 && a->H % 128 == 0 && a->I % 128 == 0);
+        MOE_REQUIRE(a->T == 0 || (a->w1t_codes && a->w1t_scales && a->w2t_codes && a->w2t_scales));
     }
     if (a->T > 0) {
         MOE_REQUIRE(a->xp && a->gu && a->h && a->y && a->offsets && a->pos && a->idx && a->w &&
@@ -256,7 +268,14 @@ extern "C" int moe_backward(const moe_bwd_args* a, void* ws, size_t ws_bytes, vo
                                     a->w + (size_t)t0 * k, Tp, k, H, prow, dy + r0 * H,
                                     a->dw_route + (size_t)t0 * k, st);
         if (rc) return rc;
-        if (prow > 0) {
+        if (prow > 0 && a->mx) {
+            rc = moe_ffn_bwd_mx(a->offsets, E, prow, H, I, a->w1t_codes, a->w1t_scales,
+                                a->w2t_codes, a->w2t_scales, (const bf16_t*)a->gu, dy, dgu, dxp,
+                                (uint8_t*)(base + L.mx), st);
+            if (rc) return rc;
+            rc = moe_ffn_wgrad_bf16(&wg, E, H, I, st);
+            if (rc) return rc;
+        } else if (prow > 0) {
             rc = moe_ffn_bwd_bf16((const bf16_t*)a->xp + r0 * H, a->offsets + (size_t)p * (E + 1),
                                   E, prow, H, I, (const bf16_t*)a->w1, (const bf16_t*)a->w2,
                                   (const bf16_t*)a->gu + r0 * 2 * I, (const bf16_t*)a->h + r0 * I,

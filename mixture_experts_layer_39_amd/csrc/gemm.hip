@@ -1015,6 +1015,36 @@ extern "C" int moe_layer_forward(const moe_fwd_args* p, void* ws, size_t ws_byte
 //   wgrad: when wg is given, dW2 = dy^T h and dW1 = dGU^T Xp over every pass it spans, in the
 //          same launches as the dgrad products (the caller passes it with the last pass, once
 //          dy and dGU of all passes exist).
+// The weight-gradient products over an expert's rows (of every pass): dW2_e = dy_e^T h_e
+// (M = H, N = I) and dW1_e = dGU_e^T Xp_e (M = 2I, N = H).
+static void wgrad_args(const MoeWgradSpan& wg, bool shared, int E, int H, int I, GemmArgs& gw,
+                       GemmArgs& gw2) {
+    gw = blank();
+    gw.A = wg.dy; gw.a_es = 0; gw.lda = H;
+    gw.B = wg.h; gw.b_es = shared ? (int64_t)wg.R * I : 0; gw.ldb = I;
+    gw.C = wg.dw2; gw.c_es = (int64_t)H * I; gw.ldc = I;
+    gw.offsets = wg.offsets; gw.E = E; gw.R = wg.R; gw.M = H; gw.N = I; gw.I = I;
+    gw.P = wg.P; gw.pass_rows = wg.pass_rows;
+    gw.total = E * cdiv(H, BM) * cdiv(I, BN);
+    gw2 = blank();
+    gw2.A = wg.dgu; gw2.a_es = shared ? (int64_t)wg.R * 2 * I : 0; gw2.lda = 2 * I;
+    gw2.B = wg.xp; gw2.b_es = 0; gw2.ldb = H;
+    gw2.C = wg.dw1; gw2.c_es = (int64_t)2 * I * H; gw2.ldc = H;
+    gw2.offsets = wg.offsets; gw2.E = E; gw2.R = wg.R; gw2.M = 2 * I; gw2.N = H; gw2.I = I;
+    gw2.P = wg.P; gw2.pass_rows = wg.pass_rows;
+    gw2.total = E * cdiv(2 * I, BM) * cdiv(H, BN);
+}
+
+// The two weight-gradient products alone (BF16), for the backward whose dgrad products run
+// in MXFP8: the launches of the BF16 backward with no dgrad tiles.
+int moe_ffn_wgrad_bf16(const MoeWgradSpan* wg, int E, int H, int I, hipStream_t st) {
+    GemmArgs none = blank(), gw, gw2;
+    wgrad_args(*wg, false, E, H, I, gw, gw2);
+    int rc = launch_pair(bwd_down, "wgrad_down", none, gw, st);
+    if (rc) return rc;
+    return launch_pair(bwd_gate_up, "wgrad_gate_up", none, gw2, st);
+}
+
 int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, int I,
                      const bf16_t* w1, const bf16_t* w2, const bf16_t* gu, const bf16_t* h,
                      const bf16_t* dy, bf16_t* dgu, bf16_t* dxp, const MoeWgradSpan* wg,
@@ -1030,16 +1060,8 @@ int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int
     gd.C2 = const_cast<bf16_t*>(gu); gd.c2_es = shared ? (int64_t)R * 2 * I : 0; gd.ldc2 = 2 * I;
     gd.offsets = offsets; gd.E = E; gd.R = R; gd.N = I; gd.K = H; gd.I = I;
     gd.total = shared ? E * cdiv(R, BM) * cdiv(I, BN) : 0;
-    // dW2_e = dy_e^T h_e: M = H, N = I, K = the expert's rows (of every pass)
-    GemmArgs gw = blank();
-    if (wg) {
-        gw.A = wg->dy; gw.a_es = 0; gw.lda = H;
-        gw.B = wg->h; gw.b_es = shared ? (int64_t)wg->R * I : 0; gw.ldb = I;
-        gw.C = wg->dw2; gw.c_es = (int64_t)H * I; gw.ldc = I;
-        gw.offsets = wg->offsets; gw.E = E; gw.R = wg->R; gw.M = H; gw.N = I; gw.I = I;
-        gw.P = wg->P; gw.pass_rows = wg->pass_rows;
-        gw.total = E * cdiv(H, BM) * cdiv(I, BN);
-    }
+    GemmArgs gw = blank(), gw2 = blank();
+    if (wg) wgrad_args(*wg, shared, E, H, I, gw, gw2);
     rc = launch_pair(bwd_down, "bwd_down", gd, gw, st);
     if (rc) return rc;
     // dXp = dGU_e W1_e (W1_e is [2I,H]: N-contiguous in H)
@@ -1049,16 +1071,6 @@ int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int
     gd2.C = dxp; gd2.c_es = shared ? (int64_t)R * H : 0; gd2.ldc = H;
     gd2.offsets = offsets; gd2.E = E; gd2.R = R; gd2.N = H; gd2.K = 2 * I; gd2.I = I;
     gd2.total = shared ? E * cdiv(R, BM) * cdiv(H, BN) : 0;
-    // dW1_e = dGU_e^T Xp_e: M = 2I, N = H
-    GemmArgs gw2 = blank();
-    if (wg) {
-        gw2.A = wg->dgu; gw2.a_es = shared ? (int64_t)wg->R * 2 * I : 0; gw2.lda = 2 * I;
-        gw2.B = wg->xp; gw2.b_es = 0; gw2.ldb = H;
-        gw2.C = wg->dw1; gw2.c_es = (int64_t)2 * I * H; gw2.ldc = H;
-        gw2.offsets = wg->offsets; gw2.E = E; gw2.R = wg->R; gw2.M = 2 * I; gw2.N = H; gw2.I = I;
-        gw2.P = wg->P; gw2.pass_rows = wg->pass_rows;
-        gw2.total = E * cdiv(2 * I, BM) * cdiv(H, BN);
-    }
     rc = launch_pair(bwd_gate_up, "bwd_gate_up", gd2, gw2, st);
     if (rc) return rc;
     return MOE_OK;

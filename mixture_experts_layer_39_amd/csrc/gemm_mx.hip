@@ -30,7 +30,7 @@ constexpr int XOPB = XP::OPB;            // bytes of one operand step (one slot)
 constexpr int XLPW = XP::LPW;            // direct loads per operand per wave per step
 constexpr int SPAN = 512;                // bytes of one panel's scales for one K step
 
-enum { XEPI_SWIGLU_F32 = 0, XEPI_STORE_BF16 = 1 };
+enum { XEPI_SWIGLU_F32 = 0, XEPI_STORE_BF16 = 1, XEPI_DSWIGLU = 2 };
 
 struct MxArgs {
     const uint8_t* A;    // codes [rows, K]
@@ -39,9 +39,13 @@ struct MxArgs {
     const uint8_t* B;    // codes [E, b_rows, K]
     const uint8_t* Bt;   // panel scales of B: [E][NT][2][K/128][512]
     int b_rows;
-    void* C;             // SwiGLU: fp32 h [rows, I];  store: bf16 y [rows, N]
+    void* C;             // SwiGLU: fp32 h [rows, I];  store: bf16 y [rows, N];
+                         // SwiGLU backward: bf16 dg|du [rows, 2I]
     int64_t c_es;        // per-expert row stride of C (shared mode), in rows
     int ldc;
+    bf16_t* C2;          // SwiGLU: bf16 g|u save [rows, 2I] or null;  SwiGLU backward: the
+                         // saved g|u (read)
+    int ldc2;
     const int32_t* offsets;
     int E, R, N, K, I;
     int total;           // tile count when static (shared mode)
@@ -226,6 +230,25 @@ __global__ __launch_bounds__(256) void mx_panel_scales_h(const uint8_t* __restri
     __shared__ uint8_t stg[256][PS_COLS + 4];
     __shared__ int srow[256];
     panel_a(blockIdx.x, sc, offsets, E, R, a_es, KB, nsteps, total_static, out, stg, srow);
+}
+
+// The panels of one product of the backward: x blocks [0, na) the A panels (ragged rows), then
+// E * N/256 B panels of a weight with plain rows; y blocks: 64-column chunks of the scales.
+__global__ __launch_bounds__(256) void mx_panel_scales_ab(const uint8_t* __restrict__ as,
+                                                          const int32_t* __restrict__ offsets,
+                                                          int E, int R, int na,
+                                                          const uint8_t* __restrict__ bs,
+                                                          int b_rows, int K,
+                                                          uint8_t* __restrict__ pa,
+                                                          uint8_t* __restrict__ pb) {
+    __shared__ uint8_t stg[256][PS_COLS + 4];
+    __shared__ int srow[256];
+    if ((int)blockIdx.y * PS_COLS >= K / 32) return;
+    const int bx = blockIdx.x;
+    if (bx < na)
+        panel_a(bx, as, offsets, E, R, 0, K / 32, K / XBK, 0, pa, stg, srow);
+    else
+        panel_b<XEPI_STORE_BF16>(bx - na, bs, b_rows, b_rows, 0, K / 32, K / XBK, pb, stg, srow);
 }
 
 // 8 bytes per lane straight to registers, issued through inline asm like the LDS loads so that
@@ -483,6 +506,49 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
                         hv[c] = gv / (1.0f + __expf(-gv)) * uv;
                     }
                     *reinterpret_cast<f32x4*>(C + (int64_t)row * g.ldc + ch) = hv;
+                    if (g.C2) {
+                        bf16_t* gr = g.C2 + ((int64_t)e * g.c_es + row0 + row) * g.ldc2;
+                        *reinterpret_cast<uint2*>(gr + ch) =
+                            make_uint2(pack_bf2(a[4 * hf], a[4 * hf + 1]),
+                                       pack_bf2(a[4 * hf + 2], a[4 * hf + 3]));
+                        *reinterpret_cast<uint2*>(gr + g.I + ch) =
+                            make_uint2(pack_bf2(a[8 + 4 * hf], a[8 + 4 * hf + 1]),
+                                       pack_bf2(a[8 + 4 * hf + 2], a[8 + 4 * hf + 3]));
+                    }
+                }
+        }
+    } else if (EPI == XEPI_DSWIGLU) {
+        // acc = dh at channels col .. col+3; the saved g|u of the row give dg|du
+        bf16_t* C = (bf16_t*)g.C + ((int64_t)e * g.c_es + row0) * g.ldc;
+        const bf16_t* GU = g.C2 + ((int64_t)e * g.c_es + row0) * g.ldc2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + wm * 128 + i * 32 + lrow;
+            if (row >= Mrows) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int ch = n0 + wn * 128 + j * 32 + 8 * q + lcol;
+                    if (ch >= g.N) continue;
+                    const uint2 gg = *reinterpret_cast<const uint2*>(GU + (int64_t)row * g.ldc2 + ch);
+                    const uint2 uu =
+                        *reinterpret_cast<const uint2*>(GU + (int64_t)row * g.ldc2 + g.I + ch);
+                    const float gv[4] = {lo_bf(gg.x), hi_bf(gg.x), lo_bf(gg.y), hi_bf(gg.y)};
+                    const float uv[4] = {lo_bf(uu.x), hi_bf(uu.x), lo_bf(uu.y), hi_bf(uu.y)};
+                    float dg[4], du[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float dh = acc[i][j][4 * q + c];
+                        const float sg = 1.0f / (1.0f + __expf(-gv[c]));
+                        dg[c] = dh * uv[c] * sg * (1.0f + gv[c] * (1.0f - sg));
+                        du[c] = dh * gv[c] * sg;
+                    }
+                    bf16_t* cr = C + (int64_t)row * g.ldc;
+                    *reinterpret_cast<uint2*>(cr + ch) =
+                        make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
+                    *reinterpret_cast<uint2*>(cr + g.I + ch) =
+                        make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
                 }
         }
     } else {
@@ -517,6 +583,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
     }
 MOE_MX_KERNEL(mx_gemm1_swiglu, XEPI_SWIGLU_F32)
 MOE_MX_KERNEL(mx_gemm2_down, XEPI_STORE_BF16)
+MOE_MX_KERNEL(mx_bwd_down, XEPI_DSWIGLU)
 #undef MOE_MX_KERNEL
 
 // Upper bound on the 256-row M tiles of an operand (host side, no device data).
@@ -526,14 +593,16 @@ static int mx_mtiles_bound(int R, int E, bool shared) {
 }
 
 template <int EPI>
-static int mx_launch(const MxArgs& g, hipStream_t st) {
+static int mx_launch(const MxArgs& g, hipStream_t st, const char* name = nullptr) {
     const int NT = mx_n_tiles<EPI>(g.N, g.I);
     const int grid = g.offsets ? mx_mtiles_bound(g.R, g.E, false) * NT : g.total;
     if (grid <= 0) return MOE_OK;
     if (EPI == XEPI_SWIGLU_F32)
         MOE_TRACED("mx_gemm1_swiglu", st, mx_gemm1_swiglu<<<grid, XNTH, 0, st>>>(g));
+    else if (EPI == XEPI_DSWIGLU)
+        MOE_TRACED("mx_bwd_down", st, mx_bwd_down<<<grid, XNTH, 0, st>>>(g));
     else
-        MOE_TRACED("mx_gemm2_down", st, mx_gemm2_down<<<grid, XNTH, 0, st>>>(g));
+        MOE_TRACED(name ? name : "mx_gemm2_down", st, mx_gemm2_down<<<grid, XNTH, 0, st>>>(g));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -582,10 +651,18 @@ size_t moe_mx_panel_bytes(int E, int R, int H, int I, bool shared) {
            mx_panel_b_bytes<XEPI_STORE_BF16>(E, H, I, I);
 }
 
+int moe_launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K,
+                             bf16_t* out, hipStream_t st);
+int moe_launch_mx_quantize_bf16(const bf16_t* in, int64_t rows, int K, uint8_t* codes,
+                                uint8_t* scales, const char* name, hipStream_t st);
+
+// gu_save [rows, 2I] bf16 (the fp32 pre-activations, rounded) and h_save [rows, I] bf16 (h as
+// GEMM2 consumes it: the MX-quantised values, exact in bf16) are optional saves for the
+// backward.
 int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int E, int R, int H,
                int I, const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q,
                const uint8_t* w2s, float* hf, uint8_t* hq, uint8_t* hs, uint8_t* panels,
-               bf16_t* y, hipStream_t st) {
+               bf16_t* gu_save, bf16_t* h_save, bf16_t* y, hipStream_t st) {
     // K steps of 128 codes: H and I multiples of 128
     if (H % XBK || I % XBK) return MOE_EINVAL;
     const bool shared = offsets == nullptr;
@@ -601,6 +678,7 @@ int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int
     g.A = xq; g.At = pa1; g.a_es = 0;
     g.B = w1q; g.Bt = pb1; g.b_rows = 2 * I;
     g.C = hf; g.c_es = shared ? R : 0; g.ldc = I;
+    g.C2 = gu_save; g.ldc2 = 2 * I;
     g.offsets = offsets; g.E = E; g.R = R; g.N = 2 * I; g.K = H; g.I = I;
     g.total = shared ? E * cdiv(R, XBM) * cdiv(I, 128) : 0;
     rc = mx_launch<XEPI_SWIGLU_F32>(g, st);
@@ -608,6 +686,10 @@ int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int
     int64_t rows = shared ? (int64_t)E * R : R;
     rc = moe_launch_mx_quantize_f32(hf, rows, I, hq, hs, st);
     if (rc) return rc;
+    if (h_save) {
+        rc = moe_launch_mx_dequantize(hq, hs, rows, I, h_save, st);
+        if (rc) return rc;
+    }
     rc = mx_panels_h(hs, offsets, E, R, shared ? R : 0, I, pa2, st);
     if (rc) return rc;
     MxArgs g2{};
@@ -617,4 +699,71 @@ int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int
     g2.offsets = offsets; g2.E = E; g2.R = R; g2.N = H; g2.K = I; g2.I = I;
     g2.total = shared ? E * cdiv(R, XBM) * cdiv(H, XBN) : 0;
     return mx_launch<XEPI_STORE_BF16>(g2, st);
+}
+
+// ---------------------------------------------------------------- backward, MXFP8 dgrad
+// Workspace of moe_ffn_bwd_mx: MX codes and scales of dy [R,H] and dGU [R,2I], and the panel
+// scales of both products' operands.
+size_t moe_ffn_bwd_mx_bytes(int E, int R, int H, int I) {
+    return moe_align256((size_t)R * H) + moe_align256((size_t)R * H / 32) +
+           moe_align256((size_t)R * 2 * I) + moe_align256((size_t)R * 2 * I / 32) +
+           mx_panel_a_bytes(E, R, H, false) + mx_panel_a_bytes(E, R, 2 * I, false) +
+           mx_panel_b_bytes<XEPI_STORE_BF16>(E, I, I, H) +
+           mx_panel_b_bytes<XEPI_STORE_BF16>(E, H, I, 2 * I);
+}
+
+static int mx_panels_ab(const uint8_t* as, const int32_t* offsets, int E, int R,
+                        const uint8_t* bs, int b_rows, int K, uint8_t* pa, uint8_t* pb,
+                        hipStream_t st) {
+    const int na = mx_mtiles_bound(R, E, false);
+    const dim3 grid(na + E * cdiv(b_rows, XBN), cdiv(K / 32, PS_COLS));
+    MOE_TRACED("mx_panel_scales", st,
+               mx_panel_scales_ab<<<grid, 256, 0, st>>>(as, offsets, E, R, na, bs, b_rows, K, pa,
+                                                        pb));
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+// The dgrad products of the routed experts' backward in MXFP8, each operand MX-quantised along
+// the product's contraction dimension:
+//   dh = Q(dy) Q(W2_e^T)^T with the SwiGLU backward in the epilogue -> dgu [R,2I] bf16,
+//   dXp = Q(dGU) Q(W1_e^T)^T -> dxp [R,H] bf16.
+// w2t: W2_e^T codes [E][I][H] and scales [E][I][H/32] (along H); w1t: W1_e^T codes [E][H][2I]
+// and scales [E][H][2I/32] (along 2I) -- mx_quantize_t of the weights.  gu: the forward's g|u.
+int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uint8_t* w1tq,
+                   const uint8_t* w1ts, const uint8_t* w2tq, const uint8_t* w2ts,
+                   const bf16_t* gu, const bf16_t* dy, bf16_t* dgu, bf16_t* dxp, uint8_t* ws,
+                   hipStream_t st) {
+    if (H % XBK || I % XBK) return MOE_EINVAL;
+    if (R == 0) return MOE_OK;
+    uint8_t* dyq = ws;
+    uint8_t* dys = dyq + moe_align256((size_t)R * H);
+    uint8_t* gq = dys + moe_align256((size_t)R * H / 32);
+    uint8_t* gs = gq + moe_align256((size_t)R * 2 * I);
+    uint8_t* pa1 = gs + moe_align256((size_t)R * 2 * I / 32);
+    uint8_t* pa2 = pa1 + mx_panel_a_bytes(E, R, H, false);
+    uint8_t* pb1 = pa2 + mx_panel_a_bytes(E, R, 2 * I, false);
+    uint8_t* pb2 = pb1 + mx_panel_b_bytes<XEPI_STORE_BF16>(E, I, I, H);
+    int rc = moe_launch_mx_quantize_bf16(dy, R, H, dyq, dys, "mx_quantize_dy", st);
+    if (rc) return rc;
+    rc = mx_panels_ab(dys, offsets, E, R, w2ts, I, H, pa1, pb1, st);
+    if (rc) return rc;
+    MxArgs g{};
+    g.A = dyq; g.At = pa1; g.a_es = 0;
+    g.B = w2tq; g.Bt = pb1; g.b_rows = I;
+    g.C = dgu; g.c_es = 0; g.ldc = 2 * I;
+    g.C2 = const_cast<bf16_t*>(gu); g.ldc2 = 2 * I;
+    g.offsets = offsets; g.E = E; g.R = R; g.N = I; g.K = H; g.I = I;
+    rc = mx_launch<XEPI_DSWIGLU>(g, st);
+    if (rc) return rc;
+    rc = moe_launch_mx_quantize_bf16(dgu, R, 2 * I, gq, gs, "mx_quantize_dgu", st);
+    if (rc) return rc;
+    rc = mx_panels_ab(gs, offsets, E, R, w1ts, H, 2 * I, pa2, pb2, st);
+    if (rc) return rc;
+    MxArgs g2{};
+    g2.A = gq; g2.At = pa2; g2.a_es = 0;
+    g2.B = w1tq; g2.Bt = pb2; g2.b_rows = H;
+    g2.C = dxp; g2.c_es = 0; g2.ldc = H;
+    g2.offsets = offsets; g2.E = E; g2.R = R; g2.N = H; g2.K = 2 * I; g2.I = I;
+    return mx_launch<XEPI_STORE_BF16>(g2, st, "mx_bwd_gate_up");
 }

@@ -491,6 +491,103 @@ extern "C" int mx_quantize(const void* in, int in_dtype, int rows, int K, uint8_
     return MOE_OK;
 }
 
+// ------------------------------------------------------------------ mx_quantize_t
+// Quantisation along the first dimension of each [A, B] matrix of a batch, written transposed:
+// codes [batch][B][A], scales [batch][B][A/32].  One thread per (column, 32-row block): it
+// reads its column's 32 values (consecutive threads read consecutive columns, so every row
+// access is coalesced) and writes the block's 32 codes as two 16-byte stores.
+__global__ __launch_bounds__(256) void mx_quantize_t_kernel(const bf16_t* __restrict__ in, int A,
+                                                            int B, int mode,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+    const int col = blockIdx.x * blockDim.x + threadIdx.x;
+    const int ab = blockIdx.y;            // 32-row block
+    const int64_t m = blockIdx.z;         // matrix of the batch
+    if (col >= B) return;
+    const bf16_t* p = in + (m * A + (int64_t)ab * 32) * B + col;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = __uint_as_float((uint32_t)p[(int64_t)i * B] << 16);
+    uint32_t q[8];
+    const int sc = mx_block(v, mode, q);
+    uint8_t* out = codes + (m * B + col) * A + ab * 32;
+    st16(out, u32x4{q[0], q[1], q[2], q[3]});
+    st16(out + 16, u32x4{q[4], q[5], q[6], q[7]});
+    scales[(m * B + col) * (A / 32) + ab] = (uint8_t)sc;
+}
+
+// ------------------------------------------------------------------ mx_dequantize
+// One thread per 32-value block: value = E4M3(code) * 2^(scale - 127), rounded to bf16
+// (exact for every normal bf16 value: a code has 3 mantissa bits).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    float v;
+    if (e == 15u && m == 7u) v = __uint_as_float(0x7FC00000u);        // NaN
+    else if (e == 0u) v = (float)m * (1.0f / 512.0f);                // subnormal: m 2^-9
+    else v = __uint_as_float(((e + 120u) << 23) | (m << 20));        // 2^(e-7) (1 + m/8)
+    return (c & 0x80u) ? -v : v;
+}
+
+__global__ __launch_bounds__(256) void mx_dequantize_kernel(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            int64_t nblocks,
+                                                            bf16_t* __restrict__ out) {
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nblocks) return;
+    const float f = ldexpf(1.0f, (int)scales[b] - 127);
+    const u32x4 c0 = ld16(codes + b * 32), c1 = ld16(codes + b * 32 + 16);
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t word = i < 4 ? c0[i] : c1[i - 4];
+        const float a = e4m3_value(word & 0xFFu) * f, b2 = e4m3_value((word >> 8) & 0xFFu) * f;
+        const float c = e4m3_value((word >> 16) & 0xFFu) * f, d = e4m3_value(word >> 24) * f;
+        w[2 * i] = pack_bf2(a, b2);
+        w[2 * i + 1] = pack_bf2(c, d);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        st16(out + b * 32 + 8 * i, u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]});
+}
+
+extern "C" int mx_quantize_t(const void* in, int batch, int A, int B, uint8_t* codes,
+                             uint8_t* scales, int scale_mode, void* stream) {
+    MOE_REQUIRE(batch >= 0 && A >= 32 && A % 32 == 0 && B >= 1 && batch <= 65535);
+    MOE_REQUIRE(scale_mode == MOE_MX_FLOOR || scale_mode == MOE_MX_CEIL);
+    MOE_REQUIRE(batch == 0 || (in && codes && scales));
+    if (batch == 0) return MOE_OK;
+    int rc = moe_check_device();
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const dim3 grid((unsigned)((B + 255) / 256), (unsigned)(A / 32), (unsigned)batch);
+    MOE_TRACED("mx_quantize_t", st,
+               mx_quantize_t_kernel<<<grid, 256, 0, st>>>((const bf16_t*)in, A, B, scale_mode,
+                                                          codes, scales));
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+int moe_launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K,
+                             bf16_t* out, hipStream_t st) {
+    const int64_t nb = rows * (K / 32);
+    if (nb == 0) return MOE_OK;
+    MOE_TRACED("mx_dequantize", st,
+               mx_dequantize_kernel<<<(unsigned)((nb + 255) / 256), 256, 0, st>>>(codes, scales,
+                                                                                  nb, out));
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+extern "C" int mx_dequantize(const uint8_t* codes, const uint8_t* scales, int rows, int K,
+                             void* out, void* stream) {
+    MOE_REQUIRE(rows >= 0 && K >= 32 && K % 32 == 0);
+    MOE_REQUIRE(rows == 0 || (codes && scales && out));
+    if (rows == 0) return MOE_OK;
+    int rc = moe_check_device();
+    if (rc) return rc;
+    return moe_launch_mx_dequantize(codes, scales, rows, K, (bf16_t*)out, (hipStream_t)stream);
+}
+
 // Internal launchers used by the backward orchestration.
 int moe_launch_combine_bwd(const bf16_t* dout, const bf16_t* y, const int32_t* pos, const float* w,
                            int T, int k, int H, int R, bf16_t* dy, float* dw, hipStream_t st) {
@@ -518,6 +615,17 @@ int moe_launch_router_bwd(const int32_t* idx, const float* w, const float* s_sel
     MOE_TRACED("router_bwd", st,
                router_bwd_kernel<<<(T + 3) / 4, 256, 0, st>>>(idx, w, s_sel, dw, logits, T, E, k,
                                                               score, renorm, c, dL));
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+int moe_launch_mx_quantize_bf16(const bf16_t* in, int64_t rows, int K, uint8_t* codes,
+                                uint8_t* scales, const char* name, hipStream_t st) {
+    int64_t nb = rows * (K / 32);
+    if (nb == 0) return MOE_OK;
+    MOE_TRACED(name, st,
+               mx_quantize_kernel<false><<<(unsigned)((nb + 255) / 256), 256, 0, st>>>(
+                   in, nb, MOE_MX_FLOOR, codes, scales));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

@@ -23,7 +23,8 @@ import torch
 from . import (BF16, MXFP8, F32, SCORE_SIGMOID, backward_workspace_size, bwd_args,
                ffn_workspace_size, fwd_args, layer_forward_workspace_size, moe_backward,
                moe_combine, moe_dispatch, moe_expert_ffn, moe_layer_forward, moe_route,
-               moe_update_bias, mx_quantize, route_workspace_size)
+               moe_update_bias, mx_dequantize, mx_quantize, mx_quantize_t,
+               route_workspace_size)
 
 
 @dataclasses.dataclass
@@ -134,9 +135,20 @@ class MoELayer:
             self.w1s = _e(tuple(inp["w1"].shape[:-1]) + (H // 32,), torch.uint8, d)
             self.w2q = _e(tuple(inp["w2"].shape), torch.uint8, d)
             self.w2s = _e(tuple(inp["w2"].shape[:-1]) + (I // 32,), torch.uint8, d)
-            self.quantize_weights()
-            self.xp = None
-            self.gu = self.h = None
+            if backward:
+                # MXFP8 dgrad: the weights quantised along the dgrad contraction dimension;
+                # the saves hold what the forward's GEMMs consumed
+                self.w2tq = _e((E, I, H), torch.uint8, d)
+                self.w2ts = _e((E, I, H // 32), torch.uint8, d)
+                self.w1tq = _e((E, H, 2 * I), torch.uint8, d)
+                self.w1ts = _e((E, H, 2 * I // 32), torch.uint8, d)
+                self.xp = _e((R, H), bf, d)
+                self.gu = _e((R, 2 * I), bf, d)
+                self.h = _e((R, I), bf, d)
+            else:
+                self.xp = None
+                self.gu = self.h = None
+            self.quantize_weights(backward)
         else:
             self.xp = _e((R, H), bf, d)
             self.gu = _e((R, 2 * I), bf, d) if backward else None
@@ -166,11 +178,14 @@ class MoELayer:
             self.bwd_ws = _e((max(backward_workspace_size(self.bargs), 256),), torch.uint8, d)
 
     # ------------------------------------------------------------------ setup
-    def quantize_weights(self):
+    def quantize_weights(self, backward=False):
         c, inp = self.cfg, self.inp
         E, H, I = c.E, c.H, c.I
         mx_quantize(inp["w1"], BF16, E * 2 * I, H, self.w1q, self.w1s)
         mx_quantize(inp["w2"], BF16, E * H, I, self.w2q, self.w2s)
+        if backward:
+            mx_quantize_t(inp["w2"], E, H, I, self.w2tq, self.w2ts)
+            mx_quantize_t(inp["w1"], E, 2 * I, H, self.w1tq, self.w1ts)
 
     def _bwd_args(self):
         c, inp = self.cfg, self.inp
@@ -185,7 +200,9 @@ class MoELayer:
                         hs=self.hs if c.S else None, ws1=inp.get("ws1"), ws2=inp.get("ws2"),
                         dout=inp.get("dout"), dx=self.dx, dw1=self.dw1, dw2=self.dw2,
                         dws1=self.dws1, dws2=self.dws2, dw_route=self.dw_route,
-                        dlogits=self.dlogits)
+                        dlogits=self.dlogits,
+                        **(dict(mx=1, w2t_codes=self.w2tq, w2t_scales=self.w2ts,
+                                w1t_codes=self.w1tq, w1t_scales=self.w1ts) if c.mx else {}))
 
     # ------------------------------------------------------------------ steps
     def route(self):
@@ -214,6 +231,8 @@ class MoELayer:
         if c.mx:
             moe_dispatch(self.inp["x"], c.T, c.H, self.kr, self.src, self.R, None, self.xq,
                          self.xs, pos=self.pos)
+            if self.xp is not None:  # GEMM1's input as the weight gradient dW1 needs it
+                mx_dequantize(self.xq, self.xs, self.R, c.H, self.xp)
         else:
             moe_dispatch(self.inp["x"], c.T, c.H, self.kr, self.src, self.R, self.xp,
                          pos=self.pos)
@@ -223,7 +242,7 @@ class MoELayer:
         if c.mx:
             moe_expert_ffn(MXFP8, self.xq, self.offsets, c.E, self.R, c.H, c.I, self.w1q,
                            self.w2q, self.y, xp_scales=self.xs, w1_scales=self.w1s,
-                           w2_scales=self.w2s, ws=self.ffn_ws)
+                           w2_scales=self.w2s, gu_save=self.gu, h_save=self.h, ws=self.ffn_ws)
         else:
             moe_expert_ffn(BF16, self.xp, self.offsets, c.E, self.R, c.H, c.I, inp["w1"],
                            inp["w2"], self.y, gu_save=self.gu, h_save=self.h, ws=self.ffn_ws)

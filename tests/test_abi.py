@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert moe.abi_version() == 4
+    assert moe.abi_version() == 5
     assert moe.strerror(0) == "ok"
     assert "workspace" in moe.strerror(-2)
     assert moe.strerror(12345) == "unknown error"
@@ -92,6 +92,13 @@ def test_dispatch_combine_mx_validation():
     assert L_.mx_quantize(FAKE, moe.BF16, 4, 48, FAKE, FAKE, 0, None) == moe.MOE_EINVAL
     assert L_.mx_quantize(FAKE, 9, 4, 64, FAKE, FAKE, 0, None) == moe.MOE_EINVAL
     assert L_.mx_quantize(FAKE, moe.BF16, 4, 64, FAKE, FAKE, 5, None) == moe.MOE_EINVAL
+    assert L_.mx_quantize_t(FAKE, 2, 48, 8, FAKE, FAKE, 0, None) == moe.MOE_EINVAL   # A % 32
+    assert L_.mx_quantize_t(FAKE, 2, 64, 0, FAKE, FAKE, 0, None) == moe.MOE_EINVAL
+    assert L_.mx_quantize_t(None, 2, 64, 8, FAKE, FAKE, 0, None) == moe.MOE_EINVAL
+    assert L_.mx_quantize_t(FAKE, 0, 64, 8, FAKE, FAKE, 0, None) == moe.MOE_OK       # empty
+    assert L_.mx_dequantize(FAKE, FAKE, 4, 40, FAKE, None) == moe.MOE_EINVAL
+    assert L_.mx_dequantize(FAKE, None, 4, 64, FAKE, None) == moe.MOE_EINVAL
+    assert L_.mx_dequantize(FAKE, FAKE, 0, 64, FAKE, None) == moe.MOE_OK
 
 
 def ffn(**kw):
@@ -111,7 +118,7 @@ def test_ffn_validation():
     assert ffn(dtype=7) == moe.MOE_EINVAL
     assert ffn(xs=FAKE) == moe.MOE_EINVAL                                   # scales in BF16
     assert ffn(dtype=moe.MXFP8) == moe.MOE_EINVAL                           # no scales
-    assert ffn(dtype=moe.MXFP8, xs=FAKE, w1s=FAKE, w2s=FAKE, gu=FAKE) == moe.MOE_EINVAL
+    assert ffn(dtype=moe.MXFP8, xs=FAKE, w1s=FAKE, w2s=FAKE, H=192) == moe.MOE_EINVAL  # H % 128
     assert ffn(h=None, ws=None) == moe.MOE_EWORKSPACE
     assert ffn(h=None, wsb=100) == moe.MOE_EWORKSPACE
     assert ffn(R=0) == moe.MOE_OK
@@ -131,6 +138,17 @@ def test_backward_validation():
     assert lib().moe_backward(ctypes.byref(b), FAKE, 1 << 20, None) == moe.MOE_OK
     c = moe.bwd_args(T=16, H=100, E=4, k=2, I=128, R=32, E_router=4)
     assert lib().moe_backward(ctypes.byref(c), FAKE, 1 << 30, None) == moe.MOE_EINVAL
+    # MXFP8 dgrad: 128-multiples, one pass, transposed weights required
+    f = dict(x=FAKE.value, xp=FAKE.value, gu=FAKE.value, h=FAKE.value, y=FAKE.value,
+             offsets=FAKE.value, pos=FAKE.value, idx=FAKE.value, w=FAKE.value,
+             s_sel=FAKE.value, w1=FAKE.value, w2=FAKE.value, dout=FAKE.value, dx=FAKE.value,
+             dw1=FAKE.value, dw2=FAKE.value, dw_route=FAKE.value, dlogits=FAKE.value)
+    m = moe.bwd_args(T=16, H=192, E=4, k=2, I=128, R=32, E_router=4, mx=1, **f)
+    assert lib().moe_backward(ctypes.byref(m), FAKE, 1 << 30, None) == moe.MOE_EINVAL  # H % 128
+    m = moe.bwd_args(T=16, H=256, E=4, k=2, I=128, R=32, E_router=4, mx=1, **f)
+    assert lib().moe_backward(ctypes.byref(m), FAKE, 1 << 30, None) == moe.MOE_EINVAL  # no w1t
+    assert moe.backward_workspace_size(m) > moe.backward_workspace_size(
+        moe.bwd_args(T=16, H=256, E=4, k=2, I=128, R=32, E_router=4))
 
 
 def test_binding_raises_on_error_code():

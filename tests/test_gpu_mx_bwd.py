@@ -1,0 +1,112 @@
+"""The MXFP8 backward's pieces on the GPU: the transposed MX quantisation and the
+dequantisation (bit-exact against the oracle's codec), the MX forward's saves, and the whole
+backward after an MXFP8 forward against the oracle (ffn_bwd_mx)."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_39_amd as moe
+import oracle as orc
+import workloads as wk
+from gpu_harness import TOL_BF16, TOL_MX, assert_close, bf, build_layer, digest, host, \
+    oracle_params
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("E,A,B", [(3, 256, 200), (1, 32, 1), (2, 4096, 96)])
+def test_quantize_t_bit_exact(E, A, B):
+    print(f"  case E={E} A={A} B={B}", flush=True)
+    g = torch.Generator().manual_seed(A + B)
+    w = (torch.randn(E, A, B, generator=g) * torch.exp2(torch.randint(-6, 6, (E, 1, B),
+                                                                      generator=g))).bfloat16()
+    wd = w.to(DEV)
+    codes = torch.empty(E, B, A, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(E, B, A // 32, dtype=torch.uint8, device=DEV)
+    moe.mx_quantize_t(wd, E, A, B, codes, scales)
+    torch.cuda.synchronize()
+    wt = orc.bf16_to_f64(wk.bf16_bits(w)).transpose(0, 2, 1).copy()
+    rc, rs = orc.mx_quantize(wt)
+    assert np.array_equal(host(codes), rc)
+    assert np.array_equal(host(scales), rs)
+
+
+def test_dequantize_bit_exact():
+    rs = np.random.default_rng(5)
+    rows, K = 300, 256
+    codes = rs.integers(0, 256, size=(rows, K)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x11           # no NaN codes
+    scales = rs.integers(110, 145, size=(rows, K // 32)).astype(np.uint8)
+    out = torch.empty(rows, K, dtype=torch.bfloat16, device=DEV)
+    moe.mx_dequantize(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV), rows,
+                      K, out)
+    torch.cuda.synchronize()
+    ref = orc.mx_dequantize(codes, scales)
+    ref_bits = wk.f32_to_bf16_bits(ref.astype(np.float32))
+    assert np.array_equal(wk.bf16_bits(out), ref_bits)
+
+
+REDUCED = dict(T=256, H=1024, I=512, R_share=2048, backward=True)
+
+
+def _mx_layer(**kw):
+    wl = wk.WORKLOADS["dsv3_ep64_mxfp8"].scaled(**{**REDUCED, **kw})
+    inp, layer = build_layer(wl)
+    return wl, inp, layer
+
+
+def test_mx_forward_saves():
+    wl, inp, layer = _mx_layer()
+    layer.forward()
+    torch.cuda.synchronize()
+    p = oracle_params(wl, inp)
+    r = orc.layer_forward(p)
+    assert_close(bf(layer.gu), r["gu"], TOL_BF16, "gu")
+    assert_close(bf(layer.h), r["h"], TOL_MX, "h")
+    # xp: the dequantised dispatch codes are exactly the oracle's quantised xp
+    assert np.array_equal(bf(layer.xp), r["xp"])
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(T=64, R_share=512, I=256)])
+def test_mx_backward_against_oracle(kw):
+    wl, inp, layer = _mx_layer(**kw)
+    print(f"  case T={wl.T} H={wl.H} E={wl.E} I={wl.I} R={wl.R}", flush=True)
+    layer.forward()
+    layer.backward()
+    torch.cuda.synchronize()
+    p = oracle_params(wl, inp)
+    r = orc.layer_forward(p)
+    g = orc.layer_backward(p, r, wk.bf16_bits(inp["dout"]))
+    assert_close(host(layer.dw_route), g["dw_route"], TOL_BF16, "dw_route")
+    assert_close(host(layer.dlogits), g["dlogits"], TOL_BF16, "dlogits")
+    assert_close(bf(layer.dw2), g["dw2"], TOL_BF16, "dw2")
+    assert_close(bf(layer.dw1), g["dw1"], TOL_MX, "dw1")
+    assert_close(bf(layer.dx), g["dx"], TOL_MX, "dx")
+    for e in np.nonzero(r["counts"] == 0)[0]:
+        assert not torch.any(layer.dw1[e] != 0) and not torch.any(layer.dw2[e] != 0)
+
+
+def test_mx_backward_full_size_deterministic_and_near_bf16_dgrad():
+    """Full EP-64 share: reruns are bit-identical, and the MXFP8 dgrad stays within the MX
+    quantisation error of the BF16 dgrad of the same saves."""
+    wl = wk.WORKLOADS["dsv3_ep64_mxfp8"].scaled(backward=True)
+    inp, layer = build_layer(wl)
+    layer.forward()
+    layer.backward()
+    torch.cuda.synchronize()
+    d0 = digest(layer.dx, layer.dw1, layer.dw2)
+    layer.forward()
+    layer.backward()
+    torch.cuda.synchronize()
+    assert digest(layer.dx, layer.dw1, layer.dw2) == d0
+    dx_mx = layer.dx.float().clone()
+    a = layer.bargs
+    a.mx = 0
+    moe.moe_backward(a, layer.bwd_ws)
+    torch.cuda.synchronize()
+    a.mx = 1
+    dx_bf = layer.dx.float()
+    rel = float(torch.linalg.norm(dx_mx - dx_bf) / torch.linalg.norm(dx_bf))
+    print(f"    dx MXFP8 vs BF16 dgrad: rel {rel:.3e}", flush=True)
+    assert rel < 0.1
