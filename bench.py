@@ -43,6 +43,10 @@ GEMM_ROLES = {  # role -> (flops per routed row in units of H*I, MX)
     "bwd_down": (4, False),       # dh = dy W2 (+ SwiGLU backward) and dW2 = dy^T h
     "bwd_gate_up": (8, False),    # dXp = dGU W1 and dW1 = dGU^T Xp
     "mx_gemm1_swiglu": (4, True), "mx_gemm2_down": (2, True),
+    "mx_bwd_down": (2, True),     # MXFP8 dgrad: dh = Q(dy) Q(W2^T)^T (+ SwiGLU backward)
+    "mx_bwd_gate_up": (4, True),  # MXFP8 dgrad: dXp = Q(dGU) Q(W1^T)^T
+    "wgrad_down": (2, False),     # dW2 = dy^T h alone (after MXFP8 dgrad)
+    "wgrad_gate_up": (4, False),  # dW1 = dGU^T Xp alone
 }
 
 
@@ -60,6 +64,8 @@ def parse():
     ap.add_argument("--ring-depth", type=int, default=16,
                     help="minibatches per pass of the macrobatch ring (workloads that stream "
                          "tokens in minibatches)")
+    ap.add_argument("--backward", action="store_true",
+                    help="add the backward to a forward-only workload (MXFP8: MXFP8 dgrad)")
     ap.add_argument("--fused", action="store_true",
                     help="run each step's forward as one cooperative launch (moe_layer_forward)")
     ap.add_argument("--bias-gamma", type=float, default=0.0,
@@ -103,6 +109,12 @@ def role_work(wl, role: str, shared: bool) -> tuple[str, float]:
         return "byte", float(T * wl.ER * 4 + T * wl.k * 16)
     if role == "mx_quantize_h":
         return "byte", float(R * I * 4 + R * I + R * I // 32)
+    if role == "mx_quantize_dy":    # bf16 dy read, codes and scales written
+        return "byte", float(R * H * bf + R * H + R * H // 32)
+    if role == "mx_quantize_dgu":
+        return "byte", float(R * 2 * I * bf + R * 2 * I + R * 2 * I // 32)
+    if role == "mx_dequantize":     # xp codes and scales read, bf16 written (and h after GEMM2)
+        return "byte", float(R * H + R * H // 32 + R * H * bf)
     return "byte", 0.0
 
 
@@ -300,6 +312,8 @@ def main():
         return
     moe.lib()  # fails loudly when the HIP library is missing
     wl = wk.WORKLOADS[a.workload]
+    if a.backward and not wl.backward:
+        wl = wl.scaled(backward=True)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     inp = wk.make_inputs(wl, device=dev)
@@ -387,6 +401,8 @@ def main():
         cfg.update(bias_gamma=a.bias_gamma)
     if a.fused:
         cfg.update(forward="one cooperative launch")
+    if wl.mx and wl.backward:
+        cfg.update(backward_precision="mxfp8 dgrad, bf16 wgrad")
     out = {
         "metric": METRIC,
         "value": round(wl.T * a.steps / elapsed, 1),

@@ -194,7 +194,18 @@ def ffn_bwd(xp, offsets, w1, w2, dy):
     return dxp, dw1, dw2
 
 
-def ffn_bwd_mx(xp, offsets, w1, w2, dy, gu, h):
+def mx_tokens(x):
+    """x [M, C] f64 MX-quantised along its first (token) dimension, in 32-row blocks from row 0
+    (a partial last block padded with zeros), returned dequantised, [M, C]."""
+    x = _c(x, np.float64)
+    M, C = x.shape
+    Mp = -(-M // 32) * 32
+    xt = np.zeros((C, Mp))
+    xt[:, :M] = x.T
+    return mx_dequantize(*mx_quantize(xt))[:, :M].T
+
+
+def ffn_bwd_mx(xp, offsets, w1, w2, dy, gu, h, mx_wgrad=False):
     """Backward of the routed FFN after an MXFP8 forward, with MXFP8 dgrad products.
 
     The two dgrad products take MX-quantised operands along their contraction dimension
@@ -202,9 +213,11 @@ def ffn_bwd_mx(xp, offsets, w1, w2, dy, gu, h):
       dh   = Q_H(dy) . Q_H(W2_e)^T      (dy per row along H; W2_e [H,I] per column, along H)
       dGU  = SwiGLU backward of dh at the saved g|u   (fp64)
       dXp  = Q_2I(dGU) . Q_2I(W1_e)^T   (dGU per row along 2I; W1_e [2I,H] per column)
-    The weight gradients are plain fp64 sums over the expert's rows of the unquantised dy and
-    dGU against the forward's GEMM inputs (h and xp as the forward consumed them):
-      dW2_e = dy_e^T h_e,   dW1_e = dGU_e^T xp_e.
+    The weight gradients are sums over the expert's rows of dy and dGU against the forward's
+    GEMM inputs (h and xp as the forward consumed them):
+      dW2_e = dy_e^T h_e,   dW1_e = dGU_e^T xp_e,
+    in fp64 from the unquantised values, or with mx_wgrad every operand MX-quantised along the
+    expert's tokens (32-row blocks from the expert's first row, mx_tokens).
     xp [R,H], dy [R,H], gu [R,2I], h [R,I] f64; w1 [E,2I,H], w2 [E,H,I] f64 (bf16 values).
     Returns dxp [R,H], dgu [R,2I], dw1, dw2.
     """
@@ -233,8 +246,12 @@ def ffn_bwd_mx(xp, offsets, w1, w2, dy, gu, h):
         dgu[r0:r1, I:] = dh * g * sg
         dguq = mx_dequantize(*mx_quantize(dgu[r0:r1]))
         dxp[r0:r1] = dguq @ w1t.T
-        dw2[e] = dy[r0:r1].T @ h[r0:r1]
-        dw1[e] = dgu[r0:r1].T @ xp[r0:r1]
+        if mx_wgrad:
+            dw2[e] = mx_tokens(dy[r0:r1]).T @ mx_tokens(h[r0:r1])
+            dw1[e] = mx_tokens(dgu[r0:r1]).T @ mx_tokens(xp[r0:r1])
+        else:
+            dw2[e] = dy[r0:r1].T @ h[r0:r1]
+            dw1[e] = dgu[r0:r1].T @ xp[r0:r1]
     return dxp, dgu, dw1, dw2
 
 
@@ -338,12 +355,14 @@ def layer_forward(p: dict) -> dict:
 
 def layer_backward(p: dict, r: dict, dout_bf16) -> dict:
     """Whole backward in fp64 given the forward record `r`: BF16-storage products, or after
-    an MXFP8 forward (p["mx"]) MXFP8 dgrad products (ffn_bwd_mx)."""
+    an MXFP8 forward (p["mx"]) MXFP8 dgrad products, and with p["mx_wgrad"] MXFP8 weight-
+    gradient products too (ffn_bwd_mx)."""
     dout = bf16_to_f64(dout_bf16)
     w1, w2 = bf16_to_f64(p["w1"]), bf16_to_f64(p["w2"])
     dy, dw = combine_bwd(dout, r["y"], r["pos"], r["w"])
     if p.get("mx", False):
-        dxp, _, dw1, dw2 = ffn_bwd_mx(r["xp"], r["offsets"], w1, w2, dy, r["gu"], r["h"])
+        dxp, _, dw1, dw2 = ffn_bwd_mx(r["xp"], r["offsets"], w1, w2, dy, r["gu"], r["h"],
+                                      mx_wgrad=p.get("mx_wgrad", False))
     else:
         dxp, dw1, dw2 = ffn_bwd(r["xp"], r["offsets"], w1, w2, dy)
     g = {"dw_route": dw, "dw1": dw1, "dw2": dw2}

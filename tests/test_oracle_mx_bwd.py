@@ -4,12 +4,16 @@ What fixes it without re-running its own formula:
 - lossless operands: when dy is exactly MX-representable along H and W2 / W1 along their
   contraction dimensions (pre-quantised), every quantisation before dGU is the identity, so
   dGU and both weight gradients equal the BF16 oracle's (itself pinned by finite
-  differences), and dXp differs from it only by one E4M3 rounding of dGU;
+  differences), and dXp differs from it only by one E4M3 rounding of dGU.  Values k/8 with
+  integer |k| <= 8 are exact in E4M3 under any block scale, so dy and h drawn from them make
+  the token-axis quantisation of dW2's operands the identity too;
 - power-of-two equivariance: MX quantisation along a dimension commutes with scaling a whole
   line along that dimension by 2^s (the block scale moves, the codes do not).  Scaling a row
   of dy, a column of W1 or a column of W2 must therefore scale the matching output lines by
   exactly 2^s; a quantisation along the wrong dimension would mix differently scaled values
-  in one block and break the equality.
+  in one block and break the equality.  For the token-axis (weight-gradient) quantisation a
+  whole channel column of xp scales dW1's column, and a W2 column scales dGU's channel and
+  with it dW1's rows.
 """
 import numpy as np
 
@@ -71,13 +75,71 @@ def test_w1_columns_equivariant(orc):
     assert np.array_equal(b[0], a[0] * 2.0 ** s[None, :])      # dXp columns
 
 
-def test_w2_columns_equivariant(orc):
+def test_w2_columns_equivariant(orc, mxw=False):
     off, xp, w1, w2, dy, gu, h = _case()
     s = RS.integers(-3, 4, size=w2.shape[2]).astype(np.float64)
-    a = orc.ffn_bwd_mx(xp, off, w1, w2, dy, gu, h)
-    b = orc.ffn_bwd_mx(xp, off, w1, w2 * 2.0 ** s[None, None, :], dy, gu, h)
+    a = orc.ffn_bwd_mx(xp, off, w1, w2, dy, gu, h, mx_wgrad=mxw)
+    b = orc.ffn_bwd_mx(xp, off, w1, w2 * 2.0 ** s[None, None, :], dy, gu, h, mx_wgrad=mxw)
     I = w2.shape[2]
     sc = np.concatenate([s, s])
     assert np.array_equal(b[1], a[1] * 2.0 ** sc[None, :])     # dGU channels (gate and up)
     assert np.array_equal(b[2], a[2] * 2.0 ** sc[None, :, None])  # dW1 rows
     assert np.array_equal(b[3], a[3])                          # dW2 does not see W2
+
+
+def test_w2_columns_equivariant_mx_wgrad(orc):
+    test_w2_columns_equivariant(orc, mxw=True)
+
+
+def test_mx_wgrad_lossless_and_xp_columns(orc):
+    off, xp, w1, w2, dy, gu, h = _case(counts=(40, 0, 37))
+    k8 = lambda shape: RS.integers(-8, 9, size=shape) / 8.0
+    dy, h, xp = k8(dy.shape), k8(h.shape), k8(xp.shape)
+    a = orc.ffn_bwd_mx(xp, off, w1, w2, dy, gu, h, mx_wgrad=True)
+    b = orc.ffn_bwd_mx(xp, off, w1, w2, dy, gu, h, mx_wgrad=False)
+    assert np.array_equal(a[3], b[3])                     # dW2: token-axis quantisation exact
+    rel = np.linalg.norm(a[2] - b[2]) / np.linalg.norm(b[2])
+    assert 1e-6 < rel < 0.1                               # dW1: dGU quantised along tokens
+    # a power-of-two scale per xp column scales dW1's columns exactly
+    s = RS.integers(-3, 4, size=xp.shape[1]).astype(np.float64)
+    c = orc.ffn_bwd_mx(xp * 2.0 ** s[None, :], off, w1, w2, dy, gu, h, mx_wgrad=True)
+    assert np.array_equal(c[2], a[2] * 2.0 ** s[None, None, :])
+
+
+def test_mx_wgrad_blocks_start_at_the_experts_first_row(orc):
+    # expert 0: 40 rows = one full 32-row block and 8 rows in a zero-padded second block.
+    # Rows 32..39 are 2^-20 smaller: in a block of their own they keep their precision, in a
+    # block shared with rows 8..31 (blocks aligned anywhere else) they would flush to zero.
+    off, xp, w1, w2, dy, gu, h = _case(counts=(40, 0, 37))
+    xp[32:40] *= 2.0 ** -20
+    tiny = xp.copy()
+    tiny[:32] = 0.0
+    a = orc.ffn_bwd_mx(xp, off, w1, w2, dy, gu, h, mx_wgrad=True)
+    b = orc.ffn_bwd_mx(tiny, off, w1, w2, dy, gu, h, mx_wgrad=True)
+    big = xp.copy()
+    big[32:40] = 0.0
+    c = orc.ffn_bwd_mx(big, off, w1, w2, dy, gu, h, mx_wgrad=True)
+    # the small rows' share of dW1_0 survives exactly as when they are quantised alone
+    assert np.array_equal(a[2][0] - c[2][0], b[2][0])
+    assert np.abs(b[2][0]).max() > 0
+
+
+def test_mx_wgrad_couples_rows_of_a_token_block(orc):
+    # doubling one token row of xp (h) changes the block's scale and with it the codes of the
+    # other rows of its 32-token block: dW1 (dW2) is no longer the linear update.  Without a
+    # token-axis quantisation (none, or along channels) the update would be exactly linear.
+    off, xp, w1, w2, dy, gu, h = _case(counts=(64, 0, 37))
+    for name, arr, out in (("xp", xp, 2), ("h", h, 3)):
+        r = int(np.argmax(np.abs(arr[:32]).max(axis=1)))      # the row holding a block max
+        two = arr.copy()
+        two[r] *= 2.0
+        kw = dict(xp=xp, h=h)
+        kw[name] = arr
+        a = orc.ffn_bwd_mx(kw["xp"], off, w1, w2, dy, gu, kw["h"], mx_wgrad=True)
+        kw[name] = two
+        b = orc.ffn_bwd_mx(kw["xp"], off, w1, w2, dy, gu, kw["h"], mx_wgrad=True)
+        only = np.zeros_like(arr)
+        only[r] = arr[r]
+        kw[name] = only
+        c = orc.ffn_bwd_mx(kw["xp"], off, w1, w2, dy, gu, kw["h"], mx_wgrad=True)
+        assert not np.allclose(b[out][0], a[out][0] + c[out][0], rtol=1e-9, atol=0), name
