@@ -47,6 +47,8 @@ GEMM_ROLES = {  # role -> (flops per routed row in units of H*I, MX)
     "mx_bwd_gate_up": (4, True),  # MXFP8 dgrad: dXp = Q(dGU) Q(W1^T)^T
     "wgrad_down": (2, False),     # dW2 = dy^T h alone (after MXFP8 dgrad)
     "wgrad_gate_up": (4, False),  # dW1 = dGU^T Xp alone
+    "mx_wgrad_down": (2, True),   # MXFP8 dW2 = Qt(dy)^T Qt(h), operands along tokens
+    "mx_wgrad_gate_up": (4, True),  # MXFP8 dW1 = Qt(dGU)^T Qt(Xp)
 }
 
 
@@ -113,6 +115,9 @@ def role_work(wl, role: str, shared: bool) -> tuple[str, float]:
         return "byte", float(R * H * bf + R * H + R * H // 32)
     if role == "mx_quantize_dgu":
         return "byte", float(R * 2 * I * bf + R * 2 * I + R * 2 * I // 32)
+    if role.startswith("mx_quantize_tok_"):  # a [R, C] bf16 operand in, codes and scales out
+        C = {"dy": H, "xp": H, "h": I, "dgu": 2 * I}[role[len("mx_quantize_tok_"):]]
+        return "byte", float(R * C * bf + R * C + R * C // 32)
     if role == "mx_dequantize":     # xp codes and scales read, bf16 written (and h after GEMM2)
         return "byte", float(R * H + R * H // 32 + R * H * bf)
     return "byte", 0.0

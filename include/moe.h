@@ -264,15 +264,17 @@ typedef struct moe_bwd_args {
      * [passes][E+1] and pos holds rows local to the token's pass.  Weight gradients reduce
      * over the rows of every pass, in pass order.  R must equal passes * pass_rows. */
     int passes, pass_tokens, pass_rows;
-    /* MXFP8 dgrad (mx != 0; after an MXFP8 forward, one pass, H % 128 == 0, I % 128 == 0):
-     * the two dgrad products of the routed experts take MX-quantised operands along their
-     * contraction dimension, dh = Q(dy) Q(W2_e^T)^T (with the SwiGLU backward) and
-     * dXp = Q(dGU) Q(W1_e^T)^T, on the scaled FP8 MFMA; dy and dGU are quantised on the fly
-     * (MOE_MX_FLOOR), the weights come quantised along the contraction dimension, as
-     * mx_quantize_t writes them.  The weight gradients stay BF16 products of the unquantised
-     * dy and dGU against xp and h, which must then hold what the MX forward's GEMMs consumed:
-     * the dequantised xp codes (mx_dequantize) and the h_save of moe_expert_ffn.  gu is the
-     * MX forward's gu_save. */
+    /* MXFP8 backward after an MXFP8 forward (mx = 1 or 2; one pass, H % 128 == 0,
+     * I % 128 == 0).  The products take MX-quantised operands (MOE_MX_FLOOR) along their
+     * contraction dimension and run on the scaled FP8 MFMA:
+     *   dgrad (mx >= 1): dh = Q(dy) Q(W2_e^T)^T (with the SwiGLU backward) and
+     *     dXp = Q(dGU) Q(W1_e^T)^T; dy and dGU are quantised on the fly, the weights come
+     *     quantised along the contraction dimension, as mx_quantize_t writes them;
+     *   weight gradients (mx == 2): dW2_e = Qt(dy_e)^T Qt(h_e), dW1_e = Qt(dGU_e)^T Qt(xp_e),
+     *     every operand quantised along the expert's rows (32-row blocks from the expert's
+     *     first row, the last one zero-padded); with mx == 1 they stay BF16 products.
+     * xp and h must hold what the MX forward's GEMMs consumed -- the dequantised xp codes
+     * (mx_dequantize) and the h_save of moe_expert_ffn -- and gu its gu_save. */
     int mx;
     const uint8_t *w2t_codes;   /* [E,I,H]  W2_e^T codes, scales [E,I,H/32] (along H) */
     const uint8_t *w2t_scales;

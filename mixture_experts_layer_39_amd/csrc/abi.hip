@@ -19,7 +19,10 @@ int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int
                int I, const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q,
                const uint8_t* w2s, float* hf, uint8_t* hq, uint8_t* hs, uint8_t* panels,
                bf16_t* gu_save, bf16_t* h_save, bf16_t* y, hipStream_t st);
-size_t moe_ffn_bwd_mx_bytes(int E, int R, int H, int I);
+size_t moe_ffn_bwd_mx_bytes(int E, int R, int H, int I, bool wgrad);
+int moe_ffn_wgrad_mx(const int32_t* offsets, int E, int R, int H, int I, const bf16_t* dy,
+                     const bf16_t* h, const bf16_t* dgu, const bf16_t* xp, bf16_t* dw1,
+                     bf16_t* dw2, uint8_t* ws, hipStream_t st);
 int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uint8_t* w1tq,
                    const uint8_t* w1ts, const uint8_t* w2tq, const uint8_t* w2ts,
                    const bf16_t* gu, const bf16_t* dy, bf16_t* dgu, bf16_t* dxp, uint8_t* ws,
@@ -190,7 +193,7 @@ BwdLayout bwd_layout(const moe_bwd_args* a) {
     L.dgus = o; o += moe_align256((size_t)a->S * a->T * 2 * a->Is * 2);
     L.dxs = o;  o += moe_align256((size_t)a->S * a->T * a->H * 2);
     L.mx = o;
-    if (a->mx) o += moe_align256(moe_ffn_bwd_mx_bytes(a->E, a->R, a->H, a->I));
+    if (a->mx) o += moe_align256(moe_ffn_bwd_mx_bytes(a->E, a->R, a->H, a->I, a->mx == 2));
     L.total = o + 256;
     return L;
 }
@@ -218,7 +221,8 @@ extern "C" int moe_backward(const moe_bwd_args* a, void* ws, size_t ws_bytes, vo
                     a->T <= (int64_t)passes * a->pass_tokens);
         MOE_REQUIRE((int64_t)a->pass_tokens * a->k <= a->pass_rows);
     }
-    if (a->mx) {  // MXFP8 dgrad products: one pass, K steps of 128 codes
+    MOE_REQUIRE(a->mx >= 0 && a->mx <= 2);
+    if (a->mx) {  // MXFP8 products: one pass, K steps of 128 codes
         MOE_REQUIRE(passes == 1 && a->H % 128 == 0 && a->I % 128 == 0);
         MOE_REQUIRE(a->T == 0 || (a->w1t_codes && a->w1t_scales && a->w2t_codes && a->w2t_scales));
     }
@@ -273,7 +277,12 @@ extern "C" int moe_backward(const moe_bwd_args* a, void* ws, size_t ws_bytes, vo
                                 a->w2t_codes, a->w2t_scales, (const bf16_t*)a->gu, dy, dgu, dxp,
                                 (uint8_t*)(base + L.mx), st);
             if (rc) return rc;
-            rc = moe_ffn_wgrad_bf16(&wg, E, H, I, st);
+            if (a->mx == 2)
+                rc = moe_ffn_wgrad_mx(a->offsets, E, prow, H, I, dy, (const bf16_t*)a->h, dgu,
+                                      (const bf16_t*)a->xp, (bf16_t*)a->dw1, (bf16_t*)a->dw2,
+                                      (uint8_t*)(base + L.mx), st);
+            else
+                rc = moe_ffn_wgrad_bf16(&wg, E, H, I, st);
             if (rc) return rc;
         } else if (prow > 0) {
             rc = moe_ffn_bwd_bf16((const bf16_t*)a->xp + r0 * H, a->offsets + (size_t)p * (E + 1),

@@ -48,7 +48,9 @@ struct MxArgs {
     int ldc2;
     const int32_t* offsets;
     int E, R, N, K, I;
-    int total;           // tile count when static (shared mode)
+    int total;           // tile count when static (shared mode, weight gradients)
+    int M;               // weight gradients: rows of A (static); K is then the row stride of
+                         // the token-axis operands and each expert takes its own code columns
 };
 
 struct alignas(1024) MxSmem {
@@ -232,8 +234,9 @@ __global__ __launch_bounds__(256) void mx_panel_scales_h(const uint8_t* __restri
     panel_a(blockIdx.x, sc, offsets, E, R, a_es, KB, nsteps, total_static, out, stg, srow);
 }
 
-// The panels of one product of the backward: x blocks [0, na) the A panels (ragged rows), then
-// E * N/256 B panels of a weight with plain rows; y blocks: 64-column chunks of the scales.
+// The panels of one product of the backward: x blocks [0, na) the A panels -- ragged rows
+// from the offsets, or (offsets null) R static rows -- then EB * b_rows/256 B panels of
+// operands with plain rows; y blocks: 64-column chunks of the scales.
 __global__ __launch_bounds__(256) void mx_panel_scales_ab(const uint8_t* __restrict__ as,
                                                           const int32_t* __restrict__ offsets,
                                                           int E, int R, int na,
@@ -246,7 +249,8 @@ __global__ __launch_bounds__(256) void mx_panel_scales_ab(const uint8_t* __restr
     if ((int)blockIdx.y * PS_COLS >= K / 32) return;
     const int bx = blockIdx.x;
     if (bx < na)
-        panel_a(bx, as, offsets, E, R, 0, K / 32, K / XBK, 0, pa, stg, srow);
+        panel_a(bx, as, offsets, offsets ? E : 1, R, 0, K / 32, K / XBK, offsets ? 0 : na, pa,
+                stg, srow);
     else
         panel_b<XEPI_STORE_BF16>(bx - na, bs, b_rows, b_rows, 0, K / 32, K / XBK, pb, stg, srow);
 }
@@ -262,16 +266,51 @@ __device__ __forceinline__ void vgpr_load8(uint2& dst, rsrc_t r, uint32_t voff, 
 }
 __device__ __forceinline__ void settle(uint2& v) { asm volatile("" : "+v"(v)); }
 
+// Token-axis operands of the weight gradients: expert e's code columns start at P_e, the sum
+// of the padded (whole K step) row counts of the experts before it, and span pad(cnt_e).
+__device__ __forceinline__ void mx_token_range(const int32_t* offsets, int E, int R, int e,
+                                               int* P, int* span) {
+    const int lane = threadIdx.x & 63;
+    int run = 0;
+    for (int base = 0; base < e; base += 64) {
+        const int x = base + lane;
+        int v = 0;
+        if (x < e) {
+            const int lo = min(max(offsets[x], 0), R);
+            const int hi = min(max(offsets[x + 1], lo), R);
+            v = cdiv(hi - lo, XBK) * XBK;
+        }
+        run += __shfl(wave_incl_scan(v), 63, 64);
+    }
+    const int lo = min(max(offsets[e], 0), R);
+    const int hi = min(max(offsets[e + 1], lo), R);
+    *P = run;
+    *span = cdiv(hi - lo, XBK) * XBK;
+}
+
 // ---------------------------------------------------------------- one output tile
-template <int EPI>
+// GK: a weight-gradient tile (expert e, static M x N, K = the expert's token columns).
+template <int EPI, bool GK = false>
 __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int logical) {
     const int tid = threadIdx.x, lane = tid & 63, wid = uni(tid >> 6);
     const int wm = wid >> 1, wn = wid & 1;
     const int NT = mx_n_tiles<EPI>(g.N, g.I);
-    const int K = g.K, nk = K / XBK;
+    const int K = g.K;  // row stride of the codes
+    int nk = K / XBK, kbase = 0;
 
     int e, t_local, Mrows, row0, mt_first;
-    if (g.offsets) {
+    if (GK) {
+        const int per = cdiv(g.M, XBM) * NT;
+        e = logical / per;
+        t_local = logical - e * per;
+        mt_first = 0;
+        row0 = 0;
+        Mrows = g.M;
+        int P = 0, span = 0;
+        mx_token_range(g.offsets, g.E, g.R, e, &P, &span);
+        kbase = uni(P);
+        nk = uni(span / XBK);
+    } else if (g.offsets) {
         int ee = 0, first = 0;
         mx_ragged_scan(g.offsets, g.E, g.R, NT, logical, &ee, &first);
         e = uni(ee);
@@ -303,20 +342,29 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
 
     // ---------------------------------------------------------------- operands
     // codes: the K-major load map of a 64-wide BF16 step (128-byte rows; ld in 2-byte units)
-    const int64_t arow = (int64_t)e * g.a_es + row0 + m0;
+    const int64_t arow = GK ? (int64_t)m0 : (int64_t)e * g.a_es + row0 + m0;
     const uint32_t arows = (uint32_t)max(Mrows - m0, 0);
+    // GK: the operands start at the expert's first code column of their shared rows
+    const uint32_t aspan = arows ? arows * (uint32_t)K - (uint32_t)kbase : 0u;
     Operand oa, ob;
-    setup_kmajor<64>(oa, g.A + arow * K, arows * (uint32_t)K, K / 2, wid, lane, wm * 128,
+    setup_kmajor<64>(oa, g.A + arow * K + kbase, aspan, K / 2, wid, lane, wm * 128,
                      [](int r) { return r; }, 2 * XP::RPI, 4 * XP::RPI);
     const int I = g.I;
-    setup_kmajor<64>(ob, g.B + (int64_t)e * g.b_rows * K, (uint32_t)g.b_rows * (uint32_t)K, K / 2,
+    setup_kmajor<64>(ob, GK ? g.B + kbase : g.B + (int64_t)e * g.b_rows * K,
+                     (uint32_t)g.b_rows * (uint32_t)K - (uint32_t)kbase, K / 2,
                      wid, lane, wn * 128, [=](int nn) { return mx_brow<EPI>(nn, n0, ch0, I); },
                      EPI == XEPI_SWIGLU_F32 ? I : 2 * XP::RPI,
                      EPI == XEPI_SWIGLU_F32 ? 16 : 4 * XP::RPI);
     // panel scales of this wave's A rows and B rows
     const uint32_t pbytes = (uint32_t)nk * SPAN;
-    const rsrc_t rsa = make_rsrc(g.At + (int64_t)(2 * (mt_first + tm) + wm) * pbytes, pbytes);
-    const rsrc_t rsb = make_rsrc(g.Bt + (int64_t)(2 * (e * NT + tn) + wn) * pbytes, pbytes);
+    // GK: panels over the whole token axis (K / 128 steps each); the expert's steps start at
+    // its first code column
+    const int64_t pstride = GK ? (int64_t)(K / XBK) * SPAN : (int64_t)pbytes;
+    const int64_t pfirst = GK ? (int64_t)(kbase / XBK) * SPAN : 0;
+    const rsrc_t rsa =
+        make_rsrc(g.At + (int64_t)(2 * (mt_first + tm) + wm) * pstride + pfirst, pbytes);
+    const rsrc_t rsb = make_rsrc(
+        g.Bt + (int64_t)(2 * ((GK ? 0 : e * NT) + tn) + wn) * pstride + pfirst, pbytes);
     const uint32_t lso = (uint32_t)lane * 8u;
     const rsrc_t rnull = make_rsrc(nullptr, 0);
 
@@ -586,6 +634,13 @@ MOE_MX_KERNEL(mx_gemm2_down, XEPI_STORE_BF16)
 MOE_MX_KERNEL(mx_bwd_down, XEPI_DSWIGLU)
 #undef MOE_MX_KERNEL
 
+// Weight gradients: E static grids of M x N tiles, each over its expert's token columns.
+__global__ __launch_bounds__(XNTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mx_wgrad(MxArgs g) {
+    __shared__ MxSmem sm;
+    if ((int)blockIdx.x < g.total) mx_tile<XEPI_STORE_BF16, true>(g, sm, blockIdx.x);
+}
+
 // Upper bound on the 256-row M tiles of an operand (host side, no device data).
 static int mx_mtiles_bound(int R, int E, bool shared) {
     if (shared) return E * cdiv(R, XBM);
@@ -702,21 +757,89 @@ int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int
 }
 
 // ---------------------------------------------------------------- backward, MXFP8 dgrad
-// Workspace of moe_ffn_bwd_mx: MX codes and scales of dy [R,H] and dGU [R,2I], and the panel
-// scales of both products' operands.
-size_t moe_ffn_bwd_mx_bytes(int E, int R, int H, int I) {
-    return moe_align256((size_t)R * H) + moe_align256((size_t)R * H / 32) +
-           moe_align256((size_t)R * 2 * I) + moe_align256((size_t)R * 2 * I / 32) +
-           mx_panel_a_bytes(E, R, H, false) + mx_panel_a_bytes(E, R, 2 * I, false) +
-           mx_panel_b_bytes<XEPI_STORE_BF16>(E, I, I, H) +
-           mx_panel_b_bytes<XEPI_STORE_BF16>(E, H, I, 2 * I);
+// Code columns of the token-axis operands: every expert's rows padded to a whole K step.
+static int mx_tok_cols(int E, int R) { return cdiv(R + E * (XBK - 1), XBK) * XBK; }
+
+// Token-axis codes, scales and panel scales of one [R, C] operand.
+static size_t mx_tok_bytes(int C, int Kp) {
+    return moe_align256((size_t)C * Kp) + moe_align256((size_t)C * Kp / 32) +
+           moe_align256(2 * (size_t)cdiv(C, XBM) * (size_t)(Kp / XBK) * SPAN);
 }
 
+// Workspace of moe_ffn_bwd_mx: MX codes and scales of dy [R,H] and dGU [R,2I], the panel
+// scales of both dgrad products' operands and, with MXFP8 weight gradients, the token-axis
+// operands dy, h, dGU and xp.
+size_t moe_ffn_bwd_mx_bytes(int E, int R, int H, int I, bool wgrad) {
+    size_t n = moe_align256((size_t)R * H) + moe_align256((size_t)R * H / 32) +
+               moe_align256((size_t)R * 2 * I) + moe_align256((size_t)R * 2 * I / 32) +
+               mx_panel_a_bytes(E, R, H, false) + mx_panel_a_bytes(E, R, 2 * I, false) +
+               mx_panel_b_bytes<XEPI_STORE_BF16>(E, I, I, H) +
+               mx_panel_b_bytes<XEPI_STORE_BF16>(E, H, I, 2 * I);
+    if (wgrad) {
+        const int Kp = mx_tok_cols(E, R);
+        n += 2 * mx_tok_bytes(H, Kp) + mx_tok_bytes(I, Kp) + mx_tok_bytes(2 * I, Kp);
+    }
+    return n;
+}
+
+int moe_launch_mx_quantize_tok(const bf16_t* X, int R, int C, const int32_t* offsets, int E,
+                               int Kp, uint8_t* codes, uint8_t* scales, const char* name,
+                               hipStream_t st);
+
 static int mx_panels_ab(const uint8_t* as, const int32_t* offsets, int E, int R,
-                        const uint8_t* bs, int b_rows, int K, uint8_t* pa, uint8_t* pb,
+                        const uint8_t* bs, int EB, int b_rows, int K, uint8_t* pa, uint8_t* pb,
+                        hipStream_t st);
+
+// One MXFP8 weight-gradient product: dW_e [M,N] = Qtok(A_e)^T Qtok(B_e) over expert e's rows,
+// with A [R,M] and B [R,N] in expert order; ws holds both token-axis operands.
+static int mx_wgrad_product(const bf16_t* A, int M, const bf16_t* B, int N,
+                            const int32_t* offsets, int E, int R, bf16_t* dw, uint8_t*& ws,
+                            const char* qa, const char* qb, const char* name, hipStream_t st) {
+    const int Kp = mx_tok_cols(E, R);
+    uint8_t* ac = ws;
+    uint8_t* as = ac + moe_align256((size_t)M * Kp);
+    uint8_t* ap = as + moe_align256((size_t)M * Kp / 32);
+    uint8_t* bc = ws + mx_tok_bytes(M, Kp);
+    uint8_t* bsc = bc + moe_align256((size_t)N * Kp);
+    uint8_t* bp = bsc + moe_align256((size_t)N * Kp / 32);
+    ws += mx_tok_bytes(M, Kp) + mx_tok_bytes(N, Kp);
+    int rc = moe_launch_mx_quantize_tok(A, R, M, offsets, E, Kp, ac, as, qa, st);
+    if (rc) return rc;
+    rc = moe_launch_mx_quantize_tok(B, R, N, offsets, E, Kp, bc, bsc, qb, st);
+    if (rc) return rc;
+    rc = mx_panels_ab(as, nullptr, 1, M, bsc, 1, N, Kp, ap, bp, st);
+    if (rc) return rc;
+    MxArgs g{};
+    g.A = ac; g.At = ap; g.a_es = 0;
+    g.B = bc; g.Bt = bp; g.b_rows = N;
+    g.C = dw; g.c_es = M; g.ldc = N;
+    g.offsets = offsets; g.E = E; g.R = R; g.N = N; g.K = Kp; g.I = 0; g.M = M;
+    g.total = E * cdiv(M, XBM) * cdiv(N, XBN);
+    MOE_TRACED(name, st, mx_wgrad<<<g.total, XNTH, 0, st>>>(g));
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+// The weight gradients of the routed experts in MXFP8 (after moe_ffn_bwd_mx's dgrad, which
+// leaves dgu): dW2_e = Qtok(dy_e)^T Qtok(h_e), dW1_e = Qtok(dGU_e)^T Qtok(xp_e).
+int moe_ffn_wgrad_mx(const int32_t* offsets, int E, int R, int H, int I, const bf16_t* dy,
+                     const bf16_t* h, const bf16_t* dgu, const bf16_t* xp, bf16_t* dw1,
+                     bf16_t* dw2, uint8_t* ws, hipStream_t st) {
+    if (H % XBK || I % XBK) return MOE_EINVAL;
+    uint8_t* p = ws + moe_ffn_bwd_mx_bytes(E, R, H, I, false);
+    int rc = mx_wgrad_product(dy, H, h, I, offsets, E, R, dw2, p, "mx_quantize_tok_dy",
+                              "mx_quantize_tok_h", "mx_wgrad_down", st);
+    if (rc) return rc;
+    return mx_wgrad_product(dgu, 2 * I, xp, H, offsets, E, R, dw1, p, "mx_quantize_tok_dgu",
+                            "mx_quantize_tok_xp", "mx_wgrad_gate_up", st);
+}
+
+// A: ragged rows (offsets) or R static rows (offsets null); B: EB operands of b_rows rows.
+static int mx_panels_ab(const uint8_t* as, const int32_t* offsets, int E, int R,
+                        const uint8_t* bs, int EB, int b_rows, int K, uint8_t* pa, uint8_t* pb,
                         hipStream_t st) {
-    const int na = mx_mtiles_bound(R, E, false);
-    const dim3 grid(na + E * cdiv(b_rows, XBN), cdiv(K / 32, PS_COLS));
+    const int na = offsets ? mx_mtiles_bound(R, E, false) : cdiv(R, XBM);
+    const dim3 grid(na + EB * cdiv(b_rows, XBN), cdiv(K / 32, PS_COLS));
     MOE_TRACED("mx_panel_scales", st,
                mx_panel_scales_ab<<<grid, 256, 0, st>>>(as, offsets, E, R, na, bs, b_rows, K, pa,
                                                         pb));
@@ -746,7 +869,7 @@ int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uin
     uint8_t* pb2 = pb1 + mx_panel_b_bytes<XEPI_STORE_BF16>(E, I, I, H);
     int rc = moe_launch_mx_quantize_bf16(dy, R, H, dyq, dys, "mx_quantize_dy", st);
     if (rc) return rc;
-    rc = mx_panels_ab(dys, offsets, E, R, w2ts, I, H, pa1, pb1, st);
+    rc = mx_panels_ab(dys, offsets, E, R, w2ts, E, I, H, pa1, pb1, st);
     if (rc) return rc;
     MxArgs g{};
     g.A = dyq; g.At = pa1; g.a_es = 0;
@@ -758,7 +881,7 @@ int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uin
     if (rc) return rc;
     rc = moe_launch_mx_quantize_bf16(dgu, R, 2 * I, gq, gs, "mx_quantize_dgu", st);
     if (rc) return rc;
-    rc = mx_panels_ab(gs, offsets, E, R, w1ts, H, 2 * I, pa2, pb2, st);
+    rc = mx_panels_ab(gs, offsets, E, R, w1ts, E, H, 2 * I, pa2, pb2, st);
     if (rc) return rc;
     MxArgs g2{};
     g2.A = gq; g2.At = pa2; g2.a_es = 0;

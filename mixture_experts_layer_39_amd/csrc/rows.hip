@@ -550,6 +550,87 @@ __global__ __launch_bounds__(256) void mx_dequantize_kernel(const uint8_t* __res
         st16(out + b * 32 + 8 * i, u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]});
 }
 
+// ------------------------------------------------------------------ token-axis quantisation
+// The weight-gradient operands of the MXFP8 backward: X [R, C] (routed rows in expert order)
+// quantised along the rows of each expert, written transposed as codes [C][Kp] and scales
+// [C][Kp/32].  Expert e's rows occupy the code columns [P_e, P_e + pad(cnt_e)), where pad
+// rounds up to a whole K step (128) and P_e is the sum of the padded counts before e; the
+// 32-row blocks start at the expert's first row and the padding holds zero codes.  Columns
+// past the last expert are zero.  One block per (64 columns, 128 padded positions): the
+// 128 x 64 tile of X is staged through LDS with 16-byte row loads, then each thread
+// quantises one column's 32-row block and writes its 32 codes (the four blocks of a column
+// fill one 128-byte line).  A 128-position block never straddles two experts.
+constexpr int TOK_PAD = 128, TOK_COLS = 64;
+
+__global__ __launch_bounds__(256) void mx_quantize_tok_kernel(const bf16_t* __restrict__ X, int R,
+                                                              int C,
+                                                              const int32_t* __restrict__ offsets,
+                                                              int E, int Kp,
+                                                              uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales) {
+    __shared__ bf16_t tile[TOK_PAD][TOK_COLS + 8];
+    const int lane = threadIdx.x & 63;
+    const int p = blockIdx.y * TOK_PAD;  // padded position of this block's first row
+    const int c0 = blockIdx.x * TOK_COLS;
+    int e = -1, P = 0, run = 0;
+    for (int base = 0; base < E && e < 0; base += 64) {
+        const int x = base + lane;
+        int v = 0;
+        if (x < E) {
+            const int lo = min(max(offsets[x], 0), R);
+            const int hi = min(max(offsets[x + 1], lo), R);
+            v = (hi - lo + TOK_PAD - 1) / TOK_PAD * TOK_PAD;
+        }
+        const int inc = wave_incl_scan(v) + run;
+        const uint64_t m = __ballot(x < E && inc > p);
+        if (m) {
+            const int l = __ffsll((unsigned long long)m) - 1;
+            e = base + l;
+            P = __shfl(inc - v, l, 64);
+        }
+        run = __shfl(inc, 63, 64);
+    }
+    int lo = 0, cnt = 0;
+    if (e >= 0) {
+        lo = min(max(offsets[e], 0), R);
+        cnt = min(max(offsets[e + 1], lo), R) - lo;
+    }
+    const int t0 = p - P;  // the block's first row within the expert
+    // stage 128 rows x 64 columns: 8 chunks of 8 values per row, 4 chunks per thread
+    for (int i = threadIdx.x; i < TOK_PAD * (TOK_COLS / 8); i += 256) {
+        const int r = i / (TOK_COLS / 8), ch = i % (TOK_COLS / 8);
+        const int col = c0 + ch * 8;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (e >= 0 && t0 + r < cnt && col < C) v = ld16(X + (int64_t)(lo + t0 + r) * C + col);
+        *reinterpret_cast<u32x4*>(&tile[r][ch * 8]) = v;
+    }
+    __syncthreads();
+    const int cl = threadIdx.x & (TOK_COLS - 1), blk = threadIdx.x / TOK_COLS;
+    const int col = c0 + cl;
+    if (col >= C) return;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = __uint_as_float((uint32_t)tile[blk * 32 + i][cl] << 16);
+    uint32_t q[8];
+    const int sc = mx_block(v, MOE_MX_FLOOR, q);
+    uint8_t* out = codes + (int64_t)col * Kp + p + blk * 32;
+    st16(out, u32x4{q[0], q[1], q[2], q[3]});
+    st16(out + 16, u32x4{q[4], q[5], q[6], q[7]});
+    scales[(int64_t)col * (Kp / 32) + p / 32 + blk] = (uint8_t)sc;
+}
+
+int moe_launch_mx_quantize_tok(const bf16_t* X, int R, int C, const int32_t* offsets, int E,
+                               int Kp, uint8_t* codes, uint8_t* scales, const char* name,
+                               hipStream_t st) {
+    if (Kp == 0 || C == 0) return MOE_OK;
+    const dim3 grid((unsigned)((C + TOK_COLS - 1) / TOK_COLS), (unsigned)(Kp / TOK_PAD));
+    MOE_TRACED(name, st,
+               mx_quantize_tok_kernel<<<grid, 256, 0, st>>>(X, R, C, offsets, E, Kp, codes,
+                                                            scales));
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
 extern "C" int mx_quantize_t(const void* in, int batch, int A, int B, uint8_t* codes,
                              uint8_t* scales, int scale_mode, void* stream) {
     MOE_REQUIRE(batch >= 0 && A >= 32 && A % 32 == 0 && B >= 1 && batch <= 65535);

@@ -46,6 +46,8 @@ class LayerCfg:
     router_proj: bool = False
     mx: bool = False
     bias_gamma: float = 0.0    # > 0: sigmoid selection bias, updated from the loads each step
+    mx_bwd: int = 2            # after an MXFP8 forward: 1 MXFP8 dgrad, BF16 weight gradients;
+                               # 2 MXFP8 dgrad and weight gradients
 
     @property
     def ER(self):
@@ -201,7 +203,7 @@ class MoELayer:
                         dout=inp.get("dout"), dx=self.dx, dw1=self.dw1, dw2=self.dw2,
                         dws1=self.dws1, dws2=self.dws2, dw_route=self.dw_route,
                         dlogits=self.dlogits,
-                        **(dict(mx=1, w2t_codes=self.w2tq, w2t_scales=self.w2ts,
+                        **(dict(mx=c.mx_bwd, w2t_codes=self.w2tq, w2t_scales=self.w2ts,
                                 w1t_codes=self.w1tq, w1t_scales=self.w1ts) if c.mx else {}))
 
     # ------------------------------------------------------------------ steps

@@ -194,6 +194,13 @@ def ffn_bwd(xp, offsets, w1, w2, dy):
     return dxp, dw1, dw2
 
 
+def bf16_round(a):
+    """Values rounded to bf16 (through fp32, to nearest even), as f64."""
+    b = np.ascontiguousarray(np.asarray(a, np.float64).astype(np.float32)).view(np.uint32)
+    r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint32) << 16
+    return r.view(np.float32).astype(np.float64)
+
+
 def mx_tokens(x):
     """x [M, C] f64 MX-quantised along its first (token) dimension, in 32-row blocks from row 0
     (a partial last block padded with zeros), returned dequantised, [M, C]."""
@@ -218,6 +225,8 @@ def ffn_bwd_mx(xp, offsets, w1, w2, dy, gu, h, mx_wgrad=False):
       dW2_e = dy_e^T h_e,   dW1_e = dGU_e^T xp_e,
     in fp64 from the unquantised values, or with mx_wgrad every operand MX-quantised along the
     expert's tokens (32-row blocks from the expert's first row, mx_tokens).
+    dy and dGU are quantised from their bf16 values (bf16_round): the precision the kernels
+    hold them in when they take the quantisation decisions.
     xp [R,H], dy [R,H], gu [R,2I], h [R,I] f64; w1 [E,2I,H], w2 [E,H,I] f64 (bf16 values).
     Returns dxp [R,H], dgu [R,2I], dw1, dw2.
     """
@@ -228,7 +237,8 @@ def ffn_bwd_mx(xp, offsets, w1, w2, dy, gu, h, mx_wgrad=False):
     E, I2, H = w1.shape
     I = I2 // 2
     R = xp.shape[0]
-    dyq = mx_dequantize(*mx_quantize(dy)) if R else dy
+    dyb = bf16_round(dy)
+    dyq = mx_dequantize(*mx_quantize(dyb)) if R else dy
     dxp = np.zeros((R, H))
     dgu = np.zeros((R, 2 * I))
     dw1 = np.zeros_like(w1)
@@ -244,11 +254,12 @@ def ffn_bwd_mx(xp, offsets, w1, w2, dy, gu, h, mx_wgrad=False):
         sg = 1.0 / (1.0 + np.exp(-g))
         dgu[r0:r1, :I] = dh * u * sg * (1.0 + g * (1.0 - sg))
         dgu[r0:r1, I:] = dh * g * sg
-        dguq = mx_dequantize(*mx_quantize(dgu[r0:r1]))
+        dgub = bf16_round(dgu[r0:r1])
+        dguq = mx_dequantize(*mx_quantize(dgub))
         dxp[r0:r1] = dguq @ w1t.T
         if mx_wgrad:
-            dw2[e] = mx_tokens(dy[r0:r1]).T @ mx_tokens(h[r0:r1])
-            dw1[e] = mx_tokens(dgu[r0:r1]).T @ mx_tokens(xp[r0:r1])
+            dw2[e] = mx_tokens(dyb[r0:r1]).T @ mx_tokens(h[r0:r1])
+            dw1[e] = mx_tokens(dgub).T @ mx_tokens(xp[r0:r1])
         else:
             dw2[e] = dy[r0:r1].T @ h[r0:r1]
             dw1[e] = dgu[r0:r1].T @ xp[r0:r1]

@@ -10,6 +10,7 @@ import oracle as orc
 import workloads as wk
 from gpu_harness import TOL_BF16, TOL_MX, assert_close, bf, build_layer, digest, host, \
     oracle_params
+from mixture_experts_layer_39_amd.layer import LayerCfg, MoELayer
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -68,28 +69,34 @@ def test_mx_forward_saves():
     assert np.array_equal(bf(layer.xp), r["xp"])
 
 
+@pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("kw", [dict(), dict(T=64, R_share=512, I=256)])
-def test_mx_backward_against_oracle(kw):
-    wl, inp, layer = _mx_layer(**kw)
-    print(f"  case T={wl.T} H={wl.H} E={wl.E} I={wl.I} R={wl.R}", flush=True)
+def test_mx_backward_against_oracle(kw, mode):
+    wl = wk.WORKLOADS["dsv3_ep64_mxfp8"].scaled(**{**REDUCED, **kw})
+    inp = wk.make_inputs(wl, device=DEV)
+    cfg = LayerCfg.from_workload(wl)
+    cfg.mx_bwd = mode
+    layer = MoELayer(cfg, inp, DEV, backward=True)
+    print(f"  case mode={mode} T={wl.T} H={wl.H} E={wl.E} I={wl.I} R={wl.R}", flush=True)
     layer.forward()
     layer.backward()
     torch.cuda.synchronize()
     p = oracle_params(wl, inp)
+    p["mx_wgrad"] = mode == 2
     r = orc.layer_forward(p)
     g = orc.layer_backward(p, r, wk.bf16_bits(inp["dout"]))
     assert_close(host(layer.dw_route), g["dw_route"], TOL_BF16, "dw_route")
     assert_close(host(layer.dlogits), g["dlogits"], TOL_BF16, "dlogits")
-    assert_close(bf(layer.dw2), g["dw2"], TOL_BF16, "dw2")
+    assert_close(bf(layer.dw2), g["dw2"], TOL_BF16 if mode == 1 else TOL_MX, "dw2")
     assert_close(bf(layer.dw1), g["dw1"], TOL_MX, "dw1")
     assert_close(bf(layer.dx), g["dx"], TOL_MX, "dx")
     for e in np.nonzero(r["counts"] == 0)[0]:
         assert not torch.any(layer.dw1[e] != 0) and not torch.any(layer.dw2[e] != 0)
 
 
-def test_mx_backward_full_size_deterministic_and_near_bf16_dgrad():
-    """Full EP-64 share: reruns are bit-identical, and the MXFP8 dgrad stays within the MX
-    quantisation error of the BF16 dgrad of the same saves."""
+def test_mx_backward_full_size_deterministic_and_near_bf16():
+    """Full EP-64 share: reruns are bit-identical, and the MXFP8 products stay within the MX
+    quantisation error of the BF16 products on the same saves."""
     wl = wk.WORKLOADS["dsv3_ep64_mxfp8"].scaled(backward=True)
     inp, layer = build_layer(wl)
     layer.forward()
@@ -100,13 +107,14 @@ def test_mx_backward_full_size_deterministic_and_near_bf16_dgrad():
     layer.backward()
     torch.cuda.synchronize()
     assert digest(layer.dx, layer.dw1, layer.dw2) == d0
-    dx_mx = layer.dx.float().clone()
+    got = {n: getattr(layer, n).float().clone() for n in ("dx", "dw1", "dw2")}
     a = layer.bargs
     a.mx = 0
     moe.moe_backward(a, layer.bwd_ws)
     torch.cuda.synchronize()
-    a.mx = 1
-    dx_bf = layer.dx.float()
-    rel = float(torch.linalg.norm(dx_mx - dx_bf) / torch.linalg.norm(dx_bf))
-    print(f"    dx MXFP8 vs BF16 dgrad: rel {rel:.3e}", flush=True)
-    assert rel < 0.1
+    a.mx = 2
+    for n in got:
+        ref = getattr(layer, n).float()
+        rel = float(torch.linalg.norm(got[n] - ref) / torch.linalg.norm(ref))
+        print(f"    {n} MXFP8 vs BF16 products: rel {rel:.3e}", flush=True)
+        assert rel < 0.1, n

@@ -143,3 +143,11 @@ def test_mx_wgrad_couples_rows_of_a_token_block(orc):
         kw[name] = only
         c = orc.ffn_bwd_mx(kw["xp"], off, w1, w2, dy, gu, kw["h"], mx_wgrad=True)
         assert not np.allclose(b[out][0], a[out][0] + c[out][0], rtol=1e-9, atol=0), name
+
+
+def test_bf16_round_matches_torch(orc):
+    import torch
+    a = np.concatenate([RS.normal(size=4000) * 10.0 ** RS.integers(-30, 30, size=4000),
+                        [0.0, -0.0, 1.0, 1.00390625, 1.01171875]])
+    ref = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(orc.bf16_round(a), ref)
