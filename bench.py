@@ -47,8 +47,8 @@ GEMM_ROLES = {  # role -> (flops per routed row in units of H*I, MX)
     "mx_bwd_gate_up": (4, True),  # MXFP8 dgrad: dXp = Q(dGU) Q(W1^T)^T
     "wgrad_down": (2, False),     # dW2 = dy^T h alone (after MXFP8 dgrad)
     "wgrad_gate_up": (4, False),  # dW1 = dGU^T Xp alone
-    "mx_wgrad_down": (2, True),   # MXFP8 dW2 = Qt(dy)^T Qt(h), operands along tokens
-    "mx_wgrad_gate_up": (4, True),  # MXFP8 dW1 = Qt(dGU)^T Qt(Xp)
+    "mx_bwd_down_wgrad": (4, True),     # MXFP8 dh (+ SwiGLU backward) and dW2 = Qt(dy)^T Qt(h)
+    "mx_bwd_gate_up_wgrad": (8, True),  # MXFP8 dXp and dW1 = Qt(dGU)^T Qt(Xp)
 }
 
 

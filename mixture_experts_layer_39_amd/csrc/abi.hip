@@ -20,12 +20,10 @@ int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int
                const uint8_t* w2s, float* hf, uint8_t* hq, uint8_t* hs, uint8_t* panels,
                bf16_t* gu_save, bf16_t* h_save, bf16_t* y, hipStream_t st);
 size_t moe_ffn_bwd_mx_bytes(int E, int R, int H, int I, bool wgrad);
-int moe_ffn_wgrad_mx(const int32_t* offsets, int E, int R, int H, int I, const bf16_t* dy,
-                     const bf16_t* h, const bf16_t* dgu, const bf16_t* xp, bf16_t* dw1,
-                     bf16_t* dw2, uint8_t* ws, hipStream_t st);
 int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uint8_t* w1tq,
                    const uint8_t* w1ts, const uint8_t* w2tq, const uint8_t* w2ts,
-                   const bf16_t* gu, const bf16_t* dy, bf16_t* dgu, bf16_t* dxp, uint8_t* ws,
+                   const bf16_t* gu, const bf16_t* dy, bf16_t* dgu, bf16_t* dxp,
+                   const bf16_t* h, const bf16_t* xp, bf16_t* dw1, bf16_t* dw2, uint8_t* ws,
                    hipStream_t st);
 int moe_ffn_wgrad_bf16(const MoeWgradSpan* wg, int E, int H, int I, hipStream_t st);
 size_t moe_mx_panel_bytes(int E, int R, int H, int I, bool shared);
@@ -273,17 +271,17 @@ extern "C" int moe_backward(const moe_bwd_args* a, void* ws, size_t ws_bytes, vo
                                     a->dw_route + (size_t)t0 * k, st);
         if (rc) return rc;
         if (prow > 0 && a->mx) {
+            const bool mxw = a->mx == 2;
             rc = moe_ffn_bwd_mx(a->offsets, E, prow, H, I, a->w1t_codes, a->w1t_scales,
                                 a->w2t_codes, a->w2t_scales, (const bf16_t*)a->gu, dy, dgu, dxp,
+                                (const bf16_t*)a->h, (const bf16_t*)a->xp,
+                                mxw ? (bf16_t*)a->dw1 : nullptr, mxw ? (bf16_t*)a->dw2 : nullptr,
                                 (uint8_t*)(base + L.mx), st);
             if (rc) return rc;
-            if (a->mx == 2)
-                rc = moe_ffn_wgrad_mx(a->offsets, E, prow, H, I, dy, (const bf16_t*)a->h, dgu,
-                                      (const bf16_t*)a->xp, (bf16_t*)a->dw1, (bf16_t*)a->dw2,
-                                      (uint8_t*)(base + L.mx), st);
-            else
+            if (!mxw) {
                 rc = moe_ffn_wgrad_bf16(&wg, E, H, I, st);
-            if (rc) return rc;
+                if (rc) return rc;
+            }
         } else if (prow > 0) {
             rc = moe_ffn_bwd_bf16((const bf16_t*)a->xp + r0 * H, a->offsets + (size_t)p * (E + 1),
                                   E, prow, H, I, (const bf16_t*)a->w1, (const bf16_t*)a->w2,

@@ -634,11 +634,26 @@ MOE_MX_KERNEL(mx_gemm2_down, XEPI_STORE_BF16)
 MOE_MX_KERNEL(mx_bwd_down, XEPI_DSWIGLU)
 #undef MOE_MX_KERNEL
 
-// Weight gradients: E static grids of M x N tiles, each over its expert's token columns.
+// A dgrad product and an independent weight-gradient product in one launch, the dgrad tiles
+// first: the weight-gradient tiles (E static grids of M x N tiles, each over its expert's
+// token columns) fill the dgrad's last, partial round of 256 CUs.
+template <int EPI>
+__device__ __forceinline__ void mx_pair(const MxArgs& gd, const MxArgs& gw, MxSmem& sm) {
+    const int td = uni(mx_ragged_scan(gd.offsets, gd.E, gd.R, mx_n_tiles<EPI>(gd.N, gd.I), -1,
+                                      nullptr, nullptr));
+    const int b = blockIdx.x;
+    if (b < td) mx_tile<EPI>(gd, sm, b);
+    else if (b - td < gw.total) mx_tile<XEPI_STORE_BF16, true>(gw, sm, b - td);
+}
 __global__ __launch_bounds__(XNTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mx_wgrad(MxArgs g) {
+void mx_bwd_down_pair(MxArgs gd, MxArgs gw) {
     __shared__ MxSmem sm;
-    if ((int)blockIdx.x < g.total) mx_tile<XEPI_STORE_BF16, true>(g, sm, blockIdx.x);
+    mx_pair<XEPI_DSWIGLU>(gd, gw, sm);
+}
+__global__ __launch_bounds__(XNTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mx_bwd_gate_up_pair(MxArgs gd, MxArgs gw) {
+    __shared__ MxSmem sm;
+    mx_pair<XEPI_STORE_BF16>(gd, gw, sm);
 }
 
 // Upper bound on the 256-row M tiles of an operand (host side, no device data).
@@ -786,15 +801,26 @@ int moe_launch_mx_quantize_tok(const bf16_t* X, int R, int C, const int32_t* off
                                int Kp, uint8_t* codes, uint8_t* scales, const char* name,
                                hipStream_t st);
 
+// A: ragged rows (offsets) or R static rows (offsets null); B: EB operands of b_rows rows.
 static int mx_panels_ab(const uint8_t* as, const int32_t* offsets, int E, int R,
                         const uint8_t* bs, int EB, int b_rows, int K, uint8_t* pa, uint8_t* pb,
-                        hipStream_t st);
+                        hipStream_t st) {
+    const int na = offsets ? mx_mtiles_bound(R, E, false) : cdiv(R, XBM);
+    const dim3 grid(na + EB * cdiv(b_rows, XBN), cdiv(K / 32, PS_COLS));
+    MOE_TRACED("mx_panel_scales", st,
+               mx_panel_scales_ab<<<grid, 256, 0, st>>>(as, offsets, E, R, na, bs, b_rows, K, pa,
+                                                        pb));
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
 
-// One MXFP8 weight-gradient product: dW_e [M,N] = Qtok(A_e)^T Qtok(B_e) over expert e's rows,
-// with A [R,M] and B [R,N] in expert order; ws holds both token-axis operands.
-static int mx_wgrad_product(const bf16_t* A, int M, const bf16_t* B, int N,
+
+// One MXFP8 weight-gradient product, prepared: dW_e [M,N] = Qt(A_e)^T Qt(B_e) over expert e's
+// rows, with A [R,M] and B [R,N] in expert order; quantises both operands along the tokens into
+// ws (advanced past them) and returns the product's arguments.
+static int mx_wgrad_prepare(const bf16_t* A, int M, const bf16_t* B, int N,
                             const int32_t* offsets, int E, int R, bf16_t* dw, uint8_t*& ws,
-                            const char* qa, const char* qb, const char* name, hipStream_t st) {
+                            const char* qa, const char* qb, MxArgs& g, hipStream_t st) {
     const int Kp = mx_tok_cols(E, R);
     uint8_t* ac = ws;
     uint8_t* as = ac + moe_align256((size_t)M * Kp);
@@ -809,56 +835,43 @@ static int mx_wgrad_product(const bf16_t* A, int M, const bf16_t* B, int N,
     if (rc) return rc;
     rc = mx_panels_ab(as, nullptr, 1, M, bsc, 1, N, Kp, ap, bp, st);
     if (rc) return rc;
-    MxArgs g{};
+    g = MxArgs{};
     g.A = ac; g.At = ap; g.a_es = 0;
     g.B = bc; g.Bt = bp; g.b_rows = N;
     g.C = dw; g.c_es = M; g.ldc = N;
     g.offsets = offsets; g.E = E; g.R = R; g.N = N; g.K = Kp; g.I = 0; g.M = M;
     g.total = E * cdiv(M, XBM) * cdiv(N, XBN);
-    MOE_TRACED(name, st, mx_wgrad<<<g.total, XNTH, 0, st>>>(g));
+    return MOE_OK;
+}
+
+template <int EPI>
+static int mx_launch_pair(const MxArgs& gd, const MxArgs& gw, const char* name, hipStream_t st) {
+    const int grid = mx_mtiles_bound(gd.R, gd.E, false) * mx_n_tiles<EPI>(gd.N, gd.I) + gw.total;
+    if (grid <= 0) return MOE_OK;
+    if (EPI == XEPI_DSWIGLU)
+        MOE_TRACED(name, st, mx_bwd_down_pair<<<grid, XNTH, 0, st>>>(gd, gw));
+    else
+        MOE_TRACED(name, st, mx_bwd_gate_up_pair<<<grid, XNTH, 0, st>>>(gd, gw));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
 
-// The weight gradients of the routed experts in MXFP8 (after moe_ffn_bwd_mx's dgrad, which
-// leaves dgu): dW2_e = Qtok(dy_e)^T Qtok(h_e), dW1_e = Qtok(dGU_e)^T Qtok(xp_e).
-int moe_ffn_wgrad_mx(const int32_t* offsets, int E, int R, int H, int I, const bf16_t* dy,
-                     const bf16_t* h, const bf16_t* dgu, const bf16_t* xp, bf16_t* dw1,
-                     bf16_t* dw2, uint8_t* ws, hipStream_t st) {
-    if (H % XBK || I % XBK) return MOE_EINVAL;
-    uint8_t* p = ws + moe_ffn_bwd_mx_bytes(E, R, H, I, false);
-    int rc = mx_wgrad_product(dy, H, h, I, offsets, E, R, dw2, p, "mx_quantize_tok_dy",
-                              "mx_quantize_tok_h", "mx_wgrad_down", st);
-    if (rc) return rc;
-    return mx_wgrad_product(dgu, 2 * I, xp, H, offsets, E, R, dw1, p, "mx_quantize_tok_dgu",
-                            "mx_quantize_tok_xp", "mx_wgrad_gate_up", st);
-}
-
-// A: ragged rows (offsets) or R static rows (offsets null); B: EB operands of b_rows rows.
-static int mx_panels_ab(const uint8_t* as, const int32_t* offsets, int E, int R,
-                        const uint8_t* bs, int EB, int b_rows, int K, uint8_t* pa, uint8_t* pb,
-                        hipStream_t st) {
-    const int na = offsets ? mx_mtiles_bound(R, E, false) : cdiv(R, XBM);
-    const dim3 grid(na + EB * cdiv(b_rows, XBN), cdiv(K / 32, PS_COLS));
-    MOE_TRACED("mx_panel_scales", st,
-               mx_panel_scales_ab<<<grid, 256, 0, st>>>(as, offsets, E, R, na, bs, b_rows, K, pa,
-                                                        pb));
-    MOE_LAUNCH_CHECK();
-    return MOE_OK;
-}
-
-// The dgrad products of the routed experts' backward in MXFP8, each operand MX-quantised along
-// the product's contraction dimension:
+// The routed experts' backward products in MXFP8, each operand MX-quantised along the
+// product's contraction dimension:
 //   dh = Q(dy) Q(W2_e^T)^T with the SwiGLU backward in the epilogue -> dgu [R,2I] bf16,
-//   dXp = Q(dGU) Q(W1_e^T)^T -> dxp [R,H] bf16.
+//   dXp = Q(dGU) Q(W1_e^T)^T -> dxp [R,H] bf16,
+// and with wgrad (dw1, dw2 given) the weight gradients dW2_e = Qt(dy_e)^T Qt(h_e) and
+// dW1_e = Qt(dGU_e)^T Qt(xp_e) in the same launches as the dgrad products.
 // w2t: W2_e^T codes [E][I][H] and scales [E][I][H/32] (along H); w1t: W1_e^T codes [E][H][2I]
-// and scales [E][H][2I/32] (along 2I) -- mx_quantize_t of the weights.  gu: the forward's g|u.
+// and scales [E][H][2I/32] (along 2I) -- mx_quantize_t of the weights.  gu: the forward's g|u;
+// h, xp: the forward's GEMM inputs (bf16).
 int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uint8_t* w1tq,
                    const uint8_t* w1ts, const uint8_t* w2tq, const uint8_t* w2ts,
-                   const bf16_t* gu, const bf16_t* dy, bf16_t* dgu, bf16_t* dxp, uint8_t* ws,
+                   const bf16_t* gu, const bf16_t* dy, bf16_t* dgu, bf16_t* dxp,
+                   const bf16_t* h, const bf16_t* xp, bf16_t* dw1, bf16_t* dw2, uint8_t* ws,
                    hipStream_t st) {
     if (H % XBK || I % XBK) return MOE_EINVAL;
-    if (R == 0) return MOE_OK;
+    const bool wgrad = dw1 && dw2;
     uint8_t* dyq = ws;
     uint8_t* dys = dyq + moe_align256((size_t)R * H);
     uint8_t* gq = dys + moe_align256((size_t)R * H / 32);
@@ -867,26 +880,39 @@ int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uin
     uint8_t* pa2 = pa1 + mx_panel_a_bytes(E, R, H, false);
     uint8_t* pb1 = pa2 + mx_panel_a_bytes(E, R, 2 * I, false);
     uint8_t* pb2 = pb1 + mx_panel_b_bytes<XEPI_STORE_BF16>(E, I, I, H);
+    uint8_t* wsw = ws + moe_ffn_bwd_mx_bytes(E, R, H, I, false);
+    MxArgs gw{}, gw2{};  // total 0: no weight-gradient tiles
     int rc = moe_launch_mx_quantize_bf16(dy, R, H, dyq, dys, "mx_quantize_dy", st);
     if (rc) return rc;
     rc = mx_panels_ab(dys, offsets, E, R, w2ts, E, I, H, pa1, pb1, st);
     if (rc) return rc;
+    if (wgrad) {
+        rc = mx_wgrad_prepare(dy, H, h, I, offsets, E, R, dw2, wsw, "mx_quantize_tok_dy",
+                              "mx_quantize_tok_h", gw, st);
+        if (rc) return rc;
+    }
     MxArgs g{};
     g.A = dyq; g.At = pa1; g.a_es = 0;
     g.B = w2tq; g.Bt = pb1; g.b_rows = I;
     g.C = dgu; g.c_es = 0; g.ldc = 2 * I;
     g.C2 = const_cast<bf16_t*>(gu); g.ldc2 = 2 * I;
     g.offsets = offsets; g.E = E; g.R = R; g.N = I; g.K = H; g.I = I;
-    rc = mx_launch<XEPI_DSWIGLU>(g, st);
+    rc = mx_launch_pair<XEPI_DSWIGLU>(g, gw, wgrad ? "mx_bwd_down_wgrad" : "mx_bwd_down", st);
     if (rc) return rc;
     rc = moe_launch_mx_quantize_bf16(dgu, R, 2 * I, gq, gs, "mx_quantize_dgu", st);
     if (rc) return rc;
     rc = mx_panels_ab(gs, offsets, E, R, w1ts, E, H, 2 * I, pa2, pb2, st);
     if (rc) return rc;
+    if (wgrad) {
+        rc = mx_wgrad_prepare(dgu, 2 * I, xp, H, offsets, E, R, dw1, wsw, "mx_quantize_tok_dgu",
+                              "mx_quantize_tok_xp", gw2, st);
+        if (rc) return rc;
+    }
     MxArgs g2{};
     g2.A = gq; g2.At = pa2; g2.a_es = 0;
     g2.B = w1tq; g2.Bt = pb2; g2.b_rows = H;
     g2.C = dxp; g2.c_es = 0; g2.ldc = H;
     g2.offsets = offsets; g2.E = E; g2.R = R; g2.N = H; g2.K = 2 * I; g2.I = I;
-    return mx_launch<XEPI_STORE_BF16>(g2, st, "mx_bwd_gate_up");
+    return mx_launch_pair<XEPI_STORE_BF16>(g2, gw2,
+                                           wgrad ? "mx_bwd_gate_up_wgrad" : "mx_bwd_gate_up", st);
 }
