@@ -118,3 +118,31 @@ def test_mx_backward_full_size_deterministic_and_near_bf16():
         rel = float(torch.linalg.norm(got[n] - ref) / torch.linalg.norm(ref))
         print(f"    {n} MXFP8 vs BF16 products: rel {rel:.3e}", flush=True)
         assert rel < 0.1, n
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_mx_backward_empty_expert_and_ragged_rows(mode):
+    """An expert with no rows (zero weight gradients, exactly) and experts whose row counts
+    are not multiples of 32 or 128 (partial token blocks, padded K steps)."""
+    wl = wk.WORKLOADS["dsv3_ep64_mxfp8"].scaled(**{**REDUCED, "T": 100, "R_share": 800})
+    inp = wk.make_inputs(wl, device=DEV)
+    li = inp["idx_local"].clone()
+    li[li == 1] = 0                       # expert 1 gets no rows
+    li[:3] = 3                            # shift counts off the 32-row grid
+    inp["idx_local"] = li
+    cfg = LayerCfg.from_workload(wl)
+    cfg.mx_bwd = mode
+    layer = MoELayer(cfg, inp, DEV, backward=True)
+    layer.forward()
+    layer.backward()
+    torch.cuda.synchronize()
+    p = oracle_params(wl, inp)
+    p["mx_wgrad"] = mode == 2
+    r = orc.layer_forward(p)
+    print(f"  case mode={mode} counts={r['counts'].tolist()}", flush=True)
+    assert r["counts"][1] == 0 and any(c % 32 for c in r["counts"])
+    g = orc.layer_backward(p, r, wk.bf16_bits(inp["dout"]))
+    assert_close(bf(layer.dw2), g["dw2"], TOL_MX, "dw2")
+    assert_close(bf(layer.dw1), g["dw1"], TOL_MX, "dw1")
+    assert_close(bf(layer.dx), g["dx"], TOL_MX, "dx")
+    assert not torch.any(layer.dw1[1] != 0) and not torch.any(layer.dw2[1] != 0)
