@@ -712,7 +712,7 @@ static size_t mx_panel_b_bytes(int E, int N, int I, int K) {
 using namespace moe;
 
 int moe_launch_mx_quantize_f32(const float* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
-                               hipStream_t st);
+                               bf16_t* deq, hipStream_t st);
 
 // Workspace bytes of the panel scales of both MXFP8 GEMMs (A and B operands).
 size_t moe_mx_panel_bytes(int E, int R, int H, int I, bool shared) {
@@ -754,12 +754,8 @@ int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int
     rc = mx_launch<XEPI_SWIGLU_F32>(g, st);
     if (rc) return rc;
     int64_t rows = shared ? (int64_t)E * R : R;
-    rc = moe_launch_mx_quantize_f32(hf, rows, I, hq, hs, st);
+    rc = moe_launch_mx_quantize_f32(hf, rows, I, hq, hs, h_save, st);
     if (rc) return rc;
-    if (h_save) {
-        rc = moe_launch_mx_dequantize(hq, hs, rows, I, h_save, st);
-        if (rc) return rc;
-    }
     rc = mx_panels_h(hs, offsets, E, R, shared ? R : 0, I, pa2, st);
     if (rc) return rc;
     MxArgs g2{};
@@ -798,8 +794,8 @@ size_t moe_ffn_bwd_mx_bytes(int E, int R, int H, int I, bool wgrad) {
 }
 
 int moe_launch_mx_quantize_tok(const bf16_t* X, int R, int C, const int32_t* offsets, int E,
-                               int Kp, uint8_t* codes, uint8_t* scales, const char* name,
-                               hipStream_t st);
+                               int Kp, uint8_t* codes, uint8_t* scales, uint8_t* rcodes,
+                               uint8_t* rscales, const char* name, hipStream_t st);
 
 // A: ragged rows (offsets) or R static rows (offsets null); B: EB operands of b_rows rows.
 static int mx_panels_ab(const uint8_t* as, const int32_t* offsets, int E, int R,
@@ -817,10 +813,12 @@ static int mx_panels_ab(const uint8_t* as, const int32_t* offsets, int E, int R,
 
 // One MXFP8 weight-gradient product, prepared: dW_e [M,N] = Qt(A_e)^T Qt(B_e) over expert e's
 // rows, with A [R,M] and B [R,N] in expert order; quantises both operands along the tokens into
-// ws (advanced past them) and returns the product's arguments.
+// ws (advanced past them) and returns the product's arguments.  The pass over A also writes A
+// quantised along its rows (arq, ars: the operand of the dgrad product that shares A).
 static int mx_wgrad_prepare(const bf16_t* A, int M, const bf16_t* B, int N,
                             const int32_t* offsets, int E, int R, bf16_t* dw, uint8_t*& ws,
-                            const char* qa, const char* qb, MxArgs& g, hipStream_t st) {
+                            uint8_t* arq, uint8_t* ars, const char* qa, const char* qb,
+                            MxArgs& g, hipStream_t st) {
     const int Kp = mx_tok_cols(E, R);
     uint8_t* ac = ws;
     uint8_t* as = ac + moe_align256((size_t)M * Kp);
@@ -829,9 +827,9 @@ static int mx_wgrad_prepare(const bf16_t* A, int M, const bf16_t* B, int N,
     uint8_t* bsc = bc + moe_align256((size_t)N * Kp);
     uint8_t* bp = bsc + moe_align256((size_t)N * Kp / 32);
     ws += mx_tok_bytes(M, Kp) + mx_tok_bytes(N, Kp);
-    int rc = moe_launch_mx_quantize_tok(A, R, M, offsets, E, Kp, ac, as, qa, st);
+    int rc = moe_launch_mx_quantize_tok(A, R, M, offsets, E, Kp, ac, as, arq, ars, qa, st);
     if (rc) return rc;
-    rc = moe_launch_mx_quantize_tok(B, R, N, offsets, E, Kp, bc, bsc, qb, st);
+    rc = moe_launch_mx_quantize_tok(B, R, N, offsets, E, Kp, bc, bsc, nullptr, nullptr, qb, st);
     if (rc) return rc;
     rc = mx_panels_ab(as, nullptr, 1, M, bsc, 1, N, Kp, ap, bp, st);
     if (rc) return rc;
@@ -882,15 +880,14 @@ int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uin
     uint8_t* pb2 = pb1 + mx_panel_b_bytes<XEPI_STORE_BF16>(E, I, I, H);
     uint8_t* wsw = ws + moe_ffn_bwd_mx_bytes(E, R, H, I, false);
     MxArgs gw{}, gw2{};  // total 0: no weight-gradient tiles
-    int rc = moe_launch_mx_quantize_bf16(dy, R, H, dyq, dys, "mx_quantize_dy", st);
+    // dy quantised along H for dh and, with the weight gradients, along the tokens for dW2 in
+    // the same pass
+    int rc = wgrad ? mx_wgrad_prepare(dy, H, h, I, offsets, E, R, dw2, wsw, dyq, dys,
+                                      "mx_quantize_tok_dy", "mx_quantize_tok_h", gw, st)
+                   : moe_launch_mx_quantize_bf16(dy, R, H, dyq, dys, "mx_quantize_dy", st);
     if (rc) return rc;
     rc = mx_panels_ab(dys, offsets, E, R, w2ts, E, I, H, pa1, pb1, st);
     if (rc) return rc;
-    if (wgrad) {
-        rc = mx_wgrad_prepare(dy, H, h, I, offsets, E, R, dw2, wsw, "mx_quantize_tok_dy",
-                              "mx_quantize_tok_h", gw, st);
-        if (rc) return rc;
-    }
     MxArgs g{};
     g.A = dyq; g.At = pa1; g.a_es = 0;
     g.B = w2tq; g.Bt = pb1; g.b_rows = I;
@@ -899,15 +896,12 @@ int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uin
     g.offsets = offsets; g.E = E; g.R = R; g.N = I; g.K = H; g.I = I;
     rc = mx_launch_pair<XEPI_DSWIGLU>(g, gw, wgrad ? "mx_bwd_down_wgrad" : "mx_bwd_down", st);
     if (rc) return rc;
-    rc = moe_launch_mx_quantize_bf16(dgu, R, 2 * I, gq, gs, "mx_quantize_dgu", st);
+    rc = wgrad ? mx_wgrad_prepare(dgu, 2 * I, xp, H, offsets, E, R, dw1, wsw, gq, gs,
+                                  "mx_quantize_tok_dgu", "mx_quantize_tok_xp", gw2, st)
+               : moe_launch_mx_quantize_bf16(dgu, R, 2 * I, gq, gs, "mx_quantize_dgu", st);
     if (rc) return rc;
     rc = mx_panels_ab(gs, offsets, E, R, w1ts, E, H, 2 * I, pa2, pb2, st);
     if (rc) return rc;
-    if (wgrad) {
-        rc = mx_wgrad_prepare(dgu, 2 * I, xp, H, offsets, E, R, dw1, wsw, "mx_quantize_tok_dgu",
-                              "mx_quantize_tok_xp", gw2, st);
-        if (rc) return rc;
-    }
     MxArgs g2{};
     g2.A = gq; g2.At = pa2; g2.a_es = 0;
     g2.B = w1tq; g2.Bt = pb2; g2.b_rows = H;

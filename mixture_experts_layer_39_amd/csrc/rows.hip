@@ -42,6 +42,16 @@ __device__ __forceinline__ int mx_scale_code(float amax, int mode) {
     return code < 0 ? 0 : (code > 254 ? 254 : code);
 }
 
+// Value of an E4M3 ("FN") code.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    float v;
+    if (e == 15u && m == 7u) v = __uint_as_float(0x7FC00000u);        // NaN
+    else if (e == 0u) v = (float)m * (1.0f / 512.0f);                // subnormal: m 2^-9
+    else v = __uint_as_float(((e + 120u) << 23) | (m << 20));        // 2^(e-7) (1 + m/8)
+    return (c & 0x80u) ? -v : v;
+}
+
 // Quantise 32 fp32 values (one block) held in v[]; returns the scale code, codes packed
 // little-endian into q[8].
 __device__ __forceinline__ int mx_block(const float* v, int mode, uint32_t* q) {
@@ -172,10 +182,27 @@ __global__ __launch_bounds__(256) void dispatch_mx_tok_kernel(const bf16_t* __re
 }
 
 // ------------------------------------------------------------------ mx_quantize
+// The quantised values of one block written back as bf16 (exact: codes x 2^k).
+__device__ __forceinline__ void mx_deq_store(const uint32_t* q, int sc, bf16_t* out) {
+    const float f = ldexpf(1.0f, sc - 127);
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t word = q[i];
+        w[2 * i] = pack_bf2(e4m3_value(word & 0xFFu) * f, e4m3_value((word >> 8) & 0xFFu) * f);
+        w[2 * i + 1] = pack_bf2(e4m3_value((word >> 16) & 0xFFu) * f, e4m3_value(word >> 24) * f);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        st16(out + 8 * i, u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]});
+}
+
+// deq (optional): the quantised values written back as bf16.
 template <bool F32>
 __global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict__ in, int64_t nblocks,
                                                           int mode, uint8_t* __restrict__ codes,
-                                                          uint8_t* __restrict__ scales) {
+                                                          uint8_t* __restrict__ scales,
+                                                          bf16_t* __restrict__ deq) {
     int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= nblocks) return;
     float v[32];
@@ -204,6 +231,7 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict
     st16(codes + b * 32, u32x4{q[0], q[1], q[2], q[3]});
     st16(codes + b * 32 + 16, u32x4{q[4], q[5], q[6], q[7]});
     scales[b] = (uint8_t)sc;
+    if (deq) mx_deq_store(q, sc, deq + b * 32);
 }
 
 // ------------------------------------------------------------------ combine
@@ -407,6 +435,134 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restri
     }
 }
 
+// ------------------------------------------------------------------ mx_quantize_t
+// Quantisation along the first dimension of each [A, B] matrix of a batch, written transposed:
+// codes [batch][B][A], scales [batch][B][A/32].  One thread per (column, 32-row block): it
+// reads its column's 32 values (consecutive threads read consecutive columns, so every row
+// access is coalesced) and writes the block's 32 codes as two 16-byte stores.
+__global__ __launch_bounds__(256) void mx_quantize_t_kernel(const bf16_t* __restrict__ in, int A,
+                                                            int B, int mode,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+    const int col = blockIdx.x * blockDim.x + threadIdx.x;
+    const int ab = blockIdx.y;            // 32-row block
+    const int64_t m = blockIdx.z;         // matrix of the batch
+    if (col >= B) return;
+    const bf16_t* p = in + (m * A + (int64_t)ab * 32) * B + col;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = __uint_as_float((uint32_t)p[(int64_t)i * B] << 16);
+    uint32_t q[8];
+    const int sc = mx_block(v, mode, q);
+    uint8_t* out = codes + (m * B + col) * A + ab * 32;
+    st16(out, u32x4{q[0], q[1], q[2], q[3]});
+    st16(out + 16, u32x4{q[4], q[5], q[6], q[7]});
+    scales[(m * B + col) * (A / 32) + ab] = (uint8_t)sc;
+}
+
+// ------------------------------------------------------------------ mx_dequantize
+// One thread per 32-value block: value = E4M3(code) * 2^(scale - 127), rounded to bf16
+// (exact for every normal bf16 value: a code has 3 mantissa bits).
+
+__global__ __launch_bounds__(256) void mx_dequantize_kernel(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            int64_t nblocks,
+                                                            bf16_t* __restrict__ out) {
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nblocks) return;
+    const u32x4 c0 = ld16(codes + b * 32), c1 = ld16(codes + b * 32 + 16);
+    const uint32_t q[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+    mx_deq_store(q, scales[b], out + b * 32);
+}
+
+// ------------------------------------------------------------------ token-axis quantisation
+// The weight-gradient operands of the MXFP8 backward: X [R, C] (routed rows in expert order)
+// quantised along the rows of each expert, written transposed as codes [C][Kp] and scales
+// [C][Kp/32].  Expert e's rows occupy the code columns [P_e, P_e + pad(cnt_e)), where pad
+// rounds up to a whole K step (128) and P_e is the sum of the padded counts before e; the
+// 32-row blocks start at the expert's first row and the padding holds zero codes.  Columns
+// past the last expert are zero.  One block per (64 columns, 128 padded positions): the
+// 128 x 64 tile of X is staged through LDS with 16-byte row loads, then each thread
+// quantises one column's 32-row block and writes its 32 codes (the four blocks of a column
+// fill one 128-byte line).  A 128-position block never straddles two experts.
+constexpr int TOK_PAD = 128, TOK_COLS = 64;
+
+// rcodes / rscales (optional): the same tile also quantised along its rows (C), written in
+// X's own layout [R, C] and [R, C/32] -- the dgrad operand -- from the one read of X.
+__global__ __launch_bounds__(256) void mx_quantize_tok_kernel(const bf16_t* __restrict__ X, int R,
+                                                              int C,
+                                                              const int32_t* __restrict__ offsets,
+                                                              int E, int Kp,
+                                                              uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales,
+                                                              uint8_t* __restrict__ rcodes,
+                                                              uint8_t* __restrict__ rscales) {
+    __shared__ bf16_t tile[TOK_PAD][TOK_COLS + 8];
+    const int lane = threadIdx.x & 63;
+    const int p = blockIdx.y * TOK_PAD;  // padded position of this block's first row
+    const int c0 = blockIdx.x * TOK_COLS;
+    int e = -1, P = 0, run = 0;
+    for (int base = 0; base < E && e < 0; base += 64) {
+        const int x = base + lane;
+        int v = 0;
+        if (x < E) {
+            const int lo = min(max(offsets[x], 0), R);
+            const int hi = min(max(offsets[x + 1], lo), R);
+            v = (hi - lo + TOK_PAD - 1) / TOK_PAD * TOK_PAD;
+        }
+        const int inc = wave_incl_scan(v) + run;
+        const uint64_t m = __ballot(x < E && inc > p);
+        if (m) {
+            const int l = __ffsll((unsigned long long)m) - 1;
+            e = base + l;
+            P = __shfl(inc - v, l, 64);
+        }
+        run = __shfl(inc, 63, 64);
+    }
+    int lo = 0, cnt = 0;
+    if (e >= 0) {
+        lo = min(max(offsets[e], 0), R);
+        cnt = min(max(offsets[e + 1], lo), R) - lo;
+    }
+    const int t0 = p - P;  // the block's first row within the expert
+    // stage 128 rows x 64 columns: 8 chunks of 8 values per row, 4 chunks per thread
+    for (int i = threadIdx.x; i < TOK_PAD * (TOK_COLS / 8); i += 256) {
+        const int r = i / (TOK_COLS / 8), ch = i % (TOK_COLS / 8);
+        const int col = c0 + ch * 8;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (e >= 0 && t0 + r < cnt && col < C) v = ld16(X + (int64_t)(lo + t0 + r) * C + col);
+        *reinterpret_cast<u32x4*>(&tile[r][ch * 8]) = v;
+    }
+    __syncthreads();
+    if (rcodes) {  // along the rows: thread -> (tile row, 32-column half)
+        const int rr = threadIdx.x >> 1, half = threadIdx.x & 1, cb = c0 + half * 32;
+        if (e >= 0 && t0 + rr < cnt && cb < C) {
+            float w[32];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) w[i] = __uint_as_float((uint32_t)tile[rr][half * 32 + i] << 16);
+            uint32_t q[8];
+            const int sc = mx_block(w, MOE_MX_FLOOR, q);
+            const int64_t row = lo + t0 + rr;
+            uint8_t* out = rcodes + row * C + cb;
+            st16(out, u32x4{q[0], q[1], q[2], q[3]});
+            st16(out + 16, u32x4{q[4], q[5], q[6], q[7]});
+            rscales[row * (C / 32) + cb / 32] = (uint8_t)sc;
+        }
+    }
+    const int cl = threadIdx.x & (TOK_COLS - 1), blk = threadIdx.x / TOK_COLS;
+    const int col = c0 + cl;
+    if (col >= C) return;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = __uint_as_float((uint32_t)tile[blk * 32 + i][cl] << 16);
+    uint32_t q[8];
+    const int sc = mx_block(v, MOE_MX_FLOOR, q);
+    uint8_t* out = codes + (int64_t)col * Kp + p + blk * 32;
+    st16(out, u32x4{q[0], q[1], q[2], q[3]});
+    st16(out + 16, u32x4{q[4], q[5], q[6], q[7]});
+    scales[(int64_t)col * (Kp / 32) + p / 32 + blk] = (uint8_t)sc;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -484,149 +640,21 @@ extern "C" int mx_quantize(const void* in, int in_dtype, int rows, int K, uint8_
     hipStream_t st = (hipStream_t)stream;
     MOE_TRACED("mx_quantize", st,
                if (in_dtype == MOE_F32)
-                   mx_quantize_kernel<true><<<grid, 256, 0, st>>>(in, nb, scale_mode, codes, scales);
+                   mx_quantize_kernel<true><<<grid, 256, 0, st>>>(in, nb, scale_mode, codes, scales, nullptr);
                else
-                   mx_quantize_kernel<false><<<grid, 256, 0, st>>>(in, nb, scale_mode, codes, scales));
+                   mx_quantize_kernel<false><<<grid, 256, 0, st>>>(in, nb, scale_mode, codes, scales, nullptr));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
 
-// ------------------------------------------------------------------ mx_quantize_t
-// Quantisation along the first dimension of each [A, B] matrix of a batch, written transposed:
-// codes [batch][B][A], scales [batch][B][A/32].  One thread per (column, 32-row block): it
-// reads its column's 32 values (consecutive threads read consecutive columns, so every row
-// access is coalesced) and writes the block's 32 codes as two 16-byte stores.
-__global__ __launch_bounds__(256) void mx_quantize_t_kernel(const bf16_t* __restrict__ in, int A,
-                                                            int B, int mode,
-                                                            uint8_t* __restrict__ codes,
-                                                            uint8_t* __restrict__ scales) {
-    const int col = blockIdx.x * blockDim.x + threadIdx.x;
-    const int ab = blockIdx.y;            // 32-row block
-    const int64_t m = blockIdx.z;         // matrix of the batch
-    if (col >= B) return;
-    const bf16_t* p = in + (m * A + (int64_t)ab * 32) * B + col;
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = __uint_as_float((uint32_t)p[(int64_t)i * B] << 16);
-    uint32_t q[8];
-    const int sc = mx_block(v, mode, q);
-    uint8_t* out = codes + (m * B + col) * A + ab * 32;
-    st16(out, u32x4{q[0], q[1], q[2], q[3]});
-    st16(out + 16, u32x4{q[4], q[5], q[6], q[7]});
-    scales[(m * B + col) * (A / 32) + ab] = (uint8_t)sc;
-}
-
-// ------------------------------------------------------------------ mx_dequantize
-// One thread per 32-value block: value = E4M3(code) * 2^(scale - 127), rounded to bf16
-// (exact for every normal bf16 value: a code has 3 mantissa bits).
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    float v;
-    if (e == 15u && m == 7u) v = __uint_as_float(0x7FC00000u);        // NaN
-    else if (e == 0u) v = (float)m * (1.0f / 512.0f);                // subnormal: m 2^-9
-    else v = __uint_as_float(((e + 120u) << 23) | (m << 20));        // 2^(e-7) (1 + m/8)
-    return (c & 0x80u) ? -v : v;
-}
-
-__global__ __launch_bounds__(256) void mx_dequantize_kernel(const uint8_t* __restrict__ codes,
-                                                            const uint8_t* __restrict__ scales,
-                                                            int64_t nblocks,
-                                                            bf16_t* __restrict__ out) {
-    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= nblocks) return;
-    const float f = ldexpf(1.0f, (int)scales[b] - 127);
-    const u32x4 c0 = ld16(codes + b * 32), c1 = ld16(codes + b * 32 + 16);
-    uint32_t w[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t word = i < 4 ? c0[i] : c1[i - 4];
-        const float a = e4m3_value(word & 0xFFu) * f, b2 = e4m3_value((word >> 8) & 0xFFu) * f;
-        const float c = e4m3_value((word >> 16) & 0xFFu) * f, d = e4m3_value(word >> 24) * f;
-        w[2 * i] = pack_bf2(a, b2);
-        w[2 * i + 1] = pack_bf2(c, d);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        st16(out + b * 32 + 8 * i, u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]});
-}
-
-// ------------------------------------------------------------------ token-axis quantisation
-// The weight-gradient operands of the MXFP8 backward: X [R, C] (routed rows in expert order)
-// quantised along the rows of each expert, written transposed as codes [C][Kp] and scales
-// [C][Kp/32].  Expert e's rows occupy the code columns [P_e, P_e + pad(cnt_e)), where pad
-// rounds up to a whole K step (128) and P_e is the sum of the padded counts before e; the
-// 32-row blocks start at the expert's first row and the padding holds zero codes.  Columns
-// past the last expert are zero.  One block per (64 columns, 128 padded positions): the
-// 128 x 64 tile of X is staged through LDS with 16-byte row loads, then each thread
-// quantises one column's 32-row block and writes its 32 codes (the four blocks of a column
-// fill one 128-byte line).  A 128-position block never straddles two experts.
-constexpr int TOK_PAD = 128, TOK_COLS = 64;
-
-__global__ __launch_bounds__(256) void mx_quantize_tok_kernel(const bf16_t* __restrict__ X, int R,
-                                                              int C,
-                                                              const int32_t* __restrict__ offsets,
-                                                              int E, int Kp,
-                                                              uint8_t* __restrict__ codes,
-                                                              uint8_t* __restrict__ scales) {
-    __shared__ bf16_t tile[TOK_PAD][TOK_COLS + 8];
-    const int lane = threadIdx.x & 63;
-    const int p = blockIdx.y * TOK_PAD;  // padded position of this block's first row
-    const int c0 = blockIdx.x * TOK_COLS;
-    int e = -1, P = 0, run = 0;
-    for (int base = 0; base < E && e < 0; base += 64) {
-        const int x = base + lane;
-        int v = 0;
-        if (x < E) {
-            const int lo = min(max(offsets[x], 0), R);
-            const int hi = min(max(offsets[x + 1], lo), R);
-            v = (hi - lo + TOK_PAD - 1) / TOK_PAD * TOK_PAD;
-        }
-        const int inc = wave_incl_scan(v) + run;
-        const uint64_t m = __ballot(x < E && inc > p);
-        if (m) {
-            const int l = __ffsll((unsigned long long)m) - 1;
-            e = base + l;
-            P = __shfl(inc - v, l, 64);
-        }
-        run = __shfl(inc, 63, 64);
-    }
-    int lo = 0, cnt = 0;
-    if (e >= 0) {
-        lo = min(max(offsets[e], 0), R);
-        cnt = min(max(offsets[e + 1], lo), R) - lo;
-    }
-    const int t0 = p - P;  // the block's first row within the expert
-    // stage 128 rows x 64 columns: 8 chunks of 8 values per row, 4 chunks per thread
-    for (int i = threadIdx.x; i < TOK_PAD * (TOK_COLS / 8); i += 256) {
-        const int r = i / (TOK_COLS / 8), ch = i % (TOK_COLS / 8);
-        const int col = c0 + ch * 8;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (e >= 0 && t0 + r < cnt && col < C) v = ld16(X + (int64_t)(lo + t0 + r) * C + col);
-        *reinterpret_cast<u32x4*>(&tile[r][ch * 8]) = v;
-    }
-    __syncthreads();
-    const int cl = threadIdx.x & (TOK_COLS - 1), blk = threadIdx.x / TOK_COLS;
-    const int col = c0 + cl;
-    if (col >= C) return;
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = __uint_as_float((uint32_t)tile[blk * 32 + i][cl] << 16);
-    uint32_t q[8];
-    const int sc = mx_block(v, MOE_MX_FLOOR, q);
-    uint8_t* out = codes + (int64_t)col * Kp + p + blk * 32;
-    st16(out, u32x4{q[0], q[1], q[2], q[3]});
-    st16(out + 16, u32x4{q[4], q[5], q[6], q[7]});
-    scales[(int64_t)col * (Kp / 32) + p / 32 + blk] = (uint8_t)sc;
-}
-
 int moe_launch_mx_quantize_tok(const bf16_t* X, int R, int C, const int32_t* offsets, int E,
-                               int Kp, uint8_t* codes, uint8_t* scales, const char* name,
-                               hipStream_t st) {
+                               int Kp, uint8_t* codes, uint8_t* scales, uint8_t* rcodes,
+                               uint8_t* rscales, const char* name, hipStream_t st) {
     if (Kp == 0 || C == 0) return MOE_OK;
     const dim3 grid((unsigned)((C + TOK_COLS - 1) / TOK_COLS), (unsigned)(Kp / TOK_PAD));
     MOE_TRACED(name, st,
                mx_quantize_tok_kernel<<<grid, 256, 0, st>>>(X, R, C, offsets, E, Kp, codes,
-                                                            scales));
+                                                            scales, rcodes, rscales));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -706,18 +734,18 @@ int moe_launch_mx_quantize_bf16(const bf16_t* in, int64_t rows, int K, uint8_t* 
     if (nb == 0) return MOE_OK;
     MOE_TRACED(name, st,
                mx_quantize_kernel<false><<<(unsigned)((nb + 255) / 256), 256, 0, st>>>(
-                   in, nb, MOE_MX_FLOOR, codes, scales));
+                   in, nb, MOE_MX_FLOOR, codes, scales, nullptr));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
 
 int moe_launch_mx_quantize_f32(const float* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
-                               hipStream_t st) {
+                               bf16_t* deq, hipStream_t st) {
     int64_t nb = rows * (K / 32);
     if (nb == 0) return MOE_OK;
     MOE_TRACED("mx_quantize_h", st,
                mx_quantize_kernel<true><<<(unsigned)((nb + 255) / 256), 256, 0, st>>>(
-                   in, nb, MOE_MX_FLOOR, codes, scales));
+                   in, nb, MOE_MX_FLOOR, codes, scales, deq));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
