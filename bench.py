@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_ep64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=16,
+    ap.add_argument("--cpu-tokens", type=int, default=48,
                     help="source tokens of the CPU-oracle sample")
     ap.add_argument("--breakdown", action="store_true",
                     help="also print per-role times to stderr")
