@@ -40,6 +40,7 @@ PEAK_HBM_GBS = 8000.0
 
 GEMM_ROLES = {  # role -> (flops per routed row in units of H*I, MX)
     "gemm1_swiglu": (4, False), "gemm2_down": (2, False),
+    "ffn_queue": (6, False),      # GEMM1 + SwiGLU and GEMM2 as one launch (tile queue)
     "bwd_down": (4, False),       # dh = dy W2 (+ SwiGLU backward) and dW2 = dy^T h
     "bwd_gate_up": (8, False),    # dXp = dGU W1 and dW1 = dGU^T Xp
     "mx_gemm1_swiglu": (4, True), "mx_gemm2_down": (2, True),

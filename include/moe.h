@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 /* return codes */
 #define MOE_OK 0
@@ -149,8 +149,18 @@ int moe_dispatch(const void *x, int T, int H, int k, const int32_t *src, const i
  *   y [R,H] bf16 (routed rows, expert order).
  * Limits: H % 64 == 0, I % 64 == 0 (both % 128 for MOE_MXFP8), offsets non-decreasing with
  * offsets[E] <= R.
- * Workspace: moe_ffn_workspace_size(). */
+ * Workspace: moe_ffn_workspace_size().  MOE_MXFP8 always needs it.  MOE_BF16 with a workspace
+ *   of that size and gu_save == NULL runs both products as ONE launch: a queue of GEMM1 and
+ *   GEMM2 tiles in which a GEMM2 tile waits only for the GEMM1 tiles of its own rows
+ *   (per-row-block counters in the workspace, cleared by a small kernel before the launch),
+ *   so the second product fills the first one's last, partial round.  With gu_save, or
+ *   without a workspace (h_save given), the two products run as two launches.  Both forms
+ *   give bit-identical outputs.  A queue wait is bounded (2 s):
+ *   past it the uint32 at byte moe_ffn_error_offset() of the workspace becomes nonzero (it is
+ *   zero after every good call with R > 0) and the outputs are not valid.  Calls that share a
+ *   workspace must be stream-ordered. */
 size_t moe_ffn_workspace_size(int dtype, int E, int R, int H, int I, int shared);
+size_t moe_ffn_error_offset(void);
 int moe_expert_ffn(int dtype, const void *xp, const uint8_t *xp_scales, const int32_t *offsets,
                    int E, int R, int H, int I, const void *w1, const uint8_t *w1_scales,
                    const void *w2, const uint8_t *w2_scales, void *gu_save, void *h_save,

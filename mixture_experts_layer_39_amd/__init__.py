@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.moe_update_bias.argtypes = [_vp, _i, ctypes.c_float, _vp, _vp]
         L.moe_ffn_workspace_size.restype = _sz
         L.moe_ffn_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i]
+        L.moe_ffn_error_offset.restype = _sz
+        L.moe_ffn_error_offset.argtypes = []
         L.moe_expert_ffn.argtypes = [_i, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
                                      _vp, _vp, _vp, _sz, _vp]
         L.moe_combine.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _vp, _vp]
@@ -167,6 +169,12 @@ def moe_dispatch(x, T, H, k, src, R, xp=None, xp_codes=None, xp_scales=None, str
 
 def ffn_workspace_size(dtype, E, R, H, I, shared=False) -> int:
     return lib().moe_ffn_workspace_size(dtype, E, R, H, I, int(shared))
+
+
+def ffn_error(ws) -> int:
+    """The one-launch FFN's error word in `ws` (0: every wait completed).  Reads the device."""
+    off = lib().moe_ffn_error_offset()
+    return int(ws[off:off + 4].view(torch.int32).item())
 
 
 def moe_expert_ffn(dtype, xp, offsets, E, R, H, I, w1, w2, y, *, xp_scales=None,

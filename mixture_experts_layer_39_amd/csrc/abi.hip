@@ -11,6 +11,12 @@ using moe::bf16_t;
 int moe_ffn_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, int I,
                  const bf16_t* w1, const bf16_t* w2, bf16_t* gu, bf16_t* h, bf16_t* y,
                  hipStream_t st);
+int64_t moe_ffn_row_blocks(int E, int R, bool shared);
+size_t moe_ffn_sync_bytes(int E, int R, bool shared);
+size_t moe_ffn_error_word();
+int moe_ffn_bf16_queue(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, int I,
+                       const bf16_t* w1, const bf16_t* w2, bf16_t* gu, bf16_t* h, bf16_t* y,
+                       unsigned* sy, hipStream_t st);
 int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, int I,
                      const bf16_t* w1, const bf16_t* w2, const bf16_t* gu, const bf16_t* h,
                      const bf16_t* dy, bf16_t* dgu, bf16_t* dxp, const MoeWgradSpan* wg,
@@ -133,8 +139,11 @@ extern "C" size_t moe_ffn_workspace_size(int dtype, int E, int R, int H, int I, 
     if (dtype == MOE_MXFP8)
         return moe_align256(rows * I * 4) + moe_align256(rows * I) +
                moe_align256(rows * (I / 32)) + moe_mx_panel_bytes(E, R, H, I, shared != 0) + 256;
-    return moe_align256(rows * I * 2) + 256;
+    // BF16: the synchronisation words of the one-launch queue, then room for h
+    return moe_ffn_sync_bytes(E, R, shared != 0) + moe_align256(rows * I * 2) + 256;
 }
+
+extern "C" size_t moe_ffn_error_offset(void) { return moe_ffn_error_word(); }
 
 extern "C" int moe_expert_ffn(int dtype, const void* xp, const uint8_t* xp_scales,
                               const int32_t* offsets, int E, int R, int H, int I, const void* w1,
@@ -152,17 +161,31 @@ extern "C" int moe_expert_ffn(int dtype, const void* xp, const uint8_t* xp_scale
         MOE_REQUIRE(!xp_scales && !w1_scales && !w2_scales);
     }
     size_t need = moe_ffn_workspace_size(dtype, E, R, H, I, offsets == nullptr);
+    const bool have_ws = ws && ws_bytes >= need;
     const bool need_ws = dtype == MOE_MXFP8 || h_save == nullptr;
-    if (need_ws && (!ws || ws_bytes < need)) return MOE_EWORKSPACE;
+    if (need_ws && !have_ws) return MOE_EWORKSPACE;
     if (R == 0) return MOE_OK;
     int rc = moe_check_device();
     if (rc) return rc;
     hipStream_t st = (hipStream_t)stream;
     size_t rows = offsets ? (size_t)R : (size_t)E * R;
     if (dtype == MOE_BF16) {
-        bf16_t* h = h_save ? (bf16_t*)h_save : (bf16_t*)ws;
-        return moe_ffn_bf16((const bf16_t*)xp, offsets, E, R, H, I, (const bf16_t*)w1,
-                            (const bf16_t*)w2, (bf16_t*)gu_save, h, (bf16_t*)y, st);
+        // The one-launch queue makes every GEMM1 tile write its XCD's L2 back before it
+        // counts itself done; with the g|u saves that flush also carries the saves' dirty
+        // lines and measured slower than two launches (1.29 against 1.27 ms at the EP-64
+        // share), without them faster (1.21 against 1.23 ms).  So: saves -> two launches.
+        if (!have_ws || gu_save)
+            return moe_ffn_bf16((const bf16_t*)xp, offsets, E, R, H, I, (const bf16_t*)w1,
+                                (const bf16_t*)w2, (bf16_t*)gu_save,
+                                h_save ? (bf16_t*)h_save
+                                       : (bf16_t*)((char*)ws + moe_ffn_sync_bytes(
+                                                              E, R, offsets == nullptr)),
+                                (bf16_t*)y, st);
+        const size_t sync = moe_ffn_sync_bytes(E, R, offsets == nullptr);
+        bf16_t* h = h_save ? (bf16_t*)h_save : (bf16_t*)((char*)ws + sync);
+        return moe_ffn_bf16_queue((const bf16_t*)xp, offsets, E, R, H, I, (const bf16_t*)w1,
+                                  (const bf16_t*)w2, (bf16_t*)gu_save, h, (bf16_t*)y,
+                                  (unsigned*)ws, st);
     }
     char* p = (char*)ws;
     float* hf = (float*)p;

@@ -39,6 +39,15 @@ __device__ __forceinline__ float hi_bf(uint32_t v) { return __uint_as_float(v & 
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Non-temporal forms, for rows that a kernel reads or writes exactly once: they neither
+// allocate in nor evict from the caches, so a stream over hundreds of MB does not first have
+// to push other kernels' dirty lines out to HBM.
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 
 
 // Wave-level inclusive scan (sum) of an int over 64 lanes, fixed order.

@@ -865,6 +865,58 @@ void layer_forward_fused(FusedFwd a) {
                                     t, lane);
 }
 
+// ---------------------------------------------------------------- the FFN in one launch
+// GEMM1 + SwiGLU and GEMM2 of one moe_expert_ffn call (BF16) as one queue of tiles, the
+// product queue of layer_forward_fused on its own: a GEMM2 tile waits only for the GEMM1
+// tiles of its row block (per-row-block counters), so GEMM2 tiles fill the last, partial
+// round of GEMM1 tiles instead of waiting for a second launch.  Every item is claimed from a
+// counter, the first one included: a tile is then only ever held by a running block, and a
+// GEMM2 tile waits only for GEMM1 tiles claimed before it, which never wait themselves.  The
+// queue cannot deadlock however many of the blocks are resident, so an ordinary launch of
+// one block per CU serves.  Same tile code as gemm1_swiglu / gemm2_down: bit-identical
+// outputs.  The synchronisation words (sy) are cleared by ffn_queue_clear just before.
+struct FfnQueue {
+    GemmArgs g1, g2;
+    unsigned* sy;
+};
+
+__global__ void ffn_queue_clear(unsigned* sy, int words) {
+    for (int i = threadIdx.x; i < words; i += blockDim.x) sy[i] = 0;
+}
+
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ffn_queue(FfnQueue q) {
+    __shared__ GemmSmem sm;
+    unsigned* const ready = q.sy + SY_READY;
+    const int n1 = tile_total<EPI_SWIGLU, false>(q.g1);
+    const int total = n1 + tile_total<EPI_STORE, false>(q.g2);
+    const unsigned nt1 = (unsigned)n_tiles<EPI_SWIGLU>(q.g1);
+    int* const bcast = reinterpret_cast<int*>(sm.st + LDS_BYTES - 16);
+    for (;;) {
+        if (threadIdx.x == 0)
+            *bcast = (int)__hip_atomic_fetch_add(q.sy + SY_CLAIM, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int item = *bcast;
+        __syncthreads();
+        if (item >= total) break;
+        if (item < n1) {
+            const TileAt at = tile_at<EPI_SWIGLU, false>(q.g1, item);
+            gemm_tile<BK_FWD, true, true, EPI_SWIGLU, false>(q.g1, sm, at);
+            tile_done(ready, at.mblock);
+        } else {
+            const TileAt at = tile_at<EPI_STORE, false>(q.g2, item - n1);
+            if (threadIdx.x == 0) {
+                spin_until(ready + at.mblock, nt1, q.sy);
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            }
+            __syncthreads();
+            gemm_tile<BK_FWD, true, true, EPI_STORE, false>(q.g2, sm, at);
+        }
+        __syncthreads();
+    }
+}
+
 static GemmArgs blank() {
     GemmArgs g{};
     return g;
@@ -904,6 +956,42 @@ int moe_ffn_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, 
     int rc = launch(gemm1_swiglu, "gemm1_swiglu", g, cdiv(I, 128), st);
     if (rc) return rc;
     return launch(gemm2_down, "gemm2_down", g2, cdiv(H, BN), st);
+}
+
+// Row blocks of one FFN call (the per-row-block counters of ffn_queue): an upper bound for
+// ragged experts, E * cdiv(R, BM) for shared ones.
+int64_t moe_ffn_row_blocks(int E, int R, bool shared) {
+    return shared ? (int64_t)E * cdiv(R, BM) : ((int64_t)R + (int64_t)E * (BM - 1)) / BM;
+}
+
+size_t moe_ffn_sync_bytes(int E, int R, bool shared) {
+    return moe_align256((size_t)(SY_READY + moe_ffn_row_blocks(E, R, shared)) * 4);
+}
+
+size_t moe_ffn_error_word() { return SY_ERR * 4; }
+
+// The same products as moe_ffn_bf16 as one launch (ffn_queue); sy: moe_ffn_sync_bytes().
+int moe_ffn_bf16_queue(const bf16_t* xp, const int32_t* offsets, int E, int R, int H, int I,
+                       const bf16_t* w1, const bf16_t* w2, bf16_t* gu, bf16_t* h, bf16_t* y,
+                       unsigned* sy, hipStream_t st) {
+    FfnQueue q{};
+    ffn_args(xp, offsets, E, R, H, I, w1, w2, gu, h, y, q.g1, q.g2);
+    q.sy = sy;
+    const int64_t tiles = (int64_t)grid_of(q.g1, cdiv(I, 128), false) +
+                          grid_of(q.g2, cdiv(H, BN), false);
+    if (tiles <= 0) return MOE_OK;
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        ncu < 1)
+        return MOE_EHIP;
+    const int grid = (int)std::min<int64_t>(tiles, ncu);  // one block per CU (LDS)
+    const int words = (int)(SY_READY + moe_ffn_row_blocks(E, R, offsets == nullptr));
+    MOE_TRACED("ffn_queue_clear", st, ffn_queue_clear<<<1, 1024, 0, st>>>(sy, words));
+    MOE_LAUNCH_CHECK();
+    MOE_TRACED("ffn_queue", st, ffn_queue<<<grid, NTH, 0, st>>>(q));
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
 }
 
 // Synchronisation words of the single launch: the fixed words and the GEMM1 counter of every

@@ -238,14 +238,22 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict
 // One block per token.  Per element, fp32: acc = 0; acc += w[t,j]*y[pos[t,j]] for j = 0..k-1;
 // acc += ys[s,t] for s = 0..S-1; one rounding to bf16.
 
-__global__ __launch_bounds__(128) void combine_kernel(const bf16_t* __restrict__ y,
-                                                      const int32_t* __restrict__ pos,
-                                                      const float* __restrict__ w, int T, int k,
-                                                      int H, int R, const bf16_t* __restrict__ ys,
-                                                      int S, bf16_t* __restrict__ out) {
+// The block size is the smallest multiple of 64 threads (at most 512) that covers the row in
+// one pass of RG chunks per thread: 448 for H = 7168, 128 for H = 2048.
+template <int NTHR>
+__global__ __launch_bounds__(NTHR) void combine_kernel(const bf16_t* __restrict__ y,
+                                                       const int32_t* __restrict__ pos,
+                                                       const float* __restrict__ w, int T, int k,
+                                                       int H, int R, const bf16_t* __restrict__ ys,
+                                                       int S, bf16_t* __restrict__ out) {
     __shared__ int sp[MAXK];
     __shared__ float sw[MAXK];
-    combine_token<128>(y, pos, w, T, k, H, R, ys, S, out, blockIdx.x, sp, sw);
+    combine_token<NTHR>(y, pos, w, T, k, H, R, ys, S, out, blockIdx.x, sp, sw);
+}
+
+static int combine_threads(int H) {
+    const int per_pass = (H / 8 + RG - 1) / RG;
+    return std::min(512, std::max(64, (per_pass + 63) / 64 * 64));
 }
 
 // ------------------------------------------------------------------ combine backward
@@ -279,7 +287,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restri
                 for (int u = 0; u < CB_UN; ++u) {
                     const int c = c0 + u * 256;
                     g[u] = c < nc ? ld16(g_row + c * 8) : u32x4{0, 0, 0, 0};
-                    v[u] = c < nc ? ld16(y_row + c * 8) : u32x4{0, 0, 0, 0};
+                    v[u] = c < nc ? ld16_nt(y_row + c * 8) : u32x4{0, 0, 0, 0};
                 }
 #pragma unroll
                 for (int u = 0; u < CB_UN; ++u) {
@@ -310,8 +318,10 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restri
 }
 
 // ------------------------------------------------------------------ un-permute reduce
-// dx[t,:] = sum_j dxp[pos[t,j],:] + sum_s dxs[s,t,:], fp32 in that order, one rounding.
-__global__ __launch_bounds__(128) void unpermute_kernel(const bf16_t* __restrict__ dxp,
+// dx[t,:] = sum_j dxp[pos[t,j],:] + sum_s dxs[s,t,:], fp32 in that order, one rounding.  As
+// the combine: block size from H, rows read and written once with non-temporal accesses.
+template <int NTHR>
+__global__ __launch_bounds__(NTHR) void unpermute_kernel(const bf16_t* __restrict__ dxp,
                                                         const int32_t* __restrict__ pos, int T,
                                                         int k, int H, int R,
                                                         const bf16_t* __restrict__ dxs, int S,
@@ -326,7 +336,7 @@ __global__ __launch_bounds__(128) void unpermute_kernel(const bf16_t* __restrict
     const int nc = H / 8;
     // each thread takes RG chunks per pass and loads every slot's rows of them before
     // summing any (the summation order per element is unchanged)
-    for (int c0 = threadIdx.x; c0 < nc; c0 += 128 * RG) {
+    for (int c0 = threadIdx.x; c0 < nc; c0 += NTHR * RG) {
         float acc[RG][8];
 #pragma unroll
         for (int g = 0; g < RG; ++g)
@@ -338,9 +348,9 @@ __global__ __launch_bounds__(128) void unpermute_kernel(const bf16_t* __restrict
             for (int g = 0; g < RG; ++g)
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
-                    const int j = j0 + u, c = c0 + g * 128;
+                    const int j = j0 + u, c = c0 + g * NTHR;
                     const int p = j < k ? sp[j] : -1;
-                    v[g][u] = (p >= 0 && c < nc) ? ld16(dxp + (size_t)p * H + c * 8) : u32x4{0, 0, 0, 0};
+                    v[g][u] = (p >= 0 && c < nc) ? ld16_nt(dxp + (size_t)p * H + c * 8) : u32x4{0, 0, 0, 0};
                 }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -357,10 +367,10 @@ __global__ __launch_bounds__(128) void unpermute_kernel(const bf16_t* __restrict
         }
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
-            const int c = c0 + g * 128;
+            const int c = c0 + g * NTHR;
             if (c >= nc) continue;
             for (int s = 0; s < S; ++s) {
-                u32x4 v = ld16(dxs + ((size_t)s * ldT + t) * H + c * 8);
+                u32x4 v = ld16_nt(dxs + ((size_t)s * ldT + t) * H + c * 8);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     acc[g][2 * q] = __fadd_rn(acc[g][2 * q], lo_bf(v[q]));
@@ -370,7 +380,7 @@ __global__ __launch_bounds__(128) void unpermute_kernel(const bf16_t* __restrict
             u32x4 o;
 #pragma unroll
             for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[g][2 * q], acc[g][2 * q + 1]);
-            st16(dx + (size_t)t * H + c * 8, o);
+            st16_nt(dx + (size_t)t * H + c * 8, o);
         }
     }
 }
@@ -619,9 +629,19 @@ extern "C" int moe_combine(const void* y, const int32_t* pos, const float* w, in
     int rc = moe_check_device();
     if (rc) return rc;
     hipStream_t st = (hipStream_t)stream;
-    MOE_TRACED("combine", st,
-               combine_kernel<<<T, 128, 0, st>>>((const bf16_t*)y, pos, w, T, k, H, R,
-                                                 (const bf16_t*)ys, S, (bf16_t*)out));
+    const bf16_t *yb = (const bf16_t*)y, *ysb = (const bf16_t*)ys;
+    bf16_t* ob = (bf16_t*)out;
+#define MOE_COMBINE_CASE(N)                                                                  \
+    case N:                                                                                  \
+        MOE_TRACED("combine", st,                                                            \
+                   combine_kernel<N><<<T, N, 0, st>>>(yb, pos, w, T, k, H, R, ysb, S, ob)); \
+        break;
+    switch (combine_threads(H)) {
+        MOE_COMBINE_CASE(64) MOE_COMBINE_CASE(128) MOE_COMBINE_CASE(192) MOE_COMBINE_CASE(256)
+        MOE_COMBINE_CASE(320) MOE_COMBINE_CASE(384) MOE_COMBINE_CASE(448) MOE_COMBINE_CASE(512)
+        default: return MOE_EINVAL;
+    }
+#undef MOE_COMBINE_CASE
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -711,8 +731,18 @@ int moe_launch_combine_bwd(const bf16_t* dout, const bf16_t* y, const int32_t* p
 int moe_launch_unpermute(const bf16_t* dxp, const int32_t* pos, int T, int k, int H, int R,
                          const bf16_t* dxs, int S, int ldT, bf16_t* dx, hipStream_t st) {
     if (T == 0) return MOE_OK;
-    MOE_TRACED("unpermute", st,
-               unpermute_kernel<<<T, 128, 0, st>>>(dxp, pos, T, k, H, R, dxs, S, ldT, dx));
+#define MOE_UNPERMUTE_CASE(N)                                                               \
+    case N:                                                                                 \
+        MOE_TRACED("unpermute", st,                                                         \
+                   unpermute_kernel<N><<<T, N, 0, st>>>(dxp, pos, T, k, H, R, dxs, S, ldT, dx)); \
+        break;
+    switch (combine_threads(H)) {
+        MOE_UNPERMUTE_CASE(64) MOE_UNPERMUTE_CASE(128) MOE_UNPERMUTE_CASE(192)
+        MOE_UNPERMUTE_CASE(256) MOE_UNPERMUTE_CASE(320) MOE_UNPERMUTE_CASE(384)
+        MOE_UNPERMUTE_CASE(448) MOE_UNPERMUTE_CASE(512)
+        default: return MOE_EINVAL;
+    }
+#undef MOE_UNPERMUTE_CASE
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

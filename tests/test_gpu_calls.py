@@ -251,3 +251,63 @@ def test_expert_ffn_mxfp8_parity():
     dq = lambda a: orc.mx_dequantize(*orc.mx_quantize(a))
     ry, _, _ = orc.ffn_fwd(dq(bf(xp)), np.array(off, np.int32), dq(bf(w1)), dq(bf(w2)), h_mx=True)
     assert_close(bf(y), ry, TOL_MX, "y_mx")
+
+
+def _ffn_forms(E, R, H, I, off, seed):
+    """The BF16 FFN in its three forms: two launches without a workspace (h and g|u saved),
+    two launches with a workspace (the g|u save keeps them), and one queue launch (workspace,
+    no g|u save).  Returns (y, gu, h, ws) of each."""
+    xp, w1, w2 = _ffn_case(E, R, H, I, off, seed)
+    offs = torch.tensor(off, dtype=torch.int32, device=DEV)
+    outs = []
+    for use_ws, save_gu in ((False, True), (True, True), (True, False)):
+        y = torch.full((R, H), -1.0, dtype=torch.bfloat16, device=DEV)
+        gu = torch.full((R, 2 * I), -1.0, dtype=torch.bfloat16, device=DEV) if save_gu else None
+        h = torch.full((R, I), -1.0, dtype=torch.bfloat16, device=DEV)
+        ws = None
+        if use_ws:  # garbage in the workspace: the call clears what it needs
+            ws = torch.full((moe.ffn_workspace_size(moe.BF16, E, R, H, I),), 0xA5,
+                            dtype=torch.uint8, device=DEV)
+        moe.moe_expert_ffn(moe.BF16, xp, offs, E, R, H, I, w1, w2, y, gu_save=gu, h_save=h,
+                           ws=ws)
+        torch.cuda.synchronize()
+        outs.append((y, gu, h, ws))
+    return outs
+
+
+@pytest.mark.parametrize("shape", [
+    (5, 512, 320, [0, 300, 300, 813, 999, 1000]),
+    (3, 1024, 384, [0, 256, 512, 1025]),
+    (1, 256, 512, [0, 7]),
+    (4, 7168, 2048, [0, 1322, 9292, 13050, 16384]),  # the EP-64 share's realised loads
+], ids=["ragged", "tails", "one_expert_7_rows", "ep64_share"])
+def test_expert_ffn_one_launch_bit_identical(shape):
+    """One launch of both products (tile queue with per-row-block dependencies) against the
+    two launches: every output bit for bit, the error word zero."""
+    E, H, I, off = shape
+    R = off[-1]
+    print(f"ffn one-launch case E={E} H={H} I={I} R={R}", flush=True)
+    (y0, gu0, h0, _), (y1, gu1, h1, _), (y2, _, h2, ws) = _ffn_forms(E, R, H, I, off, 11)
+    assert moe.ffn_error(ws) == 0
+    assert torch.equal(gu0, gu1)
+    for y, h in ((y1, h1), (y2, h2)):
+        assert torch.equal(y0, y) and torch.equal(h0, h)
+
+
+def test_expert_ffn_one_launch_parity_and_reuse():
+    """The queue form against the oracle; then the same workspace serves a second, smaller
+    call (its counters are cleared again)."""
+    E, H, I = 4, 512, 256
+    off = [0, 700, 700, 1100, 1500]
+    xp, w1, w2 = _ffn_case(E, off[-1], H, I, off, 12)
+    ws = torch.full((moe.ffn_workspace_size(moe.BF16, E, off[-1], H, I),), 0xFF,
+                    dtype=torch.uint8, device=DEV)
+    for offs in (off, [0, 100, 333, 333, 600]):
+        R = offs[-1]
+        y = torch.empty(R, H, dtype=torch.bfloat16, device=DEV)
+        moe.moe_expert_ffn(moe.BF16, xp[:R], torch.tensor(offs, dtype=torch.int32, device=DEV),
+                           E, R, H, I, w1, w2, y, ws=ws)
+        torch.cuda.synchronize()
+        assert moe.ffn_error(ws) == 0
+        ry, _, _ = orc.ffn_fwd(bf(xp[:R]), np.array(offs, np.int32), bf(w1), bf(w2))
+        assert_close(bf(y), ry, TOL_BF16, f"y_queue_R{R}")
