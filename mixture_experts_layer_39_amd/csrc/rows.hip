@@ -32,6 +32,19 @@ __device__ __forceinline__ uint32_t e4m3_rne(float a) {
     return s | code;
 }
 
+// Four values to E4M3 codes packed little-endian (first value in the low byte), by the
+// hardware conversion v_cvt_pk_fp8_f32 (round to nearest even, OCP E4M3FN) after a clamp to
+// +-448: an exhaustive run over every finite fp32 bit pattern on gfx950 gave the same code as
+// e4m3_rne above for each one.  Without the clamp the conversion turns values beyond 448 into
+// NaN codes instead of saturating.  Two instructions per four values instead of about 25 per
+// value: the quantisers become bound by memory rather than by the vector ALU.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    const auto cl = [](float x) { return fmaxf(-448.0f, fminf(x, 448.0f)); };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
+    return (uint32_t)w;
+}
+
 // E8M0 code of a block maximum: floor(log2 amax) - 8 + 127 (MOE_MX_FLOOR) or the smallest
 // exponent keeping amax/2^e <= 448 (MOE_MX_CEIL); clamped to [0,254]; zero block -> 0.
 __device__ __forceinline__ int mx_scale_code(float amax, int mode) {
@@ -61,12 +74,9 @@ __device__ __forceinline__ int mx_block(const float* v, int mode, uint32_t* q) {
     int sc = mx_scale_code(amax, mode);
     int sh = 127 - sc;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) w |= e4m3_rne(ldexpf(v[4 * i + b], sh)) << (8 * b);
-        q[i] = w;
-    }
+    for (int i = 0; i < 8; ++i)
+        q[i] = e4m3x4(ldexpf(v[4 * i], sh), ldexpf(v[4 * i + 1], sh), ldexpf(v[4 * i + 2], sh),
+                      ldexpf(v[4 * i + 3], sh));
     return sc;
 }
 

@@ -145,11 +145,14 @@ def test_dispatch_bit_exact_and_mx():
 
 @pytest.mark.parametrize("mode", [moe.MX_FLOOR, moe.MX_CEIL])
 def test_mx_quantize_bit_exact(mode):
-    # every finite bf16 bit pattern (in shuffled blocks of 32), plus wide-range fp32 values
+    # every finite bf16 bit pattern, in shuffled blocks of 32 (wide range per block) and in
+    # sorted blocks (neighbouring values: normal codes, and saturation at 448 next to each
+    # block maximum in floor mode), plus wide-range fp32 values
     rs = np.random.default_rng(4)
     bits = np.arange(65536, dtype=np.uint16)
     finite = bits[(bits & 0x7F80) != 0x7F80]
-    finite = rs.permutation(finite)[: (len(finite) // 32) * 32].reshape(-1, 32 * 8)
+    n = (len(finite) // 32) * 32
+    finite = np.concatenate([rs.permutation(finite)[:n], np.sort(finite)[:n]]).reshape(-1, 32 * 8)
     t = torch.from_numpy(finite.view(np.int16)).to(DEV).view(torch.bfloat16)
     rows, K = finite.shape
     q = torch.empty(rows, K, dtype=torch.uint8, device=DEV)
