@@ -119,13 +119,23 @@ __device__ __forceinline__ void panel_tile(const uint8_t* __restrict__ sc, int K
     {
         const int c0 = (int)blockIdx.y * PS_COLS;
         __syncthreads();  // srow written
-        // 256 rows x 16 dwords: thread i loads dword i % 16 of row i / 16 (+16 rows per pass)
-        for (int i = tid; i < 256 * (PS_COLS / 4); i += 256) {
+        // 256 rows x 16 dwords: thread i loads dword i % 16 of row i / 16 (+16 rows per pass);
+        // all 16 loads of a thread are issued before its first LDS store
+        constexpr int NLD = PS_COLS / 4;
+        uint32_t v[NLD];
+#pragma unroll
+        for (int u = 0; u < NLD; ++u) {
+            const int i = tid + 256 * u;
             const int row = i / (PS_COLS / 4), col = c0 + 4 * (i % (PS_COLS / 4));
             const int rr = srow[row];
-            uint32_t v = 0;
-            if (rr >= 0 && col < KB) v = *reinterpret_cast<const uint32_t*>(sc + (int64_t)rr * KB + col);
-            *reinterpret_cast<uint32_t*>(&stg[row][col - c0]) = v;
+            v[u] = (rr >= 0 && col < KB) ? *reinterpret_cast<const uint32_t*>(sc + (int64_t)rr * KB + col)
+                                         : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < NLD; ++u) {
+            const int i = tid + 256 * u;
+            const int row = i / (PS_COLS / 4), col = 4 * (i % (PS_COLS / 4));
+            *reinterpret_cast<uint32_t*>(&stg[row][col]) = v[u];
         }
         __syncthreads();
         // entries (half w, step s, lane L): 2 x 16 x 64 per pass, 8 per thread

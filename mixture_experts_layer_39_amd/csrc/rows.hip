@@ -484,15 +484,28 @@ __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const bf16_t* __rest
 // One thread per 32-value block: value = E4M3(code) * 2^(scale - 127), rounded to bf16
 // (exact for every normal bf16 value: a code has 3 mantissa bits).
 
+// One thread per 16 codes (half a block): 16-byte code loads, so a wave reads 1 KB in one
+// piece.  The codes decode with the hardware fp8 -> fp32 conversion (exact for every finite
+// E4M3FN code; the quantisers here never emit the NaN code) and scale by 2^(s-127) in fp32,
+// then round to bf16: the same arithmetic as mx_deq_store, with the decode in hardware.
 __global__ __launch_bounds__(256) void mx_dequantize_kernel(const uint8_t* __restrict__ codes,
                                                             const uint8_t* __restrict__ scales,
                                                             int64_t nblocks,
                                                             bf16_t* __restrict__ out) {
-    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= nblocks) return;
-    const u32x4 c0 = ld16(codes + b * 32), c1 = ld16(codes + b * 32 + 16);
-    const uint32_t q[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-    mx_deq_store(q, scales[b], out + b * 32);
+    const int64_t hb = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // half-block index
+    if (hb >= 2 * nblocks) return;
+    const u32x4 c = ld16_nt(codes + hb * 16);
+    const float f = ldexpf(1.0f, (int)scales[hb >> 1] - 127);
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[i], false);  // bytes 0, 1
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[i], true);   // bytes 2, 3
+        w[2 * i] = pack_bf2(lo[0] * f, lo[1] * f);
+        w[2 * i + 1] = pack_bf2(hi[0] * f, hi[1] * f);
+    }
+    st16(out + hb * 16, u32x4{w[0], w[1], w[2], w[3]});
+    st16(out + hb * 16 + 8, u32x4{w[4], w[5], w[6], w[7]});
 }
 
 // ------------------------------------------------------------------ token-axis quantisation
@@ -545,13 +558,22 @@ __global__ __launch_bounds__(256) void mx_quantize_tok_kernel(const bf16_t* __re
         cnt = min(max(offsets[e + 1], lo), R) - lo;
     }
     const int t0 = p - P;  // the block's first row within the expert
-    // stage 128 rows x 64 columns: 8 chunks of 8 values per row, 4 chunks per thread
-    for (int i = threadIdx.x; i < TOK_PAD * (TOK_COLS / 8); i += 256) {
+    // stage 128 rows x 64 columns: 8 chunks of 8 values per row, 4 chunks per thread, all
+    // four loads issued before the first LDS store
+    constexpr int NLD = TOK_PAD * (TOK_COLS / 8) / 256;
+    u32x4 v4[NLD];
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+        const int i = threadIdx.x + 256 * u;
+        const int r = i / (TOK_COLS / 8), col = c0 + (i % (TOK_COLS / 8)) * 8;
+        v4[u] = (e >= 0 && t0 + r < cnt && col < C) ? ld16_nt(X + (int64_t)(lo + t0 + r) * C + col)
+                                                    : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+        const int i = threadIdx.x + 256 * u;
         const int r = i / (TOK_COLS / 8), ch = i % (TOK_COLS / 8);
-        const int col = c0 + ch * 8;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (e >= 0 && t0 + r < cnt && col < C) v = ld16(X + (int64_t)(lo + t0 + r) * C + col);
-        *reinterpret_cast<u32x4*>(&tile[r][ch * 8]) = v;
+        *reinterpret_cast<u32x4*>(&tile[r][ch * 8]) = v4[u];
     }
     __syncthreads();
     if (rcodes) {  // along the rows: thread -> (tile row, 32-column half)
@@ -711,8 +733,8 @@ int moe_launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_
     const int64_t nb = rows * (K / 32);
     if (nb == 0) return MOE_OK;
     MOE_TRACED("mx_dequantize", st,
-               mx_dequantize_kernel<<<(unsigned)((nb + 255) / 256), 256, 0, st>>>(codes, scales,
-                                                                                  nb, out));
+               mx_dequantize_kernel<<<(unsigned)((2 * nb + 255) / 256), 256, 0, st>>>(
+                   codes, scales, nb, out));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

@@ -39,6 +39,14 @@ def test_dequantize_bit_exact():
     codes = rs.integers(0, 256, size=(rows, K)).astype(np.uint8)
     codes[(codes & 0x7F) == 0x7F] = 0x11           # no NaN codes
     scales = rs.integers(110, 145, size=(rows, K // 32)).astype(np.uint8)
+    # and every non-NaN code under every scale from 100 to 160 (one scale per row)
+    every = np.arange(256, dtype=np.uint8)
+    every = every[(every & 0x7F) != 0x7F]
+    every = np.concatenate([every, every[:K - len(every)]])
+    codes = np.concatenate([codes, np.tile(every, (61, 1))])
+    scales = np.concatenate([scales, np.repeat(np.arange(100, 161, dtype=np.uint8)[:, None],
+                                               K // 32, axis=1)])
+    rows = codes.shape[0]
     out = torch.empty(rows, K, dtype=torch.bfloat16, device=DEV)
     moe.mx_dequantize(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV), rows,
                       K, out)
