@@ -514,14 +514,25 @@ __global__ __launch_bounds__(256) void mx_dequantize_kernel(const uint8_t* __res
 // [C][Kp/32].  Expert e's rows occupy the code columns [P_e, P_e + pad(cnt_e)), where pad
 // rounds up to a whole K step (128) and P_e is the sum of the padded counts before e; the
 // 32-row blocks start at the expert's first row and the padding holds zero codes.  Columns
-// past the last expert are zero.  One block per (64 columns, 128 padded positions): the
-// 128 x 64 tile of X is staged through LDS with 16-byte row loads, then each thread
-// quantises one column's 32-row block and writes its 32 codes (the four blocks of a column
-// fill one 128-byte line).  A 128-position block never straddles two experts.
-constexpr int TOK_PAD = 128, TOK_COLS = 64;
+// past the last expert are zero.  Optionally (rcodes) the same rows are also quantised along
+// C into rcodes [R][C], rscales [R][C/32] (the dgrad operand).  A 128-position block never
+// straddles two experts.
+//
+// One block per (128 columns, 128 padded positions), C % 128 == 0:
+//  1. the 128 x 128 tile of X is staged through LDS with 16-byte row loads (all eight of a
+//     thread's loads issued first);
+//  2. column pass: wave w takes the rows 32w .. 32w+31, lane l the column pair 2l, 2l+1
+//     (one dword LDS read per row: 64 consecutive dwords, conflict-free); row pass: items
+//     (row r, 32-column block b), four lanes per row, 64 contiguous LDS bytes each;
+//  3. the codes and scales go back into LDS as byte images of their output lines
+//     (a column's 128 token codes, a row's 128 column codes, four scale bytes each), and
+//  4. leave as whole 128-byte lines, eight lanes per line, and 4-byte scale words.
+// The element order of every 32-value block, and so every code and scale, is unchanged.
+constexpr int TOK_PAD = 128, TOK_COLS = 128;
+constexpr int TOK_LD = TOK_COLS * 2 + 16;  // bytes per staged input row (16-byte aligned)
+constexpr int TOK_OL = 128 + 16;           // bytes per staged output line
+constexpr int TOK_LDS = 2 * TOK_PAD * TOK_OL + 2 * 128 * 4;  // >= TOK_PAD * TOK_LD
 
-// rcodes / rscales (optional): the same tile also quantised along its rows (C), written in
-// X's own layout [R, C] and [R, C/32] -- the dgrad operand -- from the one read of X.
 __global__ __launch_bounds__(256) void mx_quantize_tok_kernel(const bf16_t* __restrict__ X, int R,
                                                               int C,
                                                               const int32_t* __restrict__ offsets,
@@ -530,8 +541,9 @@ __global__ __launch_bounds__(256) void mx_quantize_tok_kernel(const bf16_t* __re
                                                               uint8_t* __restrict__ scales,
                                                               uint8_t* __restrict__ rcodes,
                                                               uint8_t* __restrict__ rscales) {
-    __shared__ bf16_t tile[TOK_PAD][TOK_COLS + 8];
-    const int lane = threadIdx.x & 63;
+    static_assert(TOK_LDS >= TOK_PAD * TOK_LD, "output images reuse the input tile");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[TOK_LDS];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int p = blockIdx.y * TOK_PAD;  // padded position of this block's first row
     const int c0 = blockIdx.x * TOK_COLS;
     int e = -1, P = 0, run = 0;
@@ -558,51 +570,108 @@ __global__ __launch_bounds__(256) void mx_quantize_tok_kernel(const bf16_t* __re
         cnt = min(max(offsets[e + 1], lo), R) - lo;
     }
     const int t0 = p - P;  // the block's first row within the expert
-    // stage 128 rows x 64 columns: 8 chunks of 8 values per row, 4 chunks per thread, all
-    // four loads issued before the first LDS store
+    // 1. stage 128 rows x 128 columns: 16 chunks of 8 values per row, 8 chunks per thread
     constexpr int NLD = TOK_PAD * (TOK_COLS / 8) / 256;
     u32x4 v4[NLD];
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-        const int i = threadIdx.x + 256 * u;
+        const int i = tid + 256 * u;
         const int r = i / (TOK_COLS / 8), col = c0 + (i % (TOK_COLS / 8)) * 8;
-        v4[u] = (e >= 0 && t0 + r < cnt && col < C) ? ld16_nt(X + (int64_t)(lo + t0 + r) * C + col)
-                                                    : u32x4{0u, 0u, 0u, 0u};
+        v4[u] = (e >= 0 && t0 + r < cnt) ? ld16_nt(X + (int64_t)(lo + t0 + r) * C + col)
+                                         : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-        const int i = threadIdx.x + 256 * u;
+        const int i = tid + 256 * u;
         const int r = i / (TOK_COLS / 8), ch = i % (TOK_COLS / 8);
-        *reinterpret_cast<u32x4*>(&tile[r][ch * 8]) = v4[u];
+        *reinterpret_cast<u32x4*>(lds + r * TOK_LD + ch * 16) = v4[u];
     }
     __syncthreads();
-    if (rcodes) {  // along the rows: thread -> (tile row, 32-column half)
-        const int rr = threadIdx.x >> 1, half = threadIdx.x & 1, cb = c0 + half * 32;
-        if (e >= 0 && t0 + rr < cnt && cb < C) {
-            float w[32];
+    // 2a. column pass: rows 32 wid .. +31, columns 2 lane and 2 lane + 1
+    uint32_t cq[2][8];
+    int csc[2];
+    {
+        uint32_t pr[32];
 #pragma unroll
-            for (int i = 0; i < 32; ++i) w[i] = __uint_as_float((uint32_t)tile[rr][half * 32 + i] << 16);
-            uint32_t q[8];
-            const int sc = mx_block(w, MOE_MX_FLOOR, q);
-            const int64_t row = lo + t0 + rr;
-            uint8_t* out = rcodes + row * C + cb;
-            st16(out, u32x4{q[0], q[1], q[2], q[3]});
-            st16(out + 16, u32x4{q[4], q[5], q[6], q[7]});
-            rscales[row * (C / 32) + cb / 32] = (uint8_t)sc;
+        for (int i = 0; i < 32; ++i)
+            pr[i] = *reinterpret_cast<const uint32_t*>(lds + (wid * 32 + i) * TOK_LD + lane * 4);
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = lo_bf(pr[i]);
+        csc[0] = mx_block(v, MOE_MX_FLOOR, cq[0]);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = hi_bf(pr[i]);
+        csc[1] = mx_block(v, MOE_MX_FLOOR, cq[1]);
+    }
+    // 2b. row pass: items tid and tid + 256 -> (row it / 4, 32-column block it % 4)
+    uint32_t rq[2][8];
+    int rsc[2] = {0, 0};
+    if (rcodes) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int it = tid + 256 * h, r = it >> 2, b = it & 3;
+            float v[32];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const u32x4 w = *reinterpret_cast<const u32x4*>(lds + r * TOK_LD + b * 64 + c * 16);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    v[8 * c + 2 * q] = lo_bf(w[q]);
+                    v[8 * c + 2 * q + 1] = hi_bf(w[q]);
+                }
+            }
+            rsc[h] = mx_block(v, MOE_MX_FLOOR, rq[h]);
         }
     }
-    const int cl = threadIdx.x & (TOK_COLS - 1), blk = threadIdx.x / TOK_COLS;
-    const int col = c0 + cl;
-    if (col >= C) return;
-    float v[32];
+    __syncthreads();  // every read of the input tile is done: its LDS takes the output images
+    // 3. output images: column lines [128][TOK_OL], row lines [128][TOK_OL], column scale
+    //    words [128], row scale words [128]
+    uint8_t* const col_img = lds;
+    uint8_t* const row_img = lds + TOK_PAD * TOK_OL;
+    uint8_t* const col_sc = lds + 2 * TOK_PAD * TOK_OL;
+    uint8_t* const row_sc = col_sc + 128 * 4;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = __uint_as_float((uint32_t)tile[blk * 32 + i][cl] << 16);
-    uint32_t q[8];
-    const int sc = mx_block(v, MOE_MX_FLOOR, q);
-    uint8_t* out = codes + (int64_t)col * Kp + p + blk * 32;
-    st16(out, u32x4{q[0], q[1], q[2], q[3]});
-    st16(out + 16, u32x4{q[4], q[5], q[6], q[7]});
-    scales[(int64_t)col * (Kp / 32) + p / 32 + blk] = (uint8_t)sc;
+    for (int h = 0; h < 2; ++h) {
+        uint8_t* d = col_img + (2 * lane + h) * TOK_OL + wid * 32;
+        *reinterpret_cast<u32x4*>(d) = u32x4{cq[h][0], cq[h][1], cq[h][2], cq[h][3]};
+        *reinterpret_cast<u32x4*>(d + 16) = u32x4{cq[h][4], cq[h][5], cq[h][6], cq[h][7]};
+        col_sc[(2 * lane + h) * 4 + wid] = (uint8_t)csc[h];
+    }
+    if (rcodes) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int it = tid + 256 * h, r = it >> 2, b = it & 3;
+            uint8_t* d = row_img + r * TOK_OL + b * 32;
+            *reinterpret_cast<u32x4*>(d) = u32x4{rq[h][0], rq[h][1], rq[h][2], rq[h][3]};
+            *reinterpret_cast<u32x4*>(d + 16) = u32x4{rq[h][4], rq[h][5], rq[h][6], rq[h][7]};
+            row_sc[r * 4 + b] = (uint8_t)rsc[h];
+        }
+    }
+    __syncthreads();
+    // 4. whole lines: column c's 128 codes at codes[(c0 + c) Kp + p], row r's 128 codes at
+    //    rcodes[(lo + t0 + r) C + c0]; scale words likewise (4-byte aligned: C, Kp and c0, p
+    //    are multiples of 128)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = tid + 256 * u, ln = i >> 3, ch = i & 7;
+        st16(codes + (int64_t)(c0 + ln) * Kp + p + ch * 16,
+             *reinterpret_cast<const u32x4*>(col_img + ln * TOK_OL + ch * 16));
+    }
+    if (tid < 128)
+        *reinterpret_cast<uint32_t*>(scales + (int64_t)(c0 + tid) * (Kp / 32) + p / 32) =
+            *reinterpret_cast<const uint32_t*>(col_sc + tid * 4);
+    if (rcodes) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + 256 * u, ln = i >> 3, ch = i & 7;
+            if (e >= 0 && t0 + ln < cnt)
+                st16(rcodes + (int64_t)(lo + t0 + ln) * C + c0 + ch * 16,
+                     *reinterpret_cast<const u32x4*>(row_img + ln * TOK_OL + ch * 16));
+        }
+        if (tid < 128 && e >= 0 && t0 + tid < cnt)
+            *reinterpret_cast<uint32_t*>(rscales + (int64_t)(lo + t0 + tid) * (C / 32) + c0 / 32) =
+                *reinterpret_cast<const uint32_t*>(row_sc + tid * 4);
+    }
 }
 
 }  // namespace moe
@@ -703,7 +772,8 @@ int moe_launch_mx_quantize_tok(const bf16_t* X, int R, int C, const int32_t* off
                                int Kp, uint8_t* codes, uint8_t* scales, uint8_t* rcodes,
                                uint8_t* rscales, const char* name, hipStream_t st) {
     if (Kp == 0 || C == 0) return MOE_OK;
-    const dim3 grid((unsigned)((C + TOK_COLS - 1) / TOK_COLS), (unsigned)(Kp / TOK_PAD));
+    if (C % TOK_COLS != 0 || Kp % TOK_PAD != 0) return MOE_EINVAL;
+    const dim3 grid((unsigned)(C / TOK_COLS), (unsigned)(Kp / TOK_PAD));
     MOE_TRACED(name, st,
                mx_quantize_tok_kernel<<<grid, 256, 0, st>>>(X, R, C, offsets, E, Kp, codes,
                                                             scales, rcodes, rscales));
