@@ -314,3 +314,36 @@ def test_expert_ffn_one_launch_parity_and_reuse():
         assert moe.ffn_error(ws) == 0
         ry, _, _ = orc.ffn_fwd(bf(xp[:R]), np.array(offs, np.int32), bf(w1), bf(w2))
         assert_close(bf(y), ry, TOL_BF16, f"y_queue_R{R}")
+
+
+@pytest.mark.parametrize("mode", [moe.MX_FLOOR, moe.MX_CEIL])
+def test_mx_encoder_every_rounding_case(mode):
+    """The E4M3 encoder on every rounding situation: each block holds 511 (block maximum:
+    scale exponent 0 in floor mode, so the other values reach the encoder unscaled; 1 in ceil
+    mode) and 31 fp32 values below 511 in magnitude whose upper 16 bits run over every sign,
+    exponent and top-7 mantissa pattern, each with low 16 bits 0 (exact or a tie at the
+    rounding bit), 1 (just above a tie), 0x7FFF, 0x8000, 0x8001 and 0xFFFF (sticky bits), so
+    ties, near-ties, subnormal codes, flushes to zero and saturation at 448 all occur."""
+    hi = np.arange(65536, dtype=np.uint32)
+    exp = (hi >> 7) & 0xFF
+    hi = hi[exp <= 135]  # |v| < 512
+    lo = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    vals = ((hi[:, None] << 16) | lo[None, :]).ravel().view(np.float32)
+    vals = vals[np.abs(vals) < 511.0]
+    nb = -(-len(vals) // 31)
+    blocks = np.zeros((nb, 32), np.float32)
+    blocks[:, 0] = 511.0
+    flat = np.zeros(nb * 31, np.float32)
+    flat[:len(vals)] = vals
+    blocks[:, 1:] = flat.reshape(nb, 31)
+    nb8 = -(-nb // 8) * 8
+    blocks = np.concatenate([blocks, np.zeros((nb8 - nb, 32), np.float32)])
+    f = blocks.reshape(-1, 256)
+    rows = f.shape[0]
+    q = torch.empty(rows, 256, dtype=torch.uint8, device=DEV)
+    s = torch.empty(rows, 8, dtype=torch.uint8, device=DEV)
+    moe.mx_quantize(torch.from_numpy(f).to(DEV), moe.F32, rows, 256, q, s, mode)
+    torch.cuda.synchronize()
+    rq, rsc = orc.mx_quantize(f.astype(np.float64), mode)
+    assert np.array_equal(host(s), rsc)
+    assert np.array_equal(host(q), rq)
