@@ -118,7 +118,8 @@ __device__ __forceinline__ void combine_token(const bf16_t* __restrict__ y,
 // The combine of one token by one wave (no LDS, no block barrier), for a kernel that keeps one
 // block per CU: each wave of the block works on its own token, so that a CU has several
 // tokens' loads in flight.  Same results, bit for bit, as combine_token (same order per
-// element).  pos / w of slot j are held by lane j and broadcast with a lane read.
+// element), and the same non-temporal accesses.  pos / w of slot j are held by lane j and
+// broadcast with a lane read.
 template <int G>
 __device__ __forceinline__ void combine_token_wave(const bf16_t* __restrict__ y,
                                                    const int32_t* __restrict__ pos,
@@ -148,7 +149,7 @@ __device__ __forceinline__ void combine_token_wave(const bf16_t* __restrict__ y,
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     const int c = c0 + g * 64;
-                    v[g][u] = (j0 + u < k && p >= 0 && c < nc) ? ld16(y + (size_t)p * H + c * 8)
+                    v[g][u] = (j0 + u < k && p >= 0 && c < nc) ? ld16_nt(y + (size_t)p * H + c * 8)
                                                                : u32x4{0, 0, 0, 0};
                 }
             }
@@ -172,7 +173,7 @@ __device__ __forceinline__ void combine_token_wave(const bf16_t* __restrict__ y,
             const int c = c0 + g * 64;
             if (c >= nc) continue;
             for (int s = 0; s < S; ++s) {
-                u32x4 v = ld16(ys + ((size_t)s * T + t) * H + c * 8);
+                u32x4 v = ld16_nt(ys + ((size_t)s * T + t) * H + c * 8);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     acc[g][2 * q] = __fadd_rn(acc[g][2 * q], lo_bf(v[q]));
@@ -182,7 +183,7 @@ __device__ __forceinline__ void combine_token_wave(const bf16_t* __restrict__ y,
             u32x4 o;
 #pragma unroll
             for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[g][2 * q], acc[g][2 * q + 1]);
-            st16(out + (size_t)t * H + c * 8, o);
+            st16_nt(out + (size_t)t * H + c * 8, o);
         }
     }
 }

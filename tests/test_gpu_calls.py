@@ -347,3 +347,23 @@ def test_mx_encoder_every_rounding_case(mode):
     rq, rsc = orc.mx_quantize(f.astype(np.float64), mode)
     assert np.array_equal(host(s), rsc)
     assert np.array_equal(host(q), rq)
+
+
+def test_expert_ffn_one_launch_shared_mode_bit_identical():
+    """Shared experts (offsets null: every expert takes all rows) through the one-launch
+    queue against the two launches, bit for bit."""
+    E, R, H, I = 3, 700, 512, 384
+    xp, w1, w2 = _ffn_case(E, R, H, I, None, 13)
+    outs = []
+    for use_ws in (False, True):
+        y = torch.full((E, R, H), -1.0, dtype=torch.bfloat16, device=DEV)
+        h = torch.full((E, R, I), -1.0, dtype=torch.bfloat16, device=DEV)
+        ws = None
+        if use_ws:
+            ws = torch.full((moe.ffn_workspace_size(moe.BF16, E, R, H, I, True),), 0x5A,
+                            dtype=torch.uint8, device=DEV)
+        moe.moe_expert_ffn(moe.BF16, xp, None, E, R, H, I, w1, w2, y, h_save=h, ws=ws)
+        torch.cuda.synchronize()
+        outs.append((y, h, ws))
+    assert moe.ffn_error(outs[1][2]) == 0
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
