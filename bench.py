@@ -112,8 +112,6 @@ def role_work(wl, role: str, shared: bool) -> tuple[str, float]:
         return "byte", float(wl.ER * 12)
     if role == "router_bwd":
         return "byte", float(T * wl.ER * 4 + T * wl.k * 16)
-    if role == "mx_quantize_h":
-        return "byte", float(R * I * 4 + R * I + R * I // 32)
     if role == "mx_quantize_dy":    # bf16 dy read, codes and scales written
         return "byte", float(R * H * bf + R * H + R * H // 32)
     if role == "mx_quantize_dgu":

@@ -23,7 +23,7 @@ int moe_ffn_bwd_bf16(const bf16_t* xp, const int32_t* offsets, int E, int R, int
                      hipStream_t st);
 int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int E, int R, int H,
                int I, const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q,
-               const uint8_t* w2s, float* hf, uint8_t* hq, uint8_t* hs, uint8_t* panels,
+               const uint8_t* w2s, uint8_t* hq, uint8_t* hs, uint8_t* panels,
                bf16_t* gu_save, bf16_t* h_save, bf16_t* y, hipStream_t st);
 size_t moe_ffn_bwd_mx_bytes(int E, int R, int H, int I, bool wgrad);
 int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uint8_t* w1tq,
@@ -137,8 +137,8 @@ extern "C" size_t moe_ffn_workspace_size(int dtype, int E, int R, int H, int I, 
     if (E < 1 || R < 0 || H < 1 || I < 1) return 0;
     size_t rows = shared ? (size_t)E * R : (size_t)R;
     if (dtype == MOE_MXFP8)
-        return moe_align256(rows * I * 4) + moe_align256(rows * I) +
-               moe_align256(rows * (I / 32)) + moe_mx_panel_bytes(E, R, H, I, shared != 0) + 256;
+        return moe_align256(rows * I) + moe_align256(rows * (I / 32)) +
+               moe_mx_panel_bytes(E, R, H, I, shared != 0) + 256;
     // BF16: the synchronisation words of the one-launch queue, then room for h
     return moe_ffn_sync_bytes(E, R, shared != 0) + moe_align256(rows * I * 2) + 256;
 }
@@ -188,15 +188,13 @@ extern "C" int moe_expert_ffn(int dtype, const void* xp, const uint8_t* xp_scale
                                   (unsigned*)ws, st);
     }
     char* p = (char*)ws;
-    float* hf = (float*)p;
-    p += moe_align256(rows * I * 4);
     uint8_t* hq = (uint8_t*)p;
     p += moe_align256(rows * I);
     uint8_t* hs = (uint8_t*)p;
     p += moe_align256(rows * (I / 32));
     uint8_t* panels = (uint8_t*)p;
     return moe_ffn_mx((const uint8_t*)xp, xp_scales, offsets, E, R, H, I, (const uint8_t*)w1,
-                      w1_scales, (const uint8_t*)w2, w2_scales, hf, hq, hs, panels,
+                      w1_scales, (const uint8_t*)w2, w2_scales, hq, hs, panels,
                       (bf16_t*)gu_save, (bf16_t*)h_save, (bf16_t*)y, st);
 }
 

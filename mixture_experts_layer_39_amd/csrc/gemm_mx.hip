@@ -18,6 +18,7 @@
 // out per K step in the order the 64 lanes consume them (8 bytes per lane, one 512-byte run
 // per panel and step), and the K loop fetches them with one 8-byte load per lane and operand
 // per step, two steps ahead.
+#include "mx_dev.h"
 #include "pipe.h"
 
 namespace moe {
@@ -30,7 +31,7 @@ constexpr int XOPB = XP::OPB;            // bytes of one operand step (one slot)
 constexpr int XLPW = XP::LPW;            // direct loads per operand per wave per step
 constexpr int SPAN = 512;                // bytes of one panel's scales for one K step
 
-enum { XEPI_SWIGLU_F32 = 0, XEPI_STORE_BF16 = 1, XEPI_DSWIGLU = 2 };
+enum { XEPI_SWIGLU_MX = 0, XEPI_STORE_BF16 = 1, XEPI_DSWIGLU = 2 };
 
 struct MxArgs {
     const uint8_t* A;    // codes [rows, K]
@@ -39,9 +40,11 @@ struct MxArgs {
     const uint8_t* B;    // codes [E, b_rows, K]
     const uint8_t* Bt;   // panel scales of B: [E][NT][2][K/128][512]
     int b_rows;
-    void* C;             // SwiGLU: fp32 h [rows, I];  store: bf16 y [rows, N];
-                         // SwiGLU backward: bf16 dg|du [rows, 2I]
-    int64_t c_es;        // per-expert row stride of C (shared mode), in rows
+    void* C;             // store: bf16 y [rows, N];  SwiGLU backward: bf16 dg|du [rows, 2I]
+    uint8_t* Cq;         // SwiGLU: h's E4M3 codes [rows, I] (MX-quantised along I in the epilogue)
+    uint8_t* Cs;         // SwiGLU: h's E8M0 scales [rows, I/32]
+    bf16_t* Ch;          // SwiGLU: h as the codes hold it, bf16 [rows, I], or null
+    int64_t c_es;        // per-expert row stride of C / Cq / Ch (shared mode), in rows
     int ldc;
     bf16_t* C2;          // SwiGLU: bf16 g|u save [rows, 2I] or null;  SwiGLU backward: the
                          // saved g|u (read)
@@ -59,14 +62,14 @@ struct alignas(1024) MxSmem {
 
 template <int EPI>
 __host__ __device__ __forceinline__ int mx_n_tiles(int N, int I) {
-    return (EPI == XEPI_SWIGLU_F32) ? cdiv(I, 128) : cdiv(N, XBN);
+    return (EPI == XEPI_SWIGLU_MX) ? cdiv(I, 128) : cdiv(N, XBN);
 }
 
 // tile row nn -> B row.  SwiGLU: a tile holds gate and up rows of 128 channels; each
 // 32-column MFMA block takes 16 channels, gate in its columns 0-15 and up in 16-31.
 template <int EPI>
 __device__ __forceinline__ int mx_brow(int nn, int n0, int ch0, int I) {
-    if (EPI == XEPI_SWIGLU_F32)
+    if (EPI == XEPI_SWIGLU_MX)
         return ((nn >> 4) & 1) * I + ch0 + (nn >> 7) * 64 + ((nn & 127) >> 5) * 16 + (nn & 15);
     return n0 + nn;
 }
@@ -216,7 +219,7 @@ struct PanelJobs {
 __global__ __launch_bounds__(256) void mx_panel_scales_pre(PanelJobs j) {
     __shared__ uint8_t stg[256][PS_COLS + 4];
     __shared__ int srow[256];
-    const int nb1 = j.E * mx_n_tiles<XEPI_SWIGLU_F32>(2 * j.I, j.I);
+    const int nb1 = j.E * mx_n_tiles<XEPI_SWIGLU_MX>(2 * j.I, j.I);
     const int bx = blockIdx.x;
     const int KBh = j.H / 32, KBi = j.I / 32;
     if (bx < j.na) {
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(256) void mx_panel_scales_pre(PanelJobs j) {
         panel_a(bx, j.xs, j.offsets, j.E, j.R, 0, KBh, j.H / XBK, j.total_static, j.pa1, stg, srow);
     } else if (bx < j.na + nb1) {
         if ((int)blockIdx.y * PS_COLS >= KBh) return;
-        panel_b<XEPI_SWIGLU_F32>(bx - j.na, j.w1s, 2 * j.I, 2 * j.I, j.I, KBh, j.H / XBK, j.pb1,
+        panel_b<XEPI_SWIGLU_MX>(bx - j.na, j.w1s, 2 * j.I, 2 * j.I, j.I, KBh, j.H / XBK, j.pb1,
                                  stg, srow);
     } else {
         if ((int)blockIdx.y * PS_COLS >= KBi) return;
@@ -363,8 +366,8 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
     setup_kmajor<64>(ob, GK ? g.B + kbase : g.B + (int64_t)e * g.b_rows * K,
                      (uint32_t)g.b_rows * (uint32_t)K - (uint32_t)kbase, K / 2,
                      wid, lane, wn * 128, [=](int nn) { return mx_brow<EPI>(nn, n0, ch0, I); },
-                     EPI == XEPI_SWIGLU_F32 ? I : 2 * XP::RPI,
-                     EPI == XEPI_SWIGLU_F32 ? 16 : 4 * XP::RPI);
+                     EPI == XEPI_SWIGLU_MX ? I : 2 * XP::RPI,
+                     EPI == XEPI_SWIGLU_MX ? 16 : 4 * XP::RPI);
     // panel scales of this wave's A rows and B rows
     const uint32_t pbytes = (uint32_t)nk * SPAN;
     // GK: panels over the whole token axis (K / 128 steps each); the expert's steps start at
@@ -542,30 +545,69 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
     // B fragment first: lane l holds row l % 32 of its 32x32 block and columns
     // 8 (v/4) + 4 (l/32) + v%4, v = 0..15: four runs of 4 consecutive columns.
     const int lrow = lane & 31, lcol = (lane >> 5) * 4;
-    if (EPI == XEPI_SWIGLU_F32) {
+    if (EPI == XEPI_SWIGLU_MX) {
         // block (i, j): channels ch0 + 64 wn + 16 j + 8 hf + lcol .. +3; gate at accumulators
-        // 4 hf .. +3, up at 8 + 4 hf .. +3
-        float* C = (float*)g.C + ((int64_t)e * g.c_es + row0) * g.ldc;
+        // 4 hf .. +3, up at 8 + 4 hf .. +3.  h = silu(g) u in fp32 is MX-quantised here, along
+        // I in blocks of 32 channels: block b of the wave's 64 channels (j = 2b, 2b + 1) of a
+        // row sits in lanes l and l ^ 32 (16 values each), so its maximum takes one exchange
+        // between the two halves of the wave.  Same values, same encoder and same order-free
+        // maximum as quantising a stored fp32 h: the same codes and scales.
+        const int64_t rb = (int64_t)e * g.c_es + row0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = m0 + wm * 128 + i * 32 + lrow;
-            if (row >= Mrows) continue;
+            if (row >= Mrows) continue;  // lanes l and l ^ 32 hold the same row
+            const int64_t r = rb + row;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int b = 0; b < 2; ++b) {
+                const int cb = ch0 + wn * 64 + b * 32;  // the block's first channel
+                if (cb >= g.I) continue;                 // uniform over the wave
+                float hv[2][2][4];
+                float amax = 0.0f;
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const int ch = ch0 + wn * 64 + j * 16 + 8 * hf + lcol;
-                    if (ch >= g.I) continue;
-                    const f32x16& a = acc[i][j];
-                    f32x4 hv;
+                for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const float gv = a[4 * hf + c], uv = a[8 + 4 * hf + c];
-                        hv[c] = gv / (1.0f + __expf(-gv)) * uv;
+                    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const f32x16& a = acc[i][2 * b + jj];
+                            const float gv = a[4 * hf + c], uv = a[8 + 4 * hf + c];
+                            const float h = gv / (1.0f + __expf(-gv)) * uv;
+                            hv[jj][hf][c] = h;
+                            amax = fmaxf(amax, fabsf(h));
+                        }
+                amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+                const int sc = mx_scale_code(amax, MOE_MX_FLOOR);
+                const int sh = 127 - sc;
+                const float f = ldexpf(1.0f, sc - 127);
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int ch = cb + 16 * jj + 8 * hf + lcol;
+                        const float* h4 = hv[jj][hf];
+                        const uint32_t w = e4m3x4(ldexpf(h4[0], sh), ldexpf(h4[1], sh),
+                                                  ldexpf(h4[2], sh), ldexpf(h4[3], sh));
+                        *reinterpret_cast<uint32_t*>(g.Cq + r * g.ldc + ch) = w;
+                        if (g.Ch) {  // the quantised values (exact in bf16)
+                            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+                            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+                            *reinterpret_cast<uint2*>(g.Ch + r * g.ldc + ch) =
+                                make_uint2(pack_bf2(lo[0] * f, lo[1] * f),
+                                           pack_bf2(hi[0] * f, hi[1] * f));
+                        }
                     }
-                    *reinterpret_cast<f32x4*>(C + (int64_t)row * g.ldc + ch) = hv;
-                    if (g.C2) {
-                        bf16_t* gr = g.C2 + ((int64_t)e * g.c_es + row0 + row) * g.ldc2;
+                if (lane < 32) g.Cs[r * (g.ldc / 32) + cb / 32] = (uint8_t)sc;
+            }
+            if (g.C2) {
+                bf16_t* gr = g.C2 + r * g.ldc2;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int ch = ch0 + wn * 64 + j * 16 + 8 * hf + lcol;
+                        if (ch >= g.I) continue;
+                        const f32x16& a = acc[i][j];
                         *reinterpret_cast<uint2*>(gr + ch) =
                             make_uint2(pack_bf2(a[4 * hf], a[4 * hf + 1]),
                                        pack_bf2(a[4 * hf + 2], a[4 * hf + 3]));
@@ -573,7 +615,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
                             make_uint2(pack_bf2(a[8 + 4 * hf], a[8 + 4 * hf + 1]),
                                        pack_bf2(a[8 + 4 * hf + 2], a[8 + 4 * hf + 3]));
                     }
-                }
+            }
         }
     } else if (EPI == XEPI_DSWIGLU) {
         // acc = dh at channels col .. col+3; the saved g|u of the row give dg|du
@@ -639,7 +681,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
                                     : g.total;                                            \
         if ((int)blockIdx.x < total) mx_tile<EPI>(g, sm, blockIdx.x);                     \
     }
-MOE_MX_KERNEL(mx_gemm1_swiglu, XEPI_SWIGLU_F32)
+MOE_MX_KERNEL(mx_gemm1_swiglu, XEPI_SWIGLU_MX)
 MOE_MX_KERNEL(mx_gemm2_down, XEPI_STORE_BF16)
 MOE_MX_KERNEL(mx_bwd_down, XEPI_DSWIGLU)
 #undef MOE_MX_KERNEL
@@ -677,7 +719,7 @@ static int mx_launch(const MxArgs& g, hipStream_t st, const char* name = nullptr
     const int NT = mx_n_tiles<EPI>(g.N, g.I);
     const int grid = g.offsets ? mx_mtiles_bound(g.R, g.E, false) * NT : g.total;
     if (grid <= 0) return MOE_OK;
-    if (EPI == XEPI_SWIGLU_F32)
+    if (EPI == XEPI_SWIGLU_MX)
         MOE_TRACED("mx_gemm1_swiglu", st, mx_gemm1_swiglu<<<grid, XNTH, 0, st>>>(g));
     else if (EPI == XEPI_DSWIGLU)
         MOE_TRACED("mx_bwd_down", st, mx_bwd_down<<<grid, XNTH, 0, st>>>(g));
@@ -688,7 +730,7 @@ static int mx_launch(const MxArgs& g, hipStream_t st, const char* name = nullptr
 }
 
 static int mx_panels_pre(const PanelJobs& j, hipStream_t st) {
-    const int nb = j.na + j.E * mx_n_tiles<XEPI_SWIGLU_F32>(2 * j.I, j.I) +
+    const int nb = j.na + j.E * mx_n_tiles<XEPI_SWIGLU_MX>(2 * j.I, j.I) +
                    j.E * mx_n_tiles<XEPI_STORE_BF16>(j.H, j.I);
     const dim3 grid(nb, cdiv(max(j.H, j.I) / 32, PS_COLS));
     MOE_TRACED("mx_panel_scales", st, mx_panel_scales_pre<<<grid, 256, 0, st>>>(j));
@@ -721,13 +763,10 @@ static size_t mx_panel_b_bytes(int E, int N, int I, int K) {
 
 using namespace moe;
 
-int moe_launch_mx_quantize_f32(const float* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
-                               bf16_t* deq, hipStream_t st);
-
 // Workspace bytes of the panel scales of both MXFP8 GEMMs (A and B operands).
 size_t moe_mx_panel_bytes(int E, int R, int H, int I, bool shared) {
     return mx_panel_a_bytes(E, R, H, shared) + mx_panel_a_bytes(E, R, I, shared) +
-           mx_panel_b_bytes<XEPI_SWIGLU_F32>(E, 2 * I, I, H) +
+           mx_panel_b_bytes<XEPI_SWIGLU_MX>(E, 2 * I, I, H) +
            mx_panel_b_bytes<XEPI_STORE_BF16>(E, H, I, I);
 }
 
@@ -741,7 +780,7 @@ int moe_launch_mx_quantize_bf16(const bf16_t* in, int64_t rows, int K, uint8_t* 
 // backward.
 int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int E, int R, int H,
                int I, const uint8_t* w1q, const uint8_t* w1s, const uint8_t* w2q,
-               const uint8_t* w2s, float* hf, uint8_t* hq, uint8_t* hs, uint8_t* panels,
+               const uint8_t* w2s, uint8_t* hq, uint8_t* hs, uint8_t* panels,
                bf16_t* gu_save, bf16_t* h_save, bf16_t* y, hipStream_t st) {
     // K steps of 128 codes: H and I multiples of 128
     if (H % XBK || I % XBK) return MOE_EINVAL;
@@ -749,7 +788,7 @@ int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int
     uint8_t* pa1 = panels;
     uint8_t* pa2 = pa1 + mx_panel_a_bytes(E, R, H, shared);
     uint8_t* pb1 = pa2 + mx_panel_a_bytes(E, R, I, shared);
-    uint8_t* pb2 = pb1 + mx_panel_b_bytes<XEPI_SWIGLU_F32>(E, 2 * I, I, H);
+    uint8_t* pb2 = pb1 + mx_panel_b_bytes<XEPI_SWIGLU_MX>(E, 2 * I, I, H);
     PanelJobs pj{xs, offsets, E, R, H, I, mx_mtiles_bound(R, E, shared),
                  shared ? mx_mtiles_bound(R, E, true) : 0, w1s, w2s, pa1, pb1, pb2};
     int rc = mx_panels_pre(pj, st);
@@ -757,14 +796,11 @@ int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int
     MxArgs g{};
     g.A = xq; g.At = pa1; g.a_es = 0;
     g.B = w1q; g.Bt = pb1; g.b_rows = 2 * I;
-    g.C = hf; g.c_es = shared ? R : 0; g.ldc = I;
+    g.Cq = hq; g.Cs = hs; g.Ch = h_save; g.c_es = shared ? R : 0; g.ldc = I;
     g.C2 = gu_save; g.ldc2 = 2 * I;
     g.offsets = offsets; g.E = E; g.R = R; g.N = 2 * I; g.K = H; g.I = I;
     g.total = shared ? E * cdiv(R, XBM) * cdiv(I, 128) : 0;
-    rc = mx_launch<XEPI_SWIGLU_F32>(g, st);
-    if (rc) return rc;
-    int64_t rows = shared ? (int64_t)E * R : R;
-    rc = moe_launch_mx_quantize_f32(hf, rows, I, hq, hs, h_save, st);
+    rc = mx_launch<XEPI_SWIGLU_MX>(g, st);
     if (rc) return rc;
     rc = mx_panels_h(hs, offsets, E, R, shared ? R : 0, I, pa2, st);
     if (rc) return rc;
