@@ -11,16 +11,6 @@
 
 namespace moe {
 
-// Value of an E4M3 ("FN") code.
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    float v;
-    if (e == 15u && m == 7u) v = __uint_as_float(0x7FC00000u);        // NaN
-    else if (e == 0u) v = (float)m * (1.0f / 512.0f);                // subnormal: m 2^-9
-    else v = __uint_as_float(((e + 120u) << 23) | (m << 20));        // 2^(e-7) (1 + m/8)
-    return (c & 0x80u) ? -v : v;
-}
-
 // Quantise 32 fp32 values (one block) held in v[]; returns the scale code, codes packed
 // little-endian into q[8].
 __device__ __forceinline__ int mx_block(const float* v, int mode, uint32_t* q) {
@@ -148,27 +138,11 @@ __global__ __launch_bounds__(256) void dispatch_mx_tok_kernel(const bf16_t* __re
 }
 
 // ------------------------------------------------------------------ mx_quantize
-// The quantised values of one block written back as bf16 (exact: codes x 2^k).
-__device__ __forceinline__ void mx_deq_store(const uint32_t* q, int sc, bf16_t* out) {
-    const float f = ldexpf(1.0f, sc - 127);
-    uint32_t w[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t word = q[i];
-        w[2 * i] = pack_bf2(e4m3_value(word & 0xFFu) * f, e4m3_value((word >> 8) & 0xFFu) * f);
-        w[2 * i + 1] = pack_bf2(e4m3_value((word >> 16) & 0xFFu) * f, e4m3_value(word >> 24) * f);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        st16(out + 8 * i, u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]});
-}
-
-// deq (optional): the quantised values written back as bf16.
+// One thread per 32-value block of a bf16 or fp32 input: the block's E8M0 scale and codes.
 template <bool F32>
 __global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict__ in, int64_t nblocks,
                                                           int mode, uint8_t* __restrict__ codes,
-                                                          uint8_t* __restrict__ scales,
-                                                          bf16_t* __restrict__ deq) {
+                                                          uint8_t* __restrict__ scales) {
     int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= nblocks) return;
     float v[32];
@@ -197,7 +171,6 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict
     st16(codes + b * 32, u32x4{q[0], q[1], q[2], q[3]});
     st16(codes + b * 32 + 16, u32x4{q[4], q[5], q[6], q[7]});
     scales[b] = (uint8_t)sc;
-    if (deq) mx_deq_store(q, sc, deq + b * 32);
 }
 
 // ------------------------------------------------------------------ combine
@@ -437,13 +410,11 @@ __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const bf16_t* __rest
 }
 
 // ------------------------------------------------------------------ mx_dequantize
-// One thread per 32-value block: value = E4M3(code) * 2^(scale - 127), rounded to bf16
-// (exact for every normal bf16 value: a code has 3 mantissa bits).
-
-// One thread per 16 codes (half a block): 16-byte code loads, so a wave reads 1 KB in one
-// piece.  The codes decode with the hardware fp8 -> fp32 conversion (exact for every finite
-// E4M3FN code; the quantisers here never emit the NaN code) and scale by 2^(s-127) in fp32,
-// then round to bf16: the same arithmetic as mx_deq_store, with the decode in hardware.
+// value = E4M3(code) * 2^(scale - 127) in fp32, rounded to bf16 (exact for every normal bf16
+// value: a code has 3 mantissa bits).  One thread per 16 codes (half a block): 16-byte code
+// loads, so a wave reads 1 KB in one piece.  The codes decode with the hardware fp8 -> fp32
+// conversion, exact for every finite E4M3FN code (the quantisers here never emit the NaN
+// code).
 __global__ __launch_bounds__(256) void mx_dequantize_kernel(const uint8_t* __restrict__ codes,
                                                             const uint8_t* __restrict__ scales,
                                                             int64_t nblocks,
@@ -717,9 +688,9 @@ extern "C" int mx_quantize(const void* in, int in_dtype, int rows, int K, uint8_
     hipStream_t st = (hipStream_t)stream;
     MOE_TRACED("mx_quantize", st,
                if (in_dtype == MOE_F32)
-                   mx_quantize_kernel<true><<<grid, 256, 0, st>>>(in, nb, scale_mode, codes, scales, nullptr);
+                   mx_quantize_kernel<true><<<grid, 256, 0, st>>>(in, nb, scale_mode, codes, scales);
                else
-                   mx_quantize_kernel<false><<<grid, 256, 0, st>>>(in, nb, scale_mode, codes, scales, nullptr));
+                   mx_quantize_kernel<false><<<grid, 256, 0, st>>>(in, nb, scale_mode, codes, scales));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -822,7 +793,7 @@ int moe_launch_mx_quantize_bf16(const bf16_t* in, int64_t rows, int K, uint8_t* 
     if (nb == 0) return MOE_OK;
     MOE_TRACED(name, st,
                mx_quantize_kernel<false><<<(unsigned)((nb + 255) / 256), 256, 0, st>>>(
-                   in, nb, MOE_MX_FLOOR, codes, scales, nullptr));
+                   in, nb, MOE_MX_FLOOR, codes, scales));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
