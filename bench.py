@@ -124,6 +124,25 @@ def role_work(wl, role: str, shared: bool) -> tuple[str, float]:
     return "byte", 0.0
 
 
+def gemm_bytes(wl, role: str, shared: bool) -> float:
+    """Algorithmic HBM bytes of one launch of a BF16 grouped-GEMM role: every operand, weight
+    and result it must read or write once (bf16), for the routed experts or (shared) the
+    shared experts.  0 for roles without a byte model (the MXFP8 products)."""
+    H, I, R, E = wl.H, wl.I, wl.R, wl.E
+    if shared:
+        I, R, E = wl.Is, wl.T, wl.S
+    b = 2.0
+    xp, h, gu, w = R * H * b, R * I * b, R * 2 * I * b, E * H * I * b  # w: one of W1/2 halves
+    gu_save = gu if wl.backward else 0.0
+    return {
+        "gemm1_swiglu": xp + 2 * w + h + gu_save,          # Xp, W1 in; h (and g|u) out
+        "gemm2_down": h + w + xp,                          # h, W2 in; y out
+        "ffn_queue": xp + 2 * w + 2 * h + w + xp,          # both products (h out and in)
+        "bwd_down": xp + w + gu + gu + h + w,              # dy, W2, g|u, h in; dGU, dW2 out
+        "bwd_gate_up": gu + 2 * w + xp + xp + 2 * w,       # dGU, W1, Xp in; dXp, dW1 out
+    }.get(role, 0.0)
+
+
 def step_work(wl, role: str) -> tuple[str, float]:
     """Algorithmic work of `role` over one step: the routed experts' share plus, for the BF16
     GEMMs, the shared experts' (each of them runs on every source token)."""
@@ -135,7 +154,9 @@ def step_work(wl, role: str) -> tuple[str, float]:
 
 def roofline_of(wl, role: str, ms_per_step: float, launches: float, traffic) -> dict:
     """Roofline of `role`: its algorithmic work per step over its measured time per step (the
-    sum of its launch durations), and the same per launch."""
+    sum of its launch durations), and the same per launch.  A BF16 GEMM role is held against
+    the bound that takes longer at the published peaks -- its flops at the MFMA peak or its
+    algorithmic bytes at the HBM peak -- and reports its fraction of both."""
     kind, work = step_work(wl, role)
     per_launch_ms = ms_per_step / launches
     common = {"work_per_launch": work / launches, "avg_launch_ms": round(per_launch_ms, 4),
@@ -143,6 +164,17 @@ def roofline_of(wl, role: str, ms_per_step: float, launches: float, traffic) -> 
     if kind == "flop":
         peak = PEAK_MXFP8_TFLOPS if GEMM_ROLES[role][1] else PEAK_BF16_TFLOPS
         ach = work / (ms_per_step * 1e-3) / 1e12
+        nbytes = gemm_bytes(wl, role, False)
+        if nbytes and wl.S and not wl.local_share:
+            nbytes += gemm_bytes(wl, role, True)
+        if nbytes:
+            gbs = nbytes / (ms_per_step * 1e-3) / 1e9
+            common.update(mfma_frac=round(ach / peak, 4), hbm_frac=round(gbs / PEAK_HBM_GBS, 4),
+                          bytes_per_launch=nbytes / launches)
+            if nbytes / (PEAK_HBM_GBS * 1e9) > work / (peak * 1e12):
+                return {"kernel": role, "bound": "hbm", "achieved": round(gbs, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "traffic": traffic, **common}
         return {"kernel": role, "bound": "mfma", "achieved": round(ach, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic, **common}
     ach = work / (ms_per_step * 1e-3) / 1e9
