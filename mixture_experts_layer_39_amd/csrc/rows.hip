@@ -197,9 +197,8 @@ static int combine_threads(int H) {
 
 // ------------------------------------------------------------------ combine backward
 // One block per token: dy[pos[t,j],:] = bf16(w[t,j] * dout[t,:]) and
-// dw[t,j] = <dout[t,:], y[pos[t,j],:]> in fp32 with a fixed reduction tree.  For each slot,
-// each thread issues the loads of up to CB_UN chunks of dout[t] and of y[pos[t,j]] before
-// reducing them (chunks in ascending order).
+// dw[t,j] = <dout[t,:], y[pos[t,j],:]> in fp32 with a fixed reduction tree: each thread sums
+// its chunks in ascending order, then a butterfly over the wave and the four waves in order.
 constexpr int CB_UN = 4;
 
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restrict__ dout,
@@ -213,24 +212,43 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restri
     const int nc = H / 8;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const bf16_t* g_row = dout + (size_t)t * H;
-    for (int j = 0; j < k; ++j) {
-        const int p = pos[(size_t)t * k + j];
-        const bool ok = p >= 0 && p < R;
-        const float wj = w[(size_t)t * k + j];
-        float part = 0.0f;
-        if (ok) {
-            const bf16_t* y_row = y + (size_t)p * H;
-            for (int c0 = threadIdx.x; c0 < nc; c0 += 256 * CB_UN) {
-                u32x4 g[CB_UN], v[CB_UN];
+    if (nc <= 256 * CB_UN) {
+        // The row in one pass: the thread's dout chunks are loaded once for all slots, slot
+        // j's position and weight come from lane j of every wave (k <= 64), and slot j+1's
+        // y chunks are loaded before slot j is summed.  Per slot and element the arithmetic
+        // and its order are those of the general loop below.
+        int myp = -1;
+        float myw = 0.0f;
+        if (lane < k) {
+            const int pp = pos[(size_t)t * k + lane];
+            myp = (pp >= 0 && pp < R) ? pp : -1;
+            myw = w[(size_t)t * k + lane];
+        }
+        u32x4 g[CB_UN], v[CB_UN], vn[CB_UN];
+#pragma unroll
+        for (int u = 0; u < CB_UN; ++u) {
+            const int c = threadIdx.x + u * 256;
+            g[u] = c < nc ? ld16(g_row + c * 8) : u32x4{0, 0, 0, 0};
+        }
+        auto load_y = [&](int p, u32x4* dst) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < CB_UN; ++u) {
+                const int c = threadIdx.x + u * 256;
+                dst[u] = (p >= 0 && c < nc) ? ld16_nt(y + (size_t)p * H + c * 8)
+                                            : u32x4{0, 0, 0, 0};
+            }
+        };
+        int p = __builtin_amdgcn_readlane(myp, 0);
+        load_y(p, v);
+        for (int j = 0; j < k; ++j) {
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myw), j));
+            const int pnext = j + 1 < k ? __builtin_amdgcn_readlane(myp, j + 1) : -1;
+            load_y(pnext, vn);
+            float part = 0.0f;
+            if (p >= 0) {
 #pragma unroll
                 for (int u = 0; u < CB_UN; ++u) {
-                    const int c = c0 + u * 256;
-                    g[u] = c < nc ? ld16(g_row + c * 8) : u32x4{0, 0, 0, 0};
-                    v[u] = c < nc ? ld16_nt(y_row + c * 8) : u32x4{0, 0, 0, 0};
-                }
-#pragma unroll
-                for (int u = 0; u < CB_UN; ++u) {
-                    const int c = c0 + u * 256;
+                    const int c = threadIdx.x + u * 256;
                     if (c >= nc) continue;
                     u32x4 o;
 #pragma unroll
@@ -243,10 +261,49 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restri
                     st16(dy + (size_t)p * H + c * 8, o);
                 }
             }
-        }
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) part = __fadd_rn(part, __shfl_xor(part, d, 64));
-        if (lane == 0) red[wid][j] = part;
+            for (int d = 1; d < 64; d <<= 1) part = __fadd_rn(part, __shfl_xor(part, d, 64));
+            if (lane == 0) red[wid][j] = part;
+#pragma unroll
+            for (int u = 0; u < CB_UN; ++u) v[u] = vn[u];
+            p = pnext;
+        }
+    } else {
+        for (int j = 0; j < k; ++j) {
+            const int p = pos[(size_t)t * k + j];
+            const bool ok = p >= 0 && p < R;
+            const float wj = w[(size_t)t * k + j];
+            float part = 0.0f;
+            if (ok) {
+                const bf16_t* y_row = y + (size_t)p * H;
+                for (int c0 = threadIdx.x; c0 < nc; c0 += 256 * CB_UN) {
+                    u32x4 g[CB_UN], v[CB_UN];
+#pragma unroll
+                    for (int u = 0; u < CB_UN; ++u) {
+                        const int c = c0 + u * 256;
+                        g[u] = c < nc ? ld16(g_row + c * 8) : u32x4{0, 0, 0, 0};
+                        v[u] = c < nc ? ld16_nt(y_row + c * 8) : u32x4{0, 0, 0, 0};
+                    }
+#pragma unroll
+                    for (int u = 0; u < CB_UN; ++u) {
+                        const int c = c0 + u * 256;
+                        if (c >= nc) continue;
+                        u32x4 o;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float g0 = lo_bf(g[u][q]), g1 = hi_bf(g[u][q]);
+                            part = __fadd_rn(part, __fmul_rn(g0, lo_bf(v[u][q])));
+                            part = __fadd_rn(part, __fmul_rn(g1, hi_bf(v[u][q])));
+                            o[q] = pack_bf2(__fmul_rn(wj, g0), __fmul_rn(wj, g1));
+                        }
+                        st16(dy + (size_t)p * H + c * 8, o);
+                    }
+                }
+            }
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) part = __fadd_rn(part, __shfl_xor(part, d, 64));
+            if (lane == 0) red[wid][j] = part;
+        }
     }
     __syncthreads();
     if (threadIdx.x < k) {
