@@ -116,8 +116,10 @@ def role_work(wl, role: str, shared: bool) -> tuple[str, float]:
         return "byte", float(R * H * bf + R * H + R * H // 32)
     if role == "mx_quantize_dgu":
         return "byte", float(R * 2 * I * bf + R * 2 * I + R * 2 * I // 32)
+    if role == "mx_quantize_tok_xp":  # xp's dispatch codes and scales in, codes and scales out
+        return "byte", float(R * H + R * H // 32 + R * H + R * H // 32)
     if role.startswith("mx_quantize_tok_"):  # a [R, C] bf16 operand in, codes and scales out
-        C = {"dy": H, "xp": H, "h": I, "dgu": 2 * I}[role[len("mx_quantize_tok_"):]]
+        C = {"dy": H, "h": I, "dgu": 2 * I}[role[len("mx_quantize_tok_"):]]
         return "byte", float(R * C * bf + R * C + R * C // 32)
     if role == "mx_dequantize":     # xp codes and scales read, bf16 written (and h after GEMM2)
         return "byte", float(R * H + R * H // 32 + R * H * bf)

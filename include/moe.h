@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 /* return codes */
 #define MOE_OK 0
@@ -284,12 +284,17 @@ typedef struct moe_bwd_args {
      *     every operand quantised along the expert's rows (32-row blocks from the expert's
      *     first row, the last one zero-padded); with mx == 1 they stay BF16 products.
      * xp and h must hold what the MX forward's GEMMs consumed -- the dequantised xp codes
-     * (mx_dequantize) and the h_save of moe_expert_ffn -- and gu its gu_save. */
+     * (mx_dequantize) and the h_save of moe_expert_ffn -- and gu its gu_save.  With mx == 2,
+     * xp may instead be given as the forward's codes and scales (xp_codes, xp_scales, from
+     * moe_dispatch): xp is then not read and may be NULL, and the weight-gradient quantiser
+     * decodes the codes itself (the same values, so the same results). */
     int mx;
     const uint8_t *w2t_codes;   /* [E,I,H]  W2_e^T codes, scales [E,I,H/32] (along H) */
     const uint8_t *w2t_scales;
     const uint8_t *w1t_codes;   /* [E,H,2I] W1_e^T codes, scales [E,H,2I/32] (along 2I) */
     const uint8_t *w1t_scales;
+    const uint8_t *xp_codes;    /* mx == 2, optional: [R,H] xp codes, scales [R,H/32] */
+    const uint8_t *xp_scales;
 } moe_bwd_args;
 
 size_t moe_backward_workspace_size(const moe_bwd_args *a);

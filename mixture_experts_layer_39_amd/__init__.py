@@ -45,7 +45,8 @@ class BwdArgs(ctypes.Structure):
                                    "dout", "dx", "dw1", "dw2", "dws1", "dws2", "dw_route",
                                    "dlogits")] + \
                [(n, _i) for n in ("passes", "pass_tokens", "pass_rows", "mx")] + \
-               [(n, _vp) for n in ("w2t_codes", "w2t_scales", "w1t_codes", "w1t_scales")]
+               [(n, _vp) for n in ("w2t_codes", "w2t_scales", "w1t_codes", "w1t_scales",
+                                   "xp_codes", "xp_scales")]
 
 
 class FwdArgs(ctypes.Structure):

@@ -29,8 +29,8 @@ size_t moe_ffn_bwd_mx_bytes(int E, int R, int H, int I, bool wgrad);
 int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uint8_t* w1tq,
                    const uint8_t* w1ts, const uint8_t* w2tq, const uint8_t* w2ts,
                    const bf16_t* gu, const bf16_t* dy, bf16_t* dgu, bf16_t* dxp,
-                   const bf16_t* h, const bf16_t* xp, bf16_t* dw1, bf16_t* dw2, uint8_t* ws,
-                   hipStream_t st);
+                   const bf16_t* h, const bf16_t* xp, const uint8_t* xq, const uint8_t* xs,
+                   bf16_t* dw1, bf16_t* dw2, uint8_t* ws, hipStream_t st);
 int moe_ffn_wgrad_bf16(const MoeWgradSpan* wg, int E, int H, int I, hipStream_t st);
 size_t moe_mx_panel_bytes(int E, int R, int H, int I, bool shared);
 int moe_launch_combine_bwd(const bf16_t* dout, const bf16_t* y, const int32_t* pos, const float* w,
@@ -245,8 +245,9 @@ extern "C" int moe_backward(const moe_bwd_args* a, void* ws, size_t ws_bytes, vo
         MOE_REQUIRE(passes == 1 && a->H % 128 == 0 && a->I % 128 == 0);
         MOE_REQUIRE(a->T == 0 || (a->w1t_codes && a->w1t_scales && a->w2t_codes && a->w2t_scales));
     }
+    const bool xp_as_codes = a->mx == 2 && a->xp_codes && a->xp_scales;
     if (a->T > 0) {
-        MOE_REQUIRE(a->xp && a->gu && a->h && a->y && a->offsets && a->pos && a->idx && a->w &&
+        MOE_REQUIRE((a->xp || xp_as_codes) && a->gu && a->h && a->y && a->offsets && a->pos && a->idx && a->w &&
                     a->s_sel && a->w1 && a->w2 && a->dout && a->dx && a->dw1 && a->dw2 &&
                     a->dw_route && a->dlogits);
         if (a->score == MOE_SCORE_SOFTMAX && !a->renorm) MOE_REQUIRE(a->logits);
@@ -296,6 +297,8 @@ extern "C" int moe_backward(const moe_bwd_args* a, void* ws, size_t ws_bytes, vo
             rc = moe_ffn_bwd_mx(a->offsets, E, prow, H, I, a->w1t_codes, a->w1t_scales,
                                 a->w2t_codes, a->w2t_scales, (const bf16_t*)a->gu, dy, dgu, dxp,
                                 (const bf16_t*)a->h, (const bf16_t*)a->xp,
+                                xp_as_codes ? a->xp_codes : nullptr,
+                                xp_as_codes ? a->xp_scales : nullptr,
                                 mxw ? (bf16_t*)a->dw1 : nullptr, mxw ? (bf16_t*)a->dw2 : nullptr,
                                 (uint8_t*)(base + L.mx), st);
             if (rc) return rc;

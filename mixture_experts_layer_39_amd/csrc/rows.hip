@@ -503,8 +503,10 @@ __global__ __launch_bounds__(256) void mx_dequantize_kernel(const uint8_t* __res
 // straddles two experts.
 //
 // One block per (128 columns, 128 padded positions), C % 128 == 0:
-//  1. the 128 x 128 tile of X is staged through LDS with 16-byte row loads (all eight of a
-//     thread's loads issued first);
+//  1. the 128 x 128 tile of X is staged through LDS with 16-byte row loads (all of a
+//     thread's loads issued first); X may also come as MX codes with scales along C (MXIN),
+//     decoded while staging exactly as mx_dequantize decodes them (so the staged values are
+//     those a dequantised copy would hold);
 //  2. column pass: wave w takes the rows 32w .. 32w+31, lane l the column pair 2l, 2l+1
 //     (one dword LDS read per row: 64 consecutive dwords, conflict-free); row pass: items
 //     (row r, 32-column block b), four lanes per row, 64 contiguous LDS bytes each;
@@ -517,8 +519,11 @@ constexpr int TOK_LD = TOK_COLS * 2 + 16;  // bytes per staged input row (16-byt
 constexpr int TOK_OL = 128 + 16;           // bytes per staged output line
 constexpr int TOK_LDS = 2 * TOK_PAD * TOK_OL + 2 * 128 * 4;  // >= TOK_PAD * TOK_LD
 
-__global__ __launch_bounds__(256) void mx_quantize_tok_kernel(const bf16_t* __restrict__ X, int R,
-                                                              int C,
+template <bool MXIN>
+__global__ __launch_bounds__(256) void mx_quantize_tok_kernel(const bf16_t* __restrict__ X,
+                                                              const uint8_t* __restrict__ Xq,
+                                                              const uint8_t* __restrict__ Xs,
+                                                              int R, int C,
                                                               const int32_t* __restrict__ offsets,
                                                               int E, int Kp,
                                                               uint8_t* __restrict__ codes,
@@ -554,21 +559,55 @@ __global__ __launch_bounds__(256) void mx_quantize_tok_kernel(const bf16_t* __re
         cnt = min(max(offsets[e + 1], lo), R) - lo;
     }
     const int t0 = p - P;  // the block's first row within the expert
-    // 1. stage 128 rows x 128 columns: 16 chunks of 8 values per row, 8 chunks per thread
-    constexpr int NLD = TOK_PAD * (TOK_COLS / 8) / 256;
-    u32x4 v4[NLD];
+    if (!MXIN) {
+        // 1. stage 128 rows x 128 columns: 16 chunks of 8 values per row, 8 per thread
+        constexpr int NLD = TOK_PAD * (TOK_COLS / 8) / 256;
+        u32x4 v4[NLD];
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-        const int i = tid + 256 * u;
-        const int r = i / (TOK_COLS / 8), col = c0 + (i % (TOK_COLS / 8)) * 8;
-        v4[u] = (e >= 0 && t0 + r < cnt) ? ld16_nt(X + (int64_t)(lo + t0 + r) * C + col)
-                                         : u32x4{0u, 0u, 0u, 0u};
-    }
+        for (int u = 0; u < NLD; ++u) {
+            const int i = tid + 256 * u;
+            const int r = i / (TOK_COLS / 8), col = c0 + (i % (TOK_COLS / 8)) * 8;
+            v4[u] = (e >= 0 && t0 + r < cnt) ? ld16_nt(X + (int64_t)(lo + t0 + r) * C + col)
+                                             : u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-        const int i = tid + 256 * u;
-        const int r = i / (TOK_COLS / 8), ch = i % (TOK_COLS / 8);
-        *reinterpret_cast<u32x4*>(lds + r * TOK_LD + ch * 16) = v4[u];
+        for (int u = 0; u < NLD; ++u) {
+            const int i = tid + 256 * u;
+            const int r = i / (TOK_COLS / 8), ch = i % (TOK_COLS / 8);
+            *reinterpret_cast<u32x4*>(lds + r * TOK_LD + ch * 16) = v4[u];
+        }
+    } else {
+        // 1. (MX input) 128 rows x 128 codes: 8 chunks of 16 codes per row, 4 per thread;
+        //    chunk ch of a row lies in the row's 32-code block c0/32 + ch/2
+        constexpr int NLD = TOK_PAD * (TOK_COLS / 16) / 256;
+        u32x4 q4[NLD];
+        int sc4[NLD];
+#pragma unroll
+        for (int u = 0; u < NLD; ++u) {
+            const int i = tid + 256 * u;
+            const int r = i / (TOK_COLS / 16), ch = i % (TOK_COLS / 16);
+            const bool ok = e >= 0 && t0 + r < cnt;
+            const int64_t row = lo + t0 + r;
+            q4[u] = ok ? ld16_nt(Xq + row * C + c0 + ch * 16) : u32x4{0u, 0u, 0u, 0u};
+            sc4[u] = ok ? (int)Xs[row * (C / 32) + c0 / 32 + ch / 2] : 127;
+        }
+#pragma unroll
+        for (int u = 0; u < NLD; ++u) {
+            const int i = tid + 256 * u;
+            const int r = i / (TOK_COLS / 16), ch = i % (TOK_COLS / 16);
+            const float f = ldexpf(1.0f, sc4[u] - 127);
+            uint32_t w8[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)q4[u][q], false);
+                const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)q4[u][q], true);
+                w8[2 * q] = pack_bf2(a[0] * f, a[1] * f);
+                w8[2 * q + 1] = pack_bf2(b[0] * f, b[1] * f);
+            }
+            uint8_t* d = lds + r * TOK_LD + ch * 32;
+            *reinterpret_cast<u32x4*>(d) = u32x4{w8[0], w8[1], w8[2], w8[3]};
+            *reinterpret_cast<u32x4*>(d + 16) = u32x4{w8[4], w8[5], w8[6], w8[7]};
+        }
     }
     __syncthreads();
     // 2a. column pass: rows 32 wid .. +31, columns 2 lane and 2 lane + 1
@@ -752,15 +791,24 @@ extern "C" int mx_quantize(const void* in, int in_dtype, int rows, int K, uint8_
     return MOE_OK;
 }
 
-int moe_launch_mx_quantize_tok(const bf16_t* X, int R, int C, const int32_t* offsets, int E,
-                               int Kp, uint8_t* codes, uint8_t* scales, uint8_t* rcodes,
-                               uint8_t* rscales, const char* name, hipStream_t st) {
+int moe_launch_mx_quantize_tok(const bf16_t* X, const uint8_t* Xq, const uint8_t* Xs, int R,
+                               int C, const int32_t* offsets, int E, int Kp, uint8_t* codes,
+                               uint8_t* scales, uint8_t* rcodes, uint8_t* rscales,
+                               const char* name, hipStream_t st) {
     if (Kp == 0 || C == 0) return MOE_OK;
     if (C % TOK_COLS != 0 || Kp % TOK_PAD != 0) return MOE_EINVAL;
     const dim3 grid((unsigned)(C / TOK_COLS), (unsigned)(Kp / TOK_PAD));
-    MOE_TRACED(name, st,
-               mx_quantize_tok_kernel<<<grid, 256, 0, st>>>(X, R, C, offsets, E, Kp, codes,
-                                                            scales, rcodes, rscales));
+    if (Xq) {  // MX codes and scales along C (X unused)
+        if (!Xs) return MOE_EINVAL;
+        MOE_TRACED(name, st,
+                   mx_quantize_tok_kernel<true><<<grid, 256, 0, st>>>(
+                       nullptr, Xq, Xs, R, C, offsets, E, Kp, codes, scales, rcodes, rscales));
+    } else {
+        MOE_TRACED(name, st,
+                   mx_quantize_tok_kernel<false><<<grid, 256, 0, st>>>(
+                       X, nullptr, nullptr, R, C, offsets, E, Kp, codes, scales, rcodes,
+                       rscales));
+    }
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

@@ -144,7 +144,9 @@ class MoELayer:
                 self.w2ts = _e((E, I, H // 32), torch.uint8, d)
                 self.w1tq = _e((E, H, 2 * I), torch.uint8, d)
                 self.w1ts = _e((E, H, 2 * I // 32), torch.uint8, d)
-                self.xp = _e((R, H), bf, d)
+                # MXFP8 weight gradients read xp as the dispatch's codes; BF16 ones (mode 1)
+                # need it dequantised
+                self.xp = _e((R, H), bf, d) if c.mx_bwd != 2 else None
                 self.gu = _e((R, 2 * I), bf, d)
                 self.h = _e((R, I), bf, d)
             else:
@@ -204,7 +206,10 @@ class MoELayer:
                         dws1=self.dws1, dws2=self.dws2, dw_route=self.dw_route,
                         dlogits=self.dlogits,
                         **(dict(mx=c.mx_bwd, w2t_codes=self.w2tq, w2t_scales=self.w2ts,
-                                w1t_codes=self.w1tq, w1t_scales=self.w1ts) if c.mx else {}))
+                                w1t_codes=self.w1tq, w1t_scales=self.w1ts,
+                                xp_codes=self.xq if c.mx_bwd == 2 else None,
+                                xp_scales=self.xs if c.mx_bwd == 2 else None)
+                           if c.mx else {}))
 
     # ------------------------------------------------------------------ steps
     def route(self):

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert moe.abi_version() == 6
+    assert moe.abi_version() == 7
     assert moe.strerror(0) == "ok"
     assert "workspace" in moe.strerror(-2)
     assert moe.strerror(12345) == "unknown error"

@@ -74,7 +74,10 @@ def test_mx_forward_saves():
     assert_close(bf(layer.gu), r["gu"], TOL_BF16, "gu")
     assert_close(bf(layer.h), r["h"], TOL_MX, "h")
     # xp: the dequantised dispatch codes are exactly the oracle's quantised xp
-    assert np.array_equal(bf(layer.xp), r["xp"])
+    xp = torch.empty(layer.R, wl.H, dtype=torch.bfloat16, device=DEV)
+    moe.mx_dequantize(layer.xq, layer.xs, layer.R, wl.H, xp)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf(xp), r["xp"])
 
 
 @pytest.mark.parametrize("mode", [1, 2])
@@ -117,10 +120,12 @@ def test_mx_backward_full_size_deterministic_and_near_bf16():
     assert digest(layer.dx, layer.dw1, layer.dw2) == d0
     got = {n: getattr(layer, n).float().clone() for n in ("dx", "dw1", "dw2")}
     a = layer.bargs
-    a.mx = 0
+    xp = torch.empty(layer.R, wl.H, dtype=torch.bfloat16, device=DEV)  # BF16 products read xp
+    moe.mx_dequantize(layer.xq, layer.xs, layer.R, wl.H, xp)
+    a.mx, a.xp = 0, xp.data_ptr()
     moe.moe_backward(a, layer.bwd_ws)
     torch.cuda.synchronize()
-    a.mx = 2
+    a.mx, a.xp = 2, None
     for n in got:
         ref = getattr(layer, n).float()
         rel = float(torch.linalg.norm(got[n] - ref) / torch.linalg.norm(ref))
@@ -154,3 +159,24 @@ def test_mx_backward_empty_expert_and_ragged_rows(mode):
     assert_close(bf(layer.dw1), g["dw1"], TOL_MX, "dw1")
     assert_close(bf(layer.dx), g["dx"], TOL_MX, "dx")
     assert not torch.any(layer.dw1[1] != 0) and not torch.any(layer.dw2[1] != 0)
+
+
+def test_mx_backward_xp_codes_match_dequantised_xp():
+    """MXFP8 weight gradients with xp given as the dispatch's codes (decoded by the token-axis
+    quantiser) and as a dequantised bf16 copy: every gradient bit for bit."""
+    wl, inp, layer = _mx_layer(T=200, R_share=1600)
+    layer.forward()
+    layer.backward()
+    torch.cuda.synchronize()
+    names = ("dx", "dw1", "dw2", "dw_route", "dlogits")
+    got = {n: getattr(layer, n).clone() for n in names}
+    a = layer.bargs
+    xp = torch.empty(layer.R, wl.H, dtype=torch.bfloat16, device=DEV)
+    moe.mx_dequantize(layer.xq, layer.xs, layer.R, wl.H, xp)
+    a.xp, a.xp_codes, a.xp_scales = xp.data_ptr(), None, None
+    for n in names:
+        getattr(layer, n).fill_(7)
+    moe.moe_backward(a, layer.bwd_ws)
+    torch.cuda.synchronize()
+    for n in names:
+        assert torch.equal(getattr(layer, n), got[n]), n
