@@ -180,3 +180,70 @@ def test_mx_backward_xp_codes_match_dequantised_xp():
     torch.cuda.synchronize()
     for n in names:
         assert torch.equal(getattr(layer, n), got[n]), n
+
+
+def test_mx_backward_full_size_sampled_against_oracle():
+    """Full EP-64 share, MXFP8 forward then the MXFP8 backward (dgrad and weight gradients),
+    against the oracle on sampled outputs it computes from the seeded inputs alone: dX, the
+    routing-weight and logit gradients of sampled tokens (their rows' forward and dgrad at
+    full width), and the weight gradients of one 32-channel block of the largest, smallest and
+    a median expert.  A whole 32-channel block keeps every MX block the slice touches intact:
+    h is quantised along I in blocks of 32, W2^T and W1 rows along H, and the weight-gradient
+    operands along each expert's tokens, column by column."""
+    from test_gpu_layer import _check_routing
+    wl = wk.WORKLOADS["dsv3_ep64_mxfp8"].scaled(backward=True)
+    inp, layer = build_layer(wl)
+    layer.forward()
+    layer.backward()
+    torch.cuda.synchronize()
+    p = oracle_params(wl, inp, weights=False)
+    L, idx, w, lidx, offsets, pos, src = _check_routing(wl, inp, layer, p)
+    k, H, I = lidx.shape[1], wl.H, wl.I
+    dq = lambda a: orc.mx_dequantize(*orc.mx_quantize(a))
+    xall = orc.bf16_to_f64(p["x"])
+    doutall = orc.bf16_to_f64(wk.bf16_bits(inp["dout"]))
+    rs = np.random.default_rng(11)
+    # sampled tokens: their rows through the forward and the MXFP8 dgrad, at full width
+    ts = np.sort(rs.choice(wl.T, size=4, replace=False))
+    yref = np.zeros((len(ts), k, H))
+    dxp = np.zeros((len(ts), k, H))
+    for e in np.unique(lidx[ts]):
+        sel = np.argwhere(lidx[ts] == e)
+        w1e, w2e = bf(inp["w1"][e:e + 1]), bf(inp["w2"][e:e + 1])
+        xs_ = dq(xall[ts][sel[:, 0]])
+        off = np.array([0, len(sel)], np.int32)
+        ye, gu, h = orc.ffn_fwd(xs_, off, dq(w1e), dq(w2e), h_mx=True, want_gu=True, want_h=True)
+        yref[sel[:, 0], sel[:, 1]] = ye
+        dy = w[ts][sel[:, 0], sel[:, 1]][:, None] * doutall[ts][sel[:, 0]]
+        dxe, _, _, _ = orc.ffn_bwd_mx(xs_, off, w1e, w2e, dy, gu, h)
+        dxp[sel[:, 0], sel[:, 1]] = dxe
+    tsd = torch.from_numpy(ts).cuda()
+    assert_close(bf(layer.dx[tsd]), dxp.sum(1), TOL_MX, "dx[sampled tokens]")
+    dwr = np.einsum("tc,tjc->tj", doutall[ts], yref)
+    assert_close(host(layer.dw_route)[ts], dwr, TOL_MX, "dw_route[sampled]")
+    dL = orc.router_bwd(L[ts].astype(np.float64), idx[ts], dwr, wl.score, wl.renorm,
+                        wl.route_scale)
+    assert_close(host(layer.dlogits)[ts], dL, TOL_MX, "dlogits[sampled]")
+    # weight gradients of one 32-channel block of sampled experts
+    counts = np.diff(offsets)
+    nz = np.nonzero(counts)[0]
+    exps = sorted({int(nz[np.argmax(counts[nz])]), int(nz[np.argmin(counts[nz])]),
+                   int(nz[len(nz) // 2])})
+    c0 = 32 * int(rs.integers(0, I // 32))
+    ch = np.arange(c0, c0 + 32)
+    rows_w1 = np.concatenate([ch, I + ch])
+    rw1, cw2 = torch.from_numpy(rows_w1).cuda(), torch.from_numpy(ch).cuda()
+    for e in exps:
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        pr = src[a:b]
+        tt, jj = pr // k, pr % k
+        print(f"    expert {e}: {b - a} rows, channels {c0}..{c0 + 31}", flush=True)
+        xe = dq(xall[tt])
+        w1s = bf(inp["w1"][e][rw1])[None]
+        w2s = bf(inp["w2"][e][:, cw2])[None]
+        off = np.array([0, b - a], np.int32)
+        _, gu, h = orc.ffn_fwd(xe, off, dq(w1s), dq(w2s), h_mx=True, want_gu=True, want_h=True)
+        dy = w[tt, jj][:, None] * doutall[tt]
+        _, _, dw1, dw2 = orc.ffn_bwd_mx(xe, off, w1s, w2s, dy, gu, h, mx_wgrad=True)
+        assert_close(bf(layer.dw1[e][rw1]), dw1[0], TOL_MX, f"dw1[e={e}, channel block]")
+        assert_close(bf(layer.dw2[e][:, cw2]), dw2[0], TOL_MX, f"dw2[e={e}, channel block]")
