@@ -336,8 +336,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print("bench.py measures one GPU's share of the layer on one GPU; runs on more than one "
-              "GPU are not part of this build (--gpus must be 1).", file=sys.stderr)
+        print("bench.py measures one GPU's share of the layer on one GPU; the expert-parallel "
+              "path across GPUs is not implemented (--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
     import torch
     import workloads as wk
