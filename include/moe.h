@@ -155,10 +155,10 @@ int moe_dispatch(const void *x, int T, int H, int k, const int32_t *src, const i
  *   (per-row-block counters in the workspace, cleared by a small kernel before the launch),
  *   so the second product fills the first one's last, partial round.  With gu_save, or
  *   without a workspace (h_save given), the two products run as two launches.  Both forms
- *   give bit-identical outputs.  A queue wait is bounded (2 s):
- *   past it the uint32 at byte moe_ffn_error_offset() of the workspace becomes nonzero (it is
- *   zero after every good call with R > 0) and the outputs are not valid.  Calls that share a
- *   workspace must be stream-ordered. */
+ *   give bit-identical outputs.  The queue form clears its counters and the uint32 at byte
+ *   moe_ffn_error_offset() of the workspace before it starts; a queue wait is bounded (2 s),
+ *   and past it that word becomes nonzero and the outputs are not valid.  The two-launch form
+ *   does not touch the word.  Calls that share a workspace must be stream-ordered. */
 size_t moe_ffn_workspace_size(int dtype, int E, int R, int H, int I, int shared);
 size_t moe_ffn_error_offset(void);
 int moe_expert_ffn(int dtype, const void *xp, const uint8_t *xp_scales, const int32_t *offsets,

@@ -174,15 +174,13 @@ extern "C" int moe_expert_ffn(int dtype, const void* xp, const uint8_t* xp_scale
         // counts itself done; with the g|u saves that flush also carries the saves' dirty
         // lines and measured slower than two launches (1.29 against 1.27 ms at the EP-64
         // share), without them faster (1.21 against 1.23 ms).  So: saves -> two launches.
-        if (!have_ws || gu_save)
-            return moe_ffn_bf16((const bf16_t*)xp, offsets, E, R, H, I, (const bf16_t*)w1,
-                                (const bf16_t*)w2, (bf16_t*)gu_save,
-                                h_save ? (bf16_t*)h_save
-                                       : (bf16_t*)((char*)ws + moe_ffn_sync_bytes(
-                                                              E, R, offsets == nullptr)),
-                                (bf16_t*)y, st);
+        // h: the caller's save, else the workspace after the synchronisation words (a
+        // workspace is there whenever h_save is not: checked above)
         const size_t sync = moe_ffn_sync_bytes(E, R, offsets == nullptr);
         bf16_t* h = h_save ? (bf16_t*)h_save : (bf16_t*)((char*)ws + sync);
+        if (!have_ws || gu_save)
+            return moe_ffn_bf16((const bf16_t*)xp, offsets, E, R, H, I, (const bf16_t*)w1,
+                                (const bf16_t*)w2, (bf16_t*)gu_save, h, (bf16_t*)y, st);
         return moe_ffn_bf16_queue((const bf16_t*)xp, offsets, E, R, H, I, (const bf16_t*)w1,
                                   (const bf16_t*)w2, (bf16_t*)gu_save, h, (bf16_t*)y,
                                   (unsigned*)ws, st);
