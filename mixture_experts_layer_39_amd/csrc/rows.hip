@@ -94,8 +94,11 @@ __global__ __launch_bounds__(256) void dispatch_mx_kernel(const bf16_t* __restri
     scales[(size_t)r * nb + b] = (uint8_t)sc;
 }
 
-// Token-driven MX dispatch: one thread per 32-value block of a source token, quantised once
-// and written to each of the token's k destination rows.
+// Token-driven dispatch with MX quantisation: one thread per 8 values (a 16-byte chunk) of a
+// source row, four consecutive lanes per 32-value block, so a wave reads 1 KB of the row and
+// writes 512 bytes of codes in one piece.  The block maximum takes two exchanges between the
+// four lanes; the codes and scale are those of mx_block (same maximum, scale rule and
+// encoder).  Each chunk's codes and its bf16 copy (xp, optional) go to all k rows.
 __global__ __launch_bounds__(256) void dispatch_mx_tok_kernel(const bf16_t* __restrict__ x, int H,
                                                               int k, const int32_t* __restrict__ pos,
                                                               int R, bf16_t* __restrict__ xp,
@@ -103,37 +106,35 @@ __global__ __launch_bounds__(256) void dispatch_mx_tok_kernel(const bf16_t* __re
                                                               uint8_t* __restrict__ scales) {
     __shared__ int sp[MAXK];
     const int t = blockIdx.y;
-    const int nb = H / 32;
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    const bool live = b < nb;
-    const bf16_t* in = x + (size_t)t * H + (live ? b : 0) * 32;
-    u32x4 raw[4];
-    float v[32];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) raw[c] = ld16(in + c * 8);
+    const int nc = H / 8, nb = H / 32;
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;  // chunk; block c / 4
+    const bool live = c < nc;  // H % 32 == 0: a block's four lanes are all live or all not
+    const u32x4 raw = live ? ld16(x + (size_t)t * H + c * 8) : u32x4{0, 0, 0, 0};
     if (threadIdx.x < k) sp[threadIdx.x] = pos[(size_t)t * k + threadIdx.x];
+    float v[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[2 * j] = lo_bf(raw[j]);
+        v[2 * j + 1] = hi_bf(raw[j]);
+        amax = fmaxf(amax, fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1])));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int sc = mx_scale_code(amax, MOE_MX_FLOOR);
+    const int sh = 127 - sc;
+    const uint2 q = make_uint2(e4m3x4(ldexpf(v[0], sh), ldexpf(v[1], sh), ldexpf(v[2], sh),
+                                      ldexpf(v[3], sh)),
+                               e4m3x4(ldexpf(v[4], sh), ldexpf(v[5], sh), ldexpf(v[6], sh),
+                                      ldexpf(v[7], sh)));
     __syncthreads();
     if (!live) return;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            v[c * 8 + 2 * j] = lo_bf(raw[c][j]);
-            v[c * 8 + 2 * j + 1] = hi_bf(raw[c][j]);
-        }
-    uint32_t q[8];
-    const int sc = mx_block(v, MOE_MX_FLOOR, q);
     for (int j = 0; j < k; ++j) {
         const int r = sp[j];
         if (r < 0 || r >= R) continue;
-        if (xp) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) st16(xp + (size_t)r * H + b * 32 + c * 8, raw[c]);
-        }
-        uint8_t* co = codes + (size_t)r * H + b * 32;
-        st16(co, u32x4{q[0], q[1], q[2], q[3]});
-        st16(co + 16, u32x4{q[4], q[5], q[6], q[7]});
-        scales[(size_t)r * nb + b] = (uint8_t)sc;
+        if (xp) st16(xp + (size_t)r * H + c * 8, raw);
+        *reinterpret_cast<uint2*>(codes + (size_t)r * H + c * 8) = q;
+        if ((c & 3) == 0) scales[(size_t)r * nb + c / 4] = (uint8_t)sc;
     }
 }
 
@@ -718,8 +719,8 @@ extern "C" int moe_dispatch(const void* x, int T, int H, int k, const int32_t* s
     int64_t n_pairs = (int64_t)T * k;
     if (pos) {
         if (xp_codes) {
-            int nb = H / 32;
-            dim3 grid((nb + 255) / 256, T);
+            const int nc = H / 8;  // 16-byte chunks of a row, one per thread
+            dim3 grid((nc + 255) / 256, T);
             MOE_TRACED("dispatch_mx", st,
                        dispatch_mx_tok_kernel<<<grid, 256, 0, st>>>((const bf16_t*)x, H, k, pos, R,
                                                                     (bf16_t*)xp, xp_codes,

@@ -139,6 +139,12 @@ def test_dispatch_bit_exact_and_mx():
     torch.cuda.synchronize()
     assert np.array_equal(wk.bf16_bits(xp3), ref)
     assert torch.equal(xq3, xq) and torch.equal(xs3, xs)
+    # token-driven MX form that also writes the bf16 rows
+    xp4, xq4, xs4 = torch.empty_like(xp), torch.empty_like(xq), torch.empty_like(xs)
+    moe.moe_dispatch(x, T, H, k, None, R, xp4, xq4, xs4, pos=pos_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(wk.bf16_bits(xp4), ref)
+    assert torch.equal(xq4, xq) and torch.equal(xs4, xs)
     cq, cs = orc.mx_quantize(orc.bf16_to_f64(ref))
     assert np.array_equal(host(xq), cq) and np.array_equal(host(xs), cs)
 
