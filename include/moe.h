@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 
 /* return codes */
 #define MOE_OK 0
@@ -96,6 +96,9 @@ size_t moe_route_workspace_size(int T, int k, int E);
  *   pos      [T,k] int32  row of pair (t,j) in expert-contiguous order; rows of one expert are
  *            in ascending (t,j) order.
  *   src      [T*k] int32  inverse of pos: src[pos[t,j]] = t*k + j.
+ *   counts/offsets and pos/src are optional in pairs: all four NULL computes the selection
+ *   alone (idx, w, s_sel; not with idx_in); counts and offsets without pos and src compute
+ *   the loads but no permutation; pos and src need counts and offsets.
  * Limits: 1 <= k <= min(E, 64), E <= 1024, T >= 0, H % 8 == 0 when projecting.
  * Outputs are bit-exact functions of the inputs. */
 int moe_route(const float *logits, const void *x, const void *w_router, int T, int H, int E,

@@ -99,7 +99,10 @@ extern "C" int moe_route(const float* logits, const void* x, const void* w_route
                          int32_t* idx, float* w, float* s_sel, int32_t* counts, int32_t* offsets,
                          int32_t* pos, int32_t* src, void* ws, size_t ws_bytes, void* stream) {
     MOE_REQUIRE(T >= 0 && E >= 1 && E <= 1024 && k >= 1 && k <= 64);
-    MOE_REQUIRE(counts && offsets && (T == 0 || (pos && src)));
+    // permutation outputs: none (selection only), counts + offsets (the loads), or all four
+    MOE_REQUIRE((counts == nullptr) == (offsets == nullptr) && (pos == nullptr) == (src == nullptr));
+    MOE_REQUIRE(!pos || counts);
+    MOE_REQUIRE(counts || !idx_in);                       // given ids: nothing but permuting
     MOE_REQUIRE((x == nullptr) == (w_router == nullptr));
     int n_groups = 1, topk_groups = 1, per_group = 1;
     if (!idx_in) {
@@ -143,6 +146,7 @@ extern "C" int moe_route(const float* logits, const void* x, const void* w_route
                    else topk_kernel<16><<<grid, block, 0, st>>>(p));
         MOE_LAUNCH_CHECK();
     }
+    if (!counts) return MOE_OK;  // selection only
     const int32_t* ids = idx_in ? idx_in : idx;
     int nch = (int)((n + CHUNK - 1) / CHUNK);
     int32_t* blk = (int32_t*)ws;
@@ -153,7 +157,7 @@ extern "C" int moe_route(const float* logits, const void* x, const void* w_route
     }
     MOE_TRACED("perm_scan", st, scan_kernel<<<1, 1024, 0, st>>>(blk, nch, E, counts, offsets));
     MOE_LAUNCH_CHECK();
-    if (nch > 0) {
+    if (nch > 0 && pos) {
         int nbits = 0;
         while ((1 << nbits) < E) ++nbits;
         MOE_TRACED("perm_rank", st,

@@ -124,11 +124,9 @@ class MoELayer:
         self.route_ws = _e((max(route_workspace_size(T, kr, E),
                                 route_workspace_size(T, self.k_router, ER), 256),),
                            torch.uint8, d)
-        if c.local_share:   # router outputs over E_router experts, kept apart
+        if c.local_share:   # the loads over the E_router experts (load-balancing bias)
             self.g_counts = _e((ER,), i32, d)
             self.g_offsets = _e((ER + 1,), i32, d)
-            self.g_pos = _e((T, self.k_router), i32, d)
-            self.g_src = _e((T * self.k_router,), i32, d)
         # expert FFN
         if c.mx:
             self.xq = _e((R, H), torch.uint8, d)
@@ -217,9 +215,14 @@ class MoELayer:
         common = dict(score=c.score, n_groups=c.n_groups, topk_groups=c.topk_groups,
                       renorm=c.renorm, route_scale=c.route_scale, ws=self.route_ws)
         if c.local_share:
+            # the selection over all E_router experts (a permutation of it would feed the
+            # exchange between GPUs, which one GPU's share does not have); the loads only
+            # when the load-balancing bias needs them
+            want_loads = c.bias_gamma > 0
             moe_route(self.logits, c.T, c.ER, self.k_router, idx=self.idx, w=self.w,
-                      s_sel=self.s_sel, counts=self.g_counts, offsets=self.g_offsets,
-                      pos=self.g_pos, src=self.g_src, sel_bias=self.sel_bias, **common)
+                      s_sel=self.s_sel, counts=self.g_counts if want_loads else None,
+                      offsets=self.g_offsets if want_loads else None, pos=None, src=None,
+                      sel_bias=self.sel_bias, **common)
             moe_route(None, c.T, c.E, self.kr, idx_in=inp["idx_local"], counts=self.counts,
                       offsets=self.offsets, pos=self.pos, src=self.src, **common)
             loads = self.g_counts

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert moe.abi_version() == 7
+    assert moe.abi_version() == 8
     assert moe.strerror(0) == "ok"
     assert "workspace" in moe.strerror(-2)
     assert moe.strerror(12345) == "unknown error"
@@ -61,7 +61,10 @@ def test_route_validation():
     assert route(k=9) == moe.MOE_EINVAL                  # k > E
     assert route(k=0) == moe.MOE_EINVAL
     assert route(E=2000) == moe.MOE_EINVAL               # E > 1024
-    assert route(counts=None) == moe.MOE_EINVAL
+    assert route(counts=None) == moe.MOE_EINVAL                       # counts without offsets
+    assert route(pos=None) == moe.MOE_EINVAL                          # src without pos
+    assert route(counts=None, offsets=None) == moe.MOE_EINVAL         # pos/src need counts
+    assert route(idx_in=FAKE, counts=None, offsets=None, pos=None, src=None) == moe.MOE_EINVAL
     assert route(x=FAKE) == moe.MOE_EINVAL               # x without w_router
     assert route(cfg=moe.RouteCfg(7, 1, 1, 1, 1.0, None)) == moe.MOE_EINVAL
     assert route(cfg=moe.RouteCfg(1, 3, 1, 1, 1.0, None)) == moe.MOE_EINVAL   # E % groups

@@ -373,3 +373,32 @@ def test_expert_ffn_one_launch_shared_mode_bit_identical():
         outs.append((y, h, ws))
     assert moe.ffn_error(outs[1][2]) == 0
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_route_selection_only_and_loads_only():
+    """moe_route without permutation outputs (selection only) and with counts and offsets alone
+    (the loads): the outputs it does write equal those of the full call, bit for bit."""
+    T, E, k = 2048, 256, 8
+    L = torch.from_numpy(np.random.default_rng(21).standard_normal((T, E)).astype(np.float32)).to(DEV)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(moe.route_workspace_size(T, k, E), 256), dtype=torch.uint8, device=DEV)
+    outs = []
+    for mode in ("full", "loads", "select"):
+        o = dict(idx=torch.full((T, k), -7, **i32), w=torch.full((T, k), -7.0, device=DEV),
+                 s_sel=torch.full((T, k), -7.0, device=DEV), counts=torch.full((E,), -7, **i32),
+                 offsets=torch.full((E + 1,), -7, **i32), pos=torch.full((T, k), -7, **i32),
+                 src=torch.full((T * k,), -7, **i32))
+        kw = dict(o)
+        if mode != "full":
+            kw["pos"] = kw["src"] = None
+        if mode == "select":
+            kw["counts"] = kw["offsets"] = None
+        moe.moe_route(L, T, E, k, score=wk.SIGMOID, ws=ws, **kw)
+        torch.cuda.synchronize()
+        outs.append(o)
+    full, loads, select = outs
+    for n in ("idx", "w", "s_sel"):
+        assert torch.equal(loads[n], full[n]) and torch.equal(select[n], full[n]), n
+    assert torch.equal(loads["counts"], full["counts"])
+    assert torch.equal(loads["offsets"], full["offsets"])
+    assert torch.all(loads["pos"] == -7) and torch.all(select["counts"] == -7)
