@@ -18,6 +18,8 @@ its algorithmic flops (or bytes) per launch over its average launch duration, me
 HIP events the library records around each of its launches on the launch stream, over K more
 steps run after the timed ones (the event records add gaps between launches, not kernel
 time; `traced_ms_per_step` is the step time with them).
+`cold_tokens_per_s` times the same steps one by one with cold caches (a 1 GiB read before each
+step evicts L2 and the Infinity Cache).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -283,6 +285,30 @@ def write_traffic(folder: str, workload: str, copy_mib: int) -> None:
           f"wrote {path}")
 
 
+def cold_ms_per_call(f, calls: int, flush_mib: int = 1024) -> float:
+    """Average device time of f() with cold caches.  Before each call a reduction reads
+    flush_mib MiB (four times the 256 MB Infinity Cache, and far beyond the L2s), which
+    writes back and evicts whatever the previous call left there, and leaves only clean lines
+    of the flush buffer behind.  HIP events on the launch stream bracket f() alone; the host
+    never waits inside the loop, so the launches queue ahead of the device."""
+    import torch
+    # float32: the reduction reads the buffer as it is (an integer sum would widen it first)
+    buf = torch.ones(flush_mib << 18, dtype=torch.float32, device="cuda:0")
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(calls)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(calls)]
+    f()
+    torch.cuda.synchronize()
+    for i in range(calls):
+        buf.sum()
+        starts[i].record()
+        f()
+        ends[i].record()
+    torch.cuda.synchronize()
+    ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / calls
+    del buf
+    return ms
+
+
 def copy_calibration(mib: int) -> None:
     """A plain device copy of known size (read mib MiB, write mib MiB), five times."""
     import torch
@@ -414,6 +440,8 @@ def main():
 
     fwd_ms = time_fwd(layer.forward)
     fused_ms = time_fwd(layer.forward_fused) if can_fuse else None
+    cold_ms = cold_ms_per_call(step, a.steps)
+    cold_fwd_ms = cold_ms_per_call(layer.forward, a.steps)
 
     # per-role statistics over the traced steps
     roles: dict[str, list[float]] = {}
@@ -470,6 +498,9 @@ def main():
         "fwd_ms_per_step": round(fwd_ms, 4),
         "step_tflops": round(flops_step / (ms_step * 1e-3) / 1e12, 1),
         "fwd_tflops": round(flops_fwd / (fwd_ms * 1e-3) / 1e12, 1),
+        "cold_tokens_per_s": round(wl.T / (cold_ms * 1e-3), 1),
+        "cold_ms_per_step": round(cold_ms, 4),
+        "cold_fwd_ms_per_step": round(cold_fwd_ms, 4),
         "fused_fwd_ms_per_step": round(fused_ms, 4) if fused_ms else None,
         "fused_fwd_tokens_per_s": round(wl.T / (fused_ms * 1e-3), 1) if fused_ms else None,
         "roofline": roof,
