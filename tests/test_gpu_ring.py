@@ -80,18 +80,22 @@ def test_ring_against_oracle():
 
 def test_ring_full_size_bit_identical_to_unstreamed():
     wl = wk.WORKLOADS["dsv3_e256_zipf"]
-    inp, base, rings = _layers(wl, wl.minibatch, [4])
-    ring = rings[4]
+    inp, base, rings = _layers(wl, wl.minibatch, [2, 4, 16])
     _run(base)
-    _run(ring)
     torch.cuda.synchronize()
-    _check_conservation(wl, ring)
-    for name in ("out", "dx", "dlogits"):
-        assert digest(getattr(ring, name)) == digest(getattr(base, name)), name
     rs = np.random.default_rng(3)
-    for e in rs.choice(wl.E, 3, replace=False):
-        assert_close(bf(ring.dw1[e]), bf(base.dw1[e]), TOL_BF16, f"dw1[{e}]")
-        assert_close(bf(ring.dw2[e]), bf(base.dw2[e]), TOL_BF16, f"dw2[{e}]")
+    sample = rs.choice(wl.E, 3, replace=False)
+    for D, ring in rings.items():   # 8 passes, 4 passes, one pass over the 16 minibatches
+        print(f"    ring depth {D}: {ring.passes} passes", flush=True)
+        _run(ring)
+        torch.cuda.synchronize()
+        _check_conservation(wl, ring)
+        for name in ("out", "dx", "dlogits"):
+            assert digest(getattr(ring, name)) == digest(getattr(base, name)), (D, name)
+        for e in sample:
+            assert_close(bf(ring.dw1[e]), bf(base.dw1[e]), TOL_BF16, f"D={D} dw1[{e}]")
+            assert_close(bf(ring.dw2[e]), bf(base.dw2[e]), TOL_BF16, f"D={D} dw2[{e}]")
+    ring = rings[4]
     hashes = set()
     for _ in range(2):
         _run(ring)
