@@ -350,9 +350,22 @@ def cpu_baseline(wl, inp, n_tokens: int) -> dict:
     rows = int(p["idx_local"].size) if "idx_local" in p else n * wl.k
     what = "forward+backward" if wl.backward else "forward"
     return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": orc.threads(),
-            "kind": "oracle", "seconds": round(dt, 2),
+            "cpu": _cpu_model(), "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"first {n} of {wl.T} source tokens ({rows} routed rows) with the full "
                       f"expert weights, oracle {what} in fp64"}
+
+
+def _cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo), or the platform's."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
 
 
 # ----------------------------------------------------------------------------- main

@@ -80,7 +80,11 @@ typedef struct moe_route_cfg {
 
 size_t moe_route_workspace_size(int T, int k, int E);
 
-/* moe_route: top-k routing plus the expert-contiguous permutation.
+/* moe_route: top-k routing plus the expert-contiguous permutation -- the router of the
+ * DeepSeek-V3-type layer the pages name (pulsen.vercel.app, "Cursor åpner megakernelen…",
+ * ¶6: sigmoid or softmax scores, optionally group-limited) and the per-expert row order its
+ * dispatch needs ("pull": the expert-side rows fetch their tokens, same page ¶5), computed
+ * with no host readback (aiexpert.news ¶3) and bit for bit reproducibly (pulsen ¶3-¶4).
  *   logits   [T,E] fp32.  Read; or, when w_router != NULL, first WRITTEN with the router
  *            projection logits[t,e] = sum_h x[t,h]*w_router[e,h], accumulated in fp32 in
  *            ascending h (exact products, so the result is fixed bit for bit).
@@ -135,7 +139,9 @@ int moe_dispatch(const void *x, int T, int H, int k, const int32_t *src, const i
                  int R, void *xp, uint8_t *xp_codes, uint8_t *xp_scales, void *stream);
 
 /* ------------------------------------------------------------------ expert FFN
- * moe_expert_ffn: per expert e, for its rows r in [offsets[e], offsets[e+1]):
+ * moe_expert_ffn: the experts of the DeepSeek-V3-type layer (pulsen.vercel.app ¶6) as
+ * grouped GEMMs, in BF16 or MXFP8 (the two forward precisions the pages report: pulsen ¶3,
+ * aiexpert.news ¶4).  Per expert e, for its rows r in [offsets[e], offsets[e+1]):
  *   [g | u] = xp_r . w1[e]^T  (w1[e] is [2I,H]: gate rows 0..I-1 over up rows I..2I-1),
  *   h = silu(g) * u,  y_r = h . w2[e]^T  (w2[e] is [H,I]);  fp32 accumulation.
  * The offsets are read on the device (no host readback); each expert's tile list is derived
@@ -304,6 +310,8 @@ size_t moe_backward_workspace_size(const moe_bwd_args *a);
 int moe_backward(const moe_bwd_args *a, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------ MX quantisation
+ * The operands of the MXFP8 forward (pulsen.vercel.app ¶3; aiexpert.news ¶4, whose headline
+ * speed-up is for that precision), in the OCP Microscaling (MX) v1.0 format.
  * mx_quantize: OCP microscaling, one E8M0 scale per 32 consecutive values along K and E4M3
  * ("FN": bias 7, no infinity, max 448) codes, rounded to nearest even and saturating.
  * MOE_MX_FLOOR: scale 2^(floor(log2 amax) - 8); MOE_MX_CEIL: smallest power of two with

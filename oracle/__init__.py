@@ -17,20 +17,30 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
-_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+# MOE_ORACLE_SANITIZE=1 selects a build with AddressSanitizer and UndefinedBehaviorSanitizer
+# (host code only; the process must preload libasan), used by the sanitizer pin run.
+SANITIZE = os.environ.get("MOE_ORACLE_SANITIZE", "") == "1"
+_LIB = os.path.join(_HERE, "libmoe_oracle_san.so" if SANITIZE else "libmoe_oracle.so")
 _lib = None
 
 SOFTMAX, SIGMOID = 0, 1
 
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+             "-fno-omit-frame-pointer", "-g"]
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (plain -O2, no fast-math, no FMA contraction)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+
+def build(force: bool = True, sanitize: bool | None = None) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math, no FMA contraction); with
+    `sanitize`, the AddressSanitizer + UndefinedBehaviorSanitizer build."""
+    san = SANITIZE if sanitize is None else sanitize
+    out = os.path.join(_HERE, "libmoe_oracle_san.so" if san else "libmoe_oracle.so")
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(_SRC):
+        tmp = out + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c99", "-fopenmp", "-ffp-contract=off",
-                               "-fno-fast-math", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+                               "-fno-fast-math", "-fPIC", "-shared"] + (SAN_FLAGS if san else [])
+                              + [_SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, out)
+    return out
 
 
 def lib():
@@ -315,22 +325,49 @@ def mx_dequantize(codes, scales):
 
 
 # ----------------------------------------------------------------------------- the layer
+def _vals(a) -> np.ndarray:
+    """A layer input as fp64 values: bf16 bit patterns (uint16) are converted exactly; fp64
+    arrays are taken as they are (the finite-difference pins perturb them continuously)."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return bf16_to_f64(a)
+    if a.dtype != np.float64:
+        raise TypeError("layer inputs are bf16 bit patterns (uint16) or fp64 values")
+    return np.ascontiguousarray(a)
+
+
+def _gather_rows(x, k, src) -> np.ndarray:
+    """Dispatch of [T,H] rows by src: bf16 bits through orc_dispatch, fp64 values through the
+    same byte copy (each fp64 value is four 16-bit words of its row)."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return dispatch(x, k, src)
+    x = np.ascontiguousarray(x, np.float64)
+    T, H = x.shape
+    words = dispatch(x.view(np.uint16).reshape(T, 4 * H), k, src)
+    return words.view(np.float64).reshape(len(src), H)
+
+
 def layer_forward(p: dict) -> dict:
     """Whole forward of the layer.
 
-    p: x [T,H] bf16 bits; logits [T,ER] f32 (or w_router [ER,H] bf16 bits); k; score;
-    renorm; route_scale; n_groups; topk_groups; bias (optional); w1/w2 [E,..] bf16 bits;
-    optional idx_local [T,k'] (one GPU's share: local expert per routed pair) with E;
-    optional ws1/ws2 (shared experts); mx (bool).
+    p: x [T,H]; logits [T,ER] (or w_router [ER,H] bf16 bits); k; score; renorm; route_scale;
+    n_groups; topk_groups; bias (optional); w1/w2 [E,..]; optional idx_local [T,k'] (one
+    GPU's share: local expert per routed pair) with E; optional ws1/ws2 (shared experts);
+    mx (bool).  x and the weights are bf16 bit patterns (uint16), or fp64 values (BF16 path
+    only).  The logits select in fp32 (as given in fp32, or rounded from fp64 values) and
+    weight in fp64.
     Returns every intermediate the backward needs plus `out` [T,H] f64.
     """
     r = {}
     if "w_router" in p:
         r["logits"] = router_logits(p["x"], p["w_router"])
+    elif np.asarray(p["logits"]).dtype == np.float64:
+        r["logits"] = np.ascontiguousarray(p["logits"])
     else:
         r["logits"] = _c(p["logits"], np.float32)
-    idx, s_sel = route_select(r["logits"], p["k"], p["score"], p.get("n_groups", 1),
-                              p.get("topk_groups", 1), p.get("bias"))
+    idx, s_sel = route_select(r["logits"].astype(np.float32), p["k"], p["score"],
+                              p.get("n_groups", 1), p.get("topk_groups", 1), p.get("bias"))
     r["idx"], r["s_sel"] = idx, s_sel
     r["w"] = route_weights(r["logits"].astype(np.float64), idx, p["score"],
                            p.get("renorm", True), p.get("route_scale", 1.0))
@@ -339,13 +376,16 @@ def layer_forward(p: dict) -> dict:
     kk = lidx.shape[1]
     counts, offsets, pos, src = permute(lidx, E)
     r.update(counts=counts, offsets=offsets, pos=pos, src=src)
-    xp_bits = dispatch(p["x"], kk, src)
-    r["xp_bits"] = xp_bits
-    w1 = bf16_to_f64(p["w1"])
-    w2 = bf16_to_f64(p["w2"])
-    xp = bf16_to_f64(xp_bits)
+    xp_rows = _gather_rows(p["x"], kk, src)
+    if xp_rows.dtype == np.uint16:
+        r["xp_bits"] = xp_rows
+    w1 = _vals(p["w1"])
+    w2 = _vals(p["w2"])
+    xp = _vals(xp_rows)
     mx = p.get("mx", False)
     if mx:
+        if np.asarray(p["x"]).dtype != np.uint16:
+            raise TypeError("the MXFP8 forward takes bf16 inputs")
         xq = mx_quantize(xp)
         xp = mx_dequantize(*xq)
         w1 = mx_dequantize(*mx_quantize(w1))
@@ -354,22 +394,23 @@ def layer_forward(p: dict) -> dict:
     y, gu, h = ffn_fwd(xp, offsets, w1, w2, h_mx=mx, want_gu=True, want_h=True)
     r.update(y=y, gu=gu, h=h)
     ys = None
-    x64 = bf16_to_f64(p["x"])
+    x64 = _vals(p["x"])
     r["x"] = x64
     if p.get("ws1") is not None and p["ws1"].shape[0] > 0:
-        ws1, ws2 = bf16_to_f64(p["ws1"]), bf16_to_f64(p["ws2"])
+        ws1, ws2 = _vals(p["ws1"]), _vals(p["ws2"])
         ys, _, _ = ffn_fwd(x64, None, ws1, ws2)
         r["ys"] = ys
     r["out"] = combine(y, pos, r["w"], ys)
     return r
 
 
-def layer_backward(p: dict, r: dict, dout_bf16) -> dict:
+def layer_backward(p: dict, r: dict, dout) -> dict:
     """Whole backward in fp64 given the forward record `r`: BF16-storage products, or after
     an MXFP8 forward (p["mx"]) MXFP8 dgrad products, and with p["mx_wgrad"] MXFP8 weight-
-    gradient products too (ffn_bwd_mx)."""
-    dout = bf16_to_f64(dout_bf16)
-    w1, w2 = bf16_to_f64(p["w1"]), bf16_to_f64(p["w2"])
+    gradient products too (ffn_bwd_mx).  dout [T,H]: bf16 bits or fp64 values.
+    Returns dx, dw1, dw2 (and dws1, dws2 with shared experts), dw_route [T,k] and dlogits."""
+    dout = _vals(dout)
+    w1, w2 = _vals(p["w1"]), _vals(p["w2"])
     dy, dw = combine_bwd(dout, r["y"], r["pos"], r["w"])
     if p.get("mx", False):
         dxp, _, dw1, dw2 = ffn_bwd_mx(r["xp"], r["offsets"], w1, w2, dy, r["gu"], r["h"],
@@ -379,7 +420,7 @@ def layer_backward(p: dict, r: dict, dout_bf16) -> dict:
     g = {"dw_route": dw, "dw1": dw1, "dw2": dw2}
     dxs = None
     if p.get("ws1") is not None and p["ws1"].shape[0] > 0:
-        ws1, ws2 = bf16_to_f64(p["ws1"]), bf16_to_f64(p["ws2"])
+        ws1, ws2 = _vals(p["ws1"]), _vals(p["ws2"])
         S = ws1.shape[0]
         dys = np.broadcast_to(dout, (S,) + dout.shape).reshape(S * dout.shape[0], -1)
         dxs, dws1, dws2 = ffn_bwd(r["x"], None, ws1, ws2, dys)

@@ -178,12 +178,16 @@ def test_layer_full_size_sampled(name):
                               chans)
 
 
-@pytest.mark.parametrize("name", ["mid_t2048", "dsv3_ep64", "dsv3_ep64_mxfp8"])
+@pytest.mark.parametrize("name", ["tiny_t128", "mid_t2048", "dsv3_ep64", "dsv3_ep64_mxfp8"])
 def test_layer_bit_identical_reruns(name):
     wl = wk.WORKLOADS[name]
     inp, layer = build_layer(wl)
     hashes = []
-    for _ in range(3):
+    for run in range(3):
+        # every output starts from a different byte pattern, so that a value a run does not
+        # write itself cannot pass for a reproduced one
+        for t in layer_outputs(layer).values():
+            t.view(torch.uint8).fill_((0x00, 0x5A, 0xC3)[run])
         layer.forward()
         if wl.backward:
             layer.backward()
