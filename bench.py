@@ -75,7 +75,7 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="add the backward to a forward-only workload (MXFP8: MXFP8 dgrad)")
     ap.add_argument("--fused", action="store_true",
-                    help="run each step's forward as one cooperative launch (moe_layer_forward)")
+                    help="run each step's forward as one launch (moe_layer_forward)")
     ap.add_argument("--bias-gamma", type=float, default=0.0,
                     help="> 0: the sigmoid router's load-balancing bias is updated from the "
                          "step's loads with this speed (auxiliary-loss-free balancing)")
@@ -441,7 +441,7 @@ def main():
     traced_ms_step = (t3 - t2) * 1e3 / a.steps
 
     # forward-only steps, untraced: the per-step calls, and (where it applies) the forward
-    # as one cooperative launch
+    # as one launch
     def time_fwd(f):
         for _ in range(2):
             f()
@@ -494,7 +494,7 @@ def main():
     if a.bias_gamma > 0:
         cfg.update(bias_gamma=a.bias_gamma)
     if a.fused:
-        cfg.update(forward="one cooperative launch")
+        cfg.update(forward="one launch")
     if wl.mx and wl.backward:
         cfg.update(backward_precision="mxfp8 dgrad, bf16 wgrad")
     out = {

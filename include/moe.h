@@ -187,7 +187,7 @@ int moe_combine(const void *y, const int32_t *pos, const float *w, int T, int k,
 /* ------------------------------------------------------------------ the forward in one launch
  * moe_layer_forward: the whole BF16 forward of the layer -- router projection (optional),
  * top-k routing, the expert-contiguous permutation, dispatch, the routed and shared experts'
- * GEMM1 + SwiGLU and GEMM2, and the weighted combine -- as ONE cooperative, persistent kernel
+ * GEMM1 + SwiGLU and GEMM2, and the weighted combine -- as ONE persistent kernel
  * launch (the single MoE kernel of pulsen.vercel.app ¶3 and ki-pruefstand.de "Kommunikation
  * im Kernel" ¶2, at one GPU): one block per compute unit walks each step's work and
  * device-wide barriers separate the steps, so no host round trip or launch gap sits between
@@ -210,14 +210,17 @@ int moe_combine(const void *y, const int32_t *pos, const float *w, int T, int k,
  *   hs [S,T,Is], ys [S,T,H] bf16;  gus [S,T,2Is] bf16 or NULL;  out [T,H] bf16.
  * Limits: 1 <= E <= 256, 1 <= E_router <= 256, 1 <= k <= min(E_router, 64), T >= 1,
  * 0 <= S <= 64, H % 64 == 0, I % 64 == 0 (Is too when S > 0), R*max(H,2I) < 2^31.
- * Execution: a one-block clear of the workspace's synchronisation words, then the cooperative
- * kernel with one block per CU (every block resident at once; MOE_EHIP if the device refuses
- * the launch).  Inside, the routing steps and the dispatch are separated by device-wide
- * barriers; the expert products and the combine form one queue of work items (GEMM1 tiles,
- * GEMM2 tiles, combine groups of tokens) claimed in order, each waiting only for the tiles it
- * reads (per-row-block completion counters).  Every wait is bounded (2 s): one that runs out
- * sets the 32-bit word at byte offset moe_layer_forward_error_offset() of ws to nonzero and
- * the outputs are then undefined; the word is 0 after a call that completed normally.
+ * Execution: a one-block clear of the workspace's synchronisation words, then the kernel as an
+ * ordinary launch of one block per CU (a block takes 160 KB of LDS, so no CU holds two; the
+ * device-wide barriers need every block resident, which an otherwise idle device gives at
+ * once, and work of other streams holding CUs only delays the start).  Inside, the routing
+ * steps, the dispatch and the combine are separated by device-wide barriers; the two expert
+ * products form one queue of tiles (GEMM1 tiles, then GEMM2 tiles) claimed in order, where a
+ * GEMM2 tile waits only for the GEMM1 tiles of its own rows (per-row-block completion
+ * counters).  Every wait is bounded (2 s): one that runs out (for instance on a device that
+ * can never hold all the blocks at once) sets the 32-bit word at byte offset
+ * moe_layer_forward_error_offset() of ws to nonzero and the outputs are then undefined; the
+ * word is 0 after a call that completed normally.
  * Concurrent calls need distinct workspaces.
  * Workspace: moe_layer_forward_workspace_size(). */
 typedef struct moe_fwd_args {

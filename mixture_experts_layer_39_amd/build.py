@@ -35,8 +35,11 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
                      if "packed-fp32-ops" not in l)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + errs)
-    if verbose and errs.strip():
-        print(errs)
+    n_warn = sum(1 for l in errs.splitlines() if ": warning:" in l)
+    if n_warn:
+        # every warning is reported, so that a new one cannot go unnoticed
+        print(f"hipcc: {n_warn} warning(s)", file=sys.stderr, flush=True)
+        print(errs, file=sys.stderr, flush=True)
     os.replace(tmp, LIB)
     return LIB
 

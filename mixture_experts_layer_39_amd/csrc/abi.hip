@@ -96,7 +96,7 @@ extern "C" int moe_trace_begin(int cap) {
         TraceRec r{"", nullptr, nullptr};
         if (hipEventCreate(&r.a) != hipSuccess) return MOE_EHIP;
         if (hipEventCreate(&r.b) != hipSuccess) {
-            hipEventDestroy(r.a);
+            (void)hipEventDestroy(r.a);
             return MOE_EHIP;
         }
         t.recs.push_back(r);

@@ -672,8 +672,8 @@ static int launch_pair(void (*kern)(GemmArgs, GemmArgs), const char* name, const
 
 // ---------------------------------------------------------------- the layer in one launch
 // The forward of the layer -- router projection, top-k routing, the expert-contiguous
-// permutation, dispatch, GEMM1 + SwiGLU, GEMM2 and the combine -- as one persistent,
-// cooperative kernel (the single fused MoE kernel of pulsen.vercel.app, "Cursor åpner
+// permutation, dispatch, GEMM1 + SwiGLU, GEMM2 and the combine -- as one persistent kernel
+// with every block resident at once (the single fused MoE kernel of pulsen.vercel.app, "Cursor åpner
 // megakernelen…", ¶3, and ki-pruefstand.de, "Cursor veröffentlicht MoE-Megakernel…",
 // "Kommunikation im Kernel" ¶2, on one GPU): one block per CU.  The routing steps, the
 // dispatch and the combine are separated by device-wide barriers.  The two expert products
@@ -685,7 +685,7 @@ static int launch_pair(void (*kern)(GemmArgs, GemmArgs), const char* name, const
 // with GEMM2 tiles.  Every item runs the same device code as its own kernel, so the outputs
 // are bit-identical to the step-by-step launches.  Claiming in order makes the queue
 // deadlock-free: a tile only waits for tiles claimed before it, which run on blocks that are
-// resident (a cooperative launch) and never wait for later tiles.
+// resident (they claimed it) and never wait for later tiles.
 // Visibility across XCDs: each XCD has its own L2, so a finished GEMM1 tile writes its L2
 // back (device-scope release) before it counts itself done; a GEMM2 tile drops stale lines
 // (acquire) before reading.  GEMM2 tiles do not signal: a write-back per tile of the second
@@ -1047,7 +1047,14 @@ extern "C" int moe_layer_forward(const moe_fwd_args* p, void* ws, size_t ws_byte
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         ncu < 1)
         return MOE_EHIP;
-    // one block per CU: every block of a cooperative launch must be resident at once
+    // One block per CU, as an ordinary launch.  The device-wide barriers need every block
+    // resident at once: a block needs 160 KB of LDS, so no CU holds two, and the ncu blocks
+    // of an otherwise idle device all start together.  Work of other streams that holds CUs
+    // only delays the late blocks until it ends (the resident blocks wait at the first
+    // barrier); a device that can never hold them all runs into the bounded waits, which set
+    // the error word instead of hanging.  (A cooperative launch would guarantee residency up
+    // front, at about 16 us more per launch, through a runtime path whose teardown faulted
+    // at process exit under rocprofv3.)
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, layer_forward_fused, NTH, 0) !=
             hipSuccess || per_cu < 1)
@@ -1081,17 +1088,10 @@ extern "C" int moe_layer_forward(const moe_fwd_args* p, void* ws, size_t ws_byte
     a.sy = (unsigned*)((char*)ws + moe_align256(moe_route_workspace_size(f.T, f.k, f.E)));
     a.mbr = (int)mbr;
     a.mbs = (int)mbs;
-    void* params[] = {&a};
-    hipError_t err = hipSuccess;
     MOE_TRACED("fused_clear", st, fused_clear<<<1, 1024, 0, st>>>(a.sy, (int)words));
     MOE_LAUNCH_CHECK();
-    MOE_TRACED("layer_forward_fused", st,
-               err = hipLaunchCooperativeKernel((const void*)layer_forward_fused, dim3(ncu),
-                                                dim3(NTH), params, 0, st));
-    if (err != hipSuccess) {
-        (void)hipGetLastError();
-        return MOE_EHIP;
-    }
+    MOE_TRACED("layer_forward_fused", st, layer_forward_fused<<<ncu, NTH, 0, st>>>(a));
+    MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
 

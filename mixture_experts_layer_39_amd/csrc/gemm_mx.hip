@@ -271,8 +271,9 @@ __global__ __launch_bounds__(256) void mx_panel_scales_ab(const uint8_t* __restr
 // 8 bytes per lane straight to registers, issued through inline asm like the LDS loads so that
 // the pipeline's explicit wait counts cover both.  The registers are read only after a wait
 // that covers the load, followed by `settle`, which redefines the value for the compiler.
+// Like lds_load16, the asm carries the wait states after a VALU write of an SGPR it reads.
 __device__ __forceinline__ void vgpr_load8(uint2& dst, rsrc_t r, uint32_t voff, uint32_t soff) {
-    asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen"
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx2 %0, %1, %2, %3 offen"
                  : "=v"(dst)
                  : "v"(voff), "s"(r), "s"(soff)
                  : "memory");
@@ -539,6 +540,14 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
             }
         }
         wait_vm_lgkm0<0>();  // no load may still be writing LDS when the block ends
+        // The last steps issued scale loads past the end of K whose values no MFMA reads:
+        // redefine every set after the wait, so that each register a load writes stays
+        // allocated to it until the load has landed.
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            settle(sca[c]);
+            settle(scb[c]);
+        }
     }
 
     // ---------------------------------------------------------------- epilogue

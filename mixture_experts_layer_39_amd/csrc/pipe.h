@@ -25,11 +25,17 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 // the compiler's own wait-count tracking of such loads cannot tell pipeline stages apart and
 // would drain every stage in flight before each LDS read; the main loops wait for exactly
 // the stage they need instead (wait_vm_lgkm0).  The loads are ordered like any volatile asm.
+// The LDS address is an operand bound to M0 ("{m0}"), so the compiler itself sets M0 and
+// knows the instruction reads it (M0 is never written behind its back).  The compiler does
+// not see into the asm, so it does not insert the wait states a vector memory instruction
+// needs after a VALU write of an SGPR it reads (its descriptor or offset: e.g. an SGPR
+// reloaded from a spill lane by v_readlane just before) or after an SALU write of M0; the
+// asm carries them itself (s_nop 4: five wait states).
 __device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t lds_dst, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
-                 : "s"(lds_dst), "v"(voff), "s"(r), "s"(soff)
-                 : "memory", "m0");
+                 : "v"(voff), "s"(r), "s"(soff), "{m0}"(lds_dst)
+                 : "memory");
 }
 
 // 32-bit LDS address of a __shared__ object (wave-uniform).

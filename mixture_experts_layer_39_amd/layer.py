@@ -276,7 +276,7 @@ class MoELayer:
 
     # ------------------------------------------------------------------ one launch
     def forward_fused(self):
-        """The same forward as forward(), as one cooperative kernel launch (moe_layer_forward).
+        """The same forward as forward(), as one kernel launch (moe_layer_forward).
         BF16, unstreamed layers; outputs are bit-identical to forward()'s."""
         c, inp = self.cfg, self.inp
         if self.ring or c.mx:

@@ -1,4 +1,4 @@
-"""The forward as one cooperative launch (moe_layer_forward) against the per-step calls
+"""The forward as one kernel launch (moe_layer_forward) against the per-step calls
 (moe_route, moe_dispatch, moe_expert_ffn, moe_combine) and against the oracle.
 
 Every step of the single launch runs the same device code as its own kernel, so every output
