@@ -110,6 +110,25 @@ int moe_route(const float *logits, const void *x, const void *w_router, int T, i
               float *s_sel, int32_t *counts, int32_t *offsets, int32_t *pos, int32_t *src,
               void *ws, size_t ws_bytes, void *stream);
 
+/* moe_route_noalloc: moe_route for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments without ws / ws_bytes, the same kernels and bit-identical outputs.  Its scratch
+ * (the permutation's chunk histograms) is a static device array of
+ * MOE_ROUTE_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on until the
+ * process ends; the call itself allocates and frees nothing.  Calls whose scratch would not
+ * fit -- moe_route_workspace_size(T, k, E) > MOE_ROUTE_NOALLOC_SCRATCH_BYTES, i.e. about
+ * ceil(T*k / 256) * E * 4 bytes -- return MOE_EWORKSPACE and enqueue nothing (1 MiB covers,
+ * e.g., T*k = 65536 routed pairs over E = 512 experts).  Every call on one device shares
+ * that device's array: calls that may overlap on one device (different streams, or different
+ * host threads without ordering) race and must be serialised by the caller; stream-ordered
+ * calls are safe, since each call writes all the scratch it reads before reading it.
+ * Other errors as moe_route; MOE_EHIP if the array's device address cannot be looked up. */
+#define MOE_ROUTE_NOALLOC_SCRATCH_BYTES (1u << 20)
+int moe_route_noalloc(const float *logits, const void *x, const void *w_router, int T, int H,
+                      int E, int k, const moe_route_cfg *cfg, const int32_t *idx_in,
+                      int32_t *idx, float *w, float *s_sel, int32_t *counts, int32_t *offsets,
+                      int32_t *pos, int32_t *src, void *stream);
+
 /* ------------------------------------------------------------------ load balancing
  * moe_update_bias: the auxiliary-loss-free load balancing of a DeepSeek-V3-type layer
  * (layer type: pulsen.vercel.app ¶6; rule: DeepSeek-V3 Technical Report, arXiv:2412.19437,

@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route_workspace_size.argtypes = [_i, _i, _i]
         L.moe_route.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, ctypes.POINTER(RouteCfg), _vp,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.moe_route_noalloc.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, ctypes.POINTER(RouteCfg),
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_dispatch.argtypes = [_vp, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp]
         L.moe_update_bias.argtypes = [_vp, _i, ctypes.c_float, _vp, _vp]
         L.moe_ffn_workspace_size.restype = _sz
@@ -154,6 +156,23 @@ def moe_route(logits, T, E, k, *, x=None, w_router=None, H=0, score=SCORE_SOFTMA
                          _p(pos), _p(src), _p(ws), ws.numel() * ws.element_size() if ws is not None else 0,
                          _stream(stream))
     _check("moe_route", rc)
+
+
+ROUTE_NOALLOC_SCRATCH_BYTES = 1 << 20
+
+
+def moe_route_noalloc(logits, T, E, k, *, x=None, w_router=None, H=0, score=SCORE_SOFTMAX,
+                      n_groups=1, topk_groups=1, renorm=True, route_scale=1.0, sel_bias=None,
+                      idx_in=None, idx=None, w=None, s_sel=None, counts, offsets, pos, src,
+                      stream=None):
+    """moe_route without a workspace: the library's static device scratch (callers that
+    cannot allocate; calls that overlap on one device race)."""
+    cfg = RouteCfg(score, n_groups, topk_groups, int(renorm), route_scale,
+                   None if sel_bias is None else sel_bias.data_ptr())
+    rc = lib().moe_route_noalloc(_p(logits), _p(x), _p(w_router), T, H, E, k, ctypes.byref(cfg),
+                                 _p(idx_in), _p(idx), _p(w), _p(s_sel), _p(counts), _p(offsets),
+                                 _p(pos), _p(src), _stream(stream))
+    _check("moe_route_noalloc", rc)
 
 
 def moe_update_bias(counts, E, gamma, bias, stream=None):

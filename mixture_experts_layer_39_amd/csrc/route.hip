@@ -6,9 +6,18 @@
 // integer output is a bit-exact function of the inputs: selection keys are fp32 values
 // computed by a fixed recipe and compared as totally ordered keys (ties: lower id first),
 // and row positions come from an ordered ballot ranking, never from atomic fetch-add.
+#include <mutex>
+
 #include "route_dev.h"
 
 namespace moe {
+
+// Scratch of moe_route_noalloc: the chunk histograms of the permutation, in a file-scope
+// device array instead of a caller's workspace.  Each device the library runs on holds its
+// own copy until the process ends.  Host code never passes the array's name to a kernel
+// (on the host it is only a stand-in for the symbol): it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[MOE_ROUTE_NOALLOC_SCRATCH_BYTES];
 
 // ------------------------------------------------------------------ router projection
 __global__ void router_proj_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr,
@@ -94,10 +103,13 @@ extern "C" size_t moe_route_workspace_size(int T, int k, int E) {
     return moe_align256((size_t)nch * E * sizeof(int32_t)) + 256;
 }
 
-extern "C" int moe_route(const float* logits, const void* x, const void* w_router, int T, int H,
-                         int E, int k, const moe_route_cfg* cfg, const int32_t* idx_in,
-                         int32_t* idx, float* w, float* s_sel, int32_t* counts, int32_t* offsets,
-                         int32_t* pos, int32_t* src, void* ws, size_t ws_bytes, void* stream) {
+// Argument checks of moe_route (host only, no HIP call); fills the group configuration.
+static int route_validate(const float* logits, const void* x, const void* w_router, int T, int H,
+                          int E, int k, const moe_route_cfg* cfg, const int32_t* idx_in,
+                          const int32_t* idx, const float* w, const float* s_sel,
+                          const int32_t* counts, const int32_t* offsets, const int32_t* pos,
+                          const int32_t* src, int* n_groups_out, int* topk_groups_out,
+                          int* per_group_out) {
     MOE_REQUIRE(T >= 0 && E >= 1 && E <= 1024 && k >= 1 && k <= 64);
     // permutation outputs: none (selection only), counts + offsets (the loads), or all four
     MOE_REQUIRE((counts == nullptr) == (offsets == nullptr) && (pos == nullptr) == (src == nullptr));
@@ -119,13 +131,20 @@ extern "C" int moe_route(const float* logits, const void* x, const void* w_route
     } else {
         MOE_REQUIRE(T == 0 || idx_in);
     }
-    int64_t n = (int64_t)T * k;
-    MOE_REQUIRE(n <= 0x7FFFFFFF);
-    size_t need = moe_route_workspace_size(T, k, E);
-    if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
-    int rc = moe_check_device();
-    if (rc) return rc;
-    hipStream_t st = (hipStream_t)stream;
+    MOE_REQUIRE((int64_t)T * k <= 0x7FFFFFFF);
+    *n_groups_out = n_groups;
+    *topk_groups_out = topk_groups;
+    *per_group_out = per_group;
+    return MOE_OK;
+}
+
+// The launches of moe_route, after validation, with a workspace of the needed size.
+static int route_launch(const float* logits, const void* x, const void* w_router, int T, int H,
+                        int E, int k, const moe_route_cfg* cfg, int n_groups, int topk_groups,
+                        int per_group, const int32_t* idx_in, int32_t* idx, float* w,
+                        float* s_sel, int32_t* counts, int32_t* offsets, int32_t* pos,
+                        int32_t* src, void* ws, hipStream_t st) {
+    const int64_t n = (int64_t)T * k;
     if (T > 0 && !idx_in) {
         if (w_router) {
             int tot = T * E;
@@ -165,4 +184,68 @@ extern "C" int moe_route(const float* logits, const void* x, const void* w_route
         MOE_LAUNCH_CHECK();
     }
     return MOE_OK;
+}
+
+extern "C" int moe_route(const float* logits, const void* x, const void* w_router, int T, int H,
+                         int E, int k, const moe_route_cfg* cfg, const int32_t* idx_in,
+                         int32_t* idx, float* w, float* s_sel, int32_t* counts, int32_t* offsets,
+                         int32_t* pos, int32_t* src, void* ws, size_t ws_bytes, void* stream) {
+    int n_groups, topk_groups, per_group;
+    int rc = route_validate(logits, x, w_router, T, H, E, k, cfg, idx_in, idx, w, s_sel, counts,
+                            offsets, pos, src, &n_groups, &topk_groups, &per_group);
+    if (rc) return rc;
+    size_t need = moe_route_workspace_size(T, k, E);
+    if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+    rc = moe_check_device();
+    if (rc) return rc;
+    return route_launch(logits, x, w_router, T, H, E, k, cfg, n_groups, topk_groups, per_group,
+                        idx_in, idx, w, s_sel, counts, offsets, pos, src, ws,
+                        (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------------ no-allocation variant
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];  // device address of `scratch` per device (null: not yet)
+}  // namespace
+
+// The device address of the current device's `scratch`, looked up once per device (with
+// that device current) and kept; null if the lookup fails.
+static void* route_scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+extern "C" int moe_route_noalloc(const float* logits, const void* x, const void* w_router, int T,
+                                 int H, int E, int k, const moe_route_cfg* cfg,
+                                 const int32_t* idx_in, int32_t* idx, float* w, float* s_sel,
+                                 int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* src,
+                                 void* stream) {
+    // the argument checks of moe_route (no HIP call), then the size limit of the scratch
+    int n_groups, topk_groups, per_group;
+    int rc = route_validate(logits, x, w_router, T, H, E, k, cfg, idx_in, idx, w, s_sel, counts,
+                            offsets, pos, src, &n_groups, &topk_groups, &per_group);
+    if (rc) return rc;
+    if (moe_route_workspace_size(T, k, E) > (size_t)MOE_ROUTE_NOALLOC_SCRATCH_BYTES)
+        return MOE_EWORKSPACE;
+    rc = moe_check_device();
+    if (rc) return rc;
+    void* ws = route_scratch_ptr();
+    if (!ws) return MOE_EHIP;
+    // Every histogram entry a call reads is written by the same call before (count_kernel
+    // writes all [chunks][E] of them): nothing has to start at zero.
+    return route_launch(logits, x, w_router, T, H, E, k, cfg, n_groups, topk_groups, per_group,
+                        idx_in, idx, w, s_sel, counts, offsets, pos, src, ws,
+                        (hipStream_t)stream);
 }

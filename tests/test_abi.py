@@ -76,6 +76,22 @@ def test_route_validation():
     assert moe.route_workspace_size(2048, 8, 256) >= 64 * 256 * 4
 
 
+def test_route_noalloc_validation():
+    # the checks of moe_route, then the static scratch's limit, all before any HIP call
+    L_ = lib()
+    cfg = moe.RouteCfg(0, 1, 1, 1, 1.0, None)
+
+    def call(T=16, E=8, k=2, idx_in=None):
+        return L_.moe_route_noalloc(FAKE, None, None, T, 64, E, k, ctypes.byref(cfg), idx_in,
+                                    FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+
+    assert call(k=9) == moe.MOE_EINVAL
+    assert call(E=2000) == moe.MOE_EINVAL
+    assert moe.route_workspace_size(32768, 8, 1024) > moe.ROUTE_NOALLOC_SCRATCH_BYTES
+    assert call(T=32768, E=1024, k=8, idx_in=FAKE) == moe.MOE_EWORKSPACE
+    assert moe.route_workspace_size(8192, 8, 256) <= moe.ROUTE_NOALLOC_SCRATCH_BYTES
+
+
 def test_dispatch_combine_mx_validation():
     L_ = lib()
     assert L_.moe_update_bias(FAKE, 0, 0.1, FAKE, None) == moe.MOE_EINVAL
