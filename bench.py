@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=48,
                     help="source tokens of the CPU-oracle sample")
+    ap.add_argument("--all-configs", action=argparse.BooleanOptionalAction, default=True,
+                    help="after the headline workload (dsv3_ep64), also measure the other "
+                         "workloads and report them under \"configs\"")
     ap.add_argument("--breakdown", action="store_true",
                     help="also print per-role times to stderr")
     ap.add_argument("--ring-depth", type=int, default=16,
@@ -325,19 +328,33 @@ def copy_calibration(mib: int) -> None:
 # ----------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(wl, inp, n_tokens: int) -> dict:
     """The CPU oracle (fp64 plain loops) on the first n_tokens source tokens of the workload,
-    forward (+ backward when the workload has one); tokens/s of that sample."""
+    forward (+ backward when the workload has one); tokens/s of that sample.  Layers with
+    many experts keep only the weights of the experts the sample's tokens select (the
+    oracle's own selection of those tokens; the tokens then reach them as a local share)."""
+    import numpy as np
     import oracle as orc
     import workloads as wk
     n = min(n_tokens, wl.T)
     p = dict(x=wk.bf16_bits(inp["x"][:n]), k=wl.k, score=wl.score, renorm=wl.renorm,
              route_scale=wl.route_scale, n_groups=wl.n_groups, topk_groups=wl.topk_groups,
-             mx=wl.mx, w1=wk.bf16_bits(inp["w1"]), w2=wk.bf16_bits(inp["w2"]))
+             mx=wl.mx)
     if "w_router" in inp:
         p["w_router"] = wk.bf16_bits(inp["w_router"])
     else:
         p["logits"] = inp["logits"][:n].cpu().numpy()
+    experts = "the full expert weights"
     if "idx_local" in inp:
         p["idx_local"] = inp["idx_local"][:n].cpu().numpy()
+        p["w1"], p["w2"] = wk.bf16_bits(inp["w1"]), wk.bf16_bits(inp["w2"])
+    elif wl.E > 64:
+        idx, _ = orc.route_select(p["logits"], wl.k, wl.score, wl.n_groups, wl.topk_groups)
+        used = np.unique(idx)
+        p["idx_local"] = np.searchsorted(used, idx).astype(np.int32)
+        sel = torch_index(used).to(inp["w1"].device)
+        p["w1"], p["w2"] = wk.bf16_bits(inp["w1"][sel]), wk.bf16_bits(inp["w2"][sel])
+        experts = f"the weights of the {len(used)} experts they select"
+    else:
+        p["w1"], p["w2"] = wk.bf16_bits(inp["w1"]), wk.bf16_bits(inp["w2"])
     if wl.S:
         p["ws1"], p["ws2"] = wk.bf16_bits(inp["ws1"]), wk.bf16_bits(inp["ws2"])
     dout = wk.bf16_bits(inp["dout"][:n]) if wl.backward else None
@@ -351,8 +368,13 @@ def cpu_baseline(wl, inp, n_tokens: int) -> dict:
     what = "forward+backward" if wl.backward else "forward"
     return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": orc.threads(),
             "cpu": _cpu_model(), "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"first {n} of {wl.T} source tokens ({rows} routed rows) with the full "
-                      f"expert weights, oracle {what} in fp64"}
+            "sample": f"first {n} of {wl.T} source tokens ({rows} routed rows) with "
+                      f"{experts}, oracle {what} in fp64"}
+
+
+def torch_index(a):
+    import torch
+    return torch.from_numpy(a.astype("int64"))
 
 
 def _cpu_model() -> str:
@@ -380,9 +402,8 @@ def main():
               "path across GPUs is not implemented (--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
     import torch
-    import workloads as wk
     import mixture_experts_layer_39_amd as moe
-    from mixture_experts_layer_39_amd.layer import LayerCfg, MoELayer
+    import workloads as wk
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -391,54 +412,108 @@ def main():
         copy_calibration(a.copy_mib)
         return
     moe.lib()  # fails loudly when the HIP library is missing
+    torch.cuda.set_device(0)
     wl = wk.WORKLOADS[a.workload]
     if a.backward and not wl.backward:
         wl = wl.scaled(backward=True)
+    head = measure(wl, a, ring_depth=a.ring_depth, steps=a.steps, warmup=a.warmup,
+                   fused=a.fused, bias_gamma=a.bias_gamma, headline=True,
+                   cpu_tokens=None if a.no_cpu_baseline else a.cpu_tokens)
+    out = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "traced_ms_per_step": head["traced_ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp8" if wl.mx else "bf16",
+        "data": "synthetic (seeded; random-init weights of the layer's shape)",
+        "config": head["config"],
+    }
+    for key in ("fwd_tokens_per_s", "fwd_ms_per_step", "step_tflops", "fwd_tflops",
+                "cold_tokens_per_s", "cold_ms_per_step", "cold_fwd_ms_per_step",
+                "fused_fwd_ms_per_step", "fused_fwd_tokens_per_s", "roofline", "breakdown",
+                "cpu_baseline"):
+        out[key] = head.get(key)
+    if a.all_configs and a.workload == "dsv3_ep64" and not a.fused:
+        # the other workloads, each measured the same way (fewer warm-up steps: the GPU is
+        # warm by now), compactly: throughput, the dominant kernel's roofline and a CPU sample
+        extra = {}
+        plan = [("tiny_t128", "tiny_t128", {}), ("mid_t2048", "mid_t2048", {}),
+                ("dsv3_ep64_mxfp8", "dsv3_ep64_mxfp8", {}),
+                ("dsv3_ep64_mxfp8_bwd", "dsv3_ep64_mxfp8", {"backward": True}),
+                ("dsv3_e256_zipf", "dsv3_e256_zipf", {"ring_depth": a.ring_depth}),
+                ("dsv3_e256_zipf_ring4", "dsv3_e256_zipf", {"ring_depth": 4})]
+        cpu_tokens = {"tiny_t128": 128, "mid_t2048": 16, "dsv3_ep64_mxfp8": 48,
+                      "dsv3_e256_zipf": 4}
+        for key, name, opt in plan:
+            w = wk.WORKLOADS[name]
+            if opt.get("backward"):
+                w = w.scaled(backward=True)
+            ct = None
+            if not a.no_cpu_baseline and key in cpu_tokens:
+                ct = cpu_tokens[key]
+            rec = measure(w, a, ring_depth=opt.get("ring_depth", a.ring_depth),
+                          steps=a.steps, warmup=min(a.warmup, 5), fused=False, bias_gamma=0.0,
+                          headline=False, cpu_tokens=ct)
+            extra[key] = rec
+            print(f"bench: {key} {rec['ms_per_step']} ms/step", file=sys.stderr, flush=True)
+        out["configs"] = extra
+    print(json.dumps(out), flush=True)
+
+
+def measure(wl, a, *, ring_depth, steps, warmup, fused, bias_gamma, headline, cpu_tokens):
+    """One workload: K untimed-warm-up, K timed and K traced steps; the record of its
+    throughput, the dominant kernel's roofline, and (headline) the cold-cache and per-role
+    figures.  The layer's buffers are freed before returning."""
+    import torch
+    import workloads as wk
+    import mixture_experts_layer_39_amd as moe
+    from mixture_experts_layer_39_amd.layer import LayerCfg, MoELayer
+
     dev = "cuda:0"
-    torch.cuda.set_device(0)
     inp = wk.make_inputs(wl, device=dev)
-    ring = dict(minibatch=wl.minibatch, ring_depth=a.ring_depth) if wl.minibatch else {}
+    ring = dict(minibatch=wl.minibatch, ring_depth=ring_depth) if wl.minibatch else {}
     lcfg = LayerCfg.from_workload(wl)
-    lcfg.bias_gamma = a.bias_gamma
+    lcfg.bias_gamma = bias_gamma
     layer = MoELayer(lcfg, inp, dev, backward=wl.backward, **ring)
-    can_fuse = not wl.mx and not layer.ring and not (wl.local_share and a.bias_gamma > 0)
-    if a.fused and not can_fuse:
+    can_fuse = not wl.mx and not layer.ring and not (wl.local_share and bias_gamma > 0)
+    if fused and not can_fuse:
         print("--fused runs the unstreamed BF16 layer only", file=sys.stderr)
         sys.exit(2)
-    fwd = layer.forward_fused if a.fused else layer.forward
+    fwd = layer.forward_fused if fused else layer.forward
 
     def step():
         fwd()
         if wl.backward:
             layer.backward()
 
-    for _ in range(a.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     # timed: K whole steps (the throughput), without instrumentation
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(a.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
-    ms_step = elapsed * 1e3 / a.steps
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / steps
 
     # traced: K more identical steps with per-launch HIP events recorded by the library on
     # each launch's stream (the kernel durations of the roofline and the breakdown).  The
     # event records add gaps between launches (about 0.1 ms per step at the EP-64 share) but
     # not kernel time, so the throughput comes from the untraced steps above.
-    moe.trace_begin(max(512, 512 * a.steps))
+    moe.trace_begin(max(512, 512 * steps))
     torch.cuda.synchronize()
     t2 = time.perf_counter()
-    for _ in range(a.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     t3 = time.perf_counter()
     recs = moe.trace_end()
-    traced_ms_step = (t3 - t2) * 1e3 / a.steps
+    traced_ms_step = (t3 - t2) * 1e3 / steps
 
     # forward-only steps, untraced: the per-step calls, and (where it applies) the forward
     # as one launch
@@ -447,42 +522,25 @@ def main():
             f()
         torch.cuda.synchronize()
         f0 = time.perf_counter()
-        for _ in range(a.steps):
+        for _ in range(steps):
             f()
         torch.cuda.synchronize()
-        return (time.perf_counter() - f0) * 1e3 / a.steps
+        return (time.perf_counter() - f0) * 1e3 / steps
 
-    fwd_ms = time_fwd(layer.forward)
+    fwd_ms = time_fwd(layer.forward) if wl.backward or fused else ms_step
     fused_ms = time_fwd(layer.forward_fused) if can_fuse else None
-    cold_ms = cold_ms_per_call(step, a.steps)
-    cold_fwd_ms = cold_ms_per_call(layer.forward, a.steps)
 
     # per-role statistics over the traced steps
     roles: dict[str, list[float]] = {}
     for name, ms in recs:
         roles.setdefault(name, []).append(ms)
-    per_step = {r: sum(v) / a.steps for r, v in roles.items()}
+    per_step = {r: sum(v) / steps for r, v in roles.items()}
     dominant = max(per_step, key=per_step.get)
-    roof = roofline_of(wl, dominant, per_step[dominant], len(roles[dominant]) / a.steps,
-                       measured_traffic(a.workload, dominant))
+    roof = roofline_of(wl, dominant, per_step[dominant], len(roles[dominant]) / steps,
+                       measured_traffic(wl.name, dominant))
 
     flops_fwd = wl.fwd_flops()
     flops_step = flops_fwd * (3.0 if wl.backward else 1.0)
-    breakdown = {}
-    for r in sorted(per_step, key=per_step.get, reverse=True):
-        n = len(roles[r]) / a.steps
-        ent = {"launches_per_step": n, "ms_per_step": round(per_step[r], 4),
-               "share": round(per_step[r] / traced_ms_step, 4)}
-        kind, work = step_work(wl, r)
-        if kind == "flop":
-            ent["tflops"] = round(work / (per_step[r] * 1e-3) / 1e12, 1)
-        elif work and n == 1:
-            ent["gbs"] = round(work / (per_step[r] * 1e-3) / 1e9, 1)
-        breakdown[r] = ent
-    if a.breakdown:
-        for r, e in breakdown.items():
-            print(f"  {r:22s} {e}", file=sys.stderr)
-
     cfg = {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "I": wl.I,
            "routed_rows": wl.R, "S": wl.S, "Is": wl.Is, "E_router": wl.ER,
            "score": "sigmoid" if wl.score == wk.SIGMOID else "softmax",
@@ -491,39 +549,53 @@ def main():
            "parallelism": "none (one GPU's share)"}
     if layer.ring:
         cfg.update(minibatch=layer.mb, ring_depth=layer.D, ring_passes=layer.passes)
-    if a.bias_gamma > 0:
-        cfg.update(bias_gamma=a.bias_gamma)
-    if a.fused:
+    if bias_gamma > 0:
+        cfg.update(bias_gamma=bias_gamma)
+    if fused:
         cfg.update(forward="one launch")
     if wl.mx and wl.backward:
-        cfg.update(backward_precision="mxfp8 dgrad, bf16 wgrad")
-    out = {
-        "metric": METRIC,
-        "value": round(wl.T * a.steps / elapsed, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        cfg.update(backward_precision="mxfp8 dgrad and weight gradients")
+    rec = {
+        "config": cfg,
+        "tokens_per_s": round(wl.T * steps / elapsed, 1),
         "ms_per_step": round(ms_step, 4),
         "traced_ms_per_step": round(traced_ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "mxfp8" if wl.mx else "bf16",
-        "data": "synthetic (seeded; random-init weights of the layer's shape)",
-        "config": cfg,
         "fwd_tokens_per_s": round(wl.T / (fwd_ms * 1e-3), 1),
         "fwd_ms_per_step": round(fwd_ms, 4),
         "step_tflops": round(flops_step / (ms_step * 1e-3) / 1e12, 1),
         "fwd_tflops": round(flops_fwd / (fwd_ms * 1e-3) / 1e12, 1),
-        "cold_tokens_per_s": round(wl.T / (cold_ms * 1e-3), 1),
-        "cold_ms_per_step": round(cold_ms, 4),
-        "cold_fwd_ms_per_step": round(cold_fwd_ms, 4),
         "fused_fwd_ms_per_step": round(fused_ms, 4) if fused_ms else None,
         "fused_fwd_tokens_per_s": round(wl.T / (fused_ms * 1e-3), 1) if fused_ms else None,
         "roofline": roof,
-        "breakdown": breakdown,
-        "cpu_baseline": None,
     }
-    if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp, a.cpu_tokens)
-    print(json.dumps(out), flush=True)
+    if layer.ring or wl.E > 8:
+        c = layer.counts.view(-1, wl.E).sum(0).cpu()
+        rec["loads"] = {"min": int(c.min()), "median": int(c.median()), "max": int(c.max())}
+    if headline:
+        cold_ms = cold_ms_per_call(step, steps)
+        cold_fwd_ms = cold_ms_per_call(layer.forward, steps)
+        rec.update(cold_tokens_per_s=round(wl.T / (cold_ms * 1e-3), 1),
+                   cold_ms_per_step=round(cold_ms, 4), cold_fwd_ms_per_step=round(cold_fwd_ms, 4))
+        breakdown = {}
+        for r in sorted(per_step, key=per_step.get, reverse=True):
+            n = len(roles[r]) / steps
+            ent = {"launches_per_step": n, "ms_per_step": round(per_step[r], 4),
+                   "share": round(per_step[r] / traced_ms_step, 4)}
+            kind, work = step_work(wl, r)
+            if kind == "flop":
+                ent["tflops"] = round(work / (per_step[r] * 1e-3) / 1e12, 1)
+            elif work and n == 1:
+                ent["gbs"] = round(work / (per_step[r] * 1e-3) / 1e9, 1)
+            breakdown[r] = ent
+        rec["breakdown"] = breakdown
+        if a.breakdown:
+            for r, e in breakdown.items():
+                print(f"  {r:22s} {e}", file=sys.stderr)
+    rec["cpu_baseline"] = cpu_baseline(wl, inp, cpu_tokens) if cpu_tokens else None
+    del layer, inp
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
 
 
 if __name__ == "__main__":

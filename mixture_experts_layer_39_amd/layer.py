@@ -110,12 +110,6 @@ class MoELayer:
             self.counts = _e((P, E), i32, d)
             self.offsets = _e((P, E + 1), i32, d)
             self.src = _e((P, self.pass_rows), i32, d)
-            # per-minibatch routing also yields a minibatch permutation (unused scratch)
-            mbk = self.mb * kr
-            self.mb_counts = _e((E,), i32, d)
-            self.mb_offsets = _e((E + 1,), i32, d)
-            self.mb_pos = _e((self.mb, kr), i32, d)
-            self.mb_src = _e((mbk,), i32, d)
         else:
             self.counts = _e((E,), i32, d)
             self.offsets = _e((E + 1,), i32, d)
@@ -305,12 +299,13 @@ class MoELayer:
 
     # ------------------------------------------------------------------ macrobatch ring
     def _route_minibatch(self, a, b):
+        # the selection alone (idx, w, s_sel of the minibatch's tokens): the rows are permuted
+        # per pass, over the pass's minibatches, below
         c = self.cfg
         moe_route(self.logits[a:b], b - a, c.E, c.k, idx=self.idx[a:b], w=self.w[a:b],
-                  s_sel=self.s_sel[a:b], counts=self.mb_counts, offsets=self.mb_offsets,
-                  pos=self.mb_pos, src=self.mb_src, score=c.score, n_groups=c.n_groups,
-                  topk_groups=c.topk_groups, renorm=c.renorm, route_scale=c.route_scale,
-                  ws=self.route_ws)
+                  s_sel=self.s_sel[a:b], counts=None, offsets=None, pos=None, src=None,
+                  score=c.score, n_groups=c.n_groups, topk_groups=c.topk_groups,
+                  renorm=c.renorm, route_scale=c.route_scale, ws=self.route_ws)
 
     def forward_ring(self):
         c, inp = self.cfg, self.inp
