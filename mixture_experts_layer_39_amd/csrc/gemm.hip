@@ -76,6 +76,9 @@ struct GemmArgs {
 #endif
 // LDS of one block: the stage ring (128 KB), or for BK = 64 five operand slots (160 KB).
 constexpr int LDS_BYTES = MOE_GEMM_SLOTS5 ? 160 * 1024 : LDS_STAGES_BYTES;
+// LDS each wave stages its output sub-tile in after the K loop (a quarter of the block's)
+constexpr int EPI_WAVE_BYTES = LDS_BYTES / 4;
+static_assert(128 * 272 <= EPI_WAVE_BYTES, "staged 128-row sub-tile");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -505,60 +508,101 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     // ---------------------------------------------------------------- epilogue
     // Accumulator layout (B fragment first): lane l holds row l % 32 of its 32x32 block and
     // columns 8 (v/4) + 4 (l/32) + v%4, v = 0..15: four runs of 4 consecutive columns.
+    // Stores go through LDS: each wave writes its 128 x 128 sub-tile (bf16) into its own
+    // 40 KB of the (now free) operand slots, row-major, then reads it back as 16-byte chunks of
+    // whole rows, so that every global store instruction writes complete 128-byte lines (four
+    // 256-byte row segments) instead of 16-byte pieces of 32 rows.  The rows' stride in LDS
+    // is padded by 16 bytes, which spreads the 32 rows of one accumulator write over the banks.
     const int lrow = lane & 31, lcol = (lane >> 5) * 4;
-    if (EPI == EPI_STORE) {
-        bf16_t* C = g.C + e * g.c_es + (GK ? 0 : (int64_t)row0 * g.ldc);
+    if (EPI == EPI_STORE || EPI == EPI_SWIGLU) {
+        constexpr int RS = 272;                   // LDS row stride of a staged sub-tile (bytes)
+        __syncthreads();                          // every wave is done reading the slots
+        char* const stg = sm.st + wid * EPI_WAVE_BYTES;
+        const int rr = lane >> 4, ck = lane & 15;  // read-back: 16 lanes per 256-byte row
+        auto lds_sync = []() __attribute__((always_inline)) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        };
+        if (EPI == EPI_STORE) {
+            bf16_t* C = g.C + e * g.c_es + (GK ? 0 : (int64_t)row0 * g.ldc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = m0 + wm * 128 + i * 32 + lrow;
-            if (row >= Mvalid) continue;
-            bf16_t* Crow = C + (int64_t)row * g.ldc;
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int col = n0 + wn * 128 + j * 32 + 8 * q + lcol;
-                    if (col < g.N) {
-                        uint2 v = make_uint2(pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                                             pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
-                        *reinterpret_cast<uint2*>(Crow + col) = v;
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<uint2*>(stg + (i * 32 + lrow) * RS +
+                                                  (j * 32 + 8 * q + lcol) * 2) =
+                            make_uint2(pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                       pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+            lds_sync();
+            const int col = n0 + wn * 128 + ck * 8;
+#pragma unroll 8
+            for (int p = 0; p < 32; ++p) {
+                const int r = 4 * p + rr, row = m0 + wm * 128 + r;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * RS + ck * 16);
+                if (row < Mvalid && col < g.N) st16(C + (int64_t)row * g.ldc + col, v);
+            }
+        } else {
+            // block (i, j) of a lane: channels 16 j + 8 hf + lcol .. +3 (hf = 0, 1) of the
+            // wave's 64 (ch_w ..), gate at accumulators 4 hf .. +3, up at 8 + 4 hf .. +3
+            const int ch_w = ch0 + wn * 64;
+            if (ch_w < g.I) {
+                if (g.C2) {
+                    // saved g|u: staged rows hold g (channels 0-63) then u (64-127)
+                    bf16_t* C2 = g.C2 + e * g.c2_es + (int64_t)row0 * g.ldc2;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+#pragma unroll
+                            for (int hf = 0; hf < 2; ++hf) {
+                                const f32x16& a = acc[i][j];
+                                char* rp = stg + (i * 32 + lrow) * RS + (j * 16 + 8 * hf + lcol) * 2;
+                                *reinterpret_cast<uint2*>(rp) =
+                                    make_uint2(pack_bf2(a[4 * hf], a[4 * hf + 1]),
+                                               pack_bf2(a[4 * hf + 2], a[4 * hf + 3]));
+                                *reinterpret_cast<uint2*>(rp + 128) =
+                                    make_uint2(pack_bf2(a[8 + 4 * hf], a[8 + 4 * hf + 1]),
+                                               pack_bf2(a[8 + 4 * hf + 2], a[8 + 4 * hf + 3]));
+                            }
+                    lds_sync();
+                    const int gcol = (ck < 8 ? 0 : g.I) + ch_w + (ck & 7) * 8;
+#pragma unroll 8
+                    for (int p = 0; p < 32; ++p) {
+                        const int r = 4 * p + rr, row = m0 + wm * 128 + r;
+                        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * RS + ck * 16);
+                        if (row < Mvalid) st16(C2 + (int64_t)row * g.ldc2 + gcol, v);
                     }
+                    lds_sync();  // the reads are done before h overwrites the rows
                 }
-        }
-    } else if (EPI == EPI_SWIGLU) {
-        // block (i, j) of a lane: channels ch0 + 64 wn + 16 j + 8 hf + lcol .. +3 (hf = 0, 1),
-        // gate at accumulators 4 hf .. +3, up at 8 + 4 hf .. +3
-        bf16_t* C = g.C + e * g.c_es + (int64_t)row0 * g.ldc;
-        bf16_t* C2 = g.C2 ? g.C2 + e * g.c2_es + (int64_t)row0 * g.ldc2 : nullptr;
+                // h = silu(g) u: staged rows of 64 channels (128 bytes), read back by 8 lanes
+                bf16_t* C = g.C + e * g.c_es + (int64_t)row0 * g.ldc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = m0 + wm * 128 + i * 32 + lrow;
-            if (row >= Mvalid) continue;
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                    for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const int ch = ch0 + wn * 64 + j * 16 + 8 * hf + lcol;
-                    if (ch >= g.I) continue;
-                    const f32x16& a = acc[i][j];
-                    float hv[4];
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const f32x16& a = acc[i][j];
+                            float hv[4];
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const float gv = a[4 * hf + c], uv = a[8 + 4 * hf + c];
-                        hv[c] = gv / (1.0f + __expf(-gv)) * uv;
-                    }
-                    *reinterpret_cast<uint2*>(C + (int64_t)row * g.ldc + ch) =
-                        make_uint2(pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3]));
-                    if (C2) {
-                        bf16_t* gr = C2 + (int64_t)row * g.ldc2;
-                        *reinterpret_cast<uint2*>(gr + ch) =
-                            make_uint2(pack_bf2(a[4 * hf], a[4 * hf + 1]),
-                                       pack_bf2(a[4 * hf + 2], a[4 * hf + 3]));
-                        *reinterpret_cast<uint2*>(gr + g.I + ch) =
-                            make_uint2(pack_bf2(a[8 + 4 * hf], a[8 + 4 * hf + 1]),
-                                       pack_bf2(a[8 + 4 * hf + 2], a[8 + 4 * hf + 3]));
-                    }
+                            for (int c = 0; c < 4; ++c) {
+                                const float gv = a[4 * hf + c], uv = a[8 + 4 * hf + c];
+                                hv[c] = gv / (1.0f + __expf(-gv)) * uv;
+                            }
+                            *reinterpret_cast<uint2*>(stg + (i * 32 + lrow) * RS +
+                                                      (j * 16 + 8 * hf + lcol) * 2) =
+                                make_uint2(pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3]));
+                        }
+                lds_sync();
+                const int r8 = lane >> 3, c8 = lane & 7;
+#pragma unroll 8
+                for (int p = 0; p < 16; ++p) {
+                    const int r = 8 * p + r8, row = m0 + wm * 128 + r;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * RS + c8 * 16);
+                    if (row < Mvalid) st16(C + (int64_t)row * g.ldc + ch_w + c8 * 8, v);
                 }
+            }
         }
     } else {  // EPI_DSWIGLU: acc = dh; read saved g|u, write dg|du
         bf16_t* C = g.C + e * g.c_es + (int64_t)row0 * g.ldc;
