@@ -605,36 +605,77 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
             }
         }
     } else {  // EPI_DSWIGLU: acc = dh; read saved g|u, write dg|du
+        // Through LDS as well, in two halves of 64 rows: the saved g and u rows of the half
+        // are loaded as whole-row 16-byte chunks into the wave's staging area (g rows 0-63,
+        // u rows 64-127), each lane turns its own g, u elements into dg, du in place (one
+        // lane owns each element), and the rows go back out as whole-row chunks.
+        constexpr int RS = 272;
+        __syncthreads();                          // every wave is done reading the slots
+        char* const stg = sm.st + wid * EPI_WAVE_BYTES;
+        const int rr = lane >> 4, ck = lane & 15;
+        const int chw = n0 + wn * 128;            // the wave's first channel
+        const bool colok = chw + ck * 8 < g.N;    // this lane's 8-channel chunk exists
         bf16_t* C = g.C + e * g.c_es + (int64_t)row0 * g.ldc;
         const bf16_t* GU = g.C2 + e * g.c2_es + (int64_t)row0 * g.ldc2;
+        auto lds_sync = []() __attribute__((always_inline)) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        };
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = m0 + wm * 128 + i * 32 + lrow;
-            if (row >= Mvalid) continue;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int ch = n0 + wn * 128 + j * 32 + 8 * q + lcol;
-                    if (ch >= g.N) continue;
-                    const uint2 gg = *reinterpret_cast<const uint2*>(GU + (int64_t)row * g.ldc2 + ch);
-                    const uint2 uu = *reinterpret_cast<const uint2*>(GU + (int64_t)row * g.ldc2 + g.I + ch);
-                    const float gv[4] = {lo_bf(gg.x), hi_bf(gg.x), lo_bf(gg.y), hi_bf(gg.y)};
-                    const float uv[4] = {lo_bf(uu.x), hi_bf(uu.x), lo_bf(uu.y), hi_bf(uu.y)};
-                    float dg[4], du[4];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const float dh = acc[i][j][4 * q + c];
-                        const float sg = 1.0f / (1.0f + __expf(-gv[c]));
-                        dg[c] = dh * uv[c] * sg * (1.0f + gv[c] * (1.0f - sg));
-                        du[c] = dh * gv[c] * sg;
-                    }
-                    bf16_t* cr = C + (int64_t)row * g.ldc;
-                    *reinterpret_cast<uint2*>(cr + ch) =
-                        make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
-                    *reinterpret_cast<uint2*>(cr + g.I + ch) =
-                        make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
+        for (int half = 0; half < 2; ++half) {
+            const int rbase = m0 + wm * 128 + half * 64;
+#pragma unroll 4
+            for (int p = 0; p < 16; ++p) {
+                const int r = 4 * p + rr, row = rbase + r;
+                u32x4 gv = {0u, 0u, 0u, 0u}, uv = {0u, 0u, 0u, 0u};
+                if (row < Mvalid && colok) {
+                    const bf16_t* src = GU + (int64_t)row * g.ldc2 + chw + ck * 8;
+                    gv = ld16(src);
+                    uv = ld16(src + g.I);
                 }
+                *reinterpret_cast<u32x4*>(stg + r * RS + ck * 16) = gv;
+                *reinterpret_cast<u32x4*>(stg + (64 + r) * RS + ck * 16) = uv;
+            }
+            lds_sync();
+#pragma unroll
+            for (int ih = 0; ih < 2; ++ih) {
+                const int i = 2 * half + ih;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        char* pg = stg + (ih * 32 + lrow) * RS + (j * 32 + 8 * q + lcol) * 2;
+                        char* pu = pg + 64 * RS;
+                        const uint2 gg = *reinterpret_cast<const uint2*>(pg);
+                        const uint2 uu = *reinterpret_cast<const uint2*>(pu);
+                        const float gv[4] = {lo_bf(gg.x), hi_bf(gg.x), lo_bf(gg.y), hi_bf(gg.y)};
+                        const float uv[4] = {lo_bf(uu.x), hi_bf(uu.x), lo_bf(uu.y), hi_bf(uu.y)};
+                        float dg[4], du[4];
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const float dh = acc[i][j][4 * q + c];
+                            const float sg = 1.0f / (1.0f + __expf(-gv[c]));
+                            dg[c] = dh * uv[c] * sg * (1.0f + gv[c] * (1.0f - sg));
+                            du[c] = dh * gv[c] * sg;
+                        }
+                        *reinterpret_cast<uint2*>(pg) =
+                            make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
+                        *reinterpret_cast<uint2*>(pu) =
+                            make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
+                    }
+            }
+            lds_sync();
+#pragma unroll 4
+            for (int p = 0; p < 16; ++p) {
+                const int r = 4 * p + rr, row = rbase + r;
+                const u32x4 dgv = *reinterpret_cast<const u32x4*>(stg + r * RS + ck * 16);
+                const u32x4 duv = *reinterpret_cast<const u32x4*>(stg + (64 + r) * RS + ck * 16);
+                if (row < Mvalid && colok) {
+                    bf16_t* dst = C + (int64_t)row * g.ldc + chw + ck * 8;
+                    st16(dst, dgv);
+                    st16(dst + g.I, duv);
+                }
+            }
+            lds_sync();  // the read-back is done before the next half overwrites the rows
         }
     }
 }
