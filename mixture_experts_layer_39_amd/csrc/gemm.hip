@@ -78,7 +78,7 @@ struct GemmArgs {
 constexpr int LDS_BYTES = MOE_GEMM_SLOTS5 ? 160 * 1024 : LDS_STAGES_BYTES;
 // LDS each wave stages its output sub-tile in after the K loop (a quarter of the block's)
 constexpr int EPI_WAVE_BYTES = LDS_BYTES / 4;
-static_assert(128 * 272 <= EPI_WAVE_BYTES, "staged 128-row sub-tile");
+static_assert(STG_BYTES <= EPI_WAVE_BYTES, "staged 128-row sub-tile");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -506,77 +506,27 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     }
 
     // ---------------------------------------------------------------- epilogue
-    // Accumulator layout (B fragment first): lane l holds row l % 32 of its 32x32 block and
-    // columns 8 (v/4) + 4 (l/32) + v%4, v = 0..15: four runs of 4 consecutive columns.
-    // Stores go through LDS: each wave writes its 128 x 128 sub-tile (bf16) into its own
-    // 40 KB of the (now free) operand slots, row-major, then reads it back as 16-byte chunks of
-    // whole rows, so that every global store instruction writes complete 128-byte lines (four
-    // 256-byte row segments) instead of 16-byte pieces of 32 rows.  The rows' stride in LDS
-    // is padded by 16 bytes, which spreads the 32 rows of one accumulator write over the banks.
+    // Through LDS (staged epilogues, pipe.h): each wave stages its 128 x 128 sub-tile in its
+    // quarter of the (now free) operand slots and stores whole rows.
     const int lrow = lane & 31, lcol = (lane >> 5) * 4;
-    if (EPI == EPI_STORE || EPI == EPI_SWIGLU) {
-        constexpr int RS = 272;                   // LDS row stride of a staged sub-tile (bytes)
-        __syncthreads();                          // every wave is done reading the slots
-        char* const stg = sm.st + wid * EPI_WAVE_BYTES;
-        const int rr = lane >> 4, ck = lane & 15;  // read-back: 16 lanes per 256-byte row
-        auto lds_sync = []() __attribute__((always_inline)) {
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        };
-        if (EPI == EPI_STORE) {
-            bf16_t* C = g.C + e * g.c_es + (GK ? 0 : (int64_t)row0 * g.ldc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<uint2*>(stg + (i * 32 + lrow) * RS +
-                                                  (j * 32 + 8 * q + lcol) * 2) =
-                            make_uint2(pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                                       pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
-            lds_sync();
-            const int col = n0 + wn * 128 + ck * 8;
-#pragma unroll 8
-            for (int p = 0; p < 32; ++p) {
-                const int r = 4 * p + rr, row = m0 + wm * 128 + r;
-                const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * RS + ck * 16);
-                if (row < Mvalid && col < g.N) st16(C + (int64_t)row * g.ldc + col, v);
-            }
-        } else {
-            // block (i, j) of a lane: channels 16 j + 8 hf + lcol .. +3 (hf = 0, 1) of the
-            // wave's 64 (ch_w ..), gate at accumulators 4 hf .. +3, up at 8 + 4 hf .. +3
-            const int ch_w = ch0 + wn * 64;
-            if (ch_w < g.I) {
-                if (g.C2) {
-                    // saved g|u: staged rows hold g (channels 0-63) then u (64-127)
-                    bf16_t* C2 = g.C2 + e * g.c2_es + (int64_t)row0 * g.ldc2;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-#pragma unroll
-                            for (int hf = 0; hf < 2; ++hf) {
-                                const f32x16& a = acc[i][j];
-                                char* rp = stg + (i * 32 + lrow) * RS + (j * 16 + 8 * hf + lcol) * 2;
-                                *reinterpret_cast<uint2*>(rp) =
-                                    make_uint2(pack_bf2(a[4 * hf], a[4 * hf + 1]),
-                                               pack_bf2(a[4 * hf + 2], a[4 * hf + 3]));
-                                *reinterpret_cast<uint2*>(rp + 128) =
-                                    make_uint2(pack_bf2(a[8 + 4 * hf], a[8 + 4 * hf + 1]),
-                                               pack_bf2(a[8 + 4 * hf + 2], a[8 + 4 * hf + 3]));
-                            }
-                    lds_sync();
-                    const int gcol = (ck < 8 ? 0 : g.I) + ch_w + (ck & 7) * 8;
-#pragma unroll 8
-                    for (int p = 0; p < 32; ++p) {
-                        const int r = 4 * p + rr, row = m0 + wm * 128 + r;
-                        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * RS + ck * 16);
-                        if (row < Mvalid) st16(C2 + (int64_t)row * g.ldc2 + gcol, v);
-                    }
-                    lds_sync();  // the reads are done before h overwrites the rows
-                }
-                // h = silu(g) u: staged rows of 64 channels (128 bytes), read back by 8 lanes
-                bf16_t* C = g.C + e * g.c_es + (int64_t)row0 * g.ldc;
+    __syncthreads();                                  // every wave is done reading the slots
+    char* const stg = sm.st + wid * EPI_WAVE_BYTES;
+    const int wrow = m0 + wm * 128;                   // the wave's first row (of the tile's rows)
+    if (EPI == EPI_STORE) {
+        bf16_t* C = g.C + e * g.c_es + (GK ? 0 : (int64_t)row0 * g.ldc);
+        const int col = n0 + wn * 128;
+        stage_bf16(stg, acc, lane);
+        lds_wait();
+        store_staged(stg, C + (int64_t)wrow * g.ldc + col, g.ldc, Mvalid - wrow, g.N - col, lane);
+    } else if (EPI == EPI_SWIGLU) {
+        // block (i, j) of a lane: channels 16 j + 8 hf + lcol .. +3 (hf = 0, 1) of the wave's
+        // 64 (ch_w ..), gate at accumulators 4 hf .. +3, up at 8 + 4 hf .. +3; the wave's 64
+        // channels exist all or none (I % 64 == 0)
+        const int ch_w = ch0 + wn * 64;
+        if (ch_w < g.I) {
+            if (g.C2) {
+                // saved g|u: staged rows hold g (channels 0-63, bytes 0-127) then u (128-255)
+                bf16_t* C2 = g.C2 + e * g.c2_es + (int64_t)row0 * g.ldc2;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -584,99 +534,59 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
 #pragma unroll
                         for (int hf = 0; hf < 2; ++hf) {
                             const f32x16& a = acc[i][j];
-                            float hv[4];
-#pragma unroll
-                            for (int c = 0; c < 4; ++c) {
-                                const float gv = a[4 * hf + c], uv = a[8 + 4 * hf + c];
-                                hv[c] = gv / (1.0f + __expf(-gv)) * uv;
-                            }
-                            *reinterpret_cast<uint2*>(stg + (i * 32 + lrow) * RS +
-                                                      (j * 16 + 8 * hf + lcol) * 2) =
-                                make_uint2(pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3]));
+                            char* rp = stg + (i * 32 + lrow) * STG_RS + (j * 16 + 8 * hf + lcol) * 2;
+                            *reinterpret_cast<uint2*>(rp) =
+                                make_uint2(pack_bf2(a[4 * hf], a[4 * hf + 1]),
+                                           pack_bf2(a[4 * hf + 2], a[4 * hf + 3]));
+                            *reinterpret_cast<uint2*>(rp + 128) =
+                                make_uint2(pack_bf2(a[8 + 4 * hf], a[8 + 4 * hf + 1]),
+                                           pack_bf2(a[8 + 4 * hf + 2], a[8 + 4 * hf + 3]));
                         }
-                lds_sync();
-                const int r8 = lane >> 3, c8 = lane & 7;
+                lds_wait();
+                const int rr = lane >> 4, ck = lane & 15;
+                const int gcol = (ck < 8 ? 0 : g.I) + ch_w + (ck & 7) * 8;
 #pragma unroll 8
-                for (int p = 0; p < 16; ++p) {
-                    const int r = 8 * p + r8, row = m0 + wm * 128 + r;
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * RS + c8 * 16);
-                    if (row < Mvalid) st16(C + (int64_t)row * g.ldc + ch_w + c8 * 8, v);
+                for (int p = 0; p < 32; ++p) {
+                    const int r = 4 * p + rr, row = wrow + r;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * STG_RS + ck * 16);
+                    if (row < Mvalid) st16(C2 + (int64_t)row * g.ldc2 + gcol, v);
                 }
+                lds_wait();  // the reads are done before h overwrites the rows
             }
-        }
-    } else {  // EPI_DSWIGLU: acc = dh; read saved g|u, write dg|du
-        // Through LDS as well, in two halves of 64 rows: the saved g and u rows of the half
-        // are loaded as whole-row 16-byte chunks into the wave's staging area (g rows 0-63,
-        // u rows 64-127), each lane turns its own g, u elements into dg, du in place (one
-        // lane owns each element), and the rows go back out as whole-row chunks.
-        constexpr int RS = 272;
-        __syncthreads();                          // every wave is done reading the slots
-        char* const stg = sm.st + wid * EPI_WAVE_BYTES;
-        const int rr = lane >> 4, ck = lane & 15;
-        const int chw = n0 + wn * 128;            // the wave's first channel
-        const bool colok = chw + ck * 8 < g.N;    // this lane's 8-channel chunk exists
-        bf16_t* C = g.C + e * g.c_es + (int64_t)row0 * g.ldc;
-        const bf16_t* GU = g.C2 + e * g.c2_es + (int64_t)row0 * g.ldc2;
-        auto lds_sync = []() __attribute__((always_inline)) {
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        };
+            // h = silu(g) u: staged rows of 64 channels (128 bytes), read back by 8 lanes
+            bf16_t* C = g.C + e * g.c_es + (int64_t)row0 * g.ldc;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int rbase = m0 + wm * 128 + half * 64;
-#pragma unroll 4
-            for (int p = 0; p < 16; ++p) {
-                const int r = 4 * p + rr, row = rbase + r;
-                u32x4 gv = {0u, 0u, 0u, 0u}, uv = {0u, 0u, 0u, 0u};
-                if (row < Mvalid && colok) {
-                    const bf16_t* src = GU + (int64_t)row * g.ldc2 + chw + ck * 8;
-                    gv = ld16(src);
-                    uv = ld16(src + g.I);
-                }
-                *reinterpret_cast<u32x4*>(stg + r * RS + ck * 16) = gv;
-                *reinterpret_cast<u32x4*>(stg + (64 + r) * RS + ck * 16) = uv;
-            }
-            lds_sync();
-#pragma unroll
-            for (int ih = 0; ih < 2; ++ih) {
-                const int i = 2 * half + ih;
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        char* pg = stg + (ih * 32 + lrow) * RS + (j * 32 + 8 * q + lcol) * 2;
-                        char* pu = pg + 64 * RS;
-                        const uint2 gg = *reinterpret_cast<const uint2*>(pg);
-                        const uint2 uu = *reinterpret_cast<const uint2*>(pu);
-                        const float gv[4] = {lo_bf(gg.x), hi_bf(gg.x), lo_bf(gg.y), hi_bf(gg.y)};
-                        const float uv[4] = {lo_bf(uu.x), hi_bf(uu.x), lo_bf(uu.y), hi_bf(uu.y)};
-                        float dg[4], du[4];
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const f32x16& a = acc[i][j];
+                        float hv[4];
 #pragma unroll
                         for (int c = 0; c < 4; ++c) {
-                            const float dh = acc[i][j][4 * q + c];
-                            const float sg = 1.0f / (1.0f + __expf(-gv[c]));
-                            dg[c] = dh * uv[c] * sg * (1.0f + gv[c] * (1.0f - sg));
-                            du[c] = dh * gv[c] * sg;
+                            const float gv = a[4 * hf + c], uv = a[8 + 4 * hf + c];
+                            hv[c] = gv / (1.0f + __expf(-gv)) * uv;
                         }
-                        *reinterpret_cast<uint2*>(pg) =
-                            make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
-                        *reinterpret_cast<uint2*>(pu) =
-                            make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
+                        *reinterpret_cast<uint2*>(stg + (i * 32 + lrow) * STG_RS +
+                                                  (j * 16 + 8 * hf + lcol) * 2) =
+                            make_uint2(pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3]));
                     }
-            }
-            lds_sync();
-#pragma unroll 4
+            lds_wait();
+            const int r8 = lane >> 3, c8 = lane & 7;
+#pragma unroll 8
             for (int p = 0; p < 16; ++p) {
-                const int r = 4 * p + rr, row = rbase + r;
-                const u32x4 dgv = *reinterpret_cast<const u32x4*>(stg + r * RS + ck * 16);
-                const u32x4 duv = *reinterpret_cast<const u32x4*>(stg + (64 + r) * RS + ck * 16);
-                if (row < Mvalid && colok) {
-                    bf16_t* dst = C + (int64_t)row * g.ldc + chw + ck * 8;
-                    st16(dst, dgv);
-                    st16(dst + g.I, duv);
-                }
+                const int r = 8 * p + r8, row = wrow + r;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * STG_RS + c8 * 16);
+                if (row < Mvalid) st16(C + (int64_t)row * g.ldc + ch_w + c8 * 8, v);
             }
-            lds_sync();  // the read-back is done before the next half overwrites the rows
         }
+    } else {  // EPI_DSWIGLU: acc = dh; the saved g|u give dg|du
+        const int chw = n0 + wn * 128;
+        bf16_t* C = g.C + e * g.c_es + (int64_t)row0 * g.ldc;
+        const bf16_t* GU = g.C2 + e * g.c2_es + (int64_t)row0 * g.ldc2;
+        dswiglu_staged(stg, acc, GU + (int64_t)wrow * g.ldc2 + chw, g.ldc2,
+                       C + (int64_t)wrow * g.ldc + chw, g.ldc, g.I, Mvalid - wrow, g.N - chw, lane);
     }
 }
 

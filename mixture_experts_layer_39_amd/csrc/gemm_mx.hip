@@ -552,8 +552,13 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
 
     // ---------------------------------------------------------------- epilogue
     // B fragment first: lane l holds row l % 32 of its 32x32 block and columns
-    // 8 (v/4) + 4 (l/32) + v%4, v = 0..15: four runs of 4 consecutive columns.
+    // 8 (v/4) + 4 (l/32) + v%4, v = 0..15: four runs of 4 consecutive columns.  Stores go
+    // through LDS (staged epilogues, pipe.h): each wave stages its 128 x 128 sub-tile in its
+    // quarter of the (now free) operand slots and stores whole rows.
     const int lrow = lane & 31, lcol = (lane >> 5) * 4;
+    __syncthreads();                                  // every wave is done reading the slots
+    char* const stg = sm.st + wid * (5 * XOPB / 4);
+    const int wrow = m0 + wm * 128;                   // the wave's first row (of the tile's rows)
     if (EPI == XEPI_SWIGLU_MX) {
         // block (i, j): channels ch0 + 64 wn + 16 j + 8 hf + lcol .. +3; gate at accumulators
         // 4 hf .. +3, up at 8 + 4 hf .. +3.  h = silu(g) u in fp32 is MX-quantised here, along
@@ -561,122 +566,117 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
         // row sits in lanes l and l ^ 32 (16 values each), so its maximum takes one exchange
         // between the two halves of the wave.  Same values, same encoder and same order-free
         // maximum as quantising a stored fp32 h: the same codes and scales.
-        const int64_t rb = (int64_t)e * g.c_es + row0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = m0 + wm * 128 + i * 32 + lrow;
-            if (row >= Mrows) continue;  // lanes l and l ^ 32 hold the same row
-            const int64_t r = rb + row;
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int cb = ch0 + wn * 64 + b * 32;  // the block's first channel
-                if (cb >= g.I) continue;                 // uniform over the wave
-                float hv[2][2][4];
-                float amax = 0.0f;
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            const f32x16& a = acc[i][2 * b + jj];
-                            const float gv = a[4 * hf + c], uv = a[8 + 4 * hf + c];
-                            const float h = gv / (1.0f + __expf(-gv)) * uv;
-                            hv[jj][hf][c] = h;
-                            amax = fmaxf(amax, fabsf(h));
-                        }
-                amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-                const int sc = mx_scale_code(amax, MOE_MX_FLOOR);
-                const int sh = 127 - sc;
-                const float f = ldexpf(1.0f, sc - 127);
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const int ch = cb + 16 * jj + 8 * hf + lcol;
-                        const float* h4 = hv[jj][hf];
-                        const uint32_t w = e4m3x4(ldexpf(h4[0], sh), ldexpf(h4[1], sh),
-                                                  ldexpf(h4[2], sh), ldexpf(h4[3], sh));
-                        *reinterpret_cast<uint32_t*>(g.Cq + r * g.ldc + ch) = w;
-                        if (g.Ch) {  // the quantised values (exact in bf16)
-                            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-                            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-                            *reinterpret_cast<uint2*>(g.Ch + r * g.ldc + ch) =
-                                make_uint2(pack_bf2(lo[0] * f, lo[1] * f),
-                                           pack_bf2(hi[0] * f, hi[1] * f));
-                        }
-                    }
-                if (lane < 32) g.Cs[r * (g.ldc / 32) + cb / 32] = (uint8_t)sc;
-            }
+        const int ch_w = ch0 + wn * 64;  // the wave's 64 channels exist all or none (I % 64)
+        if (ch_w < g.I) {
+            const int64_t rb = (int64_t)e * g.c_es + row0;  // row base of the outputs
             if (g.C2) {
-                bf16_t* gr = g.C2 + r * g.ldc2;
+                // saved g|u: staged rows hold g (channels 0-63, bytes 0-127) then u (128-255)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const int ch = ch0 + wn * 64 + j * 16 + 8 * hf + lcol;
-                        if (ch >= g.I) continue;
-                        const f32x16& a = acc[i][j];
-                        *reinterpret_cast<uint2*>(gr + ch) =
-                            make_uint2(pack_bf2(a[4 * hf], a[4 * hf + 1]),
-                                       pack_bf2(a[4 * hf + 2], a[4 * hf + 3]));
-                        *reinterpret_cast<uint2*>(gr + g.I + ch) =
-                            make_uint2(pack_bf2(a[8 + 4 * hf], a[8 + 4 * hf + 1]),
-                                       pack_bf2(a[8 + 4 * hf + 2], a[8 + 4 * hf + 3]));
-                    }
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const f32x16& a = acc[i][j];
+                            char* rp = stg + (i * 32 + lrow) * STG_RS + (j * 16 + 8 * hf + lcol) * 2;
+                            *reinterpret_cast<uint2*>(rp) =
+                                make_uint2(pack_bf2(a[4 * hf], a[4 * hf + 1]),
+                                           pack_bf2(a[4 * hf + 2], a[4 * hf + 3]));
+                            *reinterpret_cast<uint2*>(rp + 128) =
+                                make_uint2(pack_bf2(a[8 + 4 * hf], a[8 + 4 * hf + 1]),
+                                           pack_bf2(a[8 + 4 * hf + 2], a[8 + 4 * hf + 3]));
+                        }
+                lds_wait();
+                const int rr = lane >> 4, ck = lane & 15;
+                const int gcol = (ck < 8 ? 0 : g.I) + ch_w + (ck & 7) * 8;
+#pragma unroll 8
+                for (int p = 0; p < 32; ++p) {
+                    const int r = 4 * p + rr, row = wrow + r;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * STG_RS + ck * 16);
+                    if (row < Mrows) st16(g.C2 + (rb + row) * g.ldc2 + gcol, v);
+                }
+                lds_wait();  // the reads are done before the codes overwrite the rows
+            }
+            // codes (rows of 64 bytes, stride 80) and the bf16 save of the quantised values
+            // (rows of 128 bytes, stride 144, after the codes)
+            constexpr int CRS = 80, HRS = 144, HOFF = 128 * CRS;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = i * 32 + lrow, row = wrow + r;
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    float hv[2][2][4];
+                    float amax = 0.0f;
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                const f32x16& a = acc[i][2 * b + jj];
+                                const float gv = a[4 * hf + c], uv = a[8 + 4 * hf + c];
+                                const float h = gv / (1.0f + __expf(-gv)) * uv;
+                                hv[jj][hf][c] = h;
+                                amax = fmaxf(amax, fabsf(h));
+                            }
+                    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+                    const int sc = mx_scale_code(amax, MOE_MX_FLOOR);
+                    const int sh = 127 - sc;
+                    const float f = ldexpf(1.0f, sc - 127);
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const int cw = b * 32 + 16 * jj + 8 * hf + lcol;  // channel in the wave
+                            const float* h4 = hv[jj][hf];
+                            const uint32_t w = e4m3x4(ldexpf(h4[0], sh), ldexpf(h4[1], sh),
+                                                      ldexpf(h4[2], sh), ldexpf(h4[3], sh));
+                            *reinterpret_cast<uint32_t*>(stg + r * CRS + cw) = w;
+                            if (g.Ch) {  // the quantised values (exact in bf16)
+                                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+                                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+                                *reinterpret_cast<uint2*>(stg + HOFF + r * HRS + cw * 2) =
+                                    make_uint2(pack_bf2(lo[0] * f, lo[1] * f),
+                                               pack_bf2(hi[0] * f, hi[1] * f));
+                            }
+                        }
+                    if (lane < 32 && row < Mrows)
+                        g.Cs[(rb + row) * (g.ldc / 32) + (ch_w + b * 32) / 32] = (uint8_t)sc;
+                }
+            }
+            lds_wait();
+            {   // codes: 4 lanes per 64-byte row, 16 rows per instruction
+                const int r4 = lane >> 2, c4 = lane & 3;
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+                    const int r = 16 * p + r4, row = wrow + r;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * CRS + c4 * 16);
+                    if (row < Mrows) st16(g.Cq + (rb + row) * g.ldc + ch_w + c4 * 16, v);
+                }
+            }
+            if (g.Ch) {  // h save: 8 lanes per 128-byte row, 8 rows per instruction
+                const int r8 = lane >> 3, c8 = lane & 7;
+#pragma unroll 8
+                for (int p = 0; p < 16; ++p) {
+                    const int r = 8 * p + r8, row = wrow + r;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + HOFF + r * HRS + c8 * 16);
+                    if (row < Mrows) st16(g.Ch + (rb + row) * g.ldc + ch_w + c8 * 8, v);
+                }
             }
         }
     } else if (EPI == XEPI_DSWIGLU) {
-        // acc = dh at channels col .. col+3; the saved g|u of the row give dg|du
+        // acc = dh at the wave's 128 channels; the saved g|u of the rows give dg|du
+        const int chw = n0 + wn * 128;
         bf16_t* C = (bf16_t*)g.C + ((int64_t)e * g.c_es + row0) * g.ldc;
         const bf16_t* GU = g.C2 + ((int64_t)e * g.c_es + row0) * g.ldc2;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = m0 + wm * 128 + i * 32 + lrow;
-            if (row >= Mrows) continue;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int ch = n0 + wn * 128 + j * 32 + 8 * q + lcol;
-                    if (ch >= g.N) continue;
-                    const uint2 gg = *reinterpret_cast<const uint2*>(GU + (int64_t)row * g.ldc2 + ch);
-                    const uint2 uu =
-                        *reinterpret_cast<const uint2*>(GU + (int64_t)row * g.ldc2 + g.I + ch);
-                    const float gv[4] = {lo_bf(gg.x), hi_bf(gg.x), lo_bf(gg.y), hi_bf(gg.y)};
-                    const float uv[4] = {lo_bf(uu.x), hi_bf(uu.x), lo_bf(uu.y), hi_bf(uu.y)};
-                    float dg[4], du[4];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const float dh = acc[i][j][4 * q + c];
-                        const float sg = 1.0f / (1.0f + __expf(-gv[c]));
-                        dg[c] = dh * uv[c] * sg * (1.0f + gv[c] * (1.0f - sg));
-                        du[c] = dh * gv[c] * sg;
-                    }
-                    bf16_t* cr = C + (int64_t)row * g.ldc;
-                    *reinterpret_cast<uint2*>(cr + ch) =
-                        make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
-                    *reinterpret_cast<uint2*>(cr + g.I + ch) =
-                        make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
-                }
-        }
+        dswiglu_staged(stg, acc, GU + (int64_t)wrow * g.ldc2 + chw, g.ldc2,
+                       C + (int64_t)wrow * g.ldc + chw, g.ldc, g.I, Mrows - wrow, g.N - chw, lane);
     } else {
         bf16_t* C = (bf16_t*)g.C + ((int64_t)e * g.c_es + row0) * g.ldc;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = m0 + wm * 128 + i * 32 + lrow;
-            if (row >= Mrows) continue;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int col = n0 + wn * 128 + j * 32 + 8 * q + lcol;
-                    if (col >= g.N) continue;
-                    *reinterpret_cast<uint2*>(C + (int64_t)row * g.ldc + col) =
-                        make_uint2(pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                                   pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
-                }
-        }
+        const int col = n0 + wn * 128;
+        stage_bf16(stg, acc, lane);
+        lds_wait();
+        store_staged(stg, C + (int64_t)wrow * g.ldc + col, g.ldc, Mrows - wrow, g.N - col, lane);
     }
 }
 

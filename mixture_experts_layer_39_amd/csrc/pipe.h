@@ -175,4 +175,117 @@ __device__ __forceinline__ void issue_load(const Operand& o, uint32_t stage_op, 
                soff + (uint32_t)((i >> 1) & 1) * o.ist1 + (uint32_t)(i >> 2) * o.ist2);
 }
 
+// ---------------------------------------------------------------- staged epilogues
+// After the K loop each wave owns a 128 x 128 output sub-tile in accumulators: 4 x 4 blocks of
+// 32 x 32, B fragment first, so lane l holds row l % 32 of a block and columns
+// 8 (v / 4) + 4 (l / 32) + v % 4, v = 0..15.  Stores go through LDS: the wave writes its
+// sub-tile into a private staging area (row-major, rows STG_RS bytes apart: 256 bytes plus a
+// 16-byte pad that spreads the 32 rows of one accumulator write over the banks) and reads it
+// back as 16-byte chunks of whole rows, 16 lanes per 256-byte row, so that each global store
+// instruction writes complete 128-byte lines.
+constexpr int STG_RS = 272;
+constexpr int STG_BYTES = 128 * STG_RS;  // one wave's staging area
+
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// The sub-tile's values as bf16 rows of the staging area.
+__device__ __forceinline__ void stage_bf16(char* stg, const f32x16 (&acc)[4][4], int lane) {
+    const int lrow = lane & 31, lcol = (lane >> 5) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<uint2*>(stg + (i * 32 + lrow) * STG_RS + (j * 32 + 8 * q + lcol) * 2) =
+                    make_uint2(pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                               pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+}
+
+// Staged rows 0..127 (256 bytes each) to C + r * ldc for r < nrows; the 8-column chunk at
+// column c is written when c < ncols.
+__device__ __forceinline__ void store_staged(const char* stg, bf16_t* C, int64_t ldc, int nrows,
+                                             int ncols, int lane) {
+    const int rr = lane >> 4, ck = lane & 15;
+    const bool colok = ck * 8 < ncols;
+#pragma unroll 8
+    for (int p = 0; p < 32; ++p) {
+        const int r = 4 * p + rr;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * STG_RS + ck * 16);
+        if (r < nrows && colok) st16(C + (int64_t)r * ldc + ck * 8, v);
+    }
+}
+
+// The SwiGLU backward of a dgrad sub-tile (acc = dh at 128 rows x 128 channels): with the
+// saved g at GU + r * ldgu + c (u at + I) it writes dg at C + r * ldc + c and du at + I, for
+// rows r < nrows and 8-channel chunks with c < ncols.  In two halves of 64 rows: the g and u
+// rows of the half are loaded as whole-row 16-byte chunks into the staging area (g rows 0-63,
+// u rows 64-127), each lane turns its own g, u elements into dg, du in place (one lane owns
+// each element), and the rows go back out whole.
+__device__ __forceinline__ void dswiglu_staged(char* stg, const f32x16 (&acc)[4][4],
+                                               const bf16_t* GU, int64_t ldgu, bf16_t* C,
+                                               int64_t ldc, int I, int nrows, int ncols,
+                                               int lane) {
+    const int lrow = lane & 31, lcol = (lane >> 5) * 4;
+    const int rr = lane >> 4, ck = lane & 15;
+    const bool colok = ck * 8 < ncols;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int rb = half * 64;
+#pragma unroll 4
+        for (int p = 0; p < 16; ++p) {
+            const int r = 4 * p + rr;
+            u32x4 gv = {0u, 0u, 0u, 0u}, uv = {0u, 0u, 0u, 0u};
+            if (rb + r < nrows && colok) {
+                const bf16_t* src = GU + (int64_t)(rb + r) * ldgu + ck * 8;
+                gv = ld16(src);
+                uv = ld16(src + I);
+            }
+            *reinterpret_cast<u32x4*>(stg + r * STG_RS + ck * 16) = gv;
+            *reinterpret_cast<u32x4*>(stg + (64 + r) * STG_RS + ck * 16) = uv;
+        }
+        lds_wait();
+#pragma unroll
+        for (int ih = 0; ih < 2; ++ih) {
+            const int i = 2 * half + ih;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    char* pg = stg + (ih * 32 + lrow) * STG_RS + (j * 32 + 8 * q + lcol) * 2;
+                    char* pu = pg + 64 * STG_RS;
+                    const uint2 gg = *reinterpret_cast<const uint2*>(pg);
+                    const uint2 uu = *reinterpret_cast<const uint2*>(pu);
+                    const float gv[4] = {lo_bf(gg.x), hi_bf(gg.x), lo_bf(gg.y), hi_bf(gg.y)};
+                    const float uv[4] = {lo_bf(uu.x), hi_bf(uu.x), lo_bf(uu.y), hi_bf(uu.y)};
+                    float dg[4], du[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float dh = acc[i][j][4 * q + c];
+                        const float sg = 1.0f / (1.0f + __expf(-gv[c]));
+                        dg[c] = dh * uv[c] * sg * (1.0f + gv[c] * (1.0f - sg));
+                        du[c] = dh * gv[c] * sg;
+                    }
+                    *reinterpret_cast<uint2*>(pg) =
+                        make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
+                    *reinterpret_cast<uint2*>(pu) =
+                        make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
+                }
+        }
+        lds_wait();
+#pragma unroll 4
+        for (int p = 0; p < 16; ++p) {
+            const int r = 4 * p + rr;
+            const u32x4 dgv = *reinterpret_cast<const u32x4*>(stg + r * STG_RS + ck * 16);
+            const u32x4 duv = *reinterpret_cast<const u32x4*>(stg + (64 + r) * STG_RS + ck * 16);
+            if (rb + r < nrows && colok) {
+                bf16_t* dst = C + (int64_t)(rb + r) * ldc + ck * 8;
+                st16(dst, dgv);
+                st16(dst + I, duv);
+            }
+        }
+        lds_wait();  // the read-back is done before the next half overwrites the rows
+    }
+}
+
 }  // namespace moe
