@@ -145,7 +145,7 @@ def gemm_bytes(wl, role: str, shared: bool) -> float:
     return {
         "gemm1_swiglu": xp + 2 * w + h + gu_save,          # Xp, W1 in; h (and g|u) out
         "gemm2_down": h + w + xp,                          # h, W2 in; y out
-        "ffn_queue": xp + 2 * w + 2 * h + w + xp,          # both products (h out and in)
+        "ffn_queue": xp + 2 * w + 2 * h + w + xp + gu_save,  # both products (h out and in)
         "bwd_down": xp + w + gu + gu + h + w,              # dy, W2, g|u, h in; dGU, dW2 out
         "bwd_gate_up": gu + 2 * w + xp + xp + 2 * w,       # dGU, W1, Xp in; dXp, dW1 out
     }.get(role, 0.0)

@@ -178,12 +178,11 @@ int moe_dispatch(const void *x, int T, int H, int k, const int32_t *src, const i
  * Limits: H % 64 == 0, I % 64 == 0 (both % 128 for MOE_MXFP8), offsets non-decreasing with
  * offsets[E] <= R.
  * Workspace: moe_ffn_workspace_size().  MOE_MXFP8 always needs it.  MOE_BF16 with a workspace
- *   of that size and gu_save == NULL runs both products as ONE launch: a queue of GEMM1 and
- *   GEMM2 tiles in which a GEMM2 tile waits only for the GEMM1 tiles of its own rows
- *   (per-row-block counters in the workspace, cleared by a small kernel before the launch),
- *   so the second product fills the first one's last, partial round.  With gu_save, or
- *   without a workspace (h_save given), the two products run as two launches.  Both forms
- *   give bit-identical outputs.  The queue form clears its counters and the uint32 at byte
+ *   of that size runs both products as ONE launch: a queue of GEMM1 and GEMM2 tiles in which
+ *   a GEMM2 tile waits only for the GEMM1 tiles of its own rows (per-row-block counters in
+ *   the workspace, cleared by a small kernel before the launch), so the second product
+ *   fills the first one's last, partial round.  Without a workspace (h_save given) the two
+ *   products run as two launches.  Both forms give bit-identical outputs.  The queue form clears its counters and the uint32 at byte
  *   moe_ffn_error_offset() of the workspace before it starts; a queue wait is bounded (2 s),
  *   and past it that word becomes nonzero and the outputs are not valid.  The two-launch form
  *   does not touch the word.  Calls that share a workspace must be stream-ordered. */

@@ -170,15 +170,16 @@ extern "C" int moe_expert_ffn(int dtype, const void* xp, const uint8_t* xp_scale
     hipStream_t st = (hipStream_t)stream;
     size_t rows = offsets ? (size_t)R : (size_t)E * R;
     if (dtype == MOE_BF16) {
-        // The one-launch queue makes every GEMM1 tile write its XCD's L2 back before it
-        // counts itself done; with the g|u saves that flush also carries the saves' dirty
-        // lines and measured slower than two launches (1.29 against 1.27 ms at the EP-64
-        // share), without them faster (1.21 against 1.23 ms).  So: saves -> two launches.
+        // With a workspace both products run as one launch (the tile queue): GEMM2 tiles
+        // fill the last round of GEMM1 tiles.  Every GEMM1 tile writes its XCD's L2 back
+        // before it counts itself done; the g|u save goes out with whole-line non-temporal
+        // stores, so that flush carries only h (1.28 against 1.32 ms for two launches at
+        // the EP-64 share, with the save).  Without a workspace (h_save given): two launches.
         // h: the caller's save, else the workspace after the synchronisation words (a
         // workspace is there whenever h_save is not: checked above)
         const size_t sync = moe_ffn_sync_bytes(E, R, offsets == nullptr);
         bf16_t* h = h_save ? (bf16_t*)h_save : (bf16_t*)((char*)ws + sync);
-        if (!have_ws || gu_save)
+        if (!have_ws)
             return moe_ffn_bf16((const bf16_t*)xp, offsets, E, R, H, I, (const bf16_t*)w1,
                                 (const bf16_t*)w2, (bf16_t*)gu_save, h, (bf16_t*)y, st);
         return moe_ffn_bf16_queue((const bf16_t*)xp, offsets, E, R, H, I, (const bf16_t*)w1,

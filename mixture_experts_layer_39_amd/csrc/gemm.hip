@@ -549,7 +549,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
                 for (int p = 0; p < 32; ++p) {
                     const int r = 4 * p + rr, row = wrow + r;
                     const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * STG_RS + ck * 16);
-                    if (row < Mvalid) st16(C2 + (int64_t)row * g.ldc2 + gcol, v);
+                    // non-temporal: only the backward reads the save, much later
+                    if (row < Mvalid) st16_nt(C2 + (int64_t)row * g.ldc2 + gcol, v);
                 }
                 lds_wait();  // the reads are done before h overwrites the rows
             }

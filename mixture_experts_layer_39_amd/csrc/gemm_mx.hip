@@ -593,7 +593,8 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
                 for (int p = 0; p < 32; ++p) {
                     const int r = 4 * p + rr, row = wrow + r;
                     const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * STG_RS + ck * 16);
-                    if (row < Mrows) st16(g.C2 + (rb + row) * g.ldc2 + gcol, v);
+                    // non-temporal: only the backward reads the save, much later
+                    if (row < Mrows) st16_nt(g.C2 + (rb + row) * g.ldc2 + gcol, v);
                 }
                 lds_wait();  // the reads are done before the codes overwrite the rows
             }

@@ -264,8 +264,8 @@ def test_expert_ffn_mxfp8_parity():
 
 def _ffn_forms(E, R, H, I, off, seed):
     """The BF16 FFN in its three forms: two launches without a workspace (h and g|u saved),
-    two launches with a workspace (the g|u save keeps them), and one queue launch (workspace,
-    no g|u save).  Returns (y, gu, h, ws) of each."""
+    one queue launch with a workspace and the g|u save, and one queue launch without the
+    save.  Returns (y, gu, h, ws) of each."""
     xp, w1, w2 = _ffn_case(E, R, H, I, off, seed)
     offs = torch.tensor(off, dtype=torch.int32, device=DEV)
     outs = []
@@ -296,8 +296,8 @@ def test_expert_ffn_one_launch_bit_identical(shape):
     E, H, I, off = shape
     R = off[-1]
     print(f"ffn one-launch case E={E} H={H} I={I} R={R}", flush=True)
-    (y0, gu0, h0, _), (y1, gu1, h1, _), (y2, _, h2, ws) = _ffn_forms(E, R, H, I, off, 11)
-    assert moe.ffn_error(ws) == 0
+    (y0, gu0, h0, _), (y1, gu1, h1, ws1), (y2, _, h2, ws) = _ffn_forms(E, R, H, I, off, 11)
+    assert moe.ffn_error(ws) == 0 and moe.ffn_error(ws1) == 0
     assert torch.equal(gu0, gu1)
     for y, h in ((y1, h1), (y2, h2)):
         assert torch.equal(y0, y) and torch.equal(h0, h)
