@@ -517,7 +517,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         const int col = n0 + wn * 128;
         stage_bf16(stg, acc, lane);
         lds_wait();
-        store_staged(stg, C + (int64_t)wrow * g.ldc + col, g.ldc, Mvalid - wrow, g.N - col, lane);
+        // weight gradients (GK): written once per step and read by nothing in it
+        store_staged<GK>(stg, C + (int64_t)wrow * g.ldc + col, g.ldc, Mvalid - wrow, g.N - col,
+                         lane);
     } else if (EPI == EPI_SWIGLU) {
         // block (i, j) of a lane: channels 16 j + 8 hf + lcol .. +3 (hf = 0, 1) of the wave's
         // 64 (ch_w ..), gate at accumulators 4 hf .. +3, up at 8 + 4 hf .. +3; the wave's 64

@@ -204,6 +204,9 @@ __device__ __forceinline__ void stage_bf16(char* stg, const f32x16 (&acc)[4][4],
 
 // Staged rows 0..127 (256 bytes each) to C + r * ldc for r < nrows; the 8-column chunk at
 // column c is written when c < ncols.
+// Non-temporal (nt) stores neither allocate in nor evict from the caches: for results that
+// nothing reads again soon (weight gradients).
+template <bool NT = false>
 __device__ __forceinline__ void store_staged(const char* stg, bf16_t* C, int64_t ldc, int nrows,
                                              int ncols, int lane) {
     const int rr = lane >> 4, ck = lane & 15;
@@ -212,7 +215,10 @@ __device__ __forceinline__ void store_staged(const char* stg, bf16_t* C, int64_t
     for (int p = 0; p < 32; ++p) {
         const int r = 4 * p + rr;
         const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * STG_RS + ck * 16);
-        if (r < nrows && colok) st16(C + (int64_t)r * ldc + ck * 8, v);
+        if (r < nrows && colok) {
+            if (NT) st16_nt(C + (int64_t)r * ldc + ck * 8, v);
+            else st16(C + (int64_t)r * ldc + ck * 8, v);
+        }
     }
 }
 
