@@ -215,15 +215,22 @@ __device__ __forceinline__ TileAt tile_at(const GemmArgs& g, const int logical) 
     return t;
 }
 
-// One 256 x 256 output tile, number `logical` of the product (tiles run in launch order: the
+// One TM x 256 output tile at M tile `at.tm` of the product (tiles run in launch order: the
 // blocks in flight at once, spread over all XCDs, work on neighbouring tiles whose operand
 // panels meet in the shared last-level cache, which measured faster than giving each XCD
-// its own compact block of tiles).
-template <int BK, bool A_K, bool B_K, int EPI, bool GK>
+// its own compact block of tiles).  TM = 256, or 128 / 64 for the last, partial M tile of an
+// expert (K-major A only): the tile covers the first TM of the M tile's 256 rows, each wave
+// TM / 2 of them, and every output element takes exactly the same MFMAs in the same order
+// as in a 256-row tile, so the results do not depend on TM.
+template <int BK, int TM, bool A_K, bool B_K, int EPI, bool GK>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const TileAt& at) {
     typedef Pipe<BK> PP;
     constexpr int KK = PP::KK, NST = PP::NST, OPB = PP::OPB, LPW = PP::LPW, LPS = PP::LPS;
     constexpr bool SLOTS5 = (BK == 64) && MOE_GEMM_SLOTS5;
+    static_assert(TM == 256 || (TM == 128 || TM == 64) && A_K && SLOTS5, "tile heights");
+    constexpr int MI = TM / 64;      // 32-row accumulator blocks per wave
+    constexpr int LPA = TM / 32;     // A loads per wave per K step (LPW for a 256-row tile)
+    constexpr int WBA = TM * 32;     // bytes of A a wave loads per K step
     const int tid = threadIdx.x, lane = tid & 63, wid = uni(tid >> 6);
     const int wm = wid >> 1, wn = wid & 1;
     const int e = at.e, row0 = at.row0, Mrows = at.Mrows, tm = at.tm, tn = at.tn;
@@ -244,8 +251,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     Operand oa, ob;
     if (A_K) {
         const bf16_t* base = g.A + e * g.a_es + (int64_t)(row0 + m0) * g.lda;
-        setup_kmajor<BK>(oa, base, (uint32_t)max(Mrows - m0, 0) * (uint32_t)g.lda * 2u, g.lda, wid,
-                     lane, wm * 128, [](int r) { return r; }, 2 * PP::RPI, 4 * PP::RPI);
+        auto ident = [](int r) { return r; };
+        setup_kmajor<BK, decltype(ident), TM / 4>(
+            oa, base, (uint32_t)max(Mrows - m0, 0) * (uint32_t)g.lda * 2u, g.lda, wid, lane,
+            wm * (TM / 2), ident, 2 * PP::RPI, 4 * PP::RPI);
     } else {
         const bf16_t* base = g.A + e * g.a_es + (int64_t)row0 * g.lda + m0;
         setup_mnmajor<BK>(oa, base, mn_bytes(Kdim, g.lda, m0), g.lda, wid, lane, wm * 128);
@@ -268,9 +277,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         setup_mnmajor<BK>(ob, base, mn_bytes(Kdim, g.ldb, n0), g.ldb, wid, lane, wn * 128);
     }
 
-    f32x16 acc[4][4];
+    f32x16 acc[MI][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -281,7 +290,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     // other products allocate better without it).
     auto pin_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
     };
@@ -349,8 +358,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         sa = (uint32_t)(ks - cur_start) * oa.kstep;
         sb = (uint32_t)(ks - cur_start) * ob.kstep;
     };
-    bf16x8 fa[2][4], fb[2][4];
-    // read number r (0..7) of a sub-step, in MFMA consumption order: a0 b0 b1 b2 b3 a1 a2 a3
+    bf16x8 fa[2][MI], fb[2][4];
+    // read number r (0 .. NR - 1) of a sub-step, in MFMA consumption order: a0 b0 b1 b2 b3
+    // a1 .. a(MI - 1)
     auto read_ab = [&](const char* sa_, const char* sb_, int kk, int f, int r) __attribute__((always_inline)) {
         if (r == 0) fa[f][0] = read_frag<BK, A_K>(oa, sa_, 0, kk);
         else if (r <= 4) fb[f][r - 1] = read_frag<BK, B_K>(ob, sb_, r - 1, kk);
@@ -363,6 +373,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         const int i = n >> 2, j = n & 3;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0);
     };
+    // Schedule of a sub-step (NM MFMAs): fragment read r after MFMA rslot(r); the sub-step's
+    // ql loads (4 of B, or LPA / 2 of A) at lslot(q).  For TM = 256: reads at the even MFMAs,
+    // loads at every fourth odd one.
+    constexpr int NM = 4 * MI, NR = 4 + MI;
+    auto rslot = [](int r) constexpr { return r * NM / NR; };
+    auto lslot = [](int q, int ql) constexpr { return q * NM / ql + (NM / ql > 1 ? 1 : 0); };
     auto kstep = [&](char* cur, char* nxt, uint32_t cur32, int ks) __attribute__((always_inline)) {
         // sub-steps 0 .. KK-2 (fragments kk % 2), each with the reads of the next one
 #pragma unroll
@@ -370,7 +386,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
 #pragma unroll
             for (int n = 0; n < 16; ++n) {
                 mfma_one(kk & 1, n);
-                if (n < 8) read_one(cur, kk + 1, (kk + 1) & 1, n);
+                if (n < NR) read_one(cur, kk + 1, (kk + 1) & 1, n);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -390,7 +406,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
             mfma_one(fl, n);
             if (n < LPW) issue_load<BK>(oa, cur32, wid, n, ra_, sa);
             else if (n < LPS) issue_load<BK>(ob, cur32 + OPB, wid, n - LPW, rb_, sb);
-            if (n >= 8 && more) read_one(nxt, 0, 0, n - 8);
+            if (n >= 8 && n - 8 < NR && more) read_one(nxt, 0, 0, n - 8);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -421,28 +437,40 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kk = 0; kk < KK - 1; ++kk) {
+            constexpr int QA = LPA / 2;  // A loads per sub-step (sub-steps 1, 2)
 #pragma unroll
-            for (int n = 0; n < 16; ++n) {
+            for (int n = 0; n < NM; ++n) {
                 mfma_one(kk & 1, n);
-                if ((n & 1) == 0) read_ab(cA, cB, kk + 1, (kk + 1) & 1, n / 2);
-                else if ((n & 3) == 1) {
-                    const int q = n / 4;  // 0..3
-                    if (kk == 0) issue_load<BK>(ob, lB1, wid, 4 + q, rb1, sb1);
-                    else issue_load<BK>(oa, lA, wid, 4 * (kk - 1) + q, ra_, sa);
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+                    if (rslot(r) == n) read_ab(cA, cB, kk + 1, (kk + 1) & 1, r);
+                if (kk == 0) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (lslot(q, 4) == n) issue_load<BK>(ob, lB1, wid, 4 + q, rb1, sb1);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < QA; ++q)
+                        if (lslot(q, QA) == n)
+                            issue_load<BK, WBA>(oa, lA, wid, QA * (kk - 1) + q, ra_, sa);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        wait_vm_lgkm0<LPW>();  // A(ks+1), B(ks+1) landed; A(ks+2) may be in flight
+        wait_vm_lgkm0<LPA>();  // A(ks+1), B(ks+1) landed; A(ks+2) may be in flight
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         const bool more = ks + 1 < nk;
         constexpr int fl = (KK - 1) & 1;
 #pragma unroll
-        for (int n = 0; n < 16; ++n) {
+        for (int n = 0; n < NM; ++n) {
             mfma_one(fl, n);
-            if ((n & 3) == 1) issue_load<BK>(ob, lB, wid, n / 4, rb_, sb);
-            if ((n & 1) == 0 && more) read_ab(nA, nB, 0, 0, n / 2);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (lslot(q, 4) == n) issue_load<BK>(ob, lB, wid, q, rb_, sb);
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                if (rslot(r) == n && more) read_ab(nA, nB, 0, 0, r);
             __builtin_amdgcn_sched_barrier(0);
         }
         pend_rb = rb_;
@@ -460,18 +488,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
             load_src(p, ra_, rb_, sa, sb);
 #pragma unroll
             for (int i = 0; i < LPW; ++i) {
-                issue_load<BK>(oa, base32 + (2 * p) * OPB, wid, i, ra_, sa);
+                if (i < LPA) issue_load<BK, WBA>(oa, base32 + (2 * p) * OPB, wid, i, ra_, sa);
                 if (p == 0 || i < LPW / 2)
                     issue_load<BK>(ob, base32 + (2 * p + 1) * OPB, wid, i, rb_, sb);
             }
             pend_rb = rb_;
             pend_sb = sb;
         }
-        wait_vm_lgkm0<LPW + LPW / 2>();  // step 0 landed
+        wait_vm_lgkm0<LPA + LPW / 2>();  // step 0 landed
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) read_ab(sm.st, sm.st + OPB, 0, 0, r);
+        for (int r = 0; r < NR; ++r) read_ab(sm.st, sm.st + OPB, 0, 0, r);
         for (int ks = 0; ks < nk; ks += 5) {
 #pragma unroll
             for (int u = 0; u < 5; ++u)
@@ -479,6 +507,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         }
         wait_vm_lgkm0<0>();  // no load may still be writing LDS when the block ends
     } else if (nk > 0) {
+        static_assert(SLOTS5 || TM == 256, "the stage ring takes 256-row tiles");
         const uint32_t st_base = lds_addr(sm.st);  // stage p at st_base + p * 2 * OPB
 #pragma unroll
         for (int p = 0; p < NST; ++p) {
@@ -495,7 +524,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) read_one(sm.st, 0, 0, r);
+        for (int r = 0; r < NR; ++r) read_one(sm.st, 0, 0, r);
         for (int ks = 0; ks < nk; ks += NST) {
 #pragma unroll
             for (int u = 0; u < NST; ++u)
@@ -511,15 +540,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     const int lrow = lane & 31, lcol = (lane >> 5) * 4;
     __syncthreads();                                  // every wave is done reading the slots
     char* const stg = sm.st + wid * EPI_WAVE_BYTES;
-    const int wrow = m0 + wm * 128;                   // the wave's first row (of the tile's rows)
+    const int wrow = m0 + wm * (TM / 2);              // the wave's first row (of the tile's rows)
+    const int wrows = min(Mvalid - wrow, TM / 2);      // its rows that exist
     if (EPI == EPI_STORE) {
         bf16_t* C = g.C + e * g.c_es + (GK ? 0 : (int64_t)row0 * g.ldc);
         const int col = n0 + wn * 128;
-        stage_bf16(stg, acc, lane);
+        stage_bf16<MI>(stg, acc, lane);
         lds_wait();
         // weight gradients (GK): written once per step and read by nothing in it
-        store_staged<GK>(stg, C + (int64_t)wrow * g.ldc + col, g.ldc, Mvalid - wrow, g.N - col,
-                         lane);
+        store_staged<MI, GK>(stg, C + (int64_t)wrow * g.ldc + col, g.ldc, wrows, g.N - col, lane);
     } else if (EPI == EPI_SWIGLU) {
         // block (i, j) of a lane: channels 16 j + 8 hf + lcol .. +3 (hf = 0, 1) of the wave's
         // 64 (ch_w ..), gate at accumulators 4 hf .. +3, up at 8 + 4 hf .. +3; the wave's 64
@@ -530,7 +559,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
                 // saved g|u: staged rows hold g (channels 0-63, bytes 0-127) then u (128-255)
                 bf16_t* C2 = g.C2 + e * g.c2_es + (int64_t)row0 * g.ldc2;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < MI; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -548,18 +577,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
                 const int rr = lane >> 4, ck = lane & 15;
                 const int gcol = (ck < 8 ? 0 : g.I) + ch_w + (ck & 7) * 8;
 #pragma unroll 8
-                for (int p = 0; p < 32; ++p) {
+                for (int p = 0; p < 8 * MI; ++p) {
                     const int r = 4 * p + rr, row = wrow + r;
                     const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * STG_RS + ck * 16);
                     // non-temporal: only the backward reads the save, much later
-                    if (row < Mvalid) st16_nt(C2 + (int64_t)row * g.ldc2 + gcol, v);
+                    if (r < wrows) st16_nt(C2 + (int64_t)row * g.ldc2 + gcol, v);
                 }
                 lds_wait();  // the reads are done before h overwrites the rows
             }
             // h = silu(g) u: staged rows of 64 channels (128 bytes), read back by 8 lanes
             bf16_t* C = g.C + e * g.c_es + (int64_t)row0 * g.ldc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -578,19 +607,38 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
             lds_wait();
             const int r8 = lane >> 3, c8 = lane & 7;
 #pragma unroll 8
-            for (int p = 0; p < 16; ++p) {
+            for (int p = 0; p < 4 * MI; ++p) {
                 const int r = 8 * p + r8, row = wrow + r;
                 const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * STG_RS + c8 * 16);
-                if (row < Mvalid) st16(C + (int64_t)row * g.ldc + ch_w + c8 * 8, v);
+                if (r < wrows) st16(C + (int64_t)row * g.ldc + ch_w + c8 * 8, v);
             }
         }
     } else {  // EPI_DSWIGLU: acc = dh; the saved g|u give dg|du
         const int chw = n0 + wn * 128;
         bf16_t* C = g.C + e * g.c_es + (int64_t)row0 * g.ldc;
         const bf16_t* GU = g.C2 + e * g.c2_es + (int64_t)row0 * g.ldc2;
-        dswiglu_staged(stg, acc, GU + (int64_t)wrow * g.ldc2 + chw, g.ldc2,
-                       C + (int64_t)wrow * g.ldc + chw, g.ldc, g.I, Mvalid - wrow, g.N - chw, lane);
+        dswiglu_staged<MI>(stg, acc, GU + (int64_t)wrow * g.ldc2 + chw, g.ldc2,
+                           C + (int64_t)wrow * g.ldc + chw, g.ldc, g.I, wrows, g.N - chw, lane);
     }
+}
+
+// A tile of a product: the products with ragged, K-major A (rows of experts) run each
+// expert's last M tile, when it holds at most 128 (64) rows, as a 128-row (64-row) tile: less
+// MFMA work on padding rows, bit-identical results.
+template <int BK, bool A_K, bool B_K, int EPI, bool GK>
+__device__ __forceinline__ void run_tile(const GemmArgs& g, GemmSmem& sm, const TileAt& at) {
+    if (A_K && !GK) {
+        const int rem = at.Mrows - at.tm * BM;
+        if (rem <= 64) {
+            gemm_tile<BK, (A_K && !GK) ? 64 : 256, A_K, B_K, EPI, GK>(g, sm, at);
+            return;
+        }
+        if (rem <= 128) {
+            gemm_tile<BK, (A_K && !GK) ? 128 : 256, A_K, B_K, EPI, GK>(g, sm, at);
+            return;
+        }
+    }
+    gemm_tile<BK, 256, A_K, B_K, EPI, GK>(g, sm, at);
 }
 
 // One kernel symbol per product of the layer, so that profiles name each role.
@@ -604,7 +652,7 @@ constexpr int BK_FWD = 64, BK_DGRAD = 64, BK_WGRAD = 64;
         __shared__ GemmSmem sm;                                                        \
         const int total = tile_total<EPI, GK>(g);                                      \
         if ((int)blockIdx.x < total)                                                    \
-            gemm_tile<BK_FWD, AKM, BKM, EPI, GK>(g, sm, tile_at<EPI, GK>(g, blockIdx.x));  \
+            run_tile<BK_FWD, AKM, BKM, EPI, GK>(g, sm, tile_at<EPI, GK>(g, blockIdx.x));  \
     }
 MOE_GEMM_KERNEL(gemm1_swiglu, true, true, EPI_SWIGLU, false)     // [g|u] = Xp W1^T, h
 MOE_GEMM_KERNEL(gemm2_down, true, true, EPI_STORE, false)        // y = h W2^T
@@ -621,9 +669,9 @@ void bwd_down(GemmArgs gd, GemmArgs gw) {
     const int td = tile_total<EPI_DSWIGLU, false>(gd);
     const int b = blockIdx.x;
     if (b < td)
-        gemm_tile<BK_DGRAD, true, false, EPI_DSWIGLU, false>(gd, sm, tile_at<EPI_DSWIGLU, false>(gd, b));
+        run_tile<BK_DGRAD, true, false, EPI_DSWIGLU, false>(gd, sm, tile_at<EPI_DSWIGLU, false>(gd, b));
     else if (b - td < gw.total)
-        gemm_tile<BK_WGRAD, false, false, EPI_STORE, true>(gw, sm, tile_at<EPI_STORE, true>(gw, b - td));
+        run_tile<BK_WGRAD, false, false, EPI_STORE, true>(gw, sm, tile_at<EPI_STORE, true>(gw, b - td));
 }
 
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -632,9 +680,9 @@ void bwd_gate_up(GemmArgs gd, GemmArgs gw) {
     const int td = tile_total<EPI_STORE, false>(gd);
     const int b = blockIdx.x;
     if (b < td)
-        gemm_tile<BK_DGRAD, true, false, EPI_STORE, false>(gd, sm, tile_at<EPI_STORE, false>(gd, b));
+        run_tile<BK_DGRAD, true, false, EPI_STORE, false>(gd, sm, tile_at<EPI_STORE, false>(gd, b));
     else if (b - td < gw.total)
-        gemm_tile<BK_WGRAD, false, false, EPI_STORE, true>(gw, sm, tile_at<EPI_STORE, true>(gw, b - td));
+        run_tile<BK_WGRAD, false, false, EPI_STORE, true>(gw, sm, tile_at<EPI_STORE, true>(gw, b - td));
 }
 
 // Upper bound on the tile count of a ragged-M product (host side, no device data).
@@ -836,7 +884,7 @@ void layer_forward_fused(FusedFwd a) {
             const bool r = item < n1r;
             const GemmArgs& g = r ? a.g1 : a.s1;
             const TileAt at = tile_at<EPI_SWIGLU, false>(g, r ? item : item - n1r);
-            gemm_tile<BK_FWD, true, true, EPI_SWIGLU, false>(g, sm, at);
+            run_tile<BK_FWD, true, true, EPI_SWIGLU, false>(g, sm, at);
             tile_done(ready1, r ? at.mblock : a.mbr + at.mblock);
         } else {
             const int i2 = item - n1;
@@ -848,7 +896,7 @@ void layer_forward_fused(FusedFwd a) {
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             }
             __syncthreads();
-            gemm_tile<BK_FWD, true, true, EPI_STORE, false>(g, sm, at);
+            run_tile<BK_FWD, true, true, EPI_STORE, false>(g, sm, at);
         }
         __syncthreads();
         if (threadIdx.x == 0) *bcast = next;
@@ -900,7 +948,7 @@ void ffn_queue(FfnQueue q) {
         if (item >= total) break;
         if (item < n1) {
             const TileAt at = tile_at<EPI_SWIGLU, false>(q.g1, item);
-            gemm_tile<BK_FWD, true, true, EPI_SWIGLU, false>(q.g1, sm, at);
+            run_tile<BK_FWD, true, true, EPI_SWIGLU, false>(q.g1, sm, at);
             tile_done(ready, at.mblock);
         } else {
             const TileAt at = tile_at<EPI_STORE, false>(q.g2, item - n1);
@@ -909,7 +957,7 @@ void ffn_queue(FfnQueue q) {
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             }
             __syncthreads();
-            gemm_tile<BK_FWD, true, true, EPI_STORE, false>(q.g2, sm, at);
+            run_tile<BK_FWD, true, true, EPI_STORE, false>(q.g2, sm, at);
         }
         __syncthreads();
     }

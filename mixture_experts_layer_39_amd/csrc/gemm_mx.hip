@@ -677,7 +677,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
         const int col = n0 + wn * 128;
         stage_bf16(stg, acc, lane);
         lds_wait();
-        store_staged(stg, C + (int64_t)wrow * g.ldc + col, g.ldc, Mrows - wrow, g.N - col, lane);
+        store_staged<4>(stg, C + (int64_t)wrow * g.ldc + col, g.ldc, Mrows - wrow, g.N - col, lane);
     }
 }
 

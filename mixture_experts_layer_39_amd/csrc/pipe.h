@@ -110,10 +110,11 @@ struct Operand {
 };
 
 // K-major operand.  rowmap(nn) gives the global row (relative to the descriptor base) of
-// tile row nn.  Each wave loads 64 tile rows, RPI rows of BK * 2 bytes per instruction:
-// tile rows 64 w + RPI i + L / (64 / RPI) for instruction i, whose global rows must be those
-// of instruction i % 2 plus ((i / 2) % 2) rs1 + (i / 4) rs2.
-template <int BK, typename RowMap>
+// tile row nn.  Each wave loads RW tile rows (64 of a 256-row operand; 32 or 16 of a 128- or
+// 64-row one), RPI rows of BK * 2 bytes per instruction: tile rows RW w + RPI i + L / (64 / RPI)
+// for instruction i, whose global rows must be those of instruction i % 2 plus
+// ((i / 2) % 2) rs1 + (i / 4) rs2.
+template <int BK, typename RowMap, int RW = 64>
 __device__ __forceinline__ void setup_kmajor(Operand& o, const void* base, uint32_t bytes, int ld,
                                              int wid, int lane, int wsub, RowMap rowmap,
                                              int rs1, int rs2) {
@@ -122,7 +123,7 @@ __device__ __forceinline__ void setup_kmajor(Operand& o, const void* base, uint3
     o.r = make_rsrc(base, bytes);
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
-        const int r = 64 * wid + PP::RPI * par + lane / CPR;
+        const int r = RW * wid + PP::RPI * par + lane / CPR;
         const int c = (lane % CPR) ^ kswz_of<BK>(r);
         o.voff[par] = (uint32_t)rowmap(r) * (uint32_t)ld * 2u + (uint32_t)c * 16u;
     }
@@ -165,13 +166,14 @@ __device__ __forceinline__ void setup_mnmajor(Operand& o, const void* base, uint
     }
 }
 
-// Load instruction i of K step ks into the operand's area of a stage.  Steps past the end
-// of K use an empty descriptor: the load still issues (so every step issues the same number
-// of loads and the wait counts are constants) but fetches nothing and writes zeros.
-template <int BK>
+// Load instruction i of K step ks into the operand's area of a stage (wave w fills the WB
+// bytes from w WB: a quarter of the operand's rows).  Steps past the end of K use an empty
+// descriptor: the load still issues (so every step issues the same number of loads and the
+// wait counts are constants) but fetches nothing and writes zeros.
+template <int BK, int WB = Pipe<BK>::OPB / 4>
 __device__ __forceinline__ void issue_load(const Operand& o, uint32_t stage_op, int wid, int i,
                                            rsrc_t r, uint32_t soff) {
-    lds_load16(r, stage_op + (uint32_t)(wid * (Pipe<BK>::OPB / 4) + i * 1024), o.voff[i & 1],
+    lds_load16(r, stage_op + (uint32_t)(wid * WB + i * 1024), o.voff[i & 1],
                soff + (uint32_t)((i >> 1) & 1) * o.ist1 + (uint32_t)(i >> 2) * o.ist2);
 }
 
@@ -188,11 +190,12 @@ constexpr int STG_BYTES = 128 * STG_RS;  // one wave's staging area
 
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// The sub-tile's values as bf16 rows of the staging area.
-__device__ __forceinline__ void stage_bf16(char* stg, const f32x16 (&acc)[4][4], int lane) {
+// The sub-tile's values (MI blocks of 32 rows) as bf16 rows of the staging area.
+template <int MI>
+__device__ __forceinline__ void stage_bf16(char* stg, const f32x16 (&acc)[MI][4], int lane) {
     const int lrow = lane & 31, lcol = (lane >> 5) * 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -202,17 +205,16 @@ __device__ __forceinline__ void stage_bf16(char* stg, const f32x16 (&acc)[4][4],
                                pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
 }
 
-// Staged rows 0..127 (256 bytes each) to C + r * ldc for r < nrows; the 8-column chunk at
-// column c is written when c < ncols.
-// Non-temporal (nt) stores neither allocate in nor evict from the caches: for results that
-// nothing reads again soon (weight gradients).
-template <bool NT = false>
+// Staged rows 0 .. 32 MI - 1 (256 bytes each) to C + r * ldc for r < nrows; the 8-column
+// chunk at column c is written when c < ncols.  Non-temporal (NT) stores neither allocate in
+// nor evict from the caches: for results that nothing reads again soon (weight gradients).
+template <int MI, bool NT = false>
 __device__ __forceinline__ void store_staged(const char* stg, bf16_t* C, int64_t ldc, int nrows,
                                              int ncols, int lane) {
     const int rr = lane >> 4, ck = lane & 15;
     const bool colok = ck * 8 < ncols;
 #pragma unroll 8
-    for (int p = 0; p < 32; ++p) {
+    for (int p = 0; p < 8 * MI; ++p) {
         const int r = 4 * p + rr;
         const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * STG_RS + ck * 16);
         if (r < nrows && colok) {
@@ -222,24 +224,26 @@ __device__ __forceinline__ void store_staged(const char* stg, bf16_t* C, int64_t
     }
 }
 
-// The SwiGLU backward of a dgrad sub-tile (acc = dh at 128 rows x 128 channels): with the
+// The SwiGLU backward of a dgrad sub-tile (acc = dh at 32 MI rows x 128 channels): with the
 // saved g at GU + r * ldgu + c (u at + I) it writes dg at C + r * ldc + c and du at + I, for
-// rows r < nrows and 8-channel chunks with c < ncols.  In two halves of 64 rows: the g and u
-// rows of the half are loaded as whole-row 16-byte chunks into the staging area (g rows 0-63,
-// u rows 64-127), each lane turns its own g, u elements into dg, du in place (one lane owns
-// each element), and the rows go back out whole.
-__device__ __forceinline__ void dswiglu_staged(char* stg, const f32x16 (&acc)[4][4],
+// rows r < nrows and 8-channel chunks with c < ncols.  In parts of up to 64 rows (two blocks
+// of 32): the g and u rows of the part are loaded as whole-row 16-byte chunks into the staging
+// area (g rows 0-63, u rows 64-127), each lane turns its own g, u elements into dg, du in
+// place (one lane owns each element), and the rows go back out whole.
+template <int MI>
+__device__ __forceinline__ void dswiglu_staged(char* stg, const f32x16 (&acc)[MI][4],
                                                const bf16_t* GU, int64_t ldgu, bf16_t* C,
                                                int64_t ldc, int I, int nrows, int ncols,
                                                int lane) {
+    constexpr int PB = MI < 2 ? MI : 2;  // 32-row blocks per part
     const int lrow = lane & 31, lcol = (lane >> 5) * 4;
     const int rr = lane >> 4, ck = lane & 15;
     const bool colok = ck * 8 < ncols;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int rb = half * 64;
+    for (int half = 0; half < MI / PB; ++half) {
+        const int rb = half * PB * 32;
 #pragma unroll 4
-        for (int p = 0; p < 16; ++p) {
+        for (int p = 0; p < 8 * PB; ++p) {
             const int r = 4 * p + rr;
             u32x4 gv = {0u, 0u, 0u, 0u}, uv = {0u, 0u, 0u, 0u};
             if (rb + r < nrows && colok) {
@@ -252,8 +256,8 @@ __device__ __forceinline__ void dswiglu_staged(char* stg, const f32x16 (&acc)[4]
         }
         lds_wait();
 #pragma unroll
-        for (int ih = 0; ih < 2; ++ih) {
-            const int i = 2 * half + ih;
+        for (int ih = 0; ih < PB; ++ih) {
+            const int i = PB * half + ih;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -280,7 +284,7 @@ __device__ __forceinline__ void dswiglu_staged(char* stg, const f32x16 (&acc)[4]
         }
         lds_wait();
 #pragma unroll 4
-        for (int p = 0; p < 16; ++p) {
+        for (int p = 0; p < 8 * PB; ++p) {
             const int r = 4 * p + rr;
             const u32x4 dgv = *reinterpret_cast<const u32x4*>(stg + r * STG_RS + ck * 16);
             const u32x4 duv = *reinterpret_cast<const u32x4*>(stg + (64 + r) * STG_RS + ck * 16);
