@@ -270,14 +270,23 @@ def write_traffic(folder: str, workload: str, copy_mib: int) -> None:
         roles[role] = {"symbol": sym, "dispatches": n, "fetch_kib_raw": round(fk, 1),
                        "write_kib_raw": round(wk_, 1), "fetch_bytes": round(fb),
                        "write_bytes": round(wb), "hbm_bytes_per_launch": round(fb + wb)}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    workloads = {}
+    try:  # counts of other workloads taken on the same sources stay
+        with open(path) as fh:
+            prev = json.load(fh)
+        if prev.get("kernel_source_digest") == kernel_source_digest():
+            workloads = prev.get("workloads", {})
+    except (OSError, ValueError):
+        pass
+    workloads[workload] = roles
     out = {"kernel_source_digest": kernel_source_digest(),
            "counters": "rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE (separate runs), "
                        "mean KiB per dispatch",
            "copy_calibration": {"kernel": COPY_KERNEL_HINT, "mib": copy_mib,
                                 "fetch_scale": round(scale["FETCH_SIZE"], 4),
                                 "write_scale": round(scale["WRITE_SIZE"], 4)},
-           "workloads": {workload: roles}}
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+           "workloads": workloads}
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(f"| role | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes/launch (scaled) |")
