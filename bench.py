@@ -200,9 +200,10 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, role: str):
+def measured_traffic(workload: str, role: str, ring_depth=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
-    summary is missing or was taken on different kernel sources."""
+    summary is missing, was taken on different kernel sources, or in another launch
+    configuration (a ring layer's launches move different bytes at another ring depth)."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as fh:
@@ -210,6 +211,8 @@ def measured_traffic(workload: str, role: str):
     except (OSError, ValueError):
         return None
     if d.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    if d.get("ring_depth", {}).get(workload) != ring_depth:
         return None
     ent = d.get("workloads", {}).get(workload, {}).get(role)
     return None if ent is None else ent.get("hbm_bytes_per_launch")
@@ -244,7 +247,7 @@ def _counter_means(folder: str, counter: str) -> dict[str, tuple[int, float]]:
     return {k: (len(v), sum(v) / len(v)) for k, v in acc.items()}
 
 
-def write_traffic(folder: str, workload: str, copy_mib: int) -> None:
+def write_traffic(folder: str, workload: str, copy_mib: int, ring_depth=None) -> None:
     """profiles/hbm_traffic.json from four rocprofv3 --pmc runs: FETCH_SIZE and WRITE_SIZE (KiB
     per dispatch) of the layer's kernels, each scaled by the ratio of the known size of a plain
     copy to what the same counter reads for it."""
@@ -271,21 +274,24 @@ def write_traffic(folder: str, workload: str, copy_mib: int) -> None:
                        "write_kib_raw": round(wk_, 1), "fetch_bytes": round(fb),
                        "write_bytes": round(wb), "hbm_bytes_per_launch": round(fb + wb)}
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    workloads = {}
+    workloads, depths = {}, {}
     try:  # counts of other workloads taken on the same sources stay
         with open(path) as fh:
             prev = json.load(fh)
         if prev.get("kernel_source_digest") == kernel_source_digest():
             workloads = prev.get("workloads", {})
+            depths = prev.get("ring_depth", {})
     except (OSError, ValueError):
         pass
     workloads[workload] = roles
+    depths[workload] = ring_depth
     out = {"kernel_source_digest": kernel_source_digest(),
            "counters": "rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE (separate runs), "
                        "mean KiB per dispatch",
            "copy_calibration": {"kernel": COPY_KERNEL_HINT, "mib": copy_mib,
                                 "fetch_scale": round(scale["FETCH_SIZE"], 4),
                                 "write_scale": round(scale["WRITE_SIZE"], 4)},
+           "ring_depth": depths,
            "workloads": workloads}
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -403,7 +409,9 @@ def _cpu_model() -> str:
 def main():
     a = parse()
     if a.traffic_from:
-        write_traffic(a.traffic_from, a.workload, a.copy_mib or 1024)
+        import workloads as wk
+        write_traffic(a.traffic_from, a.workload, a.copy_mib or 1024,
+                      a.ring_depth if wk.WORKLOADS[a.workload].minibatch else None)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -546,7 +554,8 @@ def measure(wl, a, *, ring_depth, steps, warmup, fused, bias_gamma, headline, cp
     per_step = {r: sum(v) / steps for r, v in roles.items()}
     dominant = max(per_step, key=per_step.get)
     roof = roofline_of(wl, dominant, per_step[dominant], len(roles[dominant]) / steps,
-                       measured_traffic(wl.name, dominant))
+                       measured_traffic(wl.name, dominant,
+                                        ring_depth if wl.minibatch else None))
 
     flops_fwd = wl.fwd_flops()
     flops_step = flops_fwd * (3.0 if wl.backward else 1.0)

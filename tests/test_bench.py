@@ -79,3 +79,18 @@ def test_traffic_needs_matching_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic("w", "r") == 123
     (tmp_path / "mixture_experts_layer_39_amd" / "csrc" / "k.hip").write_text("b")
     assert bench.measured_traffic("w", "r") is None
+
+
+def test_traffic_needs_matching_ring_depth(tmp_path, monkeypatch):
+    """Counts taken through the ring at one depth are not reported for another depth."""
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "mixture_experts_layer_39_amd" / "csrc").mkdir(parents=True)
+    (tmp_path / "mixture_experts_layer_39_amd" / "csrc" / "k.hip").write_text("a")
+    import json
+    entry = {"ring_depth": {"w": 16}, "workloads": {"w": {"r": {"hbm_bytes_per_launch": 7}}}}
+    (tmp_path / "profiles" / "hbm_traffic.json").write_text(
+        json.dumps({"kernel_source_digest": bench.kernel_source_digest(), **entry}))
+    assert bench.measured_traffic("w", "r", 16) == 7
+    assert bench.measured_traffic("w", "r", 4) is None
+    assert bench.measured_traffic("w", "r") is None
