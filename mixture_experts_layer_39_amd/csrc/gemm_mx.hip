@@ -392,11 +392,15 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
 
     // ---------------------------------------------------------------- main loop
     // Slots as in the BF16 kernel: A of step s in slot 2s mod 5, B in slot 2s+1 mod 5; A(s+2)
-    // goes into the slot B(s-1) left, B(s+2) into the slot A(s) leaves at this step's
-    // barrier.  A step is two sub-steps of 16 scaled MFMAs (64 codes each).  Loads of step s:
-    //   sub-step 0: second half of B(s+1), first half of A(s+2), then the scales of step s+2
+    // goes into the slot B(s-1) left at the previous step's barrier, B(s+2) into the slot A(s)
+    // leaves at this step's barrier.  A step is two sub-steps of 16 scaled MFMAs (64 codes
+    // each).  Loads of step s:
+    //   sub-step 0: A(s+2), then the scales of step s+2
     //   barrier (A(s+1), B(s+1) and the scales of s+1 landed; every read of step s done)
-    //   sub-step 1: second half of A(s+2), first half of B(s+2)
+    //   sub-step 1: B(s+2)
+    // so every load has at least one whole sub-step to land before the barrier that waits for
+    // it (splitting B over two steps, as the four-sub-step BF16 step does, left the second
+    // half of B(s+1) only the rest of the sub-step it was issued in).
     // The scales of steps s, s+1, s+2 live in three register sets, so the loop is unrolled
     // over lcm(5, 3) = 15 steps; at its back edge the set in flight is waited for, so that no
     // register still being written crosses it.
@@ -450,8 +454,6 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
         vgpr_load8(sca[c], live ? rsa : rnull, lso, so);
         vgpr_load8(scb[c], live ? rsb : rnull, lso, so);
     };
-    rsrc_t pend_rb = rnull;  // B(s+1)'s second half is issued in step s
-    uint32_t pend_so = 0;
     auto kstep = [&](int u, int ks) __attribute__((always_inline)) {
         const int su = u % 5, c = u % 3;
         char* const cA = sm.st + ((2 * su) % 5) * XOPB;
@@ -459,50 +461,43 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
         char* const nA = sm.st + ((2 * su + 2) % 5) * XOPB;
         char* const nB = sm.st + ((2 * su + 3) % 5) * XOPB;
         const uint32_t base32 = lds_addr(sm.st);
-        const uint32_t lB1 = base32 + ((2 * su + 3) % 5) * XOPB;  // B(ks+1)
         const uint32_t lA = base32 + ((2 * su + 4) % 5) * XOPB;   // A(ks+2): slot of B(ks-1)
         const uint32_t lB = base32 + ((2 * su) % 5) * XOPB;       // B(ks+2): slot of A(ks)
-        const rsrc_t rb1 = pend_rb;
-        const uint32_t so1 = pend_so;
         rsrc_t ra_, rb_;
         uint32_t so;
         codes_src(ks + 2, ra_, rb_, so);
         __builtin_amdgcn_sched_barrier(0);
-        // sub-step 0: fragment reads of sub-step 1; 4 + 4 code loads, then the scales of ks+2
+        // sub-step 0: fragment reads of sub-step 1; the 8 code loads of A(ks+2), then the
+        // scales of ks+2
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
             mfma_one(0, 0, c, n);
             if ((n & 1) == 0) read_ab(cA, cB, 1, 1, n / 2);
-            else if (n < 8) issue_load<64>(ob, lB1, wid, 4 + n / 2, rb1, so1);
-            else issue_load<64>(oa, lA, wid, (n - 8) / 2, ra_, so);
+            else issue_load<64>(oa, lA, wid, n / 2, ra_, so);
             if (n == 15) load_scales(ks + 2, (u + 2) % 3);
             __builtin_amdgcn_sched_barrier(0);
         }
-        wait_vm_lgkm0<XLPW / 2 + 2>();  // all but A(ks+2)'s first half and its scales
+        wait_vm_lgkm0<XLPW + 2>();  // all but A(ks+2) and its scales
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         settle(sca[(u + 1) % 3]);
         settle(scb[(u + 1) % 3]);
         const bool more = ks + 1 < nk;
-        // sub-step 1: fragment reads of the next step's sub-step 0; 4 + 4 code loads
+        // sub-step 1: fragment reads of the next step's sub-step 0; the 8 code loads of B(ks+2)
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
             mfma_one(1, 1, c, n);
             if ((n & 1) == 0) {
                 if (more) read_ab(nA, nB, 0, 0, n / 2);
-            } else if (n < 8) {
-                issue_load<64>(oa, lA, wid, 4 + n / 2, ra_, so);
             } else {
-                issue_load<64>(ob, lB, wid, (n - 8) / 2, rb_, so);
+                issue_load<64>(ob, lB, wid, n / 2, rb_, so);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        pend_rb = rb_;
-        pend_so = so;
     };
     if (nk > 0) {
         const uint32_t base32 = lds_addr(sm.st);
-        // scales of steps 0 and 1; A(0), B(0), A(1) and the first half of B(1)
+        // scales of steps 0 and 1; A(0), B(0), A(1), B(1)
         load_scales(0, 0);
         load_scales(1, 1);
 #pragma unroll
@@ -513,13 +508,10 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
 #pragma unroll
             for (int i = 0; i < XLPW; ++i) {
                 issue_load<64>(oa, base32 + (2 * p) * XOPB, wid, i, ra_, so);
-                if (p == 0 || i < XLPW / 2)
-                    issue_load<64>(ob, base32 + (2 * p + 1) * XOPB, wid, i, rb_, so);
+                issue_load<64>(ob, base32 + (2 * p + 1) * XOPB, wid, i, rb_, so);
             }
-            pend_rb = rb_;
-            pend_so = so;
         }
-        wait_vm_lgkm0<XLPW + XLPW / 2>();  // the scales of steps 0, 1 and step 0 landed
+        wait_vm_lgkm0<2 * XLPW>();  // the scales of steps 0, 1 and step 0 landed
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         settle(sca[0]);

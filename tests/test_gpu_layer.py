@@ -13,6 +13,7 @@ import torch
 
 import oracle as orc
 import workloads as wk
+from mixture_experts_layer_39_amd.layer import LayerCfg, MoELayer
 from gpu_harness import (TOL_BF16, TOL_MX, assert_close, bf, build_layer, digest, host,
                          layer_outputs, oracle_params)
 
@@ -72,6 +73,33 @@ def test_layer_reduced_full_oracle(name):
         # experts that received no rows have exactly zero weight gradients
         for e in np.nonzero(r["counts"] == 0)[0]:
             assert not torch.any(layer.dw1[e] != 0) and not torch.any(layer.dw2[e] != 0)
+
+
+def test_layer_weight_gradient_tails():
+    """Weight gradients of experts with few rows: odd tile counts (45 tiles of dW1, 30 of dW2),
+    ragged M and N tails, an expert with no rows between experts with rows, and experts of one
+    K step and of several -- against the complete oracle."""
+    wl = wk.WORKLOADS["mid_t2048"].scaled(T=160, H=768, E=5, k=2, I=320, S=1, Is=192)
+    inp = wk.make_inputs(wl, device="cuda")
+    inp["logits"][:, 2] = -30.0   # expert 2 is never among the top 2
+    inp["logits"][:, 0] += 2.0    # expert 0 takes most tokens (several K steps)
+    layer = MoELayer(LayerCfg.from_workload(wl), inp, "cuda", backward=True)
+    print(f"weight-gradient tails case T={wl.T} H={wl.H} E={wl.E} I={wl.I}", flush=True)
+    layer.forward()
+    layer.backward()
+    torch.cuda.synchronize()
+    p = oracle_params(wl, inp)
+    r = orc.layer_forward(p)
+    counts = r["counts"]
+    assert counts[2] == 0 and counts.max() > 128 and counts[counts > 0].min() <= 64, counts
+    assert np.array_equal(host(layer.counts), counts)
+    g = orc.layer_backward(p, r, wk.bf16_bits(inp["dout"]))
+    assert_close(bf(layer.dw1), g["dw1"], TOL_BF16, "dw1")
+    assert_close(bf(layer.dw2), g["dw2"], TOL_BF16, "dw2")
+    assert_close(bf(layer.dx), g["dx"], TOL_BF16, "dx")
+    assert_close(bf(layer.dws1), g["dws1"], TOL_BF16, "dws1")
+    assert_close(bf(layer.dws2), g["dws2"], TOL_BF16, "dws2")
+    assert not torch.any(layer.dw1[2] != 0) and not torch.any(layer.dw2[2] != 0)
 
 
 def _sampled_forward_backward(wl, inp, layer, p, L, idx, w, lidx, offsets, pos, src, ts, exps,
