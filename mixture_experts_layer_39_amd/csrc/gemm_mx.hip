@@ -482,13 +482,15 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
         __builtin_amdgcn_sched_barrier(0);
         settle(sca[(u + 1) % 3]);
         settle(scb[(u + 1) % 3]);
-        const bool more = ks + 1 < nk;
-        // sub-step 1: fragment reads of the next step's sub-step 0; the 8 code loads of B(ks+2)
+        // sub-step 1: fragment reads of the next step's sub-step 0; the 8 code loads of B(ks+2).
+        // The reads run in the last step too (of slots inside LDS, values unused): a read
+        // under a condition makes the compiler carry each fragment's old value through
+        // register copies into MFMA source registers.
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
             mfma_one(1, 1, c, n);
             if ((n & 1) == 0) {
-                if (more) read_ab(nA, nB, 0, 0, n / 2);
+                read_ab(nA, nB, 0, 0, n / 2);
             } else {
                 issue_load<64>(ob, lB, wid, n / 2, rb_, so);
             }
