@@ -67,6 +67,8 @@ struct GemmArgs {
     // expert's rows of every pass in pass order.  P = 1: one pass, offsets [E+1].
     int P;
     int pass_rows;
+    int bound;  // blocks a pair launch gives this product: its tile count, or for ragged rows
+                // the host's upper bound of it (the blocks past the device count exit)
 };
 
 // ---------------------------------------------------------------- LDS tiles
@@ -660,29 +662,35 @@ MOE_GEMM_KERNEL(gemm2_down, true, true, EPI_STORE, false)        // y = h W2^T
 
 // The backward's two pairs of independent products run as one launch each, the dgrad tiles
 // first and the wgrad tiles after them, so that the second product fills the last,
-// partly empty round of the first (256 CUs, one tile each at a time).
+// partly empty round of the first (256 CUs, one tile each at a time).  The dgrad product
+// gets the first gd.bound blocks (for ragged rows the host's upper bound of its tiles: the
+// blocks past the device count exit at once), so that a weight-gradient block knows its tile
+// without the scan of the experts' row counts, which costs a block a few microseconds and
+// weighs on weight-gradient tiles of one or two K steps.
 //   bwd_down:     dh = dy W2 -> dg|du (SwiGLU backward)   and   dW2 = dy^T h
 //   bwd_gate_up:  dXp = dGU W1                           and   dW1 = dGU^T Xp
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_down(GemmArgs gd, GemmArgs gw) {
     __shared__ GemmSmem sm;
-    const int td = tile_total<EPI_DSWIGLU, false>(gd);
     const int b = blockIdx.x;
-    if (b < td)
-        run_tile<BK_DGRAD, true, false, EPI_DSWIGLU, false>(gd, sm, tile_at<EPI_DSWIGLU, false>(gd, b));
-    else if (b - td < gw.total)
-        run_tile<BK_WGRAD, false, false, EPI_STORE, true>(gw, sm, tile_at<EPI_STORE, true>(gw, b - td));
+    if (b < gd.bound) {
+        if (b < tile_total<EPI_DSWIGLU, false>(gd))
+            run_tile<BK_DGRAD, true, false, EPI_DSWIGLU, false>(gd, sm, tile_at<EPI_DSWIGLU, false>(gd, b));
+    } else if (b - gd.bound < gw.total) {
+        run_tile<BK_WGRAD, false, false, EPI_STORE, true>(gw, sm, tile_at<EPI_STORE, true>(gw, b - gd.bound));
+    }
 }
 
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_gate_up(GemmArgs gd, GemmArgs gw) {
     __shared__ GemmSmem sm;
-    const int td = tile_total<EPI_STORE, false>(gd);
     const int b = blockIdx.x;
-    if (b < td)
-        run_tile<BK_DGRAD, true, false, EPI_STORE, false>(gd, sm, tile_at<EPI_STORE, false>(gd, b));
-    else if (b - td < gw.total)
-        run_tile<BK_WGRAD, false, false, EPI_STORE, true>(gw, sm, tile_at<EPI_STORE, true>(gw, b - td));
+    if (b < gd.bound) {
+        if (b < tile_total<EPI_STORE, false>(gd))
+            run_tile<BK_DGRAD, true, false, EPI_STORE, false>(gd, sm, tile_at<EPI_STORE, false>(gd, b));
+    } else if (b - gd.bound < gw.total) {
+        run_tile<BK_WGRAD, false, false, EPI_STORE, true>(gw, sm, tile_at<EPI_STORE, true>(gw, b - gd.bound));
+    }
 }
 
 // Upper bound on the tile count of a ragged-M product (host side, no device data).
@@ -707,9 +715,11 @@ static int launch(void (*kern)(GemmArgs), const char* name, const GemmArgs& g, i
     return MOE_OK;
 }
 
-static int launch_pair(void (*kern)(GemmArgs, GemmArgs), const char* name, const GemmArgs& gd,
+static int launch_pair(void (*kern)(GemmArgs, GemmArgs), const char* name, const GemmArgs& gd_,
                        const GemmArgs& gw, hipStream_t st) {
-    const int grid = grid_of(gd, cdiv(gd.N, BN), false) + gw.total;
+    GemmArgs gd = gd_;
+    gd.bound = grid_of(gd, cdiv(gd.N, BN), false);
+    const int grid = gd.bound + gw.total;
     if (grid <= 0) return MOE_OK;
     MOE_TRACED(name, st, kern<<<grid, NTH, 0, st>>>(gd, gw));
     MOE_LAUNCH_CHECK();

@@ -54,6 +54,8 @@ struct MxArgs {
     int total;           // tile count when static (shared mode, weight gradients)
     int M;               // weight gradients: rows of A (static); K is then the row stride of
                          // the token-axis operands and each expert takes its own code columns
+    int bound;           // blocks a pair launch gives this product (dgrad: the host's upper
+                         // bound of its tiles; the blocks past the device count exit)
 };
 
 struct alignas(1024) MxSmem {
@@ -695,11 +697,15 @@ MOE_MX_KERNEL(mx_bwd_down, XEPI_DSWIGLU)
 // token columns) fill the dgrad's last, partial round of 256 CUs.
 template <int EPI>
 __device__ __forceinline__ void mx_pair(const MxArgs& gd, const MxArgs& gw, MxSmem& sm) {
-    const int td = uni(mx_ragged_scan(gd.offsets, gd.E, gd.R, mx_n_tiles<EPI>(gd.N, gd.I), -1,
-                                      nullptr, nullptr));
     const int b = blockIdx.x;
-    if (b < td) mx_tile<EPI>(gd, sm, b);
-    else if (b - td < gw.total) mx_tile<XEPI_STORE_BF16, true>(gw, sm, b - td);
+    if (b < gd.bound) {
+        // the dgrad tiles: the device count of the experts' tiles (blocks past it exit)
+        const int td = uni(mx_ragged_scan(gd.offsets, gd.E, gd.R, mx_n_tiles<EPI>(gd.N, gd.I), -1,
+                                          nullptr, nullptr));
+        if (b < td) mx_tile<EPI>(gd, sm, b);
+    } else if (b - gd.bound < gw.total) {
+        mx_tile<XEPI_STORE_BF16, true>(gw, sm, b - gd.bound);
+    }
 }
 __global__ __launch_bounds__(XNTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mx_bwd_down_pair(MxArgs gd, MxArgs gw) {
@@ -898,8 +904,10 @@ static int mx_wgrad_prepare(const bf16_t* A, int M, const bf16_t* B, const uint8
 }
 
 template <int EPI>
-static int mx_launch_pair(const MxArgs& gd, const MxArgs& gw, const char* name, hipStream_t st) {
-    const int grid = mx_mtiles_bound(gd.R, gd.E, false) * mx_n_tiles<EPI>(gd.N, gd.I) + gw.total;
+static int mx_launch_pair(const MxArgs& gd_, const MxArgs& gw, const char* name, hipStream_t st) {
+    MxArgs gd = gd_;
+    gd.bound = mx_mtiles_bound(gd.R, gd.E, false) * mx_n_tiles<EPI>(gd.N, gd.I);
+    const int grid = gd.bound + gw.total;
     if (grid <= 0) return MOE_OK;
     if (EPI == XEPI_DSWIGLU)
         MOE_TRACED(name, st, mx_bwd_down_pair<<<grid, XNTH, 0, st>>>(gd, gw));
