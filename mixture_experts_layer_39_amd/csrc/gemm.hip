@@ -478,7 +478,89 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         pend_rb = rb_;
         pend_sb = sb;
     };
-    if (nk > 0 && SLOTS5) {
+    // 64-row tiles (an expert's last tile of at most 64 rows) stream their weight panel from
+    // HBM with few MFMAs per byte, so the loads decide their time.  They use a deeper ring:
+    // four 32 KB slots for B and the fifth split into four 8 KB parts for A, step s in slot
+    // s mod 4 of each; step s issues the loads of step s+3 (into the slots step s-1 left at its
+    // barrier) in its first three sub-steps, so three steps of operands are in flight where the
+    // five-slot ring keeps about one and a half.
+    auto kstep4 = [&](int u, int ks) __attribute__((always_inline)) {
+        char* const cA = sm.st + 4 * OPB + u * (OPB / 4);
+        char* const cB = sm.st + u * OPB;
+        char* const nA = sm.st + 4 * OPB + ((u + 1) & 3) * (OPB / 4);
+        char* const nB = sm.st + ((u + 1) & 3) * OPB;
+        const uint32_t base32 = lds_addr(sm.st);
+        const uint32_t lA = base32 + 4 * OPB + ((u + 3) & 3) * (OPB / 4);  // A(ks+3): A(ks-1)'s part
+        const uint32_t lB = base32 + ((u + 3) & 3) * OPB;                  // B(ks+3): B(ks-1)'s slot
+        rsrc_t ra_, rb_;
+        uint32_t sa, sb;
+        load_src(ks + 3, ra_, rb_, sa, sb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < KK - 1; ++kk) {
+#pragma unroll
+            for (int n = 0; n < NM; ++n) {
+                mfma_one(kk & 1, n);
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+                    if (rslot(r) == n) read_ab(cA, cB, kk + 1, (kk + 1) & 1, r);
+                if (kk < 2) {  // B(ks+3): half in sub-step 0, half in sub-step 1
+#pragma unroll
+                    for (int q = 0; q < LPW / 2; ++q)
+                        if (lslot(q, LPW / 2) == n)
+                            issue_load<BK>(ob, lB, wid, (LPW / 2) * kk + q, rb_, sb);
+                } else {       // A(ks+3) in sub-step 2
+#pragma unroll
+                    for (int q = 0; q < LPA; ++q)
+                        if (lslot(q, LPA) == n) issue_load<BK, WBA>(oa, lA, wid, q, ra_, sa);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        wait_vm_lgkm0<2 * (LPA + LPW)>();  // step ks+1 landed; ks+2 and ks+3 may be in flight
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int fl = (KK - 1) & 1;
+        // last sub-step, with the reads of the next step's first fragments (they run after the
+        // last step too, of slots inside LDS with values unused: a read under a condition
+        // would make the compiler copy the fragments)
+#pragma unroll
+        for (int n = 0; n < NM; ++n) {
+            mfma_one(fl, n);
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                if (rslot(r) == n) read_ab(nA, nB, 0, 0, r);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if (TM == 64 && nk > 0 && SLOTS5) {
+        static_assert(TM != 64 || (KK == 4 && 4 * OPB + 4 * (OPB / 4) <= (int)sizeof(GemmSmem) &&
+                                   WBA * 4 == OPB / 4), "deep ring layout");
+        const uint32_t base32 = lds_addr(sm.st);
+        // steps 0, 1, 2
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+            rsrc_t ra_, rb_;
+            uint32_t sa, sb;
+            load_src(p, ra_, rb_, sa, sb);
+#pragma unroll
+            for (int i = 0; i < LPW; ++i) {
+                if (i < LPA) issue_load<BK, WBA>(oa, base32 + 4 * OPB + p * (OPB / 4), wid, i, ra_, sa);
+                issue_load<BK>(ob, base32 + p * OPB, wid, i, rb_, sb);
+            }
+        }
+        wait_vm_lgkm0<2 * (LPA + LPW)>();  // step 0 landed
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read_ab(sm.st + 4 * OPB, sm.st, 0, 0, r);
+        for (int ks = 0; ks < nk; ks += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (ks + u < nk) kstep4(u, ks + u);
+        }
+        wait_vm_lgkm0<0>();  // no load may still be writing LDS when the block ends
+    } else if (nk > 0 && SLOTS5) {
         static_assert(!SLOTS5 || (KK == 4 && LPW == 8 && 5 * OPB <= (int)sizeof(GemmSmem)),
                       "five-slot ring layout");
         const uint32_t base32 = lds_addr(sm.st);
