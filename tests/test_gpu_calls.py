@@ -209,6 +209,9 @@ def _ffn_case(E, R, H, I, offsets, seed, shared=False):
     (5, 512, 320, [0, 300, 300, 813, 999, 1000]),
     (3, 1024, 384, [0, 256, 512, 1025]),
     (1, 256, 512, [0, 7]),
+    # K loops of one and two steps with 64-row tiles only (the deeper ring's empty steps)
+    (3, 64, 64, [0, 10, 10, 70]),
+    (2, 128, 128, [0, 33, 97]),
 ])
 def test_expert_ffn_bf16_parity(shape):
     E, H, I, off = shape
@@ -289,7 +292,8 @@ def _ffn_forms(E, R, H, I, off, seed):
     (3, 1024, 384, [0, 256, 512, 1025]),
     (1, 256, 512, [0, 7]),
     (4, 7168, 2048, [0, 1322, 9292, 13050, 16384]),  # the EP-64 share's realised loads
-], ids=["ragged", "tails", "one_expert_7_rows", "ep64_share"])
+    (3, 64, 64, [0, 10, 10, 70]),                     # one-step K loops, 64-row tiles
+], ids=["ragged", "tails", "one_expert_7_rows", "ep64_share", "one_step_k"])
 def test_expert_ffn_one_launch_bit_identical(shape):
     """One launch of both products (tile queue with per-row-block dependencies) against the
     two launches: every output bit for bit, the error word zero."""
