@@ -102,6 +102,27 @@ def test_layer_weight_gradient_tails():
     assert not torch.any(layer.dw1[2] != 0) and not torch.any(layer.dw2[2] != 0)
 
 
+def test_layer_tiny_dimensions_full_oracle():
+    """H = I = 64 (the smallest the boundary takes): every product a K loop of one or two
+    steps, tiles far wider than the operands, weight gradients of 64 x 128 and 128 x 64 --
+    forward and backward against the complete oracle."""
+    wl = wk.WORKLOADS["mid_t2048"].scaled(T=48, H=64, E=4, k=2, I=64, S=1, Is=64)
+    inp = wk.make_inputs(wl, device="cuda")
+    layer = MoELayer(LayerCfg.from_workload(wl), inp, "cuda", backward=True)
+    print(f"tiny dimensions case T={wl.T} H={wl.H} E={wl.E} I={wl.I}", flush=True)
+    layer.forward()
+    layer.backward()
+    torch.cuda.synchronize()
+    p = oracle_params(wl, inp)
+    r = orc.layer_forward(p)
+    assert np.array_equal(host(layer.counts), r["counts"])
+    assert_close(bf(layer.out), r["out"], TOL_BF16, "out")
+    g = orc.layer_backward(p, r, wk.bf16_bits(inp["dout"]))
+    for name in ("dx", "dw1", "dw2", "dws1", "dws2"):
+        assert_close(bf(getattr(layer, name)), g[name], TOL_BF16, name)
+    assert_close(host(layer.dlogits), g["dlogits"], TOL_BF16, "dlogits")
+
+
 def _sampled_forward_backward(wl, inp, layer, p, L, idx, w, lidx, offsets, pos, src, ts, exps,
                               chans):
     k = lidx.shape[1]
