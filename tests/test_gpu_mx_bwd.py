@@ -81,8 +81,11 @@ def test_mx_forward_saves():
 
 
 @pytest.mark.parametrize("mode", [1, 2])
-@pytest.mark.parametrize("kw", [dict(), dict(T=64, R_share=512, I=256)])
+@pytest.mark.parametrize("kw", [dict(), dict(T=64, R_share=512, I=256),
+                                dict(T=48, R_share=384, H=128, I=128)])
 def test_mx_backward_against_oracle(kw, mode):
+    """The last case has K loops of one and two steps (K = H = 128, 2I = 256, and one token
+    step per expert in the weight gradients) and down-projection tiles twice as wide as H."""
     wl = wk.WORKLOADS["dsv3_ep64_mxfp8"].scaled(**{**REDUCED, **kw})
     inp = wk.make_inputs(wl, device=DEV)
     cfg = LayerCfg.from_workload(wl)
@@ -95,6 +98,7 @@ def test_mx_backward_against_oracle(kw, mode):
     p = oracle_params(wl, inp)
     p["mx_wgrad"] = mode == 2
     r = orc.layer_forward(p)
+    assert_close(bf(layer.out), r["out"], TOL_MX, "out")
     g = orc.layer_backward(p, r, wk.bf16_bits(inp["dout"]))
     assert_close(host(layer.dw_route), g["dw_route"], TOL_BF16, "dw_route")
     assert_close(host(layer.dlogits), g["dlogits"], TOL_BF16, "dlogits")
