@@ -17,7 +17,7 @@
 // rows per instruction.  A pre-pass therefore lays the scales of every 128-row operand panel
 // out per K step in the order the 64 lanes consume them (8 bytes per lane, one 512-byte run
 // per panel and step), and the K loop fetches them with one 8-byte load per lane and operand
-// per step, two steps ahead.
+// per step, two steps ahead.  GEMM1's epilogue writes the panels of h for GEMM2 directly.
 #include "mx_dev.h"
 #include "pipe.h"
 
@@ -56,6 +56,8 @@ struct MxArgs {
                          // the token-axis operands and each expert takes its own code columns
     int bound;           // blocks a pair launch gives this product (dgrad: the host's upper
                          // bound of its tiles; the blocks past the device count exit)
+    uint8_t* Ph;         // SwiGLU: the down projection's panel scales of h [A panels][I/128]
+                         // [512], written by the epilogue, or null
 };
 
 struct alignas(1024) MxSmem {
@@ -217,7 +219,8 @@ struct PanelJobs {
 
 // One launch for the panels known before GEMM1: x blocks [0, na) A panels of xp, then E NT1
 // B panels of W1, then E NT2 B panels of W2; y blocks: 64-column chunks of each operand's
-// scales (blocks past an operand's chunks exit).
+// scales (blocks past an operand's chunks exit).  GEMM2's A panels (h's scales) come from
+// GEMM1's epilogue.
 __global__ __launch_bounds__(256) void mx_panel_scales_pre(PanelJobs j) {
     __shared__ uint8_t stg[256][PS_COLS + 4];
     __shared__ int srow[256];
@@ -236,17 +239,6 @@ __global__ __launch_bounds__(256) void mx_panel_scales_pre(PanelJobs j) {
         panel_b<XEPI_STORE_BF16>(bx - j.na - nb1, j.w2s, j.H, j.H, j.I, KBi, j.I / XBK, j.pb2,
                                  stg, srow);
     }
-}
-
-// The A panels of GEMM2 (h scales, known after the MX quantisation of h).
-__global__ __launch_bounds__(256) void mx_panel_scales_h(const uint8_t* __restrict__ sc,
-                                                         const int32_t* __restrict__ offsets,
-                                                         int E, int R, int64_t a_es, int KB,
-                                                         int nsteps, int total_static,
-                                                         uint8_t* __restrict__ out) {
-    __shared__ uint8_t stg[256][PS_COLS + 4];
-    __shared__ int srow[256];
-    panel_a(blockIdx.x, sc, offsets, E, R, a_es, KB, nsteps, total_static, out, stg, srow);
 }
 
 // The panels of one product of the backward: x blocks [0, na) the A panels -- ragged rows
@@ -355,6 +347,8 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
         tn = rr / gsz;
     }
     const int m0 = tm * XBM, n0 = tn * XBN, ch0 = tn * 128;
+    // the row block's index among all 256-row blocks of the call (its panels)
+    const int mblock = mt_first + tm;
 
     // ---------------------------------------------------------------- operands
     // codes: the K-major load map of a 64-wide BF16 step (128-byte rows; ld in 2-byte units)
@@ -639,6 +633,14 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
                         }
                     if (lane < 32 && row < Mrows)
                         g.Cs[(rb + row) * (g.ldc / 32) + (ch_w + b * 32) / 32] = (uint8_t)sc;
+                    // the down projection's panel scales of h: its K step tn holds these 128
+                    // channels; the row is row 32 i + lrow of panel wm and this is its scale
+                    // column 2 wn + b of the step, so byte 8 (32 b + lrow) + 2 i + wn of the
+                    // step's run.  Rows past the expert's get the scale of zeros (code 0), as
+                    // the panels built from stored scales do.
+                    if (g.Ph && lane < 32)
+                        g.Ph[((int64_t)(2 * mblock + wm) * (g.I / XBK) + tn) * SPAN +
+                             8 * (32 * b + lrow) + 2 * i + wn] = (uint8_t)sc;
                 }
             }
             lds_wait();
@@ -677,21 +679,6 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, MxSmem& sm, const int l
     }
 }
 
-#define MOE_MX_KERNEL(NAME, EPI)                                                          \
-    __global__ __launch_bounds__(XNTH) __attribute__((amdgpu_waves_per_eu(1, 1))) void    \
-    NAME(MxArgs g) {                                                                      \
-        __shared__ MxSmem sm;                                                             \
-        const int total = g.offsets ? uni(mx_ragged_scan(g.offsets, g.E, g.R,              \
-                                                         mx_n_tiles<EPI>(g.N, g.I), -1,   \
-                                                         nullptr, nullptr))               \
-                                    : g.total;                                            \
-        if ((int)blockIdx.x < total) mx_tile<EPI>(g, sm, blockIdx.x);                     \
-    }
-MOE_MX_KERNEL(mx_gemm1_swiglu, XEPI_SWIGLU_MX)
-MOE_MX_KERNEL(mx_gemm2_down, XEPI_STORE_BF16)
-MOE_MX_KERNEL(mx_bwd_down, XEPI_DSWIGLU)
-#undef MOE_MX_KERNEL
-
 // A dgrad product and an independent weight-gradient product in one launch, the dgrad tiles
 // first: the weight-gradient tiles (E static grids of M x N tiles, each over its expert's
 // token columns) fill the dgrad's last, partial round of 256 CUs.
@@ -718,25 +705,27 @@ void mx_bwd_gate_up_pair(MxArgs gd, MxArgs gw) {
     mx_pair<XEPI_STORE_BF16>(gd, gw, sm);
 }
 
+// ---------------------------------------------------------------- the forward products
+// One block per tile (blocks past the device count of the experts' tiles exit).  GEMM1 writes
+// h's codes and, through Ph, GEMM2's panel scales of h, so GEMM2 follows it directly.
+#define MOE_MX_KERNEL(NAME, EPI)                                                          \
+    __global__ __launch_bounds__(XNTH) __attribute__((amdgpu_waves_per_eu(1, 1))) void    \
+    NAME(MxArgs g) {                                                                      \
+        __shared__ MxSmem sm;                                                             \
+        const int total = g.offsets ? uni(mx_ragged_scan(g.offsets, g.E, g.R,              \
+                                                         mx_n_tiles<EPI>(g.N, g.I), -1,   \
+                                                         nullptr, nullptr))               \
+                                    : g.total;                                            \
+        if ((int)blockIdx.x < total) mx_tile<EPI>(g, sm, blockIdx.x);                     \
+    }
+MOE_MX_KERNEL(mx_gemm1_swiglu, XEPI_SWIGLU_MX)
+MOE_MX_KERNEL(mx_gemm2_down, XEPI_STORE_BF16)
+#undef MOE_MX_KERNEL
+
 // Upper bound on the 256-row M tiles of an operand (host side, no device data).
 static int mx_mtiles_bound(int R, int E, bool shared) {
     if (shared) return E * cdiv(R, XBM);
     return (int)(((int64_t)R + (int64_t)E * (XBM - 1)) / XBM);
-}
-
-template <int EPI>
-static int mx_launch(const MxArgs& g, hipStream_t st, const char* name = nullptr) {
-    const int NT = mx_n_tiles<EPI>(g.N, g.I);
-    const int grid = g.offsets ? mx_mtiles_bound(g.R, g.E, false) * NT : g.total;
-    if (grid <= 0) return MOE_OK;
-    if (EPI == XEPI_SWIGLU_MX)
-        MOE_TRACED("mx_gemm1_swiglu", st, mx_gemm1_swiglu<<<grid, XNTH, 0, st>>>(g));
-    else if (EPI == XEPI_DSWIGLU)
-        MOE_TRACED("mx_bwd_down", st, mx_bwd_down<<<grid, XNTH, 0, st>>>(g));
-    else
-        MOE_TRACED(name ? name : "mx_gemm2_down", st, mx_gemm2_down<<<grid, XNTH, 0, st>>>(g));
-    MOE_LAUNCH_CHECK();
-    return MOE_OK;
 }
 
 static int mx_panels_pre(const PanelJobs& j, hipStream_t st) {
@@ -744,19 +733,6 @@ static int mx_panels_pre(const PanelJobs& j, hipStream_t st) {
                    j.E * mx_n_tiles<XEPI_STORE_BF16>(j.H, j.I);
     const dim3 grid(nb, cdiv(max(j.H, j.I) / 32, PS_COLS));
     MOE_TRACED("mx_panel_scales", st, mx_panel_scales_pre<<<grid, 256, 0, st>>>(j));
-    MOE_LAUNCH_CHECK();
-    return MOE_OK;
-}
-
-static int mx_panels_h(const uint8_t* sc, const int32_t* offsets, int E, int R, int64_t a_es,
-                       int K, uint8_t* out, hipStream_t st) {
-    const bool shared = offsets == nullptr;
-    const int grid = mx_mtiles_bound(R, E, shared);
-    if (grid <= 0) return MOE_OK;
-    const dim3 g2(grid, cdiv(K / 32, PS_COLS));
-    MOE_TRACED("mx_panel_scales", st,
-               mx_panel_scales_h<<<g2, 256, 0, st>>>(sc, offsets, E, R, a_es, K / 32, K / XBK,
-                                                     shared ? grid : 0, out));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -795,12 +771,14 @@ int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int
     // K steps of 128 codes: H and I multiples of 128
     if (H % XBK || I % XBK) return MOE_EINVAL;
     const bool shared = offsets == nullptr;
+    const int mtiles = mx_mtiles_bound(R, E, shared);
+    const int nt1 = mx_n_tiles<XEPI_SWIGLU_MX>(2 * I, I), nt2 = mx_n_tiles<XEPI_STORE_BF16>(H, I);
+    if (mtiles <= 0) return MOE_OK;
     uint8_t* pa1 = panels;
     uint8_t* pa2 = pa1 + mx_panel_a_bytes(E, R, H, shared);
     uint8_t* pb1 = pa2 + mx_panel_a_bytes(E, R, I, shared);
     uint8_t* pb2 = pb1 + mx_panel_b_bytes<XEPI_SWIGLU_MX>(E, 2 * I, I, H);
-    PanelJobs pj{xs, offsets, E, R, H, I, mx_mtiles_bound(R, E, shared),
-                 shared ? mx_mtiles_bound(R, E, true) : 0, w1s, w2s, pa1, pb1, pb2};
+    PanelJobs pj{xs, offsets, E, R, H, I, mtiles, shared ? mtiles : 0, w1s, w2s, pa1, pb1, pb2};
     int rc = mx_panels_pre(pj, st);
     if (rc) return rc;
     MxArgs g{};
@@ -809,18 +787,19 @@ int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int
     g.Cq = hq; g.Cs = hs; g.Ch = h_save; g.c_es = shared ? R : 0; g.ldc = I;
     g.C2 = gu_save; g.ldc2 = 2 * I;
     g.offsets = offsets; g.E = E; g.R = R; g.N = 2 * I; g.K = H; g.I = I;
-    g.total = shared ? E * cdiv(R, XBM) * cdiv(I, 128) : 0;
-    rc = mx_launch<XEPI_SWIGLU_MX>(g, st);
-    if (rc) return rc;
-    rc = mx_panels_h(hs, offsets, E, R, shared ? R : 0, I, pa2, st);
-    if (rc) return rc;
+    g.total = shared ? mtiles * nt1 : 0;
+    g.Ph = pa2;
+    MOE_TRACED("mx_gemm1_swiglu", st, mx_gemm1_swiglu<<<mtiles * nt1, XNTH, 0, st>>>(g));
+    MOE_LAUNCH_CHECK();
     MxArgs g2{};
     g2.A = hq; g2.At = pa2; g2.a_es = shared ? R : 0;
     g2.B = w2q; g2.Bt = pb2; g2.b_rows = H;
     g2.C = y; g2.c_es = shared ? R : 0; g2.ldc = H;
     g2.offsets = offsets; g2.E = E; g2.R = R; g2.N = H; g2.K = I; g2.I = I;
-    g2.total = shared ? E * cdiv(R, XBM) * cdiv(H, XBN) : 0;
-    return mx_launch<XEPI_STORE_BF16>(g2, st);
+    g2.total = shared ? mtiles * nt2 : 0;
+    MOE_TRACED("mx_gemm2_down", st, mx_gemm2_down<<<mtiles * nt2, XNTH, 0, st>>>(g2));
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
 }
 
 // ---------------------------------------------------------------- backward, MXFP8 dgrad

@@ -242,27 +242,52 @@ def test_expert_ffn_shared_mode():
     assert_close(bf(y), ry, TOL_BF16, "y_shared")
 
 
-def test_expert_ffn_mxfp8_parity():
-    E, H, I = 3, 512, 384
-    off = [0, 200, 201, 700]
-    R = off[-1]
+@pytest.mark.parametrize("shape", [
+    # E, H, I, offsets (None: shared experts, every expert on all R rows)
+    (3, 512, 384, [0, 200, 201, 700]),
+    (4, 256, 256, [0, 0, 300, 813, 1030]),  # an empty expert; several 256-row blocks
+    (1, 128, 128, [0, 7]),                  # one-step K loops; one block of 7 rows
+    (2, 384, 256, None),                    # shared mode, 300 rows per expert
+], ids=["ragged", "empty_expert", "one_step_k", "shared"])
+def test_expert_ffn_mxfp8_parity(shape):
+    """The MXFP8 products (GEMM1's epilogue writes h's panel scales for GEMM2): y and the
+    saves against the oracle, and a second call on a workspace holding other garbage
+    bit-identical."""
+    E, H, I, off = shape
+    R = off[-1] if off else 300
+    print(f"  case E={E} H={H} I={I} offsets={off}", flush=True)
+    shared = off is None
     xp, w1, w2 = _ffn_case(E, R, H, I, off, 3)
-    q = lambda t, rows, K: (torch.empty(rows, K, dtype=torch.uint8, device=DEV),
-                            torch.empty(rows, K // 32, dtype=torch.uint8, device=DEV))
-    xq, xs = q(xp, R, H)
-    w1q, w1s = q(w1, E * 2 * I, H)
-    w2q, w2s = q(w2, E * H, I)
+    q = lambda rows, K: (torch.empty(rows, K, dtype=torch.uint8, device=DEV),
+                         torch.empty(rows, K // 32, dtype=torch.uint8, device=DEV))
+    xq, xs = q(R, H)
+    w1q, w1s = q(E * 2 * I, H)
+    w2q, w2s = q(E * H, I)
     moe.mx_quantize(xp, moe.BF16, R, H, xq, xs)
     moe.mx_quantize(w1, moe.BF16, E * 2 * I, H, w1q, w1s)
     moe.mx_quantize(w2, moe.BF16, E * H, I, w2q, w2s)
-    y = torch.empty(R, H, dtype=torch.bfloat16, device=DEV)
-    ws = torch.empty(moe.ffn_workspace_size(moe.MXFP8, E, R, H, I), dtype=torch.uint8, device=DEV)
-    moe.moe_expert_ffn(moe.MXFP8, xq, torch.tensor(off, dtype=torch.int32, device=DEV), E, R, H,
-                       I, w1q, w2q, y, xp_scales=xs, w1_scales=w1s, w2_scales=w2s, ws=ws)
-    torch.cuda.synchronize()
+    offs = None if shared else torch.tensor(off, dtype=torch.int32, device=DEV)
+    rows = E * R if shared else R
+    outs = []
+    for fill in (0xA5, 0xFF):  # garbage in the workspace: the call clears what it needs
+        y = torch.full((rows, H), -1.0, dtype=torch.bfloat16, device=DEV)
+        gu = torch.full((rows, 2 * I), -1.0, dtype=torch.bfloat16, device=DEV)
+        h = torch.full((rows, I), -1.0, dtype=torch.bfloat16, device=DEV)
+        ws = torch.full((moe.ffn_workspace_size(moe.MXFP8, E, R, H, I, shared),), fill,
+                        dtype=torch.uint8, device=DEV)
+        moe.moe_expert_ffn(moe.MXFP8, xq, offs, E, R, H, I, w1q, w2q, y, xp_scales=xs,
+                           w1_scales=w1s, w2_scales=w2s, gu_save=gu, h_save=h, ws=ws)
+        torch.cuda.synchronize()
+        outs.append((y, gu, h))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    y, gu, h = outs[0]
     dq = lambda a: orc.mx_dequantize(*orc.mx_quantize(a))
-    ry, _, _ = orc.ffn_fwd(dq(bf(xp)), np.array(off, np.int32), dq(bf(w1)), dq(bf(w2)), h_mx=True)
-    assert_close(bf(y), ry, TOL_MX, "y_mx")
+    ry, rgu, rh = orc.ffn_fwd(dq(bf(xp)), None if shared else np.array(off, np.int32),
+                              dq(bf(w1)), dq(bf(w2)), h_mx=True, want_gu=True, want_h=True)
+    assert_close(bf(gu), rgu, TOL_BF16, "gu")
+    assert_close(bf(h), rh, TOL_MX, "h")
+    assert_close(bf(y).reshape(ry.shape), ry, TOL_MX, "y_mx")
 
 
 def _ffn_forms(E, R, H, I, off, seed):
