@@ -107,6 +107,8 @@ def role_work(wl, role: str, shared: bool) -> tuple[str, float]:
     if role == "combine":
         return "byte", float(R * H * bf + wl.S * T * H * bf + T * H * bf + T * k * 8)
     if role == "combine_bwd":
+        if wl.mx:  # MXFP8 weight gradients: no dy rows, each row's source slot and weight
+            return "byte", float(T * H * bf + R * H * bf + T * k * 12 + R * 8)
         return "byte", float(T * H * bf + 2 * R * H * bf + T * k * 12)
     if role == "unpermute":
         return "byte", float(R * H * bf + wl.S * T * H * bf + T * H * bf + T * k * 4)
@@ -124,8 +126,13 @@ def role_work(wl, role: str, shared: bool) -> tuple[str, float]:
         return "byte", float(R * 2 * I * bf + R * 2 * I + R * 2 * I // 32)
     if role == "mx_quantize_tok_xp":  # xp's dispatch codes and scales in, codes and scales out
         return "byte", float(R * H + R * H // 32 + R * H + R * H // 32)
+    if role == "mx_quantize_tok_dy":  # dy formed from dout (each token's row, the rows'
+        # sources) and quantised along the tokens and along H in one pass
+        return "byte", float(T * H * bf + R * 12 + 2 * (R * H + R * H // 32))
+    if role == "mx_quantize_tok_dgu":  # bf16 dGU in, codes and scales along the tokens and 2I
+        return "byte", float(R * 2 * I * bf + 2 * (R * 2 * I + R * 2 * I // 32))
     if role.startswith("mx_quantize_tok_"):  # a [R, C] bf16 operand in, codes and scales out
-        C = {"dy": H, "h": I, "dgu": 2 * I}[role[len("mx_quantize_tok_"):]]
+        C = {"h": I}[role[len("mx_quantize_tok_"):]]
         return "byte", float(R * C * bf + R * C + R * C // 32)
     if role == "mx_dequantize":     # xp codes and scales read, bf16 written (and h after GEMM2)
         return "byte", float(R * H + R * H // 32 + R * H * bf)

@@ -28,13 +28,14 @@ int moe_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int
 size_t moe_ffn_bwd_mx_bytes(int E, int R, int H, int I, bool wgrad);
 int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uint8_t* w1tq,
                    const uint8_t* w1ts, const uint8_t* w2tq, const uint8_t* w2ts,
-                   const bf16_t* gu, const bf16_t* dy, bf16_t* dgu, bf16_t* dxp,
-                   const bf16_t* h, const bf16_t* xp, const uint8_t* xq, const uint8_t* xs,
-                   bf16_t* dw1, bf16_t* dw2, uint8_t* ws, hipStream_t st);
+                   const bf16_t* gu, const bf16_t* dy, const MoeTokPull* dy_pull, bf16_t* dgu,
+                   bf16_t* dxp, const bf16_t* h, const bf16_t* xp, const uint8_t* xq,
+                   const uint8_t* xs, bf16_t* dw1, bf16_t* dw2, uint8_t* ws, hipStream_t st);
 int moe_ffn_wgrad_bf16(const MoeWgradSpan* wg, int E, int H, int I, hipStream_t st);
 size_t moe_mx_panel_bytes(int E, int R, int H, int I, bool shared);
 int moe_launch_combine_bwd(const bf16_t* dout, const bf16_t* y, const int32_t* pos, const float* w,
-                           int T, int k, int H, int R, bf16_t* dy, float* dw, hipStream_t st);
+                           int T, int k, int H, int R, bf16_t* dy, int2* src, float* dw,
+                           hipStream_t st);
 int moe_launch_unpermute(const bf16_t* dxp, const int32_t* pos, int T, int k, int H, int R,
                          const bf16_t* dxs, int S, int ldT, bf16_t* dx, hipStream_t st);
 int moe_launch_router_bwd(const int32_t* idx, const float* w, const float* s_sel, const float* dw,
@@ -286,15 +287,22 @@ extern "C" int moe_backward(const moe_bwd_args* a, void* ws, size_t ws_bytes, vo
         const size_t r0 = (size_t)p * prow;
         const bf16_t* dout_p = (const bf16_t*)a->dout + (size_t)t0 * H;
         const int32_t* pos_p = a->pos + (size_t)t0 * k;
-        // combine backward: dy rows of the pass and the routing-weight gradient of its tokens
+        // combine backward: dy rows of the pass and the routing-weight gradient of its tokens.
+        // With MXFP8 weight gradients (one pass) dy is only ever read by its quantiser, which
+        // then forms the rows itself from dout and each row's source slot and weight (written
+        // in dy's place).
+        const bool mxw = a->mx == 2;
+        int2* src = mxw ? (int2*)dy : nullptr;
+        const MoeTokPull pull{dout_p, src, pos_p, Tp, k};
         rc = moe_launch_combine_bwd(dout_p, (const bf16_t*)a->y + r0 * H, pos_p,
-                                    a->w + (size_t)t0 * k, Tp, k, H, prow, dy + r0 * H,
+                                    a->w + (size_t)t0 * k, Tp, k, H, prow,
+                                    mxw ? nullptr : dy + r0 * H, src,
                                     a->dw_route + (size_t)t0 * k, st);
         if (rc) return rc;
         if (prow > 0 && a->mx) {
-            const bool mxw = a->mx == 2;
             rc = moe_ffn_bwd_mx(a->offsets, E, prow, H, I, a->w1t_codes, a->w1t_scales,
-                                a->w2t_codes, a->w2t_scales, (const bf16_t*)a->gu, dy, dgu, dxp,
+                                a->w2t_codes, a->w2t_scales, (const bf16_t*)a->gu,
+                                mxw ? nullptr : dy, mxw ? &pull : nullptr, dgu, dxp,
                                 (const bf16_t*)a->h, (const bf16_t*)a->xp,
                                 xp_as_codes ? a->xp_codes : nullptr,
                                 xp_as_codes ? a->xp_scales : nullptr,

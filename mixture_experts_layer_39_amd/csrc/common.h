@@ -89,6 +89,17 @@ struct MoeWgradSpan {
     moe::bf16_t* dw2;
 };
 
+// dy rows formed where they are consumed, instead of read from a stored copy: routed row p is
+// bf16(w * dout[s / k]) for (s, w) = src[p] when 0 <= s < T k and pos[s] == p, and zeros
+// otherwise -- the combine backward's dy; that kernel then writes src (the weight's bits in
+// .y) instead of dy.
+struct MoeTokPull {
+    const moe::bf16_t* dout;  // [T, C]
+    const int2* src;          // [R]: routed row -> (t k + j, bits of w[t, j])
+    const int32_t* pos;       // [T, k]
+    int T, k;
+};
+
 // Returns MOE_OK when the current device is gfx950 (cached per device).
 int moe_check_device();
 

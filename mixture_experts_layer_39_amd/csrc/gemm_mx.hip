@@ -828,10 +828,10 @@ size_t moe_ffn_bwd_mx_bytes(int E, int R, int H, int I, bool wgrad) {
     return n;
 }
 
-int moe_launch_mx_quantize_tok(const bf16_t* X, const uint8_t* Xq, const uint8_t* Xs, int R,
-                               int C, const int32_t* offsets, int E, int Kp, uint8_t* codes,
-                               uint8_t* scales, uint8_t* rcodes, uint8_t* rscales,
-                               const char* name, hipStream_t st);
+int moe_launch_mx_quantize_tok(const bf16_t* X, const uint8_t* Xq, const uint8_t* Xs,
+                               const MoeTokPull* pull, int R, int C, const int32_t* offsets,
+                               int E, int Kp, uint8_t* codes, uint8_t* scales, uint8_t* rcodes,
+                               uint8_t* rscales, const char* name, hipStream_t st);
 
 // A: ragged rows (offsets) or R static rows (offsets null); B: EB operands of b_rows rows.
 static int mx_panels_ab(const uint8_t* as, const int32_t* offsets, int E, int R,
@@ -852,7 +852,8 @@ static int mx_panels_ab(const uint8_t* as, const int32_t* offsets, int E, int R,
 // ws (advanced past them) and returns the product's arguments.  The pass over A also writes A
 // quantised along its rows (arq, ars: the operand of the dgrad product that shares A).  B may
 // come as MX codes and scales along its columns (Bq, Bs; B unused), which the pass decodes.
-static int mx_wgrad_prepare(const bf16_t* A, int M, const bf16_t* B, const uint8_t* Bq,
+static int mx_wgrad_prepare(const bf16_t* A, const MoeTokPull* Ap, int M, const bf16_t* B,
+                            const uint8_t* Bq,
                             const uint8_t* Bs, int N,
                             const int32_t* offsets, int E, int R, bf16_t* dw, uint8_t*& ws,
                             uint8_t* arq, uint8_t* ars, const char* qa, const char* qb,
@@ -865,11 +866,11 @@ static int mx_wgrad_prepare(const bf16_t* A, int M, const bf16_t* B, const uint8
     uint8_t* bsc = bc + moe_align256((size_t)N * Kp);
     uint8_t* bp = bsc + moe_align256((size_t)N * Kp / 32);
     ws += mx_tok_bytes(M, Kp) + mx_tok_bytes(N, Kp);
-    int rc = moe_launch_mx_quantize_tok(A, nullptr, nullptr, R, M, offsets, E, Kp, ac, as, arq,
-                                        ars, qa, st);
+    int rc = moe_launch_mx_quantize_tok(A, nullptr, nullptr, Ap, R, M, offsets, E, Kp, ac, as,
+                                        arq, ars, qa, st);
     if (rc) return rc;
-    rc = moe_launch_mx_quantize_tok(B, Bq, Bs, R, N, offsets, E, Kp, bc, bsc, nullptr, nullptr,
-                                    qb, st);
+    rc = moe_launch_mx_quantize_tok(B, Bq, Bs, nullptr, R, N, offsets, E, Kp, bc, bsc, nullptr,
+                                    nullptr, qb, st);
     if (rc) return rc;
     rc = mx_panels_ab(as, nullptr, 1, M, bsc, 1, N, Kp, ap, bp, st);
     if (rc) return rc;
@@ -905,14 +906,16 @@ static int mx_launch_pair(const MxArgs& gd_, const MxArgs& gw, const char* name,
 // w2t: W2_e^T codes [E][I][H] and scales [E][I][H/32] (along H); w1t: W1_e^T codes [E][H][2I]
 // and scales [E][H][2I/32] (along 2I) -- mx_quantize_t of the weights.  gu: the forward's g|u;
 // h, xp: the forward's GEMM inputs (bf16); xp may instead come as its MX codes and scales
-// (xq, xs: then xp is not read; weight gradients only).
+// (xq, xs: then xp is not read; weight gradients only).  With the weight gradients, dy may
+// instead come as dy_pull (its rows formed from dout where they are quantised; dy unused).
 int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uint8_t* w1tq,
                    const uint8_t* w1ts, const uint8_t* w2tq, const uint8_t* w2ts,
-                   const bf16_t* gu, const bf16_t* dy, bf16_t* dgu, bf16_t* dxp,
-                   const bf16_t* h, const bf16_t* xp, const uint8_t* xq, const uint8_t* xs,
-                   bf16_t* dw1, bf16_t* dw2, uint8_t* ws, hipStream_t st) {
+                   const bf16_t* gu, const bf16_t* dy, const MoeTokPull* dy_pull, bf16_t* dgu,
+                   bf16_t* dxp, const bf16_t* h, const bf16_t* xp, const uint8_t* xq,
+                   const uint8_t* xs, bf16_t* dw1, bf16_t* dw2, uint8_t* ws, hipStream_t st) {
     if (H % XBK || I % XBK) return MOE_EINVAL;
     const bool wgrad = dw1 && dw2;
+    if (!wgrad && !dy) return MOE_EINVAL;
     uint8_t* dyq = ws;
     uint8_t* dys = dyq + moe_align256((size_t)R * H);
     uint8_t* gq = dys + moe_align256((size_t)R * H / 32);
@@ -925,8 +928,9 @@ int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uin
     MxArgs gw{}, gw2{};  // total 0: no weight-gradient tiles
     // dy quantised along H for dh and, with the weight gradients, along the tokens for dW2 in
     // the same pass
-    int rc = wgrad ? mx_wgrad_prepare(dy, H, h, nullptr, nullptr, I, offsets, E, R, dw2, wsw, dyq, dys,
-                                      "mx_quantize_tok_dy", "mx_quantize_tok_h", gw, st)
+    int rc = wgrad ? mx_wgrad_prepare(dy, dy_pull, H, h, nullptr, nullptr, I, offsets, E, R, dw2,
+                                      wsw, dyq, dys, "mx_quantize_tok_dy", "mx_quantize_tok_h",
+                                      gw, st)
                    : moe_launch_mx_quantize_bf16(dy, R, H, dyq, dys, "mx_quantize_dy", st);
     if (rc) return rc;
     rc = mx_panels_ab(dys, offsets, E, R, w2ts, E, I, H, pa1, pb1, st);
@@ -939,7 +943,7 @@ int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uin
     g.offsets = offsets; g.E = E; g.R = R; g.N = I; g.K = H; g.I = I;
     rc = mx_launch_pair<XEPI_DSWIGLU>(g, gw, wgrad ? "mx_bwd_down_wgrad" : "mx_bwd_down", st);
     if (rc) return rc;
-    rc = wgrad ? mx_wgrad_prepare(dgu, 2 * I, xp, xq, xs, H, offsets, E, R, dw1, wsw, gq, gs,
+    rc = wgrad ? mx_wgrad_prepare(dgu, nullptr, 2 * I, xp, xq, xs, H, offsets, E, R, dw1, wsw, gq, gs,
                                   "mx_quantize_tok_dgu", "mx_quantize_tok_xp", gw2, st)
                : moe_launch_mx_quantize_bf16(dgu, R, 2 * I, gq, gs, "mx_quantize_dgu", st);
     if (rc) return rc;

@@ -200,6 +200,8 @@ static int combine_threads(int H) {
 // One block per token: dy[pos[t,j],:] = bf16(w[t,j] * dout[t,:]) and
 // dw[t,j] = <dout[t,:], y[pos[t,j],:]> in fp32 with a fixed reduction tree: each thread sums
 // its chunks in ascending order, then a butterfly over the wave and the four waves in order.
+// dy null: no dy rows; src (if given) receives src[pos[t,j]] = (t k + j, bits of w[t,j])
+// instead, so that the consumer of dy forms its rows itself (MoeTokPull).
 constexpr int CB_UN = 4;
 
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restrict__ dout,
@@ -207,12 +209,18 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restri
                                                           const int32_t* __restrict__ pos,
                                                           const float* __restrict__ w, int k,
                                                           int H, int R, bf16_t* __restrict__ dy,
+                                                          int2* __restrict__ src,
                                                           float* __restrict__ dw) {
     const int t = blockIdx.x;
     __shared__ float red[4][MAXK];
     const int nc = H / 8;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const bf16_t* g_row = dout + (size_t)t * H;
+    if (src && threadIdx.x < k) {
+        const int s = t * k + (int)threadIdx.x;
+        const int pp = pos[s];
+        if (pp >= 0 && pp < R) src[pp] = make_int2(s, __float_as_int(w[s]));
+    }
     if (nc <= 256 * CB_UN) {
         // The row in one pass: the thread's dout chunks are loaded once for all slots, slot
         // j's position and weight come from lane j of every wave (k <= 64), and slot j+1's
@@ -259,7 +267,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restri
                         part = __fadd_rn(part, __fmul_rn(g1, hi_bf(v[u][q])));
                         o[q] = pack_bf2(__fmul_rn(wj, g0), __fmul_rn(wj, g1));
                     }
-                    st16(dy + (size_t)p * H + c * 8, o);
+                    if (dy) st16(dy + (size_t)p * H + c * 8, o);
                 }
             }
 #pragma unroll
@@ -297,7 +305,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restri
                             part = __fadd_rn(part, __fmul_rn(g1, hi_bf(v[u][q])));
                             o[q] = pack_bf2(__fmul_rn(wj, g0), __fmul_rn(wj, g1));
                         }
-                        st16(dy + (size_t)p * H + c * 8, o);
+                        if (dy) st16(dy + (size_t)p * H + c * 8, o);
                     }
                 }
             }
@@ -505,9 +513,10 @@ __global__ __launch_bounds__(256) void mx_dequantize_kernel(const uint8_t* __res
 //
 // One block per (128 columns, 128 padded positions), C % 128 == 0:
 //  1. the 128 x 128 tile of X is staged through LDS with 16-byte row loads (all of a
-//     thread's loads issued first); X may also come as MX codes with scales along C (MXIN),
-//     decoded while staging exactly as mx_dequantize decodes them (so the staged values are
-//     those a dequantised copy would hold);
+//     thread's loads issued first); X may also come as MX codes with scales along C
+//     (TOK_IN_MX), decoded while staging exactly as mx_dequantize decodes them (so the staged
+//     values are those a dequantised copy would hold), or as the combine backward's dy rows
+//     formed from their tokens (TOK_IN_PULL, MoeTokPull: the same product and rounding);
 //  2. column pass: wave w takes the rows 32w .. 32w+31, lane l the column pair 2l, 2l+1
 //     (one dword LDS read per row: 64 consecutive dwords, conflict-free); row pass: items
 //     (row r, 32-column block b), four lanes per row, 64 contiguous LDS bytes each;
@@ -520,7 +529,9 @@ constexpr int TOK_LD = TOK_COLS * 2 + 16;  // bytes per staged input row (16-byt
 constexpr int TOK_OL = 128 + 16;           // bytes per staged output line
 constexpr int TOK_LDS = 2 * TOK_PAD * TOK_OL + 2 * 128 * 4;  // >= TOK_PAD * TOK_LD
 
-template <bool MXIN>
+constexpr int TOK_IN_BF16 = 0, TOK_IN_MX = 1, TOK_IN_PULL = 2;
+
+template <int IN>
 __global__ __launch_bounds__(256) void mx_quantize_tok_kernel(const bf16_t* __restrict__ X,
                                                               const uint8_t* __restrict__ Xq,
                                                               const uint8_t* __restrict__ Xs,
@@ -530,7 +541,8 @@ __global__ __launch_bounds__(256) void mx_quantize_tok_kernel(const bf16_t* __re
                                                               uint8_t* __restrict__ codes,
                                                               uint8_t* __restrict__ scales,
                                                               uint8_t* __restrict__ rcodes,
-                                                              uint8_t* __restrict__ rscales) {
+                                                              uint8_t* __restrict__ rscales,
+                                                              MoeTokPull pull) {
     static_assert(TOK_LDS >= TOK_PAD * TOK_LD, "output images reuse the input tile");
     __shared__ __attribute__((aligned(16))) uint8_t lds[TOK_LDS];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -560,7 +572,7 @@ __global__ __launch_bounds__(256) void mx_quantize_tok_kernel(const bf16_t* __re
         cnt = min(max(offsets[e + 1], lo), R) - lo;
     }
     const int t0 = p - P;  // the block's first row within the expert
-    if (!MXIN) {
+    if (IN == TOK_IN_BF16) {
         // 1. stage 128 rows x 128 columns: 16 chunks of 8 values per row, 8 per thread
         constexpr int NLD = TOK_PAD * (TOK_COLS / 8) / 256;
         u32x4 v4[NLD];
@@ -576,6 +588,44 @@ __global__ __launch_bounds__(256) void mx_quantize_tok_kernel(const bf16_t* __re
             const int i = tid + 256 * u;
             const int r = i / (TOK_COLS / 8), ch = i % (TOK_COLS / 8);
             *reinterpret_cast<u32x4*>(lds + r * TOK_LD + ch * 16) = v4[u];
+        }
+    } else if (IN == TOK_IN_PULL) {
+        // 1. (dy rows formed here) row lo + t0 + r is bf16(w * dout[s / k]) for its source
+        //    (s, w), or zeros: 16 chunks of 8 values per row, 8 per thread.  The row's dout
+        //    chunk and the check of s against pos are loaded together, after src.
+        constexpr int NLD = TOK_PAD * (TOK_COLS / 8) / 256;
+        int2 sw[NLD];
+#pragma unroll
+        for (int u = 0; u < NLD; ++u) {
+            const int i = tid + 256 * u;
+            const int r = i / (TOK_COLS / 8);
+            sw[u] = (e >= 0 && t0 + r < cnt) ? pull.src[lo + t0 + r] : make_int2(-1, 0);
+        }
+        int back[NLD];
+        u32x4 v4[NLD];
+#pragma unroll
+        for (int u = 0; u < NLD; ++u) {
+            const int i = tid + 256 * u;
+            const int col = c0 + (i % (TOK_COLS / 8)) * 8;
+            const int sl = sw[u].x;
+            const bool in = sl >= 0 && sl < pull.T * pull.k;
+            back[u] = in ? pull.pos[sl] : -1;
+            v4[u] = in ? ld16(pull.dout + (int64_t)(sl / pull.k) * C + col)
+                       : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < NLD; ++u) {
+            const int i = tid + 256 * u;
+            const int r = i / (TOK_COLS / 8), ch = i % (TOK_COLS / 8);
+            const bool ok = back[u] == lo + t0 + r;
+            const float wv = ok ? __int_as_float(sw[u].y) : 0.0f;
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                o[q] = ok ? pack_bf2(__fmul_rn(wv, lo_bf(v4[u][q])),
+                                     __fmul_rn(wv, hi_bf(v4[u][q])))
+                          : 0u;
+            *reinterpret_cast<u32x4*>(lds + r * TOK_LD + ch * 16) = o;
         }
     } else {
         // 1. (MX input) 128 rows x 128 codes: 8 chunks of 16 codes per row, 4 per thread;
@@ -792,23 +842,31 @@ extern "C" int mx_quantize(const void* in, int in_dtype, int rows, int K, uint8_
     return MOE_OK;
 }
 
-int moe_launch_mx_quantize_tok(const bf16_t* X, const uint8_t* Xq, const uint8_t* Xs, int R,
-                               int C, const int32_t* offsets, int E, int Kp, uint8_t* codes,
-                               uint8_t* scales, uint8_t* rcodes, uint8_t* rscales,
-                               const char* name, hipStream_t st) {
+int moe_launch_mx_quantize_tok(const bf16_t* X, const uint8_t* Xq, const uint8_t* Xs,
+                               const MoeTokPull* pull, int R, int C, const int32_t* offsets,
+                               int E, int Kp, uint8_t* codes, uint8_t* scales, uint8_t* rcodes,
+                               uint8_t* rscales, const char* name, hipStream_t st) {
     if (Kp == 0 || C == 0) return MOE_OK;
     if (C % TOK_COLS != 0 || Kp % TOK_PAD != 0) return MOE_EINVAL;
     const dim3 grid((unsigned)(C / TOK_COLS), (unsigned)(Kp / TOK_PAD));
+    const MoeTokPull none{};
     if (Xq) {  // MX codes and scales along C (X unused)
         if (!Xs) return MOE_EINVAL;
         MOE_TRACED(name, st,
-                   mx_quantize_tok_kernel<true><<<grid, 256, 0, st>>>(
-                       nullptr, Xq, Xs, R, C, offsets, E, Kp, codes, scales, rcodes, rscales));
+                   mx_quantize_tok_kernel<TOK_IN_MX><<<grid, 256, 0, st>>>(
+                       nullptr, Xq, Xs, R, C, offsets, E, Kp, codes, scales, rcodes, rscales,
+                       none));
+    } else if (pull) {  // dy rows formed from dout and the rows' sources (X unused)
+        if (!pull->dout || !pull->src || !pull->pos || pull->k < 1) return MOE_EINVAL;
+        MOE_TRACED(name, st,
+                   mx_quantize_tok_kernel<TOK_IN_PULL><<<grid, 256, 0, st>>>(
+                       nullptr, nullptr, nullptr, R, C, offsets, E, Kp, codes, scales, rcodes,
+                       rscales, *pull));
     } else {
         MOE_TRACED(name, st,
-                   mx_quantize_tok_kernel<false><<<grid, 256, 0, st>>>(
+                   mx_quantize_tok_kernel<TOK_IN_BF16><<<grid, 256, 0, st>>>(
                        X, nullptr, nullptr, R, C, offsets, E, Kp, codes, scales, rcodes,
-                       rscales));
+                       rscales, none));
     }
     MOE_LAUNCH_CHECK();
     return MOE_OK;
@@ -854,10 +912,11 @@ extern "C" int mx_dequantize(const uint8_t* codes, const uint8_t* scales, int ro
 
 // Internal launchers used by the backward orchestration.
 int moe_launch_combine_bwd(const bf16_t* dout, const bf16_t* y, const int32_t* pos, const float* w,
-                           int T, int k, int H, int R, bf16_t* dy, float* dw, hipStream_t st) {
+                           int T, int k, int H, int R, bf16_t* dy, int2* src, float* dw,
+                           hipStream_t st) {
     if (T == 0) return MOE_OK;
     MOE_TRACED("combine_bwd", st,
-               combine_bwd_kernel<<<T, 256, 0, st>>>(dout, y, pos, w, k, H, R, dy, dw));
+               combine_bwd_kernel<<<T, 256, 0, st>>>(dout, y, pos, w, k, H, R, dy, src, dw));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

@@ -109,6 +109,29 @@ def test_mx_backward_against_oracle(kw, mode):
         assert not torch.any(layer.dw1[e] != 0) and not torch.any(layer.dw2[e] != 0)
 
 
+@pytest.mark.parametrize("kw", [dict(), dict(T=100, R_share=800)])
+def test_mx_backward_modes_share_dgrad_bits(kw):
+    """Both MXFP8 modes run the same dgrad products on the same codes of dy: in mode 1 they come
+    from a stored dy, in mode 2 the token-axis quantiser forms the dy rows from dout, the
+    routing weights and the inverse of pos (no dy is stored).  So dX, the routing-weight and
+    the logit gradients agree bit for bit."""
+    wl = wk.WORKLOADS["dsv3_ep64_mxfp8"].scaled(**{**REDUCED, **kw})
+    inp = wk.make_inputs(wl, device=DEV)
+    print(f"  case T={wl.T} R={wl.R}", flush=True)
+    got = []
+    for mode in (1, 2):
+        cfg = LayerCfg.from_workload(wl)
+        cfg.mx_bwd = mode
+        layer = MoELayer(cfg, inp, DEV, backward=True)
+        layer.forward()
+        layer.backward()
+        torch.cuda.synchronize()
+        got.append({n: getattr(layer, n).clone() for n in ("dx", "dw_route", "dlogits")})
+        del layer
+    for n in got[0]:
+        assert torch.equal(got[0][n], got[1][n]), n
+
+
 def test_mx_backward_full_size_deterministic_and_near_bf16():
     """Full EP-64 share: reruns are bit-identical, and the MXFP8 products stay within the MX
     quantisation error of the BF16 products on the same saves."""
