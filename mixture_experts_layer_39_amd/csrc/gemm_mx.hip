@@ -831,13 +831,15 @@ size_t moe_ffn_bwd_mx_bytes(int E, int R, int H, int I, bool wgrad) {
 int moe_launch_mx_quantize_tok(const bf16_t* X, const uint8_t* Xq, const uint8_t* Xs,
                                const MoeTokPull* pull, int R, int C, const int32_t* offsets,
                                int E, int Kp, uint8_t* codes, uint8_t* scales, uint8_t* rcodes,
-                               uint8_t* rscales, const char* name, hipStream_t st);
+                               uint8_t* rscales, uint8_t* cpanel, uint8_t* rpanel,
+                               const char* name, hipStream_t st);
 
 // A: ragged rows (offsets) or R static rows (offsets null); B: EB operands of b_rows rows.
+// as null: the B panels only (the A panels come from the operand's quantiser).
 static int mx_panels_ab(const uint8_t* as, const int32_t* offsets, int E, int R,
                         const uint8_t* bs, int EB, int b_rows, int K, uint8_t* pa, uint8_t* pb,
                         hipStream_t st) {
-    const int na = offsets ? mx_mtiles_bound(R, E, false) : cdiv(R, XBM);
+    const int na = !as ? 0 : offsets ? mx_mtiles_bound(R, E, false) : cdiv(R, XBM);
     const dim3 grid(na + EB * cdiv(b_rows, XBN), cdiv(K / 32, PS_COLS));
     MOE_TRACED("mx_panel_scales", st,
                mx_panel_scales_ab<<<grid, 256, 0, st>>>(as, offsets, E, R, na, bs, b_rows, K, pa,
@@ -849,15 +851,16 @@ static int mx_panels_ab(const uint8_t* as, const int32_t* offsets, int E, int R,
 
 // One MXFP8 weight-gradient product, prepared: dW_e [M,N] = Qt(A_e)^T Qt(B_e) over expert e's
 // rows, with A [R,M] and B [R,N] in expert order; quantises both operands along the tokens into
-// ws (advanced past them) and returns the product's arguments.  The pass over A also writes A
-// quantised along its rows (arq, ars: the operand of the dgrad product that shares A).  B may
-// come as MX codes and scales along its columns (Bq, Bs; B unused), which the pass decodes.
+// ws (advanced past them), with their panel scales, and returns the product's arguments.  The
+// pass over A also writes A quantised along its rows (arq, ars, and the panels arp: the
+// operand of the dgrad product that shares A).  B may come as MX codes and scales along its
+// columns (Bq, Bs; B unused), which the pass decodes.
 static int mx_wgrad_prepare(const bf16_t* A, const MoeTokPull* Ap, int M, const bf16_t* B,
                             const uint8_t* Bq,
                             const uint8_t* Bs, int N,
                             const int32_t* offsets, int E, int R, bf16_t* dw, uint8_t*& ws,
-                            uint8_t* arq, uint8_t* ars, const char* qa, const char* qb,
-                            MxArgs& g, hipStream_t st) {
+                            uint8_t* arq, uint8_t* ars, uint8_t* arp, const char* qa,
+                            const char* qb, MxArgs& g, hipStream_t st) {
     const int Kp = mx_tok_cols(E, R);
     uint8_t* ac = ws;
     uint8_t* as = ac + moe_align256((size_t)M * Kp);
@@ -867,12 +870,10 @@ static int mx_wgrad_prepare(const bf16_t* A, const MoeTokPull* Ap, int M, const 
     uint8_t* bp = bsc + moe_align256((size_t)N * Kp / 32);
     ws += mx_tok_bytes(M, Kp) + mx_tok_bytes(N, Kp);
     int rc = moe_launch_mx_quantize_tok(A, nullptr, nullptr, Ap, R, M, offsets, E, Kp, ac, as,
-                                        arq, ars, qa, st);
+                                        arq, ars, ap, arp, qa, st);
     if (rc) return rc;
     rc = moe_launch_mx_quantize_tok(B, Bq, Bs, nullptr, R, N, offsets, E, Kp, bc, bsc, nullptr,
-                                    nullptr, qb, st);
-    if (rc) return rc;
-    rc = mx_panels_ab(as, nullptr, 1, M, bsc, 1, N, Kp, ap, bp, st);
+                                    nullptr, bp, nullptr, qb, st);
     if (rc) return rc;
     g = MxArgs{};
     g.A = ac; g.At = ap; g.a_es = 0;
@@ -929,11 +930,11 @@ int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uin
     // dy quantised along H for dh and, with the weight gradients, along the tokens for dW2 in
     // the same pass
     int rc = wgrad ? mx_wgrad_prepare(dy, dy_pull, H, h, nullptr, nullptr, I, offsets, E, R, dw2,
-                                      wsw, dyq, dys, "mx_quantize_tok_dy", "mx_quantize_tok_h",
-                                      gw, st)
+                                      wsw, dyq, dys, pa1, "mx_quantize_tok_dy",
+                                      "mx_quantize_tok_h", gw, st)
                    : moe_launch_mx_quantize_bf16(dy, R, H, dyq, dys, "mx_quantize_dy", st);
     if (rc) return rc;
-    rc = mx_panels_ab(dys, offsets, E, R, w2ts, E, I, H, pa1, pb1, st);
+    rc = mx_panels_ab(wgrad ? nullptr : dys, offsets, E, R, w2ts, E, I, H, pa1, pb1, st);
     if (rc) return rc;
     MxArgs g{};
     g.A = dyq; g.At = pa1; g.a_es = 0;
@@ -943,11 +944,11 @@ int moe_ffn_bwd_mx(const int32_t* offsets, int E, int R, int H, int I, const uin
     g.offsets = offsets; g.E = E; g.R = R; g.N = I; g.K = H; g.I = I;
     rc = mx_launch_pair<XEPI_DSWIGLU>(g, gw, wgrad ? "mx_bwd_down_wgrad" : "mx_bwd_down", st);
     if (rc) return rc;
-    rc = wgrad ? mx_wgrad_prepare(dgu, nullptr, 2 * I, xp, xq, xs, H, offsets, E, R, dw1, wsw, gq, gs,
-                                  "mx_quantize_tok_dgu", "mx_quantize_tok_xp", gw2, st)
+    rc = wgrad ? mx_wgrad_prepare(dgu, nullptr, 2 * I, xp, xq, xs, H, offsets, E, R, dw1, wsw, gq,
+                                  gs, pa2, "mx_quantize_tok_dgu", "mx_quantize_tok_xp", gw2, st)
                : moe_launch_mx_quantize_bf16(dgu, R, 2 * I, gq, gs, "mx_quantize_dgu", st);
     if (rc) return rc;
-    rc = mx_panels_ab(gs, offsets, E, R, w1ts, E, H, 2 * I, pa2, pb2, st);
+    rc = mx_panels_ab(wgrad ? nullptr : gs, offsets, E, R, w1ts, E, H, 2 * I, pa2, pb2, st);
     if (rc) return rc;
     MxArgs g2{};
     g2.A = gq; g2.At = pa2; g2.a_es = 0;

@@ -542,29 +542,37 @@ __global__ __launch_bounds__(256) void mx_quantize_tok_kernel(const bf16_t* __re
                                                               uint8_t* __restrict__ scales,
                                                               uint8_t* __restrict__ rcodes,
                                                               uint8_t* __restrict__ rscales,
+                                                              uint8_t* __restrict__ cpanel,
+                                                              uint8_t* __restrict__ rpanel,
                                                               MoeTokPull pull) {
     static_assert(TOK_LDS >= TOK_PAD * TOK_LD, "output images reuse the input tile");
     __shared__ __attribute__((aligned(16))) uint8_t lds[TOK_LDS];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int p = blockIdx.y * TOK_PAD;  // padded position of this block's first row
     const int c0 = blockIdx.x * TOK_COLS;
-    int e = -1, P = 0, run = 0;
+    // the block's expert e, its first padded position P and (for rpanel) its first 256-row
+    // block MT among all experts' row blocks
+    int e = -1, P = 0, MT = 0, run = 0, run2 = 0;
     for (int base = 0; base < E && e < 0; base += 64) {
         const int x = base + lane;
-        int v = 0;
+        int v = 0, v2 = 0;
         if (x < E) {
             const int lo = min(max(offsets[x], 0), R);
             const int hi = min(max(offsets[x + 1], lo), R);
             v = (hi - lo + TOK_PAD - 1) / TOK_PAD * TOK_PAD;
+            v2 = (hi - lo + 255) / 256;
         }
         const int inc = wave_incl_scan(v) + run;
+        const int inc2 = wave_incl_scan(v2) + run2;
         const uint64_t m = __ballot(x < E && inc > p);
         if (m) {
             const int l = __ffsll((unsigned long long)m) - 1;
             e = base + l;
             P = __shfl(inc - v, l, 64);
+            MT = __shfl(inc2 - v2, l, 64);
         }
         run = __shfl(inc, 63, 64);
+        run2 = __shfl(inc2, 63, 64);
     }
     int lo = 0, cnt = 0;
     if (e >= 0) {
@@ -746,6 +754,38 @@ __global__ __launch_bounds__(256) void mx_quantize_tok_kernel(const bf16_t* __re
             *reinterpret_cast<uint32_t*>(rscales + (int64_t)(lo + t0 + tid) * (C / 32) + c0 / 32) =
                 *reinterpret_cast<const uint32_t*>(row_sc + tid * 4);
     }
+    // 5. the same scales in the MX GEMMs' panel layout (a run of 512 bytes per 128-row panel
+    //    and K step of 128 codes; byte 8 (32 g + l) + 2 t + kk holds the scale of panel row
+    //    32 t + l in the step's 32-code block 2 kk + g), gathered from the scale images in LDS
+    //    and written as whole words, so that no separate pass lays them out.  A panel whose
+    //    256-row block has no rows past this block's gets zeros, as the panels built from
+    //    stored scales do for rows outside the operand.
+    auto gather4 = [&](const uint8_t* img) {  // run bytes 4 tid .. 4 tid + 3 from [row][blk]
+        uint32_t wv = 0;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int j = 4 * tid + x, L = j >> 3, t = (j & 7) >> 1, kk = j & 1;
+            wv |= (uint32_t)img[(32 * t + (L & 31)) * 4 + 2 * kk + (L >> 5)] << (8 * x);
+        }
+        return wv;
+    };
+    if (cpanel && tid < 128) {
+        // token-axis operand: panel row = column c0 + row, K step = position p / 128, block =
+        // the 32 positions of wave blk
+        uint8_t* run_ = cpanel + ((int64_t)(c0 / 128) * (Kp / 128) + p / 128) * 512;
+        *reinterpret_cast<uint32_t*>(run_ + 4 * tid) = gather4(col_sc);
+        if (C % 256 == 128 && c0 == C - 128)
+            *reinterpret_cast<uint32_t*>(run_ + (int64_t)(Kp / 128) * 512 + 4 * tid) = 0u;
+    }
+    if (rpanel && rcodes && e >= 0 && tid < 128) {
+        // row-wise operand of the dgrad product: panel row = row t0 % 128 + r of the expert's
+        // 256-row block MT + t0 / 256, K step = c0 / 128, block = 32-column block b
+        const int q = 2 * (MT + t0 / 256) + ((t0 / 128) & 1);
+        uint8_t* run_ = rpanel + ((int64_t)q * (C / 128) + c0 / 128) * 512;
+        *reinterpret_cast<uint32_t*>(run_ + 4 * tid) = gather4(row_sc);
+        if (((t0 / 128) & 1) == 0 && t0 + 128 >= cnt)
+            *reinterpret_cast<uint32_t*>(run_ + (int64_t)(C / 128) * 512 + 4 * tid) = 0u;
+    }
 }
 
 }  // namespace moe
@@ -845,7 +885,8 @@ extern "C" int mx_quantize(const void* in, int in_dtype, int rows, int K, uint8_
 int moe_launch_mx_quantize_tok(const bf16_t* X, const uint8_t* Xq, const uint8_t* Xs,
                                const MoeTokPull* pull, int R, int C, const int32_t* offsets,
                                int E, int Kp, uint8_t* codes, uint8_t* scales, uint8_t* rcodes,
-                               uint8_t* rscales, const char* name, hipStream_t st) {
+                               uint8_t* rscales, uint8_t* cpanel, uint8_t* rpanel,
+                               const char* name, hipStream_t st) {
     if (Kp == 0 || C == 0) return MOE_OK;
     if (C % TOK_COLS != 0 || Kp % TOK_PAD != 0) return MOE_EINVAL;
     const dim3 grid((unsigned)(C / TOK_COLS), (unsigned)(Kp / TOK_PAD));
@@ -855,18 +896,18 @@ int moe_launch_mx_quantize_tok(const bf16_t* X, const uint8_t* Xq, const uint8_t
         MOE_TRACED(name, st,
                    mx_quantize_tok_kernel<TOK_IN_MX><<<grid, 256, 0, st>>>(
                        nullptr, Xq, Xs, R, C, offsets, E, Kp, codes, scales, rcodes, rscales,
-                       none));
+                       cpanel, rpanel, none));
     } else if (pull) {  // dy rows formed from dout and the rows' sources (X unused)
         if (!pull->dout || !pull->src || !pull->pos || pull->k < 1) return MOE_EINVAL;
         MOE_TRACED(name, st,
                    mx_quantize_tok_kernel<TOK_IN_PULL><<<grid, 256, 0, st>>>(
                        nullptr, nullptr, nullptr, R, C, offsets, E, Kp, codes, scales, rcodes,
-                       rscales, *pull));
+                       rscales, cpanel, rpanel, *pull));
     } else {
         MOE_TRACED(name, st,
                    mx_quantize_tok_kernel<TOK_IN_BF16><<<grid, 256, 0, st>>>(
                        X, nullptr, nullptr, R, C, offsets, E, Kp, codes, scales, rcodes,
-                       rscales, none));
+                       rscales, cpanel, rpanel, none));
     }
     MOE_LAUNCH_CHECK();
     return MOE_OK;
