@@ -82,10 +82,13 @@ def test_mx_forward_saves():
 
 @pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("kw", [dict(), dict(T=64, R_share=512, I=256),
-                                dict(T=48, R_share=384, H=128, I=128)])
+                                dict(T=48, R_share=384, H=128, I=128),
+                                dict(T=40, R_share=320, H=384, I=384)])
 def test_mx_backward_against_oracle(kw, mode):
-    """The last case has K loops of one and two steps (K = H = 128, 2I = 256, and one token
-    step per expert in the weight gradients) and down-projection tiles twice as wide as H."""
+    """The third case has K loops of one and two steps (K = H = 128, 2I = 256, and one token
+    step per expert in the weight gradients) and down-projection tiles twice as wide as H; the
+    last has operands of 384 columns (a 256-row block of panels whose second half holds no
+    rows) and experts of about 80 rows (one half-filled 256-row block each)."""
     wl = wk.WORKLOADS["dsv3_ep64_mxfp8"].scaled(**{**REDUCED, **kw})
     inp = wk.make_inputs(wl, device=DEV)
     cfg = LayerCfg.from_workload(wl)
