@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--all-configs", action=argparse.BooleanOptionalAction, default=True,
                     help="after the headline workload (dsv3_ep64), also measure the other "
                          "workloads and report them under \"configs\"")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed as a HIP graph (graph_ms_per_step)")
     ap.add_argument("--breakdown", action="store_true",
                     help="also print per-role times to stderr")
     ap.add_argument("--ring-depth", type=int, default=16,
@@ -457,7 +459,8 @@ def main():
     }
     for key in ("fwd_tokens_per_s", "fwd_ms_per_step", "step_tflops", "fwd_tflops",
                 "cold_tokens_per_s", "cold_ms_per_step", "cold_fwd_ms_per_step",
-                "fused_fwd_ms_per_step", "fused_fwd_tokens_per_s", "roofline", "breakdown",
+                "fused_fwd_ms_per_step", "fused_fwd_tokens_per_s", "graph_ms_per_step",
+                "graph_tokens_per_s", "roofline", "breakdown",
                 "cpu_baseline"):
         out[key] = head.get(key)
     if a.all_configs and a.workload == "dsv3_ep64" and not a.fused:
@@ -554,6 +557,21 @@ def measure(wl, a, *, ring_depth, steps, warmup, fused, bias_gamma, headline, cp
     fwd_ms = time_fwd(layer.forward) if wl.backward or fused else ms_step
     fused_ms = time_fwd(layer.forward_fused) if can_fuse else None
 
+    # the same whole step replayed as a HIP graph (every launch of the step, no host work
+    # between them), untraced
+    graph_ms = None
+    if not fused and a.graph:
+        g = layer.capture(backward=wl.backward)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - g0) * 1e3 / steps
+        del g
+
     # per-role statistics over the traced steps
     roles: dict[str, list[float]] = {}
     for name, ms in recs:
@@ -591,6 +609,8 @@ def measure(wl, a, *, ring_depth, steps, warmup, fused, bias_gamma, headline, cp
         "fwd_tflops": round(flops_fwd / (fwd_ms * 1e-3) / 1e12, 1),
         "fused_fwd_ms_per_step": round(fused_ms, 4) if fused_ms else None,
         "fused_fwd_tokens_per_s": round(wl.T / (fused_ms * 1e-3), 1) if fused_ms else None,
+        "graph_ms_per_step": round(graph_ms, 4) if graph_ms else None,
+        "graph_tokens_per_s": round(wl.T / (graph_ms * 1e-3), 1) if graph_ms else None,
         "roofline": roof,
     }
     if layer.ring or wl.E > 8:

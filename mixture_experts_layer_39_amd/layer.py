@@ -297,6 +297,29 @@ class MoELayer:
             moe_update_bias(self.counts, c.ER, c.bias_gamma, self.sel_bias)
         return self.out
 
+    # ------------------------------------------------------------------ HIP graph
+    def capture(self, backward: bool = False):
+        """One step of this layer -- the forward (per-step calls, or the ring's passes) and,
+        with backward=True, the backward -- captured as a HIP graph over the layer's buffers.
+        Replaying it reruns every launch of the step without host work between them.  The
+        library allocates, frees and synchronises nothing and clears its own counters with
+        kernels, so the calls capture as they run.  Returns the torch.cuda.CUDAGraph."""
+        def step():
+            self.forward()
+            if backward:
+                self.backward()
+
+        side = torch.cuda.Stream(device=self.dev)  # default priority
+        side.wait_stream(torch.cuda.current_stream(self.dev))
+        with torch.cuda.stream(side):
+            step()  # first calls (per-device set-up of the library) outside the capture
+        torch.cuda.current_stream(self.dev).wait_stream(side)
+        torch.cuda.synchronize(self.dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        return g
+
     # ------------------------------------------------------------------ macrobatch ring
     def _route_minibatch(self, a, b):
         # the selection alone (idx, w, s_sel of the minibatch's tokens): the rows are permuted
