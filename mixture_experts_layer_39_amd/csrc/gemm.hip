@@ -1226,9 +1226,20 @@ extern "C" int moe_layer_forward(const moe_fwd_args* p, void* ws, size_t ws_byte
     a.sy = (unsigned*)((char*)ws + moe_align256(moe_route_workspace_size(f.T, f.k, f.E)));
     a.mbr = (int)mbr;
     a.mbs = (int)mbs;
+    // Blocks: one per CU, or fewer when no step has work for that many (every step strides
+    // over the blocks, so any count gives the same outputs): the device-wide barriers then
+    // have fewer blocks to gather.  The widest steps: the product queue's tiles (an upper
+    // bound), four tokens per block (top-k, combine), one chunk per block (histograms), the
+    // router projection's logits (256 per block).
+    const int64_t tiles = mbr * (cdiv(f.I, 128) + cdiv(f.H, BN)) +
+                          (f.S > 0 ? (int64_t)f.S * mbs * (cdiv(f.Is, 128) + cdiv(f.H, BN)) : 0);
+    const int64_t widest = std::max<int64_t>(
+        std::max<int64_t>(tiles, cdiv(f.T, 4)),
+        std::max<int64_t>(a.nch, f.w_router ? ((int64_t)f.T * f.E_router + 255) / 256 : 1));
+    const int grid = (int)std::min<int64_t>(ncu, std::max<int64_t>(widest, 1));
     MOE_TRACED("fused_clear", st, fused_clear<<<1, 1024, 0, st>>>(a.sy, (int)words));
     MOE_LAUNCH_CHECK();
-    MOE_TRACED("layer_forward_fused", st, layer_forward_fused<<<ncu, NTH, 0, st>>>(a));
+    MOE_TRACED("layer_forward_fused", st, layer_forward_fused<<<grid, NTH, 0, st>>>(a));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
