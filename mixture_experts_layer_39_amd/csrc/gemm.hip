@@ -11,8 +11,10 @@
 // megakernelen…", ¶6, trained with a BF16 backward, same page ¶3).
 //
 // Design (CDNA4, wave64):
-//  - 256x256 output tile per 256-thread block, 4 waves in 2x2, each wave a 128x128 sub-tile
-//    of 4x4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane, one wave per SIMD).
+//  - 256x256 output tile per block of v_mfma_f32_32x32x16_bf16 accumulators: 4 waves in 2x2,
+//    each a 128x128 sub-tile (256 fp32 per lane, one wave per SIMD), or 8 waves in 4x2, each
+//    a 64x128 sub-tile (128 fp32 per lane, two waves per SIMD: one can issue while the other
+//    waits).  The operand ring and its loads are the same; each wave issues its share.
 //  - K steps of 64: a K-major tile row is then 128 contiguous bytes per step (a whole L2
 //    line per request).  At this tile size the chip's L2 can just about feed the MFMAs
 //    (both need about a tile's K loop worth of 229K cycles), so the loads must stream
@@ -78,9 +80,11 @@ struct GemmArgs {
 #endif
 // LDS of one block: the stage ring (128 KB), or for BK = 64 five operand slots (160 KB).
 constexpr int LDS_BYTES = MOE_GEMM_SLOTS5 ? 160 * 1024 : LDS_STAGES_BYTES;
-// LDS each wave stages its output sub-tile in after the K loop (a quarter of the block's)
-constexpr int EPI_WAVE_BYTES = LDS_BYTES / 4;
-static_assert(STG_BYTES <= EPI_WAVE_BYTES, "staged 128-row sub-tile");
+// LDS each wave stages its output sub-tile in after the K loop (its share of the block's)
+template <int NW>
+constexpr int epi_wave_bytes() { return LDS_BYTES / NW; }
+static_assert(STG_BYTES <= epi_wave_bytes<4>(), "staged 128-row sub-tile");
+static_assert(STG_BYTES / 2 <= epi_wave_bytes<8>(), "staged 64-row sub-tile");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -224,15 +228,22 @@ __device__ __forceinline__ TileAt tile_at(const GemmArgs& g, const int logical) 
 // expert (K-major A only): the tile covers the first TM of the M tile's 256 rows, each wave
 // TM / 2 of them, and every output element takes exactly the same MFMAs in the same order
 // as in a 256-row tile, so the results do not depend on TM.
-template <int BK, int TM, bool A_K, bool B_K, int EPI, bool GK>
+template <int BK, int TM, bool A_K, bool B_K, int EPI, bool GK, int NW>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const TileAt& at) {
     typedef Pipe<BK> PP;
-    constexpr int KK = PP::KK, NST = PP::NST, OPB = PP::OPB, LPW = PP::LPW, LPS = PP::LPS;
+    constexpr int KK = PP::KK, NST = PP::NST, OPB = PP::OPB;
     constexpr bool SLOTS5 = (BK == 64) && MOE_GEMM_SLOTS5;
     static_assert(TM == 256 || (TM == 128 || TM == 64) && A_K && SLOTS5, "tile heights");
-    constexpr int MI = TM / 64;      // 32-row accumulator blocks per wave
-    constexpr int LPA = TM / 32;     // A loads per wave per K step (LPW for a 256-row tile)
-    constexpr int WBA = TM * 32;     // bytes of A a wave loads per K step
+    static_assert(NW == 4 || (NW == 8 && SLOTS5 && TM >= 128), "eight waves: five slots");
+    constexpr int WM = NW / 2;       // waves along M (two along N)
+    constexpr int WR = TM / WM;      // rows of a wave's sub-tile
+    constexpr int MI = WR / 32;      // 32-row accumulator blocks per wave
+    static_assert(MI >= 1 && WR % 32 == 0, "wave rows");
+    constexpr int LPW = OPB / 1024 / NW;    // B loads per wave per K step
+    constexpr int LPS = 2 * LPW;
+    constexpr int WBB = OPB / NW;           // bytes of B a wave loads per K step
+    constexpr int LPA = TM * BK * 2 / 1024 / NW;  // A loads per wave per K step
+    constexpr int WBA = TM * BK * 2 / NW;   // bytes of A a wave loads per K step
     const int tid = threadIdx.x, lane = tid & 63, wid = uni(tid >> 6);
     const int wm = wid >> 1, wn = wid & 1;
     const int e = at.e, row0 = at.row0, Mrows = at.Mrows, tm = at.tm, tn = at.tn;
@@ -254,29 +265,32 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     if (A_K) {
         const bf16_t* base = g.A + e * g.a_es + (int64_t)(row0 + m0) * g.lda;
         auto ident = [](int r) { return r; };
-        setup_kmajor<BK, decltype(ident), TM / 4>(
+        setup_kmajor<BK, decltype(ident), TM / NW>(
             oa, base, (uint32_t)max(Mrows - m0, 0) * (uint32_t)g.lda * 2u, g.lda, wid, lane,
-            wm * (TM / 2), ident, 2 * PP::RPI, 4 * PP::RPI);
+            wm * WR, ident, 2 * PP::RPI, 4 * PP::RPI);
     } else {
         const bf16_t* base = g.A + e * g.a_es + (int64_t)row0 * g.lda + m0;
-        setup_mnmajor<BK>(oa, base, mn_bytes(Kdim, g.lda, m0), g.lda, wid, lane, wm * 128);
+        setup_mnmajor<BK, BK / NW>(oa, base, mn_bytes(Kdim, g.lda, m0), g.lda, wid, lane, wm * WR);
     }
     if (B_K) {
         const bf16_t* base = g.B + e * g.b_es;
         const int I = g.I;
+        auto swiglu_rows = [=](int nn) {
+            return ((nn >> 4) & 1) * I + ch0 + (nn >> 7) * 64 + ((nn & 127) >> 5) * 16 + (nn & 15);
+        };
+        auto plain_rows = [=](int nn) { return n0 + nn; };
         if (EPI == EPI_SWIGLU)
-            setup_kmajor<BK>(ob, base, (uint32_t)g.b_rows * (uint32_t)g.ldb * 2u, g.ldb, wid, lane,
-                         wn * 128, [=](int nn) {
-                             return ((nn >> 4) & 1) * I + ch0 + (nn >> 7) * 64 +
-                                    ((nn & 127) >> 5) * 16 + (nn & 15);
-                         }, PP::RPI == 8 ? I : 16, PP::RPI == 8 ? 16 : 32);
+            setup_kmajor<BK, decltype(swiglu_rows), 256 / NW>(
+                ob, base, (uint32_t)g.b_rows * (uint32_t)g.ldb * 2u, g.ldb, wid, lane, wn * 128,
+                swiglu_rows, PP::RPI == 8 ? I : 16, PP::RPI == 8 ? 16 : 32);
         else
-            setup_kmajor<BK>(ob, base, (uint32_t)g.b_rows * (uint32_t)g.ldb * 2u, g.ldb, wid, lane,
-                         wn * 128, [=](int nn) { return n0 + nn; }, 2 * PP::RPI, 4 * PP::RPI);
+            setup_kmajor<BK, decltype(plain_rows), 256 / NW>(
+                ob, base, (uint32_t)g.b_rows * (uint32_t)g.ldb * 2u, g.ldb, wid, lane, wn * 128,
+                plain_rows, 2 * PP::RPI, 4 * PP::RPI);
     } else {
         const int64_t kbase = GK ? row0 : 0;
         const bf16_t* base = g.B + e * g.b_es + kbase * g.ldb + n0;
-        setup_mnmajor<BK>(ob, base, mn_bytes(Kdim, g.ldb, n0), g.ldb, wid, lane, wn * 128);
+        setup_mnmajor<BK, BK / NW>(ob, base, mn_bytes(Kdim, g.ldb, n0), g.ldb, wid, lane, wn * 128);
     }
 
     f32x16 acc[MI][4];
@@ -296,7 +310,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
 #pragma unroll
             for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
     };
-    if (EPI == EPI_SWIGLU) pin_acc();
+    if (EPI == EPI_SWIGLU && NW == 4) pin_acc();
 
     // ---------------------------------------------------------------- main loop
     // NST stages in a ring: at the end of K step ks the stage it used is refilled with step
@@ -406,8 +420,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
             mfma_one(fl, n);
-            if (n < LPW) issue_load<BK>(oa, cur32, wid, n, ra_, sa);
-            else if (n < LPS) issue_load<BK>(ob, cur32 + OPB, wid, n - LPW, rb_, sb);
+            if (n < LPW) issue_load<BK, WBB>(oa, cur32, wid, n, ra_, sa);
+            else if (n < LPS) issue_load<BK, WBB>(ob, cur32 + OPB, wid, n - LPW, rb_, sb);
             if (n >= 8 && n - 8 < NR && more) read_one(nxt, 0, 0, n - 8);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -422,6 +436,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     // 8 fragment reads take the even MFMA slots and the 4 loads every fourth odd one.
     rsrc_t pend_rb = make_rsrc(nullptr, 0);  // descriptor and offset of B(s+1)'s second half
     uint32_t pend_sb = 0;
+    constexpr int QB = LPW / 2;  // B loads per sub-step (sub-steps 0 and 3)
     auto kstep5 = [&](int u, int ks) __attribute__((always_inline)) {
         char* const cA = sm.st + ((2 * u) % 5) * OPB;
         char* const cB = sm.st + ((2 * u + 1) % 5) * OPB;
@@ -440,6 +455,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
 #pragma unroll
         for (int kk = 0; kk < KK - 1; ++kk) {
             constexpr int QA = LPA / 2;  // A loads per sub-step (sub-steps 1, 2)
+            static_assert(QA >= 1 && 2 * QA == LPA, "A loads per sub-step");
 #pragma unroll
             for (int n = 0; n < NM; ++n) {
                 mfma_one(kk & 1, n);
@@ -448,8 +464,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
                     if (rslot(r) == n) read_ab(cA, cB, kk + 1, (kk + 1) & 1, r);
                 if (kk == 0) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (lslot(q, 4) == n) issue_load<BK>(ob, lB1, wid, 4 + q, rb1, sb1);
+                    for (int q = 0; q < QB; ++q)
+                        if (lslot(q, QB) == n) issue_load<BK, WBB>(ob, lB1, wid, QB + q, rb1, sb1);
                 } else {
 #pragma unroll
                     for (int q = 0; q < QA; ++q)
@@ -468,8 +484,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         for (int n = 0; n < NM; ++n) {
             mfma_one(fl, n);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (lslot(q, 4) == n) issue_load<BK>(ob, lB, wid, q, rb_, sb);
+            for (int q = 0; q < QB; ++q)
+                if (lslot(q, QB) == n) issue_load<BK, WBB>(ob, lB, wid, q, rb_, sb);
 #pragma unroll
             for (int r = 0; r < NR; ++r)
                 if (rslot(r) == n && more) read_ab(nA, nB, 0, 0, r);
@@ -508,7 +524,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
 #pragma unroll
                     for (int q = 0; q < LPW / 2; ++q)
                         if (lslot(q, LPW / 2) == n)
-                            issue_load<BK>(ob, lB, wid, (LPW / 2) * kk + q, rb_, sb);
+                            issue_load<BK, WBB>(ob, lB, wid, (LPW / 2) * kk + q, rb_, sb);
                 } else {       // A(ks+3) in sub-step 2
 #pragma unroll
                     for (int q = 0; q < LPA; ++q)
@@ -546,7 +562,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
 #pragma unroll
             for (int i = 0; i < LPW; ++i) {
                 if (i < LPA) issue_load<BK, WBA>(oa, base32 + 4 * OPB + p * (OPB / 4), wid, i, ra_, sa);
-                issue_load<BK>(ob, base32 + p * OPB, wid, i, rb_, sb);
+                issue_load<BK, WBB>(ob, base32 + p * OPB, wid, i, rb_, sb);
             }
         }
         wait_vm_lgkm0<2 * (LPA + LPW)>();  // step 0 landed
@@ -561,7 +577,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         }
         wait_vm_lgkm0<0>();  // no load may still be writing LDS when the block ends
     } else if (nk > 0 && SLOTS5) {
-        static_assert(!SLOTS5 || (KK == 4 && LPW == 8 && 5 * OPB <= (int)sizeof(GemmSmem)),
+        static_assert(!SLOTS5 || (KK == 4 && LPW * NW == 32 && 5 * OPB <= (int)sizeof(GemmSmem)),
                       "five-slot ring layout");
         const uint32_t base32 = lds_addr(sm.st);
         // A(0), B(0), A(1) and the first half of B(1); step 0 issues B(1)'s second half
@@ -574,7 +590,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
             for (int i = 0; i < LPW; ++i) {
                 if (i < LPA) issue_load<BK, WBA>(oa, base32 + (2 * p) * OPB, wid, i, ra_, sa);
                 if (p == 0 || i < LPW / 2)
-                    issue_load<BK>(ob, base32 + (2 * p + 1) * OPB, wid, i, rb_, sb);
+                    issue_load<BK, WBB>(ob, base32 + (2 * p + 1) * OPB, wid, i, rb_, sb);
             }
             pend_rb = rb_;
             pend_sb = sb;
@@ -591,7 +607,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         }
         wait_vm_lgkm0<0>();  // no load may still be writing LDS when the block ends
     } else if (nk > 0) {
-        static_assert(SLOTS5 || TM == 256, "the stage ring takes 256-row tiles");
+        static_assert(SLOTS5 || (TM == 256 && NW == 4), "the stage ring takes 256-row tiles");
         const uint32_t st_base = lds_addr(sm.st);  // stage p at st_base + p * 2 * OPB
 #pragma unroll
         for (int p = 0; p < NST; ++p) {
@@ -600,8 +616,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
             load_src(p, ra_, rb_, sa, sb);
 #pragma unroll
             for (int i = 0; i < LPW; ++i) {
-                issue_load<BK>(oa, st_base + p * 2 * OPB, wid, i, ra_, sa);
-                issue_load<BK>(ob, st_base + p * 2 * OPB + OPB, wid, i, rb_, sb);
+                issue_load<BK, WBB>(oa, st_base + p * 2 * OPB, wid, i, ra_, sa);
+                issue_load<BK, WBB>(ob, st_base + p * 2 * OPB + OPB, wid, i, rb_, sb);
             }
         }
         wait_vm_lgkm0<(NST - 1) * LPS>();  // step 0 landed
@@ -623,9 +639,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     // quarter of the (now free) operand slots and stores whole rows.
     const int lrow = lane & 31, lcol = (lane >> 5) * 4;
     __syncthreads();                                  // every wave is done reading the slots
-    char* const stg = sm.st + wid * EPI_WAVE_BYTES;
-    const int wrow = m0 + wm * (TM / 2);              // the wave's first row (of the tile's rows)
-    const int wrows = min(Mvalid - wrow, TM / 2);      // its rows that exist
+    static_assert(MI * 32 * STG_RS <= epi_wave_bytes<NW>(), "staging area of a wave");
+    char* const stg = sm.st + wid * epi_wave_bytes<NW>();
+    const int wrow = m0 + wm * WR;                    // the wave's first row (of the tile's rows)
+    const int wrows = min(Mvalid - wrow, WR);          // its rows that exist
     if (EPI == EPI_STORE) {
         bf16_t* C = g.C + e * g.c_es + (GK ? 0 : (int64_t)row0 * g.ldc);
         const int col = n0 + wn * 128;
@@ -701,7 +718,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
         const int chw = n0 + wn * 128;
         bf16_t* C = g.C + e * g.c_es + (int64_t)row0 * g.ldc;
         const bf16_t* GU = g.C2 + e * g.c2_es + (int64_t)row0 * g.ldc2;
-        dswiglu_staged<MI>(stg, acc, GU + (int64_t)wrow * g.ldc2 + chw, g.ldc2,
+        dswiglu_staged<MI, NW == 4 ? 2 : 1>(stg, acc, GU + (int64_t)wrow * g.ldc2 + chw, g.ldc2,
                            C + (int64_t)wrow * g.ldc + chw, g.ldc, g.I, wrows, g.N - chw, lane);
     }
 }
@@ -709,34 +726,49 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
 // A tile of a product: the products with ragged, K-major A (rows of experts) run each
 // expert's last M tile, when it holds at most 128 (64) rows, as a 128-row (64-row) tile: less
 // MFMA work on padding rows, bit-identical results.
-template <int BK, bool A_K, bool B_K, int EPI, bool GK>
+template <int BK, bool A_K, bool B_K, int EPI, bool GK, int NW>
 __device__ __forceinline__ void run_tile(const GemmArgs& g, GemmSmem& sm, const TileAt& at) {
     if (A_K && !GK) {
         const int rem = at.Mrows - at.tm * BM;
-        if (rem <= 64) {
-            gemm_tile<BK, (A_K && !GK) ? 64 : 256, A_K, B_K, EPI, GK>(g, sm, at);
+        if (NW == 4 && rem <= 64) {
+            gemm_tile<BK, (A_K && !GK && NW == 4) ? 64 : 256, A_K, B_K, EPI, GK, NW>(g, sm, at);
             return;
         }
         if (rem <= 128) {
-            gemm_tile<BK, (A_K && !GK) ? 128 : 256, A_K, B_K, EPI, GK>(g, sm, at);
+            gemm_tile<BK, (A_K && !GK) ? 128 : 256, A_K, B_K, EPI, GK, NW>(g, sm, at);
             return;
         }
     }
-    gemm_tile<BK, 256, A_K, B_K, EPI, GK>(g, sm, at);
+    gemm_tile<BK, 256, A_K, B_K, EPI, GK, NW>(g, sm, at);
 }
 
 // One kernel symbol per product of the layer, so that profiles name each role.
 // K step per product.  Every product measures fastest with 64-wide steps in the five-slot
 // ring (the 32-wide ring of four stages stays available to the tile routine).
 constexpr int BK_FWD = 64, BK_DGRAD = 64, BK_WGRAD = 64;
+// Waves per block: 4 (one per SIMD, each a 128 x 128 sub-tile) for the forward products, 8
+// (two per SIMD, 64 x 128 each) for the backward pairs.  Same-box measurements: the backward
+// pairs of the weight-streaming layers (many small experts, weight-gradient tiles of a few K
+// steps) ran 5-8% faster with eight waves and the EP-64 share's pairs the same or 1% faster;
+// the forward products ran 1-2% slower (and their experts' last tiles of at most 64 rows lose
+// the deep ring, which needs four waves).  The single launch keeps 4: its other steps are
+// written for 256-thread blocks.
+#ifndef MOE_FWD_NW
+#define MOE_FWD_NW 4
+#endif
+#ifndef MOE_BWD_NW
+#define MOE_BWD_NW 8
+#endif
+constexpr int FWD_NW = MOE_FWD_NW, BWD_NW = MOE_BWD_NW;
+#define MOE_GEMM_ATTRS(NW) \
+    __launch_bounds__(64 * (NW)) __attribute__((amdgpu_waves_per_eu((NW) / 4, (NW) / 4)))
 
-#define MOE_GEMM_KERNEL(NAME, AKM, BKM, EPI, GK)                                       \
-    __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))) void \
-    NAME(GemmArgs g) {                                                                 \
-        __shared__ GemmSmem sm;                                                        \
-        const int total = tile_total<EPI, GK>(g);                                      \
-        if ((int)blockIdx.x < total)                                                    \
-            run_tile<BK_FWD, AKM, BKM, EPI, GK>(g, sm, tile_at<EPI, GK>(g, blockIdx.x));  \
+#define MOE_GEMM_KERNEL(NAME, AKM, BKM, EPI, GK)                                          \
+    __global__ MOE_GEMM_ATTRS(FWD_NW) void NAME(GemmArgs g) {                             \
+        __shared__ GemmSmem sm;                                                            \
+        const int total = tile_total<EPI, GK>(g);                                          \
+        if ((int)blockIdx.x < total)                                                        \
+            run_tile<BK_FWD, AKM, BKM, EPI, GK, FWD_NW>(g, sm, tile_at<EPI, GK>(g, blockIdx.x)); \
     }
 MOE_GEMM_KERNEL(gemm1_swiglu, true, true, EPI_SWIGLU, false)     // [g|u] = Xp W1^T, h
 MOE_GEMM_KERNEL(gemm2_down, true, true, EPI_STORE, false)        // y = h W2^T
@@ -751,27 +783,25 @@ MOE_GEMM_KERNEL(gemm2_down, true, true, EPI_STORE, false)        // y = h W2^T
 // weighs on weight-gradient tiles of one or two K steps.
 //   bwd_down:     dh = dy W2 -> dg|du (SwiGLU backward)   and   dW2 = dy^T h
 //   bwd_gate_up:  dXp = dGU W1                           and   dW1 = dGU^T Xp
-__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_down(GemmArgs gd, GemmArgs gw) {
+__global__ MOE_GEMM_ATTRS(BWD_NW) void bwd_down(GemmArgs gd, GemmArgs gw) {
     __shared__ GemmSmem sm;
     const int b = blockIdx.x;
     if (b < gd.bound) {
         if (b < tile_total<EPI_DSWIGLU, false>(gd))
-            run_tile<BK_DGRAD, true, false, EPI_DSWIGLU, false>(gd, sm, tile_at<EPI_DSWIGLU, false>(gd, b));
+            run_tile<BK_DGRAD, true, false, EPI_DSWIGLU, false, BWD_NW>(gd, sm, tile_at<EPI_DSWIGLU, false>(gd, b));
     } else if (b - gd.bound < gw.total) {
-        run_tile<BK_WGRAD, false, false, EPI_STORE, true>(gw, sm, tile_at<EPI_STORE, true>(gw, b - gd.bound));
+        run_tile<BK_WGRAD, false, false, EPI_STORE, true, BWD_NW>(gw, sm, tile_at<EPI_STORE, true>(gw, b - gd.bound));
     }
 }
 
-__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_gate_up(GemmArgs gd, GemmArgs gw) {
+__global__ MOE_GEMM_ATTRS(BWD_NW) void bwd_gate_up(GemmArgs gd, GemmArgs gw) {
     __shared__ GemmSmem sm;
     const int b = blockIdx.x;
     if (b < gd.bound) {
         if (b < tile_total<EPI_STORE, false>(gd))
-            run_tile<BK_DGRAD, true, false, EPI_STORE, false>(gd, sm, tile_at<EPI_STORE, false>(gd, b));
+            run_tile<BK_DGRAD, true, false, EPI_STORE, false, BWD_NW>(gd, sm, tile_at<EPI_STORE, false>(gd, b));
     } else if (b - gd.bound < gw.total) {
-        run_tile<BK_WGRAD, false, false, EPI_STORE, true>(gw, sm, tile_at<EPI_STORE, true>(gw, b - gd.bound));
+        run_tile<BK_WGRAD, false, false, EPI_STORE, true, BWD_NW>(gw, sm, tile_at<EPI_STORE, true>(gw, b - gd.bound));
     }
 }
 
@@ -792,7 +822,7 @@ static int launch(void (*kern)(GemmArgs), const char* name, const GemmArgs& g, i
                   hipStream_t st) {
     const int grid = grid_of(g, NT, false);
     if (grid <= 0) return MOE_OK;
-    MOE_TRACED(name, st, kern<<<grid, NTH, 0, st>>>(g));
+    MOE_TRACED(name, st, kern<<<grid, 64 * FWD_NW, 0, st>>>(g));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -803,7 +833,7 @@ static int launch_pair(void (*kern)(GemmArgs, GemmArgs), const char* name, const
     gd.bound = grid_of(gd, cdiv(gd.N, BN), false);
     const int grid = gd.bound + gw.total;
     if (grid <= 0) return MOE_OK;
-    MOE_TRACED(name, st, kern<<<grid, NTH, 0, st>>>(gd, gw));
+    MOE_TRACED(name, st, kern<<<grid, 64 * BWD_NW, 0, st>>>(gd, gw));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -976,7 +1006,7 @@ void layer_forward_fused(FusedFwd a) {
             const bool r = item < n1r;
             const GemmArgs& g = r ? a.g1 : a.s1;
             const TileAt at = tile_at<EPI_SWIGLU, false>(g, r ? item : item - n1r);
-            run_tile<BK_FWD, true, true, EPI_SWIGLU, false>(g, sm, at);
+            run_tile<BK_FWD, true, true, EPI_SWIGLU, false, 4>(g, sm, at);
             tile_done(ready1, r ? at.mblock : a.mbr + at.mblock);
         } else {
             const int i2 = item - n1;
@@ -988,7 +1018,7 @@ void layer_forward_fused(FusedFwd a) {
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             }
             __syncthreads();
-            run_tile<BK_FWD, true, true, EPI_STORE, false>(g, sm, at);
+            run_tile<BK_FWD, true, true, EPI_STORE, false, 4>(g, sm, at);
         }
         __syncthreads();
         if (threadIdx.x == 0) *bcast = next;
@@ -1022,8 +1052,7 @@ __global__ void ffn_queue_clear(unsigned* sy, int words) {
     for (int i = threadIdx.x; i < words; i += blockDim.x) sy[i] = 0;
 }
 
-__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void ffn_queue(FfnQueue q) {
+__global__ MOE_GEMM_ATTRS(FWD_NW) void ffn_queue(FfnQueue q) {
     __shared__ GemmSmem sm;
     unsigned* const ready = q.sy + SY_READY;
     const int n1 = tile_total<EPI_SWIGLU, false>(q.g1);
@@ -1040,7 +1069,7 @@ void ffn_queue(FfnQueue q) {
         if (item >= total) break;
         if (item < n1) {
             const TileAt at = tile_at<EPI_SWIGLU, false>(q.g1, item);
-            run_tile<BK_FWD, true, true, EPI_SWIGLU, false>(q.g1, sm, at);
+            run_tile<BK_FWD, true, true, EPI_SWIGLU, false, FWD_NW>(q.g1, sm, at);
             tile_done(ready, at.mblock);
         } else {
             const TileAt at = tile_at<EPI_STORE, false>(q.g2, item - n1);
@@ -1049,7 +1078,7 @@ void ffn_queue(FfnQueue q) {
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             }
             __syncthreads();
-            run_tile<BK_FWD, true, true, EPI_STORE, false>(q.g2, sm, at);
+            run_tile<BK_FWD, true, true, EPI_STORE, false, FWD_NW>(q.g2, sm, at);
         }
         __syncthreads();
     }
@@ -1127,7 +1156,7 @@ int moe_ffn_bf16_queue(const bf16_t* xp, const int32_t* offsets, int E, int R, i
     const int words = (int)(SY_READY + moe_ffn_row_blocks(E, R, offsets == nullptr));
     MOE_TRACED("ffn_queue_clear", st, ffn_queue_clear<<<1, 1024, 0, st>>>(sy, words));
     MOE_LAUNCH_CHECK();
-    MOE_TRACED("ffn_queue", st, ffn_queue<<<grid, NTH, 0, st>>>(q));
+    MOE_TRACED("ffn_queue", st, ffn_queue<<<grid, 64 * FWD_NW, 0, st>>>(q));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

@@ -95,8 +95,8 @@ template <int BK>
 __device__ __forceinline__ int kswz_of(int r) { return BK == 64 ? kswz8(r) : kswz4(r); }
 
 // Per-lane description of one operand's global->LDS loads (LPW per wave per K step) and of
-// its MFMA fragment reads (4 sub-tiles of 32 rows per wave).  Wave w fills the quarter of
-// the operand's stage area at w OPB/4, 1 KB per instruction.  The global offset of load i
+// its MFMA fragment reads (up to 4 sub-tiles of 32 rows per wave).  Of NW waves, wave w fills
+// the NW-th of the operand's stage area at w OPB/NW, 1 KB per instruction.  The global offset of load i
 // is voff[i % 2] + ((i / 2) % 2) ist1 + (i / 4) ist2: the swizzled chunk depends only on the
 // parity of i, and the rows of one wave's loads advance by two scalar strides.
 struct Operand {
@@ -140,14 +140,14 @@ __device__ __forceinline__ void setup_kmajor(Operand& o, const void* base, uint3
 }
 
 // MN-major operand: element (mn, k) at base + k*ld + mn (bytes x2).  Each wave loads
-// BK/4 k-rows of the step, 2 per instruction.
-template <int BK>
+// KPW k-rows of the step (BK/4 with four waves, BK/8 with eight), 2 per instruction.
+template <int BK, int KPW = BK / 4>
 __device__ __forceinline__ void setup_mnmajor(Operand& o, const void* base, uint32_t bytes, int ld,
                                               int wid, int lane, int wsub) {
     o.r = make_rsrc(base, bytes);
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
-        const int kr = (BK / 4) * wid + 2 * par + (lane >> 5);
+        const int kr = KPW * wid + 2 * par + (lane >> 5);
         const int c = (lane & 31) ^ mswz(kr);
         o.voff[par] = (uint32_t)kr * (uint32_t)ld * 2u + (uint32_t)c * 16u;
     }
@@ -167,7 +167,7 @@ __device__ __forceinline__ void setup_mnmajor(Operand& o, const void* base, uint
 }
 
 // Load instruction i of K step ks into the operand's area of a stage (wave w fills the WB
-// bytes from w WB: a quarter of the operand's rows).  Steps past the end of K use an empty
+// bytes from w WB: its share of the operand's rows).  Steps past the end of K use an empty
 // descriptor: the load still issues (so every step issues the same number of loads and the
 // wait counts are constants) but fetches nothing and writes zeros.
 template <int BK, int WB = Pipe<BK>::OPB / 4>
@@ -178,8 +178,8 @@ __device__ __forceinline__ void issue_load(const Operand& o, uint32_t stage_op, 
 }
 
 // ---------------------------------------------------------------- staged epilogues
-// After the K loop each wave owns a 128 x 128 output sub-tile in accumulators: 4 x 4 blocks of
-// 32 x 32, B fragment first, so lane l holds row l % 32 of a block and columns
+// After the K loop each wave owns a 32 MI x 128 output sub-tile in accumulators: MI x 4 blocks
+// of 32 x 32, B fragment first, so lane l holds row l % 32 of a block and columns
 // 8 (v / 4) + 4 (l / 32) + v % 4, v = 0..15.  Stores go through LDS: the wave writes its
 // sub-tile into a private staging area (row-major, rows STG_RS bytes apart: 256 bytes plus a
 // 16-byte pad that spreads the 32 rows of one accumulator write over the banks) and reads it
@@ -226,16 +226,18 @@ __device__ __forceinline__ void store_staged(const char* stg, bf16_t* C, int64_t
 
 // The SwiGLU backward of a dgrad sub-tile (acc = dh at 32 MI rows x 128 channels): with the
 // saved g at GU + r * ldgu + c (u at + I) it writes dg at C + r * ldc + c and du at + I, for
-// rows r < nrows and 8-channel chunks with c < ncols.  In parts of up to 64 rows (two blocks
-// of 32): the g and u rows of the part are loaded as whole-row 16-byte chunks into the staging
-// area (g rows 0-63, u rows 64-127), each lane turns its own g, u elements into dg, du in
-// place (one lane owns each element), and the rows go back out whole.
-template <int MI>
+// rows r < nrows and 8-channel chunks with c < ncols.  In parts of up to 32 PBMAX rows (PBMAX
+// blocks of 32): the g and u rows of the part are loaded as whole-row 16-byte chunks into the
+// staging area (g rows first, then u rows), each lane turns its own g, u elements into dg, du
+// in place (one lane owns each element), and the rows go back out whole.  The staging area
+// takes 64 PB rows.
+template <int MI, int PBMAX = 2>
 __device__ __forceinline__ void dswiglu_staged(char* stg, const f32x16 (&acc)[MI][4],
                                                const bf16_t* GU, int64_t ldgu, bf16_t* C,
                                                int64_t ldc, int I, int nrows, int ncols,
                                                int lane) {
-    constexpr int PB = MI < 2 ? MI : 2;  // 32-row blocks per part
+    constexpr int PB = MI < PBMAX ? MI : PBMAX;  // 32-row blocks per part
+    constexpr int UR = 32 * PB;                  // first staged row of u
     const int lrow = lane & 31, lcol = (lane >> 5) * 4;
     const int rr = lane >> 4, ck = lane & 15;
     const bool colok = ck * 8 < ncols;
@@ -252,7 +254,7 @@ __device__ __forceinline__ void dswiglu_staged(char* stg, const f32x16 (&acc)[MI
                 uv = ld16(src + I);
             }
             *reinterpret_cast<u32x4*>(stg + r * STG_RS + ck * 16) = gv;
-            *reinterpret_cast<u32x4*>(stg + (64 + r) * STG_RS + ck * 16) = uv;
+            *reinterpret_cast<u32x4*>(stg + (UR + r) * STG_RS + ck * 16) = uv;
         }
         lds_wait();
 #pragma unroll
@@ -263,7 +265,7 @@ __device__ __forceinline__ void dswiglu_staged(char* stg, const f32x16 (&acc)[MI
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     char* pg = stg + (ih * 32 + lrow) * STG_RS + (j * 32 + 8 * q + lcol) * 2;
-                    char* pu = pg + 64 * STG_RS;
+                    char* pu = pg + UR * STG_RS;
                     const uint2 gg = *reinterpret_cast<const uint2*>(pg);
                     const uint2 uu = *reinterpret_cast<const uint2*>(pu);
                     const float gv[4] = {lo_bf(gg.x), hi_bf(gg.x), lo_bf(gg.y), hi_bf(gg.y)};
@@ -287,7 +289,7 @@ __device__ __forceinline__ void dswiglu_staged(char* stg, const f32x16 (&acc)[MI
         for (int p = 0; p < 8 * PB; ++p) {
             const int r = 4 * p + rr;
             const u32x4 dgv = *reinterpret_cast<const u32x4*>(stg + r * STG_RS + ck * 16);
-            const u32x4 duv = *reinterpret_cast<const u32x4*>(stg + (64 + r) * STG_RS + ck * 16);
+            const u32x4 duv = *reinterpret_cast<const u32x4*>(stg + (UR + r) * STG_RS + ck * 16);
             if (rb + r < nrows && colok) {
                 bf16_t* dst = C + (int64_t)(rb + r) * ldc + ck * 8;
                 st16(dst, dgv);
