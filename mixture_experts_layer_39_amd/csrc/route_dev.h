@@ -47,13 +47,30 @@ __device__ __forceinline__ uint64_t pack_key(float k, int id) {
 }
 __device__ __forceinline__ int key_id(uint64_t p) { return (int)(0xFFFFu - (uint32_t)(p & 0xFFFFu)); }
 
+// Maximum over the wave's 64 lanes (every lane active), returned wave-uniform.  Within each
+// row of 16 lanes by DPP moves (quad swaps of 1 and 2 lanes, then the half-row and row
+// mirrors: each step pairs groups that already hold their own maxima), then the four rows'
+// maxima through readlane.  DPP moves take a few cycles where the LDS permutes of a shuffle
+// butterfly take about a hundred each, and the top-k chains dozens of these reductions.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        uint64_t o = __shfl_xor(v, d, 64);
-        v = o > v ? o : v;
-    }
-    return v;
+    v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = max_u64(v, dpp_u64<0x141>(v));  // row_half_mirror
+    v = max_u64(v, dpp_u64<0x140>(v));  // row_mirror
+    return max_u64(max_u64(lane_u64(v, 0), lane_u64(v, 16)),
+                   max_u64(lane_u64(v, 32), lane_u64(v, 48)));
 }
 
 // Fixed-order wave sum (butterfly): every lane ends with the same bits.
@@ -137,6 +154,9 @@ __device__ __forceinline__ void topk_token(const TopkParams& p, const int t, con
     }
     if (p.n_groups > 1) {
         const int gs = p.E / p.n_groups;
+        int grp[NV];  // group of each of the lane's experts (-1: none)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) grp[i] = lane + 64 * i < p.E ? (lane + 64 * i) / gs : -1;
         // group scores: fp32 sum, largest first, of the top per_group keys of each group
         float gscore_mine = 0.0f;  // lane g holds group g's score (n_groups <= 64)
         for (int g = 0; g < p.n_groups; ++g) {
@@ -148,8 +168,7 @@ __device__ __forceinline__ void topk_token(const TopkParams& p, const int t, con
                 uint64_t best = 0;
 #pragma unroll
                 for (int i = 0; i < NV; ++i) {
-                    int e = lane + 64 * i;
-                    bool in = e < p.E && e / gs == g && !taken_bits[i];
+                    bool in = grp[i] == g && !taken_bits[i];
                     uint64_t c = in ? key[i] : 0;
                     best = c > best ? c : best;
                 }
@@ -174,10 +193,8 @@ __device__ __forceinline__ void topk_token(const TopkParams& p, const int t, con
         }
         uint64_t keepmask = __ballot(keep);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            int e = lane + 64 * i;
-            if (e < p.E && !((keepmask >> (e / gs)) & 1)) key[i] = 0;
-        }
+        for (int i = 0; i < NV; ++i)
+            if (grp[i] >= 0 && !((keepmask >> grp[i]) & 1)) key[i] = 0;
     }
     // top-k: k rounds of wave argmax; lane j keeps slot j
     int my_id = 0;
@@ -196,7 +213,7 @@ __device__ __forceinline__ void topk_token(const TopkParams& p, const int t, con
 #pragma unroll
         for (int i = 0; i < NV; ++i)
             if (lane + 64 * i == eb) lv = lg[i];
-        lv = __shfl(lv, eb & 63, 64);
+        lv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), eb & 63));
         if (lane == j) { my_id = eb; my_logit = lv; }
     }
     // weights
