@@ -102,6 +102,34 @@ def test_layer_weight_gradient_tails():
     assert not torch.any(layer.dw1[2] != 0) and not torch.any(layer.dw2[2] != 0)
 
 
+def test_layer_tile_height_boundaries():
+    """Experts of exactly 64, 65, 128, 129, 257 and 261 rows: each expert's last M tile sits
+    at a boundary of the 64-, 128- and 256-row tile heights (the forward runs tails of at most
+    64 rows in the deep ring, the eight-wave backward runs them as 128-row tiles) -- forward
+    and backward against the complete oracle.  The share's k = 8 rows per token: 113 tokens."""
+    counts = np.array([64, 65, 128, 129, 257, 261])
+    T = int(counts.sum()) // 8
+    wl = wk.WORKLOADS["dsv3_ep64"].scaled(T=T, H=512, I=256, E=len(counts),
+                                          R_share=int(counts.sum()))
+    inp = wk.make_inputs(wl, device="cuda")
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    np.random.default_rng(5).shuffle(ids)
+    inp["idx_local"] = torch.from_numpy(ids.reshape(T, -1)).to("cuda")
+    layer = MoELayer(LayerCfg.from_workload(wl), inp, "cuda", backward=True)
+    print(f"tile height boundaries case counts={counts.tolist()}", flush=True)
+    layer.forward()
+    layer.backward()
+    torch.cuda.synchronize()
+    p = oracle_params(wl, inp)
+    r = orc.layer_forward(p)
+    assert np.array_equal(r["counts"], counts)
+    assert np.array_equal(host(layer.counts), counts)
+    assert_close(bf(layer.out), r["out"], TOL_BF16, "out")
+    g = orc.layer_backward(p, r, wk.bf16_bits(inp["dout"]))
+    for name in ("dx", "dw1", "dw2"):
+        assert_close(bf(getattr(layer, name)), g[name], TOL_BF16, name)
+
+
 def test_layer_tiny_dimensions_full_oracle():
     """H = I = 64 (the smallest the boundary takes): every product a K loop of one or two
     steps, tiles far wider than the operands, weight gradients of 64 x 128 and 128 x 64 --
