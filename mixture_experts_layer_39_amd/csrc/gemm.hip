@@ -225,9 +225,9 @@ __device__ __forceinline__ TileAt tile_at(const GemmArgs& g, const int logical) 
 // blocks in flight at once, spread over all XCDs, work on neighbouring tiles whose operand
 // panels meet in the shared last-level cache, which measured faster than giving each XCD
 // its own compact block of tiles).  TM = 256, or 128 / 64 for the last, partial M tile of an
-// expert (K-major A only): the tile covers the first TM of the M tile's 256 rows, each wave
-// TM / 2 of them, and every output element takes exactly the same MFMAs in the same order
-// as in a 256-row tile, so the results do not depend on TM.
+// expert (K-major A only; 64 with 4 waves only): the tile covers the first TM of the M tile's
+// 256 rows, each wave TM / (NW / 2) of them, and every output element takes exactly the same
+// MFMAs in the same order as in a 256-row tile, so the results depend neither on TM nor on NW.
 template <int BK, int TM, bool A_K, bool B_K, int EPI, bool GK, int NW>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const TileAt& at) {
     typedef Pipe<BK> PP;
@@ -635,8 +635,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, GemmSmem& sm, const
     }
 
     // ---------------------------------------------------------------- epilogue
-    // Through LDS (staged epilogues, pipe.h): each wave stages its 128 x 128 sub-tile in its
-    // quarter of the (now free) operand slots and stores whole rows.
+    // Through LDS (staged epilogues, pipe.h): each wave stages its WR x 128 sub-tile in its
+    // share (a quarter or an eighth) of the (now free) operand slots and stores whole rows.
     const int lrow = lane & 31, lcol = (lane >> 5) * 4;
     __syncthreads();                                  // every wave is done reading the slots
     static_assert(MI * 32 * STG_RS <= epi_wave_bytes<NW>(), "staging area of a wave");
