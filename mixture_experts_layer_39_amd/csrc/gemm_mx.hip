@@ -25,7 +25,8 @@ namespace moe {
 
 constexpr int XBM = 256, XBN = 256, XNTH = 256;
 constexpr int XBK = 128;                 // codes (bytes) per K step
-constexpr int XGM = 4;                   // M tiles per L2 group
+constexpr int XGM = 2;                   // M tiles per group of the launch order (as the
+                                         // BF16 products: fewer panels per XCD than 4)
 typedef Pipe<64> XP;                     // 128-byte rows: the LDS layout of a 64-wide BF16 step
 constexpr int XOPB = XP::OPB;            // bytes of one operand step (one slot)
 constexpr int XLPW = XP::LPW;            // direct loads per operand per wave per step
